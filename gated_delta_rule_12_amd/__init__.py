@@ -1,0 +1,163 @@
+"""Python binding of the KDA HIP library (``libkda.so``, gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/kda.h``.  PyTorch provides
+device memory (outputs and workspace, when the caller does not pass them)
+and the current HIP stream.  There is no fallback: when ``libkda.so`` is
+missing the first call raises.
+
+Functions carry the C names:
+
+* ``kda_chunk_fwd``                 chunkwise forward (prefill / training forward)
+* ``kda_chunk_fwd_workspace_bytes`` workspace size of a chunkwise forward
+* ``kda_recurrent_step``            one decode step, state updated in place
+* ``kda_status_string``             name of a status code
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_SUCCESS = 0
+KDA_ERROR_INVALID_VALUE = 1
+KDA_ERROR_NOT_SUPPORTED = 2
+KDA_ERROR_WORKSPACE_TOO_SMALL = 3
+KDA_ERROR_LAUNCH = 4
+
+KDA_DTYPE_F32 = 0
+KDA_DTYPE_BF16 = 1
+
+EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
+            "kda_recurrent_step")
+
+_lib = None
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kda_status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libkda.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"KDA HIP library not built: {LIB_PATH} is missing "
+                               "(run __graft_entry__.build() or gated_delta_rule_12_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_status_string.argtypes = [i32]
+        L.kda_chunk_fwd_workspace_bytes.restype = sz
+        L.kda_chunk_fwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
+        L.kda_chunk_fwd.restype = i32
+        L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
+                                    i32, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.kda_recurrent_step.restype = i32
+        L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                         i32, i32, vp]
+        _lib = L
+    return _lib
+
+
+def kda_status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return KDA_DTYPE_F32
+    if t == torch.bfloat16:
+        return KDA_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("KDA tensors must be contiguous")
+    return t.data_ptr() or None
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def kda_chunk_fwd_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, varlen: bool,
+                                  num_seqs: int, chunk_size: int, act_dtype) -> int:
+    dt = act_dtype if isinstance(act_dtype, int) else _dt(act_dtype)
+    return int(lib().kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, int(bool(varlen)),
+                                                   num_seqs, chunk_size, dt))
+
+
+def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                  beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                  final_state=None, cu_seqlens: Optional[torch.Tensor] = None,
+                  o: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None, chunk_size: int = 64,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA forward on the GPU.
+
+    q, k, alpha [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H]; initial_state
+    [N,H,Dk,Dv] fp32 or None; cu_seqlens int32 [N+1] (B == 1) or None.
+    ``final_state``: None (not computed), True (allocate) or an fp32 tensor
+    [N,H,Dk,Dv] (may be ``initial_state`` itself, updated in place).
+    Returns (o, final_state or None).
+    """
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    act = _dt(q.dtype)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=dev)
+    if final_state is True:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, cu_seqlens is not None, N,
+                                         chunk_size, act)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                             _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
+                             _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(out_dtype),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_chunk_fwd")
+    return o, final_state
+
+
+def kda_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                       beta: torch.Tensor, state: torch.Tensor, o: Optional[torch.Tensor] = None,
+                       out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
+    """One KDA decode step on the GPU; ``state`` [N,H,Dk,Dv] fp32 is updated in place.
+
+    q, k, alpha [N,H,Dk]; v [N,H,Dv]; beta [N,H].  Returns o [N,H,Dv].
+    """
+    N, H, Dk = q.shape
+    Dv = v.shape[-1]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+    st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                  _ptr(state), _ptr(o), N, H, Dk, Dv, _dt(q.dtype),
+                                  _dt(out_dtype), _stream(stream))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_recurrent_step")
+    return o

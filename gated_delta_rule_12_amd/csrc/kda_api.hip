@@ -1,0 +1,112 @@
+// Host side of the KDA C ABI: argument validation, workspace planning and
+// kernel dispatch.  Every check runs before the first launch; a rejected call
+// launches nothing.
+#include <stdint.h>
+
+#include "kda_chunk.h"
+#include "kda_common.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool supported_head(int d) { return d == 64 || d == 128; }
+
+bool valid_dtype(kda_dtype d) { return d == KDA_DTYPE_F32 || d == KDA_DTYPE_BF16; }
+
+// Output may be fp32 for any activation type, bf16 only for bf16 activations.
+bool valid_out(kda_dtype act, kda_dtype out) {
+    return out == KDA_DTYPE_F32 || (out == KDA_DTYPE_BF16 && act == KDA_DTYPE_BF16);
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_SUCCESS: return "KDA_SUCCESS";
+        case KDA_ERROR_INVALID_VALUE: return "KDA_ERROR_INVALID_VALUE";
+        case KDA_ERROR_NOT_SUPPORTED: return "KDA_ERROR_NOT_SUPPORTED";
+        case KDA_ERROR_WORKSPACE_TOO_SMALL: return "KDA_ERROR_WORKSPACE_TOO_SMALL";
+        case KDA_ERROR_LAUNCH: return "KDA_ERROR_LAUNCH";
+    }
+    return "KDA_ERROR_UNKNOWN";
+}
+
+size_t kda_chunk_fwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv, int varlen,
+                                     int num_seqs, int chunk_size, kda_dtype act_dtype) {
+    kda::ChunkPlan plan;
+    if (kda::make_chunk_plan(B, T, H, Dk, Dv, varlen != 0, num_seqs, chunk_size,
+                             act_dtype == KDA_DTYPE_BF16, &plan) != KDA_SUCCESS)
+        return 0;
+    if (!valid_dtype(act_dtype)) return 0;
+    return plan.workspace_bytes;
+}
+
+kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* beta, const float* initial_state, float* final_state,
+                         const int32_t* cu_seqlens, int num_seqs, void* o, int B, int64_t T,
+                         int H, int Dk, int Dv, int chunk_size, kda_dtype act_dtype,
+                         kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype)) return KDA_ERROR_INVALID_VALUE;
+    if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 0)) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_head(Dk) || !supported_head(Dv) || chunk_size != 64) return KDA_ERROR_NOT_SUPPORTED;
+
+    kda::ChunkPlan plan;
+    const kda_status ps = kda::make_chunk_plan(B, T, H, Dk, Dv, cu_seqlens != nullptr, num_seqs,
+                                               chunk_size, act_dtype == KDA_DTYPE_BF16, &plan);
+    if (ps != KDA_SUCCESS) return ps;
+
+    const bool has_tokens = (int64_t)B * T > 0;
+    if (has_tokens) {
+        if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) ||
+            !aligned4(beta) || !aligned16(o))
+            return KDA_ERROR_INVALID_VALUE;
+    }
+    if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERROR_INVALID_VALUE;
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERROR_INVALID_VALUE;
+    if (plan.N == 0) return KDA_SUCCESS;                 // nothing to compute or write
+    if (plan.workspace_bytes > 0) {
+        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+            return KDA_ERROR_INVALID_VALUE;
+        if (workspace_bytes < plan.workspace_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+    }
+
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.initial_state = initial_state; a.final_state = final_state;
+    a.cu_seqlens = cu_seqlens; a.o = o; a.workspace = workspace;
+    a.act_bf16 = act_dtype == KDA_DTYPE_BF16;
+    a.out_bf16 = out_dtype == KDA_DTYPE_BF16;
+    return from_hip(kda::launch_chunk_fwd(plan, a, static_cast<hipStream_t>(stream)));
+}
+
+kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, float* state, void* o, int N, int H, int Dk,
+                              int Dv, kda_dtype act_dtype, kda_dtype out_dtype, void* stream) {
+    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype)) return KDA_ERROR_INVALID_VALUE;
+    if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
+    if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_head(Dk) || !supported_head(Dv)) return KDA_ERROR_NOT_SUPPORTED;
+    if ((int64_t)N * H > 0x7fffffffLL) return KDA_ERROR_NOT_SUPPORTED;
+    if (N == 0) return KDA_SUCCESS;
+    if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned4(beta) ||
+        !aligned16(state) || !aligned16(o))
+        return KDA_ERROR_INVALID_VALUE;
+    return from_hip(kda::launch_recurrent_step(q, k, v, alpha, beta, state, o, N, H, Dk, Dv,
+                                               act_dtype == KDA_DTYPE_BF16,
+                                               out_dtype == KDA_DTYPE_BF16,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Chunkwise forward: workspace plan and launcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+constexpr int kChunk = 64;      // tokens per chunk
+
+// Where everything lives in the caller's workspace.  All offsets are bytes
+// from the workspace base and 256-byte aligned.
+//
+//   ctrl       int32[4]            [0] = number of chunks actually used
+//   first      int32[N+1]          first chunk of each sequence (prefix sums)
+//   order      int32[N]            sequences by decreasing length (ties: index)
+//   table      int32[Gmax][4]      per chunk: sequence, first token row, length
+//   per (chunk g, head h), index g*H + h, element type E = fp16 (bf16
+//   activations) or fp32 (fp32 activations):
+//     qh       E[64][Dk]           Gamma (.) Q            (token-major)
+//     w        E[64][Dk]           W = T Diag(beta) (Gamma (.) K)
+//     ktt      E[Dk][64]           ((gamma/Gamma) (.) K)^T (channel-major)
+//     p        E[64][64]           Tril((Gamma.Q)(K/Gamma)^T), zero above the diagonal
+//     ut       f32[Dv][64]         U^T, U = T Diag(beta) V
+//     gam      f32[Dk]             whole-chunk decay gamma
+struct ChunkPlan {
+    int B = 0, H = 0, Dk = 0, Dv = 0, N = 0;
+    int64_t T = 0;
+    bool varlen = false;
+    bool f16 = false;             // bf16 activations -> fp16 matrix-core operands
+    int64_t gmax = 0;             // chunk-table capacity
+    size_t eb = 4;                // bytes per intermediate element
+    size_t off_ctrl = 0, off_first = 0, off_order = 0, off_table = 0;
+    size_t off_qh = 0, off_w = 0, off_ktt = 0, off_p = 0, off_ut = 0, off_gam = 0;
+    size_t workspace_bytes = 0;
+};
+
+struct ChunkArgs {
+    const void *q = nullptr, *k = nullptr, *v = nullptr;
+    const float *alpha = nullptr, *beta = nullptr;
+    const float* initial_state = nullptr;
+    float* final_state = nullptr;
+    const int32_t* cu_seqlens = nullptr;
+    void* o = nullptr;
+    void* workspace = nullptr;
+    bool act_bf16 = false, out_bf16 = false;
+};
+
+kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen, int num_seqs,
+                           int chunk_size, bool act_bf16, ChunkPlan* plan);
+
+hipError_t launch_chunk_fwd(const ChunkPlan& plan, const ChunkArgs& args, hipStream_t stream);
+
+}  // namespace kda

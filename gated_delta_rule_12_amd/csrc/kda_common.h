@@ -1,0 +1,54 @@
+// Device-side helpers and launch declarations shared by the KDA kernels.
+// gfx950 (CDNA4) only: 64-wide wavefronts, MFMA matrix cores, 160 KiB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+// ---------------------------------------------------------------------------
+// Scalar conversions.  bf16 is carried as its 16 raw bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Activation element type: fp32 or bf16 (raw bits).
+template <bool BF16> struct Act;
+template <> struct Act<false> {
+    using T = float;
+    __device__ static __forceinline__ float load(const T* p, size_t i) { return p[i]; }
+};
+template <> struct Act<true> {
+    using T = uint16_t;
+    __device__ static __forceinline__ float load(const T* p, size_t i) { return bf16_to_f32(p[i]); }
+};
+
+template <bool BF16> __device__ __forceinline__ void store_out(void* o, size_t i, float x);
+template <> __device__ __forceinline__ void store_out<false>(void* o, size_t i, float x) {
+    static_cast<float*>(o)[i] = x;
+}
+template <> __device__ __forceinline__ void store_out<true>(void* o, size_t i, float x) {
+    static_cast<uint16_t*>(o)[i] = f32_to_bf16(x);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers (defined next to their kernels).
+// ---------------------------------------------------------------------------
+hipError_t launch_recurrent_step(const void* q, const void* k, const void* v,
+                                 const float* alpha, const float* beta, float* state,
+                                 void* o, int N, int H, int Dk, int Dv,
+                                 bool act_bf16, bool out_bf16, hipStream_t stream);
+
+}  // namespace kda

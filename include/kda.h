@@ -1,0 +1,156 @@
+/*
+ * kda.h -- C ABI of the KDA (gated delta-rule linear attention) library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer keeps a d_k x d_v memory S per (sequence, head) and, for every
+ * token t, applies
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * with a per-key-channel forget gate alpha_t in (0,1]^{d_k} and a scalar
+ * write strength beta_t.  (KDA update rule: "Hybrid Linear Attention
+ * Architectures: Breaking Through the Long-Context Engineering Bottleneck in
+ * LLMs", Core Module Design, Stage 3; "Linear Attention KDA Gating in a 3:1
+ * Hybrid Architecture: Principles and Implementation Guide", section 2,
+ * item 5: decay each key channel first, then overwrite along k.)  The rows
+ * of S are key channels; the write is beta k v^T and the read-out S^T q is
+ * taken after the token's own write (token i sees tokens j <= i: same page,
+ * section 3.2).  No query scaling is applied.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, owned by the caller, row-major
+ *    and contiguous, 16-byte aligned (beta: 4-byte aligned).  The library never allocates, never
+ *    frees and keeps no state between calls.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; nothing synchronises the host.
+ *    Calls on different streams with disjoint outputs may run concurrently.
+ *  - Argument errors (NULL pointer, bad size, misalignment, unsupported
+ *    dtype or head size, workspace too small) are detected on the host
+ *    before anything is launched; the call then returns the status and has
+ *    launched nothing.  A failed kernel launch returns KDA_ERROR_LAUNCH.
+ *    Faults inside a kernel surface at the caller's next synchronisation.
+ *  - Data VALUES are not validated.  Preconditions: alpha in (0, 1],
+ *    beta in [0, 1]; for 16-bit activations every |v| and every state entry
+ *    stays below 6.0e4 (half-precision range of the matrix-core operands);
+ *    within any 8 consecutive tokens of a 64-token chunk the decay
+ *    -sum(log alpha) of every channel stays below 10; cu_seqlens is
+ *    non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = T.
+ *  - Supported: d_k in {64, 128}, d_v in {64, 128}, chunk_size = 64.
+ *    Activations (q, k, v) are either all fp32 or all bf16; alpha, beta and
+ *    every state are fp32.  The output o is fp32, or bf16 when the
+ *    activations are bf16 (rounded once, to nearest-even, from the fp32
+ *    accumulator).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_SUCCESS = 0,
+    KDA_ERROR_INVALID_VALUE = 1,      /* NULL pointer, negative or inconsistent size, misalignment */
+    KDA_ERROR_NOT_SUPPORTED = 2,      /* head size, chunk size or dtype combination not built    */
+    KDA_ERROR_WORKSPACE_TOO_SMALL = 3,
+    KDA_ERROR_LAUNCH = 4              /* a kernel launch failed (hipGetLastError)                */
+} kda_status;
+
+typedef enum {
+    KDA_DTYPE_F32 = 0,
+    KDA_DTYPE_BF16 = 1
+} kda_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+KDA_API const char *kda_status_string(kda_status s);
+
+/*
+ * Workspace size, in bytes, that kda_chunk_fwd needs for this problem.
+ * Same arguments as kda_chunk_fwd (num_seqs is ignored when `varlen` is 0).
+ * Returns 0 for argument combinations kda_chunk_fwd would reject.
+ * The workspace holds the chunk table and the per-(chunk, head)
+ * intermediates; it must be 256-byte aligned and its contents need not be
+ * initialised.  One workspace must not be shared by calls that may overlap.
+ */
+KDA_API size_t kda_chunk_fwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv,
+                                     int varlen, int num_seqs, int chunk_size,
+                                     kda_dtype act_dtype);
+
+/*
+ * Chunkwise-parallel forward (prefill / training forward).
+ *
+ * Follows the chunked algorithm of "Linear Attention KDA Gating in a 3:1
+ * Hybrid Architecture", section 3 (inter-chunk state transition 3.1 and
+ * masked intra-chunk output 3.2) and the "Hardware-Aware Chunkwise
+ * Parallelism" section of "Hybrid Linear Attention Architectures...": the
+ * sequence is cut into chunks of `chunk_size` tokens; inside a chunk the
+ * work is dense matrix products, and only the d_k x d_v state passes from
+ * one chunk to the next.  The result equals the token-by-token recurrence
+ * above up to rounding.
+ *
+ * Layout (contiguous):
+ *   q, k       [B, T, H, Dk]   act_dtype
+ *   v          [B, T, H, Dv]   act_dtype
+ *   alpha      [B, T, H, Dk]   fp32, in (0, 1]
+ *   beta       [B, T, H]       fp32, in [0, 1]
+ *   o          [B, T, H, Dv]   out_dtype (written for every token)
+ *   initial_state [N, H, Dk, Dv] fp32, or NULL for zeros
+ *   final_state   [N, H, Dk, Dv] fp32, or NULL (not written); it may be the
+ *                 same pointer as initial_state (updated in place).
+ * Sequences:
+ *   cu_seqlens == NULL: N = B independent sequences of length T.
+ *   cu_seqlens != NULL: device int32 [num_seqs + 1] prefix offsets of
+ *                 num_seqs sequences packed along T; B must be 1 and
+ *                 N = num_seqs.  Zero-length sequences are allowed (their
+ *                 final state equals their initial state).  Chunks never
+ *                 cross a sequence boundary.
+ * T may be 0 (then only final_state := initial_state is written).
+ */
+KDA_API kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta,
+                         const float *initial_state, float *final_state,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         void *o,
+                         int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
+                         kda_dtype act_dtype, kda_dtype out_dtype,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
+ * One recurrent decode step: every one of N sequences consumes one token and
+ * its fp32 state is updated in place ("recurrent kernels for linear
+ * attention" of "Linear Attention + Sparse Attention: The Hybrid
+ * Architecture Trade-off for Large Models", section 6; the token-by-token
+ * mode of "Linear Attention KDA Gating...", section 3).  Each state is read
+ * once and written once.
+ *
+ * Layout (contiguous):
+ *   q, k   [N, H, Dk]  act_dtype      v [N, H, Dv] act_dtype
+ *   alpha  [N, H, Dk]  fp32           beta [N, H] fp32
+ *   state  [N, H, Dk, Dv] fp32, read and overwritten
+ *   o      [N, H, Dv]  out_dtype
+ * N may be 0 (nothing is launched).
+ */
+KDA_API kda_status kda_recurrent_step(const void *q, const void *k, const void *v,
+                              const float *alpha, const float *beta,
+                              float *state, void *o,
+                              int N, int H, int Dk, int Dv,
+                              kda_dtype act_dtype, kda_dtype out_dtype,
+                              void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

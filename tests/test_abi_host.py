@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every entry point declared in include/kda.h, and rejects bad arguments before
+launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_12_amd as kda
+from tests.conftest import ROOT
+
+HDR = os.path.join(ROOT, "include", "kda.h")
+FAKE = 0x100000          # 256-byte aligned, never dereferenced: every call below fails validation
+
+
+def declared_symbols():
+    src = open(HDR).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]*?\b(kda_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    assert declared_symbols() == sorted(kda.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, re.M))
+    for name in declared_symbols():
+        assert name in exported, name
+        assert hasattr(kda.lib(), name)
+
+
+def test_header_compiles_as_c():
+    src = f'#include "{HDR}"\nint main(void) {{ return (int)sizeof(kda_status); }}\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-"],
+                       input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    names = [kda.kda_status_string(i) for i in range(5)]
+    assert names == ["KDA_SUCCESS", "KDA_ERROR_INVALID_VALUE", "KDA_ERROR_NOT_SUPPORTED",
+                     "KDA_ERROR_WORKSPACE_TOO_SMALL", "KDA_ERROR_LAUNCH"]
+    assert kda.kda_status_string(99) == "KDA_ERROR_UNKNOWN"
+
+
+def test_workspace_size_plan():
+    f = kda.kda_chunk_fwd_workspace_bytes
+    n = f(2, 4096, 8, 128, 128, False, 0, 64, kda.KDA_DTYPE_BF16)
+    gh = 2 * 64 * 8
+    per = 64 * 128 * 2 * 3 + 64 * 64 * 2 + 128 * 64 * 4 + 128 * 4   # qh, w, ktt, p, ut, gam
+    assert gh * per <= n < gh * per + 64 * 1024
+    assert f(2, 4096, 8, 128, 128, False, 0, 64, kda.KDA_DTYPE_F32) > n
+    # packed: chunk capacity is ceil(T/64) + N
+    nv = f(1, 1000, 4, 64, 64, True, 10, 64, kda.KDA_DTYPE_BF16)
+    assert nv > f(1, 1000, 4, 64, 64, False, 0, 64, kda.KDA_DTYPE_BF16)
+    # unsupported combinations report 0
+    assert f(1, 256, 1, 96, 64, False, 0, 64, kda.KDA_DTYPE_BF16) == 0
+    assert f(1, 256, 1, 64, 64, False, 0, 32, kda.KDA_DTYPE_BF16) == 0
+    assert f(2, 256, 1, 64, 64, True, 3, 64, kda.KDA_DTYPE_BF16) == 0
+    assert f(1, 1 << 31, 1, 64, 64, False, 0, 64, kda.KDA_DTYPE_BF16) == 0
+
+
+def _chunk(**over):
+    L = kda.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, s0=None, sT=None, cu=None, N=0,
+             o=FAKE, B=1, T=128, H=2, Dk=64, Dv=64, C=64, act=kda.KDA_DTYPE_BF16,
+             out=kda.KDA_DTYPE_BF16, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return L.kda_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["sT"],
+                           a["cu"], a["N"], a["o"], a["B"], a["T"], a["H"], a["Dk"], a["Dv"],
+                           a["C"], a["act"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_chunk_fwd_argument_errors():
+    assert _chunk(q=None) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(o=None) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(k=FAKE + 8) == kda.KDA_ERROR_INVALID_VALUE          # misaligned
+    assert _chunk(beta=FAKE + 2) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(T=-1) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(H=0) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(Dk=96) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(Dv=32) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(C=128) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(act=7) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(act=kda.KDA_DTYPE_F32, out=kda.KDA_DTYPE_BF16) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(cu=FAKE, B=2, N=3) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(cu=FAKE, N=-1) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(ws=None) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(ws=FAKE + 16) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk(wsb=100) == kda.KDA_ERROR_WORKSPACE_TOO_SMALL
+    assert _chunk(B=1 << 20, T=1 << 12) == kda.KDA_ERROR_NOT_SUPPORTED   # > 2^31 token rows
+
+
+def test_chunk_fwd_nothing_to_do_launches_nothing():
+    # zero sequences: success without touching the device
+    assert _chunk(B=0, q=None, k=None, v=None, alpha=None, beta=None, o=None, ws=None) == 0
+    assert _chunk(cu=FAKE, N=0, T=0, ws=None) == 0
+
+
+def _step(**over):
+    L = kda.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, state=FAKE, o=FAKE, N=4, H=2,
+             Dk=128, Dv=128, act=kda.KDA_DTYPE_BF16, out=kda.KDA_DTYPE_F32, stream=None)
+    a.update(over)
+    return L.kda_recurrent_step(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["state"],
+                                a["o"], a["N"], a["H"], a["Dk"], a["Dv"], a["act"], a["out"],
+                                a["stream"])
+
+
+def test_recurrent_step_argument_errors():
+    assert _step(state=None) == kda.KDA_ERROR_INVALID_VALUE
+    assert _step(q=FAKE + 4) == kda.KDA_ERROR_INVALID_VALUE
+    assert _step(N=-1) == kda.KDA_ERROR_INVALID_VALUE
+    assert _step(Dk=32) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _step(act=kda.KDA_DTYPE_F32, out=kda.KDA_DTYPE_BF16) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _step(out=5) == kda.KDA_ERROR_INVALID_VALUE
+    assert _step(N=0) == kda.KDA_SUCCESS
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kda, "_lib", None)
+    monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        kda.lib()

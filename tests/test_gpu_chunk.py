@@ -1,0 +1,189 @@
+"""GPU parity of kda_chunk_fwd against the fp64 oracle (through the C ABI).
+
+Small shapes span several chunks and a ragged tail and are compared element
+by element; the full-size workloads run in the benchmark's launch
+configuration and are compared on sampled (sequence, head) pairs that the
+oracle recomputes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_12_amd as kda
+import oracle
+import synth
+from tests.helpers import check_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ODT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _cuda(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def gpu_fwd(inp, out="f32", final=True):
+    o, sT = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                              initial_state=inp["initial_state"], final_state=final,
+                              cu_seqlens=inp["cu_seqlens"], out_dtype=ODT[out])
+    torch.cuda.synchronize()
+    return o, sT
+
+
+def oracle_fwd(inp):
+    cu = inp["cu_seqlens"]
+    return oracle.kda_fwd(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(inp["alpha"]),
+                          to_np(inp["beta"]), initial_state=synth.to_f64(inp["initial_state"]),
+                          cu_seqlens=None if cu is None else cu.cpu().numpy().astype(np.int64))
+
+
+def check_pair(o, sT, o_ref, s_ref, act, out):
+    kind = "f32" if act == "f32" else "bf16"
+    r1 = check_close(o, o_ref, kind, stored_bf16=(out == "bf16"), what="o")
+    r2 = check_close(sT, s_ref, kind, what="final state")
+    print(f"  error/allowed: o {r1:.3f}  S_T {r2:.3f}", flush=True)
+
+
+def test_workload0_fp32():
+    w = synth.WORKLOADS[0]
+    print(f"[chunk {w.name}]", flush=True)
+    inp = _cuda(synth.workload_inputs(0))
+    o, sT = gpu_fwd(inp, "f32")
+    o_ref, s_ref = oracle_fwd(inp)
+    check_pair(o, sT, o_ref, s_ref, "f32", "f32")
+
+
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("act,out", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16")])
+@pytest.mark.parametrize("T", [1, 64, 200])
+def test_small_shapes(Dk, Dv, act, out, T):
+    print(f"[chunk small Dk={Dk} Dv={Dv} act={act} out={out} T={T}]", flush=True)
+    inp = _cuda(synth.chunk_inputs(2, T, 3, Dk, Dv, act, mu=-2.0, s0_std=0.1, seed=T + Dk + Dv))
+    o, sT = gpu_fwd(inp, out)
+    o_ref, s_ref = oracle_fwd(inp)
+    check_pair(o, sT, o_ref, s_ref, act, out)
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_varlen_small(act):
+    lens = [0, 1, 63, 64, 65, 130, 7, 256, 0]
+    print(f"[chunk varlen lens={lens} act={act}]", flush=True)
+    inp = _cuda(synth.chunk_inputs(1, 0, 2, 128, 128, act, mu=-2.0, s0_std=0.05, seed=7,
+                                   lengths=lens))
+    o, sT = gpu_fwd(inp, "f32")
+    o_ref, s_ref = oracle_fwd(inp)
+    check_pair(o, sT, o_ref, s_ref, act, "f32")
+    # empty sequences hand their initial state through unchanged
+    s0 = inp["initial_state"]
+    assert torch.equal(sT[0], s0[0]) and torch.equal(sT[8], s0[8])
+
+
+def test_no_initial_state_and_no_final_state():
+    print("[chunk zero S0, no S_T]", flush=True)
+    inp = _cuda(synth.chunk_inputs(1, 130, 2, 128, 128, "bf16", seed=1))
+    assert inp["initial_state"] is None
+    o, sT = gpu_fwd(inp, "f32", final=False)
+    assert sT is None
+    o_ref, _ = oracle_fwd(inp)
+    check_close(o, o_ref, "bf16", what="o")
+
+
+def test_zero_tokens_passes_state_through():
+    print("[chunk T=0]", flush=True)
+    inp = _cuda(synth.chunk_inputs(3, 0, 2, 64, 64, "bf16", s0_std=1.0, seed=2))
+    o, sT = gpu_fwd(inp, "bf16")
+    assert o.numel() == 0 and torch.equal(sT, inp["initial_state"])
+
+
+def test_final_state_in_place():
+    print("[chunk in-place state]", flush=True)
+    inp = _cuda(synth.chunk_inputs(2, 300, 2, 128, 128, "bf16", s0_std=0.05, seed=4))
+    o_ref, s_ref = oracle_fwd(inp)
+    st = inp["initial_state"].clone()
+    kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], initial_state=st,
+                      final_state=st, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_close(st, s_ref, "bf16", what="in-place final state")
+
+
+def test_special_case_readback_and_no_write():
+    """beta = 1 with q = k and alpha = 1 (DeltaNet read-back) returns v; beta = 0
+    with alpha = 1 returns S0^T q (the pages' reductions, on the GPU)."""
+    print("[chunk special cases]", flush=True)
+    inp = _cuda(synth.chunk_inputs(1, 192, 2, 128, 128, "f32", s0_std=0.3, seed=9))
+    one = torch.ones_like(inp["alpha"])
+    o, _ = kda.kda_chunk_fwd(inp["k"], inp["k"], inp["v"], one, torch.ones_like(inp["beta"]),
+                             initial_state=inp["initial_state"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.max(torch.abs(o - inp["v"])).item() < 1e-3
+    o, sT = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], one, torch.zeros_like(inp["beta"]),
+                              initial_state=inp["initial_state"], final_state=True)
+    torch.cuda.synchronize()
+    ref = torch.einsum("bthc,hcj->bthj", inp["q"].double(), inp["initial_state"][0].double())
+    assert torch.max(torch.abs(o.double() - ref)).item() < 1e-5
+    assert torch.equal(sT, inp["initial_state"])
+
+
+def test_deterministic_rerun():
+    print("[chunk determinism]", flush=True)
+    inp = _cuda(synth.chunk_inputs(2, 500, 4, 128, 128, "bf16", s0_std=0.02, seed=5))
+    o1, s1 = gpu_fwd(inp, "bf16")
+    o2, s2 = gpu_fwd(inp, "bf16")
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_workload1_full(out):
+    w = synth.WORKLOADS[1]
+    print(f"[chunk {w.name} out={out}]", flush=True)
+    inp = synth.workload_inputs(1, device=DEV)
+    o, sT = gpu_fwd(inp, out)
+    o_ref, s_ref = oracle_fwd(inp)
+    check_pair(o, sT, o_ref, s_ref, "bf16", out)
+
+
+def _sampled(inp, o, sT, pairs, seq_bounds):
+    """Compare o / S_T of the listed (sequence, head) pairs with the oracle run
+    on exactly those pairs' inputs."""
+    for n, h in pairs:
+        t0, t1 = seq_bounds(n)
+        b = 0 if inp["cu_seqlens"] is not None else n
+        sl = (slice(b, b + 1), slice(t0, t1), slice(h, h + 1))
+        s0 = inp["initial_state"]
+        o_ref, s_ref = oracle.kda_fwd(
+            to_np(inp["q"][sl]), to_np(inp["k"][sl]), to_np(inp["v"][sl]), to_np(inp["alpha"][sl]),
+            to_np(inp["beta"][sl]),
+            initial_state=None if s0 is None else to_np(s0[n:n + 1, h:h + 1]))
+        yield (n, h), o[sl], sT[n:n + 1, h:h + 1], o_ref, s_ref
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_workload2_full_sampled(out):
+    """B=1, H=32, T=65536, d=128, slow decay, random S0: the chunk-forward
+    benchmark launch.  Checked on 3 full heads (all 65536 tokens each)."""
+    w = synth.WORKLOADS[2]
+    print(f"[chunk {w.name} out={out}]", flush=True)
+    inp = synth.workload_inputs(2, device=DEV)
+    o, sT = gpu_fwd(inp, out)
+    for (n, h), og, sg, o_ref, s_ref in _sampled(inp, o, sT, [(0, 0), (0, 13), (0, 31)],
+                                                 lambda n: (0, w.T)):
+        print(f"  head {h}", flush=True)
+        check_pair(og, sg, o_ref, s_ref, "bf16", out)
+
+
+def test_workload4_varlen_full_sampled():
+    """64 packed sequences, lengths ~U[512, 32768], H=16, d=128, per-sequence S0;
+    checked on the longest, the shortest and two other sequences, 2 heads each."""
+    w = synth.WORKLOADS[4]
+    print(f"[chunk {w.name}]", flush=True)
+    inp = synth.workload_inputs(4, device=DEV)
+    cu = inp["cu_seqlens"].cpu().numpy()
+    lens = np.diff(cu)
+    pick = [int(np.argmax(lens)), int(np.argmin(lens)), 17, 40]
+    o, sT = gpu_fwd(inp, "bf16")
+    pairs = [(n, h) for n in pick for h in (0, 11)]
+    for (n, h), og, sg, o_ref, s_ref in _sampled(inp, o, sT, pairs,
+                                                 lambda n: (int(cu[n]), int(cu[n + 1]))):
+        print(f"  seq {n} (len {lens[n]}) head {h}", flush=True)
+        check_pair(og, sg, o_ref, s_ref, "bf16", "bf16")
