@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""KDA benchmark on one MI355X.
+
+One step is one pass of the whole hot path:
+  * kda_chunk_fwd over B=1, H=32, T=65536, d_k=d_v=128 (bf16 q/k/v/o, fp32
+    gates, random fp32 initial state, final state returned), chunk 64; and
+  * one kda_recurrent_step over 256 sequences x 32 heads, d=128, fp32 state
+    (512 MiB) updated in place; step i consumes the i-th of 100 pre-generated
+    token batches (the decode workload is 100 such steps).
+All inputs are seeded synthetic data already resident in HBM.  HIP events on
+the stream the kernels run on time each part; `value` is the chunk forward's
+token-head throughput (B*H*T per second of kda_chunk_fwd), and the decode
+step is reported as achieved HBM GB/s.
+
+Prints ONE JSON line.  Flags:
+  --gpus N --steps K --warmup W       (N must be 1: this build is one GPU)
+  --no-cpu-baseline                   skip the oracle timing
+  --only fwd|decode                   time one part only (profiler runs)
+  --copy-calibration                  run a plain 1 GiB device copy (used to
+                                      scale rocprofv3 FETCH_SIZE/WRITE_SIZE)
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix cores, vendor figure
+
+# Algorithmic ledger per token-head of the chunk forward (d_k = d_v = 128):
+# q, k, v, o in bf16 (4 x 256 B) + alpha fp32 (512 B) + beta fp32 (4 B).
+FWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 4 * 128 + 4
+# Useful flops per token-head at C = 64, d = 128: three d x d contractions
+# (6 d^2) + C-dependent products (A, T.X, QK^T, P.U') + the triangular solve.
+FWD_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * 128 + 64 * 256 + 64 * 128 + 64 * 128 + 64 * 64 // 3
+
+
+def decode_bytes_per_step(N, H, Dk, Dv):
+    state = 2 * N * H * Dk * Dv * 4                      # read + write, fp32
+    io = N * H * (2 * Dk * 2 + Dv * 2 + Dv * 2 + Dk * 4 + 4)   # q,k,v,o bf16, alpha, beta
+    return state + io
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def copy_calibration(torch):
+    n = 1 << 28                                   # 2^28 fp32 = 1 GiB
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                      "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["fwd", "decode"], default=None)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); a multi-GPU run is not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_12_amd as kda
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    kda.lib()                       # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    K, W = args.steps, args.warmup
+    dev = "cuda"
+    wf = synth.WORKLOADS[2]
+    wd = synth.WORKLOADS[3]
+    do_fwd = args.only in (None, "fwd")
+    do_dec = args.only in (None, "decode")
+
+    # ---- inputs, outputs and workspace: all allocated before timing ----------
+    if do_fwd:
+        fi = synth.workload_inputs(2, device=dev)
+        B, T, H, Dk, Dv = wf.B, wf.T, wf.H, wf.Dk, wf.Dv
+        o = torch.empty((B, T, H, Dv), dtype=torch.bfloat16, device=dev)
+        sT = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+        ws_bytes = kda.kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, False, 0, 64, torch.bfloat16)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+        def fwd():
+            kda.kda_chunk_fwd(fi["q"], fi["k"], fi["v"], fi["alpha"], fi["beta"],
+                              initial_state=fi["initial_state"], final_state=sT, o=o,
+                              out_dtype=torch.bfloat16, workspace=ws)
+    if do_dec:
+        di = synth.workload_inputs(3, device=dev)
+        state = di["state"].clone()
+        od = torch.empty((wd.B, wd.H, wd.Dv), dtype=torch.bfloat16, device=dev)
+
+        def dec(i):
+            s = i % wd.steps
+            kda.kda_recurrent_step(di["q"][s], di["k"][s], di["v"][s], di["alpha"][s],
+                                   di["beta"][s], state, o=od, out_dtype=torch.bfloat16)
+
+    # ---- warmup and timed loop ------------------------------------------------
+    for i in range(W):
+        if do_fwd:
+            fwd()
+        if do_dec:
+            dec(i)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        if do_fwd:
+            fwd()
+        ev[i][1].record()
+        if do_dec:
+            dec(W + i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) if do_fwd else None
+    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if do_dec else None
+
+    out = {"metric": "KDA fwd tokens/s (B*H*T/s) at d=128,T=64K; decode-step HBM GB/s",
+           "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16xf32", "data": "synthetic"}
+    cfg = {"workload": "", "chunk": 64}
+    if do_fwd:
+        units = wf.B * wf.H * wf.T
+        fwd_s = fwd_ms / 1e3
+        byts = FWD_BYTES_PER_TOKEN_HEAD * units + 2 * wf.B * wf.H * wf.Dk * wf.Dv * 4
+        achieved = byts / fwd_s / 1e9
+        out.update({"value": round(units / fwd_s, 1), "unit": "token-heads/s",
+                    "fwd_ms": round(fwd_ms, 4)})
+        out["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                           "traffic": None, "kernel": "kda_chunk_fwd (plan+prep+state launches)",
+                           "algorithmic_bytes_per_launch": byts}
+        tflops = FWD_FLOPS_PER_TOKEN_HEAD * units / fwd_s / 1e12
+        out["mfma"] = {"achieved_useful": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4)}
+        cfg["workload"] = wf.name
+        cfg.update({"B": wf.B, "H": wf.H, "T": wf.T, "d_k": wf.Dk, "d_v": wf.Dv})
+    else:
+        out.update({"value": None, "unit": "token-heads/s"})
+    if do_dec:
+        dbytes = decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv)
+        gbps = dbytes / (dec_ms / 1e3) / 1e9
+        out["decode"] = {"value": round(gbps, 1), "unit": "GB/s", "us_per_step": round(dec_ms * 1e3, 2),
+                         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                      "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                                      "traffic": None, "kernel": "decode_kernel",
+                                      "algorithmic_bytes_per_launch": dbytes}}
+        cfg["decode_workload"] = wd.name
+        if not do_fwd:
+            cfg["workload"] = wd.name
+
+    out["config"] = cfg
+
+    # ---- CPU baseline: the fp64 oracle on a bounded sample ---------------------
+    if not args.no_cpu_baseline and do_fwd:
+        import oracle
+        S = min(args.cpu_sample_tokens, wf.T)
+        sl = (slice(0, 1), slice(0, S))
+        f64 = lambda x: x[sl].to("cpu").to(torch.float64).numpy()
+        q, k, v, a, b = (f64(fi[key]) for key in ("q", "k", "v", "alpha", "beta"))
+        s0 = fi["initial_state"].cpu().double().numpy()
+        c0 = time.perf_counter()
+        _, _, used = oracle.kda_fwd(q, k, v, a, b, initial_state=s0, return_threads=True)
+        c1 = time.perf_counter()
+        base = {"value": round(wf.H * S / (c1 - c0), 1), "unit": "token-heads/s", "cores": used,
+                "kind": "oracle",
+                "sample": f"first {S} of {wf.T} tokens, all {wf.H} heads of the forward workload "
+                          f"(fp64 token-by-token recurrence, {c1 - c0:.2f} s)",
+                "cpu": cpu_model()}
+        if do_dec:
+            s = W % wd.steps
+            dq, dk, dv, da, db = (di[key][s].cpu().double().numpy()
+                                  for key in ("q", "k", "v", "alpha", "beta"))
+            dst = di["state"].cpu().double().numpy()
+            c0 = time.perf_counter()
+            _, _, dused = oracle.kda_step(dq, dk, dv, da, db, dst, return_threads=True)
+            c1 = time.perf_counter()
+            base["decode"] = {"value": round(decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv)
+                                             / (c1 - c0) / 1e9, 3),
+                              "unit": "GB/s (fp32 byte ledger)", "cores": dused,
+                              "sample": f"one full decode step ({c1 - c0:.2f} s)"}
+        if np.isfinite(base["value"]) and out.get("value"):
+            base["gpu_over_cpu"] = round(out["value"] / base["value"], 1)
+        out["cpu_baseline"] = base
+
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

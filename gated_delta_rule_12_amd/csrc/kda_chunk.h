@@ -18,8 +18,9 @@ constexpr int kChunk = 64;      // tokens per chunk
 //   first      int32[N+1]          first chunk of each sequence (prefix sums)
 //   order      int32[N]            sequences by decreasing length (ties: index)
 //   table      int32[Gmax][4]      per chunk: sequence, first token row, length
-//   per (chunk g, head h), index g*H + h, element type E = fp16 (bf16
-//   activations) or fp32 (fp32 activations):
+//   records    one per (head h, chunk g), at index h*Gmax + g, rec_bytes
+//              each, so the chunks of one head follow each other.  With
+//              E = fp16 (bf16 activations) or fp32 (fp32 activations):
 //     qh       E[64][Dk]           Gamma (.) Q            (token-major)
 //     w        E[64][Dk]           W = T Diag(beta) (Gamma (.) K)
 //     ktt      E[Dk][64]           ((gamma/Gamma) (.) K)^T (channel-major)
@@ -34,7 +35,7 @@ struct ChunkPlan {
     int64_t gmax = 0;             // chunk-table capacity
     size_t eb = 4;                // bytes per intermediate element
     size_t off_ctrl = 0, off_first = 0, off_order = 0, off_table = 0;
-    size_t off_qh = 0, off_w = 0, off_ktt = 0, off_p = 0, off_ut = 0, off_gam = 0;
+    size_t off_rec = 0, rec_bytes = 0;
     size_t workspace_bytes = 0;
 };
 

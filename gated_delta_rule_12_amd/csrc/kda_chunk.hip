@@ -66,6 +66,15 @@ template <> struct Mx<true> {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ V load8(const E* p) { return *reinterpret_cast<const V*>(p); }
+    // elements 0..3 from p0, 4..7 from p1 (each 8-byte aligned)
+    static __device__ __forceinline__ V load4x2(const E* p0, const E* p1) {
+        const h4 a = *reinterpret_cast<const h4*>(p0);
+        const h4 b = *reinterpret_cast<const h4*>(p1);
+        V v;
+        v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+        v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+        return v;
+    }
     static __device__ __forceinline__ E cvt(float x) { return static_cast<E>(x); }
     static __device__ __forceinline__ float tof(E x) { return static_cast<float>(x); }
     static __device__ __forceinline__ void store4(E* p, f4 x) {
@@ -91,6 +100,14 @@ template <> struct Mx<false> {
     static __device__ __forceinline__ V load8(const E* p) {
         const f4 lo = *reinterpret_cast<const f4*>(p);
         const f4 hi = *reinterpret_cast<const f4*>(p + 4);
+        V v;
+        v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+        v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+        return v;
+    }
+    static __device__ __forceinline__ V load4x2(const E* p0, const E* p1) {
+        const f4 lo = *reinterpret_cast<const f4*>(p0);
+        const f4 hi = *reinterpret_cast<const f4*>(p1);
         V v;
         v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
         v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
@@ -124,15 +141,29 @@ template <> struct Load8<false> {
     }
 };
 
+// Operand fragments in the workspace.  Every matrix-core operand that the
+// state kernel loads is stored "fragment-major": fragment f of a matrix is
+// the 16 rows x 32 reduction indices one MFMA step consumes, laid out as
+// 64 lanes x 8 elements, so one wavefront load moves 1 KiB of contiguous
+// bytes.  Within a fragment, lane (m, j) (m = lane % 16, j = lane / 16)
+// holds row m at reduction indices frag_k(j, e), e = 0..7: two runs of four,
+// 4j..4j+3 and 16+4j..16+4j+3.  Any bijection onto the 32 indices gives the
+// same product as long as both operands of an MFMA use it; this one lets a
+// 16x16 accumulator tile pair (rows 4j..4j+3 of each tile in lane (m, j))
+// be written as a fragment without moving data between lanes.
+__device__ __forceinline__ int frag_k(int j, int e) { return e < 4 ? 4 * j + e : 12 + 4 * j + e; }
+
+__device__ __forceinline__ size_t frag_off(int f, int lane) { return (static_cast<size_t>(f) * 64 + lane) * 8; }
+
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
 // ---------------------------------------------------------------------------
 // plan_kernel: chunk table, per-sequence first chunk, longest-first order.
-// One workgroup of 1024 threads.
+// One workgroup of 1024 threads; every loop is spread over the threads.
 // ---------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
-constexpr int kRankSortMax = 2048;   // above this, sequences keep their index order
+constexpr int kRankSortMax = 4096;   // above this, sequences keep their index order
 
 __device__ __forceinline__ int seq_len(const int32_t* cu, int n, int64_t T) {
     return cu ? cu[n + 1] - cu[n] : static_cast<int>(T);
@@ -145,16 +176,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
                                                             int32_t* __restrict__ order,
                                                             int4* __restrict__ table) {
     __shared__ int s_scan[kPlanThreads];
+    __shared__ int s_len[kRankSortMax];
     __shared__ int s_carry;
     const int tid = threadIdx.x;
     if (tid == 0) s_carry = 0;
     __syncthreads();
+    // first[n] = number of chunks of sequences 0..n-1 (block-wise inclusive scan)
     for (int base = 0; base < N; base += kPlanThreads) {
         const int n = base + tid;
         int cnt = 0;
         if (n < N) {
             const int len = seq_len(cu, n, T);
             cnt = len > 0 ? (len + C - 1) / C : 0;
+            if (N <= kRankSortMax) s_len[n] = len;
         }
         s_scan[tid] = cnt;
         __syncthreads();
@@ -164,31 +198,43 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
             s_scan[tid] += add;
             __syncthreads();
         }
-        if (n < N) first[n] = s_carry + s_scan[tid] - cnt;
+        if (n < N) {
+            const int f = s_carry + s_scan[tid] - cnt;
+            first[n] = f < gmax ? f : static_cast<int>(gmax);
+        }
         __syncthreads();
         if (tid == kPlanThreads - 1) s_carry += s_scan[tid];
         __syncthreads();
     }
+    // a malformed cu_seqlens cannot push work past the table's capacity
+    const int total = s_carry < gmax ? s_carry : static_cast<int>(gmax);
     if (tid == 0) {
-        // a malformed cu_seqlens cannot push work past the table's capacity
-        const int total = s_carry < gmax ? s_carry : static_cast<int>(gmax);
         first[N] = total;
         ctrl[0] = total;
     }
     __syncthreads();
-    for (int n = tid; n < N; n += kPlanThreads) {
+    // one table entry per chunk: its sequence is the last n with first[n] <= g
+    for (int g = tid; g < total; g += kPlanThreads) {
+        int lo = 0, hi = N - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (first[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        const int n = lo;
+        const int i = g - first[n];
         const int len = seq_len(cu, n, T);
         const int start = cu ? cu[n] : static_cast<int>(static_cast<int64_t>(n) * T);
-        const int f = first[n];
-        for (int i = 0; i * C < len && f + i < gmax; ++i) {
-            const int l = len - i * C;
-            table[f + i] = make_int4(n, start + i * C, l < C ? l : C, 0);
-        }
+        const int l = len - i * C;
+        table[g] = make_int4(n, start + i * C, l < C ? l : C, 0);
+    }
+    // longest sequences first (ties by index), so long chains start early
+    for (int n = tid; n < N; n += kPlanThreads) {
         int rank = n;
         if (N <= kRankSortMax) {
+            const int len = s_len[n];
             rank = 0;
             for (int m = 0; m < N; ++m) {
-                const int lm = seq_len(cu, m, T);
+                const int lm = s_len[m];
                 rank += (lm > len) || (lm == len && m < n);
             }
         }
@@ -198,7 +244,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------
 // prep_kernel: everything of one (chunk, head) that does not depend on the
-// state entering the chunk.
+// state entering the chunk.  All global loads are issued first; the phases
+// then work out of LDS.
 // ---------------------------------------------------------------------------
 struct PrepParams {
     const void* q;
@@ -208,23 +255,33 @@ struct PrepParams {
     const float* beta;
     const int32_t* ctrl;
     const int4* table;
-    void* qh;
-    void* w;
-    void* ktt;
-    void* p;
-    float* ut;
-    float* gam;
+    unsigned char* rec;
+    size_t rec_bytes;
+    int64_t gmax;
     int H;
 };
 
 template <int a, int b> struct CMax { static constexpr int value = a > b ? a : b; };
+
+// Byte offsets inside one (head, chunk) record of the workspace.
+template <int DK, int DV, bool F16>
+struct Rec {
+    using E = typename Mx<F16>::E;
+    static constexpr size_t QH = 0;
+    static constexpr size_t W = QH + sizeof(E) * C * DK;
+    static constexpr size_t KTT = W + sizeof(E) * C * DK;
+    static constexpr size_t P = KTT + sizeof(E) * DK * C;
+    static constexpr size_t UT = P + sizeof(E) * C * C;
+    static constexpr size_t GAM = UT + 4 * DV * C;
+    static constexpr size_t END = GAM + 4 * DK;
+};
 
 template <int DK, int DV, bool F16>
 struct PrepLds {
     using A = typename Act<F16>::T;   // raw activation element
     using E = typename Mx<F16>::E;    // matrix-core operand element
     static constexpr int BP = DK + 4;        // fp32 row stride of b (log2 decay)
-    static constexpr int KP = DK + 8;        // row stride of k / K-hat
+    static constexpr int KP = DK + 8;        // row stride of k / K-hat and of q
     static constexpr int VP = DV + 8;        // row stride of v
     static constexpr int AP = C + 1;         // fp32 row stride of A
     static constexpr int TP = C + 4;         // fp32 row stride of T
@@ -234,8 +291,9 @@ struct PrepLds {
     static constexpr int R1 = CMax<C * BP * 4, C * TP * 4 + C * VP * (int)sizeof(A)>::value;
     // region 2: raw k, later K-hat in place
     static constexpr int R2 = C * KP * kElem;
-    // region 3: A (fp32), later T Diag(beta)
-    static constexpr int R3 = CMax<C * AP * 4, C * TPP * (int)sizeof(E)>::value;
+    // region 3: raw q, later A (fp32), later T Diag(beta)
+    static constexpr int R3 =
+        CMax<C * KP * (int)sizeof(A), CMax<C * AP * 4, C * TPP * (int)sizeof(E)>::value>::value;
     static constexpr int PARTS = 256 / DK;
     static constexpr int R4 = (C + PARTS * DK) * 4;   // beta, cumsum part totals
     static constexpr int bytes = R1 + R2 + R3 + R4;
@@ -249,6 +307,13 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     using E = typename M::E;
     using V = typename M::V;
     constexpr int BP = L::BP, KP = L::KP, VP = L::VP, AP = L::AP, TP = L::TP, TPP = L::TPP;
+    constexpr int PARTS = L::PARTS;
+    constexpr int RP = C / PARTS;                          // cumsum rows per thread
+    constexpr int EL16 = 16 / (int)sizeof(A);              // activations per 16 bytes
+    constexpr int KROW16 = DK / EL16;                      // 16-byte pieces per k/q row
+    constexpr int VROW16 = DV / EL16;
+    constexpr int NK = C * KROW16 / 256;                   // pieces per thread
+    constexpr int NV = C * VROW16 / 256;
 
     const int H = P.H;
     const int g = blockIdx.x / H;
@@ -257,7 +322,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     const int4 ent = P.table[g];
     const int t0 = ent.y;
     const int len = ent.z;
-    const size_t gh = static_cast<size_t>(g) * H + h;
+    using R = Rec<DK, DV, F16>;
+    unsigned char* rec = P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes;
 
     extern __shared__ __align__(16) unsigned char lds[];
     float* s_b = reinterpret_cast<float*>(lds);
@@ -265,7 +331,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     A* s_v = reinterpret_cast<A*>(lds + C * TP * 4);                  // after b is dead
     A* s_kraw = reinterpret_cast<A*>(lds + L::R1);
     E* s_khat = reinterpret_cast<E*>(lds + L::R1);                    // K-hat, in place
-    float* s_A = reinterpret_cast<float*>(lds + L::R1 + L::R2);
+    A* s_q = reinterpret_cast<A*>(lds + L::R1 + L::R2);
+    float* s_A = reinterpret_cast<float*>(lds + L::R1 + L::R2);       // after q is dead
     E* s_Tp = reinterpret_cast<E*>(lds + L::R1 + L::R2);              // after A is dead
     float* s_beta = reinterpret_cast<float*>(lds + L::R1 + L::R2 + L::R3);
     float* s_part = s_beta + C;
@@ -282,39 +349,61 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     auto row_k = [&](int r) { return (static_cast<size_t>(t0 + r) * H + h) * DK; };
     auto row_v = [&](int r) { return (static_cast<size_t>(t0 + r) * H + h) * DV; };
 
-    // ---- (a) b = cumsum(log2 alpha) along the chunk, per key channel --------
+    // ---- (0) every global load of the chunk, up front ------------------------
+    const int c_own = tid % DK;                 // cumsum: channel and row part
+    const int part = tid / DK;
+    float al[RP];
+#pragma unroll
+    for (int i = 0; i < RP; ++i) {
+        const int r = part * RP + i;
+        al[i] = r < len ? P.alpha[row_k(r) + c_own] : 1.f;
+    }
+    uint4 kreg[NK], qreg[NK], vreg[NV];
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int id = tid + 256 * j;
+        const int r = id / KROW16;
+        const int cc = (id - r * KROW16) * EL16;
+        kreg[j] = make_uint4(0, 0, 0, 0);
+        qreg[j] = make_uint4(0, 0, 0, 0);
+        if (r < len) {
+            kreg[j] = *reinterpret_cast<const uint4*>(k + row_k(r) + cc);
+            qreg[j] = *reinterpret_cast<const uint4*>(q + row_k(r) + cc);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int id = tid + 256 * j;
+        const int r = id / VROW16;
+        const int cc = (id - r * VROW16) * EL16;
+        vreg[j] = make_uint4(0, 0, 0, 0);
+        if (r < len) vreg[j] = *reinterpret_cast<const uint4*>(v + row_v(r) + cc);
+    }
+    const float bet = (tid < C && tid < len) ? P.beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
+
+    // ---- (a) k, q to LDS; b = cumsum(log2 alpha) per key channel -------------
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+        const int id = tid + 256 * j;
+        const int r = id / KROW16;
+        const int cc = (id - r * KROW16) * EL16;
+        *reinterpret_cast<uint4*>(s_kraw + r * KP + cc) = kreg[j];
+        *reinterpret_cast<uint4*>(s_q + r * KP + cc) = qreg[j];
+    }
+    if (tid < C) s_beta[tid] = bet;
     {
-        constexpr int PARTS = L::PARTS;
-        constexpr int RP = C / PARTS;
-        const int c = tid % DK;
-        const int part = tid / DK;
         float run = 0.f;
-#pragma unroll 8
+#pragma unroll
         for (int i = 0; i < RP; ++i) {
-            const int r = part * RP + i;
-            const float a = r < len ? P.alpha[row_k(r) + c] : 1.f;
-            run += flog2(a);
-            s_b[r * BP + c] = run;
+            run += flog2(al[i]);
+            al[i] = run;
         }
-        s_part[part * DK + c] = run;
-        // raw k rows, 16 bytes per access; padded rows are zero
-        constexpr int PER_ROW = DK * (int)sizeof(A) / 16;
-        constexpr int EL16 = 16 / (int)sizeof(A);
-        for (int id = tid; id < C * PER_ROW; id += 256) {
-            const int r = id / PER_ROW;
-            const int cc = (id - r * PER_ROW) * EL16;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (r < len) val = *reinterpret_cast<const uint4*>(k + row_k(r) + cc);
-            *reinterpret_cast<uint4*>(s_kraw + r * KP + cc) = val;
-        }
-        if (tid < C) s_beta[tid] = tid < len ? P.beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
+        s_part[part * DK + c_own] = run;
         __syncthreads();
         float off = 0.f;
-        for (int pp = 0; pp < part; ++pp) off += s_part[pp * DK + c];
-        if (part > 0) {
-#pragma unroll 8
-            for (int i = 0; i < RP; ++i) s_b[(part * RP + i) * BP + c] += off;
-        }
+        for (int pp = 0; pp < part; ++pp) off += s_part[pp * DK + c_own];
+#pragma unroll
+        for (int i = 0; i < RP; ++i) s_b[(part * RP + i) * BP + c_own] = al[i] + off;
         __syncthreads();
     }
 
@@ -322,35 +411,43 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
         if constexpr (F16) return bf16_to_f32(s_kraw[r * KP + c]);
         else return s_kraw[r * KP + c];
     };
+    auto qraw = [&](int r, int c) -> float {
+        if constexpr (F16) return bf16_to_f32(s_q[r * KP + c]);
+        else return s_q[r * KP + c];
+    };
 
-    // ---- (b) gamma, Gamma.Q (token-major), ((gamma/Gamma).K)^T (channel-major)
+    // ---- (b) gamma, Gamma.Q and ((gamma/Gamma).K)^T in fragment order --------
     {
-        E* __restrict__ qh = static_cast<E*>(P.qh) + gh * (C * DK);
-        E* __restrict__ ktt = static_cast<E*>(P.ktt) + gh * (DK * C);
-        if (tid < DK) P.gam[gh * DK + tid] = fexp2(s_b[(C - 1) * BP + tid]);
-        constexpr int Q8 = DK / 8;
-        for (int id = tid; id < C * Q8; id += 256) {
-            const int r = id / Q8;
-            const int c0 = (id - r * Q8) * 8;
+        E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
+        E* __restrict__ ktt = reinterpret_cast<E*>(rec + R::KTT);
+        if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = fexp2(s_b[(C - 1) * BP + tid]);
+        constexpr int KS = DK / 32;
+        // Gamma.Q: fragment f = (token tile) * KS + (channel step)
+        for (int id = tid; id < C * KS * 4; id += 256) {
+            const int m = id & 15, j = (id >> 4) & 3, f = id >> 6;
+            const int rt = f / KS, ks = f - rt * KS;
+            const int r = 16 * rt + m;
             float qv[8];
-            if (r < len) {
-                Load8<F16>::f(q + row_k(r) + c0, qv);
-            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = 0.f;
+            for (int e = 0; e < 8; ++e) {
+                const int c = 32 * ks + frag_k(j, e);
+                qv[e] = qraw(r, c) * fexp2(s_b[r * BP + c]);
             }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] *= fexp2(s_b[r * BP + c0 + e]);
-            M::store8(qh + r * DK + c0, qv);
+            M::store8(qh + frag_off(f, id & 63), qv);
         }
-        for (int id = tid; id < DK * (C / 8); id += 256) {
-            const int c = id % DK;
-            const int r0 = (id / DK) * 8;
+        // ((gamma/Gamma).K)^T: fragment f = (channel tile) * 2 + (token step)
+        for (int id = tid; id < DK * 2 * 4; id += 256) {
+            const int m = id & 15, j = (id >> 4) & 3, f = id >> 6;
+            const int ct = f >> 1, ts = f & 1;
+            const int c = 16 * ct + m;
             const float bl = s_b[(C - 1) * BP + c];
             float kv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kv[e] = kraw(r0 + e, c) * fexp2(bl - s_b[(r0 + e) * BP + c]);
-            M::store8(ktt + c * C + r0, kv);
+            for (int e = 0; e < 8; ++e) {
+                const int t = 32 * ts + frag_k(j, e);
+                kv[e] = kraw(t, c) * fexp2(bl - s_b[t * BP + c]);
+            }
+            M::store8(ktt + frag_off(f, id & 63), kv);
         }
     }
 
@@ -359,49 +456,59 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
         const int I = wave;
         const int rr = 16 * I + lm;                 // this lane's row (A operand)
         const int refr = 16 * I + 7;                // reference token of block I
-        E* __restrict__ pout = static_cast<E*>(P.p) + gh * (C * C);
+        E* __restrict__ pout = reinterpret_cast<E*>(rec + R::P);
         constexpr int KS = DK / 32;
         V kr[KS], qr[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int c0 = 32 * ks + 8 * lg;
-            float qv[8];
-            if (rr < len) {
-                Load8<F16>::f(q + row_k(rr) + c0, qv);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qv[e] = 0.f;
-            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float f = fexp2(s_b[rr * BP + c0 + e] - s_b[refr * BP + c0 + e]);
                 kr[ks][e] = M::cvt(kraw(rr, c0 + e) * f);
-                qr[ks][e] = M::cvt(qv[e] * f);
+                qr[ks][e] = M::cvt(qraw(rr, c0 + e) * f);
             }
         }
-        for (int J = 0; J <= I; ++J) {
-            const int s = 16 * J + lm;              // this lane's column token (B operand)
-            f4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+        __syncthreads();                            // q is dead; its region takes A
+        // A in the accumulator layout (rows of A) for the solve; P as P^T tiles
+        // so that its fragments can be stored straight from the accumulators.
+        f4 accP[4];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c0 = 32 * ks + 8 * lg;
-                V kc;
+        for (int J = 0; J < 4; ++J) {
+            accP[J] = f4{0.f, 0.f, 0.f, 0.f};
+            if (J <= I) {
+                const int s = 16 * J + lm;          // this lane's column token
+                f4 accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    kc[e] = M::cvt(kraw(s, c0 + e) * fexp2(s_b[refr * BP + c0 + e] - s_b[s * BP + c0 + e]));
-                accA = M::mma(kr[ks], kc, accA);
-                accP = M::mma(qr[ks], kc, accP);
-            }
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int c0 = 32 * ks + 8 * lg;
+                    V kc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * I + 4 * lg + i;
-                s_A[r * AP + s] = s < r ? s_beta[r] * accA[i] : 0.f;
-                pout[r * C + s] = M::cvt(s <= r ? accP[i] : 0.f);
+                    for (int e = 0; e < 8; ++e)
+                        kc[e] = M::cvt(kraw(s, c0 + e) *
+                                       fexp2(s_b[refr * BP + c0 + e] - s_b[s * BP + c0 + e]));
+                    accA = M::mma(kr[ks], kc, accA);
+                    accP[J] = M::mma(kc, qr[ks], accP[J]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * I + 4 * lg + i;
+                    s_A[r * AP + s] = s < r ? s_beta[r] * accA[i] : 0.f;
+                }
             }
         }
-        for (int J = I + 1; J < 4; ++J) {
+        // lane (lm, lg) of P^T tile J holds P[16I+lm][16J+4lg+i]
+        const int r = 16 * I + lm;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) pout[(16 * I + 4 * lg + i) * C + 16 * J + lm] = M::cvt(0.f);
+        for (int ks = 0; ks < 2; ++ks) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s0 = 32 * ks + 4 * lg + e, s1 = s0 + 16;
+                pv[e] = s0 <= r ? accP[2 * ks][e] : 0.f;
+                pv[4 + e] = s1 <= r ? accP[2 * ks + 1][e] : 0.f;
+            }
+            M::store8(pout + frag_off(2 * I + ks, lane), pv);
         }
     }
     __syncthreads();
@@ -418,14 +525,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
 
     // ---- (e) v into LDS; T = (I + A)^-1 --------------------------------------
     {
-        constexpr int PER_ROW = DV * (int)sizeof(A) / 16;
-        constexpr int EL16 = 16 / (int)sizeof(A);
-        for (int id = tid; id < C * PER_ROW; id += 256) {
-            const int r = id / PER_ROW;
-            const int cc = (id - r * PER_ROW) * EL16;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (r < len) val = *reinterpret_cast<const uint4*>(v + row_v(r) + cc);
-            *reinterpret_cast<uint4*>(s_v + r * VP + cc) = val;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int id = tid + 256 * j;
+            const int r = id / VROW16;
+            const int cc = (id - r * VROW16) * EL16;
+            *reinterpret_cast<uint4*>(s_v + r * VP + cc) = vreg[j];
         }
         // diagonal 16x16 blocks by forward substitution; lane j owns column j
         if (lane < 16) {
@@ -478,26 +583,32 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
 
     // ---- (f) W = T Diag(beta) K-hat and U = T Diag(beta) V ------------------
     {
-        E* __restrict__ wout = static_cast<E*>(P.w) + gh * (C * DK);
-        float* __restrict__ uout = P.ut + gh * (DV * C);
-        for (int nt = wave; nt < DK / 16; nt += 4) {
-            const int c = 16 * nt + lm;
+        E* __restrict__ wout = reinterpret_cast<E*>(rec + R::W);
+        float* __restrict__ uout = reinterpret_cast<float*>(rec + R::UT);
+        constexpr int KS = DK / 32;
+        // W^T tiles (channels x tokens): the pair of channel tiles of one
+        // channel step gives a W fragment lane by lane.
+        for (int item = wave; item < KS * 4; item += 4) {
+            const int ksc = item >> 2;              // channel step
+            const int I = item & 3;                 // token tile
+            f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            const int kmax = (16 * I + 16 + 31) / 32;
+            for (int kt = 0; kt < kmax; ++kt) {
+                const int t = 32 * kt + 8 * lg;
+                const V bT = M::load8(s_Tp + (16 * I + lm) * TPP + t);
+                V a0, a1;
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f4 acc = {0.f, 0.f, 0.f, 0.f};
-                const int kmax = (16 * I + 16 + 31) / 32;
-                for (int ks = 0; ks < kmax; ++ks) {
-                    const int t = 32 * ks + 8 * lg;
-                    const V a = M::load8(s_Tp + (16 * I + lm) * TPP + t);
-                    V b;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) b[e] = s_khat[(t + e) * KP + c];
-                    acc = M::mma(a, b, acc);
+                for (int e = 0; e < 8; ++e) {
+                    a0[e] = s_khat[(t + e) * KP + 32 * ksc + lm];
+                    a1[e] = s_khat[(t + e) * KP + 32 * ksc + 16 + lm];
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wout[(16 * I + 4 * lg + i) * DK + c] = M::cvt(acc[i]);
+                acc0 = M::mma(a0, bT, acc0);
+                acc1 = M::mma(a1, bT, acc1);
             }
+            const float wv[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
+            M::store8(wout + frag_off(I * KS + ksc, lane), wv);
         }
+        // U in the accumulator layout the state kernel consumes directly
         for (int nt = wave; nt < DV / 16; nt += 4) {
             const int c = 16 * nt + lm;
 #pragma unroll
@@ -515,7 +626,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
                     }
                     acc = M::mma(a, b, acc);
                 }
-                *reinterpret_cast<f4*>(uout + c * C + 16 * I + 4 * lg) = acc;
+                *reinterpret_cast<f4*>(uout + (static_cast<size_t>(nt * 4 + I) * 64 + lane) * 4) = acc;
             }
         }
     }
@@ -526,17 +637,16 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
 // head and 16 value columns.  Wave w keeps state rows [w*DK/4, (w+1)*DK/4) of
 // those 16 columns in registers; an fp16/fp32 copy of the whole 16-column
 // state slice lives in LDS as the matrix-core operand of the next chunk.
+// The operands of the next kDepth-1 chunks are in flight in a register ring
+// while a chunk is computed, so the chain does not wait on memory latency.
 // ---------------------------------------------------------------------------
 struct StateParams {
     const int32_t* first;
     const int32_t* order;
     const int4* table;
-    const void* qh;
-    const void* w;
-    const void* ktt;
-    const void* p;
-    const float* ut;
-    const float* gam;
+    const unsigned char* rec;
+    size_t rec_bytes;
+    int64_t gmax;
     const float* initial_state;
     float* final_state;
     void* o;
@@ -544,14 +654,33 @@ struct StateParams {
     int H;
 };
 
+template <int DK, bool F16>
+struct StateStage {
+    using V = typename Mx<F16>::V;
+    static constexpr int KS = DK / 32;
+    static constexpr int TPW = DK / 64;
+    V w[KS], q[KS];          // rows 16w..16w+15 of W and Gamma.Q
+    V p[2];                  // row 16w+lm of P, tokens 0..63
+    V k[TPW][2];             // rows of ((gamma/Gamma).K)^T owned by this wave
+    f4 u;                    // U^T: column `col`, tokens 16w+4lg..+3
+    f4 gm[TPW];              // gamma for the owned state rows
+    int t0, len;
+};
+
+template <bool F16> struct StateDepth { static constexpr int value = F16 ? 4 : 2; };
+
 template <int DK, int DV, bool F16, bool OBF16>
 __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     using M = Mx<F16>;
     using E = typename M::E;
     using V = typename M::V;
+    using Stage = StateStage<DK, F16>;
+    using R = Rec<DK, DV, F16>;
+    constexpr int D = StateDepth<F16>::value;   // chunks in flight
     constexpr int NTV = DV / 16;          // 16-column tiles per (sequence, head)
     constexpr int RPW = DK / 4;           // state rows per wave
     constexpr int TPW = RPW / 16;         // 16-row tiles per wave
+    constexpr int KS = DK / 32;
     constexpr int SP = DK + 8;            // LDS row stride of the state operand
     constexpr int UP = C + 8;             // LDS row stride of U'
 
@@ -590,65 +719,87 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
         }
         M::store4(s_S + lm * SP + RPW * wave + 16 * t + 4 * lg, S[t]);
     }
-    __syncthreads();
 
-    const E* __restrict__ qhp = static_cast<const E*>(P.qh);
-    const E* __restrict__ wp = static_cast<const E*>(P.w);
-    const E* __restrict__ kp = static_cast<const E*>(P.ktt);
-    const E* __restrict__ pp = static_cast<const E*>(P.p);
+    const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.gmax * P.rec_bytes;
 
-    for (int g = g0; g < g1; ++g) {
+    auto load = [&](Stage& st, int g) {
         const int4 ent = P.table[g];
-        const int t0 = ent.y;
-        const int len = ent.z;
-        const size_t gh = static_cast<size_t>(g) * H + h;
-        const E* wr = wp + gh * (C * DK) + (16 * wave + lm) * DK;
-        const E* qr = qhp + gh * (C * DK) + (16 * wave + lm) * DK;
+        st.t0 = ent.y;
+        st.len = ent.z;
+        const unsigned char* rec = recs + static_cast<size_t>(g) * P.rec_bytes;
+        const E* wr = reinterpret_cast<const E*>(rec + R::W);
+        const E* qr = reinterpret_cast<const E*>(rec + R::QH);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            st.w[ks] = M::load8(wr + frag_off(wave * KS + ks, lane));
+            st.q[ks] = M::load8(qr + frag_off(wave * KS + ks, lane));
+        }
+        const E* pr = reinterpret_cast<const E*>(rec + R::P);
+        st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
+        st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
+        const float* gam = reinterpret_cast<const float*>(rec + R::GAM);
+        const E* kt = reinterpret_cast<const E*>(rec + R::KTT);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            st.k[t][0] = M::load8(kt + frag_off((TPW * wave + t) * 2, lane));
+            st.k[t][1] = M::load8(kt + frag_off((TPW * wave + t) * 2 + 1, lane));
+            st.gm[t] = *reinterpret_cast<const f4*>(gam + RPW * wave + 16 * t + 4 * lg);
+        }
+        st.u = *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(rec + R::UT) +
+                                            (static_cast<size_t>(jt * 4 + wave) * 64 + lane) * 4);
+    };
 
+    auto compute = [&](const Stage& st) {
         // (1) X = W S and O = (Gamma.Q) S for tokens 16w..16w+15
         f4 X = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-            const int c0 = 32 * ks + 8 * lg;
-            const V bS = M::load8(s_S + lm * SP + c0);
-            X = M::mma(M::load8(wr + c0), bS, X);
-            O = M::mma(M::load8(qr + c0), bS, O);
+        for (int ks = 0; ks < KS; ++ks) {
+            const E* sb = s_S + lm * SP + 32 * ks + 4 * lg;
+            const V bS = M::load4x2(sb, sb + 16);
+            X = M::mma(st.w[ks], bS, X);
+            O = M::mma(st.q[ks], bS, O);
         }
-        // (2) U' = U - W S
-        const f4 Uv = *reinterpret_cast<const f4*>(P.ut + gh * (DV * C) + col * C + 16 * wave + 4 * lg);
-        const f4 Uc = Uv - X;
-        M::store4(s_U + lm * UP + 16 * wave + 4 * lg, Uc);
+        // (2) U' = U - W S, shared through LDS
+        M::store4(s_U + lm * UP + 16 * wave + 4 * lg, st.u - X);
         __syncthreads();
-
-        // (3) O += Tril(...) U'
-        const E* prow = pp + gh * (C * C) + (16 * wave + lm) * C;
-        const int kmax = (16 * wave + 16 + 31) / 32;
-        for (int ks = 0; ks < kmax; ++ks) {
-            const int c0 = 32 * ks + 8 * lg;
-            O = M::mma(M::load8(prow + c0), M::load8(s_U + lm * UP + c0), O);
+        // (3) O += Tril(...) U'  (tokens above this wave's rows are zero in P)
+        const E* ub = s_U + lm * UP + 4 * lg;
+        const V bU0 = M::load4x2(ub, ub + 16);
+        const V bU1 = M::load4x2(ub + 32, ub + 48);
+        O = M::mma(st.p[0], bU0, O);
+        if (wave >= 2) O = M::mma(st.p[1], bU1, O);
+        // (4) S <- Diag(gamma) S + ((gamma/Gamma).K)^T U'
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = M::mma(st.k[t][0], bU0, acc);
+            acc = M::mma(st.k[t][1], bU1, acc);
+            S[t] = st.gm[t] * S[t] + acc;
+            M::store4(s_S + lm * SP + RPW * wave + 16 * t + 4 * lg, S[t]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * wave + 4 * lg + i;
-            if (r < len) store_out<OBF16>(P.o, (static_cast<size_t>(t0 + r) * H + h) * DV + col, O[i]);
-        }
-
-        // (4) S <- Diag(gamma) S + ((gamma/Gamma).K)^T U'
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int rb = RPW * wave + 16 * t;
-            const E* krow = kp + gh * (DK * C) + (rb + lm) * C;
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < C / 32; ++ks) {
-                const int c0 = 32 * ks + 8 * lg;
-                acc = M::mma(M::load8(krow + c0), M::load8(s_U + lm * UP + c0), acc);
-            }
-            const f4 gm = *reinterpret_cast<const f4*>(P.gam + gh * DK + rb + 4 * lg);
-            S[t] = gm * S[t] + acc;
-            M::store4(s_S + lm * SP + rb + 4 * lg, S[t]);
+            if (r < st.len) store_out<OBF16>(P.o, (static_cast<size_t>(st.t0 + r) * H + h) * DV + col, O[i]);
         }
         __syncthreads();
+    };
+
+    __syncthreads();
+    // Ring loads are unconditional (clamped to the last chunk; the surplus
+    // loads at the tail are never used) so that the loop body is straight-line
+    // code and the hardware wait counters never have to drain the ring.
+    Stage st[D];
+    if (g0 < g1) {
+#pragma unroll
+        for (int j = 0; j < D - 1; ++j) load(st[j], min(g0 + j, g1 - 1));
+    }
+    for (int g = g0; g < g1; g += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+            load(st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1));
+            if (g + j < g1) compute(st[j]);
+        }
     }
 
     if (P.final_state) {
@@ -662,6 +813,7 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
         }
     }
 }
+
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -682,9 +834,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         PrepParams pp;
         pp.q = a.q; pp.k = a.k; pp.v = a.v; pp.alpha = a.alpha; pp.beta = a.beta;
         pp.ctrl = ctrl; pp.table = table;
-        pp.qh = ws + pl.off_qh; pp.w = ws + pl.off_w; pp.ktt = ws + pl.off_ktt; pp.p = ws + pl.off_p;
-        pp.ut = reinterpret_cast<float*>(ws + pl.off_ut);
-        pp.gam = reinterpret_cast<float*>(ws + pl.off_gam);
+        pp.rec = ws + pl.off_rec; pp.rec_bytes = pl.rec_bytes; pp.gmax = pl.gmax;
         pp.H = pl.H;
         constexpr int lds = PrepLds<DK, DV, F16>::bytes;
         auto kfn = prep_kernel<DK, DV, F16>;
@@ -698,9 +848,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
 
     StateParams sp;
     sp.first = first; sp.order = order; sp.table = table;
-    sp.qh = ws + pl.off_qh; sp.w = ws + pl.off_w; sp.ktt = ws + pl.off_ktt; sp.p = ws + pl.off_p;
-    sp.ut = reinterpret_cast<const float*>(ws + pl.off_ut);
-    sp.gam = reinterpret_cast<const float*>(ws + pl.off_gam);
+    sp.rec = ws + pl.off_rec; sp.rec_bytes = pl.rec_bytes; sp.gmax = pl.gmax;
     sp.initial_state = a.initial_state;
     sp.final_state = a.final_state;
     sp.o = a.o;
@@ -745,12 +893,10 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.off_first = off; off = align256(off + 4 * (static_cast<size_t>(p.N) + 1));
     p.off_order = off; off = align256(off + 4 * static_cast<size_t>(p.N));
     p.off_table = off; off = align256(off + 16 * static_cast<size_t>(p.gmax));
-    p.off_qh = off;    off = align256(off + gh * C * Dk * p.eb);
-    p.off_w = off;     off = align256(off + gh * C * Dk * p.eb);
-    p.off_ktt = off;   off = align256(off + gh * C * Dk * p.eb);
-    p.off_p = off;     off = align256(off + gh * C * C * p.eb);
-    p.off_ut = off;    off = align256(off + gh * C * Dv * 4);
-    p.off_gam = off;   off = align256(off + gh * Dk * 4);
+    // per (head, chunk) record: qh, w, ktt, p (operand type), ut, gam (fp32)
+    p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(C) * C * p.eb +
+                           static_cast<size_t>(C) * Dv * 4 + static_cast<size_t>(Dk) * 4);
+    p.off_rec = off;   off = align256(off + gh * p.rec_bytes);
     p.workspace_bytes = off;
     *plan = p;
     return KDA_SUCCESS;
