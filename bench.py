@@ -48,6 +48,36 @@ def decode_bytes_per_step(N, H, Dk, Dv):
     return state + io
 
 
+KERNEL_SOURCES = ["gated_delta_rule_12_amd/csrc/kda_chunk.hip", "gated_delta_rule_12_amd/csrc/kda_decode.hip",
+                  "gated_delta_rule_12_amd/csrc/kda_common.h", "gated_delta_rule_12_amd/csrc/kda_chunk.h",
+                  "gated_delta_rule_12_amd/csrc/kda_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles",
+                            "hbm_traffic_chunk_fwd_B1_H32_T65536_d128_bf16+decode_N256_H32_d128_bf16.txt")
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when the kernel sources changed since it was taken."""
+    import hashlib
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if not line.startswith("#") and ":" in line:
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.split()[0]
+        h = hashlib.sha256()
+        for s in KERNEL_SOURCES:
+            with open(os.path.join(ROOT, s), "rb") as f:
+                h.update(f.read())
+        if fields.get("sources_sha256") != h.hexdigest():
+            return None
+        return {"fwd": int(float(fields["fwd_traffic_bytes"])),
+                "decode": int(float(fields["decode_traffic_bytes"]))}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -77,7 +107,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["fwd", "decode"], default=None)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16384)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -190,6 +220,14 @@ def main():
             cfg["workload"] = wd.name
 
     out["config"] = cfg
+    traffic = measured_traffic()
+    if traffic is not None:
+        if do_fwd:
+            out["roofline"]["traffic"] = traffic["fwd"]
+            out["roofline"]["traffic_unit"] = "bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
+        if do_dec:
+            out["decode"]["roofline"]["traffic"] = traffic["decode"]
+            out["decode"]["roofline"]["traffic_unit"] = "bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
 
     # ---- CPU baseline: the fp64 oracle on a bounded sample ---------------------
     if not args.no_cpu_baseline and do_fwd:
