@@ -244,8 +244,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
 // ---------------------------------------------------------------------------
 // prep_kernel: everything of one (chunk, head) that does not depend on the
-// state entering the chunk.  All global loads are issued first; the phases
-// then work out of LDS.
+// state entering the chunk.  Wave I owns tokens 16I..16I+15 in the
+// matrix-core lane layout; all global loads are issued first.
 // ---------------------------------------------------------------------------
 struct PrepParams {
     const void* q;
@@ -276,28 +276,65 @@ struct Rec {
     static constexpr size_t END = GAM + 4 * DK;
 };
 
+template <bool BF16> struct Load4;
+template <> struct Load4<true> {
+    static __device__ __forceinline__ f4 f(const uint16_t* p) {
+        const uint2 r = *reinterpret_cast<const uint2*>(p);
+        return f4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+                  __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+    }
+};
+template <> struct Load4<false> {
+    static __device__ __forceinline__ f4 f(const float* p) { return *reinterpret_cast<const f4*>(p); }
+};
+
 template <int DK, int DV, bool F16>
 struct PrepLds {
     using A = typename Act<F16>::T;   // raw activation element
     using E = typename Mx<F16>::E;    // matrix-core operand element
-    static constexpr int BP = DK + 4;        // fp32 row stride of b (log2 decay)
-    static constexpr int KP = DK + 8;        // row stride of k / K-hat and of q
+    static constexpr int KS = DK / 32;
+    static constexpr int KP = DK + 8;        // [token][channel] row stride (K-hat, K~ staging)
     static constexpr int VP = DV + 8;        // row stride of v
-    static constexpr int AP = C + 1;         // fp32 row stride of A
+    static constexpr int ATP = C + 4;        // fp32 row stride of A^T ([s][r])
     static constexpr int TP = C + 4;         // fp32 row stride of T
     static constexpr int TPP = C + 8;        // row stride of T Diag(beta) (operand type)
-    static constexpr int kElem = sizeof(A) > sizeof(E) ? sizeof(A) : sizeof(E);
-    // region 1: b, later T (fp32) followed by v
-    static constexpr int R1 = CMax<C * BP * 4, C * TP * 4 + C * VP * (int)sizeof(A)>::value;
-    // region 2: raw k, later K-hat in place
-    static constexpr int R2 = C * KP * kElem;
-    // region 3: raw q, later A (fp32), later T Diag(beta)
-    static constexpr int R3 =
-        CMax<C * KP * (int)sizeof(A), CMax<C * AP * 4, C * TPP * (int)sizeof(E)>::value>::value;
-    static constexpr int PARTS = 256 / DK;
-    static constexpr int R4 = (C + PARTS * DK) * 4;   // beta, cumsum part totals
-    static constexpr int bytes = R1 + R2 + R3 + R4;
+    // region a: off-diagonal column-operand fragments, later T (fp32)
+    static constexpr int RA = CMax<4 * KS * 64 * 8 * (int)sizeof(E), C * TP * 4>::value;
+    // region b: K~ staging, later v
+    static constexpr int RB = CMax<C * KP * (int)sizeof(E), C * VP * (int)sizeof(A)>::value;
+    // region c: K-hat
+    static constexpr int RC = C * KP * (int)sizeof(E);
+    // region d: A^T (fp32), later T Diag(beta)
+    static constexpr int RD = CMax<C * ATP * 4, C * TPP * (int)sizeof(E)>::value;
+    // small: block references and ends [8][DK], block totals [4][DK], the
+    // per-channel rescaling table [6][DK], beta [64]
+    static constexpr int RS = (8 * DK + 4 * DK + 6 * DK + C) * 4;
+    static constexpr int bytes = RA + RB + RC + RD + RS;
 };
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr by 1, 2,
+// 4, 8; lanes shifted in from outside the row read 0).
+__device__ __forceinline__ float row_shr_f(float x, int n) {
+    const int xi = __builtin_bit_cast(int, x);
+    int y = 0;
+    switch (n) {
+        case 1: y = __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xf, 0xf, false); break;
+        case 2: y = __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xf, 0xf, false); break;
+        case 4: y = __builtin_amdgcn_update_dpp(0, xi, 0x114, 0xf, 0xf, false); break;
+        default: y = __builtin_amdgcn_update_dpp(0, xi, 0x118, 0xf, 0xf, false); break;
+    }
+    return __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float row_scan16(float x) {
+    x += row_shr_f(x, 1);
+    x += row_shr_f(x, 2);
+    x += row_shr_f(x, 4);
+    x += row_shr_f(x, 8);
+    return x;
+}
+
+// (I, J) with J < I -> index into the rescaling table
+__device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
 template <int DK, int DV, bool F16>
 __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
@@ -306,13 +343,10 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     using M = Mx<F16>;
     using E = typename M::E;
     using V = typename M::V;
-    constexpr int BP = L::BP, KP = L::KP, VP = L::VP, AP = L::AP, TP = L::TP, TPP = L::TPP;
-    constexpr int PARTS = L::PARTS;
-    constexpr int RP = C / PARTS;                          // cumsum rows per thread
+    using R = Rec<DK, DV, F16>;
+    constexpr int KS = L::KS, KP = L::KP, VP = L::VP, ATP = L::ATP, TP = L::TP, TPP = L::TPP;
     constexpr int EL16 = 16 / (int)sizeof(A);              // activations per 16 bytes
-    constexpr int KROW16 = DK / EL16;                      // 16-byte pieces per k/q row
     constexpr int VROW16 = DV / EL16;
-    constexpr int NK = C * KROW16 / 256;                   // pieces per thread
     constexpr int NV = C * VROW16 / 256;
 
     const int H = P.H;
@@ -322,183 +356,191 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     const int4 ent = P.table[g];
     const int t0 = ent.y;
     const int len = ent.z;
-    using R = Rec<DK, DV, F16>;
     unsigned char* rec = P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes;
 
     extern __shared__ __align__(16) unsigned char lds[];
-    float* s_b = reinterpret_cast<float*>(lds);
-    float* s_T = reinterpret_cast<float*>(lds);                       // after b is dead
-    A* s_v = reinterpret_cast<A*>(lds + C * TP * 4);                  // after b is dead
-    A* s_kraw = reinterpret_cast<A*>(lds + L::R1);
-    E* s_khat = reinterpret_cast<E*>(lds + L::R1);                    // K-hat, in place
-    A* s_q = reinterpret_cast<A*>(lds + L::R1 + L::R2);
-    float* s_A = reinterpret_cast<float*>(lds + L::R1 + L::R2);       // after q is dead
-    E* s_Tp = reinterpret_cast<E*>(lds + L::R1 + L::R2);              // after A is dead
-    float* s_beta = reinterpret_cast<float*>(lds + L::R1 + L::R2 + L::R3);
-    float* s_part = s_beta + C;
+    E* s_C = reinterpret_cast<E*>(lds);                                 // column fragments
+    float* s_T = reinterpret_cast<float*>(lds);                         // after s_C is dead
+    E* s_Kt = reinterpret_cast<E*>(lds + L::RA);                        // K~ [token][channel]
+    A* s_v = reinterpret_cast<A*>(lds + L::RA);                         // after s_Kt is dead
+    E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat [token][channel]
+    float* s_AT = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC);
+    E* s_Tp = reinterpret_cast<E*>(lds + L::RA + L::RB + L::RC);        // after A^T is dead
+    float* s_bnd = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC + L::RD);  // [8][DK]
+    float* s_tot = s_bnd + 8 * DK;                                      // [4][DK]
+    float* s_g = s_tot + 4 * DK;                                        // [6][DK]
+    float* s_beta = s_g + 6 * DK;                                       // [C]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int lm = lane & 15;
     const int lg = lane >> 4;
+    const int I = wave;                       // this wave's 16-token block
+    const int r = 16 * I + lm;                // this lane's token
+    const bool valid = r < len;
 
     const A* __restrict__ q = static_cast<const A*>(P.q);
     const A* __restrict__ k = static_cast<const A*>(P.k);
     const A* __restrict__ v = static_cast<const A*>(P.v);
-    auto row_k = [&](int r) { return (static_cast<size_t>(t0 + r) * H + h) * DK; };
-    auto row_v = [&](int r) { return (static_cast<size_t>(t0 + r) * H + h) * DV; };
+    const size_t rowk = (static_cast<size_t>(t0 + (valid ? r : 0)) * H + h) * DK;
+    auto row_v = [&](int rr) { return (static_cast<size_t>(t0 + rr) * H + h) * DV; };
+    // Lane (lm, lg) owns token r and, in reduction step ks, the channels
+    // 32ks + frag_k(lg, e): two runs of four, at 32ks + 4lg and 32ks + 16 + 4lg.
+    auto chan = [&](int ks, int e) { return 32 * ks + frag_k(lg, e); };
 
-    // ---- (0) every global load of the chunk, up front ------------------------
-    const int c_own = tid % DK;                 // cumsum: channel and row part
-    const int part = tid / DK;
-    float al[RP];
+    // ---- (0) every global load, up front --------------------------------------
+    float b[KS][8], kf[KS][8], qf[KS][8];
 #pragma unroll
-    for (int i = 0; i < RP; ++i) {
-        const int r = part * RP + i;
-        al[i] = r < len ? P.alpha[row_k(r) + c_own] : 1.f;
-    }
-    uint4 kreg[NK], qreg[NK], vreg[NV];
+    for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-        const int id = tid + 256 * j;
-        const int r = id / KROW16;
-        const int cc = (id - r * KROW16) * EL16;
-        kreg[j] = make_uint4(0, 0, 0, 0);
-        qreg[j] = make_uint4(0, 0, 0, 0);
-        if (r < len) {
-            kreg[j] = *reinterpret_cast<const uint4*>(k + row_k(r) + cc);
-            qreg[j] = *reinterpret_cast<const uint4*>(q + row_k(r) + cc);
+        for (int half = 0; half < 2; ++half) {
+            const int c = 32 * ks + 16 * half + 4 * lg;
+            f4 a4 = {1.f, 1.f, 1.f, 1.f}, k4 = {0.f, 0.f, 0.f, 0.f}, q4 = {0.f, 0.f, 0.f, 0.f};
+            if (valid) {
+                a4 = *reinterpret_cast<const f4*>(P.alpha + rowk + c);
+                k4 = Load4<F16>::f(k + rowk + c);
+                q4 = Load4<F16>::f(q + rowk + c);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                b[ks][4 * half + i] = a4[i];
+                kf[ks][4 * half + i] = k4[i];
+                qf[ks][4 * half + i] = q4[i];
+            }
         }
     }
+    uint4 vreg[NV];
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int id = tid + 256 * j;
-        const int r = id / VROW16;
-        const int cc = (id - r * VROW16) * EL16;
-        vreg[j] = make_uint4(0, 0, 0, 0);
-        if (r < len) vreg[j] = *reinterpret_cast<const uint4*>(v + row_v(r) + cc);
+    for (int jv = 0; jv < NV; ++jv) {
+        const int id = tid + 256 * jv;
+        const int rr = id / VROW16;
+        const int cc = (id - rr * VROW16) * EL16;
+        vreg[jv] = make_uint4(0, 0, 0, 0);
+        if (rr < len) vreg[jv] = *reinterpret_cast<const uint4*>(v + row_v(rr) + cc);
     }
-    const float bet = (tid < C && tid < len) ? P.beta[static_cast<size_t>(t0 + tid) * H + h] : 0.f;
+    const float bet = valid ? P.beta[static_cast<size_t>(t0 + r) * H + h] : 0.f;
 
-    // ---- (a) k, q to LDS; b = cumsum(log2 alpha) per key channel -------------
+    // ---- (a) b = inclusive cumsum of log2(alpha) over the chunk's tokens -----
+    // scan over the 16 tokens of this wave's block (lanes of one 16-lane row),
+    // then add the totals of the earlier blocks
 #pragma unroll
-    for (int j = 0; j < NK; ++j) {
-        const int id = tid + 256 * j;
-        const int r = id / KROW16;
-        const int cc = (id - r * KROW16) * EL16;
-        *reinterpret_cast<uint4*>(s_kraw + r * KP + cc) = kreg[j];
-        *reinterpret_cast<uint4*>(s_q + r * KP + cc) = qreg[j];
-    }
-    if (tid < C) s_beta[tid] = bet;
-    {
-        float run = 0.f;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < RP; ++i) {
-            run += flog2(al[i]);
-            al[i] = run;
+        for (int e = 0; e < 8; ++e) {
+            b[ks][e] = row_scan16(flog2(b[ks][e]));
         }
-        s_part[part * DK + c_own] = run;
-        __syncthreads();
-        float off = 0.f;
-        for (int pp = 0; pp < part; ++pp) off += s_part[pp * DK + c_own];
+    if (lm == 15) {
 #pragma unroll
-        for (int i = 0; i < RP; ++i) s_b[(part * RP + i) * BP + c_own] = al[i] + off;
-        __syncthreads();
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_tot[I * DK + chan(ks, e)] = b[ks][e];
+    }
+    if (lg == 0) s_beta[r] = bet;
+    __syncthreads();
+    for (int Ip = 0; Ip < I; ++Ip)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[ks][e] += s_tot[Ip * DK + chan(ks, e)];
+    // block references (token 16I+7) and block ends (token 16I+15)
+    if (lm == 7 || lm == 15) {
+        float* dst = s_bnd + (lm == 7 ? I : 4 + I) * DK;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[chan(ks, e)] = b[ks][e];
+    }
+    __syncthreads();
+    // gamma and the rescaling table 2^(ref_I - end_J), J < I (all <= 1)
+    if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = fexp2(s_bnd[7 * DK + tid]);
+    for (int id = tid; id < 6 * DK; id += 256) {
+        const int p = id / DK, c = id - p * DK;
+        const int Ii = p < 1 ? 1 : (p < 3 ? 2 : 3);
+        const int Jj = p - pair_index(Ii, 0);
+        s_g[id] = fexp2(s_bnd[Ii * DK + c] - s_bnd[(4 + Jj) * DK + c]);
     }
 
-    auto kraw = [&](int r, int c) -> float {
-        if constexpr (F16) return bf16_to_f32(s_kraw[r * KP + c]);
-        else return s_kraw[r * KP + c];
-    };
-    auto qraw = [&](int r, int c) -> float {
-        if constexpr (F16) return bf16_to_f32(s_q[r * KP + c]);
-        else return s_q[r * KP + c];
-    };
-
-    // ---- (b) gamma, Gamma.Q and ((gamma/Gamma).K)^T in fragment order --------
+    // ---- (b) every decay-dependent quantity of this lane's elements -----------
+    float Rk[KS][8], Rq[KS][8];   // row operands Gamma-rebased at token 16I+7 (fp32)
+    V Dc[KS];                     // block-diagonal column operand
     {
         E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
-        E* __restrict__ ktt = reinterpret_cast<E*>(rec + R::KTT);
-        if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = fexp2(s_b[(C - 1) * BP + tid]);
-        constexpr int KS = DK / 32;
-        // Gamma.Q: fragment f = (token tile) * KS + (channel step)
-        for (int id = tid; id < C * KS * 4; id += 256) {
-            const int m = id & 15, j = (id >> 4) & 3, f = id >> 6;
-            const int rt = f / KS, ks = f - rt * KS;
-            const int r = 16 * rt + m;
-            float qv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = 32 * ks + frag_k(j, e);
-                qv[e] = qraw(r, c) * fexp2(s_b[r * BP + c]);
-            }
-            M::store8(qh + frag_off(f, id & 63), qv);
-        }
-        // ((gamma/Gamma).K)^T: fragment f = (channel tile) * 2 + (token step)
-        for (int id = tid; id < DK * 2 * 4; id += 256) {
-            const int m = id & 15, j = (id >> 4) & 3, f = id >> 6;
-            const int ct = f >> 1, ts = f & 1;
-            const int c = 16 * ct + m;
-            const float bl = s_b[(C - 1) * BP + c];
-            float kv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 32 * ts + frag_k(j, e);
-                kv[e] = kraw(t, c) * fexp2(bl - s_b[t * BP + c]);
-            }
-            M::store8(ktt + frag_off(f, id & 63), kv);
-        }
-    }
-
-    // ---- (c) A and P on the matrix cores; wave I owns rows 16I..16I+15 -------
-    {
-        const int I = wave;
-        const int rr = 16 * I + lm;                 // this lane's row (A operand)
-        const int refr = 16 * I + 7;                // reference token of block I
-        E* __restrict__ pout = reinterpret_cast<E*>(rec + R::P);
-        constexpr int KS = DK / 32;
-        V kr[KS], qr[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int c0 = 32 * ks + 8 * lg;
+            float qv[8], cv[8], kh[8], kt[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float f = fexp2(s_b[rr * BP + c0 + e] - s_b[refr * BP + c0 + e]);
-                kr[ks][e] = M::cvt(kraw(rr, c0 + e) * f);
-                qr[ks][e] = M::cvt(qraw(rr, c0 + e) * f);
+                const int c = chan(ks, e);
+                const float bb = b[ks][e];
+                const float e1 = fexp2(bb - s_bnd[I * DK + c]);          // 2^(b - ref_I)
+                Rk[ks][e] = kf[ks][e] * e1;
+                Rq[ks][e] = qf[ks][e] * e1;
+                Dc[ks][e] = M::cvt(kf[ks][e] * __builtin_amdgcn_rcpf(e1));
+                cv[e] = kf[ks][e] * fexp2(s_bnd[(4 + I) * DK + c] - bb);  // 2^(end_I - b) <= 1
+                const float e3 = fexp2(bb);                               // Gamma
+                kh[e] = kf[ks][e] * e3;
+                qv[e] = qf[ks][e] * e3;
+                kt[e] = kf[ks][e] * fexp2(s_bnd[7 * DK + c] - bb);      // gamma / Gamma
             }
+            M::store8(qh + frag_off(I * KS + ks, lane), qv);
+            M::store8(s_C + frag_off(I * KS + ks, lane), cv);
+            const int c0 = 32 * ks + 4 * lg;
+            M::store4(s_khat + r * KP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
+            M::store4(s_khat + r * KP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
+            M::store4(s_Kt + r * KP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
+            M::store4(s_Kt + r * KP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
         }
-        __syncthreads();                            // q is dead; its region takes A
-        // A in the accumulator layout (rows of A) for the solve; P as P^T tiles
-        // so that its fragments can be stored straight from the accumulators.
+    }
+    __syncthreads();
+
+    // ---- (c) A (as A^T) and P (as P^T tiles) on the matrix cores ---------------
+    {
+        E* __restrict__ pout = reinterpret_cast<E*>(rec + R::P);
         f4 accP[4];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             accP[J] = f4{0.f, 0.f, 0.f, 0.f};
             if (J <= I) {
-                const int s = 16 * J + lm;          // this lane's column token
                 f4 accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const int c0 = 32 * ks + 8 * lg;
-                    V kc;
+                    V ra, rq, col;
+                    if (J == I) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        kc[e] = M::cvt(kraw(s, c0 + e) *
-                                       fexp2(s_b[refr * BP + c0 + e] - s_b[s * BP + c0 + e]));
-                    accA = M::mma(kr[ks], kc, accA);
-                    accP[J] = M::mma(kc, qr[ks], accP[J]);
+                        for (int e = 0; e < 8; ++e) {
+                            ra[e] = M::cvt(Rk[ks][e]);
+                            rq[e] = M::cvt(Rq[ks][e]);
+                        }
+                        col = Dc[ks];
+                    } else {
+                        const float* gp = s_g + pair_index(I, J) * DK + 32 * ks + 4 * lg;
+                        const f4 g0 = *reinterpret_cast<const f4*>(gp);
+                        const f4 g1 = *reinterpret_cast<const f4*>(gp + 16);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            ra[e] = M::cvt(Rk[ks][e] * g0[e]);
+                            rq[e] = M::cvt(Rq[ks][e] * g0[e]);
+                            ra[4 + e] = M::cvt(Rk[ks][4 + e] * g1[e]);
+                            rq[4 + e] = M::cvt(Rq[ks][4 + e] * g1[e]);
+                        }
+                        col = M::load8(s_C + frag_off(J * KS + ks, lane));
+                    }
+                    accA = M::mma(ra, col, accA);
+                    accP[J] = M::mma(col, rq, accP[J]);
                 }
+                // lane (lm, lg) holds A[16I + 4lg + i][16J + lm]; store A^T rows
+                const int s = 16 * J + lm;
+                f4 at;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * I + 4 * lg + i;
-                    s_A[r * AP + s] = s < r ? s_beta[r] * accA[i] : 0.f;
+                    const int rr = 16 * I + 4 * lg + i;
+                    at[i] = s < rr ? s_beta[rr] * accA[i] : 0.f;
                 }
+                *reinterpret_cast<f4*>(s_AT + s * ATP + 16 * I + 4 * lg) = at;
             }
         }
         // lane (lm, lg) of P^T tile J holds P[16I+lm][16J+4lg+i]
-        const int r = 16 * I + lm;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             float pv[8];
@@ -511,72 +553,76 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
             M::store8(pout + frag_off(2 * I + ks, lane), pv);
         }
     }
-    __syncthreads();
 
-    // ---- (d) K-hat = Gamma.K in place (operand type); b dies here -----------
-    for (int id = tid; id < C * DK; id += 256) {
-        const int r = id / DK;
-        const int c = id - r * DK;
-        // each element is read and rewritten by the same thread
-        const float kv = kraw(r, c) * fexp2(s_b[r * BP + c]);
-        s_khat[r * KP + c] = M::cvt(kv);
+    // ---- (d) ((gamma/Gamma).K)^T fragments from the staged K~ ------------------
+    {
+        E* __restrict__ ktt = reinterpret_cast<E*>(rec + R::KTT);
+        for (int id = tid; id < DK * 2 * 4; id += 256) {
+            const int m = id & 15, jj = (id >> 4) & 3, f = id >> 6;
+            const int c = 16 * (f >> 1) + m, ts = f & 1;
+            float kv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kv[e] = M::tof(s_Kt[(32 * ts + frag_k(jj, e)) * KP + c]);
+            M::store8(ktt + frag_off(f, id & 63), kv);
+        }
     }
     __syncthreads();
 
     // ---- (e) v into LDS; T = (I + A)^-1 --------------------------------------
     {
 #pragma unroll
-        for (int j = 0; j < NV; ++j) {
-            const int id = tid + 256 * j;
-            const int r = id / VROW16;
-            const int cc = (id - r * VROW16) * EL16;
-            *reinterpret_cast<uint4*>(s_v + r * VP + cc) = vreg[j];
+        for (int jv = 0; jv < NV; ++jv) {
+            const int id = tid + 256 * jv;
+            const int rr = id / VROW16;
+            const int cc = (id - rr * VROW16) * EL16;
+            *reinterpret_cast<uint4*>(s_v + rr * VP + cc) = vreg[jv];
         }
-        // diagonal 16x16 blocks by forward substitution; lane j owns column j
+        // diagonal 16x16 blocks, column-oriented forward substitution: once
+        // x[s] is final, every later row takes its contribution
         if (lane < 16) {
-            const int I = wave;
             const int j = lane;
             float x[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == j) ? 1.f : 0.f;
+            for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int s = 0; s < r; ++s) acc -= s_A[(16 * I + r) * AP + 16 * I + s] * x[s];
-                x[r] = acc;
+            for (int s = 0; s < 15; ++s) {
+                const float* col = s_AT + (16 * I + s) * ATP + 16 * I;   // A[16I+rr][16I+s], rr = 0..15
+#pragma unroll
+                for (int rr = s + 1; rr < 16; ++rr) x[rr] -= col[rr] * x[s];
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s_T[(16 * I + r) * TP + 16 * I + j] = x[r];
+            for (int rr = 0; rr < 16; ++rr) s_T[(16 * I + rr) * TP + 16 * I + j] = x[rr];
         }
         __syncthreads();
         // blocks below the diagonal: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-        for (int I = 1; I < 4; ++I) {
-            if (wave < I) {
+        for (int Ib = 1; Ib < 4; ++Ib) {
+            if (wave < Ib) {
                 const int J = wave;
                 f4 X = {0.f, 0.f, 0.f, 0.f};
-                for (int K = J; K < I; ++K) {
+                for (int K = J; K < Ib; ++K) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
-                        const float a = s_A[(16 * I + lm) * AP + 16 * K + 4 * kk + lg];
-                        const float b = s_T[(16 * K + 4 * kk + lg) * TP + 16 * J + lm];
-                        X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, X, 0, 0, 0);
+                        const float a = s_AT[(16 * K + 4 * kk + lg) * ATP + 16 * Ib + lm];
+                        const float bv = s_T[(16 * K + 4 * kk + lg) * TP + 16 * J + lm];
+                        X = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, X, 0, 0, 0);
                     }
                 }
                 f4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float a = -s_T[(16 * I + lm) * TP + 16 * I + 4 * lg + i];
+                    const float a = -s_T[(16 * Ib + lm) * TP + 16 * Ib + 4 * lg + i];
                     Y = __builtin_amdgcn_mfma_f32_16x16x4f32(a, X[i], Y, 0, 0, 0);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_T[(16 * I + 4 * lg + i) * TP + 16 * J + lm] = Y[i];
+                for (int i = 0; i < 4; ++i) s_T[(16 * Ib + 4 * lg + i) * TP + 16 * J + lm] = Y[i];
             }
             __syncthreads();
         }
         // T Diag(beta), zero above the diagonal, in the operand type
         for (int id = tid; id < C * C; id += 256) {
-            const int r = id / C;
-            const int s = id - r * C;
-            s_Tp[r * TPP + s] = M::cvt(s <= r ? s_T[r * TP + s] * s_beta[s] : 0.f);
+            const int rr = id / C;
+            const int s = id - rr * C;
+            s_Tp[rr * TPP + s] = M::cvt(s <= rr ? s_T[rr * TP + s] * s_beta[s] : 0.f);
         }
         __syncthreads();
     }
@@ -585,17 +631,16 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     {
         E* __restrict__ wout = reinterpret_cast<E*>(rec + R::W);
         float* __restrict__ uout = reinterpret_cast<float*>(rec + R::UT);
-        constexpr int KS = DK / 32;
         // W^T tiles (channels x tokens): the pair of channel tiles of one
         // channel step gives a W fragment lane by lane.
         for (int item = wave; item < KS * 4; item += 4) {
             const int ksc = item >> 2;              // channel step
-            const int I = item & 3;                 // token tile
+            const int Ib = item & 3;                // token tile
             f4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-            const int kmax = (16 * I + 16 + 31) / 32;
+            const int kmax = (16 * Ib + 16 + 31) / 32;
             for (int kt = 0; kt < kmax; ++kt) {
                 const int t = 32 * kt + 8 * lg;
-                const V bT = M::load8(s_Tp + (16 * I + lm) * TPP + t);
+                const V bT = M::load8(s_Tp + (16 * Ib + lm) * TPP + t);
                 V a0, a1;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -606,27 +651,27 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
                 acc1 = M::mma(a1, bT, acc1);
             }
             const float wv[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-            M::store8(wout + frag_off(I * KS + ksc, lane), wv);
+            M::store8(wout + frag_off(Ib * KS + ksc, lane), wv);
         }
         // U in the accumulator layout the state kernel consumes directly
         for (int nt = wave; nt < DV / 16; nt += 4) {
             const int c = 16 * nt + lm;
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
+            for (int Ib = 0; Ib < 4; ++Ib) {
                 f4 acc = {0.f, 0.f, 0.f, 0.f};
-                const int kmax = (16 * I + 16 + 31) / 32;
+                const int kmax = (16 * Ib + 16 + 31) / 32;
                 for (int ks = 0; ks < kmax; ++ks) {
                     const int t = 32 * ks + 8 * lg;
-                    const V a = M::load8(s_Tp + (16 * I + lm) * TPP + t);
-                    V b;
+                    const V a = M::load8(s_Tp + (16 * Ib + lm) * TPP + t);
+                    V bv;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        if constexpr (F16) b[e] = M::cvt(bf16_to_f32(s_v[(t + e) * VP + c]));
-                        else b[e] = s_v[(t + e) * VP + c];
+                        if constexpr (F16) bv[e] = M::cvt(bf16_to_f32(s_v[(t + e) * VP + c]));
+                        else bv[e] = s_v[(t + e) * VP + c];
                     }
-                    acc = M::mma(a, b, acc);
+                    acc = M::mma(a, bv, acc);
                 }
-                *reinterpret_cast<f4*>(uout + (static_cast<size_t>(nt * 4 + I) * 64 + lane) * 4) = acc;
+                *reinterpret_cast<f4*>(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4) = acc;
             }
         }
     }
@@ -634,11 +679,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
 
 // ---------------------------------------------------------------------------
 // state_kernel: the sequential pass over the chunks of one sequence for one
-// head and 16 value columns.  Wave w keeps state rows [w*DK/4, (w+1)*DK/4) of
-// those 16 columns in registers; an fp16/fp32 copy of the whole 16-column
-// state slice lives in LDS as the matrix-core operand of the next chunk.
-// The operands of the next kDepth-1 chunks are in flight in a register ring
-// while a chunk is computed, so the chain does not wait on memory latency.
+// head and 16*TW value columns.  Wave w keeps state rows [w*DK/4, (w+1)*DK/4)
+// of those columns in fp32 registers; an operand-type copy of the state
+// slice lives in LDS for the next chunk's products.  Every operand fragment a
+// wave loads (W, Gamma.Q, P, ((gamma/Gamma).K)^T) serves all TW column tiles,
+// whose chains are independent and interleave on the matrix cores.  The
+// operands of the next kDepth-1 chunks are in flight in a register ring.
 // ---------------------------------------------------------------------------
 struct StateParams {
     const int32_t* first;
@@ -654,7 +700,7 @@ struct StateParams {
     int H;
 };
 
-template <int DK, bool F16>
+template <int DK, bool F16, int TW>
 struct StateStage {
     using V = typename Mx<F16>::V;
     static constexpr int KS = DK / 32;
@@ -662,30 +708,40 @@ struct StateStage {
     V w[KS], q[KS];          // rows 16w..16w+15 of W and Gamma.Q
     V p[2];                  // row 16w+lm of P, tokens 0..63
     V k[TPW][2];             // rows of ((gamma/Gamma).K)^T owned by this wave
-    f4 u;                    // U^T: column `col`, tokens 16w+4lg..+3
+    f4 u[TW];                // U: tokens 16w+4lg..+3, one column per tile
     f4 gm[TPW];              // gamma for the owned state rows
     int t0, len;
 };
 
-template <bool F16> struct StateDepth { static constexpr int value = F16 ? 4 : 2; };
+#ifndef KDA_STATE_DEPTH
+#define KDA_STATE_DEPTH 2
+#endif
+template <bool F16> struct StateDepth { static constexpr int value = F16 ? KDA_STATE_DEPTH : 2; };
+
+// value-column tiles (16 columns each) per workgroup
+#ifndef KDA_STATE_TILES
+#define KDA_STATE_TILES 1
+#endif
 
 template <int DK, int DV, bool F16, bool OBF16>
 __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     using M = Mx<F16>;
     using E = typename M::E;
     using V = typename M::V;
-    using Stage = StateStage<DK, F16>;
+    constexpr int TW = KDA_STATE_TILES;
+    using Stage = StateStage<DK, F16, TW>;
     using R = Rec<DK, DV, F16>;
     constexpr int D = StateDepth<F16>::value;   // chunks in flight
-    constexpr int NTV = DV / 16;          // 16-column tiles per (sequence, head)
+    constexpr int NTV = DV / (16 * TW);   // workgroups per (sequence, head)
     constexpr int RPW = DK / 4;           // state rows per wave
     constexpr int TPW = RPW / 16;         // 16-row tiles per wave
     constexpr int KS = DK / 32;
     constexpr int SP = DK + 8;            // LDS row stride of the state operand
     constexpr int UP = C + 8;             // LDS row stride of U'
+    static_assert(NTV >= 1 && NTV * 16 * TW == DV, "value tiling");
 
-    // Workgroups are handed to the 8 XCDs round-robin; keep the NTV tiles of
-    // one (sequence, head) on the same XCD so they share its L2.
+    // Workgroups are handed to the 8 XCDs round-robin; keep the NTV
+    // workgroups of one (sequence, head) on the same XCD so they share its L2.
     const int bid = blockIdx.x;
     const int xcd = bid & 7;
     const int slot = bid >> 3;
@@ -703,84 +759,146 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     const int wave = tid >> 6;
     const int lm = lane & 15;
     const int lg = lane >> 4;
-    const int col = 16 * jt + lm;
 
-    __shared__ __align__(16) E s_S[16 * SP];   // [value column][key row]
-    __shared__ __align__(16) E s_U[16 * UP];   // [value column][token]
+    __shared__ __align__(16) E s_S[16 * TW * SP];   // [value column][key row]
+    __shared__ __align__(16) E s_U[16 * TW * UP];   // [value column][token]
 
     const size_t sbase = (static_cast<size_t>(n) * H + h) * (DK * DV);
-    f4 S[TPW];
+    f4 S[TW][TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
+    for (int c = 0; c < TW; ++c) {
+        const int col = 16 * (jt * TW + c) + lm;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = RPW * wave + 16 * t + 4 * lg + i;
-            S[t][i] = P.initial_state ? P.initial_state[sbase + row * DV + col] : 0.f;
+        for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = RPW * wave + 16 * t + 4 * lg + i;
+                S[c][t][i] = P.initial_state ? P.initial_state[sbase + row * DV + col] : 0.f;
+            }
+            M::store4(s_S + (16 * c + lm) * SP + RPW * wave + 16 * t + 4 * lg, S[c][t]);
         }
-        M::store4(s_S + lm * SP + RPW * wave + 16 * t + 4 * lg, S[t]);
     }
 
     const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.gmax * P.rec_bytes;
+    // output rows of this lane: tokens 16w + 4lg + i of the chunk
+    const size_t ostride = static_cast<size_t>(H) * DV;                 // elements per token row
+    const size_t ocol = static_cast<size_t>(h) * DV + 16 * jt * TW + lm;
 
-    auto load = [&](Stage& st, int g) {
-        const int4 ent = P.table[g];
-        st.t0 = ent.y;
-        st.len = ent.z;
+    // The next stage's loads are split into four groups issued between the
+    // phases of the current chunk: a CU's vector-memory address path moves
+    // about 64 B per clock, so issuing a whole stage at once would stall the
+    // wave for ~1000 clocks while the matrix cores idle.  sched_barrier keeps
+    // the compiler from regrouping them.
+    auto load_part = [&](Stage& st, int g, int part) {
         const unsigned char* rec = recs + static_cast<size_t>(g) * P.rec_bytes;
-        const E* wr = reinterpret_cast<const E*>(rec + R::W);
-        const E* qr = reinterpret_cast<const E*>(rec + R::QH);
+        if (part == 0) {
+            const E* wr = reinterpret_cast<const E*>(rec + R::W);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            st.w[ks] = M::load8(wr + frag_off(wave * KS + ks, lane));
-            st.q[ks] = M::load8(qr + frag_off(wave * KS + ks, lane));
-        }
-        const E* pr = reinterpret_cast<const E*>(rec + R::P);
-        st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
-        st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
-        const float* gam = reinterpret_cast<const float*>(rec + R::GAM);
-        const E* kt = reinterpret_cast<const E*>(rec + R::KTT);
+            for (int ks = 0; ks < KS; ++ks) st.w[ks] = M::load8(wr + frag_off(wave * KS + ks, lane));
+        } else if (part == 1) {
+            const E* qr = reinterpret_cast<const E*>(rec + R::QH);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            st.k[t][0] = M::load8(kt + frag_off((TPW * wave + t) * 2, lane));
-            st.k[t][1] = M::load8(kt + frag_off((TPW * wave + t) * 2 + 1, lane));
-            st.gm[t] = *reinterpret_cast<const f4*>(gam + RPW * wave + 16 * t + 4 * lg);
+            for (int ks = 0; ks < KS; ++ks) st.q[ks] = M::load8(qr + frag_off(wave * KS + ks, lane));
+        } else if (part == 2) {
+            const E* pr = reinterpret_cast<const E*>(rec + R::P);
+            st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
+            st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
+            const E* kt = reinterpret_cast<const E*>(rec + R::KTT);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                st.k[t][0] = M::load8(kt + frag_off((TPW * wave + t) * 2, lane));
+                st.k[t][1] = M::load8(kt + frag_off((TPW * wave + t) * 2 + 1, lane));
+            }
+        } else {
+            const int4 ent = P.table[g];
+            st.t0 = ent.y;
+            st.len = ent.z;
+            const float* gam = reinterpret_cast<const float*>(rec + R::GAM);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                st.gm[t] = *reinterpret_cast<const f4*>(gam + RPW * wave + 16 * t + 4 * lg);
+            const float* ut = reinterpret_cast<const float*>(rec + R::UT);
+#pragma unroll
+            for (int c = 0; c < TW; ++c)
+                st.u[c] = *reinterpret_cast<const f4*>(ut + (static_cast<size_t>((jt * TW + c) * 4 + wave) * 64 + lane) * 4);
         }
-        st.u = *reinterpret_cast<const f4*>(reinterpret_cast<const float*>(rec + R::UT) +
-                                            (static_cast<size_t>(jt * 4 + wave) * 64 + lane) * 4);
+    };
+    auto load = [&](Stage& st, int g) {
+#pragma unroll
+        for (int part = 0; part < 4; ++part) load_part(st, g, part);
     };
 
-    auto compute = [&](const Stage& st) {
-        // (1) X = W S and O = (Gamma.Q) S for tokens 16w..16w+15
-        f4 X = {0.f, 0.f, 0.f, 0.f}, O = {0.f, 0.f, 0.f, 0.f};
+    // one chunk of the chain; `nx` / `gn` receive the loads of a later chunk
+    auto compute = [&](const Stage& st, Stage& nx, int gn) {
+        // (1) X = W S and O = (Gamma.Q) S for tokens 16w..16w+15, every tile
+        f4 X[TW], O[TW];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const E* sb = s_S + lm * SP + 32 * ks + 4 * lg;
-            const V bS = M::load4x2(sb, sb + 16);
-            X = M::mma(st.w[ks], bS, X);
-            O = M::mma(st.q[ks], bS, O);
+        for (int c = 0; c < TW; ++c) {
+            X[c] = f4{0.f, 0.f, 0.f, 0.f};
+            O[c] = f4{0.f, 0.f, 0.f, 0.f};
         }
+        V bS[TW][KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int c = 0; c < TW; ++c) {
+                const E* sb = s_S + (16 * c + lm) * SP + 32 * ks + 4 * lg;
+                bS[c][ks] = M::load4x2(sb, sb + 16);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        load_part(nx, gn, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int c = 0; c < TW; ++c) {
+                X[c] = M::mma(st.w[ks], bS[c][ks], X[c]);
+                O[c] = M::mma(st.q[ks], bS[c][ks], O[c]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        load_part(nx, gn, 1);
+        __builtin_amdgcn_sched_barrier(0);
         // (2) U' = U - W S, shared through LDS
-        M::store4(s_U + lm * UP + 16 * wave + 4 * lg, st.u - X);
+#pragma unroll
+        for (int c = 0; c < TW; ++c) M::store4(s_U + (16 * c + lm) * UP + 16 * wave + 4 * lg, st.u[c] - X[c]);
         __syncthreads();
-        // (3) O += Tril(...) U'  (tokens above this wave's rows are zero in P)
-        const E* ub = s_U + lm * UP + 4 * lg;
-        const V bU0 = M::load4x2(ub, ub + 16);
-        const V bU1 = M::load4x2(ub + 32, ub + 48);
-        O = M::mma(st.p[0], bU0, O);
-        if (wave >= 2) O = M::mma(st.p[1], bU1, O);
-        // (4) S <- Diag(gamma) S + ((gamma/Gamma).K)^T U'
+        __builtin_amdgcn_sched_barrier(0);
+        load_part(nx, gn, 2);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = M::mma(st.k[t][0], bU0, acc);
-            acc = M::mma(st.k[t][1], bU1, acc);
-            S[t] = st.gm[t] * S[t] + acc;
-            M::store4(s_S + lm * SP + RPW * wave + 16 * t + 4 * lg, S[t]);
+        for (int c = 0; c < TW; ++c) {
+            const E* ub = s_U + (16 * c + lm) * UP + 4 * lg;
+            const V bU0 = M::load4x2(ub, ub + 16);
+            const V bU1 = M::load4x2(ub + 32, ub + 48);
+            // (3) O += Tril(...) U'  (tokens above this wave's rows are zero in P)
+            O[c] = M::mma(st.p[0], bU0, O[c]);
+            if (wave >= 2) O[c] = M::mma(st.p[1], bU1, O[c]);
+            // (4) S <- Diag(gamma) S + ((gamma/Gamma).K)^T U'
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = M::mma(st.k[t][0], bU0, acc);
+                acc = M::mma(st.k[t][1], bU1, acc);
+                S[c][t] = st.gm[t] * S[c][t] + acc;
+                M::store4(s_S + (16 * c + lm) * SP + RPW * wave + 16 * t + 4 * lg, S[c][t]);
+            }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        load_part(nx, gn, 3);
+        __builtin_amdgcn_sched_barrier(0);
+        // outputs: full chunks take the branch-free path
+        const size_t obase = (static_cast<size_t>(st.t0) + 16 * wave + 4 * lg) * ostride + ocol;
+        if (st.len == C) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * wave + 4 * lg + i;
-            if (r < st.len) store_out<OBF16>(P.o, (static_cast<size_t>(st.t0 + r) * H + h) * DV + col, O[i]);
+            for (int c = 0; c < TW; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store_out<OBF16>(P.o, obase + i * ostride + 16 * c, O[c][i]);
+        } else {
+#pragma unroll
+            for (int c = 0; c < TW; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * wave + 4 * lg + i < st.len) store_out<OBF16>(P.o, obase + i * ostride + 16 * c, O[c][i]);
         }
         __syncthreads();
     };
@@ -797,18 +915,21 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     for (int g = g0; g < g1; g += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            load(st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1));
-            if (g + j < g1) compute(st[j]);
+            if (g + j < g1) compute(st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1));
         }
     }
 
     if (P.final_state) {
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
+        for (int c = 0; c < TW; ++c) {
+            const int col = 16 * (jt * TW + c) + lm;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = RPW * wave + 16 * t + 4 * lg + i;
-                P.final_state[sbase + row * DV + col] = S[t][i];
+            for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = RPW * wave + 16 * t + 4 * lg + i;
+                    P.final_state[sbase + row * DV + col] = S[c][t][i];
+                }
             }
         }
     }
@@ -855,7 +976,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     sp.N = pl.N;
     sp.H = pl.H;
     const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
-    const int64_t blocks = (pairs + 7) / 8 * 8 * (DV / 16);
+    const int64_t blocks = (pairs + 7) / 8 * 8 * (DV / (16 * KDA_STATE_TILES));
     hipLaunchKernelGGL((state_kernel<DK, DV, F16, OBF16>), dim3(static_cast<unsigned>(blocks)),
                        dim3(256), 0, stream, sp);
     return hipGetLastError();

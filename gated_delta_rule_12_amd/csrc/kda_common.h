@@ -16,14 +16,6 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
-}
-
 // Activation element type: fp32 or bf16 (raw bits).
 template <bool BF16> struct Act;
 template <> struct Act<false> {
@@ -40,7 +32,8 @@ template <> __device__ __forceinline__ void store_out<false>(void* o, size_t i, 
     static_cast<float*>(o)[i] = x;
 }
 template <> __device__ __forceinline__ void store_out<true>(void* o, size_t i, float x) {
-    static_cast<uint16_t*>(o)[i] = f32_to_bf16(x);
+    // gfx950 converts with round-to-nearest-even in one instruction
+    static_cast<uint16_t*>(o)[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
 // ---------------------------------------------------------------------------
