@@ -25,7 +25,7 @@ constexpr int kChunk = 64;      // tokens per chunk
 //     w        E[64][Dk]           W = T Diag(beta) (Gamma (.) K)
 //     ktt      E[Dk][64]           ((gamma/Gamma) (.) K)^T (channel-major)
 //     p        E[64][64]           Tril((Gamma.Q)(K/Gamma)^T), zero above the diagonal
-//     ut       f32[Dv][64]         U^T, U = T Diag(beta) V
+//     ut       E[Dv][64]           U^T, U = T Diag(beta) V (accumulator fragments)
 //     gam      f32[Dk]             whole-chunk decay gamma
 struct ChunkPlan {
     int B = 0, H = 0, Dk = 0, Dv = 0, N = 0;

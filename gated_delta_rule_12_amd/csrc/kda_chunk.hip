@@ -77,6 +77,13 @@ template <> struct Mx<true> {
     }
     static __device__ __forceinline__ E cvt(float x) { return static_cast<E>(x); }
     static __device__ __forceinline__ float tof(E x) { return static_cast<float>(x); }
+    // four elements (8-byte aligned), converted where they are used
+    using V4 = h4;
+    static __device__ __forceinline__ V4 load4(const E* p) { return *reinterpret_cast<const h4*>(p); }
+    static __device__ __forceinline__ f4 tof4(V4 a) {
+        return f4{static_cast<float>(a[0]), static_cast<float>(a[1]), static_cast<float>(a[2]),
+                  static_cast<float>(a[3])};
+    }
     static __device__ __forceinline__ void store4(E* p, f4 x) {
         h4 h = {static_cast<E>(x[0]), static_cast<E>(x[1]), static_cast<E>(x[2]), static_cast<E>(x[3])};
         *reinterpret_cast<h4*>(p) = h;
@@ -115,6 +122,9 @@ template <> struct Mx<false> {
     }
     static __device__ __forceinline__ E cvt(float x) { return x; }
     static __device__ __forceinline__ float tof(E x) { return x; }
+    using V4 = f4;
+    static __device__ __forceinline__ V4 load4(const E* p) { return *reinterpret_cast<const f4*>(p); }
+    static __device__ __forceinline__ f4 tof4(V4 a) { return a; }
     static __device__ __forceinline__ void store4(E* p, f4 x) { *reinterpret_cast<f4*>(p) = x; }
     static __device__ __forceinline__ void store8(E* p, const float* x) {
         f4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
@@ -272,7 +282,7 @@ struct Rec {
     static constexpr size_t KTT = W + sizeof(E) * C * DK;
     static constexpr size_t P = KTT + sizeof(E) * DK * C;
     static constexpr size_t UT = P + sizeof(E) * C * C;
-    static constexpr size_t GAM = UT + 4 * DV * C;
+    static constexpr size_t GAM = UT + sizeof(E) * DV * C;
     static constexpr size_t END = GAM + 4 * DK;
 };
 
@@ -306,9 +316,11 @@ struct PrepLds {
     static constexpr int RC = C * KP * (int)sizeof(E);
     // region d: A^T (fp32), later T Diag(beta)
     static constexpr int RD = CMax<C * ATP * 4, C * TPP * (int)sizeof(E)>::value;
-    // small: block references and ends [8][DK], block totals [4][DK], the
-    // per-channel rescaling table [6][DK], beta [64]
-    static constexpr int RS = (8 * DK + 4 * DK + 6 * DK + C) * 4;
+    // small: the per-channel rescaling table [6][DK], beta [64]
+    static constexpr int RS = (6 * DK + C) * 4;
+    // the block totals [4][DK] and decay factors [16][DK] live in region d
+    // until A^T is written there
+    static_assert(RD >= 20 * DK * 4, "region d holds the decay tables");
     static constexpr int bytes = RA + RB + RC + RD + RS;
 };
 
@@ -366,9 +378,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat [token][channel]
     float* s_AT = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC);
     E* s_Tp = reinterpret_cast<E*>(lds + L::RA + L::RB + L::RC);        // after A^T is dead
-    float* s_bnd = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC + L::RD);  // [8][DK]
-    float* s_tot = s_bnd + 8 * DK;                                      // [4][DK]
-    float* s_g = s_tot + 4 * DK;                                        // [6][DK]
+    float* s_tot = s_AT;                                                // [4][DK], until (c)
+    float* s_fac = s_AT + 4 * DK;                                       // [16][DK], until (c)
+    float* s_g = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC + L::RD);  // [6][DK]
     float* s_beta = s_g + 6 * DK;                                       // [C]
 
     const int tid = threadIdx.x;
@@ -443,22 +455,37 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int e = 0; e < 8; ++e) b[ks][e] += s_tot[Ip * DK + chan(ks, e)];
-    // block references (token 16I+7) and block ends (token 16I+15)
+    // Gamma = 2^b and 1/Gamma for every element; every other decay factor is
+    // one of them times a per-channel constant taken at the block's reference
+    // token 16I+7 (lane 7 of the row) or its last token 16I+15 (lane 15):
+    //   s_fac rows 0..3 2^ref_I, 4..7 2^-ref_I, 8..11 2^end_I, 12..15 2^-end_I
+    float rb[KS][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            b[ks][e] = fexp2(b[ks][e]);
+            rb[ks][e] = __builtin_amdgcn_rcpf(b[ks][e]);
+        }
     if (lm == 7 || lm == 15) {
-        float* dst = s_bnd + (lm == 7 ? I : 4 + I) * DK;
+        float* d0 = s_fac + ((lm == 7 ? 0 : 8) + I) * DK + 4 * lg;
+        float* d1 = d0 + 4 * DK;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dst[chan(ks, e)] = b[ks][e];
+        for (int ks = 0; ks < KS; ++ks) {
+            *reinterpret_cast<f4*>(d0 + 32 * ks) = f4{b[ks][0], b[ks][1], b[ks][2], b[ks][3]};
+            *reinterpret_cast<f4*>(d0 + 32 * ks + 16) = f4{b[ks][4], b[ks][5], b[ks][6], b[ks][7]};
+            *reinterpret_cast<f4*>(d1 + 32 * ks) = f4{rb[ks][0], rb[ks][1], rb[ks][2], rb[ks][3]};
+            *reinterpret_cast<f4*>(d1 + 32 * ks + 16) = f4{rb[ks][4], rb[ks][5], rb[ks][6], rb[ks][7]};
+        }
     }
     __syncthreads();
     // gamma and the rescaling table 2^(ref_I - end_J), J < I (all <= 1)
-    if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = fexp2(s_bnd[7 * DK + tid]);
+    if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = s_fac[11 * DK + tid];
     for (int id = tid; id < 6 * DK; id += 256) {
         const int p = id / DK, c = id - p * DK;
         const int Ii = p < 1 ? 1 : (p < 3 ? 2 : 3);
         const int Jj = p - pair_index(Ii, 0);
-        s_g[id] = fexp2(s_bnd[Ii * DK + c] - s_bnd[(4 + Jj) * DK + c]);
+        s_g[id] = s_fac[Ii * DK + c] * s_fac[(12 + Jj) * DK + c];
     }
 
     // ---- (b) every decay-dependent quantity of this lane's elements -----------
@@ -466,22 +493,31 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     V Dc[KS];                     // block-diagonal column operand
     {
         E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
+        auto fac4 = [&](int row, int ks, int half) {
+            return *reinterpret_cast<const f4*>(s_fac + row * DK + 32 * ks + 16 * half + 4 * lg);
+        };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             float qv[8], cv[8], kh[8], kt[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = chan(ks, e);
-                const float bb = b[ks][e];
-                const float e1 = fexp2(bb - s_bnd[I * DK + c]);          // 2^(b - ref_I)
-                Rk[ks][e] = kf[ks][e] * e1;
-                Rq[ks][e] = qf[ks][e] * e1;
-                Dc[ks][e] = M::cvt(kf[ks][e] * __builtin_amdgcn_rcpf(e1));
-                cv[e] = kf[ks][e] * fexp2(s_bnd[(4 + I) * DK + c] - bb);  // 2^(end_I - b) <= 1
-                const float e3 = fexp2(bb);                               // Gamma
-                kh[e] = kf[ks][e] * e3;
-                qv[e] = qf[ks][e] * e3;
-                kt[e] = kf[ks][e] * fexp2(s_bnd[7 * DK + c] - bb);      // gamma / Gamma
+            for (int half = 0; half < 2; ++half) {
+                const f4 ref = fac4(I, ks, half);          // 2^ref_I
+                const f4 rref = fac4(4 + I, ks, half);     // 2^-ref_I
+                const f4 endi = fac4(8 + I, ks, half);     // 2^end_I
+                const f4 gam = fac4(11, ks, half);         // gamma = 2^end_3
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * half + i;
+                    const float G = b[ks][e], rG = rb[ks][e], kv = kf[ks][e];
+                    const float e1 = G * rref[i];                      // 2^(b - ref_I)
+                    Rk[ks][e] = kv * e1;
+                    Rq[ks][e] = qf[ks][e] * e1;
+                    Dc[ks][e] = M::cvt(kv * (rG * ref[i]));           // k 2^(ref_I - b)
+                    cv[e] = kv * (rG * endi[i]);                       // k 2^(end_I - b)
+                    kh[e] = kv * G;
+                    qv[e] = qf[ks][e] * G;
+                    kt[e] = kv * (rG * gam[i]);                        // k gamma / Gamma
+                }
             }
             M::store8(qh + frag_off(I * KS + ks, lane), qv);
             M::store8(s_C + frag_off(I * KS + ks, lane), cv);
@@ -630,7 +666,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     // ---- (f) W = T Diag(beta) K-hat and U = T Diag(beta) V ------------------
     {
         E* __restrict__ wout = reinterpret_cast<E*>(rec + R::W);
-        float* __restrict__ uout = reinterpret_cast<float*>(rec + R::UT);
+        E* __restrict__ uout = reinterpret_cast<E*>(rec + R::UT);
         // W^T tiles (channels x tokens): the pair of channel tiles of one
         // channel step gives a W fragment lane by lane.
         for (int item = wave; item < KS * 4; item += 4) {
@@ -671,7 +707,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
                     }
                     acc = M::mma(a, bv, acc);
                 }
-                *reinterpret_cast<f4*>(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4) = acc;
+                M::store4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc);
             }
         }
     }
@@ -708,10 +744,23 @@ struct StateStage {
     V w[KS], q[KS];          // rows 16w..16w+15 of W and Gamma.Q
     V p[2];                  // row 16w+lm of P, tokens 0..63
     V k[TPW][2];             // rows of ((gamma/Gamma).K)^T owned by this wave
-    f4 u[TW];                // U: tokens 16w+4lg..+3, one column per tile
+    typename Mx<F16>::V4 u[TW];   // U: tokens 16w+4lg..+3, one column per tile
     f4 gm[TPW];              // gamma for the owned state rows
     int t0, len;
 };
+
+// Four compute waves, plus one wave that prefetches records into L2 where
+// the register budget of two waves per SIMD allows it (the fp32 d_k = 128
+// variant needs more than 256 registers per wave).
+template <int DK, bool F16> struct StateThreads { static constexpr int value = (F16 || DK == 64) ? 320 : 256; };
+#ifndef KDA_STATE_PREFETCH
+#define KDA_STATE_PREFETCH 2
+#endif
+constexpr int kStatePrefetch = KDA_STATE_PREFETCH;   // chunks ahead
+#ifndef KDA_PREFETCH_SHIFT
+#define KDA_PREFETCH_SHIFT 7
+#endif
+constexpr int kPrefetchShift = KDA_PREFETCH_SHIFT;   // log2 of the bytes per touched word
 
 #ifndef KDA_STATE_DEPTH
 #define KDA_STATE_DEPTH 2
@@ -724,7 +773,7 @@ template <bool F16> struct StateDepth { static constexpr int value = F16 ? KDA_S
 #endif
 
 template <int DK, int DV, bool F16, bool OBF16>
-__global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
+__global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(const StateParams P) {
     using M = Mx<F16>;
     using E = typename M::E;
     using V = typename M::V;
@@ -762,11 +811,13 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
 
     __shared__ __align__(16) E s_S[16 * TW * SP];   // [value column][key row]
     __shared__ __align__(16) E s_U[16 * TW * UP];   // [value column][token]
+    __shared__ __align__(16) int s_pf[64];           // sink of the prefetch loads
 
     const size_t sbase = (static_cast<size_t>(n) * H + h) * (DK * DV);
+    const bool pf_wave = StateThreads<DK, F16>::value > 256 && wave == 4;
     f4 S[TW][TPW];
 #pragma unroll
-    for (int c = 0; c < TW; ++c) {
+    for (int c = 0; c < TW && !pf_wave; ++c) {
         const int col = 16 * (jt * TW + c) + lm;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -780,6 +831,7 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     }
 
     const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.gmax * P.rec_bytes;
+    const size_t gstride = P.rec_bytes;
     // output rows of this lane: tokens 16w + 4lg + i of the chunk
     const size_t ostride = static_cast<size_t>(H) * DV;                 // elements per token row
     const size_t ocol = static_cast<size_t>(h) * DV + 16 * jt * TW + lm;
@@ -790,26 +842,17 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     // wave for ~1000 clocks while the matrix cores idle.  sched_barrier keeps
     // the compiler from regrouping them.
     auto load_part = [&](Stage& st, int g, int part) {
-        const unsigned char* rec = recs + static_cast<size_t>(g) * P.rec_bytes;
+        const unsigned char* rec = recs + static_cast<size_t>(g) * gstride;
         if (part == 0) {
+            // W and U head the chain of the next chunk; gamma and the chunk's
+            // table entry ride along
             const E* wr = reinterpret_cast<const E*>(rec + R::W);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) st.w[ks] = M::load8(wr + frag_off(wave * KS + ks, lane));
-        } else if (part == 1) {
-            const E* qr = reinterpret_cast<const E*>(rec + R::QH);
+            const E* ut = reinterpret_cast<const E*>(rec + R::UT);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) st.q[ks] = M::load8(qr + frag_off(wave * KS + ks, lane));
-        } else if (part == 2) {
-            const E* pr = reinterpret_cast<const E*>(rec + R::P);
-            st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
-            st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
-            const E* kt = reinterpret_cast<const E*>(rec + R::KTT);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                st.k[t][0] = M::load8(kt + frag_off((TPW * wave + t) * 2, lane));
-                st.k[t][1] = M::load8(kt + frag_off((TPW * wave + t) * 2 + 1, lane));
-            }
-        } else {
+            for (int c = 0; c < TW; ++c)
+                st.u[c] = M::load4(ut + (static_cast<size_t>((jt * TW + c) * 4 + wave) * 64 + lane) * 4);
             const int4 ent = P.table[g];
             st.t0 = ent.y;
             st.len = ent.z;
@@ -817,10 +860,21 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
 #pragma unroll
             for (int t = 0; t < TPW; ++t)
                 st.gm[t] = *reinterpret_cast<const f4*>(gam + RPW * wave + 16 * t + 4 * lg);
-            const float* ut = reinterpret_cast<const float*>(rec + R::UT);
+        } else if (part == 1) {
+            const E* qr = reinterpret_cast<const E*>(rec + R::QH);
 #pragma unroll
-            for (int c = 0; c < TW; ++c)
-                st.u[c] = *reinterpret_cast<const f4*>(ut + (static_cast<size_t>((jt * TW + c) * 4 + wave) * 64 + lane) * 4);
+            for (int ks = 0; ks < KS; ++ks) st.q[ks] = M::load8(qr + frag_off(wave * KS + ks, lane));
+        } else if (part == 2) {
+            const E* kt = reinterpret_cast<const E*>(rec + R::KTT);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                st.k[t][0] = M::load8(kt + frag_off((TPW * wave + t) * 2, lane));
+                st.k[t][1] = M::load8(kt + frag_off((TPW * wave + t) * 2 + 1, lane));
+            }
+        } else {
+            const E* pr = reinterpret_cast<const E*>(rec + R::P);
+            st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
+            st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
         }
     };
     auto load = [&](Stage& st, int g) {
@@ -860,7 +914,7 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
         __builtin_amdgcn_sched_barrier(0);
         // (2) U' = U - W S, shared through LDS
 #pragma unroll
-        for (int c = 0; c < TW; ++c) M::store4(s_U + (16 * c + lm) * UP + 16 * wave + 4 * lg, st.u[c] - X[c]);
+        for (int c = 0; c < TW; ++c) M::store4(s_U + (16 * c + lm) * UP + 16 * wave + 4 * lg, M::tof4(st.u[c]) - X[c]);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
         load_part(nx, gn, 2);
@@ -904,6 +958,32 @@ __global__ __launch_bounds__(256) void state_kernel(const StateParams P) {
     };
 
     __syncthreads();
+    if (pf_wave) {
+        // Load one word of every 128-byte line of the record kStatePrefetch
+        // chunks ahead (this workgroup takes every NTV-th line, so the NTV
+        // workgroups of the pair cover the record once) to bring it into the
+        // XCD's L2.  The words go straight to a scratch area of LDS and are
+        // never waited on; they count on this wave's counters only.  The wave
+        // passes the same barriers as the compute waves, two per chunk.
+        const int nlines = static_cast<int>(P.rec_bytes >> kPrefetchShift);
+        auto prefetch = [&](int gp) {
+            const unsigned char* rec = recs + static_cast<size_t>(gp) * gstride;
+            for (int line = jt + NTV * lane; line < nlines; line += NTV * 64)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(rec + (static_cast<size_t>(line) << kPrefetchShift)),
+                    (__attribute__((address_space(3))) void*)s_pf, 4, 0, 0);
+        };
+        for (int gp = g0 + 1; gp < min(g0 + kStatePrefetch, g1); ++gp) prefetch(gp);
+        // Bare barriers: a fence here would wait for the prefetches to land.
+        for (int g = g0; g < g1; ++g) {
+            if (g + kStatePrefetch < g1) prefetch(g + kStatePrefetch);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        // let the last loads land before the wave ends
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        return;
+    }
     // Ring loads are unconditional (clamped to the last chunk; the surplus
     // loads at the tail are never used) so that the loop body is straight-line
     // code and the hardware wait counters never have to drain the ring.
@@ -946,6 +1026,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     int32_t* order = reinterpret_cast<int32_t*>(ws + pl.off_order);
     int4* table = reinterpret_cast<int4*>(ws + pl.off_table);
 
+    if (Rec<DK, DV, F16>::END > pl.rec_bytes) return hipErrorInvalidValue;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.cu_seqlens, pl.N,
                        pl.varlen ? static_cast<int64_t>(0) : pl.T, pl.gmax, ctrl, first, order, table);
     hipError_t e = hipGetLastError();
@@ -978,7 +1059,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
     const int64_t blocks = (pairs + 7) / 8 * 8 * (DV / (16 * KDA_STATE_TILES));
     hipLaunchKernelGGL((state_kernel<DK, DV, F16, OBF16>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, stream, sp);
+                       dim3(StateThreads<DK, F16>::value), 0, stream, sp);
     return hipGetLastError();
 }
 
@@ -1014,9 +1095,9 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.off_first = off; off = align256(off + 4 * (static_cast<size_t>(p.N) + 1));
     p.off_order = off; off = align256(off + 4 * static_cast<size_t>(p.N));
     p.off_table = off; off = align256(off + 16 * static_cast<size_t>(p.gmax));
-    // per (head, chunk) record: qh, w, ktt, p (operand type), ut, gam (fp32)
+    // per (head, chunk) record: qh, w, ktt, p, ut (operand type), gam (fp32)
     p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(C) * C * p.eb +
-                           static_cast<size_t>(C) * Dv * 4 + static_cast<size_t>(Dk) * 4);
+                           static_cast<size_t>(C) * Dv * p.eb + static_cast<size_t>(Dk) * 4);
     p.off_rec = off;   off = align256(off + gh * p.rec_bytes);
     p.workspace_bytes = off;
     *plan = p;
