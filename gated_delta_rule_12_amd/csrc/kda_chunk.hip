@@ -88,6 +88,7 @@ template <> struct Mx<true> {
         h4 h = {static_cast<E>(x[0]), static_cast<E>(x[1]), static_cast<E>(x[2]), static_cast<E>(x[3])};
         *reinterpret_cast<h4*>(p) = h;
     }
+    static __device__ __forceinline__ void storeV(E* p, const V& v) { *reinterpret_cast<V*>(p) = v; }
     static __device__ __forceinline__ void store8(E* p, const float* x) {
         h8 h;
 #pragma unroll
@@ -126,6 +127,10 @@ template <> struct Mx<false> {
     static __device__ __forceinline__ V4 load4(const E* p) { return *reinterpret_cast<const f4*>(p); }
     static __device__ __forceinline__ f4 tof4(V4 a) { return a; }
     static __device__ __forceinline__ void store4(E* p, f4 x) { *reinterpret_cast<f4*>(p) = x; }
+    static __device__ __forceinline__ void storeV(E* p, const V& v) {
+        *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f4*>(p + 4) = f4{v[4], v[5], v[6], v[7]};
+    }
     static __device__ __forceinline__ void store8(E* p, const float* x) {
         f4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
         *reinterpret_cast<f4*>(p) = lo;
@@ -269,6 +274,8 @@ struct PrepParams {
     size_t rec_bytes;
     int64_t gmax;
     int H;
+    int64_t T;     // tokens per sequence of a dense batch; 0 for varlen
+    int cps;       // chunks per sequence of a dense batch
 };
 
 template <int a, int b> struct CMax { static constexpr int value = a > b ? a : b; };
@@ -286,16 +293,20 @@ struct Rec {
     static constexpr size_t END = GAM + 4 * DK;
 };
 
-template <bool BF16> struct Load4;
-template <> struct Load4<true> {
-    static __device__ __forceinline__ f4 f(const uint16_t* p) {
-        const uint2 r = *reinterpret_cast<const uint2*>(p);
+// Four consecutive activations: loaded raw, widened to fp32 where used.
+template <bool BF16> struct Raw4;
+template <> struct Raw4<true> {
+    using T = uint2;
+    static __device__ __forceinline__ T load(const uint16_t* p) { return *reinterpret_cast<const uint2*>(p); }
+    static __device__ __forceinline__ f4 widen(T r) {
         return f4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
                   __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
     }
 };
-template <> struct Load4<false> {
-    static __device__ __forceinline__ f4 f(const float* p) { return *reinterpret_cast<const f4*>(p); }
+template <> struct Raw4<false> {
+    using T = f4;
+    static __device__ __forceinline__ T load(const float* p) { return *reinterpret_cast<const f4*>(p); }
+    static __device__ __forceinline__ f4 widen(T r) { return r; }
 };
 
 template <int DK, int DV, bool F16>
@@ -303,21 +314,20 @@ struct PrepLds {
     using A = typename Act<F16>::T;   // raw activation element
     using E = typename Mx<F16>::E;    // matrix-core operand element
     static constexpr int KS = DK / 32;
-    static constexpr int KP = DK + 8;        // [token][channel] row stride (K-hat, K~ staging)
-    static constexpr int VP = DV + 8;        // row stride of v
+    static constexpr int XP = C + 8;         // row stride of the channel-major K-hat, K~ and v
     static constexpr int ATP = C + 4;        // fp32 row stride of A^T ([s][r])
     static constexpr int TP = C + 4;         // fp32 row stride of T
     static constexpr int TPP = C + 8;        // row stride of T Diag(beta) (operand type)
-    // region a: off-diagonal column-operand fragments, later T (fp32)
-    static constexpr int RA = CMax<4 * KS * 64 * 8 * (int)sizeof(E), C * TP * 4>::value;
-    // region b: K~ staging, later v
-    static constexpr int RB = CMax<C * KP * (int)sizeof(E), C * VP * (int)sizeof(A)>::value;
-    // region c: K-hat
-    static constexpr int RC = C * KP * (int)sizeof(E);
+    // region a: column operands of the six blocks below the diagonal, later T (fp32)
+    static constexpr int RA = CMax<6 * KS * 64 * 8 * (int)sizeof(E), C * TP * 4>::value;
+    // region b: K~^T [channel][token], later V^T [column][token] (operand type)
+    static constexpr int RB = CMax<DK, DV>::value * XP * (int)sizeof(E);
+    // region c: K-hat^T [channel][token]
+    static constexpr int RC = DK * XP * (int)sizeof(E);
     // region d: A^T (fp32), later T Diag(beta)
     static constexpr int RD = CMax<C * ATP * 4, C * TPP * (int)sizeof(E)>::value;
-    // small: the per-channel rescaling table [6][DK], beta [64]
-    static constexpr int RS = (6 * DK + C) * 4;
+    // small: beta [64]
+    static constexpr int RS = C * 4;
     // the block totals [4][DK] and decay factors [16][DK] live in region d
     // until A^T is written there
     static_assert(RD >= 20 * DK * 4, "region d holds the decay tables");
@@ -349,14 +359,14 @@ __device__ __forceinline__ float row_scan16(float x) {
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
 template <int DK, int DV, bool F16>
-__global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
+__global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     using L = PrepLds<DK, DV, F16>;
     using A = typename L::A;
     using M = Mx<F16>;
     using E = typename M::E;
     using V = typename M::V;
     using R = Rec<DK, DV, F16>;
-    constexpr int KS = L::KS, KP = L::KP, VP = L::VP, ATP = L::ATP, TP = L::TP, TPP = L::TPP;
+    constexpr int KS = L::KS, XP = L::XP, ATP = L::ATP, TP = L::TP, TPP = L::TPP;
     constexpr int EL16 = 16 / (int)sizeof(A);              // activations per 16 bytes
     constexpr int VROW16 = DV / EL16;
     constexpr int NV = C * VROW16 / 256;
@@ -364,24 +374,32 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     const int H = P.H;
     const int g = blockIdx.x / H;
     const int h = blockIdx.x - g * H;
-    if (g >= P.ctrl[0]) return;
-    const int4 ent = P.table[g];
-    const int t0 = ent.y;
-    const int len = ent.z;
+    int t0, len;
+    if (P.T > 0) {
+        // dense batch: chunk g is chunk j of sequence n
+        const int n = g / P.cps;
+        const int j = g - n * P.cps;
+        t0 = static_cast<int>(n * P.T) + C * j;
+        len = min(C, static_cast<int>(P.T) - C * j);
+    } else {
+        if (g >= P.ctrl[0]) return;
+        const int4 ent = P.table[g];
+        t0 = ent.y;
+        len = ent.z;
+    }
     unsigned char* rec = P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes;
 
     extern __shared__ __align__(16) unsigned char lds[];
     E* s_C = reinterpret_cast<E*>(lds);                                 // column fragments
     float* s_T = reinterpret_cast<float*>(lds);                         // after s_C is dead
-    E* s_Kt = reinterpret_cast<E*>(lds + L::RA);                        // K~ [token][channel]
-    A* s_v = reinterpret_cast<A*>(lds + L::RA);                         // after s_Kt is dead
-    E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat [token][channel]
+    E* s_Kt = reinterpret_cast<E*>(lds + L::RA);                        // K~^T [channel][token]
+    E* s_v = reinterpret_cast<E*>(lds + L::RA);                         // V^T, after s_Kt is dead
+    E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat^T [channel][token]
     float* s_AT = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC);
     E* s_Tp = reinterpret_cast<E*>(lds + L::RA + L::RB + L::RC);        // after A^T is dead
     float* s_tot = s_AT;                                                // [4][DK], until (c)
     float* s_fac = s_AT + 4 * DK;                                       // [16][DK], until (c)
-    float* s_g = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC + L::RD);  // [6][DK]
-    float* s_beta = s_g + 6 * DK;                                       // [C]
+    float* s_beta = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC + L::RD);  // [C]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -395,43 +413,44 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     const A* __restrict__ q = static_cast<const A*>(P.q);
     const A* __restrict__ k = static_cast<const A*>(P.k);
     const A* __restrict__ v = static_cast<const A*>(P.v);
-    const size_t rowk = (static_cast<size_t>(t0 + (valid ? r : 0)) * H + h) * DK;
     auto row_v = [&](int rr) { return (static_cast<size_t>(t0 + rr) * H + h) * DV; };
+    // V^T rows: token groups of 8 are XOR-swizzled by the column's group of
+    // 8, so that the 16 lanes staging one token (8 columns apart) spread over
+    // the LDS banks; the 16-byte operand reads stay contiguous.
+    auto vswz = [](int c) { return 8 * ((c >> 3) & 7); };
     // Lane (lm, lg) owns token r and, in reduction step ks, the channels
     // 32ks + frag_k(lg, e): two runs of four, at 32ks + 4lg and 32ks + 16 + 4lg.
     auto chan = [&](int ks, int e) { return 32 * ks + frag_k(lg, e); };
 
-    // ---- (0) every global load, up front --------------------------------------
-    float b[KS][8], kf[KS][8], qf[KS][8];
+    // ---- (0) global loads of alpha, k, q, beta (v follows in (b)) ---------------
+    // Rows past the chunk's end re-read its last row (always in bounds) and
+    // are replaced by the neutral values (alpha 1, k = q = v = beta = 0) where
+    // used, so the loads carry no branches and nothing waits for them early.
+    using R4 = Raw4<F16>;
+    const int rl = len - 1;
+    float b[KS][8];
+    typename R4::T kraw[KS][2], qraw[KS][2];
+    f4 araw[KS][2];
+    {
+        const size_t rowk = (static_cast<size_t>(t0 + min(r, rl)) * H + h) * DK;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int c = 32 * ks + 16 * half + 4 * lg;
-            f4 a4 = {1.f, 1.f, 1.f, 1.f}, k4 = {0.f, 0.f, 0.f, 0.f}, q4 = {0.f, 0.f, 0.f, 0.f};
-            if (valid) {
-                a4 = *reinterpret_cast<const f4*>(P.alpha + rowk + c);
-                k4 = Load4<F16>::f(k + rowk + c);
-                q4 = Load4<F16>::f(q + rowk + c);
+            for (int half = 0; half < 2; ++half) {
+                const int c = 32 * ks + 16 * half + 4 * lg;
+                araw[ks][half] = *reinterpret_cast<const f4*>(P.alpha + rowk + c);
+                kraw[ks][half] = R4::load(k + rowk + c);
+                qraw[ks][half] = R4::load(q + rowk + c);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                b[ks][4 * half + i] = a4[i];
-                kf[ks][4 * half + i] = k4[i];
-                qf[ks][4 * half + i] = q4[i];
-            }
-        }
     }
-    uint4 vreg[NV];
+    const float bet_raw = P.beta[static_cast<size_t>(t0 + min(r, rl)) * H + h];
 #pragma unroll
-    for (int jv = 0; jv < NV; ++jv) {
-        const int id = tid + 256 * jv;
-        const int rr = id / VROW16;
-        const int cc = (id - rr * VROW16) * EL16;
-        vreg[jv] = make_uint4(0, 0, 0, 0);
-        if (rr < len) vreg[jv] = *reinterpret_cast<const uint4*>(v + row_v(rr) + cc);
-    }
-    const float bet = valid ? P.beta[static_cast<size_t>(t0 + r) * H + h] : 0.f;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[ks][4 * half + i] = valid ? araw[ks][half][i] : 1.f;
+    const float bet = valid ? bet_raw : 0.f;
 
     // ---- (a) b = inclusive cumsum of log2(alpha) over the chunk's tokens -----
     // scan over the 16 tokens of this wave's block (lanes of one 16-lane row),
@@ -459,38 +478,37 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
     // one of them times a per-channel constant taken at the block's reference
     // token 16I+7 (lane 7 of the row) or its last token 16I+15 (lane 15):
     //   s_fac rows 0..3 2^ref_I, 4..7 2^-ref_I, 8..11 2^end_I, 12..15 2^-end_I
-    float rb[KS][8];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            b[ks][e] = fexp2(b[ks][e]);
-            rb[ks][e] = __builtin_amdgcn_rcpf(b[ks][e]);
-        }
+        for (int e = 0; e < 8; ++e) b[ks][e] = fexp2(b[ks][e]);
     if (lm == 7 || lm == 15) {
         float* d0 = s_fac + ((lm == 7 ? 0 : 8) + I) * DK + 4 * lg;
         float* d1 = d0 + 4 * DK;
+        auto rcp4 = [&](int ks, int o) {
+            return f4{__builtin_amdgcn_rcpf(b[ks][o]), __builtin_amdgcn_rcpf(b[ks][o + 1]),
+                      __builtin_amdgcn_rcpf(b[ks][o + 2]), __builtin_amdgcn_rcpf(b[ks][o + 3])};
+        };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             *reinterpret_cast<f4*>(d0 + 32 * ks) = f4{b[ks][0], b[ks][1], b[ks][2], b[ks][3]};
             *reinterpret_cast<f4*>(d0 + 32 * ks + 16) = f4{b[ks][4], b[ks][5], b[ks][6], b[ks][7]};
-            *reinterpret_cast<f4*>(d1 + 32 * ks) = f4{rb[ks][0], rb[ks][1], rb[ks][2], rb[ks][3]};
-            *reinterpret_cast<f4*>(d1 + 32 * ks + 16) = f4{rb[ks][4], rb[ks][5], rb[ks][6], rb[ks][7]};
+            *reinterpret_cast<f4*>(d1 + 32 * ks) = rcp4(ks, 0);
+            *reinterpret_cast<f4*>(d1 + 32 * ks + 16) = rcp4(ks, 4);
         }
     }
     __syncthreads();
-    // gamma and the rescaling table 2^(ref_I - end_J), J < I (all <= 1)
+    // gamma
     if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = s_fac[11 * DK + tid];
-    for (int id = tid; id < 6 * DK; id += 256) {
-        const int p = id / DK, c = id - p * DK;
-        const int Ii = p < 1 ? 1 : (p < 3 ? 2 : 3);
-        const int Jj = p - pair_index(Ii, 0);
-        s_g[id] = s_fac[Ii * DK + c] * s_fac[(12 + Jj) * DK + c];
-    }
 
     // ---- (b) every decay-dependent quantity of this lane's elements -----------
-    float Rk[KS][8], Rq[KS][8];   // row operands Gamma-rebased at token 16I+7 (fp32)
-    V Dc[KS];                     // block-diagonal column operand
+    // A[r][s] and P[r][s] (s <= r) take 2^(b_r - b_s) = 2^(b_r - ref_I) 2^(ref_I - b_s)
+    // for r in block I: the row operands (k, q) 2^(b - ref_I) are shared by
+    // every column block; the column operand k_s 2^(ref_I - b_s) (<= 1 below
+    // the diagonal block) is made by the wave that owns token s, for every
+    // later block I, and handed over through LDS.
+    V ra[KS], rq[KS];             // row operands, rebased at token 16I+7
+    V Dc[KS];                     // column operand of the diagonal block
     {
         E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
         auto fac4 = [&](int row, int ks, int half) {
@@ -498,35 +516,57 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
         };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            float qv[8], cv[8], kh[8], kt[8];
+            float qv[8], kh[8], kt[8], cl[3][8];
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
+                const f4 kw = R4::widen(kraw[ks][half]);
+                const f4 qw = R4::widen(qraw[ks][half]);
                 const f4 ref = fac4(I, ks, half);          // 2^ref_I
                 const f4 rref = fac4(4 + I, ks, half);     // 2^-ref_I
-                const f4 endi = fac4(8 + I, ks, half);     // 2^end_I
                 const f4 gam = fac4(11, ks, half);         // gamma = 2^end_3
+                f4 refl[3];                                // 2^ref of the later blocks
+#pragma unroll
+                for (int Il = 1; Il < 4; ++Il)
+                    if (Il > I) refl[Il - 1] = fac4(Il, ks, half);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int e = 4 * half + i;
-                    const float G = b[ks][e], rG = rb[ks][e], kv = kf[ks][e];
+                    const float G = b[ks][e], rG = __builtin_amdgcn_rcpf(G);
+                    const float kv = valid ? kw[i] : 0.f, qx = valid ? qw[i] : 0.f;
                     const float e1 = G * rref[i];                      // 2^(b - ref_I)
-                    Rk[ks][e] = kv * e1;
-                    Rq[ks][e] = qf[ks][e] * e1;
+                    ra[ks][e] = M::cvt(kv * e1);
+                    rq[ks][e] = M::cvt(qx * e1);
                     Dc[ks][e] = M::cvt(kv * (rG * ref[i]));           // k 2^(ref_I - b)
-                    cv[e] = kv * (rG * endi[i]);                       // k 2^(end_I - b)
+#pragma unroll
+                    for (int Il = 1; Il < 4; ++Il)
+                        if (Il > I) cl[Il - 1][e] = kv * (rG * refl[Il - 1][i]);
                     kh[e] = kv * G;
-                    qv[e] = qf[ks][e] * G;
+                    qv[e] = qx * G;
                     kt[e] = kv * (rG * gam[i]);                        // k gamma / Gamma
                 }
             }
             M::store8(qh + frag_off(I * KS + ks, lane), qv);
-            M::store8(s_C + frag_off(I * KS + ks, lane), cv);
-            const int c0 = 32 * ks + 4 * lg;
-            M::store4(s_khat + r * KP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
-            M::store4(s_khat + r * KP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
-            M::store4(s_Kt + r * KP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
-            M::store4(s_Kt + r * KP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
+#pragma unroll
+            for (int Il = 1; Il < 4; ++Il)
+                if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
+            // channel-major copies for the transposed operands of (d) and (f)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = chan(ks, e);
+                s_khat[c * XP + r] = M::cvt(kh[e]);
+                s_Kt[c * XP + r] = M::cvt(kt[e]);
+            }
         }
+    }
+    // v is first needed in (e); loading it here keeps it out of the
+    // registers of the phases above
+    uint4 vreg[NV];
+#pragma unroll
+    for (int jv = 0; jv < NV; ++jv) {
+        const int id = tid + 256 * jv;
+        const int rr = id / VROW16;
+        const int cc = (id - rr * VROW16) * EL16;
+        vreg[jv] = *reinterpret_cast<const uint4*>(v + row_v(min(rr, rl)) + cc);
     }
     __syncthreads();
 
@@ -541,29 +581,9 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
                 f4 accA = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    V ra, rq, col;
-                    if (J == I) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            ra[e] = M::cvt(Rk[ks][e]);
-                            rq[e] = M::cvt(Rq[ks][e]);
-                        }
-                        col = Dc[ks];
-                    } else {
-                        const float* gp = s_g + pair_index(I, J) * DK + 32 * ks + 4 * lg;
-                        const f4 g0 = *reinterpret_cast<const f4*>(gp);
-                        const f4 g1 = *reinterpret_cast<const f4*>(gp + 16);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            ra[e] = M::cvt(Rk[ks][e] * g0[e]);
-                            rq[e] = M::cvt(Rq[ks][e] * g0[e]);
-                            ra[4 + e] = M::cvt(Rk[ks][4 + e] * g1[e]);
-                            rq[4 + e] = M::cvt(Rq[ks][4 + e] * g1[e]);
-                        }
-                        col = M::load8(s_C + frag_off(J * KS + ks, lane));
-                    }
-                    accA = M::mma(ra, col, accA);
-                    accP[J] = M::mma(col, rq, accP[J]);
+                    const V col = J == I ? Dc[ks] : M::load8(s_C + frag_off(pair_index(I, J) * KS + ks, lane));
+                    accA = M::mma(ra[ks], col, accA);
+                    accP[J] = M::mma(col, rq[ks], accP[J]);
                 }
                 // lane (lm, lg) holds A[16I + 4lg + i][16J + lm]; store A^T rows
                 const int s = 16 * J + lm;
@@ -596,10 +616,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
         for (int id = tid; id < DK * 2 * 4; id += 256) {
             const int m = id & 15, jj = (id >> 4) & 3, f = id >> 6;
             const int c = 16 * (f >> 1) + m, ts = f & 1;
-            float kv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kv[e] = M::tof(s_Kt[(32 * ts + frag_k(jj, e)) * KP + c]);
-            M::store8(ktt + frag_off(f, id & 63), kv);
+            const E* src = s_Kt + c * XP + 32 * ts + 4 * jj;     // tokens frag_k(jj, 0..7)
+            M::storeV(ktt + frag_off(f, id & 63), M::load4x2(src, src + 16));
         }
     }
     __syncthreads();
@@ -611,7 +629,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
             const int id = tid + 256 * jv;
             const int rr = id / VROW16;
             const int cc = (id - rr * VROW16) * EL16;
-            *reinterpret_cast<uint4*>(s_v + rr * VP + cc) = vreg[jv];
+            // V^T in the operand type, rows past the chunk's end as zeros
+            const A* vv = reinterpret_cast<const A*>(&vreg[jv]);
+#pragma unroll
+            for (int e = 0; e < EL16; ++e) {
+                float x;
+                if constexpr (F16) x = bf16_to_f32(vv[e]);
+                else x = vv[e];
+                s_v[(cc + e) * XP + (rr ^ vswz(cc + e))] = M::cvt(rr < len ? x : 0.f);
+            }
         }
         // diagonal 16x16 blocks, column-oriented forward substitution: once
         // x[s] is final, every later row takes its contribution
@@ -655,10 +681,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
             __syncthreads();
         }
         // T Diag(beta), zero above the diagonal, in the operand type
-        for (int id = tid; id < C * C; id += 256) {
-            const int rr = id / C;
-            const int s = id - rr * C;
-            s_Tp[rr * TPP + s] = M::cvt(s <= rr ? s_T[rr * TP + s] * s_beta[s] : 0.f);
+        for (int id = tid; id < C * C / 4; id += 256) {
+            const int rr = id / (C / 4);
+            const int s0 = 4 * (id - rr * (C / 4));
+            const f4 t = *reinterpret_cast<const f4*>(s_T + rr * TP + s0);
+            const f4 bt = *reinterpret_cast<const f4*>(s_beta + s0);
+            f4 x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = s0 + i <= rr ? t[i] * bt[i] : 0.f;
+            M::store4(s_Tp + rr * TPP + s0, x);
         }
         __syncthreads();
     }
@@ -677,12 +708,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
             for (int kt = 0; kt < kmax; ++kt) {
                 const int t = 32 * kt + 8 * lg;
                 const V bT = M::load8(s_Tp + (16 * Ib + lm) * TPP + t);
-                V a0, a1;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    a0[e] = s_khat[(t + e) * KP + 32 * ksc + lm];
-                    a1[e] = s_khat[(t + e) * KP + 32 * ksc + 16 + lm];
-                }
+                const V a0 = M::load8(s_khat + (32 * ksc + lm) * XP + t);
+                const V a1 = M::load8(s_khat + (32 * ksc + 16 + lm) * XP + t);
                 acc0 = M::mma(a0, bT, acc0);
                 acc1 = M::mma(a1, bT, acc1);
             }
@@ -699,12 +726,7 @@ __global__ __launch_bounds__(256) void prep_kernel(const PrepParams P) {
                 for (int ks = 0; ks < kmax; ++ks) {
                     const int t = 32 * ks + 8 * lg;
                     const V a = M::load8(s_Tp + (16 * Ib + lm) * TPP + t);
-                    V bv;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        if constexpr (F16) bv[e] = M::cvt(bf16_to_f32(s_v[(t + e) * VP + c]));
-                        else bv[e] = s_v[(t + e) * VP + c];
-                    }
+                    const V bv = M::load8(s_v + c * XP + (t ^ vswz(c)));
                     acc = M::mma(a, bv, acc);
                 }
                 M::store4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc);
@@ -1038,6 +1060,8 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         pp.ctrl = ctrl; pp.table = table;
         pp.rec = ws + pl.off_rec; pp.rec_bytes = pl.rec_bytes; pp.gmax = pl.gmax;
         pp.H = pl.H;
+        pp.T = pl.varlen ? 0 : pl.T;
+        pp.cps = static_cast<int>((pl.T + C - 1) / C);
         constexpr int lds = PrepLds<DK, DV, F16>::bytes;
         auto kfn = prep_kernel<DK, DV, F16>;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
