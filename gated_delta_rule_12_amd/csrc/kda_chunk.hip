@@ -89,6 +89,25 @@ template <> struct Mx<true> {
         *reinterpret_cast<h4*>(p) = h;
     }
     static __device__ __forceinline__ void storeV(E* p, const V& v) { *reinterpret_cast<V*>(p) = v; }
+    // Transposed operand read from a row-major LDS tile M (row stride ld):
+    // element e of lane (j = l % 16) is M[ra + e][c0 + j] for e < 4 and
+    // M[rb + e - 4][c0 + j] for e >= 4.  Within each 16-lane group, the
+    // transposing LDS read hands lane j element j % 4 of the 64-bit words read
+    // by lanes 4k + j / 4 (k = 0..3); lane s therefore points at row
+    // (ra + s / 4), columns c0 + 4 (s % 4) .. + 3.
+    static __device__ __forceinline__ V loadT(const E* M, int ld, int ra, int rb, int c0, int j) {
+        typedef short s4 __attribute__((ext_vector_type(4)));
+        const int off = (j >> 2) * ld + c0 + 4 * (j & 3);
+        const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(M + ra * ld + off));
+        const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4*)(M + rb * ld + off));
+        const h4 l4 = __builtin_bit_cast(h4, lo), h4v = __builtin_bit_cast(h4, hi);
+        V v;
+        v[0] = l4[0]; v[1] = l4[1]; v[2] = l4[2]; v[3] = l4[3];
+        v[4] = h4v[0]; v[5] = h4v[1]; v[6] = h4v[2]; v[7] = h4v[3];
+        return v;
+    }
     static __device__ __forceinline__ void store8(E* p, const float* x) {
         h8 h;
 #pragma unroll
@@ -130,6 +149,16 @@ template <> struct Mx<false> {
     static __device__ __forceinline__ void storeV(E* p, const V& v) {
         *reinterpret_cast<f4*>(p) = f4{v[0], v[1], v[2], v[3]};
         *reinterpret_cast<f4*>(p + 4) = f4{v[4], v[5], v[6], v[7]};
+    }
+    // same element order as the 16-bit variant, by plain reads
+    static __device__ __forceinline__ V loadT(const E* M, int ld, int ra, int rb, int c0, int j) {
+        V v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = M[(ra + e) * ld + c0 + j];
+            v[4 + e] = M[(rb + e) * ld + c0 + j];
+        }
+        return v;
     }
     static __device__ __forceinline__ void store8(E* p, const float* x) {
         f4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
@@ -314,16 +343,17 @@ struct PrepLds {
     using A = typename Act<F16>::T;   // raw activation element
     using E = typename Mx<F16>::E;    // matrix-core operand element
     static constexpr int KS = DK / 32;
-    static constexpr int XP = C + 8;         // row stride of the channel-major K-hat, K~ and v
+    static constexpr int KXP = DK + 16;      // row stride of the token-major K-hat and K~
+    static constexpr int VXP = DV + 16;      // row stride of the token-major V
     static constexpr int ATP = C + 4;        // fp32 row stride of A^T ([s][r])
     static constexpr int TP = C + 4;         // fp32 row stride of T
     static constexpr int TPP = C + 8;        // row stride of T Diag(beta) (operand type)
     // region a: column operands of the six blocks below the diagonal, later T (fp32)
     static constexpr int RA = CMax<6 * KS * 64 * 8 * (int)sizeof(E), C * TP * 4>::value;
-    // region b: K~^T [channel][token], later V^T [column][token] (operand type)
-    static constexpr int RB = CMax<DK, DV>::value * XP * (int)sizeof(E);
-    // region c: K-hat^T [channel][token]
-    static constexpr int RC = DK * XP * (int)sizeof(E);
+    // region b: K~ [token][channel], later V [token][column] (operand type)
+    static constexpr int RB = CMax<C * KXP, C * VXP>::value * (int)sizeof(E);
+    // region c: K-hat [token][channel]
+    static constexpr int RC = C * KXP * (int)sizeof(E);
     // region d: A^T (fp32), later T Diag(beta)
     static constexpr int RD = CMax<C * ATP * 4, C * TPP * (int)sizeof(E)>::value;
     // small: beta [64]
@@ -366,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     using E = typename M::E;
     using V = typename M::V;
     using R = Rec<DK, DV, F16>;
-    constexpr int KS = L::KS, XP = L::XP, ATP = L::ATP, TP = L::TP, TPP = L::TPP;
+    constexpr int KS = L::KS, KXP = L::KXP, VXP = L::VXP, ATP = L::ATP, TP = L::TP, TPP = L::TPP;
     constexpr int EL16 = 16 / (int)sizeof(A);              // activations per 16 bytes
     constexpr int VROW16 = DV / EL16;
     constexpr int NV = C * VROW16 / 256;
@@ -392,9 +422,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     extern __shared__ __align__(16) unsigned char lds[];
     E* s_C = reinterpret_cast<E*>(lds);                                 // column fragments
     float* s_T = reinterpret_cast<float*>(lds);                         // after s_C is dead
-    E* s_Kt = reinterpret_cast<E*>(lds + L::RA);                        // K~^T [channel][token]
-    E* s_v = reinterpret_cast<E*>(lds + L::RA);                         // V^T, after s_Kt is dead
-    E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat^T [channel][token]
+    E* s_Kt = reinterpret_cast<E*>(lds + L::RA);                        // K~ [token][channel]
+    E* s_v = reinterpret_cast<E*>(lds + L::RA);                         // V, after s_Kt is dead
+    E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat [token][channel]
     float* s_AT = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC);
     E* s_Tp = reinterpret_cast<E*>(lds + L::RA + L::RB + L::RC);        // after A^T is dead
     float* s_tot = s_AT;                                                // [4][DK], until (c)
@@ -414,10 +444,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     const A* __restrict__ k = static_cast<const A*>(P.k);
     const A* __restrict__ v = static_cast<const A*>(P.v);
     auto row_v = [&](int rr) { return (static_cast<size_t>(t0 + rr) * H + h) * DV; };
-    // V^T rows: token groups of 8 are XOR-swizzled by the column's group of
-    // 8, so that the 16 lanes staging one token (8 columns apart) spread over
-    // the LDS banks; the 16-byte operand reads stay contiguous.
-    auto vswz = [](int c) { return 8 * ((c >> 3) & 7); };
+
     // Lane (lm, lg) owns token r and, in reduction step ks, the channels
     // 32ks + frag_k(lg, e): two runs of four, at 32ks + 4lg and 32ks + 16 + 4lg.
     auto chan = [&](int ks, int e) { return 32 * ks + frag_k(lg, e); };
@@ -549,13 +576,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
 #pragma unroll
             for (int Il = 1; Il < 4; ++Il)
                 if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
-            // channel-major copies for the transposed operands of (d) and (f)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = chan(ks, e);
-                s_khat[c * XP + r] = M::cvt(kh[e]);
-                s_Kt[c * XP + r] = M::cvt(kt[e]);
-            }
+            const int c0 = 32 * ks + 4 * lg;
+            M::store4(s_khat + r * KXP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
+            M::store4(s_khat + r * KXP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
+            M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
+            M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
         }
     }
     // v is first needed in (e); loading it here keeps it out of the
@@ -614,10 +639,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     {
         E* __restrict__ ktt = reinterpret_cast<E*>(rec + R::KTT);
         for (int id = tid; id < DK * 2 * 4; id += 256) {
-            const int m = id & 15, jj = (id >> 4) & 3, f = id >> 6;
-            const int c = 16 * (f >> 1) + m, ts = f & 1;
-            const E* src = s_Kt + c * XP + 32 * ts + 4 * jj;     // tokens frag_k(jj, 0..7)
-            M::storeV(ktt + frag_off(f, id & 63), M::load4x2(src, src + 16));
+            const int jj = (id >> 4) & 3, f = id >> 6;
+            const int ts = f & 1;
+            // channel 16 (f >> 1) + lane % 16, tokens 32 ts + frag_k(jj, 0..7)
+            M::storeV(ktt + frag_off(f, id & 63),
+                      M::loadT(s_Kt, KXP, 32 * ts + 4 * jj, 32 * ts + 16 + 4 * jj, 16 * (f >> 1), lm));
         }
     }
     __syncthreads();
@@ -629,15 +655,17 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             const int id = tid + 256 * jv;
             const int rr = id / VROW16;
             const int cc = (id - rr * VROW16) * EL16;
-            // V^T in the operand type, rows past the chunk's end as zeros
+            // V in the operand type, rows past the chunk's end as zeros
             const A* vv = reinterpret_cast<const A*>(&vreg[jv]);
+            float x[EL16];
 #pragma unroll
             for (int e = 0; e < EL16; ++e) {
-                float x;
-                if constexpr (F16) x = bf16_to_f32(vv[e]);
-                else x = vv[e];
-                s_v[(cc + e) * XP + (rr ^ vswz(cc + e))] = M::cvt(rr < len ? x : 0.f);
+                if constexpr (F16) x[e] = bf16_to_f32(vv[e]);
+                else x[e] = vv[e];
+                if (rr >= len) x[e] = 0.f;
             }
+            if constexpr (F16) M::store8(s_v + rr * VXP + cc, x);
+            else M::store4(s_v + rr * VXP + cc, f4{x[0], x[1], x[2], x[3]});
         }
         // diagonal 16x16 blocks, column-oriented forward substitution: once
         // x[s] is final, every later row takes its contribution
@@ -708,8 +736,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             for (int kt = 0; kt < kmax; ++kt) {
                 const int t = 32 * kt + 8 * lg;
                 const V bT = M::load8(s_Tp + (16 * Ib + lm) * TPP + t);
-                const V a0 = M::load8(s_khat + (32 * ksc + lm) * XP + t);
-                const V a1 = M::load8(s_khat + (32 * ksc + 16 + lm) * XP + t);
+                const V a0 = M::loadT(s_khat, KXP, t, t + 4, 32 * ksc, lm);
+                const V a1 = M::loadT(s_khat, KXP, t, t + 4, 32 * ksc + 16, lm);
                 acc0 = M::mma(a0, bT, acc0);
                 acc1 = M::mma(a1, bT, acc1);
             }
@@ -726,7 +754,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
                 for (int ks = 0; ks < kmax; ++ks) {
                     const int t = 32 * ks + 8 * lg;
                     const V a = M::load8(s_Tp + (16 * Ib + lm) * TPP + t);
-                    const V bv = M::load8(s_v + c * XP + (t ^ vswz(c)));
+                    const V bv = M::loadT(s_v, VXP, t, t + 4, 16 * nt, lm);
                     acc = M::mma(a, bv, acc);
                 }
                 M::store4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc);
