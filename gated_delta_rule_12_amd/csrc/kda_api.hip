@@ -97,7 +97,8 @@ kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const
     if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
     if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
     if (!supported_head(Dk) || !supported_head(Dv)) return KDA_ERROR_NOT_SUPPORTED;
-    if ((int64_t)N * H > 0x7fffffffLL) return KDA_ERROR_NOT_SUPPORTED;
+    // one workgroup per (sequence, head, block of up to 64 value columns)
+    if ((int64_t)N * H * 2 > 0x7fffffffLL) return KDA_ERROR_NOT_SUPPORTED;
     if (N == 0) return KDA_SUCCESS;
     if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned4(beta) ||

@@ -11,13 +11,17 @@
 // memory-bound token-by-token mode that "Linear Attention + Sparse
 // Attention...", section 6, asks to benchmark apart from prefill.)
 //
-// Mapping: one 256-thread workgroup per (sequence, head).  The Dk x Dv fp32
-// state (64 KiB at 128 x 128) is held in registers between the read and the
-// write.  Thread (rg, cg) owns columns 4cg..4cg+3 of rows rg, rg+RG, ...:
-// one load instruction of the workgroup covers RG whole rows (contiguous
-// bytes), each lane moving 16 B.  Column sums over the key channels are
-// reduced with cross-lane shuffles inside a wavefront, then through LDS
-// across the four wavefronts.  State traffic bypasses the caches
+// Mapping: one 256-thread workgroup per (sequence, head, block of CB value
+// columns).  The columns of S evolve independently (decay and write act on
+// rows), and the projections p and r reduce over rows, so a column block is
+// a self-contained task: its slice of the state (32 KiB at DK = 128,
+// CB = 64) is held in registers between the read and the write.  Smaller
+// slices than a whole head keep more workgroups in flight per CU, so that
+// the reads of some overlap the writes of others.  Thread (rg, cg) owns
+// columns 4cg..4cg+3 of the block in rows rg, rg+RG, ...: one load
+// instruction of the workgroup covers RG row segments.  Column sums over the
+// key channels are reduced with cross-lane shuffles inside a wavefront, then
+// through LDS across the four wavefronts.  State traffic bypasses the caches
 // (non-temporal): it is touched exactly twice per step.
 #include "kda_common.h"
 
@@ -26,35 +30,46 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int DK, int DV, bool ABF16, bool OBF16>
-__global__ __launch_bounds__(256) void decode_kernel(
+// value columns and threads per workgroup
+#ifndef KDA_DECODE_CB
+#define KDA_DECODE_CB 64
+#endif
+#ifndef KDA_DECODE_NT
+#define KDA_DECODE_NT 256
+#endif
+constexpr int kDecodeThreads = KDA_DECODE_NT;
+
+template <int DK, int DV, int CB, bool ABF16, bool OBF16>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const typename Act<ABF16>::T* __restrict__ q, const typename Act<ABF16>::T* __restrict__ k,
     const typename Act<ABF16>::T* __restrict__ v, const float* __restrict__ alpha,
     const float* __restrict__ beta, float* __restrict__ state, void* __restrict__ o) {
-    constexpr int CG = DV / 4;            // column groups of 4 floats
-    constexpr int RG = 256 / CG;          // row groups
+    constexpr int NCB = DV / CB;          // column blocks per (sequence, head)
+    constexpr int CG = CB / 4;            // column groups of 4 floats
+    constexpr int RG = kDecodeThreads / CG;   // row groups
     constexpr int RPT = DK / RG;          // rows per thread
-    constexpr int NW = 4;                 // wavefronts per workgroup
-    static_assert(RG * CG == 256 && RPT * RG == DK && CG <= 64, "decode tiling");
+    constexpr int NW = kDecodeThreads / 64;   // wavefronts per workgroup
+    static_assert(NCB * CB == DV && RG * CG == kDecodeThreads && RPT * RG == DK && CG <= 64, "decode tiling");
 
     const int tid = threadIdx.x;
     const int cg = tid % CG;
     const int rg = tid / CG;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const size_t pair = blockIdx.x;       // n * H + h
+    const size_t pair = blockIdx.x / NCB; // n * H + h
+    const int col0 = (blockIdx.x - static_cast<int>(pair) * NCB) * CB;
 
     __shared__ float s_k[DK], s_q[DK], s_a[DK];
     __shared__ f4 s_red[2][NW][CG];
     __shared__ float s_qk;
 
     // Issue the state loads first: they are the only HBM-heavy traffic.
-    f4* sp = reinterpret_cast<f4*>(state + pair * (size_t)(DK * DV));
+    f4* sp = reinterpret_cast<f4*>(state + pair * (size_t)(DK * DV) + col0);
     f4 s[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&sp[(i * RG + rg) * CG + cg]);
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(&sp[(i * RG + rg) * (DV / 4) + cg]);
 
-    for (int c = tid; c < DK; c += 256) {
+    for (int c = tid; c < DK; c += kDecodeThreads) {
         s_k[c] = Act<ABF16>::load(k, pair * DK + c);
         s_q[c] = Act<ABF16>::load(q, pair * DK + c);
         s_a[c] = alpha[pair * DK + c];
@@ -102,20 +117,20 @@ __global__ __launch_bounds__(256) void decode_kernel(
     const float b = beta[pair];
     f4 vv;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vv[j] = Act<ABF16>::load(v, pair * DV + 4 * cg + j);
+    for (int j = 0; j < 4; ++j) vv[j] = Act<ABF16>::load(v, pair * DV + col0 + 4 * cg + j);
     const f4 d = b * (vv - p);
 
     if (rg == 0) {
         const f4 out = rr + s_qk * d;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) store_out<OBF16>(o, pair * DV + 4 * cg + j, out[j]);
+        for (int j = 0; j < 4; ++j) store_out<OBF16>(o, pair * DV + col0 + 4 * cg + j, out[j]);
     }
 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int r = i * RG + rg;
         s[i] += s_k[r] * d;
-        __builtin_nontemporal_store(s[i], &sp[(i * RG + rg) * CG + cg]);
+        __builtin_nontemporal_store(s[i], &sp[(i * RG + rg) * (DV / 4) + cg]);
     }
 }
 
@@ -123,7 +138,8 @@ template <int DK, int DV, bool ABF16, bool OBF16>
 hipError_t launch(const void* q, const void* k, const void* v, const float* alpha,
                   const float* beta, float* state, void* o, int pairs, hipStream_t stream) {
     using T = typename Act<ABF16>::T;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, ABF16, OBF16>), dim3(pairs), dim3(256), 0, stream,
+    constexpr int CB = KDA_DECODE_CB < DV ? KDA_DECODE_CB : DV;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, CB, ABF16, OBF16>), dim3(pairs * (DV / CB)), dim3(kDecodeThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                        alpha, beta, state, o);
     return hipGetLastError();
