@@ -100,6 +100,39 @@ def copy_calibration(torch):
                       "launches": 3}))
 
 
+def measured_peaks(torch):
+    """Achievable references on this GPU, reported beside the vendor peaks:
+    a 512 MiB device-to-device copy (read + write bytes) and a dense bf16
+    8192^3 matrix product through torch (hipBLASLt)."""
+    res = {}
+    n = 512 << 20
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        b.copy_(a)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    res["copy_GBps"] = round(2 * n * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    y = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        torch.mm(x, y)
+    e0.record()
+    for _ in range(10):
+        torch.mm(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    res["bf16_matmul_TFLOPs"] = round(2 * m ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12, 1)
+    res["note"] = "achievable references measured on this GPU (copy = read + write bytes)"
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -220,6 +253,8 @@ def main():
             cfg["workload"] = wd.name
 
     out["config"] = cfg
+    if args.only is None:
+        out["measured_peaks"] = measured_peaks(torch)
     traffic = measured_traffic()
     if traffic is not None:
         if do_fwd:

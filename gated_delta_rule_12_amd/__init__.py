@@ -9,9 +9,15 @@ missing the first call raises.
 Functions carry the C names:
 
 * ``kda_chunk_fwd``                 chunkwise forward (prefill / training forward)
+* ``kda_chunk_fwd_gated``           the same with the gate in any ``kda_gate`` form
 * ``kda_chunk_fwd_workspace_bytes`` workspace size of a chunkwise forward
 * ``kda_recurrent_step``            one decode step, state updated in place
+* ``kda_recurrent_step_gated``      the same with the gate in any ``kda_gate`` form
 * ``kda_status_string``             name of a status code
+
+The Python ``kda_chunk_fwd`` / ``kda_recurrent_step`` take ``gate=`` ("alpha",
+"softplus" or "scalar") and call the ``*_gated`` entry points for the other
+two forms.
 """
 from __future__ import annotations
 
@@ -33,8 +39,13 @@ KDA_ERROR_LAUNCH = 4
 KDA_DTYPE_F32 = 0
 KDA_DTYPE_BF16 = 1
 
+KDA_GATE_ALPHA = 0
+KDA_GATE_SOFTPLUS_BF16 = 1
+KDA_GATE_SCALAR = 2
+_GATES = {"alpha": KDA_GATE_ALPHA, "softplus": KDA_GATE_SOFTPLUS_BF16, "scalar": KDA_GATE_SCALAR}
+
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-            "kda_recurrent_step")
+            "kda_chunk_fwd_gated", "kda_recurrent_step", "kda_recurrent_step_gated")
 
 _lib = None
 
@@ -61,9 +72,15 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd.restype = i32
         L.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                     i32, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.kda_chunk_fwd_gated.restype = i32
+        L.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                          i32, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kda_recurrent_step.restype = i32
         L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                          i32, i32, vp]
+        L.kda_recurrent_step_gated.restype = i32
+        L.kda_recurrent_step_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32,
+                                               i32, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -108,11 +125,14 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
                   final_state=None, cu_seqlens: Optional[torch.Tensor] = None,
                   o: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                   workspace: Optional[torch.Tensor] = None, chunk_size: int = 64,
-                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                  stream=None, gate: str = "alpha") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA forward on the GPU.
 
-    q, k, alpha [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H]; initial_state
+    q, k [B,T,H,Dk]; v [B,T,H,Dv]; beta [B,T,H]; initial_state
     [N,H,Dk,Dv] fp32 or None; cu_seqlens int32 [N+1] (B == 1) or None.
+    ``alpha`` is the forget gate in the form ``gate``: "alpha" (fp32
+    [B,T,H,Dk]), "softplus" (bf16 pre-activation x [B,T,H,Dk], log alpha =
+    -softplus(x)) or "scalar" (fp32 [B,T,H], one alpha per token and head).
     ``final_state``: None (not computed), True (allocate) or an fp32 tensor
     [N,H,Dk,Dv] (may be ``initial_state`` itself, updated in place).
     Returns (o, final_state or None).
@@ -134,30 +154,49 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                             _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
-                             _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(out_dtype),
-                             _ptr(workspace), ws_bytes, _stream(stream))
+    g = _GATES[gate]
+    if g == KDA_GATE_ALPHA:
+        st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                 _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
+                                 _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(out_dtype),
+                                 _ptr(workspace), ws_bytes, _stream(stream))
+        where = "kda_chunk_fwd"
+    else:
+        st = lib().kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), g, _ptr(beta),
+                                       _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
+                                       _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(out_dtype),
+                                       _ptr(workspace), ws_bytes, _stream(stream))
+        where = "kda_chunk_fwd_gated"
     if st != KDA_SUCCESS:
-        raise KDAError(st, "kda_chunk_fwd")
+        raise KDAError(st, where)
     return o, final_state
 
 
 def kda_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
                        beta: torch.Tensor, state: torch.Tensor, o: Optional[torch.Tensor] = None,
-                       out_dtype: Optional[torch.dtype] = None, stream=None) -> torch.Tensor:
+                       out_dtype: Optional[torch.dtype] = None, stream=None,
+                       gate: str = "alpha") -> torch.Tensor:
     """One KDA decode step on the GPU; ``state`` [N,H,Dk,Dv] fp32 is updated in place.
 
-    q, k, alpha [N,H,Dk]; v [N,H,Dv]; beta [N,H].  Returns o [N,H,Dv].
+    q, k [N,H,Dk]; v [N,H,Dv]; beta [N,H]; ``alpha`` in the form ``gate``
+    (as for kda_chunk_fwd: [N,H,Dk], or [N,H] for "scalar").  Returns o [N,H,Dv].
     """
     N, H, Dk = q.shape
     Dv = v.shape[-1]
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if o is None:
         o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
-    st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                                  _ptr(state), _ptr(o), N, H, Dk, Dv, _dt(q.dtype),
-                                  _dt(out_dtype), _stream(stream))
+    g = _GATES[gate]
+    if g == KDA_GATE_ALPHA:
+        st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(state), _ptr(o), N, H, Dk, Dv, _dt(q.dtype),
+                                      _dt(out_dtype), _stream(stream))
+        where = "kda_recurrent_step"
+    else:
+        st = lib().kda_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), g, _ptr(beta),
+                                            _ptr(state), _ptr(o), N, H, Dk, Dv, _dt(q.dtype),
+                                            _dt(out_dtype), _stream(stream))
+        where = "kda_recurrent_step_gated"
     if st != KDA_SUCCESS:
-        raise KDAError(st, "kda_recurrent_step")
+        raise KDAError(st, where)
     return o

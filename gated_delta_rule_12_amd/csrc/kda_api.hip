@@ -9,7 +9,19 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+bool valid_gate(kda_gate g) {
+    return g == KDA_GATE_ALPHA || g == KDA_GATE_SOFTPLUS_BF16 || g == KDA_GATE_SCALAR;
+}
+
+// alignment the kernels' gate loads need: 16 B (fp32 x 4), 8 B (bf16 x 4), 4 B
+bool gate_aligned(const void* p, kda_gate g) {
+    if (g == KDA_GATE_ALPHA) return aligned16(p);
+    if (g == KDA_GATE_SOFTPLUS_BF16) return aligned8(p);
+    return aligned4(p);
+}
 
 bool supported_head(int d) { return d == 64 || d == 128; }
 
@@ -53,7 +65,19 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
                          int H, int Dk, int Dv, int chunk_size, kda_dtype act_dtype,
                          kda_dtype out_dtype, void* workspace, size_t workspace_bytes,
                          void* stream) {
-    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype)) return KDA_ERROR_INVALID_VALUE;
+    return kda_chunk_fwd_gated(q, k, v, alpha, KDA_GATE_ALPHA, beta, initial_state, final_state,
+                               cu_seqlens, num_seqs, o, B, T, H, Dk, Dv, chunk_size, act_dtype,
+                               out_dtype, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, const void* gate,
+                               kda_gate gate_kind, const float* beta, const float* initial_state,
+                               float* final_state, const int32_t* cu_seqlens, int num_seqs,
+                               void* o, int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
+                               kda_dtype act_dtype, kda_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate_kind))
+        return KDA_ERROR_INVALID_VALUE;
     if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens != nullptr && (B != 1 || num_seqs < 0)) return KDA_ERROR_INVALID_VALUE;
@@ -66,8 +90,8 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 
     const bool has_tokens = (int64_t)B * T > 0;
     if (has_tokens) {
-        if (!q || !k || !v || !alpha || !beta || !o) return KDA_ERROR_INVALID_VALUE;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) ||
+        if (!q || !k || !v || !gate || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !gate_aligned(gate, gate_kind) ||
             !aligned4(beta) || !aligned16(o))
             return KDA_ERROR_INVALID_VALUE;
     }
@@ -82,7 +106,7 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
     }
 
     kda::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.gate_kind = gate_kind; a.beta = beta;
     a.initial_state = initial_state; a.final_state = final_state;
     a.cu_seqlens = cu_seqlens; a.o = o; a.workspace = workspace;
     a.act_bf16 = act_dtype == KDA_DTYPE_BF16;
@@ -93,18 +117,28 @@ kda_status kda_chunk_fwd(const void* q, const void* k, const void* v, const floa
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, float* state, void* o, int N, int H, int Dk,
                               int Dv, kda_dtype act_dtype, kda_dtype out_dtype, void* stream) {
-    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype)) return KDA_ERROR_INVALID_VALUE;
+    return kda_recurrent_step_gated(q, k, v, alpha, KDA_GATE_ALPHA, beta, state, o, N, H, Dk, Dv,
+                                    act_dtype, out_dtype, stream);
+}
+
+kda_status kda_recurrent_step_gated(const void* q, const void* k, const void* v, const void* gate,
+                                    kda_gate gate_kind, const float* beta, float* state, void* o,
+                                    int N, int H, int Dk, int Dv, kda_dtype act_dtype,
+                                    kda_dtype out_dtype, void* stream) {
+    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate_kind))
+        return KDA_ERROR_INVALID_VALUE;
     if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
     if (N < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
     if (!supported_head(Dk) || !supported_head(Dv)) return KDA_ERROR_NOT_SUPPORTED;
     // one workgroup per (sequence, head, block of up to 64 value columns)
     if ((int64_t)N * H * 2 > 0x7fffffffLL) return KDA_ERROR_NOT_SUPPORTED;
     if (N == 0) return KDA_SUCCESS;
-    if (!q || !k || !v || !alpha || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(alpha) || !aligned4(beta) ||
-        !aligned16(state) || !aligned16(o))
+    if (!q || !k || !v || !gate || !beta || !state || !o) return KDA_ERROR_INVALID_VALUE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !gate_aligned(gate, gate_kind) ||
+        !aligned4(beta) || !aligned16(state) || !aligned16(o))
         return KDA_ERROR_INVALID_VALUE;
-    return from_hip(kda::launch_recurrent_step(q, k, v, alpha, beta, state, o, N, H, Dk, Dv,
+    return from_hip(kda::launch_recurrent_step(q, k, v, gate, static_cast<int>(gate_kind), beta,
+                                               state, o, N, H, Dk, Dv,
                                                act_dtype == KDA_DTYPE_BF16,
                                                out_dtype == KDA_DTYPE_BF16,
                                                static_cast<hipStream_t>(stream)));

@@ -41,7 +41,9 @@ struct ChunkPlan {
 
 struct ChunkArgs {
     const void *q = nullptr, *k = nullptr, *v = nullptr;
-    const float *alpha = nullptr, *beta = nullptr;
+    const void* gate = nullptr;               // forget gate, in the form gate_kind
+    kda_gate gate_kind = KDA_GATE_ALPHA;
+    const float* beta = nullptr;
     const float* initial_state = nullptr;
     float* final_state = nullptr;
     const int32_t* cu_seqlens = nullptr;

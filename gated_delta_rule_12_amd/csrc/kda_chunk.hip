@@ -295,7 +295,7 @@ struct PrepParams {
     const void* q;
     const void* k;
     const void* v;
-    const float* alpha;
+    const void* gate;         // forget gate in the form of the kernel's GATE (kda_gate)
     const float* beta;
     const int32_t* ctrl;
     const int4* table;
@@ -388,7 +388,7 @@ __device__ __forceinline__ float row_scan16(float x) {
 // (I, J) with J < I -> index into the rescaling table
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
-template <int DK, int DV, bool F16>
+template <int DK, int DV, bool F16, int GATE>
 __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     using L = PrepLds<DK, DV, F16>;
     using A = typename L::A;
@@ -457,37 +457,59 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     const int rl = len - 1;
     float b[KS][8];
     typename R4::T kraw[KS][2], qraw[KS][2];
-    f4 araw[KS][2];
+    // the gate as given: fp32 alpha or bf16 pre-activation per channel, or one
+    // fp32 alpha per token
+    using GRaw = typename Raw4<GATE == KDA_GATE_SOFTPLUS_BF16>::T;
+    GRaw graw[KS][2];
+    float gscalar = 1.f;
     {
-        const size_t rowk = (static_cast<size_t>(t0 + min(r, rl)) * H + h) * DK;
+        const size_t rowt = static_cast<size_t>(t0 + min(r, rl)) * H + h;
+        const size_t rowk = rowt * DK;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 const int c = 32 * ks + 16 * half + 4 * lg;
-                araw[ks][half] = *reinterpret_cast<const f4*>(P.alpha + rowk + c);
+                if constexpr (GATE == KDA_GATE_ALPHA)
+                    graw[ks][half] = *reinterpret_cast<const f4*>(static_cast<const float*>(P.gate) + rowk + c);
+                else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16)
+                    graw[ks][half] = Raw4<true>::load(static_cast<const uint16_t*>(P.gate) + rowk + c);
                 kraw[ks][half] = R4::load(k + rowk + c);
                 qraw[ks][half] = R4::load(q + rowk + c);
             }
+        if constexpr (GATE == KDA_GATE_SCALAR) gscalar = static_cast<const float*>(P.gate)[rowt];
     }
     const float bet_raw = P.beta[static_cast<size_t>(t0 + min(r, rl)) * H + h];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) b[ks][4 * half + i] = valid ? araw[ks][half][i] : 1.f;
     const float bet = valid ? bet_raw : 0.f;
 
     // ---- (a) b = inclusive cumsum of log2(alpha) over the chunk's tokens -----
     // scan over the 16 tokens of this wave's block (lanes of one 16-lane row),
     // then add the totals of the earlier blocks
+    // log2(alpha) of this lane's elements (0 past the chunk's end), scanned
+    if constexpr (GATE == KDA_GATE_SCALAR) {
+        const float x = row_scan16(valid ? flog2(gscalar) : 0.f);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            b[ks][e] = row_scan16(flog2(b[ks][e]));
-        }
+            for (int e = 0; e < 8; ++e) b[ks][e] = x;
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f4 lv;
+                if constexpr (GATE == KDA_GATE_ALPHA) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) lv[i] = flog2(graw[ks][half][i]);
+                } else {
+                    const f4 xv = Raw4<true>::widen(graw[ks][half]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) lv[i] = log2_alpha_from_softplus_arg(xv[i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) b[ks][4 * half + i] = row_scan16(valid ? lv[i] : 0.f);
+            }
+    }
     if (lm == 15) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -1084,14 +1106,16 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
 
     if (pl.gmax > 0) {
         PrepParams pp;
-        pp.q = a.q; pp.k = a.k; pp.v = a.v; pp.alpha = a.alpha; pp.beta = a.beta;
+        pp.q = a.q; pp.k = a.k; pp.v = a.v; pp.gate = a.gate; pp.beta = a.beta;
         pp.ctrl = ctrl; pp.table = table;
         pp.rec = ws + pl.off_rec; pp.rec_bytes = pl.rec_bytes; pp.gmax = pl.gmax;
         pp.H = pl.H;
         pp.T = pl.varlen ? 0 : pl.T;
         pp.cps = static_cast<int>((pl.T + C - 1) / C);
         constexpr int lds = PrepLds<DK, DV, F16>::bytes;
-        auto kfn = prep_kernel<DK, DV, F16>;
+        auto kfn = a.gate_kind == KDA_GATE_SOFTPLUS_BF16 ? prep_kernel<DK, DV, F16, KDA_GATE_SOFTPLUS_BF16>
+                 : a.gate_kind == KDA_GATE_SCALAR        ? prep_kernel<DK, DV, F16, KDA_GATE_SCALAR>
+                                                         : prep_kernel<DK, DV, F16, KDA_GATE_ALPHA>;
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;

@@ -37,10 +37,20 @@ template <> __device__ __forceinline__ void store_out<true>(void* o, size_t i, f
 }
 
 // ---------------------------------------------------------------------------
+// Forget-gate forms (kda_gate): log2 of alpha from the value as given.
+// softplus(x) / ln 2 = max(x, 0) log2(e) + log2(1 + 2^(-|x| log2(e))).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float log2_alpha_from_softplus_arg(float x) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float t = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    return -(fmaxf(x, 0.f) * kLog2e + __builtin_amdgcn_logf(1.f + t));
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v,
-                                 const float* alpha, const float* beta, float* state,
+                                 const void* gate, int gate_kind, const float* beta, float* state,
                                  void* o, int N, int H, int Dk, int Dv,
                                  bool act_bf16, bool out_bf16, hipStream_t stream);
 

@@ -39,10 +39,20 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 #endif
 constexpr int kDecodeThreads = KDA_DECODE_NT;
 
-template <int DK, int DV, int CB, bool ABF16, bool OBF16>
+// the forget gate of key channel c of task `pair`, in the form GATE (kda_gate)
+template <int GATE, int DK>
+__device__ __forceinline__ float gate_alpha(const void* __restrict__ gate, size_t pair, int c) {
+    if constexpr (GATE == KDA_GATE_ALPHA) return static_cast<const float*>(gate)[pair * DK + c];
+    else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16)
+        return __builtin_amdgcn_exp2f(log2_alpha_from_softplus_arg(
+            bf16_to_f32(static_cast<const uint16_t*>(gate)[pair * DK + c])));
+    else return static_cast<const float*>(gate)[pair];
+}
+
+template <int DK, int DV, int CB, bool ABF16, bool OBF16, int GATE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const typename Act<ABF16>::T* __restrict__ q, const typename Act<ABF16>::T* __restrict__ k,
-    const typename Act<ABF16>::T* __restrict__ v, const float* __restrict__ alpha,
+    const typename Act<ABF16>::T* __restrict__ v, const void* __restrict__ gate,
     const float* __restrict__ beta, float* __restrict__ state, void* __restrict__ o) {
     constexpr int NCB = DV / CB;          // column blocks per (sequence, head)
     constexpr int CG = CB / 4;            // column groups of 4 floats
@@ -72,7 +82,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     for (int c = tid; c < DK; c += kDecodeThreads) {
         s_k[c] = Act<ABF16>::load(k, pair * DK + c);
         s_q[c] = Act<ABF16>::load(q, pair * DK + c);
-        s_a[c] = alpha[pair * DK + c];
+        s_a[c] = gate_alpha<GATE, DK>(gate, pair, c);
     }
     __syncthreads();
 
@@ -134,41 +144,52 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
 }
 
-template <int DK, int DV, bool ABF16, bool OBF16>
-hipError_t launch(const void* q, const void* k, const void* v, const float* alpha,
+template <int DK, int DV, bool ABF16, bool OBF16, int GATE>
+hipError_t launch(const void* q, const void* k, const void* v, const void* gate,
                   const float* beta, float* state, void* o, int pairs, hipStream_t stream) {
     using T = typename Act<ABF16>::T;
     constexpr int CB = KDA_DECODE_CB < DV ? KDA_DECODE_CB : DV;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, CB, ABF16, OBF16>), dim3(pairs * (DV / CB)), dim3(kDecodeThreads), 0, stream,
-                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                       alpha, beta, state, o);
+    hipLaunchKernelGGL((decode_kernel<DK, DV, CB, ABF16, OBF16, GATE>), dim3(pairs * (DV / CB)),
+                       dim3(kDecodeThreads), 0, stream, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), gate, beta, state, o);
     return hipGetLastError();
 }
 
-template <int DK, int DV>
-hipError_t dispatch_types(const void* q, const void* k, const void* v, const float* alpha,
+template <int DK, int DV, int GATE>
+hipError_t dispatch_types(const void* q, const void* k, const void* v, const void* gate,
                           const float* beta, float* state, void* o, int pairs, bool abf16,
                           bool obf16, hipStream_t stream) {
-    if (!abf16) return launch<DK, DV, false, false>(q, k, v, alpha, beta, state, o, pairs, stream);
-    if (obf16) return launch<DK, DV, true, true>(q, k, v, alpha, beta, state, o, pairs, stream);
-    return launch<DK, DV, true, false>(q, k, v, alpha, beta, state, o, pairs, stream);
+    if (!abf16) return launch<DK, DV, false, false, GATE>(q, k, v, gate, beta, state, o, pairs, stream);
+    if (obf16) return launch<DK, DV, true, true, GATE>(q, k, v, gate, beta, state, o, pairs, stream);
+    return launch<DK, DV, true, false, GATE>(q, k, v, gate, beta, state, o, pairs, stream);
+}
+
+template <int DK, int DV>
+hipError_t dispatch_gate(const void* q, const void* k, const void* v, const void* gate,
+                         int gate_kind, const float* beta, float* state, void* o, int pairs,
+                         bool abf16, bool obf16, hipStream_t stream) {
+    if (gate_kind == KDA_GATE_ALPHA)
+        return dispatch_types<DK, DV, KDA_GATE_ALPHA>(q, k, v, gate, beta, state, o, pairs, abf16, obf16, stream);
+    if (gate_kind == KDA_GATE_SOFTPLUS_BF16)
+        return dispatch_types<DK, DV, KDA_GATE_SOFTPLUS_BF16>(q, k, v, gate, beta, state, o, pairs, abf16, obf16, stream);
+    return dispatch_types<DK, DV, KDA_GATE_SCALAR>(q, k, v, gate, beta, state, o, pairs, abf16, obf16, stream);
 }
 
 }  // namespace
 
 hipError_t launch_recurrent_step(const void* q, const void* k, const void* v,
-                                 const float* alpha, const float* beta, float* state, void* o,
-                                 int N, int H, int Dk, int Dv, bool act_bf16, bool out_bf16,
-                                 hipStream_t stream) {
+                                 const void* gate, int gate_kind, const float* beta, float* state,
+                                 void* o, int N, int H, int Dk, int Dv, bool act_bf16,
+                                 bool out_bf16, hipStream_t stream) {
     const int pairs = N * H;
     if (Dk == 128 && Dv == 128)
-        return dispatch_types<128, 128>(q, k, v, alpha, beta, state, o, pairs, act_bf16, out_bf16, stream);
+        return dispatch_gate<128, 128>(q, k, v, gate, gate_kind, beta, state, o, pairs, act_bf16, out_bf16, stream);
     if (Dk == 64 && Dv == 64)
-        return dispatch_types<64, 64>(q, k, v, alpha, beta, state, o, pairs, act_bf16, out_bf16, stream);
+        return dispatch_gate<64, 64>(q, k, v, gate, gate_kind, beta, state, o, pairs, act_bf16, out_bf16, stream);
     if (Dk == 128 && Dv == 64)
-        return dispatch_types<128, 64>(q, k, v, alpha, beta, state, o, pairs, act_bf16, out_bf16, stream);
+        return dispatch_gate<128, 64>(q, k, v, gate, gate_kind, beta, state, o, pairs, act_bf16, out_bf16, stream);
     if (Dk == 64 && Dv == 128)
-        return dispatch_types<64, 128>(q, k, v, alpha, beta, state, o, pairs, act_bf16, out_bf16, stream);
+        return dispatch_gate<64, 128>(q, k, v, gate, gate_kind, beta, state, o, pairs, act_bf16, out_bf16, stream);
     return hipErrorInvalidValue;
 }
 

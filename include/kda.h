@@ -72,6 +72,34 @@ typedef enum {
     KDA_DTYPE_BF16 = 1
 } kda_dtype;
 
+/*
+ * Form of the forget gate passed to the *_gated entry points.
+ *   KDA_GATE_ALPHA          alpha itself: fp32, one value per key channel
+ *                           ([..., Dk]), in (0, 1].  The plain entry points
+ *                           take this form.
+ *   KDA_GATE_SOFTPLUS_BF16  the gate's pre-activation x: bf16, one value per
+ *                           key channel ([..., Dk]), with
+ *                           log alpha = -softplus(x) = -log(1 + e^x), so
+ *                           alpha = 1 / (1 + e^x) lies in (0, 1).  Half the
+ *                           gate bytes of KDA_GATE_ALPHA; the kernels form
+ *                           log alpha directly, exact near alpha -> 1.
+ *   KDA_GATE_SCALAR         alpha fp32, ONE value per token and head
+ *                           ([..., 1], i.e. the layout of beta), in (0, 1],
+ *                           applied to every key channel: the coarse scalar
+ *                           gate of Gated DeltaNet ("Hybrid Linear Attention
+ *                           Architectures...", Core Module Design, Stage 2).
+ * The pages compute the gating parameters inside each chunk from the layer
+ * inputs ("Hybrid Linear Attention Architectures...", Hardware-Aware
+ * Chunkwise Parallelism, implementation checklist; "Linear Attention KDA
+ * Gating...", section 3.3); they print no activation function, and
+ * -softplus is the log-sigmoid form with alpha in (0, 1).
+ */
+typedef enum {
+    KDA_GATE_ALPHA = 0,
+    KDA_GATE_SOFTPLUS_BF16 = 1,
+    KDA_GATE_SCALAR = 2
+} kda_gate;
+
 /* Human-readable name of a status code (static string, never NULL). */
 KDA_API const char *kda_status_string(kda_status s);
 
@@ -128,6 +156,24 @@ KDA_API kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          void *stream);
 
 /*
+ * kda_chunk_fwd with the forget gate in any form of kda_gate: `gate` takes
+ * the place of `alpha` (layouts: [B, T, H, Dk] for KDA_GATE_ALPHA and
+ * KDA_GATE_SOFTPLUS_BF16, [B, T, H] for KDA_GATE_SCALAR; alignment 16, 8
+ * and 4 bytes).  Everything else is as for kda_chunk_fwd, which is this call
+ * with KDA_GATE_ALPHA.  For KDA_GATE_SOFTPLUS_BF16 the decay precondition
+ * reads: softplus(x) summed over any 8 consecutive tokens stays below 10.
+ */
+KDA_API kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                         const void *gate, kda_gate gate_kind, const float *beta,
+                         const float *initial_state, float *final_state,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         void *o,
+                         int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
+                         kda_dtype act_dtype, kda_dtype out_dtype,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
  * One recurrent decode step: every one of N sequences consumes one token and
  * its fp32 state is updated in place ("recurrent kernels for linear
  * attention" of "Linear Attention + Sparse Attention: The Hybrid
@@ -140,10 +186,23 @@ KDA_API kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
  *   alpha  [N, H, Dk]  fp32           beta [N, H] fp32
  *   state  [N, H, Dk, Dv] fp32, read and overwritten
  *   o      [N, H, Dv]  out_dtype
- * N may be 0 (nothing is launched).
+ * N may be 0 (nothing is launched); N * H must stay below 2^30.
  */
 KDA_API kda_status kda_recurrent_step(const void *q, const void *k, const void *v,
                               const float *alpha, const float *beta,
+                              float *state, void *o,
+                              int N, int H, int Dk, int Dv,
+                              kda_dtype act_dtype, kda_dtype out_dtype,
+                              void *stream);
+
+/*
+ * kda_recurrent_step with the forget gate in any form of kda_gate (layouts
+ * [N, H, Dk], or [N, H] for KDA_GATE_SCALAR; alignment 16, 8 and 4 bytes).
+ * kda_recurrent_step is this call with KDA_GATE_ALPHA.  N * H must stay
+ * below 2^30.
+ */
+KDA_API kda_status kda_recurrent_step_gated(const void *q, const void *k, const void *v,
+                              const void *gate, kda_gate gate_kind, const float *beta,
                               float *state, void *o,
                               int N, int H, int Dk, int Dv,
                               kda_dtype act_dtype, kda_dtype out_dtype,

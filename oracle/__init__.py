@@ -75,6 +75,31 @@ def _ptr(a):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
 
 
+def alpha_from_gate(gate, kind: str, Dk: int):
+    """The per-channel forget gate alpha (fp64) that a gate given in the form
+    ``kind`` stands for:
+
+    * "alpha"    -- alpha itself, [..., Dk].
+    * "softplus" -- the pre-activation x, [..., Dk]: log alpha = -softplus(x),
+      softplus(x) = log(1 + e^x), evaluated as logaddexp(0, x); so alpha =
+      1 / (1 + e^x).  (The pages compute the gates inside each chunk -- "Hybrid
+      Linear Attention Architectures...", Hardware-Aware Chunkwise
+      Parallelism, implementation checklist -- without printing the
+      activation; this is the log-sigmoid reading.)
+    * "scalar"   -- one alpha per token and head, [...], applied to every key
+      channel: the scalar gate of Gated DeltaNet ("Hybrid Linear Attention
+      Architectures...", Core Module Design, Stage 2).
+    """
+    g = _f64(gate)
+    if kind == "alpha":
+        return g
+    if kind == "softplus":
+        return np.exp(-np.logaddexp(0.0, g))
+    if kind == "scalar":
+        return np.repeat(g[..., None], Dk, axis=-1)
+    raise ValueError(kind)
+
+
 def kda_fwd(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None,
             nthreads: int = 0, return_threads: bool = False):
     """Token-by-token KDA forward in fp64.

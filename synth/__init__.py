@@ -12,6 +12,10 @@ Value recipe (the same for every workload unless a field overrides it):
   alpha = exp(-softplus(N(mu, 1))) per (token, head, key channel), fp32
   S_0   = N(0, s0_std) fp32 per (sequence, head), or absent
 
+Other gate forms (``draw_gate``): "softplus" passes the pre-activation
+x = N(mu, 1) itself, cast to bf16; "scalar" draws one
+alpha = exp(-softplus(N(mu, 1))) per (token, head), fp32.
+
 Every tensor is drawn from a torch.Generator seeded from (seed, tensor tag),
 on the device where it is generated; a run is reproducible on the same
 device type.  The oracle receives the exact values the GPU receives (they are
@@ -25,7 +29,7 @@ from typing import Optional
 import torch
 import torch.nn.functional as F
 
-_TAGS = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "s0": 6, "len": 7}
+_TAGS = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "s0": 6, "len": 7, "gx": 8, "ga": 9}
 
 
 def _gen(seed: int, tag: str, device) -> torch.Generator:
@@ -93,6 +97,22 @@ def draw_qkv_gates(lead: tuple, H: int, Dk: int, Dv: int, dtype: str, mu: float,
     alpha = torch.exp(-F.softplus(x))
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(),
                 alpha=alpha.contiguous(), beta=beta.contiguous())
+
+
+def draw_gate(kind: str, lead: tuple, H: int, Dk: int, mu: float, seed: int, device):
+    """The forget gate in one of the forms of the library's ``gate=`` argument:
+    "alpha" (fp32 [lead, H, Dk]), "softplus" (bf16 pre-activation
+    [lead, H, Dk]) or "scalar" (fp32 alpha [lead, H])."""
+    if kind == "alpha":
+        x = torch.randn(tuple(lead) + (H, Dk), generator=_gen(seed, "alpha", device), device=device) + mu
+        return torch.exp(-F.softplus(x)).contiguous()
+    if kind == "softplus":
+        x = torch.randn(tuple(lead) + (H, Dk), generator=_gen(seed, "gx", device), device=device) + mu
+        return x.to(torch.bfloat16).contiguous()
+    if kind == "scalar":
+        x = torch.randn(tuple(lead) + (H,), generator=_gen(seed, "ga", device), device=device) + mu
+        return torch.exp(-F.softplus(x)).contiguous()
+    raise ValueError(kind)
 
 
 def draw_state(N: int, H: int, Dk: int, Dv: int, std: Optional[float], seed: int, device):

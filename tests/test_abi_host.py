@@ -95,6 +95,41 @@ def test_chunk_fwd_argument_errors():
     assert _chunk(B=1 << 20, T=1 << 12) == kda.KDA_ERROR_NOT_SUPPORTED   # > 2^31 token rows
 
 
+def _chunk_gated(gate_kind, gate=FAKE, **over):
+    L = kda.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, s0=None, sT=None, cu=None, N=0,
+             o=FAKE, B=1, T=128, H=2, Dk=64, Dv=64, C=64, act=kda.KDA_DTYPE_BF16,
+             out=kda.KDA_DTYPE_BF16, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(over)
+    return L.kda_chunk_fwd_gated(a["q"], a["k"], a["v"], gate, gate_kind, a["beta"], a["s0"],
+                                 a["sT"], a["cu"], a["N"], a["o"], a["B"], a["T"], a["H"],
+                                 a["Dk"], a["Dv"], a["C"], a["act"], a["out"], a["ws"], a["wsb"],
+                                 a["stream"])
+
+
+def test_gated_entry_points_argument_errors():
+    assert _chunk_gated(3) == kda.KDA_ERROR_INVALID_VALUE                       # unknown form
+    assert _chunk_gated(kda.KDA_GATE_SOFTPLUS_BF16, gate=None) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_gated(kda.KDA_GATE_ALPHA, gate=FAKE + 8) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_gated(kda.KDA_GATE_SOFTPLUS_BF16, gate=FAKE + 4) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_gated(kda.KDA_GATE_SCALAR, gate=FAKE + 2) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_gated(kda.KDA_GATE_SCALAR, Dk=96) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk_gated(kda.KDA_GATE_SCALAR, B=0, q=None, k=None, v=None, beta=None, o=None,
+                        ws=None, gate=None) == kda.KDA_SUCCESS
+    L = kda.lib()
+    st = L.kda_recurrent_step_gated(FAKE, FAKE, FAKE, FAKE + 4, kda.KDA_GATE_SOFTPLUS_BF16, FAKE,
+                                    FAKE, FAKE, 4, 2, 128, 128, kda.KDA_DTYPE_BF16,
+                                    kda.KDA_DTYPE_F32, None)
+    assert st == kda.KDA_ERROR_INVALID_VALUE
+    st = L.kda_recurrent_step_gated(FAKE, FAKE, FAKE, FAKE, 5, FAKE, FAKE, FAKE, 4, 2, 128, 128,
+                                    kda.KDA_DTYPE_BF16, kda.KDA_DTYPE_F32, None)
+    assert st == kda.KDA_ERROR_INVALID_VALUE
+    st = L.kda_recurrent_step_gated(FAKE, FAKE, FAKE, FAKE, kda.KDA_GATE_SCALAR, FAKE, FAKE,
+                                    FAKE, 1 << 29, 4, 128, 128, kda.KDA_DTYPE_BF16,
+                                    kda.KDA_DTYPE_F32, None)
+    assert st == kda.KDA_ERROR_NOT_SUPPORTED                                    # N * H >= 2^30
+
+
 def test_chunk_fwd_nothing_to_do_launches_nothing():
     # zero sequences: success without touching the device
     assert _chunk(B=0, q=None, k=None, v=None, alpha=None, beta=None, o=None, ws=None) == 0

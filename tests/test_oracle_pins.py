@@ -303,6 +303,45 @@ def test_scalar_gate_is_gated_deltanet():
         assert np.max(np.abs(o[0, t, 0] - S.T @ q[0, t, 0])) < 1e-13
 
 
+# Gate forms of the library's gate= argument (oracle.alpha_from_gate).
+# Pre-activation form: log alpha = -softplus(x) is alpha = 1 / (1 + e^x)
+# (the closed form, not the oracle's logaddexp), with alpha(0) = 1/2, alpha
+# falling in x, alpha -> 1 for x -> -inf (where KDA becomes DeltaNet, P4) and
+# alpha ~ e^-x for large x.
+def test_gate_softplus_closed_form():
+    x = np.array([-60.0, -20.0, -3.5, -1.0, -0.25, 0.0, 0.5, 2.0, 7.0, 30.0])
+    a = oracle.alpha_from_gate(x, "softplus", 1)
+    assert np.max(np.abs(a / (1.0 / (1.0 + np.exp(x))) - 1.0)) < 1e-14
+    assert a[5] == 0.5 and a[0] == 1.0
+    assert np.all(np.diff(a) < 0)
+    assert abs(a[-1] / np.exp(-30.0) - 1.0) < 1e-12
+
+
+def test_gate_softplus_limit_is_deltanet():
+    q, k, v, _, beta = rand_inputs(1, 20, 2, 6, 5)
+    S0 = RNG.standard_normal((1, 2, 6, 5))
+    x = np.full((1, 20, 2, 6), -60.0)
+    o1, s1 = oracle.kda_fwd(q, k, v, oracle.alpha_from_gate(x, "softplus", 6), beta, initial_state=S0)
+    o2, s2 = oracle.kda_fwd(q, k, v, np.ones((1, 20, 2, 6)), beta, initial_state=S0)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+# Scalar form: one alpha per (token, head) on every key channel; through the
+# recurrence it is the gated DeltaNet update of P11.
+def test_gate_scalar_is_gated_deltanet():
+    T, Dk, Dv = 12, 5, 4
+    q, k, v, _, beta = rand_inputs(1, T, 1, Dk, Dv)
+    a = RNG.uniform(0.4, 1.0, size=(1, T, 1))
+    alpha = oracle.alpha_from_gate(a, "scalar", Dk)
+    assert alpha.shape == (1, T, 1, Dk) and np.all(alpha == a[..., None])
+    S = RNG.standard_normal((Dk, Dv))
+    o, _ = oracle.kda_fwd(q, k, v, alpha, beta, initial_state=S[None, None])
+    for t in range(T):
+        kt, bt = k[0, t, 0], beta[0, t, 0]
+        S = a[0, t, 0] * (np.eye(Dk) - bt * np.outer(kt, kt)) @ S + bt * np.outer(kt, v[0, t, 0])
+        assert np.max(np.abs(o[0, t, 0] - S.T @ q[0, t, 0])) < 1e-13
+
+
 def test_threads_do_not_change_results():
     q, k, v, alpha, beta = rand_inputs(2, 33, 5, 8, 8)
     o1, s1, n1 = oracle.kda_fwd(q, k, v, alpha, beta, nthreads=1, return_threads=True)
