@@ -42,10 +42,29 @@ FWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 4 * 128 + 4
 FWD_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * 128 + 64 * 256 + 64 * 128 + 64 * 128 + 64 * 64 // 3
 
 
-def decode_bytes_per_step(N, H, Dk, Dv):
+# bytes of the forget gate per token-head, by form (gate= argument)
+GATE_BYTES = {"alpha": 4 * 128, "softplus": 2 * 128, "scalar": 4}
+
+
+def decode_bytes_per_step(N, H, Dk, Dv, gate="alpha"):
     state = 2 * N * H * Dk * Dv * 4                      # read + write, fp32
-    io = N * H * (2 * Dk * 2 + Dv * 2 + Dv * 2 + Dk * 4 + 4)   # q,k,v,o bf16, alpha, beta
+    gbytes = {"alpha": Dk * 4, "softplus": Dk * 2, "scalar": 4}[gate]
+    io = N * H * (2 * Dk * 2 + Dv * 2 + Dv * 2 + gbytes + 4)   # q,k,v,o bf16, gate, beta
     return state + io
+
+
+def time_events(fn, reps, warm=3):
+    """Mean milliseconds of fn() over reps calls (HIP events on the current stream)."""
+    import torch
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
 
 
 KERNEL_SOURCES = ["gated_delta_rule_12_amd/csrc/kda_chunk.hip", "gated_delta_rule_12_amd/csrc/kda_decode.hip",
@@ -255,6 +274,49 @@ def main():
     out["config"] = cfg
     if args.only is None:
         out["measured_peaks"] = measured_peaks(torch)
+        # the other forget-gate forms on the same shapes (q, k, v, beta, states reused)
+        var = {}
+        units = wf.B * wf.H * wf.T
+        for gate in ("softplus", "scalar"):
+            g = synth.draw_gate(gate, (wf.B, wf.T), wf.H, wf.Dk, wf.mu, 2, dev)
+
+            def fwd_g():
+                kda.kda_chunk_fwd(fi["q"], fi["k"], fi["v"], g, fi["beta"],
+                                  initial_state=fi["initial_state"], final_state=sT, o=o,
+                                  out_dtype=torch.bfloat16, workspace=ws, gate=gate)
+            ms = time_events(fwd_g, 10)
+            byts = ((FWD_BYTES_PER_TOKEN_HEAD - GATE_BYTES["alpha"] + GATE_BYTES[gate]) * units
+                    + 2 * wf.B * wf.H * wf.Dk * wf.Dv * 4)
+            ach = byts / (ms / 1e3) / 1e9
+            var[f"fwd_gate_{gate}"] = {"value": round(units / (ms / 1e3), 1), "unit": "token-heads/s",
+                                       "fwd_ms": round(ms, 4),
+                                       "roofline": {"bound": "hbm", "achieved": round(ach, 1),
+                                                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                                    "frac": round(ach / HBM_PEAK_GBPS, 4),
+                                                    "algorithmic_bytes_per_launch": byts}}
+            del g
+            gd = synth.draw_gate(gate, (wd.steps, wd.B), wd.H, wd.Dk, wd.mu, 3, dev)
+            st2 = di["state"].clone()
+            it = [0]
+
+            def dec_g():
+                s = it[0] % wd.steps
+                it[0] += 1
+                kda.kda_recurrent_step(di["q"][s], di["k"][s], di["v"][s], gd[s], di["beta"][s],
+                                       st2, o=od, out_dtype=torch.bfloat16, gate=gate)
+            ms = time_events(dec_g, 20)
+            dbytes = decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv, gate)
+            gb = dbytes / (ms / 1e3) / 1e9
+            var[f"decode_gate_{gate}"] = {"value": round(gb, 1), "unit": "GB/s",
+                                          "us_per_step": round(ms * 1e3, 2),
+                                          "roofline": {"bound": "hbm", "achieved": round(gb, 1),
+                                                       "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                                       "frac": round(gb / HBM_PEAK_GBPS, 4),
+                                                       "algorithmic_bytes_per_launch": dbytes}}
+            del gd, st2
+        var["note"] = ("forget gate given as the bf16 softplus pre-activation, or one fp32 alpha "
+                       "per token and head; same shapes as the main lines")
+        out["variants"] = var
     traffic = measured_traffic()
     if traffic is not None:
         if do_fwd:
