@@ -161,6 +161,8 @@ def main():
     ap.add_argument("--only", choices=["fwd", "decode"], default=None)
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the measured peaks and the other gate forms (profiler runs)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -272,7 +274,7 @@ def main():
             cfg["workload"] = wd.name
 
     out["config"] = cfg
-    if args.only is None:
+    if args.only is None and not args.no_variants:
         out["measured_peaks"] = measured_peaks(torch)
         # the other forget-gate forms on the same shapes (q, k, v, beta, states reused)
         var = {}
