@@ -11,6 +11,9 @@ Two implementations of the same mathematics live here:
   computes ("Hybrid Linear Attention Architectures...", "Core Module Design",
   Stage 3; "Linear Attention KDA Gating in a 3:1 Hybrid Architecture",
   section 2, item 5).
+* ``kda_bwd`` -- reverse-mode differentiation of that recurrence, token by
+  token (the vector-Jacobian product of a training backward), and
+  ``gate_grad`` for the chain rule from alpha to the other gate forms.
 * ``oracle.chunked`` -- the chunkwise form of "Linear Attention KDA Gating in
   a 3:1 Hybrid Architecture", sections 3.1 and 3.2, in numpy fp64, exposing
   its per-chunk intermediates.  It is pinned to the recurrence by the tests.
@@ -57,6 +60,10 @@ def _load():
         lib.kda_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, lp, ctypes.c_int, dp,
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ip]
+        lib.kda_oracle_bwd.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, dp, lp, ctypes.c_int, dp, dp,
+                                       dp, dp, dp, dp, dp, dp, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ip]
         lib.kda_oracle_step.restype = ctypes.c_int
         lib.kda_oracle_step.argtypes = [dp, dp, dp, dp, dp, dp, dp, ctypes.c_int,
                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -165,3 +172,69 @@ def kda_step(q, k, v, alpha, beta, state, nthreads: int = 0, return_threads: boo
     if return_threads:
         return o, st, used.value
     return o, st
+
+
+def _cu_arg(cu_seqlens, B, T):
+    if cu_seqlens is None:
+        return None, B, None
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    if B != 1 or cu.ndim != 1 or cu[0] != 0 or cu[-1] != T or np.any(np.diff(cu) < 0):
+        raise ValueError("oracle: bad cu_seqlens")
+    return cu, cu.shape[0] - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def kda_bwd(q, k, v, alpha, beta, dout, initial_state=None, dfinal_state=None,
+            cu_seqlens=None, nthreads: int = 0):
+    """Gradients of L = sum(dout * o) + sum(dfinal_state * S_T) in fp64.
+
+    Same inputs as ``kda_fwd`` plus dout [B,T,H,Dv] and dfinal_state
+    [N,H,Dk,Dv] (None = zeros).  Returns a dict with dq, dk [B,T,H,Dk],
+    dv [B,T,H,Dv], dalpha [B,T,H,Dk] (per channel), dbeta [B,T,H] and
+    dinitial_state [N,H,Dk,Dv] (dL/dS_0; meaningful whether or not an
+    initial state was given, zeros standing in for a missing one).
+    """
+    q, k, v, alpha, beta, dout = map(_f64, (q, k, v, alpha, beta, dout))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if k.shape != q.shape or alpha.shape != q.shape or v.shape[:3] != q.shape[:3] \
+            or beta.shape != q.shape[:3] or dout.shape != v.shape:
+        raise ValueError("oracle: inconsistent input shapes")
+    cu, N, cu_p = _cu_arg(cu_seqlens, B, T)
+    s0 = None if initial_state is None else _f64(initial_state)
+    dsT = None if dfinal_state is None else _f64(dfinal_state)
+    for x in (s0, dsT):
+        if x is not None and x.shape != (N, H, Dk, Dv):
+            raise ValueError("oracle: state shape")
+    r = dict(dq=np.zeros((B, T, H, Dk)), dk=np.zeros((B, T, H, Dk)), dv=np.zeros((B, T, H, Dv)),
+             dalpha=np.zeros((B, T, H, Dk)), dbeta=np.zeros((B, T, H)),
+             dinitial_state=np.zeros((N, H, Dk, Dv)))
+    used = ctypes.c_int(0)
+    rc = _load().kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(s0),
+                                cu_p, N, _ptr(dout), _ptr(dsT), _ptr(r["dq"]), _ptr(r["dk"]),
+                                _ptr(r["dv"]), _ptr(r["dalpha"]), _ptr(r["dbeta"]),
+                                _ptr(r["dinitial_state"]), B, T, H, Dk, Dv, int(nthreads),
+                                ctypes.byref(used))
+    if rc != 0:
+        raise RuntimeError(f"kda_oracle_bwd failed: {rc}")
+    r["threads"] = used.value
+    return r
+
+
+def gate_grad(dalpha, gate, kind: str):
+    """dL/d(gate) in the form ``kind`` from the per-channel dL/dalpha.
+
+    * "alpha"    -- dalpha itself.
+    * "softplus" -- alpha = 1 / (1 + e^x), so dalpha/dx = -alpha (1 - alpha),
+      evaluated as -sigmoid(x) sigmoid(-x).
+    * "scalar"   -- the one gate feeds every key channel: the channel
+      gradients add up.
+    """
+    da = _f64(dalpha)
+    if kind == "alpha":
+        return da
+    if kind == "softplus":
+        x = _f64(gate)
+        return -da * np.exp(-np.logaddexp(0.0, x)) * np.exp(-np.logaddexp(0.0, -x))
+    if kind == "scalar":
+        return da.sum(axis=-1)
+    raise ValueError(kind)

@@ -82,3 +82,105 @@ def kda_fwd_chunked(q, k, v, alpha, beta, initial_state=None, cu_seqlens=None, c
                 S = r["S_next"]
             sT[n, h] = S
     return o, sT
+
+
+def chunk_grads(q, k, v, alpha, beta, S, dO, dS_next):
+    """Backward of one chunk's map (S, inputs) -> (O, S_next) of ``chunk_intermediates``.
+
+    dO: [c, Dv] gradient of the chunk's outputs; dS_next: [Dk, Dv] gradient of
+    the state leaving the chunk.  Returns a dict with dq, dk, dalpha ([c, Dk]),
+    dv ([c, Dv]), dbeta ([c]), dS (gradient of the state entering the chunk)
+    and dUc (= dL/d(U - W S)).
+
+    Each step is the chain rule through one line of the forward, in reverse:
+      O = Qh S + P Uc,  S_next = Diag(gamma) S + Kt^T Uc,  Uc = U - W S,
+      P = Tril(Qh Kb^T),  W = T Y,  U = T Z  (T = (I + A)^-1, Y = Diag(beta) Kh,
+      Z = Diag(beta) V),  A = StrictTril(Diag(beta) Kh Kb^T),
+      Qh = Gamma Q, Kh = Gamma K, Kb = K / Gamma, Kt = (gamma / Gamma) K,
+      Gamma = exp(b), b = cumsum(log alpha).
+    """
+    r = chunk_intermediates(q, k, v, alpha, beta, S)
+    q, k, v, alpha, beta, S, dO, dS_next = (np.asarray(x, dtype=np.float64)
+                                            for x in (q, k, v, alpha, beta, S, dO, dS_next))
+    c = q.shape[0]
+    Qh, Kh, Kb, Kt, W, Uc, P = r["Qh"], r["Kh"], r["Kb"], r["Kt"], r["W"], r["Uc"], r["P"]
+    Gamma, gamma = r["Gamma"], r["gamma"]
+    T = solve_triangular(np.eye(c) + r["A"], np.eye(c), lower=True, unit_diagonal=True)
+
+    # the state pass (reverse): gradients of Uc and of the incoming state
+    dUc = P.T @ dO + Kt @ dS_next
+    dS = gamma[:, None] * dS_next + Qh.T @ dO - W.T @ dUc
+    # O = Qh S + P Uc;  P = Tril(Qh Kb^T)
+    M = np.tril(dO @ Uc.T)                       # dP, masked like P
+    dQh = dO @ S.T + M @ Kb
+    dKb = M.T @ Qh
+    # S_next = Diag(gamma) S + Kt^T Uc;  Uc = U - W S
+    dKt = Uc @ dS_next.T
+    dgamma = np.sum(dS_next * S, axis=1)
+    dW = -dUc @ S.T
+    dU = dUc
+    # W = T Y, U = T Z
+    Y = beta[:, None] * Kh
+    dT = dW @ Y.T + dU @ (beta[:, None] * v).T
+    dY = T.T @ dW
+    dZ = T.T @ dU
+    dv = beta[:, None] * dZ
+    dbeta = np.sum(dZ * v, axis=1) + np.sum(dY * Kh, axis=1)
+    dKh = beta[:, None] * dY
+    # T = (I + A)^-1:  dA = -T^T dT T^T, kept where A lives (strictly lower)
+    dA = np.tril(-T.T @ dT @ T.T, -1)
+    R = Kh @ Kb.T
+    dbeta += np.sum(dA * R, axis=1)
+    dR = beta[:, None] * dA
+    dKh += dR @ Kb
+    dKb += dR.T @ Kh
+    # gates
+    dq = Gamma * dQh
+    dk = Gamma * dKh + dKb / Gamma + (gamma[None, :] / Gamma) * dKt
+    db = Qh * dQh + Kh * dKh - Kb * dKb - Kt * dKt
+    db[-1] += gamma * dgamma + np.sum(Kt * dKt, axis=0)
+    dg = np.cumsum(db[::-1], axis=0)[::-1]       # b_r = sum_{s <= r} log alpha_s
+    dalpha = dg / alpha
+    return dict(dq=dq, dk=dk, dv=dv, dalpha=dalpha, dbeta=dbeta, dS=dS, dUc=dUc)
+
+
+def kda_bwd_chunked(q, k, v, alpha, beta, dout, initial_state=None, dfinal_state=None,
+                    cu_seqlens=None, chunk_size=64):
+    """Chunkwise backward with the same interface and result as ``oracle.kda_bwd``:
+    a forward pass over the chunks records the state entering each chunk, then
+    the chunks are differentiated last to first, the state gradient flowing
+    backwards between them."""
+    q, k, v, alpha, beta, dout = (np.asarray(x, dtype=np.float64)
+                                  for x in (q, k, v, alpha, beta, dout))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if cu_seqlens is None:
+        seqs = [(bb, 0, T) for bb in range(B)]
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        assert B == 1
+        seqs = [(0, int(cu[n]), int(cu[n + 1])) for n in range(len(cu) - 1)]
+    N = len(seqs)
+    out = dict(dq=np.zeros((B, T, H, Dk)), dk=np.zeros((B, T, H, Dk)), dv=np.zeros((B, T, H, Dv)),
+               dalpha=np.zeros((B, T, H, Dk)), dbeta=np.zeros((B, T, H)),
+               dinitial_state=np.zeros((N, H, Dk, Dv)))
+    for n, (bb, t0, t1) in enumerate(seqs):
+        for h in range(H):
+            S = np.zeros((Dk, Dv)) if initial_state is None else np.array(initial_state[n, h], dtype=np.float64)
+            bounds, states = [], []
+            for c0 in range(t0, t1, chunk_size):
+                c1 = min(c0 + chunk_size, t1)
+                bounds.append((c0, c1))
+                states.append(S)
+                S = chunk_intermediates(q[bb, c0:c1, h], k[bb, c0:c1, h], v[bb, c0:c1, h],
+                                        alpha[bb, c0:c1, h], beta[bb, c0:c1, h], S)["S_next"]
+            dS = np.zeros((Dk, Dv)) if dfinal_state is None else np.array(dfinal_state[n, h], dtype=np.float64)
+            for (c0, c1), S_in in zip(reversed(bounds), reversed(states)):
+                g = chunk_grads(q[bb, c0:c1, h], k[bb, c0:c1, h], v[bb, c0:c1, h],
+                                alpha[bb, c0:c1, h], beta[bb, c0:c1, h], S_in,
+                                dout[bb, c0:c1, h], dS)
+                for key in ("dq", "dk", "dv", "dalpha", "dbeta"):
+                    out[key][bb, c0:c1, h] = g[key]
+                dS = g["dS"]
+            out["dinitial_state"][n, h] = dS
+    return out
