@@ -11,6 +11,8 @@ Functions carry the C names:
 * ``kda_chunk_fwd``                 chunkwise forward (prefill / training forward)
 * ``kda_chunk_fwd_gated``           the same with the gate in any ``kda_gate`` form
 * ``kda_chunk_fwd_workspace_bytes`` workspace size of a chunkwise forward
+* ``kda_chunk_bwd``                 chunkwise backward (training): all input gradients
+* ``kda_chunk_bwd_workspace_bytes`` workspace size of a chunkwise backward
 * ``kda_recurrent_step``            one decode step, state updated in place
 * ``kda_recurrent_step_gated``      the same with the gate in any ``kda_gate`` form
 * ``kda_status_string``             name of a status code
@@ -45,7 +47,8 @@ KDA_GATE_SCALAR = 2
 _GATES = {"alpha": KDA_GATE_ALPHA, "softplus": KDA_GATE_SOFTPLUS_BF16, "scalar": KDA_GATE_SCALAR}
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-            "kda_chunk_fwd_gated", "kda_recurrent_step", "kda_recurrent_step_gated")
+            "kda_chunk_fwd_gated", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd",
+            "kda_recurrent_step", "kda_recurrent_step_gated")
 
 _lib = None
 
@@ -75,6 +78,12 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_gated.restype = i32
         L.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                           i32, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.kda_chunk_bwd_workspace_bytes.restype = sz
+        L.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
+        L.kda_chunk_bwd.restype = i32
+        L.kda_chunk_bwd.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, vp, vp,
+                                    vp, vp, vp, vp, vp, vp,
+                                    i32, i64, i32, i32, i32, i32, i32, vp, sz, vp]
         L.kda_recurrent_step.restype = i32
         L.kda_recurrent_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
                                          i32, i32, vp]
@@ -170,6 +179,60 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     if st != KDA_SUCCESS:
         raise KDAError(st, where)
     return o, final_state
+
+
+def kda_chunk_bwd_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, varlen: bool,
+                                  num_seqs: int, chunk_size: int, act_dtype) -> int:
+    dt = act_dtype if isinstance(act_dtype, int) else _dt(act_dtype)
+    return int(lib().kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, int(bool(varlen)),
+                                                   num_seqs, chunk_size, dt))
+
+
+def kda_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                  beta: torch.Tensor, dout: torch.Tensor,
+                  initial_state: Optional[torch.Tensor] = None,
+                  dfinal_state: Optional[torch.Tensor] = None,
+                  cu_seqlens: Optional[torch.Tensor] = None, need_dinitial_state: bool = True,
+                  workspace: Optional[torch.Tensor] = None, chunk_size: int = 64, stream=None,
+                  gate: str = "alpha", out: Optional[dict] = None) -> dict:
+    """Chunkwise KDA backward on the GPU: gradients of
+    L = sum(dout * o) + sum(dfinal_state * S_T) for the forward with the same
+    inputs (see kda_chunk_fwd; ``alpha`` is the gate in the form ``gate``).
+
+    dout [B,T,H,Dv] in the dtype of q; dfinal_state [N,H,Dk,Dv] fp32 or None.
+    Returns a dict with dq, dk (like q), dv (like v), dgate (fp32, the shape
+    of ``alpha``), dbeta (fp32 [B,T,H]) and dinitial_state (fp32 [N,H,Dk,Dv],
+    or None when ``need_dinitial_state`` is False).  ``out`` may hold
+    preallocated tensors under those names.
+    """
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    act = _dt(q.dtype)
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = q.device
+    r = dict(out) if out else {}
+    r.setdefault("dq", torch.empty_like(q))
+    r.setdefault("dk", torch.empty_like(k))
+    r.setdefault("dv", torch.empty_like(v))
+    r.setdefault("dgate", torch.empty(alpha.shape, dtype=torch.float32, device=dev))
+    r.setdefault("dbeta", torch.empty(beta.shape, dtype=torch.float32, device=dev))
+    if need_dinitial_state:
+        r.setdefault("dinitial_state", torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev))
+    else:
+        r["dinitial_state"] = None
+    need = kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, cu_seqlens is not None, N, chunk_size, act)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _GATES[gate], _ptr(beta),
+                             _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(dout),
+                             _ptr(dfinal_state), _ptr(r["dq"]), _ptr(r["dk"]), _ptr(r["dv"]),
+                             _ptr(r["dgate"]), _ptr(r["dbeta"]), _ptr(r["dinitial_state"]),
+                             B, T, H, Dk, Dv, chunk_size, act, _ptr(workspace), ws_bytes,
+                             _stream(stream))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_chunk_bwd")
+    return r
 
 
 def kda_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,

@@ -114,6 +114,61 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
     return from_hip(kda::launch_chunk_fwd(plan, a, static_cast<hipStream_t>(stream)));
 }
 
+size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv, int varlen,
+                                     int num_seqs, int chunk_size, kda_dtype act_dtype) {
+    if (!valid_dtype(act_dtype)) return 0;
+    kda::ChunkBwdPlan plan;
+    if (kda::make_chunk_bwd_plan(B, T, H, Dk, Dv, varlen != 0, num_seqs, chunk_size,
+                                 act_dtype == KDA_DTYPE_BF16, &plan) != KDA_SUCCESS)
+        return 0;
+    return plan.workspace_bytes;
+}
+
+kda_status kda_chunk_bwd(const void* q, const void* k, const void* v, const void* gate,
+                         kda_gate gate_kind, const float* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, int num_seqs, const void* dout,
+                         const float* dfinal_state, void* dq, void* dk, void* dv, float* dgate,
+                         float* dbeta, float* dinitial_state, int B, int64_t T, int H, int Dk,
+                         int Dv, int chunk_size, kda_dtype act_dtype, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(act_dtype) || !valid_gate(gate_kind)) return KDA_ERROR_INVALID_VALUE;
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 0)) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_head(Dk) || !supported_head(Dv) || chunk_size != 64) return KDA_ERROR_NOT_SUPPORTED;
+
+    kda::ChunkBwdPlan plan;
+    const kda_status ps = kda::make_chunk_bwd_plan(B, T, H, Dk, Dv, cu_seqlens != nullptr,
+                                                   num_seqs, chunk_size,
+                                                   act_dtype == KDA_DTYPE_BF16, &plan);
+    if (ps != KDA_SUCCESS) return ps;
+
+    if ((int64_t)B * T > 0) {
+        if (!q || !k || !v || !gate || !beta || !dout || !dq || !dk || !dv || !dgate || !dbeta)
+            return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !gate_aligned(gate, gate_kind) ||
+            !aligned4(beta) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+            !aligned16(dv) || !aligned4(dgate) || !aligned4(dbeta))
+            return KDA_ERROR_INVALID_VALUE;
+    }
+    if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERROR_INVALID_VALUE;
+    if ((initial_state && !aligned16(initial_state)) || (dfinal_state && !aligned16(dfinal_state)) ||
+        (dinitial_state && !aligned16(dinitial_state)))
+        return KDA_ERROR_INVALID_VALUE;
+    if (plan.fwd.N == 0) return KDA_SUCCESS;             // nothing to compute or write
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return KDA_ERROR_INVALID_VALUE;
+    if (workspace_bytes < plan.workspace_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+
+    kda::ChunkBwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.gate_kind = gate_kind; a.beta = beta;
+    a.initial_state = initial_state; a.cu_seqlens = cu_seqlens;
+    a.dout = dout; a.dfinal_state = dfinal_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dgate = dgate; a.dbeta = dbeta;
+    a.dinitial_state = dinitial_state; a.workspace = workspace;
+    a.act_bf16 = act_dtype == KDA_DTYPE_BF16;
+    return from_hip(kda::launch_chunk_bwd(plan, a, static_cast<hipStream_t>(stream)));
+}
+
 kda_status kda_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, float* state, void* o, int N, int H, int Dk,
                               int Dv, kda_dtype act_dtype, kda_dtype out_dtype, void* stream) {

@@ -57,4 +57,39 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
 
 hipError_t launch_chunk_fwd(const ChunkPlan& plan, const ChunkArgs& args, hipStream_t stream);
 
+// Enqueue the chunk-table kernel: fills ctrl, first, order and table of the
+// plan's layout inside `workspace`.
+hipError_t launch_chunk_plan(const ChunkPlan& plan, const int32_t* cu_seqlens, void* workspace,
+                             hipStream_t stream);
+
+// Backward: the forward's chunk table followed by one fp32 record per
+// (head, chunk), at index h * gmax + g (layout in kda_chunk_bwd.hip).
+struct ChunkBwdPlan {
+    ChunkPlan fwd;                // sizes and chunk-table offsets (its records are unused)
+    size_t off_rec = 0, rec_bytes = 0;
+    size_t workspace_bytes = 0;
+};
+
+struct ChunkBwdArgs {
+    const void *q = nullptr, *k = nullptr, *v = nullptr;
+    const void* gate = nullptr;
+    kda_gate gate_kind = KDA_GATE_ALPHA;
+    const float* beta = nullptr;
+    const float* initial_state = nullptr;
+    const int32_t* cu_seqlens = nullptr;
+    const void* dout = nullptr;
+    const float* dfinal_state = nullptr;
+    void *dq = nullptr, *dk = nullptr, *dv = nullptr;
+    float* dgate = nullptr;
+    float* dbeta = nullptr;
+    float* dinitial_state = nullptr;
+    void* workspace = nullptr;
+    bool act_bf16 = false;
+};
+
+kda_status make_chunk_bwd_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen, int num_seqs,
+                               int chunk_size, bool act_bf16, ChunkBwdPlan* plan);
+
+hipError_t launch_chunk_bwd(const ChunkBwdPlan& plan, const ChunkBwdArgs& args, hipStream_t stream);
+
 }  // namespace kda

@@ -768,7 +768,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
         }
         // U in the accumulator layout the state kernel consumes directly
         for (int nt = wave; nt < DV / 16; nt += 4) {
-            const int c = 16 * nt + lm;
 #pragma unroll
             for (int Ib = 0; Ib < 4; ++Ib) {
                 f4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -1099,9 +1098,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     int4* table = reinterpret_cast<int4*>(ws + pl.off_table);
 
     if (Rec<DK, DV, F16>::END > pl.rec_bytes) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a.cu_seqlens, pl.N,
-                       pl.varlen ? static_cast<int64_t>(0) : pl.T, pl.gmax, ctrl, first, order, table);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_chunk_plan(pl, a.cu_seqlens, a.workspace, stream);
     if (e != hipSuccess) return e;
 
     if (pl.gmax > 0) {
@@ -1178,6 +1175,18 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.workspace_bytes = off;
     *plan = p;
     return KDA_SUCCESS;
+}
+
+hipError_t launch_chunk_plan(const ChunkPlan& pl, const int32_t* cu_seqlens, void* workspace,
+                             hipStream_t stream) {
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_seqlens, pl.N,
+                       pl.varlen ? static_cast<int64_t>(0) : pl.T, pl.gmax,
+                       reinterpret_cast<int32_t*>(ws + pl.off_ctrl),
+                       reinterpret_cast<int32_t*>(ws + pl.off_first),
+                       reinterpret_cast<int32_t*>(ws + pl.off_order),
+                       reinterpret_cast<int4*>(ws + pl.off_table));
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_fwd(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t stream) {

@@ -1,0 +1,939 @@
+// Chunkwise KDA backward for gfx950: the vector-Jacobian product of the
+// chunked forward for L = sum(dO * o) + sum(dS_T * S_T).
+//
+// The pages present the chunk algorithm as the training form ("Hybrid Linear
+// Attention Architectures...", Hardware-Aware Chunkwise Parallelism;
+// "Linear Attention KDA Gating in a 3:1 Hybrid Architecture", section 3).
+// Its backward is the chain rule through each line of that forward, chunk by
+// chunk and last chunk first, with only the state gradient dS flowing from
+// one chunk to the one before:
+//
+//   forward per chunk (state S entering it):
+//     U' = U - W S,  O = Qh S + P U',  S_next = Diag(gamma) S + Kt^T U'
+//   reverse per chunk (dS_next = gradient of the state leaving it):
+//     dU' = P^T dO + Kt dS_next
+//     dS  = Diag(gamma) dS_next + Qh^T dO - W^T dU'
+//   then, per chunk and independent of the others,
+//     M = Tril(dO U'^T), dQh = dO S^T + M Kb, dKb = M^T Qh + dR^T Kh,
+//     dW = -dU' S^T, dKt = U' dS_next^T, dgamma = rowsum(dS_next .* S),
+//     dT = dW Y^T + dU' Z^T, dY = T^T dW, dZ = T^T dU'  (Y = beta.Kh, Z = beta.V),
+//     dA = -StrictTril(T^T dT T^T), dR = Diag(beta) dA  (R = Kh Kb^T),
+//     dV = beta.dZ, dbeta = rowsum(dZ.V + dY.Kh + dA.R), dKh = beta.dY + dR Kb,
+//     and the gate terms through Gamma = exp(b), b = cumsum(log alpha).
+//
+// Launches, on the caller's stream:
+//   plan_kernel        the forward's chunk table (shared launcher)
+//   bwd_prep_kernel    one WG per (chunk, head): b, Gamma.Q, (gamma/Gamma).K,
+//                      A, T = (I + A)^-1, W, U, P, gamma -> fp32 record
+//   bwd_ckpt_kernel    one WG per (sequence, head, 16 value columns),
+//                      chunks in order: the state entering each chunk and U'
+//   bwd_rev_kernel     one WG per (sequence, head, 16 value columns),
+//                      chunks last to first: dS_next of each chunk and dU';
+//                      dS_0 at the end
+//   bwd_vside_kernel   one WG per (chunk, head): every contraction over the
+//                      value dimension (dO S^T, dU' S^T, U' dS_next^T, M,
+//                      dU' V^T, dgamma) and dv = beta . T^T dU'
+//   bwd_kside_kernel   one WG per (chunk, head): dT, dA, R, dY, dKh, dQh, dKb,
+//                      the gate chain rule, dq, dk, dgate, dbeta
+//
+// Numerics: every product is fp32 on the fp32 matrix cores (16x16x4), every
+// intermediate is stored in fp32.  Under the decay precondition of the
+// forward (per channel, < e^10 over any 8 tokens, so < e^80 over a chunk)
+// Gamma = 2^b and 1/Gamma stay fp32-normal over a chunk, so Kh = Gamma.K and
+// Kb = K/Gamma are formed directly.
+#include "kda_chunk.h"
+#include "kda_common.h"
+
+namespace kda {
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = kChunk;
+constexpr int LC = C + 4;          // LDS row stride of C x C fp32 tiles
+constexpr int L16 = 16;            // LDS row stride of 16-column tiles
+
+template <int D> struct Ld { static constexpr int value = D + 4; };   // LDS row stride, D columns
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------------------
+// 16x16 fp32 matrix-core tile, 4-deep steps (v_mfma_f32_16x16x4f32):
+//   A lane l holds A[l % 16][l / 16], B lane l holds B[l / 16][l % 16],
+//   D lane l holds D[4 (l / 16) + e][l % 16], e = 0..3.
+// mm: acc += sum_{k < K} A(m, k) B(k, n) with A(m, k) = pa[m am + k ak] and
+// B(k, n) = pb[k bk + n bn]; the strides express any transpose.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int K>
+__device__ __forceinline__ f4 mm(const float* pa, int am, int ak, const float* pb, int bk, int bn, f4 acc) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa += i * am + j * ak;
+    pb += j * bk + i * bn;
+#pragma unroll 8
+    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * ak], pb[k * bk], acc);
+    return acc;
+}
+
+__device__ __forceinline__ f4 mm_n(const float* pa, int am, int ak, const float* pb, int bk, int bn,
+                                   int K, f4 acc) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa += i * am + j * ak;
+    pb += j * bk + i * bn;
+    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * ak], pb[k * bk], acc);
+    return acc;
+}
+
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// D-layout tile <-> row-major memory (row stride ld, origin at the tile)
+__device__ __forceinline__ void store_tile(float* p, int ld, f4 v) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[(4 * j + e) * ld + i] = v[e];
+}
+__device__ __forceinline__ f4 load_tile(const float* p, int ld) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    f4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p[(4 * j + e) * ld + i];
+    return v;
+}
+
+// sum of x over the 16 lanes that share l / 16 (one row of a D-layout tile)
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// four consecutive activations as fp32 (16-byte / 8-byte aligned)
+template <bool BF16> __device__ __forceinline__ f4 act4(const void* p, size_t i);
+template <> __device__ __forceinline__ f4 act4<false>(const void* p, size_t i) {
+    return *reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
+}
+template <> __device__ __forceinline__ f4 act4<true>(const void* p, size_t i) {
+    const u16x4 r = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(p) + i);
+    return f4{bf16_to_f32(r[0]), bf16_to_f32(r[1]), bf16_to_f32(r[2]), bf16_to_f32(r[3])};
+}
+template <bool BF16> __device__ __forceinline__ float act1(const void* p, size_t i) {
+    if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    else return static_cast<const float*>(p)[i];
+}
+
+// C token rows x COLS of a [rows, H, COLS] activation tensor (head h, first
+// row row0, rows >= len read as zero) into LDS as fp32, row stride ld.
+template <bool BF16, int COLS, int NTH>
+__device__ __forceinline__ void load_tokens(float* dst, int ld, const void* src, int64_t row0, int len,
+                                            int h, int H, int c0 = 0, int ncols = COLS) {
+    const int v4 = ncols / 4;
+    for (int idx = threadIdx.x; idx < C * v4; idx += NTH) {
+        const int r = idx / v4, c = (idx % v4) * 4;
+        f4 x = zero4();
+        if (r < len) x = act4<BF16>(src, (static_cast<size_t>(row0 + r) * H + h) * COLS + c0 + c);
+        *reinterpret_cast<f4*>(dst + r * ld + c) = x;
+    }
+}
+
+// rows x ncols fp32 block (source row stride sld) into LDS (row stride ld)
+template <int NTH>
+__device__ __forceinline__ void load_block(float* dst, int ld, const float* src, int sld, int rows, int ncols) {
+    const int v4 = ncols / 4;
+    for (int idx = threadIdx.x; idx < rows * v4; idx += NTH) {
+        const int r = idx / v4, c = (idx % v4) * 4;
+        *reinterpret_cast<f4*>(dst + r * ld + c) = *reinterpret_cast<const f4*>(src + static_cast<size_t>(r) * sld + c);
+    }
+}
+template <int NTH>
+__device__ __forceinline__ void store_block(float* dst, int dld, const float* src, int ld, int rows, int ncols) {
+    const int v4 = ncols / 4;
+    for (int idx = threadIdx.x; idx < rows * v4; idx += NTH) {
+        const int r = idx / v4, c = (idx % v4) * 4;
+        *reinterpret_cast<f4*>(dst + static_cast<size_t>(r) * dld + c) = *reinterpret_cast<const f4*>(src + r * ld + c);
+    }
+}
+
+// log2 alpha of (row, head, channel c) from the gate as given
+template <int GATE, int DK>
+__device__ __forceinline__ float gate_log2(const void* gate, int64_t row, int h, int H, int c) {
+    if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
+        const uint16_t x = static_cast<const uint16_t*>(gate)[(static_cast<size_t>(row) * H + h) * DK + c];
+        return log2_alpha_from_softplus_arg(bf16_to_f32(x));
+    } else if constexpr (GATE == KDA_GATE_SCALAR) {
+        return __builtin_amdgcn_logf(static_cast<const float*>(gate)[static_cast<size_t>(row) * H + h]);
+    } else {
+        return __builtin_amdgcn_logf(static_cast<const float*>(gate)[(static_cast<size_t>(row) * H + h) * DK + c]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-(head, chunk) fp32 record of the backward (byte offsets).  Rows are
+// chunk-local tokens; the tail of a partial chunk holds zeros (Qh, Kt, W, U,
+// P, dU', ...) or the last valid row's b.
+// ---------------------------------------------------------------------------
+template <int DK, int DV> struct BRec {
+    static constexpr size_t CK = size_t(C) * DK * 4, CV = size_t(C) * DV * 4, CC = size_t(C) * C * 4;
+    static constexpr size_t KV = size_t(DK) * DV * 4;
+    static constexpr size_t QH = 0;              // Gamma . Q                 [C][DK]
+    static constexpr size_t KT = QH + CK;        // (gamma / Gamma) . K       [C][DK]
+    static constexpr size_t W = KT + CK;         // T Diag(beta) (Gamma . K)  [C][DK]
+    static constexpr size_t B = W + CK;          // b = cumsum(log2 alpha)     [C][DK]
+    static constexpr size_t U = B + CK;          // T Diag(beta) V            [C][DV]
+    static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]
+    static constexpr size_t TT = P + CC;         // (I + A)^-1                [C][C]
+    static constexpr size_t GAM = TT + CC;       // gamma                     [DK]
+    static constexpr size_t SIN = GAM + size_t(DK) * 4;   // state entering  [DK][DV]
+    static constexpr size_t DSO = SIN + KV;      // dL/d(state leaving)       [DK][DV]
+    static constexpr size_t UC = DSO + KV;       // U' = U - W S              [C][DV]
+    static constexpr size_t DUC = UC + CV;       // dL/dU'                    [C][DV]
+    static constexpr size_t DQH = DUC + CV;      // dO S^T                    [C][DK]
+    static constexpr size_t DW = DQH + CK;       // -dU' S^T                  [C][DK]
+    static constexpr size_t DKT = DW + CK;       // U' dS_next^T              [C][DK]
+    static constexpr size_t M = DKT + CK;        // Tril(dO U'^T)             [C][C]
+    static constexpr size_t N = M + CC;          // dU' V^T                   [C][C]
+    static constexpr size_t DGAM = N + CC;       // rowsum(dS_next . S)       [DK]
+    static constexpr size_t DBZ = DGAM + size_t(DK) * 4;  // rowsum(dZ . V)  [C]
+    static constexpr size_t END = DBZ + size_t(C) * 4;
+};
+
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* gate;
+    const void* dout;
+    const float* beta;
+    const float* initial_state;
+    const float* dfinal_state;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dgate;
+    float* dbeta;
+    float* dinitial_state;
+    const int32_t* ctrl;
+    const int32_t* first;
+    const int32_t* order;
+    const int4* table;
+    unsigned char* rec;
+    size_t rec_bytes;
+    int64_t gmax;
+    int N, H;
+};
+
+__device__ __forceinline__ float* rec_at(const BwdParams& P, int h, int g, size_t off) {
+    return reinterpret_cast<float*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep_kernel: one (chunk, head), 256 threads.
+// ---------------------------------------------------------------------------
+template <int DK, int DV> struct PrepB {
+    static constexpr int LK = Ld<DK>::value, LV = Ld<DV>::value, LM = LK > LV ? LK : LV;
+    static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + C) * 4;
+};
+
+template <int DK, int DV, bool ABF16, int GATE>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int LK = PrepB<DK, DV>::LK, LV = PrepB<DK, DV>::LV;
+    extern __shared__ float lds[];
+    float* sKh = lds;                    // K -> Gamma.K -> beta.Gamma.K      [C][LK]
+    float* sKb = sKh + C * LK;           // log2 alpha -> K / Gamma            [C][LK]
+    float* sQ = sKb + C * LK;            // Q -> Gamma.Q, later V -> beta.V    [C][LM]
+    float* sA = sQ + C * PrepB<DK, DV>::LM;   // A                            [C][LC]
+    float* sT = sA + C * LC;             // T                                  [C][LC]
+    float* sBeta = sT + C * LC;          // [C]
+
+    const int H = P.H;
+    const int h = blockIdx.x % H, g = blockIdx.x / H;
+    if (g >= P.ctrl[0]) return;
+    const int4 ent = P.table[g];
+    const int64_t row0 = ent.y;
+    const int len = ent.z;
+    const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+
+    load_tokens<ABF16, DK, 256>(sKh, LK, P.k, row0, len, h, H);
+    load_tokens<ABF16, DK, 256>(sQ, LK, P.q, row0, len, h, H);
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, c = idx % DK;
+        sKb[r * LK + c] = r < len ? gate_log2<GATE, DK>(P.gate, row0 + r, h, H, c) : 0.f;
+    }
+    if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
+    __syncthreads();
+
+    // b = cumsum(log2 alpha) per channel; Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q
+    float* gB = rec_at(P, h, g, R::B);
+    float* gGam = rec_at(P, h, g, R::GAM);
+    float* gKt = rec_at(P, h, g, R::KT);
+    for (int c = tid; c < DK; c += 256) {
+        float b = 0.f;
+        for (int r = 0; r < C; ++r) {
+            b += sKb[r * LK + c];
+            const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+            const float kv = sKh[r * LK + c];
+            sKh[r * LK + c] = G * kv;
+            sKb[r * LK + c] = Gi * kv;
+            sQ[r * LK + c] *= G;
+            gB[r * DK + c] = b;
+        }
+        const float gam = __builtin_amdgcn_exp2f(b);
+        gGam[c] = gam;
+        for (int r = 0; r < C; ++r) gKt[r * DK + c] = gam * sKb[r * LK + c];
+    }
+    __syncthreads();
+    store_block<256>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
+
+    // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record
+    float* gP = rec_at(P, h, g, R::P);
+    for (int t = wave; t < 32; t += 4) {
+        const int which = t >> 4, mb = (t >> 2) & 3, nb = t & 3;
+        f4 acc = zero4();
+        if (nb <= mb)
+            acc = mm<DK>((which ? sQ : sKh) + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = mb * 16 + 4 * j + e, s = nb * 16 + i;
+            if (which) acc[e] = s <= r ? acc[e] : 0.f;
+            else acc[e] = s < r ? sBeta[r] * acc[e] : 0.f;
+        }
+        if (which) store_tile(gP + mb * 16 * C + nb * 16, C, acc);
+        else store_tile(sA + mb * 16 * LC + nb * 16, LC, acc);
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1 by forward substitution, one column per thread
+    if (tid < C) {
+        const int col = tid;
+        for (int r = 0; r < C; ++r) {
+            float x = r == col ? 1.f : 0.f;
+            for (int s = col; s < r; ++s) x -= sA[r * LC + s] * sT[s * LC + col];
+            sT[r * LC + col] = r < col ? 0.f : x;
+        }
+    }
+    // Y = Diag(beta) Kh (in place); V -> sQ, Z = Diag(beta) V
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, c = idx % DK;
+        sKh[r * LK + c] *= sBeta[r];
+    }
+    __syncthreads();
+    store_block<256>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
+    load_tokens<ABF16, DV, 256>(sQ, LV, P.v, row0, len, h, H);
+    __syncthreads();
+    for (int idx = tid; idx < C * DV; idx += 256) {
+        const int r = idx / DV, c = idx % DV;
+        sQ[r * LV + c] *= sBeta[r];
+    }
+    __syncthreads();
+
+    // W = T Y, U = T Z (T lower triangular: row block mb reduces over 16 (mb + 1) tokens)
+    float* gW = rec_at(P, h, g, R::W);
+    float* gU = rec_at(P, h, g, R::U);
+    constexpr int NK = DK / 16, NV = DV / 16;
+    for (int t = wave; t < 4 * (NK + NV); t += 4) {
+        const bool isw = t < 4 * NK;
+        const int tt = isw ? t : t - 4 * NK;
+        const int nn = isw ? NK : NV;
+        const int mb = tt / nn, nb = tt % nn;
+        const f4 acc = mm_n(sT + mb * 16 * LC, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1,
+                            (mb + 1) * 16, zero4());
+        if (isw) store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
+        else store_tile(gU + mb * 16 * DV + nb * 16, DV, acc);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_ckpt_kernel: one (sequence, head, 16 value columns), 256 threads.
+// Wave w computes U' rows 16w..16w+15 and owns state row blocks w, w+4, ...
+// ---------------------------------------------------------------------------
+template <int DK> struct CkptB {
+    static constexpr int LK = Ld<DK>::value;
+    static constexpr int bytes = (2 * C * LK + DK * L16 + C * L16 + DK) * 4;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int LK = CkptB<DK>::LK, NT = DV / 16, RBW = DK / 64;
+    extern __shared__ float lds[];
+    float* sW = lds;                 // [C][LK]
+    float* sKt = sW + C * LK;        // [C][LK]
+    float* sS = sKt + C * LK;        // [DK][16]
+    float* sU = sS + DK * L16;       // [C][16]
+    float* sGam = sU + C * L16;      // [DK]
+
+    const int tile = blockIdx.x % NT;
+    const int pair = blockIdx.x / NT;
+    if (pair >= P.N * P.H) return;
+    const int n = P.order[pair / P.H], h = pair % P.H;
+    const int g0 = P.first[n], g1 = P.first[n + 1];
+    const int wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+    const int c0 = tile * 16;
+
+    f4 S[RBW];
+    for (int u = 0; u < RBW; ++u) {
+        const int rb = wave + 4 * u;
+        S[u] = P.initial_state
+                   ? load_tile(P.initial_state + (static_cast<size_t>(n) * P.H + h) * DK * DV + rb * 16 * DV + c0, DV)
+                   : zero4();
+    }
+    for (int g = g0; g < g1; ++g) {
+        float* gS = rec_at(P, h, g, R::SIN);
+        for (int u = 0; u < RBW; ++u) {
+            const int rb = wave + 4 * u;
+            store_tile(sS + rb * 16 * L16, L16, S[u]);
+            store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
+        }
+        load_block<256>(sW, LK, rec_at(P, h, g, R::W), DK, C, DK);
+        load_block<256>(sKt, LK, rec_at(P, h, g, R::KT), DK, C, DK);
+        if (threadIdx.x < DK) sGam[threadIdx.x] = rec_at(P, h, g, R::GAM)[threadIdx.x];
+        __syncthreads();
+        // U' = U - W S  (row block = wave)
+        {
+            const int mb = wave;
+            const f4 x = mm<DK>(sW + mb * 16 * LK, LK, 1, sS, L16, 1, zero4());
+            const f4 uu = load_tile(rec_at(P, h, g, R::U) + mb * 16 * DV + c0, DV);
+            const f4 uc = uu - x;
+            store_tile(sU + mb * 16 * L16, L16, uc);
+            store_tile(rec_at(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
+        }
+        __syncthreads();
+        // S <- Diag(gamma) S + Kt^T U'
+        for (int u = 0; u < RBW; ++u) {
+            const int rb = wave + 4 * u;
+            f4 s = S[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] *= sGam[rb * 16 + 4 * j + e];
+            S[u] = mm<C>(sKt + rb * 16, 1, LK, sU, L16, 1, s);
+        }
+        __syncthreads();
+    }
+    (void)i;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_rev_kernel: one (sequence, head, 16 value columns), 256 threads,
+// chunks last to first.
+// ---------------------------------------------------------------------------
+template <int DK> struct RevB {
+    static constexpr int LK = Ld<DK>::value;
+    static constexpr int bytes = (C * LC + 3 * C * LK + 2 * C * L16 + DK * L16 + DK) * 4;
+};
+
+template <int DK, int DV, bool ABF16>
+__global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int LK = RevB<DK>::LK, NT = DV / 16, RBW = DK / 64;
+    extern __shared__ float lds[];
+    float* sP = lds;                 // [C][LC]
+    float* sKt = sP + C * LC;        // [C][LK]
+    float* sQh = sKt + C * LK;       // [C][LK]
+    float* sW = sQh + C * LK;        // [C][LK]
+    float* sdO = sW + C * LK;        // [C][16]
+    float* sdU = sdO + C * L16;      // [C][16]
+    float* sdS = sdU + C * L16;      // [DK][16]
+    float* sGam = sdS + DK * L16;    // [DK]
+
+    const int tile = blockIdx.x % NT;
+    const int pair = blockIdx.x / NT;
+    if (pair >= P.N * P.H) return;
+    const int H = P.H;
+    const int n = P.order[pair / H], h = pair % H;
+    const int g0 = P.first[n], g1 = P.first[n + 1];
+    const int wave = wave_id(), j = lane_id() >> 4;
+    const int c0 = tile * 16;
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+
+    f4 dS[RBW];
+    for (int u = 0; u < RBW; ++u) {
+        const int rb = wave + 4 * u;
+        dS[u] = P.dfinal_state ? load_tile(P.dfinal_state + sbase + rb * 16 * DV + c0, DV) : zero4();
+    }
+    for (int g = g1 - 1; g >= g0; --g) {
+        const int4 ent = P.table[g];
+        float* gdS = rec_at(P, h, g, R::DSO);
+        for (int u = 0; u < RBW; ++u) {
+            const int rb = wave + 4 * u;
+            store_tile(sdS + rb * 16 * L16, L16, dS[u]);
+            store_tile(gdS + rb * 16 * DV + c0, DV, dS[u]);
+        }
+        load_block<256>(sP, LC, rec_at(P, h, g, R::P), C, C, C);
+        load_block<256>(sKt, LK, rec_at(P, h, g, R::KT), DK, C, DK);
+        load_block<256>(sQh, LK, rec_at(P, h, g, R::QH), DK, C, DK);
+        load_block<256>(sW, LK, rec_at(P, h, g, R::W), DK, C, DK);
+        load_tokens<ABF16, DV, 256>(sdO, L16, P.dout, ent.y, ent.z, h, H, c0, 16);
+        if (threadIdx.x < DK) sGam[threadIdx.x] = rec_at(P, h, g, R::GAM)[threadIdx.x];
+        __syncthreads();
+        // dU' = P^T dO + Kt dS  (row block = wave; P^T[m][k] = P[k][m], zero for k < m)
+        {
+            const int mb = wave;
+            f4 acc = mm_n(sP + mb * 16 * LC + mb * 16, 1, LC, sdO + mb * 16 * L16, L16, 1, C - mb * 16, zero4());
+            acc = mm<DK>(sKt + mb * 16 * LK, LK, 1, sdS, L16, 1, acc);
+            store_tile(sdU + mb * 16 * L16, L16, acc);
+            store_tile(rec_at(P, h, g, R::DUC) + mb * 16 * DV + c0, DV, acc);
+        }
+        __syncthreads();
+        // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'
+        for (int u = 0; u < RBW; ++u) {
+            const int rb = wave + 4 * u;
+            f4 s = dS[u];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[e] *= sGam[rb * 16 + 4 * j + e];
+            s = mm<C>(sQh + rb * 16, 1, LK, sdO, L16, 1, s);
+            const f4 x = mm<C>(sW + rb * 16, 1, LK, sdU, L16, 1, zero4());
+            dS[u] = s - x;
+        }
+        __syncthreads();
+    }
+    if (P.dinitial_state) {
+        for (int u = 0; u < RBW; ++u) {
+            const int rb = wave + 4 * u;
+            store_tile(P.dinitial_state + sbase + rb * 16 * DV + c0, DV, dS[u]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_vside_kernel: one (chunk, head), 512 threads; the value dimension is
+// taken in slices of 32 columns, the products accumulate in registers.
+// ---------------------------------------------------------------------------
+constexpr int kSW = 32, kLS = kSW + 4;
+
+template <int DK> struct VsideB {
+    static constexpr int bytes = (2 * DK * kLS + 4 * C * kLS + C * LC + 3 * C) * 4;
+};
+
+template <int DK, int DV, bool ABF16>
+__global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int NB = DK / 16;
+    constexpr int NTASK = 12 * NB + 10 + 16;
+    constexpr int KT = (NTASK + 7) / 8;
+    extern __shared__ float lds[];
+    float* sS = lds;                 // S[:, slice]        [DK][kLS]
+    float* sdS = sS + DK * kLS;      // dS_next[:, slice]  [DK][kLS]
+    float* sdO = sdS + DK * kLS;     // [C][kLS]
+    float* sUc = sdO + C * kLS;      // [C][kLS]
+    float* sdU = sUc + C * kLS;      // [C][kLS]
+    float* sV = sdU + C * kLS;       // [C][kLS]
+    float* sT = sV + C * kLS;        // [C][LC]
+    float* sBeta = sT + C * LC;      // [C]
+    float* sDbz = sBeta + C;         // rowsum(dZ . V), one row per column half  [2][C]
+
+    const int H = P.H;
+    const int h = blockIdx.x % H, g = blockIdx.x / H;
+    if (g >= P.ctrl[0]) return;
+    const int4 ent = P.table[g];
+    const int64_t row0 = ent.y;
+    const int len = ent.z;
+    const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+
+    load_block<512>(sT, LC, rec_at(P, h, g, R::TT), C, C, C);
+    if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
+    f4 acc[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) acc[k] = zero4();
+    float dgam = 0.f;
+    float dbz[4] = {0.f, 0.f, 0.f, 0.f};
+    const int zmb = wave >> 1, znb = wave & 1;      // this wave's block of dZ = T^T dU'[:, slice]
+
+    for (int s0 = 0; s0 < DV; s0 += kSW) {
+        load_block<512>(sS, kLS, rec_at(P, h, g, R::SIN) + s0, DV, DK, kSW);
+        load_block<512>(sdS, kLS, rec_at(P, h, g, R::DSO) + s0, DV, DK, kSW);
+        load_block<512>(sUc, kLS, rec_at(P, h, g, R::UC) + s0, DV, C, kSW);
+        load_block<512>(sdU, kLS, rec_at(P, h, g, R::DUC) + s0, DV, C, kSW);
+        load_tokens<ABF16, DV, 512>(sdO, kLS, P.dout, row0, len, h, H, s0, kSW);
+        load_tokens<ABF16, DV, 512>(sV, kLS, P.v, row0, len, h, H, s0, kSW);
+        __syncthreads();
+        if (tid < DK) {
+#pragma unroll 8
+            for (int c = 0; c < kSW; ++c) dgam += sdS[tid * kLS + c] * sS[tid * kLS + c];
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const int t = wave + 8 * k;
+            if (t < NTASK) {
+                const float *pa, *pb;
+                if (t < 12 * NB) {
+                    const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
+                    pa = (which == 0 ? sdO : which == 1 ? sdU : sUc) + mb * 16 * kLS;
+                    pb = (which == 2 ? sdS : sS) + nb * 16 * kLS;
+                } else if (t < 12 * NB + 10) {
+                    int idx = t - 12 * NB, mb = 0;
+                    while (idx > mb) { idx -= mb + 1; ++mb; }
+                    pa = sdO + mb * 16 * kLS;
+                    pb = sUc + idx * 16 * kLS;
+                } else {
+                    const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
+                    pa = sdU + mb * 16 * kLS;
+                    pb = sV + nb * 16 * kLS;
+                }
+                acc[k] = mm<kSW>(pa, kLS, 1, pb, 1, kLS, acc[k]);
+            }
+        }
+        // dZ = T^T dU'[:, slice] (T^T[m][k] = T[k][m], zero for k < m); dv = beta . dZ
+        {
+            const f4 z = mm_n(sT + zmb * 16 * LC + zmb * 16, 1, LC, sdU + zmb * 16 * kLS + znb * 16, kLS, 1,
+                              C - zmb * 16, zero4());
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = zmb * 16 + 4 * j + e, col = s0 + znb * 16 + i;
+                if (r < len)
+                    store_out<ABF16>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
+                dbz[e] += z[e] * sV[r * kLS + znb * 16 + i];
+            }
+        }
+        __syncthreads();
+    }
+
+    // write the value-side products
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const int t = wave + 8 * k;
+        if (t >= NTASK) continue;
+        if (t < 12 * NB) {
+            const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
+            const size_t off = which == 0 ? R::DQH : which == 1 ? R::DW : R::DKT;
+            store_tile(rec_at(P, h, g, off) + mb * 16 * DK + nb * 16, DK, which == 1 ? -acc[k] : acc[k]);
+        } else if (t < 12 * NB + 10) {
+            int idx = t - 12 * NB, mb = 0;
+            while (idx > mb) { idx -= mb + 1; ++mb; }
+            f4 x = acc[k];
+            if (idx == mb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
+            }
+            store_tile(rec_at(P, h, g, R::M) + mb * 16 * C + idx * 16, C, x);
+        } else {
+            const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
+            store_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C, acc[k]);
+        }
+    }
+    // upper blocks of M are zero
+    for (int idx = tid; idx < 6 * 256; idx += 512) {
+        const int blk = idx >> 8, e = idx & 255;
+        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        rec_at(P, h, g, R::M)[(mb * 16 + (e >> 4)) * C + nb * 16 + (e & 15)] = 0.f;
+    }
+    if (tid < DK) rec_at(P, h, g, R::DGAM)[tid] = dgam;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float x = row16_sum(dbz[e]);
+        if (i == 0) sDbz[znb * C + zmb * 16 + 4 * j + e] = x;
+    }
+    __syncthreads();
+    if (tid < C) rec_at(P, h, g, R::DBZ)[tid] = sDbz[tid] + sDbz[C + tid];
+}
+
+// ---------------------------------------------------------------------------
+// bwd_kside_kernel: one (chunk, head), 256 threads.  Wave w owns the key
+// column blocks w, w + 4, ... of every C x DK gradient.
+// ---------------------------------------------------------------------------
+template <int DK> struct KsideB {
+    static constexpr int LK = Ld<DK>::value;
+    static constexpr int bytes = (3 * C * LK + 3 * C * LC + 5 * C + DK) * 4;
+};
+
+template <int DK, int DV, bool ABF16, int GATE>
+__global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int LK = KsideB<DK>::LK, CBW = DK / 64;
+    extern __shared__ float lds[];
+    float* sKh = lds;                // Gamma.K; later db                       [C][LK]
+    float* sKb = sKh + C * LK;       // K / Gamma                               [C][LK]
+    float* sW = sKb + C * LK;        // dW; later Qh                            [C][LK]
+    float* sX = sW + C * LK;         // dT; later dR                            [C][LC]
+    float* sY = sX + C * LC;         // T^T dT                                  [C][LC]
+    float* sT = sY + C * LC;         // T; later M                              [C][LC]
+    float* sBeta = sT + C * LC;      // [C]
+    float* sRow = sBeta + C;         // dbeta parts (A and Y), one row per wave [4][C]
+    float* sCol = sRow + 4 * C;      // column sums of Kt . dKt                  [DK]
+
+    const int H = P.H;
+    const int h = blockIdx.x % H, g = blockIdx.x / H;
+    if (g >= P.ctrl[0]) return;
+    const int4 ent = P.table[g];
+    const int64_t row0 = ent.y;
+    const int len = ent.z;
+    const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+    const float* gB = rec_at(P, h, g, R::B);
+
+    load_tokens<ABF16, DK, 256>(sKh, LK, P.k, row0, len, h, H);
+    load_block<256>(sT, LC, rec_at(P, h, g, R::TT), C, C, C);
+    load_block<256>(sW, LK, rec_at(P, h, g, R::DW), DK, C, DK);
+    if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
+    sRow[tid] = 0.f;
+    __syncthreads();
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, c = idx % DK;
+        const float b = gB[r * DK + c], kv = sKh[r * LK + c];
+        sKh[r * LK + c] = __builtin_amdgcn_exp2f(b) * kv;
+        sKb[r * LK + c] = __builtin_amdgcn_exp2f(-b) * kv;
+    }
+    __syncthreads();
+
+    // dT = (dW Kh^T + N) Diag(beta)
+    for (int t = wave; t < 16; t += 4) {
+        const int mb = t >> 2, nb = t & 3;
+        f4 acc = load_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C);
+        acc = mm<DK>(sW + mb * 16 * LK, LK, 1, sKh + nb * 16 * LK, 1, LK, acc);
+        acc *= sBeta[nb * 16 + i];
+        store_tile(sX + mb * 16 * LC + nb * 16, LC, acc);
+    }
+    __syncthreads();
+    // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m)
+    for (int t = wave; t < 16; t += 4) {
+        const int mb = t >> 2, nb = t & 3;
+        const f4 acc = mm_n(sT + mb * 16 * LC + mb * 16, 1, LC, sX + mb * 16 * LC + nb * 16, LC, 1,
+                            C - mb * 16, zero4());
+        store_tile(sY + mb * 16 * LC + nb * 16, LC, acc);
+    }
+    __syncthreads();
+    // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX
+    for (int t = wave; t < 16; t += 4) {
+        const int mb = t >> 2, nb = t & 3;
+        f4 dr = zero4();
+        if (nb <= mb) {
+            // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
+            const f4 ya = mm_n(sY + mb * 16 * LC, LC, 1, sT + nb * 16 * LC, 1, LC, (nb + 1) * 16, zero4());
+            const f4 rr = mm<DK>(sKh + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, zero4());
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = mb * 16 + 4 * j + e, s = nb * 16 + i;
+                const float da = s < r ? -ya[e] : 0.f;
+                const float part = row16_sum(da * rr[e]);
+                if (i == 0) sRow[wave * C + r] += part;
+                dr[e] = sBeta[r] * da;
+            }
+        }
+        store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
+    }
+    __syncthreads();
+
+    // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh)
+    f4 dKh[4][CBW];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int u = 0; u < CBW; ++u) {
+            const int nb = wave + 4 * u;
+            const f4 dy = mm_n(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1,
+                               C - mb * 16, zero4());
+            f4 x;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = mb * 16 + 4 * j + e, c = nb * 16 + i;
+                const float part = row16_sum(dy[e] * sKh[r * LK + c]);
+                if (i == 0) sRow[wave * C + r] += part;
+                x[e] = sBeta[r] * dy[e];
+            }
+            // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
+            dKh[mb][u] = mm_n(sX + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16, x);
+        }
+    }
+    __syncthreads();
+    load_block<256>(sT, LC, rec_at(P, h, g, R::M), C, C, C);
+    load_block<256>(sW, LK, rec_at(P, h, g, R::QH), DK, C, DK);
+    __syncthreads();
+
+    // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
+    f4 dQh[4][CBW], dKb[4][CBW];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int u = 0; u < CBW; ++u) {
+            const int nb = wave + 4 * u;
+            dQh[mb][u] = mm_n(sT + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16,
+                              load_tile(rec_at(P, h, g, R::DQH) + mb * 16 * DK + nb * 16, DK));
+            f4 y = mm_n(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1, C - mb * 16,
+                        zero4());
+            dKb[mb][u] = mm_n(sX + mb * 16 * LC + mb * 16, 1, LC, sKh + mb * 16 * LK + nb * 16, LK, 1,
+                              C - mb * 16, y);
+        }
+    }
+    __syncthreads();
+
+    // gate chain rule, dq, dk; db -> sKh; column sums of Kt . dKt -> sCol
+    const float* gGam = rec_at(P, h, g, R::GAM);
+    const float* gDkt = rec_at(P, h, g, R::DKT);
+#pragma unroll
+    for (int u = 0; u < CBW; ++u) {
+        const int nb = wave + 4 * u, c = nb * 16 + i;
+        const float gam = gGam[c];
+        float col = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = mb * 16 + 4 * j + e;
+                const float b = gB[r * DK + c];
+                const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+                const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
+                const float qv = r < len ? act1<ABF16>(P.q, ai) : 0.f;
+                const float kv = r < len ? act1<ABF16>(P.k, ai) : 0.f;
+                const float dkt = gDkt[r * DK + c];
+                const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam * kb;
+                const float dqh = dQh[mb][u][e], dkh = dKh[mb][u][e], dkb = dKb[mb][u][e];
+                if (r < len) {
+                    store_out<ABF16>(P.dq, ai, G * dqh);
+                    store_out<ABF16>(P.dk, ai, G * dkh + Gi * dkb + gam * Gi * dkt);
+                }
+                sKh[r * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;
+                col += kt * dkt;
+            }
+        }
+        col += __shfl_xor(col, 16, 64);
+        col += __shfl_xor(col, 32, 64);
+        if (j == 0) sCol[c] = col;
+    }
+    __syncthreads();
+
+    // dlog(alpha)_r = sum_{s >= r} db_s (natural-log units), per channel
+    const float* gDgam = rec_at(P, h, g, R::DGAM);
+    for (int c = tid; c < DK; c += 256) {
+        float acc = gGam[c] * gDgam[c] + sCol[c];
+        for (int r = C - 1; r >= 0; --r) {
+            acc += sKh[r * LK + c];
+            if (r < len) {
+                const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
+                if constexpr (GATE == KDA_GATE_ALPHA) {
+                    P.dgate[ai] = acc / static_cast<const float*>(P.gate)[ai];
+                } else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
+                    // log alpha = -softplus(x): d/dx = -sigmoid(x)
+                    const float x = bf16_to_f32(static_cast<const uint16_t*>(P.gate)[ai]);
+                    const float sg = 1.f / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+                    P.dgate[ai] = -acc * sg;
+                } else {
+                    sKh[r * LK + c] = acc;
+                }
+            }
+        }
+    }
+    if constexpr (GATE == KDA_GATE_SCALAR) {
+        __syncthreads();
+        if (tid < len) {
+            float s = 0.f;
+            for (int c = 0; c < DK; ++c) s += sKh[tid * LK + c];
+            const size_t ai = static_cast<size_t>(row0 + tid) * H + h;
+            P.dgate[ai] = s / static_cast<const float*>(P.gate)[ai];
+        }
+    }
+    if (tid < len)
+        P.dbeta[(row0 + tid) * H + h] = rec_at(P, h, g, R::DBZ)[tid] +
+                                        ((sRow[tid] + sRow[C + tid]) + (sRow[2 * C + tid] + sRow[3 * C + tid]));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+template <typename F>
+hipError_t set_lds(F* kfn, int bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kfn), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int DK, int DV, bool ABF16, int GATE>
+hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipStream_t stream) {
+    const ChunkPlan& pl = bp.fwd;
+    unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+    if (BRec<DK, DV>::END > bp.rec_bytes) return hipErrorInvalidValue;
+    BwdParams p;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.dout = a.dout; p.beta = a.beta;
+    p.initial_state = a.initial_state; p.dfinal_state = a.dfinal_state;
+    p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dgate = a.dgate; p.dbeta = a.dbeta;
+    p.dinitial_state = a.dinitial_state;
+    p.ctrl = reinterpret_cast<const int32_t*>(ws + pl.off_ctrl);
+    p.first = reinterpret_cast<const int32_t*>(ws + pl.off_first);
+    p.order = reinterpret_cast<const int32_t*>(ws + pl.off_order);
+    p.table = reinterpret_cast<const int4*>(ws + pl.off_table);
+    p.rec = ws + bp.off_rec;
+    p.rec_bytes = bp.rec_bytes;
+    p.gmax = pl.gmax;
+    p.N = pl.N;
+    p.H = pl.H;
+
+    hipError_t e = launch_chunk_plan(pl, a.cu_seqlens, a.workspace, stream);
+    if (e != hipSuccess) return e;
+    const unsigned chunk_blocks = static_cast<unsigned>(pl.gmax * pl.H);
+    const unsigned chain_blocks = static_cast<unsigned>(static_cast<int64_t>(pl.N) * pl.H * (DV / 16));
+    if (chunk_blocks > 0) {
+        auto k1 = bwd_prep_kernel<DK, DV, ABF16, GATE>;
+        constexpr int l1 = PrepB<DK, DV>::bytes;
+        if ((e = set_lds(k1, l1)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(256), l1, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto k2 = bwd_ckpt_kernel<DK, DV>;
+        constexpr int l2 = CkptB<DK>::bytes;
+        if ((e = set_lds(k2, l2)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(256), l2, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (chain_blocks > 0) {
+        auto k3 = bwd_rev_kernel<DK, DV, ABF16>;
+        constexpr int l3 = RevB<DK>::bytes;
+        if ((e = set_lds(k3, l3)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k3, dim3(chain_blocks), dim3(256), l3, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (chunk_blocks > 0) {
+        auto k4 = bwd_vside_kernel<DK, DV, ABF16>;
+        constexpr int l4 = VsideB<DK>::bytes;
+        if ((e = set_lds(k4, l4)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k4, dim3(chunk_blocks), dim3(512), l4, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto k5 = bwd_kside_kernel<DK, DV, ABF16, GATE>;
+        constexpr int l5 = KsideB<DK>::bytes;
+        if ((e = set_lds(k5, l5)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k5, dim3(chunk_blocks), dim3(256), l5, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <int DK, int DV, bool ABF16>
+hipError_t launch_bwd_gate(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipStream_t stream) {
+    if (a.gate_kind == KDA_GATE_SOFTPLUS_BF16)
+        return launch_bwd_typed<DK, DV, ABF16, KDA_GATE_SOFTPLUS_BF16>(bp, a, stream);
+    if (a.gate_kind == KDA_GATE_SCALAR) return launch_bwd_typed<DK, DV, ABF16, KDA_GATE_SCALAR>(bp, a, stream);
+    return launch_bwd_typed<DK, DV, ABF16, KDA_GATE_ALPHA>(bp, a, stream);
+}
+
+template <int DK, int DV>
+hipError_t launch_bwd_dims(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipStream_t stream) {
+    return a.act_bf16 ? launch_bwd_gate<DK, DV, true>(bp, a, stream) : launch_bwd_gate<DK, DV, false>(bp, a, stream);
+}
+
+}  // namespace
+
+kda_status make_chunk_bwd_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen, int num_seqs,
+                               int chunk_size, bool act_bf16, ChunkBwdPlan* plan) {
+    ChunkBwdPlan bp;
+    const kda_status st = make_chunk_plan(B, T, H, Dk, Dv, varlen, num_seqs, chunk_size, act_bf16, &bp.fwd);
+    if (st != KDA_SUCCESS) return st;
+    // the forward's records are not used: the backward keeps its own fp32 record
+    size_t end = 0;
+    if (Dk == 128 && Dv == 128) end = BRec<128, 128>::END;
+    else if (Dk == 64 && Dv == 64) end = BRec<64, 64>::END;
+    else if (Dk == 128 && Dv == 64) end = BRec<128, 64>::END;
+    else end = BRec<64, 128>::END;
+    bp.rec_bytes = align256(end);
+    bp.off_rec = bp.fwd.off_rec;
+    bp.workspace_bytes = align256(bp.off_rec + static_cast<size_t>(bp.fwd.gmax) * H * bp.rec_bytes);
+    *plan = bp;
+    return KDA_SUCCESS;
+}
+
+hipError_t launch_chunk_bwd(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipStream_t stream) {
+    const ChunkPlan& pl = bp.fwd;
+    if (pl.Dk == 128 && pl.Dv == 128) return launch_bwd_dims<128, 128>(bp, a, stream);
+    if (pl.Dk == 64 && pl.Dv == 64) return launch_bwd_dims<64, 64>(bp, a, stream);
+    if (pl.Dk == 128 && pl.Dv == 64) return launch_bwd_dims<128, 64>(bp, a, stream);
+    if (pl.Dk == 64 && pl.Dv == 128) return launch_bwd_dims<64, 128>(bp, a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -174,6 +174,55 @@ KDA_API kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void 
                          void *stream);
 
 /*
+ * Workspace size, in bytes, that kda_chunk_bwd needs for this problem (same
+ * arguments as kda_chunk_fwd_workspace_bytes).  Returns 0 for argument
+ * combinations kda_chunk_bwd would reject.  256-byte alignment; contents
+ * need not be initialised; not to be shared by calls that may overlap.
+ * About (7 C d_k + 4 C d_v + 2 d_k d_v + 4 C^2) * 4 bytes per (chunk, head).
+ */
+KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv,
+                                     int varlen, int num_seqs, int chunk_size,
+                                     kda_dtype act_dtype);
+
+/*
+ * Chunkwise backward (training): the gradients of
+ *     L = sum(dout * o) + sum(dfinal_state * S_T)
+ * with respect to every input of kda_chunk_fwd_gated, for the same inputs.
+ * The pages present the chunk algorithm as the training form ("Hybrid
+ * Linear Attention Architectures...", Hardware-Aware Chunkwise Parallelism;
+ * "Linear Attention KDA Gating in a 3:1 Hybrid Architecture", section 3);
+ * this is the chain rule through that chunked forward, chunk by chunk from
+ * the last, carrying only the state gradient between chunks.  The forward
+ * is recomputed inside the call (nothing has to be kept from it).
+ *
+ * Inputs, as for kda_chunk_fwd_gated (same layouts, alignment, sequences,
+ * preconditions): q, k, v, gate (form gate_kind), beta, initial_state
+ * (NULL = zeros), cu_seqlens / num_seqs.  Upstream gradients:
+ *   dout          [B, T, H, Dv]  act_dtype
+ *   dfinal_state  [N, H, Dk, Dv] fp32, or NULL for zeros
+ * Outputs (written for every token; none may overlap an input):
+ *   dq, dk        [B, T, H, Dk]  act_dtype (bf16: rounded once, nearest-even)
+ *   dv            [B, T, H, Dv]  act_dtype
+ *   dgate         fp32, the shape of gate: dL/dalpha for KDA_GATE_ALPHA,
+ *                 dL/dx for KDA_GATE_SOFTPLUS_BF16, dL/da for KDA_GATE_SCALAR
+ *   dbeta         [B, T, H]      fp32
+ *   dinitial_state [N, H, Dk, Dv] fp32 dL/dS_0, or NULL (not written)
+ * q, k, v, dout, dq, dk, dv, the states and their gradients are 16-byte
+ * aligned; dgate and dbeta 4-byte aligned.  All arithmetic is fp32.
+ */
+KDA_API kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
+                         const void *gate, kda_gate gate_kind, const float *beta,
+                         const float *initial_state,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         const void *dout, const float *dfinal_state,
+                         void *dq, void *dk, void *dv, float *dgate, float *dbeta,
+                         float *dinitial_state,
+                         int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
+                         kda_dtype act_dtype,
+                         void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/*
  * One recurrent decode step: every one of N sequences consumes one token and
  * its fp32 state is updated in place ("recurrent kernels for linear
  * attention" of "Linear Attention + Sparse Attention: The Hybrid

@@ -12,6 +12,9 @@ Value recipe (the same for every workload unless a field overrides it):
   alpha = exp(-softplus(N(mu, 1))) per (token, head, key channel), fp32
   S_0   = N(0, s0_std) fp32 per (sequence, head), or absent
 
+Upstream gradients of a backward (``draw_upstream``): dO ~ N(0, 1) cast to
+the activation dtype, dS_T ~ N(0, ds_std) fp32 per (sequence, head), or absent.
+
 Other gate forms (``draw_gate``): "softplus" passes the pre-activation
 x = N(mu, 1) itself, cast to bf16; "scalar" draws one
 alpha = exp(-softplus(N(mu, 1))) per (token, head), fp32.
@@ -29,7 +32,8 @@ from typing import Optional
 import torch
 import torch.nn.functional as F
 
-_TAGS = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "s0": 6, "len": 7, "gx": 8, "ga": 9}
+_TAGS = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "s0": 6, "len": 7, "gx": 8, "ga": 9,
+         "do": 10, "dst": 11}
 
 
 def _gen(seed: int, tag: str, device) -> torch.Generator:
@@ -113,6 +117,17 @@ def draw_gate(kind: str, lead: tuple, H: int, Dk: int, mu: float, seed: int, dev
         x = torch.randn(tuple(lead) + (H,), generator=_gen(seed, "ga", device), device=device) + mu
         return torch.exp(-F.softplus(x)).contiguous()
     raise ValueError(kind)
+
+
+def draw_upstream(lead: tuple, N: int, H: int, Dk: int, Dv: int, dtype: str,
+                  ds_std: Optional[float], seed: int, device) -> dict:
+    """Upstream gradients of a backward: dout [lead, H, Dv] in the activation
+    dtype and dfinal_state [N, H, Dk, Dv] fp32 (None when ds_std is None)."""
+    do = torch.randn(tuple(lead) + (H, Dv), generator=_gen(seed, "do", device), device=device)
+    ds = None
+    if ds_std is not None:
+        ds = torch.randn((N, H, Dk, Dv), generator=_gen(seed, "dst", device), device=device) * ds_std
+    return {"dout": do.to(_act_dtype(dtype)).contiguous(), "dfinal_state": ds}
 
 
 def draw_state(N: int, H: int, Dk: int, Dv: int, std: Optional[float], seed: int, device):
