@@ -15,7 +15,10 @@ step is reported as achieved HBM GB/s.
 Prints ONE JSON line.  Flags:
   --gpus N --steps K --warmup W       (N must be 1: this build is one GPU)
   --no-cpu-baseline                   skip the oracle timing
-  --only fwd|decode                   time one part only (profiler runs)
+  --only fwd|decode|bwd               time one part only (profiler runs; bwd = the
+                                      chunkwise backward on the forward's shape)
+  --no-variants                       skip the measured peaks, the other gate forms
+                                      and the backward line
   --copy-calibration                  run a plain 1 GiB device copy (used to
                                       scale rocprofv3 FETCH_SIZE/WRITE_SIZE)
 """
@@ -33,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix cores, vendor figure
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix cores, vendor figure
 
 # Algorithmic ledger per token-head of the chunk forward (d_k = d_v = 128):
 # q, k, v, o in bf16 (4 x 256 B) + alpha fp32 (512 B) + beta fp32 (4 B).
@@ -40,6 +44,20 @@ FWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 4 * 128 + 4
 # Useful flops per token-head at C = 64, d = 128: three d x d contractions
 # (6 d^2) + C-dependent products (A, T.X, QK^T, P.U') + the triangular solve.
 FWD_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * 128 + 64 * 256 + 64 * 128 + 64 * 128 + 64 * 64 // 3
+
+
+# Chunkwise backward, per token-head: reads q, k, v, dO (bf16), alpha, beta;
+# writes dq, dk, dv (bf16), dalpha, dbeta (fp32).
+BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 128 * 4 + 4 + 3 * 2 * 128 + 128 * 4 + 4
+
+
+def bwd_flops_per_token_head(C=64, dk=128, dv=128):
+    """Useful flops (2 x multiply-adds, triangular products at half) per
+    token-head of the chunkwise backward with the forward recomputed:
+    8 C dk dv (two state-chain passes, the value-side contractions) +
+    5.5 C^2 dk + 3 C^2 dv + 7/6 C^3 per chunk, divided by C."""
+    macs = 8 * dk * dv + 5.5 * C * dk + 3 * C * dv + (7.0 / 6.0) * C * C
+    return 2 * macs
 
 
 # bytes of the forget gate per token-head, by form (gate= argument)
@@ -152,13 +170,46 @@ def measured_peaks(torch):
     return res
 
 
+def bench_bwd(kda, synth, torch, fi, wf, reps, warm):
+    """Time kda_chunk_bwd on the forward workload's inputs (alpha gate, initial
+    state, upstream dO and dS_T drawn N(0, 1)); outputs and workspace are
+    allocated before timing."""
+    B, T, H, Dk, Dv = wf.B, wf.T, wf.H, wf.Dk, wf.Dv
+    up = synth.draw_upstream((B, T), B, H, Dk, Dv, wf.dtype, 1.0, 2, "cuda")
+    nb = kda.kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, False, 0, 64, torch.bfloat16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = {}
+
+    def run():
+        return kda.kda_chunk_bwd(fi["q"], fi["k"], fi["v"], fi["alpha"], fi["beta"], up["dout"],
+                                 initial_state=fi["initial_state"], dfinal_state=up["dfinal_state"],
+                                 workspace=ws, out=out)
+    out = run()
+    ms = time_events(run, reps, warm)
+    units = B * H * T
+    fl = bwd_flops_per_token_head(64, Dk, Dv) * units
+    tf = fl / (ms / 1e3) / 1e12
+    byts = BWD_BYTES_PER_TOKEN_HEAD * units + 3 * B * H * Dk * Dv * 4
+    del ws, out
+    return {"value": round(units / (ms / 1e3), 1), "unit": "token-heads/s", "bwd_ms": round(ms, 3),
+            "workspace_GiB": round(nb / 2 ** 30, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "dtype": "f32 (every product on the fp32 matrix cores)",
+                         "useful_flops_per_launch": round(fl)},
+            "hbm_algorithmic": {"bytes_per_launch": byts,
+                                "GBps": round(byts / (ms / 1e3) / 1e9, 1)},
+            "note": "gradients of sum(dO*o) + sum(dS_T*S_T) w.r.t. q, k, v, alpha, beta, S_0; "
+                    "the forward is recomputed inside the call"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["fwd", "decode"], default=None)
+    ap.add_argument("--only", choices=["fwd", "decode", "bwd"], default=None)
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
@@ -189,8 +240,14 @@ def main():
     dev = "cuda"
     wf = synth.WORKLOADS[2]
     wd = synth.WORKLOADS[3]
-    do_fwd = args.only in (None, "fwd")
+    do_fwd = args.only in (None, "fwd", "bwd")
     do_dec = args.only in (None, "decode")
+    if args.only == "bwd":
+        fi = synth.workload_inputs(2, device=dev)
+        r = bench_bwd(kda, synth, torch, fi, wf, K, W)
+        print(json.dumps({"metric": "KDA chunkwise backward token-heads/s", "n_gpus": 1, "steps": K,
+                          "warmup": W, "bwd": r, "config": {"workload": wf.name, "chunk": 64}}))
+        return
 
     # ---- inputs, outputs and workspace: all allocated before timing ----------
     if do_fwd:
@@ -318,6 +375,7 @@ def main():
             del gd, st2
         var["note"] = ("forget gate given as the bf16 softplus pre-activation, or one fp32 alpha "
                        "per token and head; same shapes as the main lines")
+        var["bwd"] = bench_bwd(kda, synth, torch, fi, wf, 5, 2)
         out["variants"] = var
     traffic = measured_traffic()
     if traffic is not None:
@@ -356,6 +414,21 @@ def main():
                                              / (c1 - c0) / 1e9, 3),
                               "unit": "GB/s (fp32 byte ledger)", "cores": dused,
                               "sample": f"one full decode step ({c1 - c0:.2f} s)"}
+        if "variants" in out:
+            Sb = min(4096, wf.T)
+            slb = (slice(0, 1), slice(0, Sb))
+            f64b = lambda x: x[slb].to("cpu").to(torch.float64).numpy()
+            up = synth.draw_upstream((1, Sb), wf.B, wf.H, wf.Dk, wf.Dv, wf.dtype, 1.0, 2, "cpu")
+            qb, kb, vb, ab, bb = (f64b(fi[key]) for key in ("q", "k", "v", "alpha", "beta"))
+            dob = up["dout"].to(torch.float64).numpy()
+            c0 = time.perf_counter()
+            rb = oracle.kda_bwd(qb, kb, vb, ab, bb, dob, initial_state=s0,
+                                dfinal_state=up["dfinal_state"].double().numpy())
+            c1 = time.perf_counter()
+            base["bwd"] = {"value": round(wf.H * Sb / (c1 - c0), 1), "unit": "token-heads/s",
+                           "cores": rb["threads"], "kind": "oracle",
+                           "sample": f"first {Sb} tokens, all {wf.H} heads, backward of the fp64 "
+                                     f"recurrence ({c1 - c0:.2f} s)"}
         if np.isfinite(base["value"]) and out.get("value"):
             base["gpu_over_cpu"] = round(out["value"] / base["value"], 1)
         out["cpu_baseline"] = base

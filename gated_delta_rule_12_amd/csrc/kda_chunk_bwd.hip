@@ -126,29 +126,87 @@ template <bool BF16> __device__ __forceinline__ float act1(const void* p, size_t
     else return static_cast<const float*>(p)[i];
 }
 
-// C token rows x COLS of a [rows, H, COLS] activation tensor (head h, first
-// row row0, rows >= len read as zero) into LDS as fp32, row stride ld.
-template <bool BF16, int COLS, int NTH>
-__device__ __forceinline__ void load_tokens(float* dst, int ld, const void* src, int64_t row0, int len,
-                                            int h, int H, int c0 = 0, int ncols = COLS) {
-    const int v4 = ncols / 4;
-    for (int idx = threadIdx.x; idx < C * v4; idx += NTH) {
-        const int r = idx / v4, c = (idx % v4) * 4;
-        f4 x = zero4();
-        if (r < len) x = act4<BF16>(src, (static_cast<size_t>(row0 + r) * H + h) * COLS + c0 + c);
-        *reinterpret_cast<f4*>(dst + r * ld + c) = x;
+// Register-staged copies: load() issues every global load of a block before
+// any is consumed, put() writes the block to LDS as fp32.  A block staged
+// one step ahead keeps its loads in flight while the current step computes.
+//
+// Blk: ROWS x NC fp32 values, source row stride sld (floats).
+template <int ROWS, int NC, int NTH>
+struct Blk {
+    static constexpr int V4 = NC / 4, N = ROWS * V4, IT = (N + NTH - 1) / NTH;
+    f4 t[IT];
+    __device__ __forceinline__ void load(const float* src, int sld) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N)
+                t[it] = *reinterpret_cast<const f4*>(src + static_cast<size_t>(idx / V4) * sld + (idx % V4) * 4);
+        }
     }
+    __device__ __forceinline__ void put(float* dst, int ld) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) *reinterpret_cast<f4*>(dst + (idx / V4) * ld + (idx % V4) * 4) = t[it];
+        }
+    }
+};
+
+template <bool B> struct RawT { using type = f4; };
+template <> struct RawT<true> { using type = u16x4; };
+
+// Tok: C token rows x NC columns (from column c0) of a [rows, H, COLS]
+// activation tensor, head h, first row row0; rows >= len (>= 1) read as
+// zero.  The row index is clamped, so every load is issued unconditionally.
+template <bool BF16, int COLS, int NC, int NTH>
+struct Tok {
+    static constexpr int V4 = NC / 4, N = C * V4, IT = (N + NTH - 1) / NTH;
+    using Raw = typename RawT<BF16>::type;
+    Raw t[IT];
+    __device__ __forceinline__ void load(const void* src, int64_t row0, int len, int h, int H, int c0 = 0) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) {
+                const int r = idx / V4, c = (idx % V4) * 4;
+                const int rr = r < len ? r : len - 1;
+                const size_t off = (static_cast<size_t>(row0 + rr) * H + h) * COLS + c0 + c;
+                if constexpr (BF16) t[it] = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(src) + off);
+                else t[it] = *reinterpret_cast<const f4*>(static_cast<const float*>(src) + off);
+                if (r >= len) t[it] = Raw{0, 0, 0, 0};
+            }
+        }
+    }
+    __device__ __forceinline__ void put(float* dst, int ld) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) {
+                f4 x;
+                if constexpr (BF16)
+                    x = f4{bf16_to_f32(t[it][0]), bf16_to_f32(t[it][1]), bf16_to_f32(t[it][2]), bf16_to_f32(t[it][3])};
+                else x = t[it];
+                *reinterpret_cast<f4*>(dst + (idx / V4) * ld + (idx % V4) * 4) = x;
+            }
+        }
+    }
+};
+
+template <int ROWS, int NC, int NTH>
+__device__ __forceinline__ void load_block(float* dst, int ld, const float* src, int sld) {
+    Blk<ROWS, NC, NTH> b;
+    b.load(src, sld);
+    b.put(dst, ld);
 }
 
-// rows x ncols fp32 block (source row stride sld) into LDS (row stride ld)
-template <int NTH>
-__device__ __forceinline__ void load_block(float* dst, int ld, const float* src, int sld, int rows, int ncols) {
-    const int v4 = ncols / 4;
-    for (int idx = threadIdx.x; idx < rows * v4; idx += NTH) {
-        const int r = idx / v4, c = (idx % v4) * 4;
-        *reinterpret_cast<f4*>(dst + r * ld + c) = *reinterpret_cast<const f4*>(src + static_cast<size_t>(r) * sld + c);
-    }
+template <bool BF16, int COLS, int NC, int NTH>
+__device__ __forceinline__ void load_tokens(float* dst, int ld, const void* src, int64_t row0, int len, int h,
+                                            int H, int c0 = 0) {
+    Tok<BF16, COLS, NC, NTH> t;
+    t.load(src, row0, len, h, H, c0);
+    t.put(dst, ld);
 }
+
 template <int NTH>
 __device__ __forceinline__ void store_block(float* dst, int dld, const float* src, int ld, int rows, int ncols) {
     const int v4 = ncols / 4;
@@ -226,6 +284,18 @@ struct BwdParams {
     int N, H;
 };
 
+// Sequential passes: one workgroup per (sequence-head pair, 16 value
+// columns).  Workgroups are dealt to the 8 XCDs round-robin; the NT column
+// tiles of one pair read the same per-chunk record, so they are kept on the
+// same XCD (and its L2): block b = (group * NT + tile) * 8 + xcd serves
+// pair group * 8 + xcd.  The grid is padded to a multiple of 8 pairs.
+template <int NT>
+__device__ __forceinline__ void chain_coords(int& tile, int& pair) {
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    tile = slot % NT;
+    pair = (slot / NT) * 8 + xcd;
+}
+
 __device__ __forceinline__ float* rec_at(const BwdParams& P, int h, int g, size_t off) {
     return reinterpret_cast<float*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
 }
@@ -235,20 +305,23 @@ __device__ __forceinline__ float* rec_at(const BwdParams& P, int h, int g, size_
 // ---------------------------------------------------------------------------
 template <int DK, int DV> struct PrepB {
     static constexpr int LK = Ld<DK>::value, LV = Ld<DV>::value, LM = LK > LV ? LK : LV;
-    static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + C) * 4;
+    static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + 2 * C + DK) * 4;
 };
 
 template <int DK, int DV, bool ABF16, int GATE>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
     constexpr int LK = PrepB<DK, DV>::LK, LV = PrepB<DK, DV>::LV;
+    constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
     float* sKh = lds;                    // K -> Gamma.K -> beta.Gamma.K      [C][LK]
-    float* sKb = sKh + C * LK;           // log2 alpha -> K / Gamma            [C][LK]
+    float* sKb = sKh + C * LK;           // gate -> K / Gamma -> T-solve scratch [C][LK]
     float* sQ = sKb + C * LK;            // Q -> Gamma.Q, later V -> beta.V    [C][LM]
     float* sA = sQ + C * PrepB<DK, DV>::LM;   // A                            [C][LC]
     float* sT = sA + C * LC;             // T                                  [C][LC]
     float* sBeta = sT + C * LC;          // [C]
+    float* sGs = sBeta + C;              // scalar gate per row                [C]
+    float* sGam = sGs + C;               // gamma                              [DK]
 
     const int H = P.H;
     const int h = blockIdx.x % H, g = blockIdx.x / H;
@@ -256,25 +329,40 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
     const int4 ent = P.table[g];
     const int64_t row0 = ent.y;
     const int len = ent.z;
-    const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+    const int tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
 
-    load_tokens<ABF16, DK, 256>(sKh, LK, P.k, row0, len, h, H);
-    load_tokens<ABF16, DK, 256>(sQ, LK, P.q, row0, len, h, H);
-    for (int idx = tid; idx < C * DK; idx += 256) {
-        const int r = idx / DK, c = idx % DK;
-        sKb[r * LK + c] = r < len ? gate_log2<GATE, DK>(P.gate, row0 + r, h, H, c) : 0.f;
+    {
+        Tok<ABF16, DK, DK, 256> tk, tq;
+        tk.load(P.k, row0, len, h, H);
+        tq.load(P.q, row0, len, h, H);
+        if constexpr (GATE == KDA_GATE_SCALAR) {
+            if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+        } else {
+            Tok<GBF16, DK, DK, 256> tg;
+            tg.load(P.gate, row0, len, h, H);
+            tg.put(sKb, LK);
+        }
+        if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
+        tk.put(sKh, LK);
+        tq.put(sQ, LK);
     }
-    if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
     __syncthreads();
 
-    // b = cumsum(log2 alpha) per channel; Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q
+    // b = cumsum(log2 alpha) per channel (padding rows add 0);
+    // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
     float* gB = rec_at(P, h, g, R::B);
     float* gGam = rec_at(P, h, g, R::GAM);
     float* gKt = rec_at(P, h, g, R::KT);
     for (int c = tid; c < DK; c += 256) {
         float b = 0.f;
         for (int r = 0; r < C; ++r) {
-            b += sKb[r * LK + c];
+            float l2 = 0.f;
+            if (r < len) {
+                if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
+                else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sKb[r * LK + c]);
+                else l2 = __builtin_amdgcn_logf(sKb[r * LK + c]);
+            }
+            b += l2;
             const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
             const float kv = sKh[r * LK + c];
             sKh[r * LK + c] = G * kv;
@@ -282,11 +370,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
             sQ[r * LK + c] *= G;
             gB[r * DK + c] = b;
         }
-        const float gam = __builtin_amdgcn_exp2f(b);
-        gGam[c] = gam;
-        for (int r = 0; r < C; ++r) gKt[r * DK + c] = gam * sKb[r * LK + c];
+        gGam[c] = sGam[c] = __builtin_amdgcn_exp2f(b);
     }
     __syncthreads();
+    for (int idx = tid; idx < C * DK; idx += 256) {
+        const int r = idx / DK, c = idx % DK;
+        gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
+    }
     store_block<256>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
 
     // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record
@@ -298,32 +388,66 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
             acc = mm<DK>((which ? sQ : sKh) + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = mb * 16 + 4 * j + e, s = nb * 16 + i;
-            if (which) acc[e] = s <= r ? acc[e] : 0.f;
-            else acc[e] = s < r ? sBeta[r] * acc[e] : 0.f;
+            const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+            if (which) acc[e] = s2 <= r ? acc[e] : 0.f;
+            else acc[e] = s2 < r ? sBeta[r] * acc[e] : 0.f;
         }
         if (which) store_tile(gP + mb * 16 * C + nb * 16, C, acc);
         else store_tile(sA + mb * 16 * LC + nb * 16, LC, acc);
     }
     __syncthreads();
 
-    // T = (I + A)^-1 by forward substitution, one column per thread
-    if (tid < C) {
-        const int col = tid;
-        for (int r = 0; r < C; ++r) {
+    // T = (I + A)^-1 (A strictly lower) by 16 x 16 blocks: each wave inverts
+    // one diagonal block by substitution (16 lanes, one column each), then
+    // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj for i - j = 1, 2, 3.
+    float* sX = sKb;                     // scratch: one 16 x 16 tile per wave
+    if (lane < 16) {
+        const int col = lane, o = 16 * wave;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
             float x = r == col ? 1.f : 0.f;
-            for (int s = col; s < r; ++s) x -= sA[r * LC + s] * sT[s * LC + col];
-            sT[r * LC + col] = r < col ? 0.f : x;
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2) x -= sA[(o + r) * LC + o + s2] * t[s2];
+            t[r] = x;
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(o + r) * LC + o + col] = t[r];
     }
-    // Y = Diag(beta) Kh (in place); V -> sQ, Z = Diag(beta) V
+    for (int idx = tid; idx < 6 * 256; idx += 256) {      // blocks above the diagonal
+        const int blk = idx >> 8, e = idx & 255;
+        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        sT[(mb * 16 + (e >> 4)) * LC + nb * 16 + (e & 15)] = 0.f;
+    }
+    // Y = Diag(beta) Kh (in place)
     for (int idx = tid; idx < C * DK; idx += 256) {
         const int r = idx / DK, c = idx % DK;
         sKh[r * LK + c] *= sBeta[r];
     }
     __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        if (wave < 4 - d) {
+            const int bi = wave + d, bj = wave;
+            f4 x = zero4();
+            for (int bk = bj; bk < bi; ++bk)
+                x = mm<16>(sA + 16 * bi * LC + 16 * bk, LC, 1, sT + 16 * bk * LC + 16 * bj, LC, 1, x);
+            store_tile(sX + wave * 256, 16, x);
+        }
+        __syncthreads();
+        if (wave < 4 - d) {
+            const int bi = wave + d, bj = wave;
+            const f4 y = mm<16>(sT + 16 * bi * LC + 16 * bi, LC, 1, sX + wave * 256, 16, 1, zero4());
+            store_tile(sT + 16 * bi * LC + 16 * bj, LC, -y);
+        }
+        __syncthreads();
+    }
     store_block<256>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
-    load_tokens<ABF16, DV, 256>(sQ, LV, P.v, row0, len, h, H);
+    {
+        Tok<ABF16, DV, DV, 256> tv;
+        tv.load(P.v, row0, len, h, H);
+        tv.put(sQ, LV);
+    }
     __syncthreads();
     for (int idx = tid; idx < C * DV; idx += 256) {
         const int r = idx / DV, c = idx % DV;
@@ -367,12 +491,12 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
     float* sU = sS + DK * L16;       // [C][16]
     float* sGam = sU + C * L16;      // [DK]
 
-    const int tile = blockIdx.x % NT;
-    const int pair = blockIdx.x / NT;
+    int tile, pair;
+    chain_coords<NT>(tile, pair);
     if (pair >= P.N * P.H) return;
     const int n = P.order[pair / P.H], h = pair % P.H;
     const int g0 = P.first[n], g1 = P.first[n + 1];
-    const int wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+    const int wave = wave_id(), j = lane_id() >> 4;
     const int c0 = tile * 16;
 
     f4 S[RBW];
@@ -382,22 +506,34 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
                    ? load_tile(P.initial_state + (static_cast<size_t>(n) * P.H + h) * DK * DV + rb * 16 * DV + c0, DV)
                    : zero4();
     }
+    // the next chunk's operands, in flight while the current one computes
+    Blk<C, DK, 256> nW, nKt;
+    f4 nU = zero4();
+    float nGam = 0.f;
+    auto fetch = [&](int g) {
+        nW.load(rec_at(P, h, g, R::W), DK);
+        nKt.load(rec_at(P, h, g, R::KT), DK);
+        nU = load_tile(rec_at(P, h, g, R::U) + wave * 16 * DV + c0, DV);
+        if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
+    };
+    if (g0 < g1) fetch(g0);
     for (int g = g0; g < g1; ++g) {
+        nW.put(sW, LK);
+        nKt.put(sKt, LK);
+        const f4 uu = nU;
+        if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         float* gS = rec_at(P, h, g, R::SIN);
         for (int u = 0; u < RBW; ++u) {
             const int rb = wave + 4 * u;
             store_tile(sS + rb * 16 * L16, L16, S[u]);
             store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
         }
-        load_block<256>(sW, LK, rec_at(P, h, g, R::W), DK, C, DK);
-        load_block<256>(sKt, LK, rec_at(P, h, g, R::KT), DK, C, DK);
-        if (threadIdx.x < DK) sGam[threadIdx.x] = rec_at(P, h, g, R::GAM)[threadIdx.x];
         __syncthreads();
+        if (g + 1 < g1) fetch(g + 1);
         // U' = U - W S  (row block = wave)
         {
             const int mb = wave;
             const f4 x = mm<DK>(sW + mb * 16 * LK, LK, 1, sS, L16, 1, zero4());
-            const f4 uu = load_tile(rec_at(P, h, g, R::U) + mb * 16 * DV + c0, DV);
             const f4 uc = uu - x;
             store_tile(sU + mb * 16 * L16, L16, uc);
             store_tile(rec_at(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
@@ -406,14 +542,13 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
         // S <- Diag(gamma) S + Kt^T U'
         for (int u = 0; u < RBW; ++u) {
             const int rb = wave + 4 * u;
-            f4 s = S[u];
+            f4 sv = S[u];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] *= sGam[rb * 16 + 4 * j + e];
-            S[u] = mm<C>(sKt + rb * 16, 1, LK, sU, L16, 1, s);
+            for (int e = 0; e < 4; ++e) sv[e] *= sGam[rb * 16 + 4 * j + e];
+            S[u] = mm<C>(sKt + rb * 16, 1, LK, sU, L16, 1, sv);
         }
         __syncthreads();
     }
-    (void)i;
 }
 
 // ---------------------------------------------------------------------------
@@ -439,8 +574,8 @@ __global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
     float* sdS = sdU + C * L16;      // [DK][16]
     float* sGam = sdS + DK * L16;    // [DK]
 
-    const int tile = blockIdx.x % NT;
-    const int pair = blockIdx.x / NT;
+    int tile, pair;
+    chain_coords<NT>(tile, pair);
     if (pair >= P.N * P.H) return;
     const int H = P.H;
     const int n = P.order[pair / H], h = pair % H;
@@ -454,21 +589,36 @@ __global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
         const int rb = wave + 4 * u;
         dS[u] = P.dfinal_state ? load_tile(P.dfinal_state + sbase + rb * 16 * DV + c0, DV) : zero4();
     }
-    for (int g = g1 - 1; g >= g0; --g) {
+    // the next (earlier) chunk's operands, in flight while the current one computes
+    Blk<C, C, 256> nP;
+    Blk<C, DK, 256> nKt, nQh, nW;
+    Tok<ABF16, DV, 16, 256> ndO;
+    float nGam = 0.f;
+    auto fetch = [&](int g) {
         const int4 ent = P.table[g];
+        nP.load(rec_at(P, h, g, R::P), C);
+        nKt.load(rec_at(P, h, g, R::KT), DK);
+        nQh.load(rec_at(P, h, g, R::QH), DK);
+        nW.load(rec_at(P, h, g, R::W), DK);
+        ndO.load(P.dout, ent.y, ent.z, h, H, c0);
+        if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
+    };
+    if (g1 > g0) fetch(g1 - 1);
+    for (int g = g1 - 1; g >= g0; --g) {
+        nP.put(sP, LC);
+        nKt.put(sKt, LK);
+        nQh.put(sQh, LK);
+        nW.put(sW, LK);
+        ndO.put(sdO, L16);
+        if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         float* gdS = rec_at(P, h, g, R::DSO);
         for (int u = 0; u < RBW; ++u) {
             const int rb = wave + 4 * u;
             store_tile(sdS + rb * 16 * L16, L16, dS[u]);
             store_tile(gdS + rb * 16 * DV + c0, DV, dS[u]);
         }
-        load_block<256>(sP, LC, rec_at(P, h, g, R::P), C, C, C);
-        load_block<256>(sKt, LK, rec_at(P, h, g, R::KT), DK, C, DK);
-        load_block<256>(sQh, LK, rec_at(P, h, g, R::QH), DK, C, DK);
-        load_block<256>(sW, LK, rec_at(P, h, g, R::W), DK, C, DK);
-        load_tokens<ABF16, DV, 256>(sdO, L16, P.dout, ent.y, ent.z, h, H, c0, 16);
-        if (threadIdx.x < DK) sGam[threadIdx.x] = rec_at(P, h, g, R::GAM)[threadIdx.x];
         __syncthreads();
+        if (g > g0) fetch(g - 1);
         // dU' = P^T dO + Kt dS  (row block = wave; P^T[m][k] = P[k][m], zero for k < m)
         {
             const int mb = wave;
@@ -481,12 +631,12 @@ __global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
         // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'
         for (int u = 0; u < RBW; ++u) {
             const int rb = wave + 4 * u;
-            f4 s = dS[u];
+            f4 sv = dS[u];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] *= sGam[rb * 16 + 4 * j + e];
-            s = mm<C>(sQh + rb * 16, 1, LK, sdO, L16, 1, s);
+            for (int e = 0; e < 4; ++e) sv[e] *= sGam[rb * 16 + 4 * j + e];
+            sv = mm<C>(sQh + rb * 16, 1, LK, sdO, L16, 1, sv);
             const f4 x = mm<C>(sW + rb * 16, 1, LK, sdU, L16, 1, zero4());
-            dS[u] = s - x;
+            dS[u] = sv - x;
         }
         __syncthreads();
     }
@@ -533,7 +683,20 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
     const int len = ent.z;
     const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
 
-    load_block<512>(sT, LC, rec_at(P, h, g, R::TT), C, C, C);
+    // value slices, the next one in flight while the current one computes
+    Blk<DK, kSW, 512> nS, ndS;
+    Blk<C, kSW, 512> nUc, ndU;
+    Tok<ABF16, DV, kSW, 512> ndO, nV;
+    auto fetch = [&](int s0) {
+        nS.load(rec_at(P, h, g, R::SIN) + s0, DV);
+        ndS.load(rec_at(P, h, g, R::DSO) + s0, DV);
+        nUc.load(rec_at(P, h, g, R::UC) + s0, DV);
+        ndU.load(rec_at(P, h, g, R::DUC) + s0, DV);
+        ndO.load(P.dout, row0, len, h, H, s0);
+        nV.load(P.v, row0, len, h, H, s0);
+    };
+    fetch(0);
+    load_block<C, C, 512>(sT, LC, rec_at(P, h, g, R::TT), C);
     if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
     f4 acc[KT];
 #pragma unroll
@@ -543,13 +706,14 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
     const int zmb = wave >> 1, znb = wave & 1;      // this wave's block of dZ = T^T dU'[:, slice]
 
     for (int s0 = 0; s0 < DV; s0 += kSW) {
-        load_block<512>(sS, kLS, rec_at(P, h, g, R::SIN) + s0, DV, DK, kSW);
-        load_block<512>(sdS, kLS, rec_at(P, h, g, R::DSO) + s0, DV, DK, kSW);
-        load_block<512>(sUc, kLS, rec_at(P, h, g, R::UC) + s0, DV, C, kSW);
-        load_block<512>(sdU, kLS, rec_at(P, h, g, R::DUC) + s0, DV, C, kSW);
-        load_tokens<ABF16, DV, 512>(sdO, kLS, P.dout, row0, len, h, H, s0, kSW);
-        load_tokens<ABF16, DV, 512>(sV, kLS, P.v, row0, len, h, H, s0, kSW);
+        nS.put(sS, kLS);
+        ndS.put(sdS, kLS);
+        nUc.put(sUc, kLS);
+        ndU.put(sdU, kLS);
+        ndO.put(sdO, kLS);
+        nV.put(sV, kLS);
         __syncthreads();
+        if (s0 + kSW < DV) fetch(s0 + kSW);
         if (tid < DK) {
 #pragma unroll 8
             for (int c = 0; c < kSW; ++c) dgam += sdS[tid * kLS + c] * sS[tid * kLS + c];
@@ -664,15 +828,24 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
     const float* gB = rec_at(P, h, g, R::B);
 
-    load_tokens<ABF16, DK, 256>(sKh, LK, P.k, row0, len, h, H);
-    load_block<256>(sT, LC, rec_at(P, h, g, R::TT), C, C, C);
-    load_block<256>(sW, LK, rec_at(P, h, g, R::DW), DK, C, DK);
+    {
+        Tok<ABF16, DK, DK, 256> tk;
+        Blk<C, C, 256> bt;
+        Blk<C, DK, 256> bw;
+        tk.load(P.k, row0, len, h, H);
+        bt.load(rec_at(P, h, g, R::TT), C);
+        bw.load(rec_at(P, h, g, R::DW), DK);
+        tk.put(sKh, LK);
+        bt.put(sT, LC);
+        bw.put(sW, LK);
+    }
     if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
     sRow[tid] = 0.f;
+    load_block<C, DK, 256>(sKb, LK, gB, DK);
     __syncthreads();
     for (int idx = tid; idx < C * DK; idx += 256) {
         const int r = idx / DK, c = idx % DK;
-        const float b = gB[r * DK + c], kv = sKh[r * LK + c];
+        const float b = sKb[r * LK + c], kv = sKh[r * LK + c];
         sKh[r * LK + c] = __builtin_amdgcn_exp2f(b) * kv;
         sKb[r * LK + c] = __builtin_amdgcn_exp2f(-b) * kv;
     }
@@ -738,8 +911,8 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
         }
     }
     __syncthreads();
-    load_block<256>(sT, LC, rec_at(P, h, g, R::M), C, C, C);
-    load_block<256>(sW, LK, rec_at(P, h, g, R::QH), DK, C, DK);
+    load_block<C, C, 256>(sT, LC, rec_at(P, h, g, R::M), C);
+    load_block<C, DK, 256>(sW, LK, rec_at(P, h, g, R::QH), DK);
     __syncthreads();
 
     // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
@@ -775,8 +948,10 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
                 const float b = gB[r * DK + c];
                 const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
                 const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
-                const float qv = r < len ? act1<ABF16>(P.q, ai) : 0.f;
-                const float kv = r < len ? act1<ABF16>(P.k, ai) : 0.f;
+                // clamped row: every load is issued unconditionally
+                const size_t ac = (static_cast<size_t>(row0 + (r < len ? r : len - 1)) * H + h) * DK + c;
+                const float qraw = act1<ABF16>(P.q, ac), kraw = act1<ABF16>(P.k, ac);
+                const float qv = r < len ? qraw : 0.f, kv = r < len ? kraw : 0.f;
                 const float dkt = gDkt[r * DK + c];
                 const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam * kb;
                 const float dqh = dQh[mb][u][e], dkh = dKh[mb][u][e], dkb = dKb[mb][u][e];
@@ -792,6 +967,12 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
         col += __shfl_xor(col, 32, 64);
         if (j == 0) sCol[c] = col;
     }
+    // the gate as given, for the chain rule below (Kb is no longer needed)
+    if constexpr (GATE == KDA_GATE_SCALAR) {
+        if (tid < C) sKb[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+    } else {
+        load_tokens<GATE == KDA_GATE_SOFTPLUS_BF16, DK, DK, 256>(sKb, LK, P.gate, row0, len, h, H);
+    }
     __syncthreads();
 
     // dlog(alpha)_r = sum_{s >= r} db_s (natural-log units), per channel
@@ -803,10 +984,10 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
             if (r < len) {
                 const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
                 if constexpr (GATE == KDA_GATE_ALPHA) {
-                    P.dgate[ai] = acc / static_cast<const float*>(P.gate)[ai];
+                    P.dgate[ai] = acc / sKb[r * LK + c];
                 } else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
                     // log alpha = -softplus(x): d/dx = -sigmoid(x)
-                    const float x = bf16_to_f32(static_cast<const uint16_t*>(P.gate)[ai]);
+                    const float x = sKb[r * LK + c];
                     const float sg = 1.f / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
                     P.dgate[ai] = -acc * sg;
                 } else {
@@ -820,8 +1001,7 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
         if (tid < len) {
             float s = 0.f;
             for (int c = 0; c < DK; ++c) s += sKh[tid * LK + c];
-            const size_t ai = static_cast<size_t>(row0 + tid) * H + h;
-            P.dgate[ai] = s / static_cast<const float*>(P.gate)[ai];
+            P.dgate[static_cast<size_t>(row0 + tid) * H + h] = s / sKb[tid];
         }
     }
     if (tid < len)
@@ -859,7 +1039,8 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
     hipError_t e = launch_chunk_plan(pl, a.cu_seqlens, a.workspace, stream);
     if (e != hipSuccess) return e;
     const unsigned chunk_blocks = static_cast<unsigned>(pl.gmax * pl.H);
-    const unsigned chain_blocks = static_cast<unsigned>(static_cast<int64_t>(pl.N) * pl.H * (DV / 16));
+    const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
+    const unsigned chain_blocks = static_cast<unsigned>((pairs + 7) / 8 * 8 * (DV / 16));
     if (chunk_blocks > 0) {
         auto k1 = bwd_prep_kernel<DK, DV, ABF16, GATE>;
         constexpr int l1 = PrepB<DK, DV>::bytes;
