@@ -66,30 +66,81 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // mm: acc += sum_{k < K} A(m, k) B(k, n) with A(m, k) = pa[m am + k ak] and
 // B(k, n) = pb[k bk + n bn]; the strides express any transpose.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
 __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Operand values are loaded a batch of steps ahead (two register batches,
+// the next one's LDS reads in flight while the current one's products run).
 template <int K>
 __device__ __forceinline__ f4 mm(const float* pa, int am, int ak, const float* pb, int bk, int bn, f4 acc) {
     const int i = lane_id() & 15, j = lane_id() >> 4;
     pa += i * am + j * ak;
     pb += j * bk + i * bn;
-#pragma unroll 8
-    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * ak], pb[k * bk], acc);
+    constexpr int S = K / 4, BS = S < 8 ? S : 8, NBATCH = S / BS;
+    float a[2][BS], b[2][BS];
+#pragma unroll
+    for (int s = 0; s < BS; ++s) {
+        a[0][s] = pa[4 * s * ak];
+        b[0][s] = pb[4 * s * bk];
+    }
+#pragma unroll
+    for (int nb = 0; nb < NBATCH; ++nb) {
+        const int cur = nb & 1;
+        if (nb + 1 < NBATCH) {
+#pragma unroll
+            for (int s = 0; s < BS; ++s) {
+                a[cur ^ 1][s] = pa[4 * ((nb + 1) * BS + s) * ak];
+                b[cur ^ 1][s] = pb[4 * ((nb + 1) * BS + s) * bk];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < BS; ++s) acc = mfma4(a[cur][s], b[cur][s], acc);
+    }
     return acc;
 }
 
+// Runtime depth K, a multiple of 16: groups of four steps, the next group's
+// operands loaded before the current group's products.
 __device__ __forceinline__ f4 mm_n(const float* pa, int am, int ak, const float* pb, int bk, int bn,
                                    int K, f4 acc) {
     const int i = lane_id() & 15, j = lane_id() >> 4;
     pa += i * am + j * ak;
     pb += j * bk + i * bn;
-    for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * ak], pb[k * bk], acc);
+    if (K <= 0) return acc;
+    float a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        a0[s] = pa[4 * s * ak];
+        b0[s] = pb[4 * s * bk];
+    }
+    for (int k = 0; k < K; k += 32) {
+        const bool more1 = k + 16 < K;
+        if (more1) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                a1[s] = pa[(k + 16 + 4 * s) * ak];
+                b1[s] = pb[(k + 16 + 4 * s) * bk];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma4(a0[s], b0[s], acc);
+        if (!more1) break;
+        if (k + 32 < K) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                a0[s] = pa[(k + 32 + 4 * s) * ak];
+                b0[s] = pb[(k + 32 + 4 * s) * bk];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma4(a1[s], b1[s], acc);
+    }
     return acc;
 }
 
-__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
 // D-layout tile <-> row-major memory (row stride ld, origin at the tile)
 __device__ __forceinline__ void store_tile(float* p, int ld, f4 v) {
@@ -163,7 +214,10 @@ struct Tok {
     static constexpr int V4 = NC / 4, N = C * V4, IT = (N + NTH - 1) / NTH;
     using Raw = typename RawT<BF16>::type;
     Raw t[IT];
+    int len_ = 0;
+    // the rows past len are zeroed in put(), so no load result is needed here
     __device__ __forceinline__ void load(const void* src, int64_t row0, int len, int h, int H, int c0 = 0) {
+        len_ = len;
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
             const int idx = threadIdx.x + it * NTH;
@@ -173,7 +227,6 @@ struct Tok {
                 const size_t off = (static_cast<size_t>(row0 + rr) * H + h) * COLS + c0 + c;
                 if constexpr (BF16) t[it] = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(src) + off);
                 else t[it] = *reinterpret_cast<const f4*>(static_cast<const float*>(src) + off);
-                if (r >= len) t[it] = Raw{0, 0, 0, 0};
             }
         }
     }
@@ -186,6 +239,7 @@ struct Tok {
                 if constexpr (BF16)
                     x = f4{bf16_to_f32(t[it][0]), bf16_to_f32(t[it][1]), bf16_to_f32(t[it][2]), bf16_to_f32(t[it][3])};
                 else x = t[it];
+                if (idx / V4 >= len_) x = zero4();
                 *reinterpret_cast<f4*>(dst + (idx / V4) * ld + (idx % V4) * 4) = x;
             }
         }
@@ -932,34 +986,62 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     }
     __syncthreads();
 
-    // gate chain rule, dq, dk; db -> sKh; column sums of Kt . dKt -> sCol
+    // gate chain rule, dq, dk.  Every operand is staged in LDS first (the
+    // regions are free now), so no load waits behind a store of dq or dk:
+    // q -> sKh, k -> sKb, b -> sW, dKt -> sX (sX and sY are contiguous).
     const float* gGam = rec_at(P, h, g, R::GAM);
     const float* gDkt = rec_at(P, h, g, R::DKT);
+    const float* gDgam = rec_at(P, h, g, R::DGAM);
+    float* sD = sX;                          // dKt, row stride LK
+    static_assert(C * LK <= 2 * C * LC, "dKt staging spans the sX and sY regions");
+    constexpr int NS = 256 / DK, SEG = C / NS;   // reverse-cumsum split: NS row segments per channel
+    float gam_u[CBW];
+    Tok<GATE == KDA_GATE_SOFTPLUS_BF16, DK, DK, 256> tg;
+    float gs = 1.f;
+    float gam_t = 0.f, dgam_t = 0.f;
+    {
+        Tok<ABF16, DK, DK, 256> tq, tk;
+        Blk<C, DK, 256> bb, bd;
+        tq.load(P.q, row0, len, h, H);
+        tk.load(P.k, row0, len, h, H);
+        bb.load(gB, DK);
+        bd.load(gDkt, DK);
+        if constexpr (GATE == KDA_GATE_SCALAR) {
+            if (tid < C && tid < len) gs = static_cast<const float*>(P.gate)[(row0 + tid) * H + h];
+        } else {
+            tg.load(P.gate, row0, len, h, H);
+        }
+#pragma unroll
+        for (int u = 0; u < CBW; ++u) gam_u[u] = gGam[(wave + 4 * u) * 16 + i];
+        gam_t = gGam[tid % DK];
+        dgam_t = gDgam[tid % DK];
+        tq.put(sKh, LK);
+        tk.put(sKb, LK);
+        bb.put(sW, LK);
+        bd.put(sD, LK);
+    }
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < CBW; ++u) {
         const int nb = wave + 4 * u, c = nb * 16 + i;
-        const float gam = gGam[c];
+        const float gam = gam_u[u];
         float col = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = mb * 16 + 4 * j + e;
-                const float b = gB[r * DK + c];
+                const float b = sW[r * LK + c];
                 const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-                const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
-                // clamped row: every load is issued unconditionally
-                const size_t ac = (static_cast<size_t>(row0 + (r < len ? r : len - 1)) * H + h) * DK + c;
-                const float qraw = act1<ABF16>(P.q, ac), kraw = act1<ABF16>(P.k, ac);
-                const float qv = r < len ? qraw : 0.f, kv = r < len ? kraw : 0.f;
-                const float dkt = gDkt[r * DK + c];
+                const float qv = sKh[r * LK + c], kv = sKb[r * LK + c], dkt = sD[r * LK + c];
                 const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam * kb;
                 const float dqh = dQh[mb][u][e], dkh = dKh[mb][u][e], dkb = dKb[mb][u][e];
                 if (r < len) {
+                    const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
                     store_out<ABF16>(P.dq, ai, G * dqh);
                     store_out<ABF16>(P.dk, ai, G * dkh + Gi * dkb + gam * Gi * dkt);
                 }
-                sKh[r * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;
+                sKh[r * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;   // db
                 col += kt * dkt;
             }
         }
@@ -967,31 +1049,41 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
         col += __shfl_xor(col, 32, 64);
         if (j == 0) sCol[c] = col;
     }
-    // the gate as given, for the chain rule below (Kb is no longer needed)
+    __syncthreads();
+    // the gate as given (b is no longer needed); partial sums of db per segment
     if constexpr (GATE == KDA_GATE_SCALAR) {
-        if (tid < C) sKb[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+        if (tid < C) sW[tid] = gs;
     } else {
-        load_tokens<GATE == KDA_GATE_SOFTPLUS_BF16, DK, DK, 256>(sKb, LK, P.gate, row0, len, h, H);
+        tg.put(sW, LK);
+    }
+    float* sPart = sT;                       // [NS][DK]
+    {
+        const int c = tid % DK, sg = tid / DK;
+        float part = 0.f;
+        for (int r = sg * SEG; r < sg * SEG + SEG; ++r) part += sKh[r * LK + c];
+        sPart[sg * DK + c] = part;
     }
     __syncthreads();
 
-    // dlog(alpha)_r = sum_{s >= r} db_s (natural-log units), per channel
-    const float* gDgam = rec_at(P, h, g, R::DGAM);
-    for (int c = tid; c < DK; c += 256) {
-        float acc = gGam[c] * gDgam[c] + sCol[c];
-        for (int r = C - 1; r >= 0; --r) {
+    // dlog(alpha)_r = sum_{s >= r} db_s (natural-log units), per channel; gamma's own
+    // gradient and the Kt terms enter at the last row
+    {
+        const int c = tid % DK, sg = tid / DK;
+        float acc = gam_t * dgam_t + sCol[c];
+        for (int s2 = sg + 1; s2 < NS; ++s2) acc += sPart[s2 * DK + c];
+        for (int r = sg * SEG + SEG - 1; r >= sg * SEG; --r) {
             acc += sKh[r * LK + c];
             if (r < len) {
                 const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
                 if constexpr (GATE == KDA_GATE_ALPHA) {
-                    P.dgate[ai] = acc / sKb[r * LK + c];
+                    P.dgate[ai] = acc / sW[r * LK + c];
                 } else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
                     // log alpha = -softplus(x): d/dx = -sigmoid(x)
-                    const float x = sKb[r * LK + c];
-                    const float sg = 1.f / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
-                    P.dgate[ai] = -acc * sg;
+                    const float x = sW[r * LK + c];
+                    const float sgm = 1.f / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+                    P.dgate[ai] = -acc * sgm;
                 } else {
-                    sKh[r * LK + c] = acc;
+                    sKb[r * LK + c] = acc;
                 }
             }
         }
@@ -1000,8 +1092,8 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
         __syncthreads();
         if (tid < len) {
             float s = 0.f;
-            for (int c = 0; c < DK; ++c) s += sKh[tid * LK + c];
-            P.dgate[static_cast<size_t>(row0 + tid) * H + h] = s / sKb[tid];
+            for (int c = 0; c < DK; ++c) s += sKb[tid * LK + c];
+            P.dgate[static_cast<size_t>(row0 + tid) * H + h] = s / sW[tid];
         }
     }
     if (tid < len)
