@@ -61,10 +61,16 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ---------------------------------------------------------------------------
 // 16x16 fp32 matrix-core tile, 4-deep steps (v_mfma_f32_16x16x4f32):
-//   A lane l holds A[l % 16][l / 16], B lane l holds B[l / 16][l % 16],
-//   D lane l holds D[4 (l / 16) + e][l % 16], e = 0..3.
+//   A lane l holds A[l % 16][k], B lane l holds B[k][l % 16] for the step's
+//   k, D lane l holds D[4 (l / 16) + e][l % 16], e = 0..3.
 // mm: acc += sum_{k < K} A(m, k) B(k, n) with A(m, k) = pa[m am + k ak] and
 // B(k, n) = pb[k bk + n bn]; the strides express any transpose.
+// Within each 16-deep group of the reduction, lane group j = l / 16 takes
+// the indices 4j..4j+3 in the group's four steps (any assignment gives the
+// same product when both operands follow it), so an operand that is
+// contiguous along the reduction (AV: ak == 1, BV: bk == 1) is read with one
+// 16-byte LDS load per group instead of four.  Each group's operands are
+// loaded one group ahead of its products.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
@@ -72,75 +78,64 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// Operand values are loaded a batch of steps ahead (two register batches,
-// the next one's LDS reads in flight while the current one's products run).
-template <int K>
+template <bool V>
+__device__ __forceinline__ f4 grp4(const float* p, int stride) {
+    if constexpr (V) return *reinterpret_cast<const f4*>(p);
+    else return f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
+}
+
+template <int K, bool AV, bool BV>
 __device__ __forceinline__ f4 mm(const float* pa, int am, int ak, const float* pb, int bk, int bn, f4 acc) {
     const int i = lane_id() & 15, j = lane_id() >> 4;
-    pa += i * am + j * ak;
-    pb += j * bk + i * bn;
-    constexpr int S = K / 4, BS = S < 8 ? S : 8, NBATCH = S / BS;
-    float a[2][BS], b[2][BS];
-#pragma unroll
-    for (int s = 0; s < BS; ++s) {
-        a[0][s] = pa[4 * s * ak];
-        b[0][s] = pb[4 * s * bk];
+    pa += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
+    constexpr int G = K / 16;
+    f4 a[3], b[3];
+    a[0] = grp4<AV>(pa, ak);
+    b[0] = grp4<BV>(pb, bk);
+    if constexpr (G > 1) {
+        a[1] = grp4<AV>(pa + 16 * ak, ak);
+        b[1] = grp4<BV>(pb + 16 * bk, bk);
     }
 #pragma unroll
-    for (int nb = 0; nb < NBATCH; ++nb) {
-        const int cur = nb & 1;
-        if (nb + 1 < NBATCH) {
-#pragma unroll
-            for (int s = 0; s < BS; ++s) {
-                a[cur ^ 1][s] = pa[4 * ((nb + 1) * BS + s) * ak];
-                b[cur ^ 1][s] = pb[4 * ((nb + 1) * BS + s) * bk];
-            }
+    for (int g = 0; g < G; ++g) {
+        if (g + 2 < G) {
+            a[(g + 2) % 3] = grp4<AV>(pa + 16 * (g + 2) * ak, ak);
+            b[(g + 2) % 3] = grp4<BV>(pb + 16 * (g + 2) * bk, bk);
         }
 #pragma unroll
-        for (int s = 0; s < BS; ++s) acc = mfma4(a[cur][s], b[cur][s], acc);
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a[g % 3][s2], b[g % 3][s2], acc);
     }
     return acc;
 }
 
-// Runtime depth K, a multiple of 16: groups of four steps, the next group's
-// operands loaded before the current group's products.
+// Runtime depth K, a multiple of 16.
+template <bool AV, bool BV>
 __device__ __forceinline__ f4 mm_n(const float* pa, int am, int ak, const float* pb, int bk, int bn,
                                    int K, f4 acc) {
     const int i = lane_id() & 15, j = lane_id() >> 4;
-    pa += i * am + j * ak;
-    pb += j * bk + i * bn;
+    pa += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
     if (K <= 0) return acc;
-    float a0[4], b0[4], a1[4], b1[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        a0[s] = pa[4 * s * ak];
-        b0[s] = pb[4 * s * bk];
-    }
+    f4 a0 = grp4<AV>(pa, ak), b0 = grp4<BV>(pb, bk), a1, b1;
     for (int k = 0; k < K; k += 32) {
         const bool more1 = k + 16 < K;
         if (more1) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                a1[s] = pa[(k + 16 + 4 * s) * ak];
-                b1[s] = pb[(k + 16 + 4 * s) * bk];
-            }
+            a1 = grp4<AV>(pa + (k + 16) * ak, ak);
+            b1 = grp4<BV>(pb + (k + 16) * bk, bk);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma4(a0[s], b0[s], acc);
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a0[s2], b0[s2], acc);
         if (!more1) break;
         if (k + 32 < K) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                a0[s] = pa[(k + 32 + 4 * s) * ak];
-                b0[s] = pb[(k + 32 + 4 * s) * bk];
-            }
+            a0 = grp4<AV>(pa + (k + 32) * ak, ak);
+            b0 = grp4<BV>(pb + (k + 32) * bk, bk);
         }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma4(a1[s], b1[s], acc);
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a1[s2], b1[s2], acc);
     }
     return acc;
 }
-
 
 // D-layout tile <-> row-major memory (row stride ld, origin at the tile)
 __device__ __forceinline__ void store_tile(float* p, int ld, f4 v) {
@@ -357,14 +352,17 @@ __device__ __forceinline__ float* rec_at(const BwdParams& P, int h, int g, size_
 // ---------------------------------------------------------------------------
 // bwd_prep_kernel: one (chunk, head), 256 threads.
 // ---------------------------------------------------------------------------
+constexpr int kPrepThreads = 512, kPrepWaves = kPrepThreads / 64;
+
 template <int DK, int DV> struct PrepB {
     static constexpr int LK = Ld<DK>::value, LV = Ld<DV>::value, LM = LK > LV ? LK : LV;
     static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + 2 * C + DK) * 4;
 };
 
 template <int DK, int DV, bool ABF16, int GATE>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
+    constexpr int NTH = kPrepThreads, NW = kPrepWaves;
     constexpr int LK = PrepB<DK, DV>::LK, LV = PrepB<DK, DV>::LV;
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
@@ -386,13 +384,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
     const int tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
 
     {
-        Tok<ABF16, DK, DK, 256> tk, tq;
+        Tok<ABF16, DK, DK, NTH> tk, tq;
         tk.load(P.k, row0, len, h, H);
         tq.load(P.q, row0, len, h, H);
         if constexpr (GATE == KDA_GATE_SCALAR) {
             if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
         } else {
-            Tok<GBF16, DK, DK, 256> tg;
+            Tok<GBF16, DK, DK, NTH> tg;
             tg.load(P.gate, row0, len, h, H);
             tg.put(sKb, LK);
         }
@@ -402,21 +400,37 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
     }
     __syncthreads();
 
-    // b = cumsum(log2 alpha) per channel (padding rows add 0);
+    // b = cumsum(log2 alpha) per channel (padding rows add 0), in NS row
+    // segments per channel: segment sums first, then each segment's scan from
+    // the sum of the segments before it.
     // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
     float* gB = rec_at(P, h, g, R::B);
     float* gGam = rec_at(P, h, g, R::GAM);
     float* gKt = rec_at(P, h, g, R::KT);
-    for (int c = tid; c < DK; c += 256) {
-        float b = 0.f;
-        for (int r = 0; r < C; ++r) {
+    constexpr int NS = NTH / DK, SEG = C / NS;
+    float* sPart = sA;                   // [NS][DK] (A is formed later)
+    {
+        const int c = tid % DK, sg = tid / DK;
+        float part = 0.f;
+        for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
             float l2 = 0.f;
             if (r < len) {
                 if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
                 else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sKb[r * LK + c]);
                 else l2 = __builtin_amdgcn_logf(sKb[r * LK + c]);
             }
-            b += l2;
+            sKb[r * LK + c] = l2;
+            part += l2;
+        }
+        sPart[sg * DK + c] = part;
+    }
+    __syncthreads();
+    {
+        const int c = tid % DK, sg = tid / DK;
+        float b = 0.f;
+        for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * DK + c];
+        for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
+            b += sKb[r * LK + c];
             const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
             const float kv = sKh[r * LK + c];
             sKh[r * LK + c] = G * kv;
@@ -424,22 +438,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
             sQ[r * LK + c] *= G;
             gB[r * DK + c] = b;
         }
-        gGam[c] = sGam[c] = __builtin_amdgcn_exp2f(b);
+        if (sg == NS - 1) gGam[c] = sGam[c] = __builtin_amdgcn_exp2f(b);
     }
     __syncthreads();
-    for (int idx = tid; idx < C * DK; idx += 256) {
+    for (int idx = tid; idx < C * DK; idx += NTH) {
         const int r = idx / DK, c = idx % DK;
         gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
     }
-    store_block<256>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
+    store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
 
     // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record
     float* gP = rec_at(P, h, g, R::P);
-    for (int t = wave; t < 32; t += 4) {
+    for (int t = wave; t < 32; t += NW) {
         const int which = t >> 4, mb = (t >> 2) & 3, nb = t & 3;
         f4 acc = zero4();
         if (nb <= mb)
-            acc = mm<DK>((which ? sQ : sKh) + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, acc);
+            acc = mm<DK, true, true>((which ? sQ : sKh) + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, acc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
@@ -455,7 +469,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
     // one diagonal block by substitution (16 lanes, one column each), then
     // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj for i - j = 1, 2, 3.
     float* sX = sKb;                     // scratch: one 16 x 16 tile per wave
-    if (lane < 16) {
+    if (wave < 4 && lane < 16) {
         const int col = lane, o = 16 * wave;
         float t[16];
 #pragma unroll
@@ -468,14 +482,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(o + r) * LC + o + col] = t[r];
     }
-    for (int idx = tid; idx < 6 * 256; idx += 256) {      // blocks above the diagonal
+    for (int idx = tid; idx < 6 * 256; idx += NTH) {      // blocks above the diagonal
         const int blk = idx >> 8, e = idx & 255;
         const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
         const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
         sT[(mb * 16 + (e >> 4)) * LC + nb * 16 + (e & 15)] = 0.f;
     }
     // Y = Diag(beta) Kh (in place)
-    for (int idx = tid; idx < C * DK; idx += 256) {
+    for (int idx = tid; idx < C * DK; idx += NTH) {
         const int r = idx / DK, c = idx % DK;
         sKh[r * LK + c] *= sBeta[r];
     }
@@ -485,25 +499,25 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
             const int bi = wave + d, bj = wave;
             f4 x = zero4();
             for (int bk = bj; bk < bi; ++bk)
-                x = mm<16>(sA + 16 * bi * LC + 16 * bk, LC, 1, sT + 16 * bk * LC + 16 * bj, LC, 1, x);
+                x = mm<16, true, false>(sA + 16 * bi * LC + 16 * bk, LC, 1, sT + 16 * bk * LC + 16 * bj, LC, 1, x);
             store_tile(sX + wave * 256, 16, x);
         }
         __syncthreads();
         if (wave < 4 - d) {
             const int bi = wave + d, bj = wave;
-            const f4 y = mm<16>(sT + 16 * bi * LC + 16 * bi, LC, 1, sX + wave * 256, 16, 1, zero4());
+            const f4 y = mm<16, true, false>(sT + 16 * bi * LC + 16 * bi, LC, 1, sX + wave * 256, 16, 1, zero4());
             store_tile(sT + 16 * bi * LC + 16 * bj, LC, -y);
         }
         __syncthreads();
     }
-    store_block<256>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
+    store_block<NTH>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
     {
-        Tok<ABF16, DV, DV, 256> tv;
+        Tok<ABF16, DV, DV, NTH> tv;
         tv.load(P.v, row0, len, h, H);
         tv.put(sQ, LV);
     }
     __syncthreads();
-    for (int idx = tid; idx < C * DV; idx += 256) {
+    for (int idx = tid; idx < C * DV; idx += NTH) {
         const int r = idx / DV, c = idx % DV;
         sQ[r * LV + c] *= sBeta[r];
     }
@@ -513,12 +527,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
     float* gW = rec_at(P, h, g, R::W);
     float* gU = rec_at(P, h, g, R::U);
     constexpr int NK = DK / 16, NV = DV / 16;
-    for (int t = wave; t < 4 * (NK + NV); t += 4) {
+    for (int t = wave; t < 4 * (NK + NV); t += NW) {
         const bool isw = t < 4 * NK;
         const int tt = isw ? t : t - 4 * NK;
         const int nn = isw ? NK : NV;
         const int mb = tt / nn, nb = tt % nn;
-        const f4 acc = mm_n(sT + mb * 16 * LC, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1,
+        const f4 acc = mm_n<true, false>(sT + mb * 16 * LC, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1,
                             (mb + 1) * 16, zero4());
         if (isw) store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
         else store_tile(gU + mb * 16 * DV + nb * 16, DV, acc);
@@ -526,24 +540,31 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const BwdParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_ckpt_kernel: one (sequence, head, 16 value columns), 256 threads.
-// Wave w computes U' rows 16w..16w+15 and owns state row blocks w, w+4, ...
+// Sequential passes: one 512-thread WG per (sequence, head, 16 value
+// columns).  The d_k x 16 state tile is kept in registers, row block rb in
+// wave rb (and rb - 8 for d_k > 128); the C x 16 per-chunk product (U' or
+// dU') is split over the two halves of the workgroup, waves 4..7 handing
+// their partial sums to waves 0..3 through LDS.
 // ---------------------------------------------------------------------------
+constexpr int kChainThreads = 512, kChainWaves = kChainThreads / 64;
+
 template <int DK> struct CkptB {
     static constexpr int LK = Ld<DK>::value;
-    static constexpr int bytes = (2 * C * LK + DK * L16 + C * L16 + DK) * 4;
+    static constexpr int bytes = (2 * C * LK + DK * L16 + 2 * C * L16 + DK) * 4;
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kChainThreads) void bwd_ckpt_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
-    constexpr int LK = CkptB<DK>::LK, NT = DV / 16, RBW = DK / 64;
+    constexpr int NTH = kChainThreads, NW = kChainWaves;
+    constexpr int LK = CkptB<DK>::LK, NT = DV / 16, NRB = DK / 16, RBW = (NRB + NW - 1) / NW;
     extern __shared__ float lds[];
     float* sW = lds;                 // [C][LK]
     float* sKt = sW + C * LK;        // [C][LK]
     float* sS = sKt + C * LK;        // [DK][16]
     float* sU = sS + DK * L16;       // [C][16]
-    float* sGam = sU + C * L16;      // [DK]
+    float* sPart = sU + C * L16;     // [C][16] partial W S from waves 4..7
+    float* sGam = sPart + C * L16;   // [DK]
 
     int tile, pair;
     chain_coords<NT>(tile, pair);
@@ -552,22 +573,23 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
     const int g0 = P.first[n], g1 = P.first[n + 1];
     const int wave = wave_id(), j = lane_id() >> 4;
     const int c0 = tile * 16;
+    const int mb = wave & 3, khalf = wave >> 2;          // U' row block and half of the d_k reduction
 
     f4 S[RBW];
     for (int u = 0; u < RBW; ++u) {
-        const int rb = wave + 4 * u;
-        S[u] = P.initial_state
+        const int rb = wave + NW * u;
+        S[u] = (P.initial_state && rb < NRB)
                    ? load_tile(P.initial_state + (static_cast<size_t>(n) * P.H + h) * DK * DV + rb * 16 * DV + c0, DV)
                    : zero4();
     }
     // the next chunk's operands, in flight while the current one computes
-    Blk<C, DK, 256> nW, nKt;
+    Blk<C, DK, NTH> nW, nKt;
     f4 nU = zero4();
     float nGam = 0.f;
     auto fetch = [&](int g) {
         nW.load(rec_at(P, h, g, R::W), DK);
         nKt.load(rec_at(P, h, g, R::KT), DK);
-        nU = load_tile(rec_at(P, h, g, R::U) + wave * 16 * DV + c0, DV);
+        if (khalf == 0) nU = load_tile(rec_at(P, h, g, R::U) + mb * 16 * DV + c0, DV);
         if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
     };
     if (g0 < g1) fetch(g0);
@@ -578,46 +600,48 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(const BwdParams P) {
         if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         float* gS = rec_at(P, h, g, R::SIN);
         for (int u = 0; u < RBW; ++u) {
-            const int rb = wave + 4 * u;
+            const int rb = wave + NW * u;
+            if (rb >= NRB) continue;
             store_tile(sS + rb * 16 * L16, L16, S[u]);
             store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
         }
         __syncthreads();
         if (g + 1 < g1) fetch(g + 1);
-        // U' = U - W S  (row block = wave)
-        {
-            const int mb = wave;
-            const f4 x = mm<DK>(sW + mb * 16 * LK, LK, 1, sS, L16, 1, zero4());
-            const f4 uc = uu - x;
+        // U' = U - W S  (row block mb, d_k split over the two halves)
+        const f4 x = mm<DK / 2, true, false>(sW + mb * 16 * LK + khalf * (DK / 2), LK, 1,
+                                             sS + khalf * (DK / 2) * L16, L16, 1, zero4());
+        if (khalf) store_tile(sPart + mb * 16 * L16, L16, x);
+        __syncthreads();
+        if (!khalf) {
+            const f4 uc = uu - x - load_tile(sPart + mb * 16 * L16, L16);
             store_tile(sU + mb * 16 * L16, L16, uc);
             store_tile(rec_at(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
         }
         __syncthreads();
         // S <- Diag(gamma) S + Kt^T U'
         for (int u = 0; u < RBW; ++u) {
-            const int rb = wave + 4 * u;
+            const int rb = wave + NW * u;
+            if (rb >= NRB) continue;
             f4 sv = S[u];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sv[e] *= sGam[rb * 16 + 4 * j + e];
-            S[u] = mm<C>(sKt + rb * 16, 1, LK, sU, L16, 1, sv);
+            S[u] = mm<C, false, false>(sKt + rb * 16, 1, LK, sU, L16, 1, sv);
         }
         __syncthreads();
     }
 }
 
-// ---------------------------------------------------------------------------
-// bwd_rev_kernel: one (sequence, head, 16 value columns), 256 threads,
-// chunks last to first.
-// ---------------------------------------------------------------------------
 template <int DK> struct RevB {
     static constexpr int LK = Ld<DK>::value;
-    static constexpr int bytes = (C * LC + 3 * C * LK + 2 * C * L16 + DK * L16 + DK) * 4;
+    static constexpr int bytes = (C * LC + 3 * C * LK + 3 * C * L16 + DK * L16 + DK) * 4;
 };
 
+// chunks last to first
 template <int DK, int DV, bool ABF16>
-__global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kChainThreads) void bwd_rev_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
-    constexpr int LK = RevB<DK>::LK, NT = DV / 16, RBW = DK / 64;
+    constexpr int NTH = kChainThreads, NW = kChainWaves;
+    constexpr int LK = RevB<DK>::LK, NT = DV / 16, NRB = DK / 16, RBW = (NRB + NW - 1) / NW;
     extern __shared__ float lds[];
     float* sP = lds;                 // [C][LC]
     float* sKt = sP + C * LC;        // [C][LK]
@@ -625,7 +649,8 @@ __global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
     float* sW = sQh + C * LK;        // [C][LK]
     float* sdO = sW + C * LK;        // [C][16]
     float* sdU = sdO + C * L16;      // [C][16]
-    float* sdS = sdU + C * L16;      // [DK][16]
+    float* sPart = sdU + C * L16;    // [C][16] partial P^T dO from waves 4..7
+    float* sdS = sPart + C * L16;    // [DK][16]
     float* sGam = sdS + DK * L16;    // [DK]
 
     int tile, pair;
@@ -636,17 +661,18 @@ __global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
     const int g0 = P.first[n], g1 = P.first[n + 1];
     const int wave = wave_id(), j = lane_id() >> 4;
     const int c0 = tile * 16;
+    const int mb = wave & 3, half = wave >> 2;           // dU' row block; half 0: Kt dS, half 1: P^T dO
     const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
 
     f4 dS[RBW];
     for (int u = 0; u < RBW; ++u) {
-        const int rb = wave + 4 * u;
-        dS[u] = P.dfinal_state ? load_tile(P.dfinal_state + sbase + rb * 16 * DV + c0, DV) : zero4();
+        const int rb = wave + NW * u;
+        dS[u] = (P.dfinal_state && rb < NRB) ? load_tile(P.dfinal_state + sbase + rb * 16 * DV + c0, DV) : zero4();
     }
     // the next (earlier) chunk's operands, in flight while the current one computes
-    Blk<C, C, 256> nP;
-    Blk<C, DK, 256> nKt, nQh, nW;
-    Tok<ABF16, DV, 16, 256> ndO;
+    Blk<C, C, NTH> nP;
+    Blk<C, DK, NTH> nKt, nQh, nW;
+    Tok<ABF16, DV, 16, NTH> ndO;
     float nGam = 0.f;
     auto fetch = [&](int g) {
         const int4 ent = P.table[g];
@@ -667,36 +693,46 @@ __global__ __launch_bounds__(256) void bwd_rev_kernel(const BwdParams P) {
         if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         float* gdS = rec_at(P, h, g, R::DSO);
         for (int u = 0; u < RBW; ++u) {
-            const int rb = wave + 4 * u;
+            const int rb = wave + NW * u;
+            if (rb >= NRB) continue;
             store_tile(sdS + rb * 16 * L16, L16, dS[u]);
             store_tile(gdS + rb * 16 * DV + c0, DV, dS[u]);
         }
         __syncthreads();
         if (g > g0) fetch(g - 1);
-        // dU' = P^T dO + Kt dS  (row block = wave; P^T[m][k] = P[k][m], zero for k < m)
-        {
-            const int mb = wave;
-            f4 acc = mm_n(sP + mb * 16 * LC + mb * 16, 1, LC, sdO + mb * 16 * L16, L16, 1, C - mb * 16, zero4());
-            acc = mm<DK>(sKt + mb * 16 * LK, LK, 1, sdS, L16, 1, acc);
+        // dU' = Kt dS + P^T dO  (row block mb; P^T[m][k] = P[k][m], zero for k < m)
+        f4 acc;
+        if (half == 0) {
+            acc = mm<DK, true, false>(sKt + mb * 16 * LK, LK, 1, sdS, L16, 1, zero4());
+        } else {
+            acc = mm_n<false, false>(sP + mb * 16 * LC + mb * 16, 1, LC, sdO + mb * 16 * L16, L16, 1, C - mb * 16,
+                                     zero4());
+            store_tile(sPart + mb * 16 * L16, L16, acc);
+        }
+        __syncthreads();
+        if (half == 0) {
+            acc += load_tile(sPart + mb * 16 * L16, L16);
             store_tile(sdU + mb * 16 * L16, L16, acc);
             store_tile(rec_at(P, h, g, R::DUC) + mb * 16 * DV + c0, DV, acc);
         }
         __syncthreads();
         // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'
         for (int u = 0; u < RBW; ++u) {
-            const int rb = wave + 4 * u;
+            const int rb = wave + NW * u;
+            if (rb >= NRB) continue;
             f4 sv = dS[u];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sv[e] *= sGam[rb * 16 + 4 * j + e];
-            sv = mm<C>(sQh + rb * 16, 1, LK, sdO, L16, 1, sv);
-            const f4 x = mm<C>(sW + rb * 16, 1, LK, sdU, L16, 1, zero4());
+            sv = mm<C, false, false>(sQh + rb * 16, 1, LK, sdO, L16, 1, sv);
+            const f4 x = mm<C, false, false>(sW + rb * 16, 1, LK, sdU, L16, 1, zero4());
             dS[u] = sv - x;
         }
         __syncthreads();
     }
     if (P.dinitial_state) {
         for (int u = 0; u < RBW; ++u) {
-            const int rb = wave + 4 * u;
+            const int rb = wave + NW * u;
+            if (rb >= NRB) continue;
             store_tile(P.dinitial_state + sbase + rb * 16 * DV + c0, DV, dS[u]);
         }
     }
@@ -791,12 +827,12 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
                     pa = sdU + mb * 16 * kLS;
                     pb = sV + nb * 16 * kLS;
                 }
-                acc[k] = mm<kSW>(pa, kLS, 1, pb, 1, kLS, acc[k]);
+                acc[k] = mm<kSW, true, true>(pa, kLS, 1, pb, 1, kLS, acc[k]);
             }
         }
         // dZ = T^T dU'[:, slice] (T^T[m][k] = T[k][m], zero for k < m); dv = beta . dZ
         {
-            const f4 z = mm_n(sT + zmb * 16 * LC + zmb * 16, 1, LC, sdU + zmb * 16 * kLS + znb * 16, kLS, 1,
+            const f4 z = mm_n<false, false>(sT + zmb * 16 * LC + zmb * 16, 1, LC, sdU + zmb * 16 * kLS + znb * 16, kLS, 1,
                               C - zmb * 16, zero4());
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -853,15 +889,19 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
 // bwd_kside_kernel: one (chunk, head), 256 threads.  Wave w owns the key
 // column blocks w, w + 4, ... of every C x DK gradient.
 // ---------------------------------------------------------------------------
+constexpr int kKsideThreads = 512, kKsideWaves = kKsideThreads / 64;
+
 template <int DK> struct KsideB {
     static constexpr int LK = Ld<DK>::value;
-    static constexpr int bytes = (3 * C * LK + 3 * C * LC + 5 * C + DK) * 4;
+    static constexpr int bytes = (3 * C * LK + 3 * C * LC + (2 + kKsideWaves) * C + DK) * 4;
 };
 
 template <int DK, int DV, bool ABF16, int GATE>
-__global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
-    constexpr int LK = KsideB<DK>::LK, CBW = DK / 64;
+    // eight waves; wave w owns the key column blocks w, w + 8, ... of every C x DK gradient
+    constexpr int NTH = kKsideThreads, NW = kKsideWaves, LK = KsideB<DK>::LK, NCB = DK / 16;
+    constexpr int CBW = (NCB + NW - 1) / NW;
     extern __shared__ float lds[];
     float* sKh = lds;                // Gamma.K; later db                       [C][LK]
     float* sKb = sKh + C * LK;       // K / Gamma                               [C][LK]
@@ -870,8 +910,8 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     float* sY = sX + C * LC;         // T^T dT                                  [C][LC]
     float* sT = sY + C * LC;         // T; later M                              [C][LC]
     float* sBeta = sT + C * LC;      // [C]
-    float* sRow = sBeta + C;         // dbeta parts (A and Y), one row per wave [4][C]
-    float* sCol = sRow + 4 * C;      // column sums of Kt . dKt                  [DK]
+    float* sRow = sBeta + C;         // dbeta parts (A and Y), one row per wave [NW][C]
+    float* sCol = sRow + NW * C;     // column sums of Kt . dKt                  [DK]
 
     const int H = P.H;
     const int h = blockIdx.x % H, g = blockIdx.x / H;
@@ -883,9 +923,9 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     const float* gB = rec_at(P, h, g, R::B);
 
     {
-        Tok<ABF16, DK, DK, 256> tk;
-        Blk<C, C, 256> bt;
-        Blk<C, DK, 256> bw;
+        Tok<ABF16, DK, DK, NTH> tk;
+        Blk<C, C, NTH> bt;
+        Blk<C, DK, NTH> bw;
         tk.load(P.k, row0, len, h, H);
         bt.load(rec_at(P, h, g, R::TT), C);
         bw.load(rec_at(P, h, g, R::DW), DK);
@@ -894,10 +934,10 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
         bw.put(sW, LK);
     }
     if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
-    sRow[tid] = 0.f;
-    load_block<C, DK, 256>(sKb, LK, gB, DK);
+    for (int idx = tid; idx < NW * C; idx += NTH) sRow[idx] = 0.f;
+    load_block<C, DK, NTH>(sKb, LK, gB, DK);
     __syncthreads();
-    for (int idx = tid; idx < C * DK; idx += 256) {
+    for (int idx = tid; idx < C * DK; idx += NTH) {
         const int r = idx / DK, c = idx % DK;
         const float b = sKb[r * LK + c], kv = sKh[r * LK + c];
         sKh[r * LK + c] = __builtin_amdgcn_exp2f(b) * kv;
@@ -906,30 +946,30 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     __syncthreads();
 
     // dT = (dW Kh^T + N) Diag(beta)
-    for (int t = wave; t < 16; t += 4) {
+    for (int t = wave; t < 16; t += NW) {
         const int mb = t >> 2, nb = t & 3;
         f4 acc = load_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C);
-        acc = mm<DK>(sW + mb * 16 * LK, LK, 1, sKh + nb * 16 * LK, 1, LK, acc);
+        acc = mm<DK, true, true>(sW + mb * 16 * LK, LK, 1, sKh + nb * 16 * LK, 1, LK, acc);
         acc *= sBeta[nb * 16 + i];
         store_tile(sX + mb * 16 * LC + nb * 16, LC, acc);
     }
     __syncthreads();
     // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m)
-    for (int t = wave; t < 16; t += 4) {
+    for (int t = wave; t < 16; t += NW) {
         const int mb = t >> 2, nb = t & 3;
-        const f4 acc = mm_n(sT + mb * 16 * LC + mb * 16, 1, LC, sX + mb * 16 * LC + nb * 16, LC, 1,
+        const f4 acc = mm_n<false, false>(sT + mb * 16 * LC + mb * 16, 1, LC, sX + mb * 16 * LC + nb * 16, LC, 1,
                             C - mb * 16, zero4());
         store_tile(sY + mb * 16 * LC + nb * 16, LC, acc);
     }
     __syncthreads();
     // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX
-    for (int t = wave; t < 16; t += 4) {
+    for (int t = wave; t < 16; t += NW) {
         const int mb = t >> 2, nb = t & 3;
         f4 dr = zero4();
         if (nb <= mb) {
             // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
-            const f4 ya = mm_n(sY + mb * 16 * LC, LC, 1, sT + nb * 16 * LC, 1, LC, (nb + 1) * 16, zero4());
-            const f4 rr = mm<DK>(sKh + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, zero4());
+            const f4 ya = mm_n<true, true>(sY + mb * 16 * LC, LC, 1, sT + nb * 16 * LC, 1, LC, (nb + 1) * 16, zero4());
+            const f4 rr = mm<DK, true, true>(sKh + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, zero4());
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = mb * 16 + 4 * j + e, s = nb * 16 + i;
@@ -944,13 +984,18 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     __syncthreads();
 
     // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh)
-    f4 dKh[4][CBW];
+    f4 dKh[4][CBW], dQh[4][CBW], dKb[4][CBW];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int u = 0; u < CBW; ++u) dKh[mb][u] = dQh[mb][u] = dKb[mb][u] = zero4();
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
         for (int u = 0; u < CBW; ++u) {
-            const int nb = wave + 4 * u;
-            const f4 dy = mm_n(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1,
+            const int nb = wave + NW * u;
+            if (nb >= NCB) continue;
+            const f4 dy = mm_n<false, false>(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1,
                                C - mb * 16, zero4());
             f4 x;
 #pragma unroll
@@ -961,26 +1006,26 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
                 x[e] = sBeta[r] * dy[e];
             }
             // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
-            dKh[mb][u] = mm_n(sX + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16, x);
+            dKh[mb][u] = mm_n<true, false>(sX + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16, x);
         }
     }
     __syncthreads();
-    load_block<C, C, 256>(sT, LC, rec_at(P, h, g, R::M), C);
-    load_block<C, DK, 256>(sW, LK, rec_at(P, h, g, R::QH), DK);
+    load_block<C, C, NTH>(sT, LC, rec_at(P, h, g, R::M), C);
+    load_block<C, DK, NTH>(sW, LK, rec_at(P, h, g, R::QH), DK);
     __syncthreads();
 
     // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
-    f4 dQh[4][CBW], dKb[4][CBW];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
         for (int u = 0; u < CBW; ++u) {
-            const int nb = wave + 4 * u;
-            dQh[mb][u] = mm_n(sT + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16,
+            const int nb = wave + NW * u;
+            if (nb >= NCB) continue;
+            dQh[mb][u] = mm_n<true, false>(sT + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16,
                               load_tile(rec_at(P, h, g, R::DQH) + mb * 16 * DK + nb * 16, DK));
-            f4 y = mm_n(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1, C - mb * 16,
+            f4 y = mm_n<false, false>(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1, C - mb * 16,
                         zero4());
-            dKb[mb][u] = mm_n(sX + mb * 16 * LC + mb * 16, 1, LC, sKh + mb * 16 * LK + nb * 16, LK, 1,
+            dKb[mb][u] = mm_n<false, false>(sX + mb * 16 * LC + mb * 16, 1, LC, sKh + mb * 16 * LK + nb * 16, LK, 1,
                               C - mb * 16, y);
         }
     }
@@ -994,14 +1039,14 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     const float* gDgam = rec_at(P, h, g, R::DGAM);
     float* sD = sX;                          // dKt, row stride LK
     static_assert(C * LK <= 2 * C * LC, "dKt staging spans the sX and sY regions");
-    constexpr int NS = 256 / DK, SEG = C / NS;   // reverse-cumsum split: NS row segments per channel
+    constexpr int NS = NTH / DK, SEG = C / NS;   // reverse-cumsum split: NS row segments per channel
     float gam_u[CBW];
-    Tok<GATE == KDA_GATE_SOFTPLUS_BF16, DK, DK, 256> tg;
+    Tok<GATE == KDA_GATE_SOFTPLUS_BF16, DK, DK, NTH> tg;
     float gs = 1.f;
     float gam_t = 0.f, dgam_t = 0.f;
     {
-        Tok<ABF16, DK, DK, 256> tq, tk;
-        Blk<C, DK, 256> bb, bd;
+        Tok<ABF16, DK, DK, NTH> tq, tk;
+        Blk<C, DK, NTH> bb, bd;
         tq.load(P.q, row0, len, h, H);
         tk.load(P.k, row0, len, h, H);
         bb.load(gB, DK);
@@ -1012,7 +1057,7 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
             tg.load(P.gate, row0, len, h, H);
         }
 #pragma unroll
-        for (int u = 0; u < CBW; ++u) gam_u[u] = gGam[(wave + 4 * u) * 16 + i];
+        for (int u = 0; u < CBW; ++u) gam_u[u] = gGam[((wave + NW * u) % NCB) * 16 + i];
         gam_t = gGam[tid % DK];
         dgam_t = gDgam[tid % DK];
         tq.put(sKh, LK);
@@ -1023,7 +1068,8 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < CBW; ++u) {
-        const int nb = wave + 4 * u, c = nb * 16 + i;
+        const int nb = wave + NW * u, c = nb * 16 + i;
+        if (nb >= NCB) continue;
         const float gam = gam_u[u];
         float col = 0.f;
 #pragma unroll
@@ -1096,9 +1142,12 @@ __global__ __launch_bounds__(256) void bwd_kside_kernel(const BwdParams P) {
             P.dgate[static_cast<size_t>(row0 + tid) * H + h] = s / sW[tid];
         }
     }
-    if (tid < len)
-        P.dbeta[(row0 + tid) * H + h] = rec_at(P, h, g, R::DBZ)[tid] +
-                                        ((sRow[tid] + sRow[C + tid]) + (sRow[2 * C + tid] + sRow[3 * C + tid]));
+    if (tid < len) {
+        float db = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) db += sRow[w * C + tid];
+        P.dbeta[(row0 + tid) * H + h] = rec_at(P, h, g, R::DBZ)[tid] + db;
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -1137,19 +1186,19 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         auto k1 = bwd_prep_kernel<DK, DV, ABF16, GATE>;
         constexpr int l1 = PrepB<DK, DV>::bytes;
         if ((e = set_lds(k1, l1)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(256), l1, stream, p);
+        hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kPrepThreads), l1, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         auto k2 = bwd_ckpt_kernel<DK, DV>;
         constexpr int l2 = CkptB<DK>::bytes;
         if ((e = set_lds(k2, l2)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(256), l2, stream, p);
+        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(kChainThreads), l2, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chain_blocks > 0) {
         auto k3 = bwd_rev_kernel<DK, DV, ABF16>;
         constexpr int l3 = RevB<DK>::bytes;
         if ((e = set_lds(k3, l3)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k3, dim3(chain_blocks), dim3(256), l3, stream, p);
+        hipLaunchKernelGGL(k3, dim3(chain_blocks), dim3(kChainThreads), l3, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chunk_blocks > 0) {
@@ -1161,7 +1210,7 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         auto k5 = bwd_kside_kernel<DK, DV, ABF16, GATE>;
         constexpr int l5 = KsideB<DK>::bytes;
         if ((e = set_lds(k5, l5)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k5, dim3(chunk_blocks), dim3(256), l5, stream, p);
+        hipLaunchKernelGGL(k5, dim3(chunk_blocks), dim3(kKsideThreads), l5, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
