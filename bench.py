@@ -85,9 +85,9 @@ def time_events(fn, reps, warm=3):
     return e0.elapsed_time(e1) / reps
 
 
+# the device code of the forward and decode kernels (host-side validation lives elsewhere)
 KERNEL_SOURCES = ["gated_delta_rule_12_amd/csrc/kda_chunk.hip", "gated_delta_rule_12_amd/csrc/kda_decode.hip",
-                  "gated_delta_rule_12_amd/csrc/kda_common.h", "gated_delta_rule_12_amd/csrc/kda_chunk.h",
-                  "gated_delta_rule_12_amd/csrc/kda_api.hip"]
+                  "gated_delta_rule_12_amd/csrc/kda_common.h", "gated_delta_rule_12_amd/csrc/kda_chunk.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles",
                             "hbm_traffic_chunk_fwd_B1_H32_T65536_d128_bf16+decode_N256_H32_d128_bf16.txt")
 
