@@ -350,7 +350,7 @@ __device__ __forceinline__ float* rec_at(const BwdParams& P, int h, int g, size_
 }
 
 // ---------------------------------------------------------------------------
-// bwd_prep_kernel: one (chunk, head), 256 threads.
+// bwd_prep_kernel: one (chunk, head), 512 threads.
 // ---------------------------------------------------------------------------
 constexpr int kPrepThreads = 512, kPrepWaves = kPrepThreads / 64;
 
@@ -886,8 +886,8 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_kside_kernel: one (chunk, head), 256 threads.  Wave w owns the key
-// column blocks w, w + 4, ... of every C x DK gradient.
+// bwd_kside_kernel: one (chunk, head), 512 threads.  Wave w owns the key
+// column blocks w, w + 8, ... of every C x DK gradient.
 // ---------------------------------------------------------------------------
 constexpr int kKsideThreads = 512, kKsideWaves = kKsideThreads / 64;
 
