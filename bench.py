@@ -46,6 +46,13 @@ FWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 4 * 128 + 4
 FWD_FLOPS_PER_TOKEN_HEAD = 6 * 128 * 128 + 64 * 128 + 64 * 256 + 64 * 128 + 64 * 128 + 64 * 64 // 3
 
 
+def fwd_flops_per_token_head(C=64, dk=128, dv=128):
+    """Useful flops per token-head of the chunk forward at chunk size C: the
+    three d x d contractions plus the C-dependent products (A, T.X, QK^T,
+    P.U') and the triangular solve."""
+    return 6 * dk * dv + C * dk + C * (dk + dv) + C * dk + C * dv + C * C // 3
+
+
 # Chunkwise backward, per token-head: reads q, k, v, dO (bf16), alpha, beta;
 # writes dq, dk, dv (bf16), dalpha, dbeta (fp32).
 BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 128 * 4 + 4 + 3 * 2 * 128 + 128 * 4 + 4
@@ -375,6 +382,31 @@ def main():
             del gd, st2
         var["note"] = ("forget gate given as the bf16 softplus pre-activation, or one fp32 alpha "
                        "per token and head; same shapes as the main lines")
+        # chunk-size ablation: C = 32 and 128 run the generic fp32 path (C = 64 is the main line)
+        for C in (32, 128):
+            nbc = kda.kda_chunk_fwd_workspace_bytes(wf.B, wf.T, wf.H, wf.Dk, wf.Dv, False, 0, C, torch.bfloat16)
+            wsc = torch.empty(nbc, dtype=torch.uint8, device=dev)
+
+            def fwd_c():
+                kda.kda_chunk_fwd(fi["q"], fi["k"], fi["v"], fi["alpha"], fi["beta"],
+                                  initial_state=fi["initial_state"], final_state=sT, o=o,
+                                  out_dtype=torch.bfloat16, workspace=wsc, chunk_size=C)
+            ms = time_events(fwd_c, 5, 2)
+            byts = FWD_BYTES_PER_TOKEN_HEAD * units + 2 * wf.B * wf.H * wf.Dk * wf.Dv * 4
+            ach = byts / (ms / 1e3) / 1e9
+            tf = fwd_flops_per_token_head(C, wf.Dk, wf.Dv) * units / (ms / 1e3) / 1e12
+            var[f"fwd_chunk{C}"] = {"value": round(units / (ms / 1e3), 1), "unit": "token-heads/s",
+                                    "fwd_ms": round(ms, 4), "workspace_GiB": round(nbc / 2 ** 30, 2),
+                                    "roofline": {"bound": "hbm", "achieved": round(ach, 1),
+                                                 "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                                 "frac": round(ach / HBM_PEAK_GBPS, 4),
+                                                 "algorithmic_bytes_per_launch": byts},
+                                    "mfma": {"achieved_useful": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                                             "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                                             "dtype": "f32"}}
+            del wsc
+        var["chunk_note"] = ("chunk sizes 32 and 128 take the generic path (every product on the fp32 "
+                             "matrix cores, fp32 record); chunk 64 is the main line")
         var["bwd"] = bench_bwd(kda, synth, torch, fi, wf, 5, 2)
         out["variants"] = var
     traffic = measured_traffic()

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk_bwd.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_chunk.hip", "kda_chunk_bwd.hip", "kda_chunk_generic.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -25,6 +25,9 @@ bool gate_aligned(const void* p, kda_gate g) {
 
 bool supported_head(int d) { return d == 64 || d == 128; }
 
+// chunk sizes of the forward: 64 (the main kernels) and 32 / 128 (generic fp32 path)
+bool supported_chunk(int c) { return c == 32 || c == 64 || c == 128; }
+
 bool valid_dtype(kda_dtype d) { return d == KDA_DTYPE_F32 || d == KDA_DTYPE_BF16; }
 
 // Output may be fp32 for any activation type, bf16 only for bf16 activations.
@@ -81,7 +84,8 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
     if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
     if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
     if (cu_seqlens != nullptr && (B != 1 || num_seqs < 0)) return KDA_ERROR_INVALID_VALUE;
-    if (!supported_head(Dk) || !supported_head(Dv) || chunk_size != 64) return KDA_ERROR_NOT_SUPPORTED;
+    if (!supported_head(Dk) || !supported_head(Dv) || !supported_chunk(chunk_size))
+        return KDA_ERROR_NOT_SUPPORTED;
 
     kda::ChunkPlan plan;
     const kda_status ps = kda::make_chunk_plan(B, T, H, Dk, Dv, cu_seqlens != nullptr, num_seqs,

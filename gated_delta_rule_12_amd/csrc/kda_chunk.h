@@ -29,6 +29,7 @@ constexpr int kChunk = 64;      // tokens per chunk
 //     gam      f32[Dk]             whole-chunk decay gamma
 struct ChunkPlan {
     int B = 0, H = 0, Dk = 0, Dv = 0, N = 0;
+    int C = kChunk;               // tokens per chunk: 64 (kernels above) or 32 / 128 (generic path)
     int64_t T = 0;
     bool varlen = false;
     bool f16 = false;             // bf16 activations -> fp16 matrix-core operands
@@ -56,6 +57,11 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
                            int chunk_size, bool act_bf16, ChunkPlan* plan);
 
 hipError_t launch_chunk_fwd(const ChunkPlan& plan, const ChunkArgs& args, hipStream_t stream);
+
+// Chunk sizes other than 64 (kda_chunk_generic.hip): an fp32 path with its
+// own per-(head, chunk) record of generic_record_bytes bytes.
+size_t generic_record_bytes(int Dk, int Dv, int chunk_size);
+hipError_t launch_chunk_fwd_generic(const ChunkPlan& plan, const ChunkArgs& args, hipStream_t stream);
 
 // Enqueue the chunk-table kernel: fills ctrl, first, order and table of the
 // plan's layout inside `workspace`.

@@ -214,7 +214,7 @@ __device__ __forceinline__ int seq_len(const int32_t* cu, int n, int64_t T) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu, int N,
-                                                            int64_t T, int64_t gmax,
+                                                            int64_t T, int64_t gmax, int csize,
                                                             int32_t* __restrict__ ctrl,
                                                             int32_t* __restrict__ first,
                                                             int32_t* __restrict__ order,
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         int cnt = 0;
         if (n < N) {
             const int len = seq_len(cu, n, T);
-            cnt = len > 0 ? (len + C - 1) / C : 0;
+            cnt = len > 0 ? (len + csize - 1) / csize : 0;
             if (N <= kRankSortMax) s_len[n] = len;
         }
         s_scan[tid] = cnt;
@@ -268,8 +268,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         const int i = g - first[n];
         const int len = seq_len(cu, n, T);
         const int start = cu ? cu[n] : static_cast<int>(static_cast<int64_t>(n) * T);
-        const int l = len - i * C;
-        table[g] = make_int4(n, start + i * C, l < C ? l : C, 0);
+        const int l = len - i * csize;
+        table[g] = make_int4(n, start + i * csize, l < csize ? l : csize, 0);
     }
     // longest sequences first (ties by index), so long chains start early
     for (int n = tid; n < N; n += kPlanThreads) {
@@ -1148,7 +1148,8 @@ hipError_t launch_dims(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t stre
 kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen, int num_seqs,
                            int chunk_size, bool act_bf16, ChunkPlan* plan) {
     if (B < 0 || T < 0 || H <= 0 || num_seqs < 0) return KDA_ERROR_INVALID_VALUE;
-    if ((Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128) || chunk_size != C)
+    if ((Dk != 64 && Dk != 128) || (Dv != 64 && Dv != 128) ||
+        (chunk_size != 32 && chunk_size != 64 && chunk_size != 128))
         return KDA_ERROR_NOT_SUPPORTED;
     if (varlen && B != 1) return KDA_ERROR_INVALID_VALUE;
     ChunkPlan p;
@@ -1156,7 +1157,8 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.N = varlen ? num_seqs : B;
     const int64_t tokens = static_cast<int64_t>(B) * T;
     if (tokens >= (static_cast<int64_t>(1) << 31)) return KDA_ERROR_NOT_SUPPORTED;
-    const int64_t per_seq_chunks = (T + C - 1) / C;
+    p.C = chunk_size;
+    const int64_t per_seq_chunks = (T + chunk_size - 1) / chunk_size;
     p.gmax = varlen ? per_seq_chunks + p.N : static_cast<int64_t>(B) * per_seq_chunks;
     if (p.gmax * H >= (static_cast<int64_t>(1) << 31)) return KDA_ERROR_NOT_SUPPORTED;
     const int64_t pairs = static_cast<int64_t>(p.N) * H;
@@ -1169,8 +1171,11 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.off_order = off; off = align256(off + 4 * static_cast<size_t>(p.N));
     p.off_table = off; off = align256(off + 16 * static_cast<size_t>(p.gmax));
     // per (head, chunk) record: qh, w, ktt, p, ut (operand type), gam (fp32)
-    p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(C) * C * p.eb +
-                           static_cast<size_t>(C) * Dv * p.eb + static_cast<size_t>(Dk) * 4);
+    if (chunk_size == C)
+        p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(C) * C * p.eb +
+                               static_cast<size_t>(C) * Dv * p.eb + static_cast<size_t>(Dk) * 4);
+    else
+        p.rec_bytes = align256(generic_record_bytes(Dk, Dv, chunk_size));
     p.off_rec = off;   off = align256(off + gh * p.rec_bytes);
     p.workspace_bytes = off;
     *plan = p;
@@ -1181,7 +1186,7 @@ hipError_t launch_chunk_plan(const ChunkPlan& pl, const int32_t* cu_seqlens, voi
                              hipStream_t stream) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, cu_seqlens, pl.N,
-                       pl.varlen ? static_cast<int64_t>(0) : pl.T, pl.gmax,
+                       pl.varlen ? static_cast<int64_t>(0) : pl.T, pl.gmax, pl.C,
                        reinterpret_cast<int32_t*>(ws + pl.off_ctrl),
                        reinterpret_cast<int32_t*>(ws + pl.off_first),
                        reinterpret_cast<int32_t*>(ws + pl.off_order),
@@ -1190,6 +1195,7 @@ hipError_t launch_chunk_plan(const ChunkPlan& pl, const int32_t* cu_seqlens, voi
 }
 
 hipError_t launch_chunk_fwd(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t stream) {
+    if (pl.C != C) return launch_chunk_fwd_generic(pl, a, stream);
     if (pl.Dk == 128 && pl.Dv == 128) return launch_dims<128, 128>(pl, a, stream);
     if (pl.Dk == 64 && pl.Dv == 64) return launch_dims<64, 64>(pl, a, stream);
     if (pl.Dk == 128 && pl.Dv == 64) return launch_dims<128, 64>(pl, a, stream);

@@ -1,0 +1,258 @@
+// fp32 matrix-core building blocks shared by the chunkwise backward and the
+// chunk-size-generic forward (gfx950): a 16x16 fp32 MFMA tile over LDS
+// operands with arbitrary strides, register-staged global -> LDS copies,
+// and the gate forms as log2(alpha).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_chunk.h"
+#include "kda_common.h"
+
+namespace kda {
+namespace mm32 {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int L16 = 16;            // LDS row stride of 16-column tiles
+
+template <int D> struct Ld { static constexpr int value = D + 4; };   // LDS row stride, D columns
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---------------------------------------------------------------------------
+// 16x16 fp32 matrix-core tile, 4-deep steps (v_mfma_f32_16x16x4f32):
+//   A lane l holds A[l % 16][k], B lane l holds B[k][l % 16] for the step's
+//   k, D lane l holds D[4 (l / 16) + e][l % 16], e = 0..3.
+// mm: acc += sum_{k < K} A(m, k) B(k, n) with A(m, k) = pa[m am + k ak] and
+// B(k, n) = pb[k bk + n bn]; the strides express any transpose.
+// Within each 16-deep group of the reduction, lane group j = l / 16 takes
+// the indices 4j..4j+3 in the group's four steps (any assignment gives the
+// same product when both operands follow it), so an operand that is
+// contiguous along the reduction (AV: ak == 1, BV: bk == 1) is read with one
+// 16-byte LDS load per group instead of four.  Each group's operands are
+// loaded one group ahead of its products.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <bool V>
+__device__ __forceinline__ f4 grp4(const float* p, int stride) {
+    if constexpr (V) return *reinterpret_cast<const f4*>(p);
+    else return f4{p[0], p[stride], p[2 * stride], p[3 * stride]};
+}
+
+template <int K, bool AV, bool BV>
+__device__ __forceinline__ f4 mm(const float* pa, int am, int ak, const float* pb, int bk, int bn, f4 acc) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
+    constexpr int G = K / 16;
+    f4 a[3], b[3];
+    a[0] = grp4<AV>(pa, ak);
+    b[0] = grp4<BV>(pb, bk);
+    if constexpr (G > 1) {
+        a[1] = grp4<AV>(pa + 16 * ak, ak);
+        b[1] = grp4<BV>(pb + 16 * bk, bk);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g + 2 < G) {
+            a[(g + 2) % 3] = grp4<AV>(pa + 16 * (g + 2) * ak, ak);
+            b[(g + 2) % 3] = grp4<BV>(pb + 16 * (g + 2) * bk, bk);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a[g % 3][s2], b[g % 3][s2], acc);
+    }
+    return acc;
+}
+
+// Runtime depth K, a multiple of 16.
+template <bool AV, bool BV>
+__device__ __forceinline__ f4 mm_n(const float* pa, int am, int ak, const float* pb, int bk, int bn,
+                                   int K, f4 acc) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
+    if (K <= 0) return acc;
+    f4 a0 = grp4<AV>(pa, ak), b0 = grp4<BV>(pb, bk), a1, b1;
+    for (int k = 0; k < K; k += 32) {
+        const bool more1 = k + 16 < K;
+        if (more1) {
+            a1 = grp4<AV>(pa + (k + 16) * ak, ak);
+            b1 = grp4<BV>(pb + (k + 16) * bk, bk);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a0[s2], b0[s2], acc);
+        if (!more1) break;
+        if (k + 32 < K) {
+            a0 = grp4<AV>(pa + (k + 32) * ak, ak);
+            b0 = grp4<BV>(pb + (k + 32) * bk, bk);
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a1[s2], b1[s2], acc);
+    }
+    return acc;
+}
+
+// D-layout tile <-> row-major memory (row stride ld, origin at the tile)
+__device__ __forceinline__ void store_tile(float* p, int ld, f4 v) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[(4 * j + e) * ld + i] = v[e];
+}
+__device__ __forceinline__ f4 load_tile(const float* p, int ld) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    f4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p[(4 * j + e) * ld + i];
+    return v;
+}
+
+// sum of x over the 16 lanes that share l / 16 (one row of a D-layout tile)
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// four consecutive activations as fp32 (16-byte / 8-byte aligned)
+template <bool BF16> __device__ __forceinline__ f4 act4(const void* p, size_t i);
+template <> __device__ __forceinline__ f4 act4<false>(const void* p, size_t i) {
+    return *reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
+}
+template <> __device__ __forceinline__ f4 act4<true>(const void* p, size_t i) {
+    const u16x4 r = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(p) + i);
+    return f4{bf16_to_f32(r[0]), bf16_to_f32(r[1]), bf16_to_f32(r[2]), bf16_to_f32(r[3])};
+}
+template <bool BF16> __device__ __forceinline__ float act1(const void* p, size_t i) {
+    if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+    else return static_cast<const float*>(p)[i];
+}
+
+// Register-staged copies: load() issues every global load of a block before
+// any is consumed, put() writes the block to LDS as fp32.  A block staged
+// one step ahead keeps its loads in flight while the current step computes.
+//
+// Blk: ROWS x NC fp32 values, source row stride sld (floats).
+template <int ROWS, int NC, int NTH>
+struct Blk {
+    static constexpr int V4 = NC / 4, N = ROWS * V4, IT = (N + NTH - 1) / NTH;
+    f4 t[IT];
+    __device__ __forceinline__ void load(const float* src, int sld) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N)
+                t[it] = *reinterpret_cast<const f4*>(src + static_cast<size_t>(idx / V4) * sld + (idx % V4) * 4);
+        }
+    }
+    __device__ __forceinline__ void put(float* dst, int ld) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) *reinterpret_cast<f4*>(dst + (idx / V4) * ld + (idx % V4) * 4) = t[it];
+        }
+    }
+};
+
+template <bool B> struct RawT { using type = f4; };
+template <> struct RawT<true> { using type = u16x4; };
+
+// Tok: ROWS token rows x NC columns (from column c0) of a [rows, H, COLS]
+// activation tensor, head h, first row row0; rows >= len (>= 1) read as
+// zero.  The row index is clamped, so every load is issued unconditionally.
+template <bool BF16, int COLS, int NC, int NTH, int ROWS = kChunk>
+struct Tok {
+    static constexpr int V4 = NC / 4, N = ROWS * V4, IT = (N + NTH - 1) / NTH;
+    using Raw = typename RawT<BF16>::type;
+    Raw t[IT];
+    int len_ = 0;
+    // the rows past len are zeroed in put(), so no load result is needed here
+    __device__ __forceinline__ void load(const void* src, int64_t row0, int len, int h, int H, int c0 = 0) {
+        len_ = len;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) {
+                const int r = idx / V4, c = (idx % V4) * 4;
+                const int rr = r < len ? r : len - 1;
+                const size_t off = (static_cast<size_t>(row0 + rr) * H + h) * COLS + c0 + c;
+                if constexpr (BF16) t[it] = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(src) + off);
+                else t[it] = *reinterpret_cast<const f4*>(static_cast<const float*>(src) + off);
+            }
+        }
+    }
+    __device__ __forceinline__ void put(float* dst, int ld) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) {
+                f4 x;
+                if constexpr (BF16)
+                    x = f4{bf16_to_f32(t[it][0]), bf16_to_f32(t[it][1]), bf16_to_f32(t[it][2]), bf16_to_f32(t[it][3])};
+                else x = t[it];
+                if (idx / V4 >= len_) x = zero4();
+                *reinterpret_cast<f4*>(dst + (idx / V4) * ld + (idx % V4) * 4) = x;
+            }
+        }
+    }
+};
+
+template <int ROWS, int NC, int NTH>
+__device__ __forceinline__ void load_block(float* dst, int ld, const float* src, int sld) {
+    Blk<ROWS, NC, NTH> b;
+    b.load(src, sld);
+    b.put(dst, ld);
+}
+
+template <bool BF16, int COLS, int NC, int NTH, int ROWS = kChunk>
+__device__ __forceinline__ void load_tokens(float* dst, int ld, const void* src, int64_t row0, int len, int h,
+                                            int H, int c0 = 0) {
+    Tok<BF16, COLS, NC, NTH, ROWS> t;
+    t.load(src, row0, len, h, H, c0);
+    t.put(dst, ld);
+}
+
+template <int NTH>
+__device__ __forceinline__ void store_block(float* dst, int dld, const float* src, int ld, int rows, int ncols) {
+    const int v4 = ncols / 4;
+    for (int idx = threadIdx.x; idx < rows * v4; idx += NTH) {
+        const int r = idx / v4, c = (idx % v4) * 4;
+        *reinterpret_cast<f4*>(dst + static_cast<size_t>(r) * dld + c) = *reinterpret_cast<const f4*>(src + r * ld + c);
+    }
+}
+
+// log2 alpha of (row, head, channel c) from the gate as given
+template <int GATE, int DK>
+__device__ __forceinline__ float gate_log2(const void* gate, int64_t row, int h, int H, int c) {
+    if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
+        const uint16_t x = static_cast<const uint16_t*>(gate)[(static_cast<size_t>(row) * H + h) * DK + c];
+        return log2_alpha_from_softplus_arg(bf16_to_f32(x));
+    } else if constexpr (GATE == KDA_GATE_SCALAR) {
+        return __builtin_amdgcn_logf(static_cast<const float*>(gate)[static_cast<size_t>(row) * H + h]);
+    } else {
+        return __builtin_amdgcn_logf(static_cast<const float*>(gate)[(static_cast<size_t>(row) * H + h) * DK + c]);
+    }
+}
+
+// Sequential passes: one workgroup per (sequence-head pair, 16 value
+// columns).  Workgroups are dealt to the 8 XCDs round-robin; the NT column
+// tiles of one pair read the same per-chunk record, so they are kept on the
+// same XCD (and its L2): block b = (group * NT + tile) * 8 + xcd serves
+// pair group * 8 + xcd.  The grid is padded to a multiple of 8 pairs.
+template <int NT>
+__device__ __forceinline__ void chain_coords(int& tile, int& pair) {
+    const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+    tile = slot % NT;
+    pair = (slot / NT) * 8 + xcd;
+}
+
+}  // namespace mm32
+}  // namespace kda

@@ -37,7 +37,10 @@
  *    within any 8 consecutive tokens of a 64-token chunk the decay
  *    -sum(log alpha) of every channel stays below 10; cu_seqlens is
  *    non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = T.
- *  - Supported: d_k in {64, 128}, d_v in {64, 128}, chunk_size = 64.
+ *  - Supported: d_k in {64, 128}, d_v in {64, 128}; chunk_size 64 for
+ *    every call, and also 32 or 128 for the chunkwise forward (a generic
+ *    path with every product in fp32; the result is the same recurrence,
+ *    the chunk size only changes how the work is cut).
  *    Activations (q, k, v) are either all fp32 or all bf16; alpha, beta and
  *    every state are fp32.  The output o is fp32, or bf16 when the
  *    activations are bf16 (rounded once, to nearest-even, from the fp32

@@ -59,7 +59,15 @@ def test_workspace_size_plan():
     assert nv > f(1, 1000, 4, 64, 64, False, 0, 64, kda.KDA_DTYPE_BF16)
     # unsupported combinations report 0
     assert f(1, 256, 1, 96, 64, False, 0, 64, kda.KDA_DTYPE_BF16) == 0
-    assert f(1, 256, 1, 64, 64, False, 0, 32, kda.KDA_DTYPE_BF16) == 0
+    assert f(1, 256, 1, 64, 64, False, 0, 96, kda.KDA_DTYPE_BF16) == 0
+    # chunk sizes 32 and 128 take the generic path, with its own (fp32) record
+    assert f(1, 256, 1, 64, 64, False, 0, 32, kda.KDA_DTYPE_BF16) > 0
+    assert f(1, 256, 1, 64, 64, False, 0, 128, kda.KDA_DTYPE_BF16) > 0
+    # the backward runs at C = 64 only
+    fb = kda.kda_chunk_bwd_workspace_bytes
+    assert fb(1, 256, 1, 64, 64, False, 0, 64, kda.KDA_DTYPE_BF16) > 0
+    assert fb(1, 256, 1, 64, 64, False, 0, 32, kda.KDA_DTYPE_BF16) == 0
+    assert fb(1, 256, 1, 64, 64, False, 0, 128, kda.KDA_DTYPE_BF16) == 0
     assert f(2, 256, 1, 64, 64, True, 3, 64, kda.KDA_DTYPE_BF16) == 0
     assert f(1, 1 << 31, 1, 64, 64, False, 0, 64, kda.KDA_DTYPE_BF16) == 0
 
@@ -84,7 +92,8 @@ def test_chunk_fwd_argument_errors():
     assert _chunk(H=0) == kda.KDA_ERROR_INVALID_VALUE
     assert _chunk(Dk=96) == kda.KDA_ERROR_NOT_SUPPORTED
     assert _chunk(Dv=32) == kda.KDA_ERROR_NOT_SUPPORTED
-    assert _chunk(C=128) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(C=96) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk(C=16) == kda.KDA_ERROR_NOT_SUPPORTED
     assert _chunk(act=7) == kda.KDA_ERROR_INVALID_VALUE
     assert _chunk(act=kda.KDA_DTYPE_F32, out=kda.KDA_DTYPE_BF16) == kda.KDA_ERROR_NOT_SUPPORTED
     assert _chunk(cu=FAKE, B=2, N=3) == kda.KDA_ERROR_INVALID_VALUE

@@ -1,0 +1,109 @@
+"""GPU parity of the chunkwise forward at chunk sizes 32 and 128 (the
+generic fp32 path) against the fp64 oracle.  The result is C-invariant in
+exact arithmetic ("Linear Attention KDA Gating in a 3:1 Hybrid
+Architecture", section 3.1 and its chunk-size table), so the reference is
+the same token recurrence at every C; tolerances as for C = 64."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_12_amd as kda
+import oracle
+import synth
+from tests.helpers import check_close, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+ODT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _case(C, B, T, H, Dk, Dv, act, out, seed, gate="alpha", lengths=None, s0_std=0.02, final=True):
+    inp = synth.chunk_inputs(B, T, H, Dk, Dv, act, mu=-2.0, s0_std=s0_std, seed=seed, device=DEV,
+                             lengths=lengths)
+    Tt = inp["q"].shape[1]
+    g = inp["alpha"] if gate == "alpha" else synth.draw_gate(gate, (B, Tt), H, Dk, -2.0, seed, DEV)
+    o, sT = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], g, inp["beta"],
+                              initial_state=inp["initial_state"], final_state=final,
+                              cu_seqlens=inp["cu_seqlens"], out_dtype=ODT[out], chunk_size=C, gate=gate)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"]
+    o_ref, s_ref = oracle.kda_fwd(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]),
+                                  oracle.alpha_from_gate(to_np(g), gate, Dk), to_np(inp["beta"]),
+                                  initial_state=synth.to_f64(inp["initial_state"]),
+                                  cu_seqlens=None if cu is None else cu.cpu().numpy().astype(np.int64))
+    kind = "f32" if act == "f32" else "bf16"
+    r1 = check_close(o, o_ref, kind, stored_bf16=(out == "bf16"), what="o")
+    r2 = check_close(sT, s_ref, kind, what="final state") if final else 0.0
+    print(f"  error/allowed: o {r1:.3f}  S_T {r2:.3f}", flush=True)
+
+
+@pytest.mark.parametrize("C", [32, 128])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+@pytest.mark.parametrize("act,out", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("T", [128, 300])
+def test_chunk_size_small(C, Dk, Dv, act, out, T):
+    print(f"[C={C} Dk={Dk} Dv={Dv} act={act} out={out} T={T}]", flush=True)
+    _case(C, 2, T, 2, Dk, Dv, act, out, seed=C + T)
+
+
+@pytest.mark.parametrize("C", [32, 128])
+@pytest.mark.parametrize("gate", ["softplus", "scalar"])
+def test_chunk_size_gate_forms(C, gate):
+    print(f"[C={C} gate={gate}]", flush=True)
+    _case(C, 2, 200, 3, 128, 128, "bf16", "bf16", seed=41, gate=gate)
+
+
+@pytest.mark.parametrize("C", [32, 128])
+def test_chunk_size_varlen(C):
+    """Packed sequences, including an empty and a one-token one; chunks restart
+    at every sequence start."""
+    print(f"[C={C} varlen]", flush=True)
+    _case(C, 1, 0, 3, 128, 128, "bf16", "bf16", seed=9, lengths=[0, 70, 1, 256, 133, 300])
+
+
+@pytest.mark.parametrize("C", [32, 128])
+def test_chunk_size_no_state(C):
+    _case(C, 2, 150, 2, 64, 64, "f32", "f32", seed=3, s0_std=None, final=False)
+
+
+@pytest.mark.parametrize("C", [32, 128])
+def test_chunk_size_medium(C):
+    """B=2, H=8, T=4096, d=128, bf16 (the shape of the element-wise workload)."""
+    print(f"[C={C} B2 H8 T4096 d128 bf16]", flush=True)
+    _case(C, 2, 4096, 8, 128, 128, "bf16", "f32", seed=1, s0_std=None)
+
+
+def test_chunk_sizes_agree():
+    """C = 32, 64 and 128 on the same inputs: the three outputs differ only by
+    rounding (fp32 activations)."""
+    inp = synth.chunk_inputs(1, 1000, 4, 128, 128, "f32", s0_std=0.02, seed=12, device=DEV)
+    outs = []
+    for C in (32, 64, 128):
+        o, sT = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                  initial_state=inp["initial_state"], final_state=True, chunk_size=C)
+        outs.append((to_np(o), to_np(sT)))
+    torch.cuda.synchronize()
+    for o, sT in outs[1:]:
+        assert np.max(np.abs(o - outs[0][0])) <= 1e-4 * np.max(np.abs(outs[0][0]))
+        assert np.max(np.abs(sT - outs[0][1])) <= 1e-4 * np.max(np.abs(outs[0][1]))
+
+
+def test_full_workload2_chunk128_sampled():
+    """B=1, H=32, T=65536, d=128, slow decay, random S0 at C = 128; 2 full heads
+    recomputed by the oracle."""
+    w = synth.WORKLOADS[2]
+    print(f"[C=128 {w.name}]", flush=True)
+    inp = synth.workload_inputs(2, device=DEV)
+    o, sT = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                              initial_state=inp["initial_state"], final_state=True,
+                              out_dtype=torch.bfloat16, chunk_size=128)
+    torch.cuda.synchronize()
+    heads = [0, 21]
+    sl = (slice(None), slice(None), heads)
+    o_ref, s_ref = oracle.kda_fwd(to_np(inp["q"][sl]), to_np(inp["k"][sl]), to_np(inp["v"][sl]),
+                                  to_np(inp["alpha"][sl]), to_np(inp["beta"][sl]),
+                                  initial_state=to_np(inp["initial_state"][:, heads]))
+    for hi, h in enumerate(heads):
+        r1 = check_close(o[:, :, h], o_ref[:, :, hi], "bf16", stored_bf16=True, what=f"o head {h}")
+        r2 = check_close(sT[:, h], s_ref[:, hi], "bf16", what=f"S_T head {h}")
+        print(f"  head {h}: error/allowed o {r1:.3f}  S_T {r2:.3f}", flush=True)
