@@ -80,7 +80,15 @@ template <int DK, int DV> struct BRec {
     static constexpr size_t N = M + CC;          // dU' V^T                   [C][C]
     static constexpr size_t DGAM = N + CC;       // rowsum(dS_next . S)       [DK]
     static constexpr size_t DBZ = DGAM + size_t(DK) * 4;  // rowsum(dZ . V)  [C]
-    static constexpr size_t END = DBZ + size_t(C) * 4;
+    // fp16 A fragments of the state passes' products (16-bit activations only)
+    static constexpr size_t HK = size_t(C) * DK * 2;
+    static constexpr size_t FKT = DBZ + size_t(C) * 4;    // Kt                [C][DK]
+    static constexpr size_t FKTT = FKT + HK;              // Kt^T              [DK][C]
+    static constexpr size_t FQHT = FKTT + HK;             // Qh^T              [DK][C]
+    static constexpr size_t FW = FQHT + HK;               // W                 [C][DK]
+    static constexpr size_t FWT = FW + HK;                // W^T               [DK][C]
+    static constexpr size_t FPT = FWT + HK;               // P^T               [C][C]
+    static constexpr size_t END = FPT + size_t(C) * C * 2;
 };
 
 struct BwdParams {
@@ -209,6 +217,13 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
         gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
     }
     store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
+    if constexpr (ABF16) {
+        // fp16 fragments for the 16-bit state passes: Kt, Kt^T and Qh^T
+        auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+        write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sGam[k] * sKb[m * LK + k]; });
+        write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sGam[m] * sKb[k * LK + m]; });
+        write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
+    }
 
     // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record
     float* gP = rec_at(P, h, g, R::P);
@@ -223,10 +238,19 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
             if (which) acc[e] = s2 <= r ? acc[e] : 0.f;
             else acc[e] = s2 < r ? sBeta[r] * acc[e] : 0.f;
         }
-        if (which) store_tile(gP + mb * 16 * C + nb * 16, C, acc);
-        else store_tile(sA + mb * 16 * LC + nb * 16, LC, acc);
+        if (which) {
+            store_tile(gP + mb * 16 * C + nb * 16, C, acc);
+            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, acc);   // P, for P^T fragments
+        } else {
+            store_tile(sA + mb * 16 * LC + nb * 16, LC, acc);
+        }
     }
     __syncthreads();
+    if constexpr (ABF16) {
+        auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+        write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
+        __syncthreads();
+    }
 
     // T = (I + A)^-1 (A strictly lower) by 16 x 16 blocks: each wave inverts
     // one diagonal block by substitution (16 lanes, one column each), then
@@ -297,8 +321,18 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
         const int mb = tt / nn, nb = tt % nn;
         const f4 acc = mm_n<true, false>(sT + mb * 16 * LC, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1,
                             (mb + 1) * 16, zero4());
-        if (isw) store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
-        else store_tile(gU + mb * 16 * DV + nb * 16, DV, acc);
+        if (isw) {
+            store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
+            if constexpr (ABF16) store_tile(sKb + mb * 16 * LK + nb * 16, LK, acc);   // W, for its fragments
+        } else {
+            store_tile(gU + mb * 16 * DV + nb * 16, DV, acc);
+        }
+    }
+    if constexpr (ABF16) {
+        __syncthreads();
+        auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+        write_afrags<C, DK, NTH>(hrec(R::FW), [&](int m, int k) { return sKb[m * LK + k]; });
+        write_afrags<DK, C, NTH>(hrec(R::FWT), [&](int m, int k) { return sKb[k * LK + m]; });
     }
 }
 
@@ -498,6 +532,210 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev_kernel(const BwdParams 
             if (rb >= NRB) continue;
             store_tile(P.dinitial_state + sbase + rb * 16 * DV + c0, DV, dS[u]);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit activations: the same two state passes on the fp16 matrix cores
+// (16x16x32), as the forward's state pass does.  Each wave reads its A
+// fragments (Kt, P^T, Qh^T, W^T; or W, Kt^T) straight from the record,
+// fragment-major, one chunk ahead; the B operands (dO, dS, dU'; or S, U')
+// pass through LDS as column-major fp16 tiles.  The states and their
+// gradients stay fp32 in registers, and every record value is written in
+// fp32.  Waves 0..3 compute the C x 16 product (row block = wave), every
+// wave one 16-row block of the d_k x 16 state tile.
+// ---------------------------------------------------------------------------
+template <int DK> struct Chain16B {
+    static constexpr int KPD = DK + 8, KPC = C + 8;      // column-major tile strides (halves)
+    static constexpr int bytes = (2 * 16 * KPC + 16 * KPD) * 2 + DK * 4;
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int NW = kChainWaves, NT = DV / 16, NRB = DK / 16;
+    constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
+    extern __shared__ float lds[];
+    _Float16* sdO = reinterpret_cast<_Float16*>(lds);    // dO tile, column-major  [16][KPC]
+    _Float16* sdU = sdO + 16 * KPC;                      // dU'                   [16][KPC]
+    _Float16* sdS = sdU + 16 * KPC;                      // dS                    [16][KPD]
+    float* sGam = reinterpret_cast<float*>(sdS + 16 * KPD);   // [DK]
+
+    int tile, pair;
+    chain_coords<NT>(tile, pair);
+    if (pair >= P.N * P.H) return;
+    const int H = P.H;
+    const int n = P.order[pair / H], h = pair % H;
+    const int g0 = P.first[n], g1 = P.first[n + 1];
+    const int wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
+    const int c0 = tile * 16;
+    const bool du = wave < 4, hasrb = wave < NRB;
+    const int mb = wave & 3, rb = wave;
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * DK * DV;
+
+    f4 dS = (P.dfinal_state && hasrb) ? load_tile(P.dfinal_state + sbase + rb * 16 * DV + c0, DV) : zero4();
+    auto hrec = [&](int g, size_t off) {
+        return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
+    };
+    // the next (earlier) chunk's operands
+    h8 nKt[NKD], nPt[NKC], nQt[NKC], nWt[NKC];
+    u16x4 ndO = {0, 0, 0, 0};
+    int ndO_len = 0;
+    float nGam = 0.f;
+    const int dr = threadIdx.x >> 2, dc = 4 * (threadIdx.x & 3);      // dO element rows / columns of this thread
+    auto fetch = [&](int g) {
+        const int4 ent = P.table[g];
+        if (du) {
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb) nKt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKT) + afrag_off(mb, kb, NKD, lane));
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) nPt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FPT) + afrag_off(mb, kb, NKC, lane));
+        }
+        if (hasrb) {
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) {
+                nQt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FQHT) + afrag_off(rb, kb, NKC, lane));
+                nWt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FWT) + afrag_off(rb, kb, NKC, lane));
+            }
+        }
+        if (dr < C) {
+            const int rr = dr < ent.z ? dr : ent.z - 1;
+            ndO = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(P.dout) +
+                                                  (static_cast<size_t>(ent.y + rr) * H + h) * DV + c0 + dc);
+        }
+        ndO_len = ent.z;
+        if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
+    };
+    if (g1 > g0) fetch(g1 - 1);
+    for (int g = g1 - 1; g >= g0; --g) {
+        h8 Kt[NKD], Pt[NKC], Qt[NKC], Wt[NKC];
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) Kt[kb] = nKt[kb];
+#pragma unroll
+        for (int kb = 0; kb < NKC; ++kb) {
+            Pt[kb] = nPt[kb];
+            Qt[kb] = nQt[kb];
+            Wt[kb] = nWt[kb];
+        }
+        if (dr < C) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sdO[(dc + e) * KPC + dr] = static_cast<_Float16>(dr < ndO_len ? bf16_to_f32(ndO[e]) : 0.f);
+        }
+        if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
+        if (hasrb) {
+            put_btile(sdS, KPD, rb * 16, dS);
+            store_tile(rec_at(P, h, g, R::DSO) + rb * 16 * DV + c0, DV, dS);
+        }
+        __syncthreads();
+        if (g > g0) fetch(g - 1);
+        // dU' = Kt dS + P^T dO   (P^T[m][k] = P[k][m], zero for k < m)
+        if (du) {
+            f4 acc = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb) acc = mfma16(Kt[kb], bfrag(sdS, KPD, kb), acc);
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb)
+                if (32 * kb + 31 >= 16 * mb) acc = mfma16(Pt[kb], bfrag(sdO, KPC, kb), acc);
+            put_btile(sdU, KPC, mb * 16, acc);
+            store_tile(rec_at(P, h, g, R::DUC) + mb * 16 * DV + c0, DV, acc);
+        }
+        __syncthreads();
+        // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'
+        if (hasrb) {
+            f4 x = dS, y = zero4();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] *= sGam[rb * 16 + 4 * j + e];
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) {
+                x = mfma16(Qt[kb], bfrag(sdO, KPC, kb), x);
+                y = mfma16(Wt[kb], bfrag(sdU, KPC, kb), y);
+            }
+            dS = x - y;
+        }
+        __syncthreads();
+    }
+    (void)i;
+    if (P.dinitial_state && hasrb) store_tile(P.dinitial_state + sbase + rb * 16 * DV + c0, DV, dS);
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    constexpr int NT = DV / 16, NRB = DK / 16;
+    constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
+    extern __shared__ float lds[];
+    _Float16* sU = reinterpret_cast<_Float16*>(lds);     // U', column-major        [16][KPC]
+    _Float16* sS = sU + 2 * 16 * KPC;                    // S                       [16][KPD]
+    float* sGam = reinterpret_cast<float*>(sS + 16 * KPD);   // [DK]
+
+    int tile, pair;
+    chain_coords<NT>(tile, pair);
+    if (pair >= P.N * P.H) return;
+    const int n = P.order[pair / P.H], h = pair % P.H;
+    const int g0 = P.first[n], g1 = P.first[n + 1];
+    const int wave = wave_id(), lane = lane_id(), j = lane >> 4;
+    const int c0 = tile * 16;
+    const bool du = wave < 4, hasrb = wave < NRB;
+    const int mb = wave & 3, rb = wave;
+
+    f4 S = (P.initial_state && hasrb)
+               ? load_tile(P.initial_state + (static_cast<size_t>(n) * P.H + h) * DK * DV + rb * 16 * DV + c0, DV)
+               : zero4();
+    auto hrec = [&](int g, size_t off) {
+        return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
+    };
+    h8 nW[NKD], nKtt[NKC];
+    f4 nU = zero4();
+    float nGam = 0.f;
+    auto fetch = [&](int g) {
+        if (du) {
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb) nW[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FW) + afrag_off(mb, kb, NKD, lane));
+            nU = load_tile(rec_at(P, h, g, R::U) + mb * 16 * DV + c0, DV);
+        }
+        if (hasrb) {
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb)
+                nKtt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKTT) + afrag_off(rb, kb, NKC, lane));
+        }
+        if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
+    };
+    if (g0 < g1) fetch(g0);
+    for (int g = g0; g < g1; ++g) {
+        h8 Wf[NKD], Ktt[NKC];
+#pragma unroll
+        for (int kb = 0; kb < NKD; ++kb) Wf[kb] = nW[kb];
+#pragma unroll
+        for (int kb = 0; kb < NKC; ++kb) Ktt[kb] = nKtt[kb];
+        const f4 uu = nU;
+        if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
+        if (hasrb) {
+            put_btile(sS, KPD, rb * 16, S);
+            store_tile(rec_at(P, h, g, R::SIN) + rb * 16 * DV + c0, DV, S);
+        }
+        __syncthreads();
+        if (g + 1 < g1) fetch(g + 1);
+        // U' = U - W S
+        if (du) {
+            f4 x = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKD; ++kb) x = mfma16(Wf[kb], bfrag(sS, KPD, kb), x);
+            const f4 uc = uu - x;
+            put_btile(sU, KPC, mb * 16, uc);
+            store_tile(rec_at(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
+        }
+        __syncthreads();
+        // S <- Diag(gamma) S + Kt^T U'
+        if (hasrb) {
+            f4 sv = S;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sv[e] *= sGam[rb * 16 + 4 * j + e];
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb) sv = mfma16(Ktt[kb], bfrag(sU, KPC, kb), sv);
+            S = sv;
+        }
+        __syncthreads();
     }
 }
 
@@ -951,15 +1189,15 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         if ((e = set_lds(k1, l1)) != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kPrepThreads), l1, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        auto k2 = bwd_ckpt_kernel<DK, DV>;
-        constexpr int l2 = CkptB<DK>::bytes;
+        auto k2 = ABF16 ? bwd_ckpt16_kernel<DK, DV> : bwd_ckpt_kernel<DK, DV>;
+        constexpr int l2 = ABF16 ? Chain16B<DK>::bytes : CkptB<DK>::bytes;
         if ((e = set_lds(k2, l2)) != hipSuccess) return e;
         hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(kChainThreads), l2, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chain_blocks > 0) {
-        auto k3 = bwd_rev_kernel<DK, DV, ABF16>;
-        constexpr int l3 = RevB<DK>::bytes;
+        auto k3 = ABF16 ? bwd_rev16_kernel<DK, DV> : bwd_rev_kernel<DK, DV, ABF16>;
+        constexpr int l3 = ABF16 ? Chain16B<DK>::bytes : RevB<DK>::bytes;
         if ((e = set_lds(k3, l3)) != hipSuccess) return e;
         hipLaunchKernelGGL(k3, dim3(chain_blocks), dim3(kChainThreads), l3, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -254,5 +254,55 @@ __device__ __forceinline__ void chain_coords(int& tile, int& pair) {
     pair = (slot / NT) * 8 + xcd;
 }
 
+
+// ---------------------------------------------------------------------------
+// fp16 matrix-core operands (v_mfma_f32_16x16x32_f16) for the 16-bit paths.
+//   A lane l holds A[l % 16][32 kb + 8 (l / 16) + e], e = 0..7
+//   B lane l holds B[32 kb + 8 (l / 16) + e][l % 16]
+//   D as for the fp32 tile.
+// A operands live in memory fragment-major: fragment (mb, kb) of an M x K
+// matrix is 64 lanes x 8 halves at ((mb * K / 32 + kb) * 64 + lane) * 8, so a
+// wavefront reads 1 KiB of consecutive bytes.  B operands are staged in LDS
+// column by column ([16][K + 8] halves), so a lane reads its 8 reduction
+// indices as one 16-byte word.
+// ---------------------------------------------------------------------------
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma16(const h8& a, const h8& b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ size_t afrag_off(int mb, int kb, int nkb, int lane) {
+    return (static_cast<size_t>(mb * nkb + kb) * 64 + lane) * 8;
+}
+
+// Write the fp16 A fragments of an M x K matrix whose element (m, k) is elem(m, k).
+template <int M, int K, int NTH, typename F>
+__device__ __forceinline__ void write_afrags(_Float16* dst, F elem) {
+    constexpr int NKB = K / 32, N = (M / 16) * NKB * 64;
+    for (int idx = threadIdx.x; idx < N; idx += NTH) {
+        const int f = idx >> 6, lane = idx & 63, mb = f / NKB, kb = f % NKB;
+        const int m = 16 * mb + (lane & 15), k0 = 32 * kb + 8 * (lane >> 4);
+        h8 v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(elem(m, k0 + e));
+        *reinterpret_cast<h8*>(dst + static_cast<size_t>(idx) * 8) = v;
+    }
+}
+
+// B operand word of lane l from a column-major LDS tile (row stride KP halves)
+__device__ __forceinline__ h8 bfrag(const _Float16* t, int kp, int kb) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    return *reinterpret_cast<const h8*>(t + i * kp + 32 * kb + 8 * j);
+}
+
+// D-layout fp32 tile holding rows k = k0 + 4 (l / 16) + e of B -> column-major fp16 LDS tile
+__device__ __forceinline__ void put_btile(_Float16* t, int kp, int k0, f4 v) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    h4 h = {static_cast<_Float16>(v[0]), static_cast<_Float16>(v[1]), static_cast<_Float16>(v[2]),
+            static_cast<_Float16>(v[3])};
+    *reinterpret_cast<h4*>(t + i * kp + k0 + 4 * j) = h;
+}
 }  // namespace mm32
 }  // namespace kda
