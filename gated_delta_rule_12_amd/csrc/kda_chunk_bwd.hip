@@ -541,8 +541,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev_kernel(const BwdParams 
 // fragments (Kt, P^T, Qh^T, W^T; or W, Kt^T) straight from the record,
 // fragment-major, one chunk ahead; the B operands (dO, dS, dU'; or S, U')
 // pass through LDS as column-major fp16 tiles.  The states and their
-// gradients stay fp32 in registers, and every record value is written in
-// fp32.  Waves 0..3 compute the C x 16 product (row block = wave), every
+// gradients stay fp32 in registers; the state entering each chunk, the
+// state gradient, U' and dU' go to the record in fp16 (their one reader,
+// the 16-bit value-side kernel, takes them as fp16 operands anyway).  Waves 0..3 compute the C x 16 product (row block = wave), every
 // wave one 16-row block of the d_k x 16 state tile.
 // ---------------------------------------------------------------------------
 template <int DK> struct Chain16B {
@@ -576,6 +577,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
     f4 dS = (P.dfinal_state && hasrb) ? load_tile(P.dfinal_state + sbase + rb * 16 * DV + c0, DV) : zero4();
     auto hrec = [&](int g, size_t off) {
         return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
+    };
+    auto hrec_w = [&](int g, size_t off) {
+        return reinterpret_cast<_Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
     // the next (earlier) chunk's operands
     h8 nKt[NKD], nPt[NKC], nQt[NKC], nWt[NKC];
@@ -625,7 +629,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
         if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         if (hasrb) {
             put_btile(sdS, KPD, rb * 16, dS);
-            store_tile(rec_at(P, h, g, R::DSO) + rb * 16 * DV + c0, DV, dS);
+            store_tile16(hrec_w(g, R::DSO) + rb * 16 * DV + c0, DV, dS);
         }
         __syncthreads();
         if (g > g0) fetch(g - 1);
@@ -638,7 +642,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
             for (int kb = 0; kb < NKC; ++kb)
                 if (32 * kb + 31 >= 16 * mb) acc = mfma16(Pt[kb], bfrag(sdO, KPC, kb), acc);
             put_btile(sdU, KPC, mb * 16, acc);
-            store_tile(rec_at(P, h, g, R::DUC) + mb * 16 * DV + c0, DV, acc);
+            store_tile16(hrec_w(g, R::DUC) + mb * 16 * DV + c0, DV, acc);
         }
         __syncthreads();
         // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'
@@ -685,6 +689,9 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
     auto hrec = [&](int g, size_t off) {
         return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
+    auto hrec_w = [&](int g, size_t off) {
+        return reinterpret_cast<_Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
+    };
     h8 nW[NKD], nKtt[NKC];
     f4 nU = zero4();
     float nGam = 0.f;
@@ -712,7 +719,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
         if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         if (hasrb) {
             put_btile(sS, KPD, rb * 16, S);
-            store_tile(rec_at(P, h, g, R::SIN) + rb * 16 * DV + c0, DV, S);
+            store_tile16(hrec_w(g, R::SIN) + rb * 16 * DV + c0, DV, S);
         }
         __syncthreads();
         if (g + 1 < g1) fetch(g + 1);
@@ -723,7 +730,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
             for (int kb = 0; kb < NKD; ++kb) x = mfma16(Wf[kb], bfrag(sS, KPD, kb), x);
             const f4 uc = uu - x;
             put_btile(sU, KPC, mb * 16, uc);
-            store_tile(rec_at(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
+            store_tile16(hrec_w(g, R::UC) + mb * 16 * DV + c0, DV, uc);
         }
         __syncthreads();
         // S <- Diag(gamma) S + Kt^T U'
@@ -884,6 +891,242 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
     }
     __syncthreads();
     if (tid < C) rec_at(P, h, g, R::DBZ)[tid] = sDbz[tid] + sDbz[C + tid];
+}
+
+// ---------------------------------------------------------------------------
+// bwd_vside16_kernel: the value-side contractions for 16-bit activations, on
+// the fp16 matrix cores.  One 512-thread WG per (chunk, head), the value
+// dimension in slices of 64 columns: S, dS_next, U', dU' (fp16 in the
+// record), dO and V are staged row-major in LDS, so both operands of every
+// product read their 8 reduction indices as one 16-byte word; T^T and a
+// transposed copy of dU' serve dZ = T^T dU'.  Same outputs as the fp32 kernel.
+// ---------------------------------------------------------------------------
+template <int DK, int DV> struct Vside16B {
+    static constexpr int SW = DV < 64 ? DV : 64, RS = SW + 8, CS = C + 8, NZB = SW / 16;
+    static constexpr int halves = 2 * DK * RS + 4 * C * RS + SW * CS + C * CS;
+    static constexpr int bytes = halves * 2 + (C + NZB * C) * 4;
+};
+
+template <int DK, int DV, bool ABF16>
+__global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
+    using R = BRec<DK, DV>;
+    using VB = Vside16B<DK, DV>;
+    constexpr int NTH = 512, SW = VB::SW, RS = VB::RS, CS = VB::CS, NZB = VB::NZB, NKS = SW / 32;
+    constexpr int NB = DK / 16;
+    constexpr int NTASK = 12 * NB + 10 + 16;
+    constexpr int KT = (NTASK + 7) / 8;
+    extern __shared__ float lds[];
+    _Float16* sS = reinterpret_cast<_Float16*>(lds);   // S[:, slice]         [DK][RS]
+    _Float16* sdS = sS + DK * RS;                       // dS_next[:, slice]   [DK][RS]
+    _Float16* sdO = sdS + DK * RS;                      // [C][RS]
+    _Float16* sUc = sdO + C * RS;                       // [C][RS]
+    _Float16* sdU = sUc + C * RS;                       // [C][RS]
+    _Float16* sV = sdU + C * RS;                        // [C][RS]
+    _Float16* sdUt = sV + C * RS;                       // dU'[:, slice]^T     [SW][CS]
+    _Float16* sTt = sdUt + SW * CS;                     // T^T                 [C][CS]
+    float* sBeta = reinterpret_cast<float*>(sTt + C * CS);   // [C]
+    float* sDbz = sBeta + C;                            // rowsum(dZ . V) per column block  [NZB][C]
+
+    const int H = P.H;
+    const int h = blockIdx.x % H, g = blockIdx.x / H;
+    if (g >= P.ctrl[0]) return;
+    const int4 ent = P.table[g];
+    const int64_t row0 = ent.y;
+    const int len = ent.z;
+    const int tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
+    auto hrec = [&](size_t off) {
+        return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
+    };
+
+    // Staged slices: every global load of a slice is issued before the first
+    // LDS store, and the next slice's loads are in flight while the current
+    // slice computes.  fp16 record rows ([rows][DV] halves) and activation rows
+    // (clamped to the chunk, zeroed past its end) in 16-byte words.
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    constexpr int W8 = SW / 8, NSK = (DK * W8 + NTH - 1) / NTH, NSC = (C * W8 + NTH - 1) / NTH;
+    h8 nS[NSK], ndS[NSK], nUc[NSC], ndU[NSC];
+    u16x8 ndO[NSC], nV[NSC];
+    auto fetch = [&](int s0) {
+#pragma unroll
+        for (int it = 0; it < NSK; ++it) {
+            const int idx = tid + it * NTH, r = idx / W8, c = (idx % W8) * 8;
+            if (idx < DK * W8) {
+                nS[it] = *reinterpret_cast<const h8*>(hrec(R::SIN) + static_cast<size_t>(r) * DV + s0 + c);
+                ndS[it] = *reinterpret_cast<const h8*>(hrec(R::DSO) + static_cast<size_t>(r) * DV + s0 + c);
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NSC; ++it) {
+            const int idx = tid + it * NTH, r = idx / W8, c = (idx % W8) * 8;
+            if (idx < C * W8) {
+                nUc[it] = *reinterpret_cast<const h8*>(hrec(R::UC) + static_cast<size_t>(r) * DV + s0 + c);
+                ndU[it] = *reinterpret_cast<const h8*>(hrec(R::DUC) + static_cast<size_t>(r) * DV + s0 + c);
+                const int rr = r < len ? r : len - 1;
+                const size_t off = (static_cast<size_t>(row0 + rr) * H + h) * DV + s0 + c;
+                ndO[it] = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(P.dout) + off);
+                nV[it] = *reinterpret_cast<const u16x8*>(static_cast<const uint16_t*>(P.v) + off);
+            }
+        }
+    };
+    auto put = [&]() {
+#pragma unroll
+        for (int it = 0; it < NSK; ++it) {
+            const int idx = tid + it * NTH, r = idx / W8, c = (idx % W8) * 8;
+            if (idx < DK * W8) {
+                *reinterpret_cast<h8*>(sS + r * RS + c) = nS[it];
+                *reinterpret_cast<h8*>(sdS + r * RS + c) = ndS[it];
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < NSC; ++it) {
+            const int idx = tid + it * NTH, r = idx / W8, c = (idx % W8) * 8;
+            if (idx < C * W8) {
+                *reinterpret_cast<h8*>(sUc + r * RS + c) = nUc[it];
+                *reinterpret_cast<h8*>(sdU + r * RS + c) = ndU[it];
+                h8 o, vv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[e] = static_cast<_Float16>(r < len ? bf16_to_f32(ndO[it][e]) : 0.f);
+                    vv[e] = static_cast<_Float16>(r < len ? bf16_to_f32(nV[it][e]) : 0.f);
+                }
+                *reinterpret_cast<h8*>(sdO + r * RS + c) = o;
+                *reinterpret_cast<h8*>(sV + r * RS + c) = vv;
+            }
+        }
+    };
+    static_assert(ABF16, "the 16-bit value-side kernel takes bf16 activations");
+    fetch(0);
+    // T^T (fp16) and beta, once
+    {
+        constexpr int NTT = C * C / 4 / NTH;
+        f4 tv[NTT];
+        const float* gT = rec_at(P, h, g, R::TT);
+#pragma unroll
+        for (int it = 0; it < NTT; ++it) tv[it] = *reinterpret_cast<const f4*>(gT + 4 * (tid + it * NTH));
+        if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
+#pragma unroll
+        for (int it = 0; it < NTT; ++it) {
+            const int idx = 4 * (tid + it * NTH), r = idx / C, c = idx % C;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sTt[(c + e) * CS + r] = static_cast<_Float16>(tv[it][e]);
+        }
+    }
+
+    f4 acc[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) acc[k] = zero4();
+    float dgam = 0.f;
+    float dbz[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+
+    for (int s0 = 0; s0 < DV; s0 += SW) {
+        put();
+        __syncthreads();
+        if (s0 + SW < DV) fetch(s0 + SW);
+        // dU'^T for dZ
+        for (int idx = tid; idx < C * SW; idx += NTH) {
+            const int r = idx / SW, c = idx % SW;
+            sdUt[c * CS + r] = sdU[r * RS + c];
+        }
+        if (tid < DK) {
+#pragma unroll 8
+            for (int c = 0; c < SW; ++c)
+                dgam += static_cast<float>(sdS[tid * RS + c]) * static_cast<float>(sS[tid * RS + c]);
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            const int t = wave + 8 * k;
+            if (t < NTASK) {
+                const _Float16 *pa, *pb;
+                if (t < 12 * NB) {
+                    const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
+                    pa = (which == 0 ? sdO : which == 1 ? sdU : sUc) + mb * 16 * RS;
+                    pb = (which == 2 ? sdS : sS) + nb * 16 * RS;
+                } else if (t < 12 * NB + 10) {
+                    int idx = t - 12 * NB, mb = 0;
+                    while (idx > mb) { idx -= mb + 1; ++mb; }
+                    pa = sdO + mb * 16 * RS;
+                    pb = sUc + idx * 16 * RS;
+                } else {
+                    const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
+                    pa = sdU + mb * 16 * RS;
+                    pb = sV + nb * 16 * RS;
+                }
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc[k] = mfma16(*reinterpret_cast<const h8*>(pa + i * RS + 32 * ks + 8 * j),
+                                    *reinterpret_cast<const h8*>(pb + i * RS + 32 * ks + 8 * j), acc[k]);
+            }
+        }
+        __syncthreads();
+        // dZ = T^T dU'[:, slice] (T^T[m][k] = T[k][m], zero for k < m); dv = beta . dZ
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = wave + 8 * u, zmb = t / NZB, znb = t % NZB;
+            if (zmb >= 4) continue;
+            f4 z = zero4();
+#pragma unroll
+            for (int kb = 0; kb < C / 32; ++kb)
+                if (32 * kb + 31 >= 16 * zmb)
+                    z = mfma16(*reinterpret_cast<const h8*>(sTt + (16 * zmb + i) * CS + 32 * kb + 8 * j),
+                               *reinterpret_cast<const h8*>(sdUt + (16 * znb + i) * CS + 32 * kb + 8 * j), z);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = zmb * 16 + 4 * j + e, col = s0 + znb * 16 + i;
+                if (r < len)
+                    store_out<ABF16>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
+                dbz[u][e] += z[e] * static_cast<float>(sV[r * RS + znb * 16 + i]);
+            }
+        }
+        __syncthreads();
+    }
+
+    // write the value-side products (as the fp32 kernel)
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const int t = wave + 8 * k;
+        if (t >= NTASK) continue;
+        if (t < 12 * NB) {
+            const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
+            const size_t off = which == 0 ? R::DQH : which == 1 ? R::DW : R::DKT;
+            store_tile(rec_at(P, h, g, off) + mb * 16 * DK + nb * 16, DK, which == 1 ? -acc[k] : acc[k]);
+        } else if (t < 12 * NB + 10) {
+            int idx = t - 12 * NB, mb = 0;
+            while (idx > mb) { idx -= mb + 1; ++mb; }
+            f4 x = acc[k];
+            if (idx == mb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
+            }
+            store_tile(rec_at(P, h, g, R::M) + mb * 16 * C + idx * 16, C, x);
+        } else {
+            const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
+            store_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C, acc[k]);
+        }
+    }
+    for (int idx = tid; idx < 6 * 256; idx += NTH) {      // upper blocks of M are zero
+        const int blk = idx >> 8, e = idx & 255;
+        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        rec_at(P, h, g, R::M)[(mb * 16 + (e >> 4)) * C + nb * 16 + (e & 15)] = 0.f;
+    }
+    if (tid < DK) rec_at(P, h, g, R::DGAM)[tid] = dgam;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int t = wave + 8 * u, zmb = t / NZB, znb = t % NZB;
+        if (zmb >= 4) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = row16_sum(dbz[u][e]);
+            if (i == 0) sDbz[znb * C + zmb * 16 + 4 * j + e] = x;
+        }
+    }
+    __syncthreads();
+    if (tid < C) {
+        float x = 0.f;
+#pragma unroll
+        for (int z = 0; z < NZB; ++z) x += sDbz[z * C + tid];
+        rec_at(P, h, g, R::DBZ)[tid] = x;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1203,8 +1446,8 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chunk_blocks > 0) {
-        auto k4 = bwd_vside_kernel<DK, DV, ABF16>;
-        constexpr int l4 = VsideB<DK>::bytes;
+        auto k4 = ABF16 ? bwd_vside16_kernel<DK, DV, true> : bwd_vside_kernel<DK, DV, ABF16>;
+        constexpr int l4 = ABF16 ? Vside16B<DK, DV>::bytes : VsideB<DK>::bytes;
         if ((e = set_lds(k4, l4)) != hipSuccess) return e;
         hipLaunchKernelGGL(k4, dim3(chunk_blocks), dim3(512), l4, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -304,5 +304,12 @@ __device__ __forceinline__ void put_btile(_Float16* t, int kp, int k0, f4 v) {
             static_cast<_Float16>(v[3])};
     *reinterpret_cast<h4*>(t + i * kp + k0 + 4 * j) = h;
 }
+
+// D-layout fp32 tile -> fp16 row-major memory (row stride ld halves)
+__device__ __forceinline__ void store_tile16(_Float16* p, int ld, f4 v) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[(4 * j + e) * ld + i] = static_cast<_Float16>(v[e]);
+}
 }  // namespace mm32
 }  // namespace kda
