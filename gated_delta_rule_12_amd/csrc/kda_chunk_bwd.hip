@@ -1189,69 +1189,84 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
     }
     __syncthreads();
 
+    // C x C products: wave w takes column block nb = w % 4 and row blocks
+    // w / 4 and w / 4 + 2 (two tiles sharing their column block)
+    constexpr int GC = C / 16, GK = DK / 16;
+    const int tnb = wave & 3, tmb0 = wave >> 2;
+    static_assert(NW == 8, "two C x C tiles per wave");
     // dT = (dW Kh^T + N) Diag(beta)
-    for (int t = wave; t < 16; t += NW) {
-        const int mb = t >> 2, nb = t & 3;
-        f4 acc = load_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C);
-        acc = mm<DK, true, true>(sW + mb * 16 * LK, LK, 1, sKh + nb * 16 * LK, 1, LK, acc);
-        acc *= sBeta[nb * 16 + i];
-        store_tile(sX + mb * 16 * LC + nb * 16, LC, acc);
+    {
+        f4 acc[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) acc[r] = load_tile(rec_at(P, h, g, R::N) + (tmb0 + 2 * r) * 16 * C + tnb * 16, C);
+        mm_rows<2, GK, true, true>(sW, LK, 1, sKh + tnb * 16 * LK, 1, LK, tmb0, 2,
+                                   [](int, int) { return true; }, acc);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, acc[r] * sBeta[tnb * 16 + i]);
     }
     __syncthreads();
     // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m)
-    for (int t = wave; t < 16; t += NW) {
-        const int mb = t >> 2, nb = t & 3;
-        const f4 acc = mm_n<false, false>(sT + mb * 16 * LC + mb * 16, 1, LC, sX + mb * 16 * LC + nb * 16, LC, 1,
-                            C - mb * 16, zero4());
-        store_tile(sY + mb * 16 * LC + nb * 16, LC, acc);
+    {
+        f4 acc[2] = {zero4(), zero4()};
+        mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, tmb0, 2,
+                                     [](int mb, int gg) { return gg >= mb; }, acc);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) store_tile(sY + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, acc[r]);
     }
     __syncthreads();
     // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX
-    for (int t = wave; t < 16; t += NW) {
-        const int mb = t >> 2, nb = t & 3;
-        f4 dr = zero4();
-        if (nb <= mb) {
-            // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
-            const f4 ya = mm_n<true, true>(sY + mb * 16 * LC, LC, 1, sT + nb * 16 * LC, 1, LC, (nb + 1) * 16, zero4());
-            const f4 rr = mm<DK, true, true>(sKh + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, zero4());
+    {
+        // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n; tiles above the diagonal are zero
+        f4 ya[2] = {zero4(), zero4()}, rr[2] = {zero4(), zero4()};
+        mm_rows<2, GC, true, true>(sY, LC, 1, sT + tnb * 16 * LC, 1, LC, tmb0, 2,
+                                   [tnb](int mb, int gg) { return tnb <= mb && gg <= tnb; }, ya);
+        mm_rows<2, GK, true, true>(sKh, LK, 1, sKb + tnb * 16 * LK, 1, LK, tmb0, 2,
+                                   [tnb](int mb, int) { return tnb <= mb; }, rr);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = mb * 16 + 4 * j + e, s = nb * 16 + i;
-                const float da = s < r ? -ya[e] : 0.f;
-                const float part = row16_sum(da * rr[e]);
-                if (i == 0) sRow[wave * C + r] += part;
-                dr[e] = sBeta[r] * da;
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int mb = tmb0 + 2 * r2;
+            f4 dr = zero4();
+            if (tnb <= mb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = mb * 16 + 4 * j + e, s = tnb * 16 + i;
+                    const float da = s < r ? -ya[r2][e] : 0.f;
+                    const float part = row16_sum(da * rr[r2][e]);
+                    if (i == 0) sRow[wave * C + r] += part;
+                    dr[e] = sBeta[r] * da;
+                }
             }
+            store_tile(sX + mb * 16 * LC + tnb * 16, LC, dr);
         }
-        store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
     }
     __syncthreads();
 
+    // Column-block products: wave w owns key column block nb = w and all four
+    // row blocks (independent accumulators sharing each B group).
     // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh)
-    f4 dKh[4][CBW], dQh[4][CBW], dKb[4][CBW];
+    f4 dKh[4], dQh[4], dKb[4];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb) dKh[mb] = dQh[mb] = dKb[mb] = zero4();
+    const int nb = wave;
+    const bool own = nb < NCB;
+    static_assert(CBW == 1, "one key column block per wave");
+    if (own) {
+        f4 dy[4] = {zero4(), zero4(), zero4(), zero4()};
+        mm_rows<4, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, 0, 1,
+                                     [](int mb, int gg) { return gg >= mb; }, dy);
 #pragma unroll
-        for (int u = 0; u < CBW; ++u) dKh[mb][u] = dQh[mb][u] = dKb[mb][u] = zero4();
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-        for (int u = 0; u < CBW; ++u) {
-            const int nb = wave + NW * u;
-            if (nb >= NCB) continue;
-            const f4 dy = mm_n<false, false>(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1,
-                               C - mb * 16, zero4());
-            f4 x;
+        for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = mb * 16 + 4 * j + e, c = nb * 16 + i;
-                const float part = row16_sum(dy[e] * sKh[r * LK + c]);
+                const float part = row16_sum(dy[mb][e] * sKh[r * LK + c]);
                 if (i == 0) sRow[wave * C + r] += part;
-                x[e] = sBeta[r] * dy[e];
+                dKh[mb][e] = sBeta[r] * dy[mb][e];
             }
-            // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
-            dKh[mb][u] = mm_n<true, false>(sX + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16, x);
         }
+        // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
+        mm_rows<4, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, 0, 1,
+                                    [](int mb, int gg) { return gg <= mb; }, dKh);
     }
     __syncthreads();
     load_block<C, C, NTH>(sT, LC, rec_at(P, h, g, R::M), C);
@@ -1259,19 +1274,15 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
     __syncthreads();
 
     // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
+    if (own) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-        for (int u = 0; u < CBW; ++u) {
-            const int nb = wave + NW * u;
-            if (nb >= NCB) continue;
-            dQh[mb][u] = mm_n<true, false>(sT + mb * 16 * LC, LC, 1, sKb + nb * 16, LK, 1, (mb + 1) * 16,
-                              load_tile(rec_at(P, h, g, R::DQH) + mb * 16 * DK + nb * 16, DK));
-            f4 y = mm_n<false, false>(sT + mb * 16 * LC + mb * 16, 1, LC, sW + mb * 16 * LK + nb * 16, LK, 1, C - mb * 16,
-                        zero4());
-            dKb[mb][u] = mm_n<false, false>(sX + mb * 16 * LC + mb * 16, 1, LC, sKh + mb * 16 * LK + nb * 16, LK, 1,
-                              C - mb * 16, y);
-        }
+        for (int mb = 0; mb < 4; ++mb) dQh[mb] = load_tile(rec_at(P, h, g, R::DQH) + mb * 16 * DK + nb * 16, DK);
+        mm_rows<4, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, 0, 1,
+                                    [](int mb, int gg) { return gg <= mb; }, dQh);
+        mm_rows<4, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, 0, 1,
+                                     [](int mb, int gg) { return gg >= mb; }, dKb);
+        mm_rows<4, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, 0, 1,
+                                     [](int mb, int gg) { return gg >= mb; }, dKb);
     }
     __syncthreads();
 
@@ -1325,7 +1336,7 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
                 const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
                 const float qv = sKh[r * LK + c], kv = sKb[r * LK + c], dkt = sD[r * LK + c];
                 const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam * kb;
-                const float dqh = dQh[mb][u][e], dkh = dKh[mb][u][e], dkb = dKb[mb][u][e];
+                const float dqh = dQh[mb][e], dkh = dKh[mb][e], dkb = dKb[mb][e];
                 if (r < len) {
                     const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
                     store_out<ABF16>(P.dq, ai, G * dqh);

@@ -311,5 +311,35 @@ __device__ __forceinline__ void store_tile16(_Float16* p, int ld, f4 v) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[(4 * j + e) * ld + i] = static_cast<_Float16>(v[e]);
 }
+
+// R output tiles that share their column block: tile r is row block
+// mb0 + r * mstep, and acc[r] += sum over the 16-deep groups g of the
+// reduction with inrange(row block, g) of A(m, k) B(k, n).  Each group's B
+// operand is read once for all R tiles, and the R accumulators are
+// independent chains, so their products overlap.
+template <int R, int G, bool AV, bool BV, typename Range>
+__device__ __forceinline__ void mm_rows(const float* pa, int am, int ak, const float* pb, int bk, int bn,
+                                        int mb0, int mstep, Range inrange, f4 (&acc)[R]) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        bool any = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) any |= inrange(mb0 + r * mstep, g);
+        if (!any) continue;
+        const f4 b = grp4<BV>(pb + 16 * g * bk, bk);
+        f4 a[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            if (inrange(mb0 + r * mstep, g)) a[r] = grp4<AV>(pa + 16 * (mb0 + r * mstep) * am + 16 * g * ak, ak);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (inrange(mb0 + r * mstep, g)) acc[r] = mfma4(a[r][s2], b[s2], acc[r]);
+    }
+}
 }  // namespace mm32
 }  // namespace kda
