@@ -24,23 +24,26 @@
 // Launches, on the caller's stream:
 //   plan_kernel        the forward's chunk table (shared launcher)
 //   bwd_prep_kernel    one WG per (chunk, head): b, Gamma.Q, (gamma/Gamma).K,
-//                      A, T = (I + A)^-1, W, U, P, gamma -> fp32 record
+//                      A, T = (I + A)^-1, W, U, P, gamma -> record
 //   bwd_ckpt_kernel    one WG per (sequence, head, 16 value columns),
-//                      chunks in order: the state entering each chunk and U'
+//   (bwd_ckpt16)       chunks in order: the state entering each chunk and U'
 //   bwd_rev_kernel     one WG per (sequence, head, 16 value columns),
-//                      chunks last to first: dS_next of each chunk and dU';
+//   (bwd_rev16)        chunks last to first: dS_next of each chunk and dU';
 //                      dS_0 at the end
-//   bwd_vside_kernel   one WG per (chunk, head): every contraction over the
+//   bwd_grad_kernel    one WG per (chunk, head): every contraction over the
 //                      value dimension (dO S^T, dU' S^T, U' dS_next^T, M,
-//                      dU' V^T, dgamma) and dv = beta . T^T dU'
-//   bwd_kside_kernel   one WG per (chunk, head): dT, dA, R, dY, dKh, dQh, dKb,
-//                      the gate chain rule, dq, dk, dgate, dbeta
+//                      dU' V^T, dgamma), dv = beta . T^T dU', then dT, dA, R,
+//                      dY, dKh, dQh, dKb, the gate chain rule, dq, dk, dgate,
+//                      dbeta
 //
-// Numerics: every product is fp32 on the fp32 matrix cores (16x16x4), every
-// intermediate is stored in fp32.  Under the decay precondition of the
-// forward (per channel, < e^10 over any 8 tokens, so < e^80 over a chunk)
-// Gamma = 2^b and 1/Gamma stay fp32-normal over a chunk, so Kh = Gamma.K and
-// Kb = K/Gamma are formed directly.
+// Numerics: with fp32 activations every product runs on the fp32 matrix
+// cores (16x16x4) and every intermediate is stored in fp32.  With bf16
+// activations the two state passes and the value-side contractions take
+// fp16 operands (fp32 accumulation) and the record keeps S, dS_next, U', dU'
+// and those operands in fp16; the key-side products stay fp32.  Under the
+// decay precondition of the forward (per channel, < e^10 over any 8 tokens,
+// so < e^80 over a chunk) Gamma = 2^b and 1/Gamma stay fp32-normal over a
+// chunk, so Kh = Gamma.K and Kb = K/Gamma are formed directly.
 #include "kda_chunk.h"
 #include "kda_common.h"
 #include "kda_mm32.h"
@@ -64,8 +67,7 @@ template <int DK, int DV> struct BRec {
     static constexpr size_t QH = 0;              // Gamma . Q                 [C][DK]
     static constexpr size_t KT = QH + CK;        // (gamma / Gamma) . K       [C][DK]
     static constexpr size_t W = KT + CK;         // T Diag(beta) (Gamma . K)  [C][DK]
-    static constexpr size_t B = W + CK;          // b = cumsum(log2 alpha)     [C][DK]
-    static constexpr size_t U = B + CK;          // T Diag(beta) V            [C][DV]
+    static constexpr size_t U = W + CK;          // T Diag(beta) V            [C][DV]
     static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]
     static constexpr size_t TT = P + CC;         // (I + A)^-1                [C][C]
     static constexpr size_t GAM = TT + CC;       // gamma                     [DK]
@@ -73,16 +75,9 @@ template <int DK, int DV> struct BRec {
     static constexpr size_t DSO = SIN + KV;      // dL/d(state leaving)       [DK][DV]
     static constexpr size_t UC = DSO + KV;       // U' = U - W S              [C][DV]
     static constexpr size_t DUC = UC + CV;       // dL/dU'                    [C][DV]
-    static constexpr size_t DQH = DUC + CV;      // dO S^T                    [C][DK]
-    static constexpr size_t DW = DQH + CK;       // -dU' S^T                  [C][DK]
-    static constexpr size_t DKT = DW + CK;       // U' dS_next^T              [C][DK]
-    static constexpr size_t M = DKT + CK;        // Tril(dO U'^T)             [C][C]
-    static constexpr size_t N = M + CC;          // dU' V^T                   [C][C]
-    static constexpr size_t DGAM = N + CC;       // rowsum(dS_next . S)       [DK]
-    static constexpr size_t DBZ = DGAM + size_t(DK) * 4;  // rowsum(dZ . V)  [C]
     // fp16 A fragments of the state passes' products (16-bit activations only)
     static constexpr size_t HK = size_t(C) * DK * 2;
-    static constexpr size_t FKT = DBZ + size_t(C) * 4;    // Kt                [C][DK]
+    static constexpr size_t FKT = DUC + CV;               // Kt                [C][DK]
     static constexpr size_t FKTT = FKT + HK;              // Kt^T              [DK][C]
     static constexpr size_t FQHT = FKTT + HK;             // Qh^T              [DK][C]
     static constexpr size_t FW = FQHT + HK;               // W                 [C][DK]
@@ -123,6 +118,38 @@ __device__ __forceinline__ float* rec_at(const BwdParams& P, int h, int g, size_
 // ---------------------------------------------------------------------------
 // bwd_prep_kernel: one (chunk, head), 512 threads.
 // ---------------------------------------------------------------------------
+// b = cumsum over the chunk's rows of log2 alpha, per key channel; padding
+// rows add 0.  On entry s[r * ld + c] holds the gate as given (for the scalar
+// gate, sGs[r]); `each(r, c, b)` receives every b in row order per channel and
+// may overwrite s[r * ld + c].  NTH / DK row segments per channel: segment
+// sums first, then each segment's scan from the sum of the segments before
+// it.  sPart holds NTH floats of scratch; one barrier inside, none at the end.
+template <int DK, int NTH, int GATE, typename F>
+__device__ __forceinline__ void gate_cumsum(float* s, int ld, const float* sGs, int len, float* sPart, F&& each) {
+    constexpr int NS = NTH / DK, SEG = C / NS;
+    static_assert(NS * SEG == C, "row segments tile the chunk");
+    const int c = threadIdx.x % DK, sg = threadIdx.x / DK;
+    float part = 0.f;
+    for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
+        float l2 = 0.f;
+        if (r < len) {
+            if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
+            else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) l2 = log2_alpha_from_softplus_arg(s[r * ld + c]);
+            else l2 = __builtin_amdgcn_logf(s[r * ld + c]);
+        }
+        s[r * ld + c] = l2;
+        part += l2;
+    }
+    sPart[sg * DK + c] = part;
+    __syncthreads();
+    float b = 0.f;
+    for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * DK + c];
+    for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
+        b += s[r * ld + c];
+        each(r, c, b);
+    }
+}
+
 constexpr int kPrepThreads = 512, kPrepWaves = kPrepThreads / 64;
 
 template <int DK, int DV> struct PrepB {
@@ -171,50 +198,24 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
     }
     __syncthreads();
 
-    // b = cumsum(log2 alpha) per channel (padding rows add 0), in NS row
-    // segments per channel: segment sums first, then each segment's scan from
-    // the sum of the segments before it.
+    // b = cumsum(log2 alpha) per channel;
     // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
-    float* gB = rec_at(P, h, g, R::B);
     float* gGam = rec_at(P, h, g, R::GAM);
     float* gKt = rec_at(P, h, g, R::KT);
-    constexpr int NS = NTH / DK, SEG = C / NS;
-    float* sPart = sA;                   // [NS][DK] (A is formed later)
-    {
-        const int c = tid % DK, sg = tid / DK;
-        float part = 0.f;
-        for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-            float l2 = 0.f;
-            if (r < len) {
-                if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
-                else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sKb[r * LK + c]);
-                else l2 = __builtin_amdgcn_logf(sKb[r * LK + c]);
-            }
-            sKb[r * LK + c] = l2;
-            part += l2;
-        }
-        sPart[sg * DK + c] = part;
-    }
+    gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sA, [&](int r, int c, float b) {
+        const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+        const float kv = sKh[r * LK + c];
+        sKh[r * LK + c] = G * kv;
+        sKb[r * LK + c] = Gi * kv;
+        sQ[r * LK + c] *= G;
+        if (r == C - 1) gGam[c] = sGam[c] = G;
+    });
     __syncthreads();
-    {
-        const int c = tid % DK, sg = tid / DK;
-        float b = 0.f;
-        for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * DK + c];
-        for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-            b += sKb[r * LK + c];
-            const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-            const float kv = sKh[r * LK + c];
-            sKh[r * LK + c] = G * kv;
-            sKb[r * LK + c] = Gi * kv;
-            sQ[r * LK + c] *= G;
-            gB[r * DK + c] = b;
+    if constexpr (!ABF16) {              // the 16-bit passes read Kt as fp16 fragments only
+        for (int idx = tid; idx < C * DK; idx += NTH) {
+            const int r = idx / DK, c = idx % DK;
+            gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
         }
-        if (sg == NS - 1) gGam[c] = sGam[c] = __builtin_amdgcn_exp2f(b);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < C * DK; idx += NTH) {
-        const int r = idx / DK, c = idx % DK;
-        gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
     }
     store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
     if constexpr (ABF16) {
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
             else acc[e] = s2 < r ? sBeta[r] * acc[e] : 0.f;
         }
         if (which) {
-            store_tile(gP + mb * 16 * C + nb * 16, C, acc);
             if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, acc);   // P, for P^T fragments
+            else store_tile(gP + mb * 16 * C + nb * 16, C, acc);
         } else {
             store_tile(sA + mb * 16 * LC + nb * 16, LC, acc);
         }
@@ -322,8 +323,8 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
         const f4 acc = mm_n<true, false>(sT + mb * 16 * LC, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1,
                             (mb + 1) * 16, zero4());
         if (isw) {
-            store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
             if constexpr (ABF16) store_tile(sKb + mb * 16 * LK + nb * 16, LK, acc);   // W, for its fragments
+            else store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
         } else {
             store_tile(gU + mb * 16 * DV + nb * 16, DV, acc);
         }
@@ -554,7 +555,7 @@ template <int DK> struct Chain16B {
 template <int DK, int DV>
 __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
-    constexpr int NW = kChainWaves, NT = DV / 16, NRB = DK / 16;
+    constexpr int NT = DV / 16, NRB = DK / 16;
     constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
     extern __shared__ float lds[];
     _Float16* sdO = reinterpret_cast<_Float16*>(lds);    // dO tile, column-major  [16][KPC]
@@ -747,44 +748,93 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
 }
 
 // ---------------------------------------------------------------------------
-// bwd_vside_kernel: one (chunk, head), 512 threads; the value dimension is
-// taken in slices of 32 columns, the products accumulate in registers.
+// bwd_grad_kernel: every per-chunk gradient, after the two state passes.  One
+// 512-thread WG per (chunk, head), in two phases over the same LDS:
+//
+//   value side  every contraction over d_v (dO S^T, dU' S^T, U' dS_next^T,
+//               M = Tril(dO U'^T), N = dU' V^T, dgamma), dZ = T^T dU' and
+//               dv = beta . dZ; the products stay in the accumulators of the
+//               waves that consume them below (only dW and M pass through LDS)
+//   key side    dT, dA, R, dY, dKh, dQh, dKb, the gate chain rule, dq, dk,
+//               dgate, dbeta
+//
+// Task numbering of the value-side products (t = wave + 8 k, accumulator k):
+//   t < 12 NB            dO S^T, dU' S^T, U' dS_next^T: tile (mb, nb) of the
+//                        which-th product at which * 4 NB + mb * NB + nb
+//   12 NB + 4 mb + nb    M tile (mb, nb), zero above the diagonal
+//   12 NB + 16 + ...     N tile (mb, nb)
+// so with NB = d_k / 16 key column blocks the C x d_k tiles of wave w are
+// column block w % NB, row blocks w / NB + r 8 / NB (r < NB / 2), and its
+// C x C tiles are column block w % 4, row blocks w / 4 and w / 4 + 2: the
+// ownership of the key-side phase.
 // ---------------------------------------------------------------------------
-constexpr int kSW = 32, kLS = kSW + 4;
+constexpr int kGradThreads = 512, kGradWaves = kGradThreads / 64;
 
-template <int DK> struct VsideB {
-    static constexpr int bytes = (2 * DK * kLS + 4 * C * kLS + C * LC + 3 * C) * 4;
+template <int DK> struct GradTasks {
+    static constexpr int NB = DK / 16;          // key column blocks
+    static constexpr int RW = NB / 2;           // tiles of one C x d_k product per wave
+    static constexpr int MSTEP = 8 / NB;        // row-block step between them (= waves per column block)
+    static constexpr int KM = 12 * NB / 8;      // accumulator of the wave's first M tile (then M, N, N)
+    static constexpr int NTASK = 12 * NB + 32;
+    static constexpr int KT = NTASK / 8;
+    static_assert(NB == 4 || NB == 8, "d_k of 64 or 128");
 };
 
-template <int DK, int DV, bool ABF16>
-__global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
+template <int DK> struct GradB {
+    static constexpr int LK = Ld<DK>::value;
+    // key side: Kh, Kb, dW | three C x C tiles | beta, dbeta rows, Kt.dKt column sums, dgamma, rowsum(dZ.V)
+    static constexpr int region = (3 * C * LK + 2 * C * LC) * 4;   // value-side scratch: everything before T
+    static constexpr int bytes =
+        (3 * C * LK + 3 * C * LC + C + kGradWaves * C + GradTasks<DK>::MSTEP * DK + DK + C) * 4;
+};
+
+// Decode value-side task t: operand rows of A and B (row-major, reduction
+// along the row) and whether the tile is computed at all.
+template <int NB, typename E>
+__device__ __forceinline__ bool grad_task(int t, const E* sdO, const E* sdU, const E* sUc, const E* sS,
+                                          const E* sdS, const E* sV, int ld, const E*& pa, const E*& pb) {
+    if (t < 12 * NB) {
+        const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
+        pa = (which == 0 ? sdO : which == 1 ? sdU : sUc) + mb * 16 * ld;
+        pb = (which == 2 ? sdS : sS) + nb * 16 * ld;
+        return true;
+    }
+    const int tt = (t - 12 * NB) & 15, mb = tt >> 2, nb = tt & 3;
+    if (t < 12 * NB + 16) {
+        pa = sdO + mb * 16 * ld;
+        pb = sUc + nb * 16 * ld;
+        return nb <= mb;
+    }
+    pa = sdU + mb * 16 * ld;
+    pb = sV + nb * 16 * ld;
+    return true;
+}
+
+// Value side, fp32 activations: the value dimension in slices of kSW
+// columns, fp32 matrix cores; sT holds T (fp32), sBeta beta.
+constexpr int kSW = 32, kLS = kSW + 4;
+
+template <int DK, int DV>
+__device__ __forceinline__ void vside_phase32(const BwdParams& P, int h, int g, int64_t row0, int len, float* region,
+                                              float* sT, float* sBeta, f4 (&acc)[GradTasks<DK>::KT],
+                                              float* sDgam, float* sDbz) {
     using R = BRec<DK, DV>;
-    constexpr int NB = DK / 16;
-    constexpr int NTASK = 12 * NB + 10 + 16;
-    constexpr int KT = (NTASK + 7) / 8;
-    extern __shared__ float lds[];
-    float* sS = lds;                 // S[:, slice]        [DK][kLS]
+    using GT = GradTasks<DK>;
+    constexpr int NTH = kGradThreads, NB = GT::NB, KT = GT::KT;
+    static_assert((2 * DK * kLS + 4 * C * kLS + 2 * C) * 4 <= GradB<DK>::region, "value-side scratch fits");
+    float* sS = region;              // S[:, slice]        [DK][kLS]
     float* sdS = sS + DK * kLS;      // dS_next[:, slice]  [DK][kLS]
     float* sdO = sdS + DK * kLS;     // [C][kLS]
     float* sUc = sdO + C * kLS;      // [C][kLS]
     float* sdU = sUc + C * kLS;      // [C][kLS]
     float* sV = sdU + C * kLS;       // [C][kLS]
-    float* sT = sV + C * kLS;        // [C][LC]
-    float* sBeta = sT + C * LC;      // [C]
-    float* sDbz = sBeta + C;         // rowsum(dZ . V), one row per column half  [2][C]
-
-    const int H = P.H;
-    const int h = blockIdx.x % H, g = blockIdx.x / H;
-    if (g >= P.ctrl[0]) return;
-    const int4 ent = P.table[g];
-    const int64_t row0 = ent.y;
-    const int len = ent.z;
-    const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
+    float* sDbzP = sV + C * kLS;     // rowsum(dZ . V), one row per column half  [2][C]
+    const int H = P.H, tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
 
     // value slices, the next one in flight while the current one computes
-    Blk<DK, kSW, 512> nS, ndS;
-    Blk<C, kSW, 512> nUc, ndU;
-    Tok<ABF16, DV, kSW, 512> ndO, nV;
+    Blk<DK, kSW, NTH> nS, ndS;
+    Blk<C, kSW, NTH> nUc, ndU;
+    Tok<false, DV, kSW, NTH> ndO, nV;
     auto fetch = [&](int s0) {
         nS.load(rec_at(P, h, g, R::SIN) + s0, DV);
         ndS.load(rec_at(P, h, g, R::DSO) + s0, DV);
@@ -794,9 +844,8 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
         nV.load(P.v, row0, len, h, H, s0);
     };
     fetch(0);
-    load_block<C, C, 512>(sT, LC, rec_at(P, h, g, R::TT), C);
+    load_block<C, C, NTH>(sT, LC, rec_at(P, h, g, R::TT), C);
     if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
-    f4 acc[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) acc[k] = zero4();
     float dgam = 0.f;
@@ -818,25 +867,9 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
         }
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
-            const int t = wave + 8 * k;
-            if (t < NTASK) {
-                const float *pa, *pb;
-                if (t < 12 * NB) {
-                    const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
-                    pa = (which == 0 ? sdO : which == 1 ? sdU : sUc) + mb * 16 * kLS;
-                    pb = (which == 2 ? sdS : sS) + nb * 16 * kLS;
-                } else if (t < 12 * NB + 10) {
-                    int idx = t - 12 * NB, mb = 0;
-                    while (idx > mb) { idx -= mb + 1; ++mb; }
-                    pa = sdO + mb * 16 * kLS;
-                    pb = sUc + idx * 16 * kLS;
-                } else {
-                    const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
-                    pa = sdU + mb * 16 * kLS;
-                    pb = sV + nb * 16 * kLS;
-                }
+            const float *pa, *pb;
+            if (grad_task<NB>(wave + 8 * k, sdO, sdU, sUc, sS, sdS, sV, kLS, pa, pb))
                 acc[k] = mm<kSW, true, true>(pa, kLS, 1, pb, 1, kLS, acc[k]);
-            }
         }
         // dZ = T^T dU'[:, slice] (T^T[m][k] = T[k][m], zero for k < m); dv = beta . dZ
         {
@@ -845,95 +878,52 @@ __global__ __launch_bounds__(512) void bwd_vside_kernel(const BwdParams P) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = zmb * 16 + 4 * j + e, col = s0 + znb * 16 + i;
-                if (r < len)
-                    store_out<ABF16>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
+                if (r < len) store_out<false>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
                 dbz[e] += z[e] * sV[r * kLS + znb * 16 + i];
             }
         }
         __syncthreads();
     }
-
-    // write the value-side products
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        const int t = wave + 8 * k;
-        if (t >= NTASK) continue;
-        if (t < 12 * NB) {
-            const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
-            const size_t off = which == 0 ? R::DQH : which == 1 ? R::DW : R::DKT;
-            store_tile(rec_at(P, h, g, off) + mb * 16 * DK + nb * 16, DK, which == 1 ? -acc[k] : acc[k]);
-        } else if (t < 12 * NB + 10) {
-            int idx = t - 12 * NB, mb = 0;
-            while (idx > mb) { idx -= mb + 1; ++mb; }
-            f4 x = acc[k];
-            if (idx == mb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
-            }
-            store_tile(rec_at(P, h, g, R::M) + mb * 16 * C + idx * 16, C, x);
-        } else {
-            const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
-            store_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C, acc[k]);
-        }
-    }
-    // upper blocks of M are zero
-    for (int idx = tid; idx < 6 * 256; idx += 512) {
-        const int blk = idx >> 8, e = idx & 255;
-        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-        rec_at(P, h, g, R::M)[(mb * 16 + (e >> 4)) * C + nb * 16 + (e & 15)] = 0.f;
-    }
-    if (tid < DK) rec_at(P, h, g, R::DGAM)[tid] = dgam;
+    if (tid < DK) sDgam[tid] = dgam;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const float x = row16_sum(dbz[e]);
-        if (i == 0) sDbz[znb * C + zmb * 16 + 4 * j + e] = x;
+        if (i == 0) sDbzP[znb * C + zmb * 16 + 4 * j + e] = x;
     }
     __syncthreads();
-    if (tid < C) rec_at(P, h, g, R::DBZ)[tid] = sDbz[tid] + sDbz[C + tid];
+    if (tid < C) sDbz[tid] = sDbzP[tid] + sDbzP[C + tid];
 }
 
-// ---------------------------------------------------------------------------
-// bwd_vside16_kernel: the value-side contractions for 16-bit activations, on
-// the fp16 matrix cores.  One 512-thread WG per (chunk, head), the value
-// dimension in slices of 64 columns: S, dS_next, U', dU' (fp16 in the
-// record), dO and V are staged row-major in LDS, so both operands of every
-// product read their 8 reduction indices as one 16-byte word; T^T and a
-// transposed copy of dU' serve dZ = T^T dU'.  Same outputs as the fp32 kernel.
-// ---------------------------------------------------------------------------
-template <int DK, int DV> struct Vside16B {
+// Value side, 16-bit activations: fp16 matrix cores, the value dimension in
+// slices of 64 columns.  S, dS_next, U', dU' (fp16 in the record), dO and V
+// are staged row-major in LDS, so both operands of every product read their
+// 8 reduction indices as one 16-byte word; T^T and a transposed copy of dU'
+// serve dZ = T^T dU'.
+template <int DK, int DV> struct V16L {
     static constexpr int SW = DV < 64 ? DV : 64, RS = SW + 8, CS = C + 8, NZB = SW / 16;
-    static constexpr int halves = 2 * DK * RS + 4 * C * RS + SW * CS + C * CS;
-    static constexpr int bytes = halves * 2 + (C + NZB * C) * 4;
+    static constexpr int bytes = (2 * DK * RS + 4 * C * RS + SW * CS + C * CS) * 2 + NZB * C * 4;
 };
 
-template <int DK, int DV, bool ABF16>
-__global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
+template <int DK, int DV>
+__device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, int64_t row0, int len, float* region,
+                                              float* sT, float* sBeta, f4 (&acc)[GradTasks<DK>::KT],
+                                              float* sDgam, float* sDbz) {
     using R = BRec<DK, DV>;
-    using VB = Vside16B<DK, DV>;
-    constexpr int NTH = 512, SW = VB::SW, RS = VB::RS, CS = VB::CS, NZB = VB::NZB, NKS = SW / 32;
-    constexpr int NB = DK / 16;
-    constexpr int NTASK = 12 * NB + 10 + 16;
-    constexpr int KT = (NTASK + 7) / 8;
-    extern __shared__ float lds[];
-    _Float16* sS = reinterpret_cast<_Float16*>(lds);   // S[:, slice]         [DK][RS]
-    _Float16* sdS = sS + DK * RS;                       // dS_next[:, slice]   [DK][RS]
-    _Float16* sdO = sdS + DK * RS;                      // [C][RS]
-    _Float16* sUc = sdO + C * RS;                       // [C][RS]
-    _Float16* sdU = sUc + C * RS;                       // [C][RS]
-    _Float16* sV = sdU + C * RS;                        // [C][RS]
-    _Float16* sdUt = sV + C * RS;                       // dU'[:, slice]^T     [SW][CS]
-    _Float16* sTt = sdUt + SW * CS;                     // T^T                 [C][CS]
-    float* sBeta = reinterpret_cast<float*>(sTt + C * CS);   // [C]
-    float* sDbz = sBeta + C;                            // rowsum(dZ . V) per column block  [NZB][C]
-
-    const int H = P.H;
-    const int h = blockIdx.x % H, g = blockIdx.x / H;
-    if (g >= P.ctrl[0]) return;
-    const int4 ent = P.table[g];
-    const int64_t row0 = ent.y;
-    const int len = ent.z;
-    const int tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
+    using VB = V16L<DK, DV>;
+    using GT = GradTasks<DK>;
+    constexpr int NTH = kGradThreads, SW = VB::SW, RS = VB::RS, CS = VB::CS, NZB = VB::NZB, NKS = SW / 32;
+    constexpr int NB = GT::NB, KT = GT::KT;
+    static_assert(VB::bytes <= GradB<DK>::region, "value-side scratch fits");
+    _Float16* sS = reinterpret_cast<_Float16*>(region);   // S[:, slice]         [DK][RS]
+    _Float16* sdS = sS + DK * RS;                          // dS_next[:, slice]   [DK][RS]
+    _Float16* sdO = sdS + DK * RS;                         // [C][RS]
+    _Float16* sUc = sdO + C * RS;                          // [C][RS]
+    _Float16* sdU = sUc + C * RS;                          // [C][RS]
+    _Float16* sV = sdU + C * RS;                           // [C][RS]
+    _Float16* sdUt = sV + C * RS;                          // dU'[:, slice]^T     [SW][CS]
+    _Float16* sTt = sdUt + SW * CS;                        // T^T                 [C][CS]
+    float* sDbzP = reinterpret_cast<float*>(sTt + C * CS); // rowsum(dZ . V) per column block  [NZB][C]
+    const int H = P.H, tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
     auto hrec = [&](size_t off) {
         return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
@@ -994,9 +984,8 @@ __global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
             }
         }
     };
-    static_assert(ABF16, "the 16-bit value-side kernel takes bf16 activations");
     fetch(0);
-    // T^T (fp16) and beta, once
+    // T (fp32, kept for the key side) and its fp16 transpose; beta
     {
         constexpr int NTT = C * C / 4 / NTH;
         f4 tv[NTT];
@@ -1007,12 +996,11 @@ __global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
 #pragma unroll
         for (int it = 0; it < NTT; ++it) {
             const int idx = 4 * (tid + it * NTH), r = idx / C, c = idx % C;
+            *reinterpret_cast<f4*>(sT + r * LC + c) = tv[it];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sTt[(c + e) * CS + r] = static_cast<_Float16>(tv[it][e]);
         }
     }
-
-    f4 acc[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) acc[k] = zero4();
     float dgam = 0.f;
@@ -1034,23 +1022,8 @@ __global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
         }
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
-            const int t = wave + 8 * k;
-            if (t < NTASK) {
-                const _Float16 *pa, *pb;
-                if (t < 12 * NB) {
-                    const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
-                    pa = (which == 0 ? sdO : which == 1 ? sdU : sUc) + mb * 16 * RS;
-                    pb = (which == 2 ? sdS : sS) + nb * 16 * RS;
-                } else if (t < 12 * NB + 10) {
-                    int idx = t - 12 * NB, mb = 0;
-                    while (idx > mb) { idx -= mb + 1; ++mb; }
-                    pa = sdO + mb * 16 * RS;
-                    pb = sUc + idx * 16 * RS;
-                } else {
-                    const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
-                    pa = sdU + mb * 16 * RS;
-                    pb = sV + nb * 16 * RS;
-                }
+            const _Float16 *pa, *pb;
+            if (grad_task<NB>(wave + 8 * k, sdO, sdU, sUc, sS, sdS, sV, RS, pa, pb)) {
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks)
                     acc[k] = mfma16(*reinterpret_cast<const h8*>(pa + i * RS + 32 * ks + 8 * j),
@@ -1072,44 +1045,13 @@ __global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = zmb * 16 + 4 * j + e, col = s0 + znb * 16 + i;
-                if (r < len)
-                    store_out<ABF16>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
+                if (r < len) store_out<true>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
                 dbz[u][e] += z[e] * static_cast<float>(sV[r * RS + znb * 16 + i]);
             }
         }
         __syncthreads();
     }
-
-    // write the value-side products (as the fp32 kernel)
-#pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        const int t = wave + 8 * k;
-        if (t >= NTASK) continue;
-        if (t < 12 * NB) {
-            const int which = t / (4 * NB), tt = t % (4 * NB), mb = tt / NB, nb = tt % NB;
-            const size_t off = which == 0 ? R::DQH : which == 1 ? R::DW : R::DKT;
-            store_tile(rec_at(P, h, g, off) + mb * 16 * DK + nb * 16, DK, which == 1 ? -acc[k] : acc[k]);
-        } else if (t < 12 * NB + 10) {
-            int idx = t - 12 * NB, mb = 0;
-            while (idx > mb) { idx -= mb + 1; ++mb; }
-            f4 x = acc[k];
-            if (idx == mb) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
-            }
-            store_tile(rec_at(P, h, g, R::M) + mb * 16 * C + idx * 16, C, x);
-        } else {
-            const int tt = t - 12 * NB - 10, mb = tt >> 2, nb = tt & 3;
-            store_tile(rec_at(P, h, g, R::N) + mb * 16 * C + nb * 16, C, acc[k]);
-        }
-    }
-    for (int idx = tid; idx < 6 * 256; idx += NTH) {      // upper blocks of M are zero
-        const int blk = idx >> 8, e = idx & 255;
-        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-        rec_at(P, h, g, R::M)[(mb * 16 + (e >> 4)) * C + nb * 16 + (e & 15)] = 0.f;
-    }
-    if (tid < DK) rec_at(P, h, g, R::DGAM)[tid] = dgam;
+    if (tid < DK) sDgam[tid] = dgam;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int t = wave + 8 * u, zmb = t / NZB, znb = t % NZB;
@@ -1117,35 +1059,26 @@ __global__ __launch_bounds__(512) void bwd_vside16_kernel(const BwdParams P) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x = row16_sum(dbz[u][e]);
-            if (i == 0) sDbz[znb * C + zmb * 16 + 4 * j + e] = x;
+            if (i == 0) sDbzP[znb * C + zmb * 16 + 4 * j + e] = x;
         }
     }
     __syncthreads();
     if (tid < C) {
         float x = 0.f;
 #pragma unroll
-        for (int z = 0; z < NZB; ++z) x += sDbz[z * C + tid];
-        rec_at(P, h, g, R::DBZ)[tid] = x;
+        for (int z = 0; z < NZB; ++z) x += sDbzP[z * C + tid];
+        sDbz[tid] = x;
     }
 }
 
-// ---------------------------------------------------------------------------
-// bwd_kside_kernel: one (chunk, head), 512 threads.  Wave w owns the key
-// column blocks w, w + 8, ... of every C x DK gradient.
-// ---------------------------------------------------------------------------
-constexpr int kKsideThreads = 512, kKsideWaves = kKsideThreads / 64;
-
-template <int DK> struct KsideB {
-    static constexpr int LK = Ld<DK>::value;
-    static constexpr int bytes = (3 * C * LK + 3 * C * LC + (2 + kKsideWaves) * C + DK) * 4;
-};
-
 template <int DK, int DV, bool ABF16, int GATE>
-__global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
-    // eight waves; wave w owns the key column blocks w, w + 8, ... of every C x DK gradient
-    constexpr int NTH = kKsideThreads, NW = kKsideWaves, LK = KsideB<DK>::LK, NCB = DK / 16;
-    constexpr int CBW = (NCB + NW - 1) / NW;
+    using GT = GradTasks<DK>;
+    constexpr int NTH = kGradThreads, NW = kGradWaves, LK = GradB<DK>::LK;
+    constexpr int NB = GT::NB, RW = GT::RW, MSTEP = GT::MSTEP, KM = GT::KM;
+    constexpr int GC = C / 16, GK = DK / 16;
+    constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
     float* sKh = lds;                // Gamma.K; later db                       [C][LK]
     float* sKb = sKh + C * LK;       // K / Gamma                               [C][LK]
@@ -1155,7 +1088,12 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
     float* sT = sY + C * LC;         // T; later M                              [C][LC]
     float* sBeta = sT + C * LC;      // [C]
     float* sRow = sBeta + C;         // dbeta parts (A and Y), one row per wave [NW][C]
-    float* sCol = sRow + NW * C;     // column sums of Kt . dKt                  [DK]
+    float* sCol = sRow + NW * C;     // column sums of Kt . dKt, one row per wave sharing a column block [MSTEP][DK]
+    float* sDgam = sCol + MSTEP * DK;   // dgamma                               [DK]
+    float* sDbz = sDgam + DK;        // rowsum(dZ . V)                          [C]
+    float* sGs = sCol;               // scalar gate per row while b is formed  [C]
+    static_assert(C <= MSTEP * DK, "scalar gate rows fit the column-sum buffer");
+    static_assert(GradB<DK>::bytes <= 160 * 1024, "LDS of one CU");
 
     const int H = P.H;
     const int h = blockIdx.x % H, g = blockIdx.x / H;
@@ -1164,54 +1102,57 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
     const int64_t row0 = ent.y;
     const int len = ent.z;
     const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
-    const float* gB = rec_at(P, h, g, R::B);
+    for (int idx = tid; idx < NW * C; idx += NTH) sRow[idx] = 0.f;
 
+    // ---- value side (LDS before T is its scratch) ----
+    f4 acc[GT::KT];
+    if constexpr (ABF16) vside_phase16<DK, DV>(P, h, g, row0, len, lds, sT, sBeta, acc, sDgam, sDbz);
+    else vside_phase32<DK, DV>(P, h, g, row0, len, lds, sT, sBeta, acc, sDgam, sDbz);
+    __syncthreads();
+
+    // ---- key side ----
+    const int tnb = wave & 3, tmb0 = wave >> 2;     // C x C tiles: column block tnb, row blocks tmb0, tmb0 + 2
+    const int nb = wave % NB, cmb0 = wave / NB;     // C x d_k tiles: column block nb, row blocks cmb0 + r MSTEP
+    // dW -> sW; the gate, then b = cumsum(log2 alpha) as in the preparation
+    // kernel; Kh = 2^b K, Kb = 2^-b K
     {
         Tok<ABF16, DK, DK, NTH> tk;
-        Blk<C, C, NTH> bt;
-        Blk<C, DK, NTH> bw;
+        Tok<GBF16, DK, DK, NTH> tg0;
         tk.load(P.k, row0, len, h, H);
-        bt.load(rec_at(P, h, g, R::TT), C);
-        bw.load(rec_at(P, h, g, R::DW), DK);
+        if constexpr (GATE == KDA_GATE_SCALAR) {
+            if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+        } else {
+            tg0.load(P.gate, row0, len, h, H);
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) store_tile(sW + (cmb0 + r * MSTEP) * 16 * LK + nb * 16, LK, -acc[RW + r]);
         tk.put(sKh, LK);
-        bt.put(sT, LC);
-        bw.put(sW, LK);
+        if constexpr (GATE != KDA_GATE_SCALAR) tg0.put(sKb, LK);
     }
-    if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
-    for (int idx = tid; idx < NW * C; idx += NTH) sRow[idx] = 0.f;
-    load_block<C, DK, NTH>(sKb, LK, gB, DK);
     __syncthreads();
-    for (int idx = tid; idx < C * DK; idx += NTH) {
-        const int r = idx / DK, c = idx % DK;
-        const float b = sKb[r * LK + c], kv = sKh[r * LK + c];
+    gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sX, [&](int r, int c, float b) {
+        const float kv = sKh[r * LK + c];
         sKh[r * LK + c] = __builtin_amdgcn_exp2f(b) * kv;
         sKb[r * LK + c] = __builtin_amdgcn_exp2f(-b) * kv;
-    }
+    });
     __syncthreads();
 
-    // C x C products: wave w takes column block nb = w % 4 and row blocks
-    // w / 4 and w / 4 + 2 (two tiles sharing their column block)
-    constexpr int GC = C / 16, GK = DK / 16;
-    const int tnb = wave & 3, tmb0 = wave >> 2;
-    static_assert(NW == 8, "two C x C tiles per wave");
     // dT = (dW Kh^T + N) Diag(beta)
     {
-        f4 acc[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r) acc[r] = load_tile(rec_at(P, h, g, R::N) + (tmb0 + 2 * r) * 16 * C + tnb * 16, C);
+        f4 dt[2] = {acc[KM + 2], acc[KM + 3]};
         mm_rows<2, GK, true, true>(sW, LK, 1, sKh + tnb * 16 * LK, 1, LK, tmb0, 2,
-                                   [](int, int) { return true; }, acc);
+                                   [](int, int) { return true; }, dt);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, acc[r] * sBeta[tnb * 16 + i]);
+        for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, dt[r] * sBeta[tnb * 16 + i]);
     }
     __syncthreads();
     // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m)
     {
-        f4 acc[2] = {zero4(), zero4()};
+        f4 y1[2] = {zero4(), zero4()};
         mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, tmb0, 2,
-                                     [](int mb, int gg) { return gg >= mb; }, acc);
+                                     [](int mb, int gg) { return gg >= mb; }, y1);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) store_tile(sY + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, acc[r]);
+        for (int r = 0; r < 2; ++r) store_tile(sY + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
     }
     __syncthreads();
     // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX
@@ -1241,114 +1182,115 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
     }
     __syncthreads();
 
-    // Column-block products: wave w owns key column block nb = w and all four
-    // row blocks (independent accumulators sharing each B group).
     // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh)
-    f4 dKh[4], dQh[4], dKb[4];
+    f4 dKh[RW], dKb[RW];
+    {
+        f4 dy[RW];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) dKh[mb] = dQh[mb] = dKb[mb] = zero4();
-    const int nb = wave;
-    const bool own = nb < NCB;
-    static_assert(CBW == 1, "one key column block per wave");
-    if (own) {
-        f4 dy[4] = {zero4(), zero4(), zero4(), zero4()};
-        mm_rows<4, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, 0, 1,
-                                     [](int mb, int gg) { return gg >= mb; }, dy);
+        for (int r = 0; r < RW; ++r) dy[r] = dKb[r] = zero4();
+        mm_rows<RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+                                      [](int mb, int gg) { return gg >= mb; }, dy);
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int r = 0; r < RW; ++r) {
+            const int mb = cmb0 + r * MSTEP;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = mb * 16 + 4 * j + e, c = nb * 16 + i;
-                const float part = row16_sum(dy[mb][e] * sKh[r * LK + c]);
-                if (i == 0) sRow[wave * C + r] += part;
-                dKh[mb][e] = sBeta[r] * dy[mb][e];
+                const int row = mb * 16 + 4 * j + e, c = nb * 16 + i;
+                const float part = row16_sum(dy[r][e] * sKh[row * LK + c]);
+                if (i == 0) sRow[wave * C + row] += part;
+                dKh[r][e] = sBeta[row] * dy[r][e];
             }
         }
         // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
-        mm_rows<4, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, 0, 1,
-                                    [](int mb, int gg) { return gg <= mb; }, dKh);
+        mm_rows<RW, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
+                                     [](int mb, int gg) { return gg <= mb; }, dKh);
     }
     __syncthreads();
-    load_block<C, C, NTH>(sT, LC, rec_at(P, h, g, R::M), C);
+    // M -> sT (tiles above the diagonal were never accumulated), Qh -> sW
+#pragma unroll
+    for (int r2 = 0; r2 < 2; ++r2) {
+        const int mb = tmb0 + 2 * r2;
+        f4 x = acc[KM + r2];
+        if (tnb == mb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
+        }
+        store_tile(sT + mb * 16 * LC + tnb * 16, LC, x);
+    }
     load_block<C, DK, NTH>(sW, LK, rec_at(P, h, g, R::QH), DK);
     __syncthreads();
 
     // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
-    if (own) {
+    f4 dQh[RW];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) dQh[mb] = load_tile(rec_at(P, h, g, R::DQH) + mb * 16 * DK + nb * 16, DK);
-        mm_rows<4, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, 0, 1,
-                                    [](int mb, int gg) { return gg <= mb; }, dQh);
-        mm_rows<4, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, 0, 1,
-                                     [](int mb, int gg) { return gg >= mb; }, dKb);
-        mm_rows<4, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, 0, 1,
-                                     [](int mb, int gg) { return gg >= mb; }, dKb);
-    }
+    for (int r = 0; r < RW; ++r) dQh[r] = acc[r];
+    mm_rows<RW, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
+                                 [](int mb, int gg) { return gg <= mb; }, dQh);
+    mm_rows<RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+                                  [](int mb, int gg) { return gg >= mb; }, dKb);
+    mm_rows<RW, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, cmb0, MSTEP,
+                                  [](int mb, int gg) { return gg >= mb; }, dKb);
     __syncthreads();
 
     // gate chain rule, dq, dk.  Every operand is staged in LDS first (the
     // regions are free now), so no load waits behind a store of dq or dk:
-    // q -> sKh, k -> sKb, b -> sW, dKt -> sX (sX and sY are contiguous).
+    // q -> sKh, k -> sKb, the gate -> sW (b after the scan); dKt is the
+    // value-side accumulator of the same tile.
     const float* gGam = rec_at(P, h, g, R::GAM);
-    const float* gDkt = rec_at(P, h, g, R::DKT);
-    const float* gDgam = rec_at(P, h, g, R::DGAM);
-    float* sD = sX;                          // dKt, row stride LK
-    static_assert(C * LK <= 2 * C * LC, "dKt staging spans the sX and sY regions");
     constexpr int NS = NTH / DK, SEG = C / NS;   // reverse-cumsum split: NS row segments per channel
-    float gam_u[CBW];
-    Tok<GATE == KDA_GATE_SOFTPLUS_BF16, DK, DK, NTH> tg;
+    Tok<GBF16, DK, DK, NTH> tg;
     float gs = 1.f;
-    float gam_t = 0.f, dgam_t = 0.f;
+    float gam_c, gam_t, dgam_t;
     {
         Tok<ABF16, DK, DK, NTH> tq, tk;
-        Blk<C, DK, NTH> bb, bd;
         tq.load(P.q, row0, len, h, H);
         tk.load(P.k, row0, len, h, H);
-        bb.load(gB, DK);
-        bd.load(gDkt, DK);
         if constexpr (GATE == KDA_GATE_SCALAR) {
             if (tid < C && tid < len) gs = static_cast<const float*>(P.gate)[(row0 + tid) * H + h];
         } else {
             tg.load(P.gate, row0, len, h, H);
         }
-#pragma unroll
-        for (int u = 0; u < CBW; ++u) gam_u[u] = gGam[((wave + NW * u) % NCB) * 16 + i];
+        gam_c = gGam[nb * 16 + i];
         gam_t = gGam[tid % DK];
-        dgam_t = gDgam[tid % DK];
+        dgam_t = sDgam[tid % DK];
         tq.put(sKh, LK);
         tk.put(sKb, LK);
-        bb.put(sW, LK);
-        bd.put(sD, LK);
+        if constexpr (GATE == KDA_GATE_SCALAR) {
+            if (tid < C) sGs[tid] = tid < len ? gs : 1.f;
+        } else {
+            tg.put(sW, LK);
+        }
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < CBW; ++u) {
-        const int nb = wave + NW * u, c = nb * 16 + i;
-        if (nb >= NCB) continue;
-        const float gam = gam_u[u];
+    // b again (the same scan, so the same values as above) -> sW
+    gate_cumsum<DK, NTH, GATE>(sW, LK, sGs, len, sT, [&](int r, int c, float b) { sW[r * LK + c] = b; });
+    __syncthreads();
+    {
+        const int c = nb * 16 + i;
         float col = 0.f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+        for (int r = 0; r < RW; ++r) {
+            const int mb = cmb0 + r * MSTEP;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = mb * 16 + 4 * j + e;
-                const float b = sW[r * LK + c];
+                const int row = mb * 16 + 4 * j + e;
+                const float b = sW[row * LK + c];
                 const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-                const float qv = sKh[r * LK + c], kv = sKb[r * LK + c], dkt = sD[r * LK + c];
-                const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam * kb;
-                const float dqh = dQh[mb][e], dkh = dKh[mb][e], dkb = dKb[mb][e];
-                if (r < len) {
-                    const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
+                const float qv = sKh[row * LK + c], kv = sKb[row * LK + c], dkt = acc[2 * RW + r][e];
+                const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam_c * kb;
+                const float dqh = dQh[r][e], dkh = dKh[r][e], dkb = dKb[r][e];
+                if (row < len) {
+                    const size_t ai = (static_cast<size_t>(row0 + row) * H + h) * DK + c;
                     store_out<ABF16>(P.dq, ai, G * dqh);
-                    store_out<ABF16>(P.dk, ai, G * dkh + Gi * dkb + gam * Gi * dkt);
+                    store_out<ABF16>(P.dk, ai, G * dkh + Gi * dkb + gam_c * Gi * dkt);
                 }
-                sKh[r * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;   // db
+                sKh[row * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;   // db
                 col += kt * dkt;
             }
         }
         col += __shfl_xor(col, 16, 64);
         col += __shfl_xor(col, 32, 64);
-        if (j == 0) sCol[c] = col;
+        if (j == 0) sCol[cmb0 * DK + c] = col;
     }
     __syncthreads();
     // the gate as given (b is no longer needed); partial sums of db per segment
@@ -1370,21 +1312,23 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
     // gradient and the Kt terms enter at the last row
     {
         const int c = tid % DK, sg = tid / DK;
-        float acc = gam_t * dgam_t + sCol[c];
-        for (int s2 = sg + 1; s2 < NS; ++s2) acc += sPart[s2 * DK + c];
+        float acc2 = gam_t * dgam_t;
+#pragma unroll
+        for (int z = 0; z < MSTEP; ++z) acc2 += sCol[z * DK + c];
+        for (int s2 = sg + 1; s2 < NS; ++s2) acc2 += sPart[s2 * DK + c];
         for (int r = sg * SEG + SEG - 1; r >= sg * SEG; --r) {
-            acc += sKh[r * LK + c];
+            acc2 += sKh[r * LK + c];
             if (r < len) {
                 const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
                 if constexpr (GATE == KDA_GATE_ALPHA) {
-                    P.dgate[ai] = acc / sW[r * LK + c];
+                    P.dgate[ai] = acc2 / sW[r * LK + c];
                 } else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
                     // log alpha = -softplus(x): d/dx = -sigmoid(x)
                     const float x = sW[r * LK + c];
                     const float sgm = 1.f / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
-                    P.dgate[ai] = -acc * sgm;
+                    P.dgate[ai] = -acc2 * sgm;
                 } else {
-                    sKb[r * LK + c] = acc;
+                    sKb[r * LK + c] = acc2;
                 }
             }
         }
@@ -1401,7 +1345,7 @@ __global__ __launch_bounds__(kKsideThreads) void bwd_kside_kernel(const BwdParam
         float db = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) db += sRow[w * C + tid];
-        P.dbeta[(row0 + tid) * H + h] = rec_at(P, h, g, R::DBZ)[tid] + db;
+        P.dbeta[(row0 + tid) * H + h] = sDbz[tid] + db;
     }
 }
 
@@ -1457,15 +1401,10 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chunk_blocks > 0) {
-        auto k4 = ABF16 ? bwd_vside16_kernel<DK, DV, true> : bwd_vside_kernel<DK, DV, ABF16>;
-        constexpr int l4 = ABF16 ? Vside16B<DK, DV>::bytes : VsideB<DK>::bytes;
+        auto k4 = bwd_grad_kernel<DK, DV, ABF16, GATE>;
+        constexpr int l4 = GradB<DK>::bytes;
         if ((e = set_lds(k4, l4)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k4, dim3(chunk_blocks), dim3(512), l4, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        auto k5 = bwd_kside_kernel<DK, DV, ABF16, GATE>;
-        constexpr int l5 = KsideB<DK>::bytes;
-        if ((e = set_lds(k5, l5)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k5, dim3(chunk_blocks), dim3(kKsideThreads), l5, stream, p);
+        hipLaunchKernelGGL(k4, dim3(chunk_blocks), dim3(kGradThreads), l4, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
