@@ -549,19 +549,25 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev_kernel(const BwdParams 
 // ---------------------------------------------------------------------------
 template <int DK> struct Chain16B {
     static constexpr int KPD = DK + 8, KPC = C + 8;      // column-major tile strides (halves)
-    static constexpr int bytes = (2 * 16 * KPC + 16 * KPD) * 2 + DK * 4;
+    static constexpr int sink = (3 * 16 * KPC + 16 * KPD) * 2;   // byte offset of the prefetch sink
+    static constexpr int bytes = sink + 64 * 4;
 };
+// Eight compute waves and one wave that brings the records (and dO rows) of
+// the chunk kChainPrefetch steps ahead of the chain into the XCD's L2; the
+// compute waves load each chunk's operands one step ahead.  The prefetch
+// wave passes the same two barriers per chunk, bare (a fenced barrier would
+// wait for its loads).
+constexpr int kChain16Threads = kChainThreads + 64, kChainPrefetch = 3;
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
     constexpr int NT = DV / 16, NRB = DK / 16;
     constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
     extern __shared__ float lds[];
-    _Float16* sdO = reinterpret_cast<_Float16*>(lds);    // dO tile, column-major  [16][KPC]
-    _Float16* sdU = sdO + 16 * KPC;                      // dU'                   [16][KPC]
+    _Float16* sdO2 = reinterpret_cast<_Float16*>(lds);   // dO tile, column-major, by chunk parity  [2][16][KPC]
+    _Float16* sdU = sdO2 + 2 * 16 * KPC;                 // dU'                   [16][KPC]
     _Float16* sdS = sdU + 16 * KPC;                      // dS                    [16][KPD]
-    float* sGam = reinterpret_cast<float*>(sdS + 16 * KPD);   // [DK]
 
     int tile, pair;
     chain_coords<NT>(tile, pair);
@@ -569,7 +575,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
     const int H = P.H;
     const int n = P.order[pair / H], h = pair % H;
     const int g0 = P.first[n], g1 = P.first[n + 1];
-    const int wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
+    const int wave = wave_id(), lane = lane_id(), j = lane >> 4;
     const int c0 = tile * 16;
     const bool du = wave < 4, hasrb = wave < NRB;
     const int mb = wave & 3, rb = wave;
@@ -582,14 +588,45 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
     auto hrec_w = [&](int g, size_t off) {
         return reinterpret_cast<_Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
-    // the next (earlier) chunk's operands
+    // The next (earlier) chunk's operands, loaded while the current chunk
+    // computes.  A sequence's chunks are consecutive rows of C tokens, so the
+    // dO rows of chunk g follow from the sequence's first row and last
+    // length (no per-chunk table load for a prefetch to wait on).
     h8 nKt[NKD], nPt[NKC], nQt[NKC], nWt[NKC];
     u16x4 ndO = {0, 0, 0, 0};
     int ndO_len = 0;
-    float nGam = 0.f;
+    f4 nGam = zero4();
+    const int row_first = g1 > g0 ? P.table[g0].y : 0;
+    const int len_last = g1 > g0 ? P.table[g1 - 1].z : 0;
+    if (wave == kChainWaves) {
+        int* sink = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(lds) + Chain16B<DK>::sink);
+        auto touch = [&](int gp) {
+            l2_touch(hrec(gp, R::FKT), C * DK * 2, tile, NT, sink);
+            l2_touch(hrec(gp, R::FPT), C * C * 2, tile, NT, sink);
+            l2_touch(hrec(gp, R::FQHT), C * DK * 2, tile, NT, sink);
+            l2_touch(hrec(gp, R::FWT), C * DK * 2, tile, NT, sink);
+            l2_touch(rec_at(P, h, gp, R::GAM), DK * 4, tile, NT, sink);
+            const int len = gp == g1 - 1 ? len_last : C;
+            if (lane < len) {
+                const size_t row = static_cast<size_t>(row_first) + (gp - g0) * C + lane;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(static_cast<const uint16_t*>(P.dout) +
+                                                                    (row * H + h) * DV + c0),
+                    (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
+            }
+        };
+        for (int gp = g1 - 2; gp >= max(g1 - kChainPrefetch, g0); --gp) touch(gp);
+        for (int g = g1 - 1; g >= g0; --g) {
+            if (g - kChainPrefetch >= g0) touch(g - kChainPrefetch);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);       // every load has landed before the wave ends
+        return;
+    }
     const int dr = threadIdx.x >> 2, dc = 4 * (threadIdx.x & 3);      // dO element rows / columns of this thread
     auto fetch = [&](int g) {
-        const int4 ent = P.table[g];
+        const int row0 = row_first + (g - g0) * C, len = g == g1 - 1 ? len_last : C;
         if (du) {
 #pragma unroll
             for (int kb = 0; kb < NKD; ++kb) nKt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKT) + afrag_off(mb, kb, NKD, lane));
@@ -602,17 +639,18 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
                 nQt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FQHT) + afrag_off(rb, kb, NKC, lane));
                 nWt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FWT) + afrag_off(rb, kb, NKC, lane));
             }
+            nGam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
         }
         if (dr < C) {
-            const int rr = dr < ent.z ? dr : ent.z - 1;
+            const int rr = dr < len ? dr : len - 1;
             ndO = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(P.dout) +
-                                                  (static_cast<size_t>(ent.y + rr) * H + h) * DV + c0 + dc);
+                                                  (static_cast<size_t>(row0 + rr) * H + h) * DV + c0 + dc);
         }
-        ndO_len = ent.z;
-        if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
+        ndO_len = len;
     };
     if (g1 > g0) fetch(g1 - 1);
     for (int g = g1 - 1; g >= g0; --g) {
+        _Float16* sdO = sdO2 + (g & 1) * 16 * KPC;
         h8 Kt[NKD], Pt[NKC], Qt[NKC], Wt[NKC];
 #pragma unroll
         for (int kb = 0; kb < NKD; ++kb) Kt[kb] = nKt[kb];
@@ -622,12 +660,12 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
             Qt[kb] = nQt[kb];
             Wt[kb] = nWt[kb];
         }
+        const f4 gam = nGam;
         if (dr < C) {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 sdO[(dc + e) * KPC + dr] = static_cast<_Float16>(dr < ndO_len ? bf16_to_f32(ndO[e]) : 0.f);
         }
-        if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
         if (hasrb) {
             put_btile(sdS, KPD, rb * 16, dS);
             store_tile16(hrec_w(g, R::DSO) + rb * 16 * DV + c0, DV, dS);
@@ -646,11 +684,11 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
             store_tile16(hrec_w(g, R::DUC) + mb * 16 * DV + c0, DV, acc);
         }
         __syncthreads();
-        // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'
+        // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'.  No barrier after: the next
+        // chunk writes dS and its own dO buffer before its first barrier, and
+        // dU' after it.
         if (hasrb) {
-            f4 x = dS, y = zero4();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] *= sGam[rb * 16 + 4 * j + e];
+            f4 x = dS * gam, y = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) {
                 x = mfma16(Qt[kb], bfrag(sdO, KPC, kb), x);
@@ -658,21 +696,18 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev16_kernel(const BwdParam
             }
             dS = x - y;
         }
-        __syncthreads();
     }
-    (void)i;
     if (P.dinitial_state && hasrb) store_tile(P.dinitial_state + sbase + rb * 16 * DV + c0, DV, dS);
 }
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdParams P) {
     using R = BRec<DK, DV>;
     constexpr int NT = DV / 16, NRB = DK / 16;
     constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
     extern __shared__ float lds[];
     _Float16* sU = reinterpret_cast<_Float16*>(lds);     // U', column-major        [16][KPC]
     _Float16* sS = sU + 2 * 16 * KPC;                    // S                       [16][KPD]
-    float* sGam = reinterpret_cast<float*>(sS + 16 * KPD);   // [DK]
 
     int tile, pair;
     chain_coords<NT>(tile, pair);
@@ -693,9 +728,25 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
     auto hrec_w = [&](int g, size_t off) {
         return reinterpret_cast<_Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
+    if (wave == kChainWaves) {
+        int* sink = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(lds) + Chain16B<DK>::sink);
+        auto touch = [&](int gp) {
+            l2_touch(hrec(gp, R::FW), C * DK * 2, tile, NT, sink);
+            l2_touch(hrec(gp, R::FKTT), C * DK * 2, tile, NT, sink);
+            l2_touch(rec_at(P, h, gp, R::U), C * DV * 4, tile, NT, sink);
+            l2_touch(rec_at(P, h, gp, R::GAM), DK * 4, tile, NT, sink);
+        };
+        for (int gp = g0 + 1; gp < min(g0 + kChainPrefetch, g1); ++gp) touch(gp);
+        for (int g = g0; g < g1; ++g) {
+            if (g + kChainPrefetch < g1) touch(g + kChainPrefetch);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);       // every load has landed before the wave ends
+        return;
+    }
     h8 nW[NKD], nKtt[NKC];
-    f4 nU = zero4();
-    float nGam = 0.f;
+    f4 nU = zero4(), nGam = zero4();
     auto fetch = [&](int g) {
         if (du) {
 #pragma unroll
@@ -706,8 +757,8 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
                 nKtt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKTT) + afrag_off(rb, kb, NKC, lane));
+            nGam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
         }
-        if (threadIdx.x < DK) nGam = rec_at(P, h, g, R::GAM)[threadIdx.x];
     };
     if (g0 < g1) fetch(g0);
     for (int g = g0; g < g1; ++g) {
@@ -716,8 +767,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
         for (int kb = 0; kb < NKD; ++kb) Wf[kb] = nW[kb];
 #pragma unroll
         for (int kb = 0; kb < NKC; ++kb) Ktt[kb] = nKtt[kb];
-        const f4 uu = nU;
-        if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
+        const f4 uu = nU, gam = nGam;
         if (hasrb) {
             put_btile(sS, KPD, rb * 16, S);
             store_tile16(hrec_w(g, R::SIN) + rb * 16 * DV + c0, DV, S);
@@ -734,16 +784,15 @@ __global__ __launch_bounds__(kChainThreads) void bwd_ckpt16_kernel(const BwdPara
             store_tile16(hrec_w(g, R::UC) + mb * 16 * DV + c0, DV, uc);
         }
         __syncthreads();
-        // S <- Diag(gamma) S + Kt^T U'
+        // S <- Diag(gamma) S + Kt^T U'.  No barrier after: the next chunk
+        // writes S before its first barrier (every read of S is before this
+        // chunk's second one) and U' after it.
         if (hasrb) {
-            f4 sv = S;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sv[e] *= sGam[rb * 16 + 4 * j + e];
+            f4 sv = S * gam;
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb) sv = mfma16(Ktt[kb], bfrag(sU, KPC, kb), sv);
             S = sv;
         }
-        __syncthreads();
     }
 }
 
@@ -1390,14 +1439,14 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         auto k2 = ABF16 ? bwd_ckpt16_kernel<DK, DV> : bwd_ckpt_kernel<DK, DV>;
         constexpr int l2 = ABF16 ? Chain16B<DK>::bytes : CkptB<DK>::bytes;
         if ((e = set_lds(k2, l2)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(kChainThreads), l2, stream, p);
+        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(ABF16 ? kChain16Threads : kChainThreads), l2, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chain_blocks > 0) {
         auto k3 = ABF16 ? bwd_rev16_kernel<DK, DV> : bwd_rev_kernel<DK, DV, ABF16>;
         constexpr int l3 = ABF16 ? Chain16B<DK>::bytes : RevB<DK>::bytes;
         if ((e = set_lds(k3, l3)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k3, dim3(chain_blocks), dim3(kChainThreads), l3, stream, p);
+        hipLaunchKernelGGL(k3, dim3(chain_blocks), dim3(ABF16 ? kChain16Threads : kChainThreads), l3, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chunk_blocks > 0) {

@@ -255,6 +255,19 @@ __device__ __forceinline__ void chain_coords(int& tile, int& pair) {
 }
 
 
+// L2 prefetch by one wave: one word of every 128-byte line of
+// [base, base + bytes) whose line index is part (mod parts) goes to an LDS
+// sink of 64 words that nothing reads.  Only the issuing wave's counters see
+// these loads, so a wave that does nothing else never waits for them.
+__device__ __forceinline__ void l2_touch(const void* base, int bytes, int part, int parts, int* sink) {
+    const int lines = bytes >> 7;
+    const unsigned char* b = static_cast<const unsigned char*>(base);
+    for (int line = part + parts * lane_id(); line < lines; line += parts * 64)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(b + (static_cast<size_t>(line) << 7)),
+            (__attribute__((address_space(3))) void*)sink, 4, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // fp16 matrix-core operands (v_mfma_f32_16x16x32_f16) for the 16-bit paths.
 //   A lane l holds A[l % 16][32 kb + 8 (l / 16) + e], e = 0..7
