@@ -58,13 +58,30 @@ def fwd_flops_per_token_head(C=64, dk=128, dv=128):
 BWD_BYTES_PER_TOKEN_HEAD = 4 * 2 * 128 + 128 * 4 + 4 + 3 * 2 * 128 + 128 * 4 + 4
 
 
-def bwd_flops_per_token_head(C=64, dk=128, dv=128):
+def bwd_flops_split(C=64, dk=128, dv=128):
     """Useful flops (2 x multiply-adds, triangular products at half) per
-    token-head of the chunkwise backward with the forward recomputed:
-    8 C dk dv (two state-chain passes, the value-side contractions) +
-    5.5 C^2 dk + 3 C^2 dv + 7/6 C^3 per chunk, divided by C."""
-    macs = 8 * dk * dv + 5.5 * C * dk + 3 * C * dv + (7.0 / 6.0) * C * C
-    return 2 * macs
+    token-head of the chunkwise backward with the forward recomputed, split by
+    the matrix cores that run them with 16-bit activations:
+      fp16  the two state-chain passes and the value-side contractions:
+            8 dk dv + 2.5 C dv per token (W S, Kt^T U', Kt dS, Qh^T dO, W^T dU',
+            dO S^T, dU' S^T, U' dS^T; P^T dO, M, N, T^T dU')
+      fp32  preparation and key side: 5.5 C dk + 0.5 C dv + 7/6 C^2 per token
+            (A, P, W, U, T; dT, R, dY, dKh, dQh, dKb; Y1, dA).
+    With fp32 activations every product runs on the fp32 matrix cores."""
+    f16 = 2 * (8 * dk * dv + 2.5 * C * dv)
+    f32 = 2 * (5.5 * C * dk + 0.5 * C * dv + (7.0 / 6.0) * C * C)
+    return f16, f32
+
+
+def bwd_flops_per_token_head(C=64, dk=128, dv=128):
+    return sum(bwd_flops_split(C, dk, dv))
+
+
+def bwd_mixed_peak(C=64, dk=128, dv=128):
+    """Matrix-core roofline of the 16-bit backward: its useful flops over the
+    time they take at the fp16 and fp32 peaks (each part at its own peak)."""
+    f16, f32 = bwd_flops_split(C, dk, dv)
+    return (f16 + f32) / (f16 / BF16_MFMA_PEAK_TFLOPS + f32 / FP32_MFMA_PEAK_TFLOPS)
 
 
 # bytes of the forget gate per token-head, by form (gate= argument)
@@ -194,15 +211,20 @@ def bench_bwd(kda, synth, torch, fi, wf, reps, warm):
     out = run()
     ms = time_events(run, reps, warm)
     units = B * H * T
-    fl = bwd_flops_per_token_head(64, Dk, Dv) * units
+    f16, f32 = bwd_flops_split(64, Dk, Dv)
+    fl = (f16 + f32) * units
+    peak = bwd_mixed_peak(64, Dk, Dv)
     tf = fl / (ms / 1e3) / 1e12
     byts = BWD_BYTES_PER_TOKEN_HEAD * units + 3 * B * H * Dk * Dv * 4
     del ws, out
     return {"value": round(units / (ms / 1e3), 1), "unit": "token-heads/s", "bwd_ms": round(ms, 3),
             "workspace_GiB": round(nb / 2 ** 30, 2),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
-                         "dtype": "f32 (every product on the fp32 matrix cores)",
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": round(peak, 1),
+                         "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                         "dtype": "mixed: state passes and value side on the fp16 matrix cores "
+                                  f"({f16 / (f16 + f32):.0%} of the flops, peak {BF16_MFMA_PEAK_TFLOPS:g}), "
+                                  f"preparation and key side on fp32 (peak {FP32_MFMA_PEAK_TFLOPS:g}); "
+                                  "peak = useful flops / their time with each part at its own peak",
                          "useful_flops_per_launch": round(fl)},
             "hbm_algorithmic": {"bytes_per_launch": byts,
                                 "GBps": round(byts / (ms / 1e3) / 1e9, 1)},

@@ -44,6 +44,8 @@
 // decay precondition of the forward (per channel, < e^10 over any 8 tokens,
 // so < e^80 over a chunk) Gamma = 2^b and 1/Gamma stay fp32-normal over a
 // chunk, so Kh = Gamma.K and Kb = K/Gamma are formed directly.
+#include <type_traits>
+
 #include "kda_chunk.h"
 #include "kda_common.h"
 #include "kda_mm32.h"
@@ -57,33 +59,36 @@ constexpr int C = kChunk;
 constexpr int LC = C + 4;          // LDS row stride of C x C fp32 tiles
 
 // ---------------------------------------------------------------------------
-// Per-(head, chunk) fp32 record of the backward (byte offsets).  Rows are
+// Per-(head, chunk) record of the backward (byte offsets).  Rows are
 // chunk-local tokens; the tail of a partial chunk holds zeros (Qh, Kt, W, U,
-// P, dU', ...) or the last valid row's b.
+// P, dU', ...).  With 16-bit activations (F16) the state passes read their A
+// operands as fp16 fragments, so the fp32 Kt, W and P are absent, and S,
+// dS_next, U' and dU' are stored in fp16; with fp32 activations the fragments
+// are absent.
 // ---------------------------------------------------------------------------
-template <int DK, int DV> struct BRec {
+template <int DK, int DV, bool F16> struct BRec {
     static constexpr size_t CK = size_t(C) * DK * 4, CV = size_t(C) * DV * 4, CC = size_t(C) * C * 4;
-    static constexpr size_t KV = size_t(DK) * DV * 4;
+    static constexpr size_t SE = F16 ? 2 : 4;    // bytes per element of S, dS_next, U', dU'
     static constexpr size_t QH = 0;              // Gamma . Q                 [C][DK]
-    static constexpr size_t KT = QH + CK;        // (gamma / Gamma) . K       [C][DK]
-    static constexpr size_t W = KT + CK;         // T Diag(beta) (Gamma . K)  [C][DK]
-    static constexpr size_t U = W + CK;          // T Diag(beta) V            [C][DV]
-    static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]
-    static constexpr size_t TT = P + CC;         // (I + A)^-1                [C][C]
+    static constexpr size_t KT = QH + CK;        // (gamma / Gamma) . K       [C][DK]  (fp32 path)
+    static constexpr size_t W = KT + (F16 ? 0 : CK);   // T Diag(beta) (Gamma . K)  [C][DK]  (fp32 path)
+    static constexpr size_t U = W + (F16 ? 0 : CK);    // T Diag(beta) V            [C][DV]
+    static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]   (fp32 path)
+    static constexpr size_t TT = P + (F16 ? 0 : CC);   // (I + A)^-1                [C][C]
     static constexpr size_t GAM = TT + CC;       // gamma                     [DK]
-    static constexpr size_t SIN = GAM + size_t(DK) * 4;   // state entering  [DK][DV]
-    static constexpr size_t DSO = SIN + KV;      // dL/d(state leaving)       [DK][DV]
-    static constexpr size_t UC = DSO + KV;       // U' = U - W S              [C][DV]
-    static constexpr size_t DUC = UC + CV;       // dL/dU'                    [C][DV]
-    // fp16 A fragments of the state passes' products (16-bit activations only)
-    static constexpr size_t HK = size_t(C) * DK * 2;
-    static constexpr size_t FKT = DUC + CV;               // Kt                [C][DK]
+    static constexpr size_t SIN = GAM + size_t(DK) * 4;       // state entering   [DK][DV]
+    static constexpr size_t DSO = SIN + size_t(DK) * DV * SE; // dL/d(state leaving) [DK][DV]
+    static constexpr size_t UC = DSO + size_t(DK) * DV * SE;  // U' = U - W S      [C][DV]
+    static constexpr size_t DUC = UC + size_t(C) * DV * SE;   // dL/dU'            [C][DV]
+    // fp16 A fragments of the state passes' products (16-bit path)
+    static constexpr size_t HK = F16 ? size_t(C) * DK * 2 : 0;
+    static constexpr size_t FKT = DUC + size_t(C) * DV * SE;  // Kt                [C][DK]
     static constexpr size_t FKTT = FKT + HK;              // Kt^T              [DK][C]
     static constexpr size_t FQHT = FKTT + HK;             // Qh^T              [DK][C]
     static constexpr size_t FW = FQHT + HK;               // W                 [C][DK]
     static constexpr size_t FWT = FW + HK;                // W^T               [DK][C]
     static constexpr size_t FPT = FWT + HK;               // P^T               [C][C]
-    static constexpr size_t END = FPT + size_t(C) * C * 2;
+    static constexpr size_t END = FPT + (F16 ? size_t(C) * C * 2 : 0);
 };
 
 struct BwdParams {
@@ -159,7 +164,7 @@ template <int DK, int DV> struct PrepB {
 
 template <int DK, int DV, bool ABF16, int GATE>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams P) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, ABF16>;
     constexpr int NTH = kPrepThreads, NW = kPrepWaves;
     constexpr int LK = PrepB<DK, DV>::LK, LV = PrepB<DK, DV>::LV;
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
@@ -353,7 +358,7 @@ template <int DK> struct CkptB {
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kChainThreads) void bwd_ckpt_kernel(const BwdParams P) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, false>;
     constexpr int NTH = kChainThreads, NW = kChainWaves;
     constexpr int LK = CkptB<DK>::LK, NT = DV / 16, NRB = DK / 16, RBW = (NRB + NW - 1) / NW;
     extern __shared__ float lds[];
@@ -437,7 +442,7 @@ template <int DK> struct RevB {
 // chunks last to first
 template <int DK, int DV, bool ABF16>
 __global__ __launch_bounds__(kChainThreads) void bwd_rev_kernel(const BwdParams P) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, false>;
     constexpr int NTH = kChainThreads, NW = kChainWaves;
     constexpr int LK = RevB<DK>::LK, NT = DV / 16, NRB = DK / 16, RBW = (NRB + NW - 1) / NW;
     extern __shared__ float lds[];
@@ -557,11 +562,14 @@ template <int DK> struct Chain16B {
 // compute waves load each chunk's operands one step ahead.  The prefetch
 // wave passes the same two barriers per chunk, bare (a fenced barrier would
 // wait for its loads).
-constexpr int kChain16Threads = kChainThreads + 64, kChainPrefetch = 3;
+#ifndef KDA_CHAIN_PREFETCH
+#define KDA_CHAIN_PREFETCH 3
+#endif
+constexpr int kChain16Threads = kChainThreads + 64, kChainPrefetch = KDA_CHAIN_PREFETCH;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdParams P) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, true>;
     constexpr int NT = DV / 16, NRB = DK / 16;
     constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
     extern __shared__ float lds[];
@@ -702,7 +710,7 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdParams P) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, true>;
     constexpr int NT = DV / 16, NRB = DK / 16;
     constexpr int KPD = Chain16B<DK>::KPD, KPC = Chain16B<DK>::KPC, NKD = DK / 32, NKC = C / 32;
     extern __shared__ float lds[];
@@ -867,7 +875,7 @@ template <int DK, int DV>
 __device__ __forceinline__ void vside_phase32(const BwdParams& P, int h, int g, int64_t row0, int len, float* region,
                                               float* sT, float* sBeta, f4 (&acc)[GradTasks<DK>::KT],
                                               float* sDgam, float* sDbz) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, false>;
     using GT = GradTasks<DK>;
     constexpr int NTH = kGradThreads, NB = GT::NB, KT = GT::KT;
     static_assert((2 * DK * kLS + 4 * C * kLS + 2 * C) * 4 <= GradB<DK>::region, "value-side scratch fits");
@@ -957,7 +965,7 @@ template <int DK, int DV>
 __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, int64_t row0, int len, float* region,
                                               float* sT, float* sBeta, f4 (&acc)[GradTasks<DK>::KT],
                                               float* sDgam, float* sDbz) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, true>;
     using VB = V16L<DK, DV>;
     using GT = GradTasks<DK>;
     constexpr int NTH = kGradThreads, SW = VB::SW, RS = VB::RS, CS = VB::CS, NZB = VB::NZB, NKS = SW / 32;
@@ -1122,7 +1130,7 @@ __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, 
 
 template <int DK, int DV, bool ABF16, int GATE>
 __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams P) {
-    using R = BRec<DK, DV>;
+    using R = BRec<DK, DV, ABF16>;
     using GT = GradTasks<DK>;
     constexpr int NTH = kGradThreads, NW = kGradWaves, LK = GradB<DK>::LK;
     constexpr int NB = GT::NB, RW = GT::RW, MSTEP = GT::MSTEP, KM = GT::KM;
@@ -1409,7 +1417,7 @@ template <int DK, int DV, bool ABF16, int GATE>
 hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipStream_t stream) {
     const ChunkPlan& pl = bp.fwd;
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-    if (BRec<DK, DV>::END > bp.rec_bytes) return hipErrorInvalidValue;
+    if (BRec<DK, DV, ABF16>::END > bp.rec_bytes) return hipErrorInvalidValue;
     BwdParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.dout = a.dout; p.beta = a.beta;
     p.initial_state = a.initial_state; p.dfinal_state = a.dfinal_state;
@@ -1480,12 +1488,15 @@ kda_status make_chunk_bwd_plan(int B, int64_t T, int H, int Dk, int Dv, bool var
     ChunkBwdPlan bp;
     const kda_status st = make_chunk_plan(B, T, H, Dk, Dv, varlen, num_seqs, chunk_size, act_bf16, &bp.fwd);
     if (st != KDA_SUCCESS) return st;
-    // the forward's records are not used: the backward keeps its own fp32 record
-    size_t end = 0;
-    if (Dk == 128 && Dv == 128) end = BRec<128, 128>::END;
-    else if (Dk == 64 && Dv == 64) end = BRec<64, 64>::END;
-    else if (Dk == 128 && Dv == 64) end = BRec<128, 64>::END;
-    else end = BRec<64, 128>::END;
+    // the forward's records are not used: the backward keeps its own record
+    auto rec_end = [&](auto f16) -> size_t {
+        constexpr bool F = decltype(f16)::value;
+        if (Dk == 128 && Dv == 128) return BRec<128, 128, F>::END;
+        if (Dk == 64 && Dv == 64) return BRec<64, 64, F>::END;
+        if (Dk == 128 && Dv == 64) return BRec<128, 64, F>::END;
+        return BRec<64, 128, F>::END;
+    };
+    const size_t end = act_bf16 ? rec_end(std::true_type{}) : rec_end(std::false_type{});
     bp.rec_bytes = align256(end);
     bp.off_rec = bp.fwd.off_rec;
     bp.workspace_bytes = align256(bp.off_rec + static_cast<size_t>(bp.fwd.gmax) * H * bp.rec_bytes);
