@@ -68,7 +68,7 @@ hipError_t launch_chunk_fwd_generic(const ChunkPlan& plan, const ChunkArgs& args
 hipError_t launch_chunk_plan(const ChunkPlan& plan, const int32_t* cu_seqlens, void* workspace,
                              hipStream_t stream);
 
-// Backward: the forward's chunk table followed by one fp32 record per
+// Backward: the forward's chunk table followed by one record per
 // (head, chunk), at index h * gmax + g (layout in kda_chunk_bwd.hip).
 struct ChunkBwdPlan {
     ChunkPlan fwd;                // sizes and chunk-table offsets (its records are unused)

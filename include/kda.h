@@ -181,7 +181,9 @@ KDA_API kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void 
  * arguments as kda_chunk_fwd_workspace_bytes).  Returns 0 for argument
  * combinations kda_chunk_bwd would reject.  256-byte alignment; contents
  * need not be initialised; not to be shared by calls that may overlap.
- * About (7 C d_k + 4 C d_v + 2 d_k d_v + 4 C^2) * 4 bytes per (chunk, head).
+ * Per (chunk, head), with C = chunk_size: (3 C d_k + 3 C d_v + 2 d_k d_v +
+ * 2 C^2 + d_k) * 4 bytes for fp32 activations, 14 C d_k + 8 C d_v +
+ * 4 d_k d_v + 6 C^2 + 4 d_k bytes for bf16 (each rounded up to 256).
  */
 KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv,
                                      int varlen, int num_seqs, int chunk_size,
@@ -211,7 +213,10 @@ KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, in
  *   dbeta         [B, T, H]      fp32
  *   dinitial_state [N, H, Dk, Dv] fp32 dL/dS_0, or NULL (not written)
  * q, k, v, dout, dq, dk, dv, the states and their gradients are 16-byte
- * aligned; dgate and dbeta 4-byte aligned.  All arithmetic is fp32.
+ * aligned; dgate and dbeta 4-byte aligned.  Accumulation is fp32
+ * throughout; with fp32 activations every operand is fp32, with bf16 the
+ * products of the two state passes and of the value-side contractions take
+ * fp16 operands (the key-side products stay fp32).
  */
 KDA_API kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
                          const void *gate, kda_gate gate_kind, const float *beta,

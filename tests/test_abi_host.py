@@ -83,6 +83,20 @@ def _chunk(**over):
                            a["C"], a["act"], a["out"], a["ws"], a["wsb"], a["stream"])
 
 
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_bwd_record_size_matches_the_header(Dk, Dv):
+    """One more chunk adds H records of the size include/kda.h states (plus at
+    most one 256-byte step of the chunk table's alignment)."""
+    C, H = 64, 3
+    rec = {kda.KDA_DTYPE_F32: (3 * C * Dk + 3 * C * Dv + 2 * Dk * Dv + 2 * C * C + Dk) * 4,
+           kda.KDA_DTYPE_BF16: 14 * C * Dk + 8 * C * Dv + 4 * Dk * Dv + 6 * C * C + 4 * Dk}
+    for act, r in rec.items():
+        r = (r + 255) // 256 * 256
+        fb = kda.kda_chunk_bwd_workspace_bytes
+        diff = fb(1, 10 * C, H, Dk, Dv, False, 0, C, act) - fb(1, 9 * C, H, Dk, Dv, False, 0, C, act)
+        assert 0 <= diff - H * r <= 256, (act, diff, H * r)
+
+
 def test_chunk_fwd_argument_errors():
     assert _chunk(q=None) == kda.KDA_ERROR_INVALID_VALUE
     assert _chunk(o=None) == kda.KDA_ERROR_INVALID_VALUE
