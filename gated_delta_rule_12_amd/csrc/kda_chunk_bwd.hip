@@ -1067,15 +1067,26 @@ __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, 
         put();
         __syncthreads();
         if (s0 + SW < DV) fetch(s0 + SW);
-        // dU'^T for dZ
-        for (int idx = tid; idx < C * SW; idx += NTH) {
-            const int r = idx / SW, c = idx % SW;
-            sdUt[c * CS + r] = sdU[r * RS + c];
+        // dU'^T for dZ: eight tokens of one column per thread, one 16-byte store
+        for (int idx = tid; idx < C * SW / 8; idx += NTH) {
+            const int c = idx % SW, r0 = (idx / SW) * 8;
+            h8 x;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = sdU[(r0 + e) * RS + c];
+            *reinterpret_cast<h8*>(sdUt + c * CS + r0) = x;
         }
-        if (tid < DK) {
-#pragma unroll 8
-            for (int c = 0; c < SW; ++c)
-                dgam += static_cast<float>(sdS[tid * RS + c]) * static_cast<float>(sS[tid * RS + c]);
+        // dgamma: NTH / DK threads per key row, 16-byte reads
+        {
+            constexpr int TPR = NTH / DK, CPT = SW / TPR;
+            static_assert(CPT % 8 == 0, "whole 16-byte words per thread");
+            const int r = tid / TPR, c0 = (tid % TPR) * CPT;
+#pragma unroll
+            for (int c = 0; c < CPT; c += 8) {
+                const h8 a = *reinterpret_cast<const h8*>(sdS + r * RS + c0 + c);
+                const h8 b = *reinterpret_cast<const h8*>(sS + r * RS + c0 + c);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dgam += static_cast<float>(a[e]) * static_cast<float>(b[e]);
+            }
         }
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
@@ -1108,7 +1119,12 @@ __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, 
         }
         __syncthreads();
     }
-    if (tid < DK) sDgam[tid] = dgam;
+    {
+        constexpr int TPR = NTH / DK;          // the threads of one key row are adjacent lanes
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) dgam += __shfl_xor(dgam, o, 64);
+        if (tid % TPR == 0) sDgam[tid / TPR] = dgam;
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int t = wave + 8 * u, zmb = t / NZB, znb = t % NZB;
@@ -1212,29 +1228,35 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
         for (int r = 0; r < 2; ++r) store_tile(sY + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
     }
     __syncthreads();
-    // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX
+    // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX.
+    // Tile (mb, nb) below the diagonal costs 8 + nb + 1 product steps; two
+    // tiles per wave, spread so the waves sharing a SIMD (w, w + 4) carry
+    // 28, 28, 22, 22 steps; the six tiles above the diagonal are only zeroed.
     {
-        // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n; tiles above the diagonal are zero
-        f4 ya[2] = {zero4(), zero4()}, rr[2] = {zero4(), zero4()};
-        mm_rows<2, GC, true, true>(sY, LC, 1, sT + tnb * 16 * LC, 1, LC, tmb0, 2,
-                                   [tnb](int mb, int gg) { return tnb <= mb && gg <= tnb; }, ya);
-        mm_rows<2, GK, true, true>(sKh, LK, 1, sKb + tnb * 16 * LK, 1, LK, tmb0, 2,
-                                   [tnb](int mb, int) { return tnb <= mb; }, rr);
+        // (mb, nb) of each wave's first and second tile, 4 bits each
+        constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x3301, 0x2202, 0x1103, 0x2112, 0x3113, 0x3223};
 #pragma unroll
-        for (int r2 = 0; r2 < 2; ++r2) {
-            const int mb = tmb0 + 2 * r2;
+        for (int slot = 0; slot < 2; ++slot) {
+            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
+            const int mb = tt >> 4, nb = tt & 15;
             f4 dr = zero4();
-            if (tnb <= mb) {
+            if (nb <= mb) {
+                // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
+                f4 ya[1] = {zero4()}, rr[1] = {zero4()};
+                mm_rows<1, GC, true, true>(sY, LC, 1, sT + nb * 16 * LC, 1, LC, mb, 1,
+                                           [nb](int, int gg) { return gg <= nb; }, ya);
+                mm_rows<1, GK, true, true>(sKh, LK, 1, sKb + nb * 16 * LK, 1, LK, mb, 1,
+                                           [](int, int) { return true; }, rr);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int r = mb * 16 + 4 * j + e, s = tnb * 16 + i;
-                    const float da = s < r ? -ya[r2][e] : 0.f;
-                    const float part = row16_sum(da * rr[r2][e]);
+                    const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+                    const float da = s2 < r ? -ya[0][e] : 0.f;
+                    const float part = row16_sum(da * rr[0][e]);
                     if (i == 0) sRow[wave * C + r] += part;
                     dr[e] = sBeta[r] * da;
                 }
             }
-            store_tile(sX + mb * 16 * LC + tnb * 16, LC, dr);
+            store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
         }
     }
     __syncthreads();
