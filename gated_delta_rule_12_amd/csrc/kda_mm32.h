@@ -116,9 +116,17 @@ __device__ __forceinline__ f4 load_tile(const float* p, int ld) {
 }
 
 // sum of x over the 16 lanes that share l / 16 (one row of a D-layout tile)
+// Sum over the 16 lanes of each DPP row (lanes 16r..16r+15), in every lane
+// of the row: DPP adds, no trip through the LDS pipe.  Partners: quad xor 1,
+// quad xor 2, half-row mirror (i <-> 7 - i), row mirror (i <-> 15 - i).
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    x += dpp_f<0xB1>(x);     // quad_perm [1, 0, 3, 2]
+    x += dpp_f<0x4E>(x);     // quad_perm [2, 3, 0, 1]
+    x += dpp_f<0x141>(x);    // row_half_mirror
+    x += dpp_f<0x140>(x);    // row_mirror
     return x;
 }
 
