@@ -133,25 +133,29 @@ template <int DK, int NTH, int GATE, typename F>
 __device__ __forceinline__ void gate_cumsum(float* s, int ld, const float* sGs, int len, float* sPart, F&& each) {
     constexpr int NS = NTH / DK, SEG = C / NS;
     static_assert(NS * SEG == C, "row segments tile the chunk");
-    const int c = threadIdx.x % DK, sg = threadIdx.x / DK;
+    const int c = threadIdx.x % DK, sg = threadIdx.x / DK, r0 = sg * SEG;
+    float l2[SEG];
+#pragma unroll
+    for (int r = 0; r < SEG; ++r) l2[r] = GATE == KDA_GATE_SCALAR ? sGs[r0 + r] : s[(r0 + r) * ld + c];
     float part = 0.f;
-    for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-        float l2 = 0.f;
-        if (r < len) {
-            if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
-            else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) l2 = log2_alpha_from_softplus_arg(s[r * ld + c]);
-            else l2 = __builtin_amdgcn_logf(s[r * ld + c]);
+#pragma unroll
+    for (int r = 0; r < SEG; ++r) {
+        float x = 0.f;
+        if (r0 + r < len) {
+            if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) x = log2_alpha_from_softplus_arg(l2[r]);
+            else x = __builtin_amdgcn_logf(l2[r]);
         }
-        s[r * ld + c] = l2;
-        part += l2;
+        l2[r] = x;
+        part += x;
     }
     sPart[sg * DK + c] = part;
     __syncthreads();
     float b = 0.f;
     for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * DK + c];
-    for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-        b += s[r * ld + c];
-        each(r, c, b);
+#pragma unroll
+    for (int r = 0; r < SEG; ++r) {
+        b += l2[r];
+        each(r0 + r, c, b);
     }
 }
 
