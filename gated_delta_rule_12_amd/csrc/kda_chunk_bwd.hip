@@ -235,24 +235,29 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
         write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
     }
 
-    // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record
+    // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record.
+    // Tile (mb, nb) of both shares its B operand; two tile positions per wave,
+    // the ten below or on the diagonal spread so the waves sharing a SIMD
+    // (w, w + 4) hold 3, 3, 2, 2 of them; the six above are only zeroed.
     float* gP = rec_at(P, h, g, R::P);
-    for (int t = wave; t < 32; t += NW) {
-        const int which = t >> 4, mb = (t >> 2) & 3, nb = t & 3;
-        f4 acc = zero4();
-        if (nb <= mb)
-            acc = mm<DK, true, true>((which ? sQ : sKh) + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, acc);
+    {
+        constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x1101, 0x2102, 0x2203, 0x3112, 0x3213, 0x3323};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
-            if (which) acc[e] = s2 <= r ? acc[e] : 0.f;
-            else acc[e] = s2 < r ? sBeta[r] * acc[e] : 0.f;
-        }
-        if (which) {
-            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, acc);   // P, for P^T fragments
-            else store_tile(gP + mb * 16 * C + nb * 16, C, acc);
-        } else {
-            store_tile(sA + mb * 16 * LC + nb * 16, LC, acc);
+        for (int slot = 0; slot < 2; ++slot) {
+            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
+            const int mb = tt >> 4, nb = tt & 15;
+            f4 a = zero4(), pp = zero4();
+            if (nb <= mb)
+                mm_two<DK / 16, true, true>(sKh + mb * 16 * LK, sQ + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, a, pp);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+                a[e] = s2 < r ? sBeta[r] * a[e] : 0.f;
+                pp[e] = s2 <= r ? pp[e] : 0.f;
+            }
+            store_tile(sA + mb * 16 * LC + nb * 16, LC, a);
+            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
+            else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
         }
     }
     __syncthreads();
@@ -323,19 +328,23 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
     // W = T Y, U = T Z (T lower triangular: row block mb reduces over 16 (mb + 1) tokens)
     float* gW = rec_at(P, h, g, R::W);
     float* gU = rec_at(P, h, g, R::U);
+    // wave w: column blocks w, w + 8, ... of [W | U], all four row blocks
+    // sharing each B read
     constexpr int NK = DK / 16, NV = DV / 16;
-    for (int t = wave; t < 4 * (NK + NV); t += NW) {
-        const bool isw = t < 4 * NK;
-        const int tt = isw ? t : t - 4 * NK;
-        const int nn = isw ? NK : NV;
-        const int mb = tt / nn, nb = tt % nn;
-        const f4 acc = mm_n<true, false>(sT + mb * 16 * LC, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1,
-                            (mb + 1) * 16, zero4());
-        if (isw) {
-            if constexpr (ABF16) store_tile(sKb + mb * 16 * LK + nb * 16, LK, acc);   // W, for its fragments
-            else store_tile(gW + mb * 16 * DK + nb * 16, DK, acc);
-        } else {
-            store_tile(gU + mb * 16 * DV + nb * 16, DV, acc);
+    for (int cb = wave; cb < NK + NV; cb += NW) {
+        const bool isw = cb < NK;
+        const int nb = isw ? cb : cb - NK;
+        f4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+        mm_rows<4, C / 16, true, false>(sT, LC, 1, (isw ? sKh : sQ) + nb * 16, isw ? LK : LV, 1, 0, 1,
+                                        [](int mb, int gg) { return gg <= mb; }, acc);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            if (isw) {
+                if constexpr (ABF16) store_tile(sKb + mb * 16 * LK + nb * 16, LK, acc[mb]);   // W, for its fragments
+                else store_tile(gW + mb * 16 * DK + nb * 16, DK, acc[mb]);
+            } else {
+                store_tile(gU + mb * 16 * DV + nb * 16, DV, acc[mb]);
+            }
         }
     }
     if constexpr (ABF16) {

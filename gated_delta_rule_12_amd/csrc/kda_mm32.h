@@ -362,5 +362,26 @@ __device__ __forceinline__ void mm_rows(const float* pa, int am, int ak, const f
                 if (inrange(mb0 + r * mstep, g)) acc[r] = mfma4(a[r][s2], b[s2], acc[r]);
     }
 }
+
+// Two products that share their B operand: acc0 += A0 B, acc1 += A1 B over
+// G groups of 16 reduction indices (pa0, pa1 at their tile's first row).
+template <int G, bool AV, bool BV>
+__device__ __forceinline__ void mm_two(const float* pa0, const float* pa1, int am, int ak, const float* pb, int bk,
+                                       int bn, f4& acc0, f4& acc1) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa0 += i * am + 4 * j * ak;
+    pa1 += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const f4 b = grp4<BV>(pb + 16 * g * bk, bk);
+        const f4 a0 = grp4<AV>(pa0 + 16 * g * ak, ak), a1 = grp4<AV>(pa1 + 16 * g * ak, ak);
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            acc0 = mfma4(a0[s2], b[s2], acc0);
+            acc1 = mfma4(a1[s2], b[s2], acc1);
+        }
+    }
+}
 }  // namespace mm32
 }  // namespace kda
