@@ -766,55 +766,73 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdPa
         __builtin_amdgcn_s_waitcnt(0);       // every load has landed before the wave ends
         return;
     }
-    h8 nW[NKD], nKtt[NKC];
-    f4 nU = zero4(), nGam = zero4();
-    auto fetch = [&](int g) {
-        if (du) {
-#pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) nW[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FW) + afrag_off(mb, kb, NKD, lane));
-            nU = load_tile(rec_at(P, h, g, R::U) + mb * 16 * DV + c0, DV);
-        }
-        if (hasrb) {
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)
-                nKtt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKTT) + afrag_off(rb, kb, NKC, lane));
-            nGam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
-        }
+    // A ring of three operand stages: the operands of chunk g + 2 are loaded
+    // while chunk g computes (stage indices stay static: the loop is unrolled
+    // by three).  Each wave role runs its own copy of the loop, so no load or
+    // store sits under a per-wave branch and the compiler can count what is
+    // still in flight instead of draining every load each chunk.
+    struct Stage {
+        h8 w[NKD], ktt[NKC];
+        f4 u, gam;
     };
-    if (g0 < g1) fetch(g0);
-    for (int g = g0; g < g1; ++g) {
-        h8 Wf[NKD], Ktt[NKC];
+    auto run = [&](auto du_c, auto rb_c) {
+        constexpr bool DU = decltype(du_c)::value, RB = decltype(rb_c)::value;
+        auto fetch = [&](Stage& st, int g) {
+            if constexpr (DU) {
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) Wf[kb] = nW[kb];
+                for (int kb = 0; kb < NKD; ++kb) st.w[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FW) + afrag_off(mb, kb, NKD, lane));
+                st.u = load_tile(rec_at(P, h, g, R::U) + mb * 16 * DV + c0, DV);
+            }
+            if constexpr (RB) {
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) Ktt[kb] = nKtt[kb];
-        const f4 uu = nU, gam = nGam;
-        if (hasrb) {
-            put_btile(sS, KPD, rb * 16, S);
-            store_tile16(hrec_w(g, R::SIN) + rb * 16 * DV + c0, DV, S);
+                for (int kb = 0; kb < NKC; ++kb)
+                    st.ktt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKTT) + afrag_off(rb, kb, NKC, lane));
+                st.gam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
+            }
+        };
+        auto step = [&](const Stage& cur, Stage& nxt, int g) {
+            if constexpr (RB) {
+                put_btile(sS, KPD, rb * 16, S);
+                store_tile16(hrec_w(g, R::SIN) + rb * 16 * DV + c0, DV, S);
+            }
+            __syncthreads();
+            fetch(nxt, min(g + 2, g1 - 1));      // unconditional (past the end: re-reads the last chunk)
+            // U' = U - W S
+            if constexpr (DU) {
+                f4 x = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKD; ++kb) x = mfma16(cur.w[kb], bfrag(sS, KPD, kb), x);
+                const f4 uc = cur.u - x;
+                put_btile(sU, KPC, mb * 16, uc);
+                store_tile16(hrec_w(g, R::UC) + mb * 16 * DV + c0, DV, uc);
+            }
+            __syncthreads();
+            // S <- Diag(gamma) S + Kt^T U'.  No barrier after: the next chunk
+            // writes S before its first barrier (every read of S is before this
+            // chunk's second one) and U' after it.
+            if constexpr (RB) {
+                f4 sv = S * cur.gam;
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) sv = mfma16(cur.ktt[kb], bfrag(sU, KPC, kb), sv);
+                S = sv;
+            }
+        };
+        if (g0 >= g1) return;
+        Stage st0, st1, st2;
+        fetch(st0, g0);
+        fetch(st1, min(g0 + 1, g1 - 1));
+        int g = g0;
+        for (; g + 2 < g1; g += 3) {         // whole rounds: straight-line code
+            step(st0, st2, g);
+            step(st1, st0, g + 1);
+            step(st2, st1, g + 2);
         }
-        __syncthreads();
-        if (g + 1 < g1) fetch(g + 1);
-        // U' = U - W S
-        if (du) {
-            f4 x = zero4();
-#pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) x = mfma16(Wf[kb], bfrag(sS, KPD, kb), x);
-            const f4 uc = uu - x;
-            put_btile(sU, KPC, mb * 16, uc);
-            store_tile16(hrec_w(g, R::UC) + mb * 16 * DV + c0, DV, uc);
-        }
-        __syncthreads();
-        // S <- Diag(gamma) S + Kt^T U'.  No barrier after: the next chunk
-        // writes S before its first barrier (every read of S is before this
-        // chunk's second one) and U' after it.
-        if (hasrb) {
-            f4 sv = S * gam;
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) sv = mfma16(Ktt[kb], bfrag(sU, KPC, kb), sv);
-            S = sv;
-        }
-    }
+        if (g < g1) step(st0, st2, g);
+        if (g + 1 < g1) step(st1, st0, g + 1);
+    };
+    if (du) run(std::true_type{}, std::true_type{});            // waves 0..3 own a row block of U' and of S
+    else if (hasrb) run(std::false_type{}, std::true_type{});
+    else run(std::false_type{}, std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
