@@ -558,11 +558,12 @@ __global__ __launch_bounds__(kChainThreads) void bwd_rev_kernel(const BwdParams 
 // 16-bit activations: the same two state passes on the fp16 matrix cores
 // (16x16x32), as the forward's state pass does.  Each wave reads its A
 // fragments (Kt, P^T, Qh^T, W^T; or W, Kt^T) straight from the record,
-// fragment-major, one chunk ahead; the B operands (dO, dS, dU'; or S, U')
+// fragment-major, ahead of the chain; the B operands (dO, dS, dU'; or S, U')
 // pass through LDS as column-major fp16 tiles.  The states and their
 // gradients stay fp32 in registers; the state entering each chunk, the
 // state gradient, U' and dU' go to the record in fp16 (their one reader,
-// the 16-bit value-side kernel, takes them as fp16 operands anyway).  Waves 0..3 compute the C x 16 product (row block = wave), every
+// the 16-bit value side of the gradient kernel, takes them as fp16 operands
+// anyway).  Waves 0..3 compute the C x 16 product (row block = wave), every
 // wave one 16-row block of the d_k x 16 state tile.
 // ---------------------------------------------------------------------------
 template <int DK> struct Chain16B {
@@ -572,7 +573,8 @@ template <int DK> struct Chain16B {
 };
 // Eight compute waves and one wave that brings the records (and dO rows) of
 // the chunk kChainPrefetch steps ahead of the chain into the XCD's L2; the
-// compute waves load each chunk's operands one step ahead.  The prefetch
+// compute waves load each chunk's operands two (checkpoint pass) or one
+// (reverse pass, whose operands take more registers) steps ahead.  The prefetch
 // wave passes the same two barriers per chunk, bare (a fenced barrier would
 // wait for its loads).
 #ifndef KDA_CHAIN_PREFETCH
@@ -613,10 +615,6 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
     // computes.  A sequence's chunks are consecutive rows of C tokens, so the
     // dO rows of chunk g follow from the sequence's first row and last
     // length (no per-chunk table load for a prefetch to wait on).
-    h8 nKt[NKD], nPt[NKC], nQt[NKC], nWt[NKC];
-    u16x4 ndO = {0, 0, 0, 0};
-    int ndO_len = 0;
-    f4 nGam = zero4();
     const int row_first = g1 > g0 ? P.table[g0].y : 0;
     const int len_last = g1 > g0 ? P.table[g1 - 1].z : 0;
     if (wave == kChainWaves) {
@@ -646,78 +644,92 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
         return;
     }
     const int dr = threadIdx.x >> 2, dc = 4 * (threadIdx.x & 3);      // dO element rows / columns of this thread
-    auto fetch = [&](int g) {
-        const int row0 = row_first + (g - g0) * C, len = g == g1 - 1 ? len_last : C;
-        if (du) {
-#pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) nKt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKT) + afrag_off(mb, kb, NKD, lane));
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) nPt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FPT) + afrag_off(mb, kb, NKC, lane));
-        }
-        if (hasrb) {
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                nQt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FQHT) + afrag_off(rb, kb, NKC, lane));
-                nWt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FWT) + afrag_off(rb, kb, NKC, lane));
-            }
-            nGam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
-        }
-        if (dr < C) {
-            const int rr = dr < len ? dr : len - 1;
-            ndO = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(P.dout) +
-                                                  (static_cast<size_t>(row0 + rr) * H + h) * DV + c0 + dc);
-        }
-        ndO_len = len;
+    // Two operand stages: the operands of chunk g - 1 are loaded while chunk g
+    // computes (the loop is unrolled by two so stage indices stay static; a
+    // third stage would exceed the registers nine waves leave).  Each wave
+    // role runs its own copy of the loop, so no load or store sits under a
+    // per-wave branch and the compiler counts what is in flight instead of
+    // draining every load each chunk.
+    struct Stage {
+        h8 kt[NKD], pt[NKC], qt[NKC], wt[NKC];
+        u16x4 dO;
+        f4 gam;
+        int len;
     };
-    if (g1 > g0) fetch(g1 - 1);
-    for (int g = g1 - 1; g >= g0; --g) {
-        _Float16* sdO = sdO2 + (g & 1) * 16 * KPC;
-        h8 Kt[NKD], Pt[NKC], Qt[NKC], Wt[NKC];
+    auto run = [&](auto du_c, auto rb_c) {
+        constexpr bool DU = decltype(du_c)::value, RB = decltype(rb_c)::value;
+        auto fetch = [&](Stage& st, int g) {
+            const int row0 = row_first + (g - g0) * C, len = g == g1 - 1 ? len_last : C;
+            st.len = len;
+            if constexpr (DU) {              // waves 0..3: dU' row block mb, and the dO tile (threads 0..4C-1)
 #pragma unroll
-        for (int kb = 0; kb < NKD; ++kb) Kt[kb] = nKt[kb];
+                for (int kb = 0; kb < NKD; ++kb) st.kt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKT) + afrag_off(mb, kb, NKD, lane));
 #pragma unroll
-        for (int kb = 0; kb < NKC; ++kb) {
-            Pt[kb] = nPt[kb];
-            Qt[kb] = nQt[kb];
-            Wt[kb] = nWt[kb];
-        }
-        const f4 gam = nGam;
-        if (dr < C) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sdO[(dc + e) * KPC + dr] = static_cast<_Float16>(dr < ndO_len ? bf16_to_f32(ndO[e]) : 0.f);
-        }
-        if (hasrb) {
-            put_btile(sdS, KPD, rb * 16, dS);
-            store_tile16(hrec_w(g, R::DSO) + rb * 16 * DV + c0, DV, dS);
-        }
-        __syncthreads();
-        if (g > g0) fetch(g - 1);
-        // dU' = Kt dS + P^T dO   (P^T[m][k] = P[k][m], zero for k < m)
-        if (du) {
-            f4 acc = zero4();
-#pragma unroll
-            for (int kb = 0; kb < NKD; ++kb) acc = mfma16(Kt[kb], bfrag(sdS, KPD, kb), acc);
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb)
-                if (32 * kb + 31 >= 16 * mb) acc = mfma16(Pt[kb], bfrag(sdO, KPC, kb), acc);
-            put_btile(sdU, KPC, mb * 16, acc);
-            store_tile16(hrec_w(g, R::DUC) + mb * 16 * DV + c0, DV, acc);
-        }
-        __syncthreads();
-        // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'.  No barrier after: the next
-        // chunk writes dS and its own dO buffer before its first barrier, and
-        // dU' after it.
-        if (hasrb) {
-            f4 x = dS * gam, y = zero4();
-#pragma unroll
-            for (int kb = 0; kb < NKC; ++kb) {
-                x = mfma16(Qt[kb], bfrag(sdO, KPC, kb), x);
-                y = mfma16(Wt[kb], bfrag(sdU, KPC, kb), y);
+                for (int kb = 0; kb < NKC; ++kb) st.pt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FPT) + afrag_off(mb, kb, NKC, lane));
+                const int rr = dr < len ? dr : len - 1;
+                st.dO = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(P.dout) +
+                                                       (static_cast<size_t>(row0 + rr) * H + h) * DV + c0 + dc);
             }
-            dS = x - y;
+            if constexpr (RB) {
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    st.qt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FQHT) + afrag_off(rb, kb, NKC, lane));
+                    st.wt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FWT) + afrag_off(rb, kb, NKC, lane));
+                }
+                st.gam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
+            }
+        };
+        auto step = [&](const Stage& cur, Stage& nxt, int g) {
+            _Float16* sdO = sdO2 + (g & 1) * 16 * KPC;
+            if constexpr (DU) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    sdO[(dc + e) * KPC + dr] = static_cast<_Float16>(dr < cur.len ? bf16_to_f32(cur.dO[e]) : 0.f);
+            }
+            if constexpr (RB) {
+                put_btile(sdS, KPD, rb * 16, dS);
+                store_tile16(hrec_w(g, R::DSO) + rb * 16 * DV + c0, DV, dS);
+            }
+            __syncthreads();
+            fetch(nxt, max(g - 1, g0));          // unconditional (past the start: re-reads the first chunk)
+            // dU' = Kt dS + P^T dO   (P^T[m][k] = P[k][m], zero for k < m)
+            if constexpr (DU) {
+                f4 acc = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKD; ++kb) acc = mfma16(cur.kt[kb], bfrag(sdS, KPD, kb), acc);
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb)
+                    if (32 * kb + 31 >= 16 * mb) acc = mfma16(cur.pt[kb], bfrag(sdO, KPC, kb), acc);
+                put_btile(sdU, KPC, mb * 16, acc);
+                store_tile16(hrec_w(g, R::DUC) + mb * 16 * DV + c0, DV, acc);
+            }
+            __syncthreads();
+            // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'.  No barrier after: the next
+            // chunk writes dS and its own dO buffer before its first barrier, and
+            // dU' after it.
+            if constexpr (RB) {
+                f4 x = dS * cur.gam, y = zero4();
+#pragma unroll
+                for (int kb = 0; kb < NKC; ++kb) {
+                    x = mfma16(cur.qt[kb], bfrag(sdO, KPC, kb), x);
+                    y = mfma16(cur.wt[kb], bfrag(sdU, KPC, kb), y);
+                }
+                dS = x - y;
+            }
+        };
+        if (g0 >= g1) return;
+        Stage st0, st1;
+        fetch(st0, g1 - 1);
+        int g = g1 - 1;
+        for (; g - 1 >= g0; g -= 2) {        // whole rounds: straight-line code
+            step(st0, st1, g);
+            step(st1, st0, g - 1);
         }
-    }
+        if (g >= g0) step(st0, st1, g);
+    };
+    if (du) run(std::true_type{}, std::true_type{});            // waves 0..3 own a row block of dU' and of dS
+    else if (hasrb) run(std::false_type{}, std::true_type{});
+    else run(std::false_type{}, std::false_type{});
     if (P.dinitial_state && hasrb) store_tile(P.dinitial_state + sbase + rb * 16 * DV + c0, DV, dS);
 }
 
