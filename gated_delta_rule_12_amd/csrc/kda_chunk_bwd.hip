@@ -190,10 +190,12 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
     const int len = ent.z;
     const int tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
 
+    Tok<ABF16, DV, DV, NTH> tv;          // V, held in registers until T is done
     {
         Tok<ABF16, DK, DK, NTH> tk, tq;
         tk.load(P.k, row0, len, h, H);
         tq.load(P.q, row0, len, h, H);
+        tv.load(P.v, row0, len, h, H);
         if constexpr (GATE == KDA_GATE_SCALAR) {
             if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
         } else {
@@ -271,16 +273,23 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
     // one diagonal block by substitution (16 lanes, one column each), then
     // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj for i - j = 1, 2, 3.
     float* sX = sKb;                     // scratch: one 16 x 16 tile per wave
+    // Column-oriented: once t[s] is final, every later row takes its term at
+    // once (the same operations, in the same order per row, as row by row,
+    // but a chain of 16 steps instead of 120).
     if (wave < 4 && lane < 16) {
         const int col = lane, o = 16 * wave;
+        float a[120];                    // the block's strict lower triangle, all reads issued first
+#pragma unroll
+        for (int r = 1, q = 0; r < 16; ++r)
+#pragma unroll
+            for (int s2 = 0; s2 < r; ++s2, ++q) a[q] = sA[(o + r) * LC + o + s2];
         float t[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float x = r == col ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) t[r] = r == col ? 1.f : 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < r; ++s2) x -= sA[(o + r) * LC + o + s2] * t[s2];
-            t[r] = x;
-        }
+        for (int s2 = 0; s2 < 15; ++s2)
+#pragma unroll
+            for (int r = s2 + 1; r < 16; ++r) t[r] -= a[r * (r - 1) / 2 + s2] * t[s2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(o + r) * LC + o + col] = t[r];
     }
@@ -313,16 +322,7 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
         __syncthreads();
     }
     store_block<NTH>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
-    {
-        Tok<ABF16, DV, DV, NTH> tv;
-        tv.load(P.v, row0, len, h, H);
-        tv.put(sQ, LV);
-    }
-    __syncthreads();
-    for (int idx = tid; idx < C * DV; idx += NTH) {
-        const int r = idx / DV, c = idx % DV;
-        sQ[r * LV + c] *= sBeta[r];
-    }
+    tv.put_scaled(sQ, LV, sBeta);        // Z = Diag(beta) V
     __syncthreads();
 
     // W = T Y, U = T Z (T lower triangular: row block mb reduces over 16 (mb + 1) tokens)

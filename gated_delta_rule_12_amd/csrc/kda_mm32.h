@@ -211,6 +211,22 @@ struct Tok {
             }
         }
     }
+    // put() with every row r multiplied by scale[r]
+    __device__ __forceinline__ void put_scaled(float* dst, int ld, const float* scale) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N) {
+                f4 x;
+                if constexpr (BF16)
+                    x = f4{bf16_to_f32(t[it][0]), bf16_to_f32(t[it][1]), bf16_to_f32(t[it][2]), bf16_to_f32(t[it][3])};
+                else x = t[it];
+                const int r = idx / V4;
+                x = r < len_ ? x * scale[r] : zero4();
+                *reinterpret_cast<f4*>(dst + r * ld + (idx % V4) * 4) = x;
+            }
+        }
+    }
 };
 
 template <int ROWS, int NC, int NTH>
