@@ -1438,16 +1438,24 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
 #pragma unroll
         for (int z = 0; z < MSTEP; ++z) acc2 += sCol[z * DK + c];
         for (int s2 = sg + 1; s2 < NS; ++s2) acc2 += sPart[s2 * DK + c];
-        for (int r = sg * SEG + SEG - 1; r >= sg * SEG; --r) {
-            acc2 += sKh[r * LK + c];
+        // the segment's db and gate values first (independent reads), then the scan
+        float dbv[SEG], gv[SEG];
+#pragma unroll
+        for (int q = 0; q < SEG; ++q) {
+            dbv[q] = sKh[(sg * SEG + q) * LK + c];
+            if constexpr (GATE != KDA_GATE_SCALAR) gv[q] = sW[(sg * SEG + q) * LK + c];
+        }
+#pragma unroll
+        for (int q = SEG - 1; q >= 0; --q) {
+            const int r = sg * SEG + q;
+            acc2 += dbv[q];
             if (r < len) {
                 const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c;
                 if constexpr (GATE == KDA_GATE_ALPHA) {
-                    P.dgate[ai] = acc2 / sW[r * LK + c];
+                    P.dgate[ai] = acc2 / gv[q];
                 } else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
                     // log alpha = -softplus(x): d/dx = -sigmoid(x)
-                    const float x = sW[r * LK + c];
-                    const float sgm = 1.f / (1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+                    const float sgm = 1.f / (1.f + __builtin_amdgcn_exp2f(-gv[q] * 1.4426950408889634f));
                     P.dgate[ai] = -acc2 * sgm;
                 } else {
                     sKb[r * LK + c] = acc2;
