@@ -1354,6 +1354,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
                                   [](int mb, int gg) { return gg >= mb; }, dKb);
     __syncthreads();
 
+    // bf16 dq and dk rows, staged in the (now free) dT / Y1 regions
+    constexpr int LDQ = DK + 8;
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    uint16_t* sDq = reinterpret_cast<uint16_t*>(sX);
+    uint16_t* sDk = sDq + C * LDQ;
+    static_assert(2 * C * LDQ * 2 <= 2 * C * LC * 4, "dq and dk fit the dT and Y1 regions");
     // gate chain rule, dq, dk.  Every operand is staged in LDS first (the
     // regions are free now), so no load waits behind a store of dq or dk:
     // q -> sKh, k -> sKb, the gate -> sW (b after the scan); dKt is the
@@ -1401,10 +1407,14 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
                 const float qv = sKh[row * LK + c], kv = sKb[row * LK + c], dkt = acc[2 * RW + r][e];
                 const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam_c * kb;
                 const float dqh = dQh[r][e], dkh = dKh[r][e], dkb = dKb[r][e];
-                if (row < len) {
+                const float dqv = G * dqh, dkv = G * dkh + Gi * dkb + gam_c * Gi * dkt;
+                if constexpr (ABF16) {           // staged in LDS, written below as whole 16-byte words
+                    sDq[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dqv));
+                    sDk[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dkv));
+                } else if (row < len) {
                     const size_t ai = (static_cast<size_t>(row0 + row) * H + h) * DK + c;
-                    store_out<ABF16>(P.dq, ai, G * dqh);
-                    store_out<ABF16>(P.dk, ai, G * dkh + Gi * dkb + gam_c * Gi * dkt);
+                    store_out<false>(P.dq, ai, dqv);
+                    store_out<false>(P.dk, ai, dkv);
                 }
                 sKh[row * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;   // db
                 col += kt * dkt;
@@ -1415,6 +1425,17 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
         if (j == 0) sCol[cmb0 * DK + c] = col;
     }
     __syncthreads();
+    if constexpr (ABF16) {
+        constexpr int W8 = DK / 8;
+        for (int idx = tid; idx < C * W8; idx += NTH) {
+            const int r = idx / W8, c8 = (idx % W8) * 8;
+            if (r < len) {
+                const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c8;
+                *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dq) + ai) = *reinterpret_cast<const u16x8*>(sDq + r * LDQ + c8);
+                *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dk) + ai) = *reinterpret_cast<const u16x8*>(sDk + r * LDQ + c8);
+            }
+        }
+    }
     // the gate as given (b is no longer needed); partial sums of db per segment
     if constexpr (GATE == KDA_GATE_SCALAR) {
         if (tid < C) sW[tid] = gs;
