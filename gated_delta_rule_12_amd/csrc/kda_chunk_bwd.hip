@@ -1001,7 +1001,7 @@ __device__ __forceinline__ void vside_phase32(const BwdParams& P, int h, int g, 
 // serve dZ = T^T dU'.
 template <int DK, int DV> struct V16L {
     static constexpr int SW = DV < 64 ? DV : 64, RS = SW + 8, CS = C + 8, NZB = SW / 16;
-    static constexpr int bytes = (2 * DK * RS + 4 * C * RS + SW * CS + C * CS) * 2 + NZB * C * 4;
+    static constexpr int bytes = (2 * DK * RS + 4 * C * RS + SW * CS + C * CS) * 2 + NZB * C * 4 + C * RS * 2;
 };
 
 template <int DK, int DV>
@@ -1023,6 +1023,7 @@ __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, 
     _Float16* sdUt = sV + C * RS;                          // dU'[:, slice]^T     [SW][CS]
     _Float16* sTt = sdUt + SW * CS;                        // T^T                 [C][CS]
     float* sDbzP = reinterpret_cast<float*>(sTt + C * CS); // rowsum(dZ . V) per column block  [NZB][C]
+    uint16_t* sDv = reinterpret_cast<uint16_t*>(sDbzP + NZB * C);   // dv of the slice, bf16   [C][RS]
     const int H = P.H, tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
     auto hrec = [&](size_t off) {
         return reinterpret_cast<const _Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
@@ -1155,12 +1156,19 @@ __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, 
                                *reinterpret_cast<const h8*>(sdUt + (16 * znb + i) * CS + 32 * kb + 8 * j), z);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = zmb * 16 + 4 * j + e, col = s0 + znb * 16 + i;
-                if (r < len) store_out<true>(P.dv, (static_cast<size_t>(row0 + r) * H + h) * DV + col, sBeta[r] * z[e]);
+                const int r = zmb * 16 + 4 * j + e;
+                sDv[r * RS + znb * 16 + i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(sBeta[r] * z[e]));
                 dbz[u][e] += z[e] * static_cast<float>(sV[r * RS + znb * 16 + i]);
             }
         }
         __syncthreads();
+        // dv rows of the slice as 16-byte words
+        for (int idx = tid; idx < C * W8; idx += NTH) {
+            const int r = idx / W8, c = (idx % W8) * 8;
+            if (r < len)
+                *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dv) + (static_cast<size_t>(row0 + r) * H + h) * DV + s0 + c) =
+                    *reinterpret_cast<const u16x8*>(sDv + r * RS + c);
+        }
     }
     {
         constexpr int TPR = NTH / DK;          // the threads of one key row are adjacent lanes
