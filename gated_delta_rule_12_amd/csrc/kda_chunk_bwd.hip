@@ -686,13 +686,11 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
                 for (int e = 0; e < 4; ++e)
                     sdO[(dc + e) * KPC + dr] = static_cast<_Float16>(dr < cur.len ? bf16_to_f32(cur.dO[e]) : 0.f);
             }
-            if constexpr (RB) {
-                put_btile(sdS, KPD, rb * 16, dS);
-                store_tile16(hrec_w(g, R::DSO) + rb * 16 * DV + c0, DV, dS);
-            }
+            if constexpr (RB) put_btile(sdS, KPD, rb * 16, dS);
             __syncthreads();
             fetch(nxt, max(g - 1, g0));          // unconditional (past the start: re-reads the first chunk)
-            // dU' = Kt dS + P^T dO   (P^T[m][k] = P[k][m], zero for k < m)
+            // dU' = Kt dS + P^T dO   (P^T[m][k] = P[k][m], zero for k < m); waves 4..7
+            // meanwhile write dS to the record as 16-byte row words
             if constexpr (DU) {
                 f4 acc = zero4();
 #pragma unroll
@@ -701,9 +699,12 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
                 for (int kb = 0; kb < NKC; ++kb)
                     if (32 * kb + 31 >= 16 * mb) acc = mfma16(cur.pt[kb], bfrag(sdO, KPC, kb), acc);
                 put_btile(sdU, KPC, mb * 16, acc);
-                store_tile16(hrec_w(g, R::DUC) + mb * 16 * DV + c0, DV, acc);
+            } else {
+                store_ctile16<DK, kChainThreads / 2>(hrec_w(g, R::DSO) + c0, DV, sdS, KPD, threadIdx.x - kChainThreads / 2);
             }
             __syncthreads();
+            if constexpr (!DU)
+                store_ctile16<C, kChainThreads / 2>(hrec_w(g, R::DUC) + c0, DV, sdU, KPC, threadIdx.x - kChainThreads / 2);
             // dS <- Diag(gamma) dS + Qh^T dO - W^T dU'.  No barrier after: the next
             // chunk writes dS and its own dO buffer before its first barrier, and
             // dU' after it.
@@ -803,22 +804,22 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdPa
             }
         };
         auto step = [&](const Stage& cur, Stage& nxt, int g) {
-            if constexpr (RB) {
-                put_btile(sS, KPD, rb * 16, S);
-                store_tile16(hrec_w(g, R::SIN) + rb * 16 * DV + c0, DV, S);
-            }
+            if constexpr (RB) put_btile(sS, KPD, rb * 16, S);
             __syncthreads();
             fetch(nxt, min(g + 2, g1 - 1));      // unconditional (past the end: re-reads the last chunk)
-            // U' = U - W S
+            // U' = U - W S; waves 4..7 meanwhile write S to the record as 16-byte row words
             if constexpr (DU) {
                 f4 x = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) x = mfma16(cur.w[kb], bfrag(sS, KPD, kb), x);
                 const f4 uc = cur.u - x;
                 put_btile(sU, KPC, mb * 16, uc);
-                store_tile16(hrec_w(g, R::UC) + mb * 16 * DV + c0, DV, uc);
+            } else {
+                store_ctile16<DK, kChainThreads / 2>(hrec_w(g, R::SIN) + c0, DV, sS, KPD, threadIdx.x - kChainThreads / 2);
             }
             __syncthreads();
+            if constexpr (!DU)
+                store_ctile16<C, kChainThreads / 2>(hrec_w(g, R::UC) + c0, DV, sU, KPC, threadIdx.x - kChainThreads / 2);
             // S <- Diag(gamma) S + Kt^T U'.  No barrier after: the next chunk
             // writes S before its first barrier (every read of S is before this
             // chunk's second one) and U' after it.

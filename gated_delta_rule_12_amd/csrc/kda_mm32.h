@@ -342,6 +342,20 @@ __device__ __forceinline__ void put_btile(_Float16* t, int kp, int k0, f4 v) {
     *reinterpret_cast<h4*>(t + i * kp + k0 + 4 * j) = h;
 }
 
+// A 16-column fp16 LDS tile stored column-major (element (r, c) at
+// t[c * kp + r], as put_btile leaves it), rows 0..ROWS-1, to row-major memory
+// (row stride ld halves) as 16-byte words, from threads tix = 0 .. NT-1.
+template <int ROWS, int NT>
+__device__ __forceinline__ void store_ctile16(_Float16* p, int ld, const _Float16* t, int kp, int tix) {
+    for (int w = tix; w < ROWS * 2; w += NT) {
+        const int r = w >> 1, c8 = (w & 1) * 8;
+        h8 x;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = t[(c8 + e) * kp + r];
+        *reinterpret_cast<h8*>(p + static_cast<size_t>(r) * ld + c8) = x;
+    }
+}
+
 // D-layout fp32 tile -> fp16 row-major memory (row stride ld halves)
 __device__ __forceinline__ void store_tile16(_Float16* p, int ld, f4 v) {
     const int i = lane_id() & 15, j = lane_id() >> 4;
