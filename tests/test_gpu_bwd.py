@@ -75,6 +75,16 @@ def test_bwd_varlen(gate):
     _bwd_case(1, 0, 3, 128, 128, "bf16", seed=5, gate=gate, lengths=[0, 70, 1, 256, 133])
 
 
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_bwd_chunk_counts_past_the_unrolled_rounds(act):
+    """Sequences of 5, 6 and 3 chunks (ragged tails): the state passes run
+    their operand rings in whole rounds of three (checkpoint) or two
+    (reverse) chunks plus a remainder, and these lengths reach every
+    remainder after at least one whole round."""
+    print(f"[bwd chunk counts act={act}]", flush=True)
+    _bwd_case(1, 0, 2, 128, 128, act, seed=31, lengths=[300, 327, 129])
+
+
 def test_bwd_without_state_arguments():
     print("[bwd no S0, no dS_T, no dS0]", flush=True)
     _bwd_case(2, 130, 2, 128, 128, "f32", seed=17, s0_std=None, ds_std=None, need_ds0=False)
