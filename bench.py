@@ -139,6 +139,34 @@ def measured_traffic():
         return None
 
 
+# the device code of the backward kernels
+BWD_KERNEL_SOURCES = ["gated_delta_rule_12_amd/csrc/kda_chunk_bwd.hip", "gated_delta_rule_12_amd/csrc/kda_mm32.h",
+                      "gated_delta_rule_12_amd/csrc/kda_common.h", "gated_delta_rule_12_amd/csrc/kda_chunk.h"]
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_chunk_bwd_B1_H32_T65536_d128_bf16.txt")
+
+
+def measured_bwd_traffic():
+    """HBM bytes per backward launch from the committed rocprofv3 summary, or
+    None when the backward's sources changed since it was taken."""
+    import hashlib
+    try:
+        fields = {}
+        with open(BWD_TRAFFIC_FILE) as f:
+            for line in f:
+                if not line.startswith("#") and ":" in line:
+                    key, val = line.split(":", 1)
+                    fields[key.strip()] = val.split()[0]
+        h = hashlib.sha256()
+        for s in BWD_KERNEL_SOURCES:
+            with open(os.path.join(ROOT, s), "rb") as f:
+                h.update(f.read())
+        if fields.get("sources_sha256") != h.hexdigest():
+            return None
+        return int(float(fields["bwd_traffic_bytes"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -227,7 +255,10 @@ def bench_bwd(kda, synth, torch, fi, wf, reps, warm):
                                   "peak = useful flops / their time with each part at its own peak",
                          "useful_flops_per_launch": round(fl)},
             "hbm_algorithmic": {"bytes_per_launch": byts,
-                                "GBps": round(byts / (ms / 1e3) / 1e9, 1)},
+                                "GBps": round(byts / (ms / 1e3) / 1e9, 1),
+                                "traffic": measured_bwd_traffic(),
+                                "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated; "
+                                                "null if the kernels changed since)"},
             "note": "gradients of sum(dO*o) + sum(dS_T*S_T) w.r.t. q, k, v, alpha, beta, S_0; "
                     "the forward is recomputed inside the call"}
 
