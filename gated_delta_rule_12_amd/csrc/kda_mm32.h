@@ -1,7 +1,8 @@
-// fp32 matrix-core building blocks shared by the chunkwise backward and the
-// chunk-size-generic forward (gfx950): a 16x16 fp32 MFMA tile over LDS
+// Matrix-core building blocks shared by the chunkwise backward and the
+// chunk-size-generic forward (gfx950): 16x16 fp32 MFMA tiles over LDS
 // operands with arbitrary strides, register-staged global -> LDS copies,
-// and the gate forms as log2(alpha).
+// DPP row sums, the XCD-aware chain grid, fp16 MFMA fragments and L2
+// prefetch touches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -115,7 +116,6 @@ __device__ __forceinline__ f4 load_tile(const float* p, int ld) {
     return v;
 }
 
-// sum of x over the 16 lanes that share l / 16 (one row of a D-layout tile)
 // Sum over the 16 lanes of each DPP row (lanes 16r..16r+15), in every lane
 // of the row: DPP adds, no trip through the LDS pipe.  Partners: quad xor 1,
 // quad xor 2, half-row mirror (i <-> 7 - i), row mirror (i <-> 15 - i).
@@ -128,20 +128,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     x += dpp_f<0x141>(x);    // row_half_mirror
     x += dpp_f<0x140>(x);    // row_mirror
     return x;
-}
-
-// four consecutive activations as fp32 (16-byte / 8-byte aligned)
-template <bool BF16> __device__ __forceinline__ f4 act4(const void* p, size_t i);
-template <> __device__ __forceinline__ f4 act4<false>(const void* p, size_t i) {
-    return *reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
-}
-template <> __device__ __forceinline__ f4 act4<true>(const void* p, size_t i) {
-    const u16x4 r = *reinterpret_cast<const u16x4*>(static_cast<const uint16_t*>(p) + i);
-    return f4{bf16_to_f32(r[0]), bf16_to_f32(r[1]), bf16_to_f32(r[2]), bf16_to_f32(r[3])};
-}
-template <bool BF16> __device__ __forceinline__ float act1(const void* p, size_t i) {
-    if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
-    else return static_cast<const float*>(p)[i];
 }
 
 // Register-staged copies: load() issues every global load of a block before
@@ -236,33 +222,12 @@ __device__ __forceinline__ void load_block(float* dst, int ld, const float* src,
     b.put(dst, ld);
 }
 
-template <bool BF16, int COLS, int NC, int NTH, int ROWS = kChunk>
-__device__ __forceinline__ void load_tokens(float* dst, int ld, const void* src, int64_t row0, int len, int h,
-                                            int H, int c0 = 0) {
-    Tok<BF16, COLS, NC, NTH, ROWS> t;
-    t.load(src, row0, len, h, H, c0);
-    t.put(dst, ld);
-}
-
 template <int NTH>
 __device__ __forceinline__ void store_block(float* dst, int dld, const float* src, int ld, int rows, int ncols) {
     const int v4 = ncols / 4;
     for (int idx = threadIdx.x; idx < rows * v4; idx += NTH) {
         const int r = idx / v4, c = (idx % v4) * 4;
         *reinterpret_cast<f4*>(dst + static_cast<size_t>(r) * dld + c) = *reinterpret_cast<const f4*>(src + r * ld + c);
-    }
-}
-
-// log2 alpha of (row, head, channel c) from the gate as given
-template <int GATE, int DK>
-__device__ __forceinline__ float gate_log2(const void* gate, int64_t row, int h, int H, int c) {
-    if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) {
-        const uint16_t x = static_cast<const uint16_t*>(gate)[(static_cast<size_t>(row) * H + h) * DK + c];
-        return log2_alpha_from_softplus_arg(bf16_to_f32(x));
-    } else if constexpr (GATE == KDA_GATE_SCALAR) {
-        return __builtin_amdgcn_logf(static_cast<const float*>(gate)[static_cast<size_t>(row) * H + h]);
-    } else {
-        return __builtin_amdgcn_logf(static_cast<const float*>(gate)[(static_cast<size_t>(row) * H + h) * DK + c]);
     }
 }
 
@@ -354,13 +319,6 @@ __device__ __forceinline__ void store_ctile16(_Float16* p, int ld, const _Float1
         for (int e = 0; e < 8; ++e) x[e] = t[(c8 + e) * kp + r];
         *reinterpret_cast<h8*>(p + static_cast<size_t>(r) * ld + c8) = x;
     }
-}
-
-// D-layout fp32 tile -> fp16 row-major memory (row stride ld halves)
-__device__ __forceinline__ void store_tile16(_Float16* p, int ld, f4 v) {
-    const int i = lane_id() & 15, j = lane_id() >> 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[(4 * j + e) * ld + i] = static_cast<_Float16>(v[e]);
 }
 
 // R output tiles that share their column block: tile r is row block
