@@ -693,14 +693,22 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
         // x[s] is final, every later row takes its contribution
         if (lane < 16) {
             const int j = lane;
+            // the block's strict lower triangle, every read issued before the
+            // first use: a[rr(rr-1)/2 + s] = A[16I+rr][16I+s]
+            float a[120];
+#pragma unroll
+            for (int s = 0; s < 15; ++s) {
+                const float* col = s_AT + (16 * I + s) * ATP + 16 * I;
+#pragma unroll
+                for (int rr = s + 1; rr < 16; ++rr) a[rr * (rr - 1) / 2 + s] = col[rr];
+            }
             float x[16];
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == j) ? 1.f : 0.f;
 #pragma unroll
             for (int s = 0; s < 15; ++s) {
-                const float* col = s_AT + (16 * I + s) * ATP + 16 * I;   // A[16I+rr][16I+s], rr = 0..15
 #pragma unroll
-                for (int rr = s + 1; rr < 16; ++rr) x[rr] -= col[rr] * x[s];
+                for (int rr = s + 1; rr < 16; ++rr) x[rr] -= a[rr * (rr - 1) / 2 + s] * x[s];
             }
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) s_T[(16 * I + rr) * TP + 16 * I + j] = x[rr];
@@ -816,8 +824,7 @@ struct StateStage {
     V p[2];                  // row 16w+lm of P, tokens 0..63
     V k[TPW][2];             // rows of ((gamma/Gamma).K)^T owned by this wave
     typename Mx<F16>::V4 u[TW];   // U: tokens 16w+4lg..+3, one column per tile
-    f4 gm[TPW];              // gamma for the owned state rows
-    int t0, len;
+    float gm;                // gamma of owned state row (lane mod DK/4); lanes trade them at use
 };
 
 // Four compute waves, plus one wave that prefetches records into L2 where
@@ -901,6 +908,15 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
         }
     }
 
+    // The chunks of a sequence are consecutive runs of C tokens from its
+    // first row: the first and last table entries give every chunk's rows.
+    int seq_t0 = 0, seq_end = 0;
+    if (g0 < g1) {
+        const int4 e0 = P.table[g0];
+        const int4 e1 = P.table[g1 - 1];
+        seq_t0 = e0.y;
+        seq_end = e1.y + e1.z;
+    }
     const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.gmax * P.rec_bytes;
     const size_t gstride = P.rec_bytes;
     // output rows of this lane: tokens 16w + 4lg + i of the chunk
@@ -924,13 +940,11 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
 #pragma unroll
             for (int c = 0; c < TW; ++c)
                 st.u[c] = M::load4(ut + (static_cast<size_t>((jt * TW + c) * 4 + wave) * 64 + lane) * 4);
-            const int4 ent = P.table[g];
-            st.t0 = ent.y;
-            st.len = ent.z;
+            // one word per lane: the address path is paid per byte each lane
+            // asks for, repeats included, and two 16-byte loads per lane of
+            // the rows in the MFMA layout would ask 2 KiB for 128 bytes
             const float* gam = reinterpret_cast<const float*>(rec + R::GAM);
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                st.gm[t] = *reinterpret_cast<const f4*>(gam + RPW * wave + 16 * t + 4 * lg);
+            st.gm = gam[RPW * wave + (lane & (RPW - 1))];
         } else if (part == 1) {
             const E* qr = reinterpret_cast<const E*>(rec + R::QH);
 #pragma unroll
@@ -954,7 +968,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
     };
 
     // one chunk of the chain; `nx` / `gn` receive the loads of a later chunk
-    auto compute = [&](const Stage& st, Stage& nx, int gn) {
+    auto compute = [&](const Stage& st, Stage& nx, int gn, int gc) {
         // (1) X = W S and O = (Gamma.Q) S for tokens 16w..16w+15, every tile
         f4 X[TW], O[TW];
 #pragma unroll
@@ -980,6 +994,14 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
                 X[c] = M::mma(st.w[ks], bS[c][ks], X[c]);
                 O[c] = M::mma(st.q[ks], bS[c][ks], O[c]);
             }
+        // gamma of state rows 16t + 4lg + i from the lanes that loaded them
+        // (needed in (4); the exchange rides under the barrier below)
+        f4 gmv[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                gmv[t][i] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * t + 4 * lg + i) << 2, __float_as_int(st.gm)));
         __builtin_amdgcn_sched_barrier(0);
         load_part(nx, gn, 1);
         __builtin_amdgcn_sched_barrier(0);
@@ -1004,7 +1026,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
                 f4 acc = {0.f, 0.f, 0.f, 0.f};
                 acc = M::mma(st.k[t][0], bU0, acc);
                 acc = M::mma(st.k[t][1], bU1, acc);
-                S[c][t] = st.gm[t] * S[c][t] + acc;
+                S[c][t] = gmv[t] * S[c][t] + acc;
                 M::store4(s_S + (16 * c + lm) * SP + RPW * wave + 16 * t + 4 * lg, S[c][t]);
             }
         }
@@ -1012,8 +1034,10 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
         load_part(nx, gn, 3);
         __builtin_amdgcn_sched_barrier(0);
         // outputs: full chunks take the branch-free path
-        const size_t obase = (static_cast<size_t>(st.t0) + 16 * wave + 4 * lg) * ostride + ocol;
-        if (st.len == C) {
+        const int t0 = seq_t0 + C * (gc - g0);
+        const int len = min(C, seq_end - t0);
+        const size_t obase = (static_cast<size_t>(t0) + 16 * wave + 4 * lg) * ostride + ocol;
+        if (len == C) {
 #pragma unroll
             for (int c = 0; c < TW; ++c)
 #pragma unroll
@@ -1023,7 +1047,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
             for (int c = 0; c < TW; ++c)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (16 * wave + 4 * lg + i < st.len) store_out<OBF16>(P.o, obase + i * ostride + 16 * c, O[c][i]);
+                    if (16 * wave + 4 * lg + i < len) store_out<OBF16>(P.o, obase + i * ostride + 16 * c, O[c][i]);
         }
         __syncthreads();
     };
@@ -1066,7 +1090,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
     for (int g = g0; g < g1; g += D) {
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-            if (g + j < g1) compute(st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1));
+            if (g + j < g1) compute(st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1), g + j);
         }
     }
 
