@@ -611,6 +611,16 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
     auto hrec_w = [&](int g, size_t off) {
         return reinterpret_cast<_Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
+    // gamma: one word per lane (a 16-byte load per lane of the four rows in
+    // the accumulator layout asks the address path for 1 KiB per wave for 64
+    // distinct bytes); the lanes then trade them into the tile's rows
+    auto gam_word = [&](int g) { return rec_at(P, h, g, R::GAM)[rb * 16 + (lane & 15)]; };
+    auto gam_rows = [&](float w) {
+        f4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * j + i) << 2, __float_as_int(w)));
+        return r;
+    };
     // The next (earlier) chunk's operands, loaded while the current chunk
     // computes.  A sequence's chunks are consecutive rows of C tokens, so the
     // dO rows of chunk g follow from the sequence's first row and last
@@ -653,7 +663,7 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
     struct Stage {
         h8 kt[NKD], pt[NKC], qt[NKC], wt[NKC];
         u16x4 dO;
-        f4 gam;
+        float gam;                       // gamma of row rb * 16 + lane mod 16
         int len;
     };
     auto run = [&](auto du_c, auto rb_c) {
@@ -661,6 +671,7 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
         auto fetch = [&](Stage& st, int g) {
             const int row0 = row_first + (g - g0) * C, len = g == g1 - 1 ? len_last : C;
             st.len = len;
+            if constexpr (RB) st.gam = gam_word(g);
             if constexpr (DU) {              // waves 0..3: dU' row block mb, and the dO tile (threads 0..4C-1)
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) st.kt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKT) + afrag_off(mb, kb, NKD, lane));
@@ -676,7 +687,6 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
                     st.qt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FQHT) + afrag_off(rb, kb, NKC, lane));
                     st.wt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FWT) + afrag_off(rb, kb, NKC, lane));
                 }
-                st.gam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
             }
         };
         auto step = [&](const Stage& cur, Stage& nxt, int g) {
@@ -689,6 +699,8 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
             if constexpr (RB) put_btile(sdS, KPD, rb * 16, dS);
             __syncthreads();
             fetch(nxt, max(g - 1, g0));          // unconditional (past the start: re-reads the first chunk)
+            f4 gv = zero4();
+            if constexpr (RB) gv = gam_rows(cur.gam);
             // dU' = Kt dS + P^T dO   (P^T[m][k] = P[k][m], zero for k < m); waves 4..7
             // meanwhile write dS to the record as 16-byte row words
             if constexpr (DU) {
@@ -709,7 +721,7 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdPar
             // chunk writes dS and its own dO buffer before its first barrier, and
             // dU' after it.
             if constexpr (RB) {
-                f4 x = dS * cur.gam, y = zero4();
+                f4 x = dS * gv, y = zero4();
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb) {
                     x = mfma16(cur.qt[kb], bfrag(sdO, KPC, kb), x);
@@ -762,6 +774,16 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdPa
     auto hrec_w = [&](int g, size_t off) {
         return reinterpret_cast<_Float16*>(P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes + off);
     };
+    // gamma: one word per lane (a 16-byte load per lane of the four rows in
+    // the accumulator layout asks the address path for 1 KiB per wave for 64
+    // distinct bytes); the lanes then trade them into the tile's rows
+    auto gam_word = [&](int g) { return rec_at(P, h, g, R::GAM)[rb * 16 + (lane & 15)]; };
+    auto gam_rows = [&](float w) {
+        f4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[i] = __int_as_float(__builtin_amdgcn_ds_bpermute((4 * j + i) << 2, __float_as_int(w)));
+        return r;
+    };
     if (wave == kChainWaves) {
         int* sink = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(lds) + Chain16B<DK>::sink);
         auto touch = [&](int gp) {
@@ -786,11 +808,13 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdPa
     // still in flight instead of draining every load each chunk.
     struct Stage {
         h8 w[NKD], ktt[NKC];
-        f4 u, gam;
+        f4 u;
+        float gam;                       // gamma of row rb * 16 + lane mod 16
     };
     auto run = [&](auto du_c, auto rb_c) {
         constexpr bool DU = decltype(du_c)::value, RB = decltype(rb_c)::value;
         auto fetch = [&](Stage& st, int g) {
+            if constexpr (RB) st.gam = gam_word(g);
             if constexpr (DU) {
 #pragma unroll
                 for (int kb = 0; kb < NKD; ++kb) st.w[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FW) + afrag_off(mb, kb, NKD, lane));
@@ -800,13 +824,14 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdPa
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)
                     st.ktt[kb] = *reinterpret_cast<const h8*>(hrec(g, R::FKTT) + afrag_off(rb, kb, NKC, lane));
-                st.gam = *reinterpret_cast<const f4*>(rec_at(P, h, g, R::GAM) + rb * 16 + 4 * j);
             }
         };
         auto step = [&](const Stage& cur, Stage& nxt, int g) {
             if constexpr (RB) put_btile(sS, KPD, rb * 16, S);
             __syncthreads();
             fetch(nxt, min(g + 2, g1 - 1));      // unconditional (past the end: re-reads the last chunk)
+            f4 gv = zero4();
+            if constexpr (RB) gv = gam_rows(cur.gam);
             // U' = U - W S; waves 4..7 meanwhile write S to the record as 16-byte row words
             if constexpr (DU) {
                 f4 x = zero4();
@@ -824,7 +849,7 @@ __global__ __launch_bounds__(kChain16Threads) void bwd_ckpt16_kernel(const BwdPa
             // writes S before its first barrier (every read of S is before this
             // chunk's second one) and U' after it.
             if constexpr (RB) {
-                f4 sv = S * cur.gam;
+                f4 sv = S * gv;
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb) sv = mfma16(cur.ktt[kb], bfrag(sU, KPC, kb), sv);
                 S = sv;
