@@ -35,6 +35,8 @@
 // as e^{b_r - ref} * e^{ref - b_s} around a reference token in the middle of
 // each 16-token block ("chunk-wise normalization", same section), so every
 // factor is bounded by the decay over at most 8 tokens.
+#include <type_traits>
+
 #include "kda_chunk.h"
 #include "kda_common.h"
 
@@ -928,7 +930,10 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
     // about 64 B per clock, so issuing a whole stage at once would stall the
     // wave for ~1000 clocks while the matrix cores idle.  sched_barrier keeps
     // the compiler from regrouping them.
-    auto load_part = [&](Stage& st, int g, int part) {
+    // P2: the wave's rows reach tokens 32..63 of P (waves 2 and 3; the
+    // second P fragment of waves 0 and 1 lies above the diagonal)
+    auto load_part = [&](auto p2c, Stage& st, int g, int part) {
+        constexpr bool P2 = decltype(p2c)::value;
         const unsigned char* rec = recs + static_cast<size_t>(g) * gstride;
         if (part == 0) {
             // W and U head the chain of the next chunk; gamma and the chunk's
@@ -959,16 +964,17 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
         } else {
             const E* pr = reinterpret_cast<const E*>(rec + R::P);
             st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
-            st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
+            if constexpr (P2) st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
         }
     };
-    auto load = [&](Stage& st, int g) {
+    auto load = [&](auto p2c, Stage& st, int g) {
 #pragma unroll
-        for (int part = 0; part < 4; ++part) load_part(st, g, part);
+        for (int part = 0; part < 4; ++part) load_part(p2c, st, g, part);
     };
 
     // one chunk of the chain; `nx` / `gn` receive the loads of a later chunk
-    auto compute = [&](const Stage& st, Stage& nx, int gn, int gc) {
+    auto compute = [&](auto p2c, const Stage& st, Stage& nx, int gn, int gc) {
+        constexpr bool P2 = decltype(p2c)::value;
         // (1) X = W S and O = (Gamma.Q) S for tokens 16w..16w+15, every tile
         f4 X[TW], O[TW];
 #pragma unroll
@@ -985,7 +991,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
                 bS[c][ks] = M::load4x2(sb, sb + 16);
             }
         __builtin_amdgcn_sched_barrier(0);
-        load_part(nx, gn, 0);
+        load_part(p2c, nx, gn, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -1003,14 +1009,14 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
             for (int i = 0; i < 4; ++i)
                 gmv[t][i] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * t + 4 * lg + i) << 2, __float_as_int(st.gm)));
         __builtin_amdgcn_sched_barrier(0);
-        load_part(nx, gn, 1);
+        load_part(p2c, nx, gn, 1);
         __builtin_amdgcn_sched_barrier(0);
         // (2) U' = U - W S, shared through LDS
 #pragma unroll
         for (int c = 0; c < TW; ++c) M::store4(s_U + (16 * c + lm) * UP + 16 * wave + 4 * lg, M::tof4(st.u[c]) - X[c]);
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        load_part(nx, gn, 2);
+        load_part(p2c, nx, gn, 2);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < TW; ++c) {
@@ -1019,7 +1025,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
             const V bU1 = M::load4x2(ub + 32, ub + 48);
             // (3) O += Tril(...) U'  (tokens above this wave's rows are zero in P)
             O[c] = M::mma(st.p[0], bU0, O[c]);
-            if (wave >= 2) O[c] = M::mma(st.p[1], bU1, O[c]);
+            if constexpr (P2) O[c] = M::mma(st.p[1], bU1, O[c]);
             // (4) S <- Diag(gamma) S + ((gamma/Gamma).K)^T U'
 #pragma unroll
             for (int t = 0; t < TPW; ++t) {
@@ -1031,7 +1037,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        load_part(nx, gn, 3);
+        load_part(p2c, nx, gn, 3);
         __builtin_amdgcn_sched_barrier(0);
         // outputs: full chunks take the branch-free path
         const int t0 = seq_t0 + C * (gc - g0);
@@ -1080,19 +1086,24 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
         return;
     }
     // Ring loads are unconditional (clamped to the last chunk; the surplus
-    // loads at the tail are never used) so that the loop body is straight-line
-    // code and the hardware wait counters never have to drain the ring.
-    Stage st[D];
-    if (g0 < g1) {
+    // loads at the tail are never used) and each wave role runs its own copy
+    // of the loop, so the loop body is straight-line code and the hardware
+    // wait counters never have to drain the ring.
+    auto run = [&](auto p2c) {
+        Stage st[D];
+        if (g0 < g1) {
 #pragma unroll
-        for (int j = 0; j < D - 1; ++j) load(st[j], min(g0 + j, g1 - 1));
-    }
-    for (int g = g0; g < g1; g += D) {
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-            if (g + j < g1) compute(st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1), g + j);
+            for (int j = 0; j < D - 1; ++j) load(p2c, st[j], min(g0 + j, g1 - 1));
         }
-    }
+        for (int g = g0; g < g1; g += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (g + j < g1) compute(p2c, st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1), g + j);
+            }
+        }
+    };
+    if (wave >= 2) run(std::true_type{});
+    else run(std::false_type{});
 
     if (P.final_state) {
 #pragma unroll
