@@ -201,6 +201,12 @@ __device__ __forceinline__ int frag_k(int j, int e) { return e < 4 ? 4 * j + e :
 
 __device__ __forceinline__ size_t frag_off(int f, int lane) { return (static_cast<size_t>(f) * 64 + lane) * 8; }
 
+// P (C x C, lower triangular) in the record: fragment 2I + h holds token rows
+// 16I..16I+15 and columns 32h..32h+31, and the fragments 1 and 3 (rows below
+// 32, columns from 32 on) are all zero, so only the other six are stored.
+constexpr int kPFrags = 6;
+__device__ __forceinline__ int p_slot(int f) { return f == 0 ? 0 : f == 2 ? 1 : f - 2; }
+
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
@@ -319,7 +325,7 @@ struct Rec {
     static constexpr size_t W = QH + sizeof(E) * C * DK;
     static constexpr size_t KTT = W + sizeof(E) * C * DK;
     static constexpr size_t P = KTT + sizeof(E) * DK * C;
-    static constexpr size_t UT = P + sizeof(E) * C * C;
+    static constexpr size_t UT = P + sizeof(E) * kPFrags * 512;
     static constexpr size_t GAM = UT + sizeof(E) * DV * C;
     static constexpr size_t END = GAM + 4 * DK;
 };
@@ -655,7 +661,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
                 pv[e] = s0 <= r ? accP[2 * ks][e] : 0.f;
                 pv[4 + e] = s1 <= r ? accP[2 * ks + 1][e] : 0.f;
             }
-            M::store8(pout + frag_off(2 * I + ks, lane), pv);
+            if (ks == 0 || I >= 2) M::store8(pout + frag_off(p_slot(2 * I + ks), lane), pv);
         }
     }
 
@@ -963,8 +969,8 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
             }
         } else {
             const E* pr = reinterpret_cast<const E*>(rec + R::P);
-            st.p[0] = M::load8(pr + frag_off(2 * wave, lane));
-            if constexpr (P2) st.p[1] = M::load8(pr + frag_off(2 * wave + 1, lane));
+            st.p[0] = M::load8(pr + frag_off(p_slot(2 * wave), lane));
+            if constexpr (P2) st.p[1] = M::load8(pr + frag_off(p_slot(2 * wave + 1), lane));
         }
     };
     auto load = [&](auto p2c, Stage& st, int g) {
@@ -1205,9 +1211,10 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.off_first = off; off = align256(off + 4 * (static_cast<size_t>(p.N) + 1));
     p.off_order = off; off = align256(off + 4 * static_cast<size_t>(p.N));
     p.off_table = off; off = align256(off + 16 * static_cast<size_t>(p.gmax));
-    // per (head, chunk) record: qh, w, ktt, p, ut (operand type), gam (fp32)
+    // per (head, chunk) record: qh, w, ktt, p (its six lower fragments), ut
+    // (operand type), gam (fp32)
     if (chunk_size == C)
-        p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(C) * C * p.eb +
+        p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(kPFrags) * 512 * p.eb +
                                static_cast<size_t>(C) * Dv * p.eb + static_cast<size_t>(Dk) * 4);
     else
         p.rec_bytes = align256(generic_record_bytes(Dk, Dv, chunk_size));

@@ -51,7 +51,7 @@ def test_workspace_size_plan():
     f = kda.kda_chunk_fwd_workspace_bytes
     n = f(2, 4096, 8, 128, 128, False, 0, 64, kda.KDA_DTYPE_BF16)
     gh = 2 * 64 * 8
-    per = 64 * 128 * 2 * 3 + 64 * 64 * 2 + 128 * 64 * 2 + 128 * 4   # qh, w, ktt, p, ut (fp16), gam
+    per = 64 * 128 * 2 * 3 + 6 * 16 * 32 * 2 + 128 * 64 * 2 + 128 * 4   # qh, w, ktt, p (6 fragments), ut (fp16), gam
     assert gh * per <= n < gh * per + 64 * 1024
     assert f(2, 4096, 8, 128, 128, False, 0, 64, kda.KDA_DTYPE_F32) > n
     # packed: chunk capacity is ceil(T/64) + N
