@@ -1262,7 +1262,10 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
 
     // ---- key side ----
     const int tnb = wave & 3, tmb0 = wave >> 2;     // C x C tiles: column block tnb, row blocks tmb0, tmb0 + 2
-    const int nb = wave % NB, cmb0 = wave / NB;     // C x d_k tiles: column block nb, row blocks cmb0 + r MSTEP
+    // C x d_k tiles: column block nb, row blocks cmb0 + r MSTEP (with one
+    // column block per wave, cmb0 is 0 at compile time, so the triangular
+    // skips inside the products fold away instead of branching)
+    const int nb = wave % NB, cmb0 = NB == NW ? 0 : wave / NB;
     // dW -> sW; the gate, then b = cumsum(log2 alpha) as in the preparation
     // kernel; Kh = 2^b K, Kb = 2^-b K
     {
