@@ -906,6 +906,15 @@ template <int DK> struct GradTasks {
     static_assert(NB == 4 || NB == 8, "d_k of 64 or 128");
 };
 
+// dA / R tiles of wave w in the gradient kernel: (mb, nb) of its first and
+// second tile, 4 bits each.  Tile (mb, nb) below the diagonal costs
+// 8 + nb + 1 product steps; the spread gives the waves sharing a SIMD
+// (w, w + 4) 28, 28, 22, 22 steps; tiles above the diagonal are only zeroed.
+constexpr unsigned grad_tiles(int w) {
+    constexpr unsigned t[8] = {0x0010, 0x2030, 0x3301, 0x2202, 0x1103, 0x2112, 0x3113, 0x3223};
+    return t[w];
+}
+
 template <int DK> struct GradB {
     static constexpr int LK = Ld<DK>::value;
     // key side: Kh, Kb, dW | three C x C tiles | beta, dbeta rows, Kt.dKt column sums, dgamma, rowsum(dZ.V)
@@ -1299,44 +1308,61 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
         for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, dt[r] * sBeta[tnb * 16 + i]);
     }
     __syncthreads();
-    // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m)
+    // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m).  One copy per
+    // value of tmb0, so the triangular skips are known at compile time.
     {
-        f4 y1[2] = {zero4(), zero4()};
-        mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, tmb0, 2,
-                                     [](int mb, int gg) { return gg >= mb; }, y1);
+        auto y1_rows = [&](auto m0c) {
+            constexpr int M0 = decltype(m0c)::value;
+            f4 y1[2] = {zero4(), zero4()};
+            mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, M0, 2,
+                                         [](int mb, int gg) { return gg >= mb; }, y1);
 #pragma unroll
-        for (int r = 0; r < 2; ++r) store_tile(sY + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
+            for (int r = 0; r < 2; ++r) store_tile(sY + (M0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
+        };
+        if (tmb0 == 0) y1_rows(std::integral_constant<int, 0>{});
+        else y1_rows(std::integral_constant<int, 1>{});
     }
     __syncthreads();
-    // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX.
-    // Tile (mb, nb) below the diagonal costs 8 + nb + 1 product steps; two
-    // tiles per wave, spread so the waves sharing a SIMD (w, w + 4) carry
-    // 28, 28, 22, 22 steps; the six tiles above the diagonal are only zeroed.
+    // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX,
+    // two tiles per wave (grad_tiles).  The tiles are fixed at compile time
+    // (one copy of the phase per wave), so the tile tests and the triangular
+    // skips fold away.
     {
-        // (mb, nb) of each wave's first and second tile, 4 bits each
-        constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x3301, 0x2202, 0x1103, 0x2112, 0x3113, 0x3223};
+        auto tiles = [&](auto wc) {
+            constexpr int WV = decltype(wc)::value;
 #pragma unroll
-        for (int slot = 0; slot < 2; ++slot) {
-            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
-            const int mb = tt >> 4, nb = tt & 15;
-            f4 dr = zero4();
-            if (nb <= mb) {
-                // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
-                f4 ya[1] = {zero4()}, rr[1] = {zero4()};
-                mm_rows<1, GC, true, true>(sY, LC, 1, sT + nb * 16 * LC, 1, LC, mb, 1,
-                                           [nb](int, int gg) { return gg <= nb; }, ya);
-                mm_rows<1, GK, true, true>(sKh, LK, 1, sKb + nb * 16 * LK, 1, LK, mb, 1,
-                                           [](int, int) { return true; }, rr);
+            for (int slot = 0; slot < 2; ++slot) {
+                const unsigned tt = (grad_tiles(WV) >> (8 * (1 - slot))) & 0xff;
+                const int mb = tt >> 4, nb = tt & 15;
+                f4 dr = zero4();
+                if (nb <= mb) {
+                    // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
+                    f4 ya[1] = {zero4()}, rr[1] = {zero4()};
+                    mm_rows<1, GC, true, true>(sY, LC, 1, sT + nb * 16 * LC, 1, LC, mb, 1,
+                                               [nb](int, int gg) { return gg <= nb; }, ya);
+                    mm_rows<1, GK, true, true>(sKh, LK, 1, sKb + nb * 16 * LK, 1, LK, mb, 1,
+                                               [](int, int) { return true; }, rr);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
-                    const float da = s2 < r ? -ya[0][e] : 0.f;
-                    const float part = row16_sum(da * rr[0][e]);
-                    if (i == 0) sRow[wave * C + r] += part;
-                    dr[e] = sBeta[r] * da;
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+                        const float da = s2 < r ? -ya[0][e] : 0.f;
+                        const float part = row16_sum(da * rr[0][e]);
+                        if (i == 0) sRow[wave * C + r] += part;
+                        dr[e] = sBeta[r] * da;
+                    }
                 }
+                store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
             }
-            store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
+        };
+        switch (wave) {
+            case 0: tiles(std::integral_constant<int, 0>{}); break;
+            case 1: tiles(std::integral_constant<int, 1>{}); break;
+            case 2: tiles(std::integral_constant<int, 2>{}); break;
+            case 3: tiles(std::integral_constant<int, 3>{}); break;
+            case 4: tiles(std::integral_constant<int, 4>{}); break;
+            case 5: tiles(std::integral_constant<int, 5>{}); break;
+            case 6: tiles(std::integral_constant<int, 6>{}); break;
+            default: tiles(std::integral_constant<int, 7>{}); break;
         }
     }
     __syncthreads();
