@@ -1373,7 +1373,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
         f4 dy[RW];
 #pragma unroll
         for (int r = 0; r < RW; ++r) dy[r] = dKb[r] = zero4();
-        mm_rows<RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+        mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
                                       [](int mb, int gg) { return gg >= mb; }, dy);
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
@@ -1387,7 +1387,7 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
             }
         }
         // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
-        mm_rows<RW, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
+        mm_rows_k<ABF16, RW, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
                                      [](int mb, int gg) { return gg <= mb; }, dKh);
     }
     __syncthreads();
@@ -1409,11 +1409,11 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
     f4 dQh[RW];
 #pragma unroll
     for (int r = 0; r < RW; ++r) dQh[r] = acc[r];
-    mm_rows<RW, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
+    mm_rows_k<ABF16, RW, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
                                  [](int mb, int gg) { return gg <= mb; }, dQh);
-    mm_rows<RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+    mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
                                   [](int mb, int gg) { return gg >= mb; }, dKb);
-    mm_rows<RW, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, cmb0, MSTEP,
+    mm_rows_k<ABF16, RW, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, cmb0, MSTEP,
                                   [](int mb, int gg) { return gg >= mb; }, dKb);
     __syncthreads();
 

@@ -351,6 +351,64 @@ __device__ __forceinline__ void mm_rows(const float* pa, int am, int ak, const f
     }
 }
 
+// mm_rows on the bf16 matrix cores with fp32 operands split in two: every
+// operand x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (|x - hi - lo| <=
+// 2^-18 |x|, fp32's exponent range), and A B ~ Ah Bh + Ah Bl + Al Bh (the
+// dropped Al Bl is below 2^-16 of each term), accumulated in fp32.  One
+// 16x16x32 step takes two 16-deep groups: lane group j feeds the reduction
+// indices 16g + 4j + e and 16(g + 1) + 4j + e (e = 0..3) that the fp32 reads
+// of mm_rows already hand it, so the operands are read exactly as there.  G
+// is even; a pair of groups is taken when either is in range, so the skipped
+// products must be of stored zeros.
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ void split_bf16(const f4& x0, const f4& x1, bf8& hi, bf8& lo) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const __bf16 h = static_cast<__bf16>(x);
+        hi[e] = h;
+        lo[e] = static_cast<__bf16>(x - static_cast<float>(h));
+    }
+}
+template <int R, int G, bool AV, bool BV, typename Range>
+__device__ __forceinline__ void mm_rows_x3(const float* pa, int am, int ak, const float* pb, int bk, int bn,
+                                           int mb0, int mstep, Range inrange, f4 (&acc)[R]) {
+    static_assert(G % 2 == 0, "pairs of 16-deep groups");
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    pa += i * am + 4 * j * ak;
+    pb += 4 * j * bk + i * bn;
+#pragma unroll
+    for (int g = 0; g < G; g += 2) {
+        bool in[R], any = false;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            in[r] = inrange(mb0 + r * mstep, g) || inrange(mb0 + r * mstep, g + 1);
+            any |= in[r];
+        }
+        if (!any) continue;
+        bf8 bh, bl;
+        split_bf16(grp4<BV>(pb + 16 * g * bk, bk), grp4<BV>(pb + 16 * (g + 1) * bk, bk), bh, bl);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (!in[r]) continue;
+            const float* p = pa + 16 * (mb0 + r * mstep) * am + 16 * g * ak;
+            bf8 ah, al;
+            split_bf16(grp4<AV>(p, ak), grp4<AV>(p + 16 * ak, ak), ah, al);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc[r], 0, 0, 0);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc[r], 0, 0, 0);
+            acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc[r], 0, 0, 0);
+        }
+    }
+}
+
+// mm_rows, or mm_rows_x3 when SPLIT
+template <bool SPLIT, int R, int G, bool AV, bool BV, typename Range>
+__device__ __forceinline__ void mm_rows_k(const float* pa, int am, int ak, const float* pb, int bk, int bn,
+                                          int mb0, int mstep, Range inrange, f4 (&acc)[R]) {
+    if constexpr (SPLIT) mm_rows_x3<R, G, AV, BV>(pa, am, ak, pb, bk, bn, mb0, mstep, inrange, acc);
+    else mm_rows<R, G, AV, BV>(pa, am, ak, pb, bk, bn, mb0, mstep, inrange, acc);
+}
+
 // Two products that share their B operand: acc0 += A0 B, acc1 += A1 B over
 // G groups of 16 reduction indices (pa0, pa1 at their tile's first row).
 template <int G, bool AV, bool BV>
