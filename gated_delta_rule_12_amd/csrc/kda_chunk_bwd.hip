@@ -40,7 +40,9 @@
 // cores (16x16x4) and every intermediate is stored in fp32.  With bf16
 // activations the two state passes and the value-side contractions take
 // fp16 operands (fp32 accumulation) and the record keeps S, dS_next, U', dU'
-// and those operands in fp16; the key-side products stay fp32.  Under the
+// and those operands in fp16; the key-side products keep fp32 operands (the
+// five C x d_k ones split each into bf16 hi + lo for the bf16 matrix cores,
+// which keeps fp32's exponent range and ~2^-16 relative accuracy).  Under the
 // decay precondition of the forward (per channel, < e^10 over any 8 tokens,
 // so < e^80 over a chunk) Gamma = 2^b and 1/Gamma stay fp32-normal over a
 // chunk, so Kh = Gamma.K and Kb = K/Gamma are formed directly.

@@ -216,7 +216,8 @@ KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, in
  * aligned; dgate and dbeta 4-byte aligned.  Accumulation is fp32
  * throughout; with fp32 activations every operand is fp32, with bf16 the
  * products of the two state passes and of the value-side contractions take
- * fp16 operands (the key-side products stay fp32).
+ * fp16 operands; the key-side products keep fp32 operands (the largest run
+ * on the bf16 matrix cores with each operand split into bf16 hi + lo).
  */
 KDA_API kda_status kda_chunk_bwd(const void *q, const void *k, const void *v,
                          const void *gate, kda_gate gate_kind, const float *beta,
