@@ -460,6 +460,69 @@ def main():
             del wsc
         var["chunk_note"] = ("chunk sizes 32 and 128 take the generic path (every product on the fp32 "
                              "matrix cores, fp32 record); chunk 64 is the main line")
+        del o, sT, ws, fi
+        torch.cuda.empty_cache()
+        # the small dense workload (~0.1 GB, fits the 256 MB memory-side cache):
+        # back to back ("hot"), and with a 512 MiB device write before each call
+        # so that none of its inputs or records are still cached ("flushed")
+        w1 = synth.WORKLOADS[1]
+        f1 = synth.workload_inputs(1, device=dev)
+        o1 = torch.empty((w1.B, w1.T, w1.H, w1.Dv), dtype=torch.bfloat16, device=dev)
+        s1 = torch.empty((w1.B, w1.H, w1.Dk, w1.Dv), dtype=torch.float32, device=dev)
+        ws1 = torch.empty(kda.kda_chunk_fwd_workspace_bytes(w1.B, w1.T, w1.H, w1.Dk, w1.Dv, False, 0, 64,
+                                                            torch.bfloat16), dtype=torch.uint8, device=dev)
+
+        def fwd1():
+            kda.kda_chunk_fwd(f1["q"], f1["k"], f1["v"], f1["alpha"], f1["beta"], final_state=s1, o=o1,
+                              out_dtype=torch.bfloat16, workspace=ws1)
+        hot = time_events(fwd1, 50, 5)
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for n, (a, b) in enumerate(ev):
+            scrub.fill_(n & 255)
+            a.record()
+            fwd1()
+            b.record()
+        torch.cuda.synchronize()
+        cold = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+        u1 = w1.B * w1.H * w1.T
+        b1 = FWD_BYTES_PER_TOKEN_HEAD * u1 + w1.B * w1.H * w1.Dk * w1.Dv * 4
+        var["fwd_B2_H8_T4096"] = {
+            "unit": "token-heads/s", "workload": w1.name, "algorithmic_bytes_per_launch": b1,
+            "hot": {"value": round(u1 / (hot / 1e3), 1), "fwd_ms": round(hot, 4),
+                    "hbm_frac": round(b1 / (hot / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "flushed": {"value": round(u1 / (cold / 1e3), 1), "fwd_ms": round(cold, 4),
+                        "hbm_frac": round(b1 / (cold / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "note": "flushed: a 512 MiB device write before each timed call evicts the 256 MB memory-side cache"}
+        del f1, o1, s1, ws1, scrub
+        torch.cuda.empty_cache()
+        # the packed variable-length workload: 64 sequences of 512..32768 tokens, 16 heads
+        w4 = synth.WORKLOADS[4]
+        f4 = synth.workload_inputs(4, device=dev)
+        cu = f4["cu_seqlens"]
+        T4 = f4["q"].shape[1]
+        N4 = cu.numel() - 1
+        o4 = torch.empty((1, T4, w4.H, w4.Dv), dtype=torch.bfloat16, device=dev)
+        s4 = torch.empty((N4, w4.H, w4.Dk, w4.Dv), dtype=torch.float32, device=dev)
+        ws4 = torch.empty(kda.kda_chunk_fwd_workspace_bytes(1, T4, w4.H, w4.Dk, w4.Dv, True, N4, 64,
+                                                            torch.bfloat16), dtype=torch.uint8, device=dev)
+
+        def fwd4():
+            kda.kda_chunk_fwd(f4["q"], f4["k"], f4["v"], f4["alpha"], f4["beta"],
+                              initial_state=f4["initial_state"], final_state=s4, cu_seqlens=cu, o=o4,
+                              out_dtype=torch.bfloat16, workspace=ws4)
+        ms4 = time_events(fwd4, 5, 2)
+        u4 = w4.H * T4
+        b4 = FWD_BYTES_PER_TOKEN_HEAD * u4 + 2 * N4 * w4.H * w4.Dk * w4.Dv * 4
+        ach4 = b4 / (ms4 / 1e3) / 1e9
+        var["fwd_varlen"] = {"value": round(u4 / (ms4 / 1e3), 1), "unit": "token-heads/s", "fwd_ms": round(ms4, 4),
+                             "workload": w4.name, "tokens": T4, "sequences": N4,
+                             "roofline": {"bound": "hbm", "achieved": round(ach4, 1), "peak": HBM_PEAK_GBPS,
+                                          "unit": "GB/s", "frac": round(ach4 / HBM_PEAK_GBPS, 4),
+                                          "algorithmic_bytes_per_launch": b4}}
+        del f4, o4, s4, ws4, cu
+        torch.cuda.empty_cache()
+        fi = synth.workload_inputs(2, device=dev)
         var["bwd"] = bench_bwd(kda, synth, torch, fi, wf, 5, 2)
         out["variants"] = var
     traffic = measured_traffic()
