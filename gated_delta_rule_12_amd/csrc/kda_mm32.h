@@ -1,8 +1,9 @@
 // Matrix-core building blocks shared by the chunkwise backward and the
 // chunk-size-generic forward (gfx950): 16x16 fp32 MFMA tiles over LDS
-// operands with arbitrary strides, register-staged global -> LDS copies,
-// DPP row sums, the XCD-aware chain grid, fp16 MFMA fragments and L2
-// prefetch touches.
+// operands with arbitrary strides, the same products on the bf16 matrix
+// cores with fp32 operands split into bf16 hi + lo, register-staged
+// global -> LDS copies, DPP row sums, the XCD-aware chain grid, fp16 MFMA
+// fragments and L2 prefetch touches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -34,8 +35,11 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // the indices 4j..4j+3 in the group's four steps (any assignment gives the
 // same product when both operands follow it), so an operand that is
 // contiguous along the reduction (AV: ak == 1, BV: bk == 1) is read with one
-// 16-byte LDS load per group instead of four.  Each group's operands are
-// loaded one group ahead of its products.
+// 16-byte LDS load per group instead of four.  mm keeps the operands of
+// the next two groups in flight ahead of each group's products; mm_rows and
+// mm_two read a group's operands just before its products and leave their
+// interleaving to the compiler (with two waves per SIMD that measured
+// faster than forcing the reads ahead).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
