@@ -874,6 +874,7 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
     constexpr int SP = DK + 8;            // LDS row stride of the state operand
     constexpr int UP = C + 8;             // LDS row stride of U'
     static_assert(NTV >= 1 && NTV * 16 * TW == DV, "value tiling");
+    static_assert((RPW & (RPW - 1)) == 0 && RPW <= 64, "a wave's gamma rows fit one word per lane");
 
     // Workgroups are handed to the 8 XCDs round-robin; keep the NTV
     // workgroups of one (sequence, head) on the same XCD so they share its L2.

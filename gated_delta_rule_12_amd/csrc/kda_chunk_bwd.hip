@@ -1369,7 +1369,9 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
     }
     __syncthreads();
 
-    // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh)
+    // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh).  (T, dR
+    // and, below, M hold exact zeros above their diagonals, which the split
+    // products' pair-wise skipping with bf16 activations relies on.)
     f4 dKh[RW], dKb[RW];
     {
         f4 dy[RW];
