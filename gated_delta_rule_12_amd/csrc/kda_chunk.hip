@@ -566,7 +566,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     // later block I, and handed over through LDS.
     V ra[KS], rq[KS];             // row operands, rebased at token 16I+7
     V Dc[KS];                     // column operand of the diagonal block
-    {
+    // one copy per block index I (= the wave), so the tests of the later
+    // blocks fold at compile time and the column operands of blocks that do
+    // not exist take no registers (181 instead of 247)
+    auto derive = [&](auto ic) {
+        constexpr int I = decltype(ic)::value;
         E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
         auto fac4 = [&](int row, int ks, int half) {
             return *reinterpret_cast<const f4*>(s_fac + row * DK + 32 * ks + 16 * half + 4 * lg);
@@ -612,6 +616,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
             M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
         }
+        };
+    switch (I) {
+        case 0: derive(std::integral_constant<int, 0>{}); break;
+        case 1: derive(std::integral_constant<int, 1>{}); break;
+        case 2: derive(std::integral_constant<int, 2>{}); break;
+        default: derive(std::integral_constant<int, 3>{}); break;
     }
     // v is first needed in (e); loading it here keeps it out of the
     // registers of the phases above
