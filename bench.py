@@ -13,7 +13,7 @@ token-head throughput (B*H*T per second of kda_chunk_fwd), and the decode
 step is reported as achieved HBM GB/s.
 
 Prints ONE JSON line.  Flags:
-  --gpus N --steps K --warmup W       (N must be 1: this build is one GPU)
+  --gpus N --steps K --warmup W       (N must be 1: the benchmark runs on one GPU)
   --no-cpu-baseline                   skip the oracle timing
   --only fwd|decode|bwd               time one part only (profiler runs; bwd = the
                                       chunkwise backward on the forward's shape)
@@ -278,7 +278,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, "
+        print(f"bench.py: the benchmark runs on exactly one GPU (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE={world}); a multi-GPU run is not part of it.", file=sys.stderr)
         sys.exit(2)
 
