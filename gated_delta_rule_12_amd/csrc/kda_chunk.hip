@@ -192,12 +192,11 @@ template <> struct Load8<false> {
 // the 16 rows x 32 reduction indices one MFMA step consumes, laid out as
 // 64 lanes x 8 elements, so one wavefront load moves 1 KiB of contiguous
 // bytes.  Within a fragment, lane (m, j) (m = lane % 16, j = lane / 16)
-// holds row m at reduction indices frag_k(j, e), e = 0..7: two runs of four,
-// 4j..4j+3 and 16+4j..16+4j+3.  Any bijection onto the 32 indices gives the
+// holds row m at reduction indices frag_k(j, e) = e < 4 ? 4j + e : 12 + 4j + e,
+// e = 0..7: two runs of four, 4j..4j+3 and 16+4j..16+4j+3.  Any bijection onto the 32 indices gives the
 // same product as long as both operands of an MFMA use it; this one lets a
 // 16x16 accumulator tile pair (rows 4j..4j+3 of each tile in lane (m, j))
 // be written as a fragment without moving data between lanes.
-__device__ __forceinline__ int frag_k(int j, int e) { return e < 4 ? 4 * j + e : 12 + 4 * j + e; }
 
 __device__ __forceinline__ size_t frag_off(int f, int lane) { return (static_cast<size_t>(f) * 64 + lane) * 8; }
 
@@ -207,8 +206,6 @@ __device__ __forceinline__ size_t frag_off(int f, int lane) { return (static_cas
 constexpr int kPFrags = 6;
 __device__ __forceinline__ int p_slot(int f) { return f == 0 ? 0 : f == 2 ? 1 : f - 2; }
 
-__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 
 // ---------------------------------------------------------------------------
 // plan_kernel: chunk table, per-sequence first chunk, longest-first order.
@@ -366,31 +363,26 @@ struct PrepLds {
     static constexpr int RD = CMax<C * ATP * 4, C * TPP * (int)sizeof(E)>::value;
     // small: beta [64]
     static constexpr int RS = C * 4;
-    // the block totals [4][DK] and decay factors [16][DK] live in region d
-    // until A^T is written there
-    static_assert(RD >= 20 * DK * 4, "region d holds the decay tables");
+    // the block totals of the decay [4][DK] live in region d until A^T is
+    // written there
+    static_assert(RD >= 4 * DK * 4, "region d holds the block totals");
     static constexpr int bytes = RA + RB + RC + RD + RS;
 };
 
-// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr by 1, 2,
-// 4, 8; lanes shifted in from outside the row read 0).
-__device__ __forceinline__ float row_shr_f(float x, int n) {
+// Lanes of one 16-lane row hold 16 consecutive tokens.  Returns x of lane
+// (lane ^ 2^p) | (2^p - 1): the last token of the other half of this token's
+// aligned group of 2^(p+1) tokens.  p = 0, 1 stay inside a quad (DPP quad
+// permutes [1,0,3,2] and [3,3,1,1]); p = 2, 3 go through the LDS crossbar.
+__device__ __forceinline__ float other_half_last(int p, float x, int lane) {
     const int xi = __builtin_bit_cast(int, x);
-    int y = 0;
-    switch (n) {
-        case 1: y = __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xf, 0xf, false); break;
-        case 2: y = __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xf, 0xf, false); break;
-        case 4: y = __builtin_amdgcn_update_dpp(0, xi, 0x114, 0xf, 0xf, false); break;
-        default: y = __builtin_amdgcn_update_dpp(0, xi, 0x118, 0xf, 0xf, false); break;
+    int y;
+    if (p == 0) y = __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xf, 0xf, false);
+    else if (p == 1) y = __builtin_amdgcn_update_dpp(0, xi, 0x5F, 0xf, 0xf, false);
+    else {
+        const int src = (lane ^ (1 << p)) | ((1 << p) - 1);
+        y = __builtin_amdgcn_ds_bpermute(src << 2, xi);
     }
     return __builtin_bit_cast(float, y);
-}
-__device__ __forceinline__ float row_scan16(float x) {
-    x += row_shr_f(x, 1);
-    x += row_shr_f(x, 2);
-    x += row_shr_f(x, 4);
-    x += row_shr_f(x, 8);
-    return x;
 }
 
 // (I, J) with J < I -> index into the rescaling table
@@ -435,8 +427,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     E* s_khat = reinterpret_cast<E*>(lds + L::RA + L::RB);              // K-hat [token][channel]
     float* s_AT = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC);
     E* s_Tp = reinterpret_cast<E*>(lds + L::RA + L::RB + L::RC);        // after A^T is dead
-    float* s_tot = s_AT;                                                // [4][DK], until (c)
-    float* s_fac = s_AT + 4 * DK;                                       // [16][DK], until (c)
+    float* s_F = s_AT;                                                  // [4][DK] block totals, until (c)
     float* s_beta = reinterpret_cast<float*>(lds + L::RA + L::RB + L::RC + L::RD);  // [C]
 
     const int tid = threadIdx.x;
@@ -455,7 +446,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
 
     // Lane (lm, lg) owns token r and, in reduction step ks, the channels
     // 32ks + frag_k(lg, e): two runs of four, at 32ks + 4lg and 32ks + 16 + 4lg.
-    auto chan = [&](int ks, int e) { return 32 * ks + frag_k(lg, e); };
 
     // ---- (0) global loads of alpha, k, q, beta (v follows in (b)) ---------------
     // Rows past the chunk's end re-read its last row (always in bounds) and
@@ -463,7 +453,6 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     // used, so the loads carry no branches and nothing waits for them early.
     using R4 = Raw4<F16>;
     const int rl = len - 1;
-    float b[KS][8];
     typename R4::T kraw[KS][2], qraw[KS][2];
     // the gate as given: fp32 alpha or bf16 pre-activation per channel, or one
     // fp32 alpha per token
@@ -490,91 +479,150 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     const float bet_raw = P.beta[static_cast<size_t>(t0 + min(r, rl)) * H + h];
     const float bet = valid ? bet_raw : 0.f;
 
-    // ---- (a) b = inclusive cumsum of log2(alpha) over the chunk's tokens -----
-    // scan over the 16 tokens of this wave's block (lanes of one 16-lane row),
-    // then add the totals of the earlier blocks
-    // log2(alpha) of this lane's elements (0 past the chunk's end), scanned
-    if constexpr (GATE == KDA_GATE_SCALAR) {
-        const float x = row_scan16(valid ? flog2(gscalar) : 0.f);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[ks][e] = x;
+    // ---- (a) decay inside each 16-token block, as products of alpha -------------
+    // No decay factor is ever formed above 1: every factor below is a product
+    // of alpha over a run of tokens, in [0, 1], so no gate in [0, 1] can
+    // overflow anything (strongly forgetting channels only underflow, towards
+    // the exact limit 0).  This is the chunk-wise normalisation that keeps chunk
+    // boundaries from overflowing ("Designing and Deploying Hybrid MLA and
+    // Linear Attention Architectures", section 3), taken down to single tokens.
+    // For this lane's token r and p = 0..4:
+    //   pf_p(r) = product of alpha over r's aligned group of 2^p tokens, up to r
+    //   sf_p(r) = product of alpha after r, to the end of that group.
+    // From groups of 2^p to 2^(p+1) tokens, a token in the upper half takes the
+    // lower half's total into pf, a token in the lower half the upper half's
+    // total into sf; that total is pf_p of the other half's last token.
+    constexpr bool SCAL = GATE == KDA_GATE_SCALAR;
+    float pf[KS][8], sf[KS][8];
+    auto PF = [&](int ks, int e) -> float& { return SCAL ? pf[0][0] : pf[ks][e]; };
+    auto SF = [&](int ks, int e) -> float& { return SCAL ? sf[0][0] : sf[ks][e]; };
+    if constexpr (SCAL) {
+        pf[0][0] = valid ? gscalar : 1.f;
+        sf[0][0] = 1.f;
     } else {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                f4 lv;
+                f4 av;
                 if constexpr (GATE == KDA_GATE_ALPHA) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) lv[i] = flog2(graw[ks][half][i]);
+                    av = graw[ks][half];
                 } else {
                     const f4 xv = Raw4<true>::widen(graw[ks][half]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) lv[i] = log2_alpha_from_softplus_arg(xv[i]);
+                    for (int i = 0; i < 4; ++i) av[i] = alpha_from_softplus_arg(xv[i]);
                 }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) b[ks][4 * half + i] = row_scan16(valid ? lv[i] : 0.f);
+                for (int i = 0; i < 4; ++i) {
+                    pf[ks][4 * half + i] = valid ? av[i] : 1.f;
+                    sf[ks][4 * half + i] = 1.f;
+                }
             }
     }
+    if (lg == 0) s_beta[r] = bet;
+
+    // Diagonal 16 x 16 blocks of A and P.  A pair of tokens s < r of this block
+    // is taken at the level p of the highest bit in which r and s differ: both
+    // lie in one aligned group of 2^(p+1) tokens, s in its lower half and r in
+    // its upper half, and the decay between them factors exactly as
+    //   prod_{t = s+1..r} alpha_t = pf_p(r) * sf_p(s),   both factors <= 1.
+    // Level p is one matrix-core product of k (and q) scaled by pf_p on tokens
+    // with bit p set and by sf_p on the others; only its own pairs are kept.
+    // Lane (lm, lg) gathers A[16I + 4lg + i][16I + lm] in dA and
+    // P[16I + lm][16I + 4lg + i] in dP (the layouts of the blocks below the
+    // diagonal in (c)).
+    f4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const bool up = (lm >> p) & 1;
+        f4 la = {0.f, 0.f, 0.f, 0.f}, lp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            V kc, qc;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f4 kw = R4::widen(kraw[ks][half]);
+                const f4 qw = R4::widen(qraw[ks][half]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int e = 4 * half + i;
+                    const float f = up ? PF(ks, e) : SF(ks, e);
+                    kc[e] = M::cvt((valid ? kw[i] : 0.f) * f);
+                    qc[e] = M::cvt((valid ? qw[i] : 0.f) * f);
+                }
+            }
+            la = M::mma(kc, kc, la);      // rows r (A operand), columns s (B operand)
+            lp = M::mma(kc, qc, lp);      // P^T: rows s, columns r
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ra_ = 4 * lg + i;
+            if (((ra_ ^ lm) >> p) == 1) {
+                if ((ra_ >> p) & 1) dA[i] = la[i];     // r = 4lg + i above s = lm
+                else dP[i] = lp[i];                    // r = lm above s = 4lg + i
+            }
+        }
+        // pf_p, sf_p -> pf_{p+1}, sf_{p+1}
+#pragma unroll
+        for (int ks = 0; ks < (SCAL ? 1 : KS); ++ks)
+#pragma unroll
+            for (int e = 0; e < (SCAL ? 1 : 8); ++e) {
+                const float o = other_half_last(p, pf[ks][e], lane);
+                if (up) pf[ks][e] *= o;
+                else sf[ks][e] *= o;
+            }
+    }
+    {   // the diagonal of P: q_r . k_r, no decay
+        f4 pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            V kc, qc;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const f4 kw = R4::widen(kraw[ks][half]);
+                const f4 qw = R4::widen(qraw[ks][half]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kc[4 * half + i] = M::cvt(valid ? kw[i] : 0.f);
+                    qc[4 * half + i] = M::cvt(valid ? qw[i] : 0.f);
+                }
+            }
+            pd = M::mma(kc, qc, pd);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * lg + i == lm) dP[i] = pd[i];
+    }
+    // block totals F_I (= pf_4 of the block's last token), [4][DK]
     if (lm == 15) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_tot[I * DK + chan(ks, e)] = b[ks][e];
-    }
-    if (lg == 0) s_beta[r] = bet;
-    __syncthreads();
-    for (int Ip = 0; Ip < I; ++Ip)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b[ks][e] += s_tot[Ip * DK + chan(ks, e)];
-    // Gamma = 2^b and 1/Gamma for every element; every other decay factor is
-    // one of them times a per-channel constant taken at the block's reference
-    // token 16I+7 (lane 7 of the row) or its last token 16I+15 (lane 15):
-    //   s_fac rows 0..3 2^ref_I, 4..7 2^-ref_I, 8..11 2^end_I, 12..15 2^-end_I
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) b[ks][e] = fexp2(b[ks][e]);
-    if (lm == 7 || lm == 15) {
-        float* d0 = s_fac + ((lm == 7 ? 0 : 8) + I) * DK + 4 * lg;
-        float* d1 = d0 + 4 * DK;
-        auto rcp4 = [&](int ks, int o) {
-            return f4{__builtin_amdgcn_rcpf(b[ks][o]), __builtin_amdgcn_rcpf(b[ks][o + 1]),
-                      __builtin_amdgcn_rcpf(b[ks][o + 2]), __builtin_amdgcn_rcpf(b[ks][o + 3])};
-        };
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            *reinterpret_cast<f4*>(d0 + 32 * ks) = f4{b[ks][0], b[ks][1], b[ks][2], b[ks][3]};
-            *reinterpret_cast<f4*>(d0 + 32 * ks + 16) = f4{b[ks][4], b[ks][5], b[ks][6], b[ks][7]};
-            *reinterpret_cast<f4*>(d1 + 32 * ks) = rcp4(ks, 0);
-            *reinterpret_cast<f4*>(d1 + 32 * ks + 16) = rcp4(ks, 4);
-        }
+            for (int half = 0; half < 2; ++half)
+                *reinterpret_cast<f4*>(s_F + I * DK + 32 * ks + 16 * half + 4 * lg) =
+                    f4{PF(ks, 4 * half), PF(ks, 4 * half + 1), PF(ks, 4 * half + 2), PF(ks, 4 * half + 3)};
     }
     __syncthreads();
-    // gamma
-    if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = s_fac[11 * DK + tid];
+    // gamma = F_0 F_1 F_2 F_3
+    if (tid < DK)
+        reinterpret_cast<float*>(rec + R::GAM)[tid] =
+            s_F[tid] * s_F[DK + tid] * s_F[2 * DK + tid] * s_F[3 * DK + tid];
 
     // ---- (b) every decay-dependent quantity of this lane's elements -----------
-    // A[r][s] and P[r][s] (s <= r) take 2^(b_r - b_s) = 2^(b_r - ref_I) 2^(ref_I - b_s)
-    // for r in block I: the row operands (k, q) 2^(b - ref_I) are shared by
-    // every column block; the column operand k_s 2^(ref_I - b_s) (<= 1 below
-    // the diagonal block) is made by the wave that owns token s, for every
-    // later block I, and handed over through LDS.
-    V ra[KS], rq[KS];             // row operands, rebased at token 16I+7
-    V Dc[KS];                     // column operand of the diagonal block
+    // With E_I = F_0..F_{I-1} and X_I = F_{I+1}..F_3 (products, per channel):
+    //   Gamma_r = E_I pf_4(r),  gamma / Gamma_r = sf_4(r) X_I.
+    // Blocks below the diagonal (J < I) take 2^(b_r - b_s) as
+    //   [pf_4(r)] * [sf_4(s) F_{J+1} .. F_{I-1}]
+    // (split at the end of block I - 1): the row operands k pf_4, q pf_4 of
+    // block I serve every J < I, and the column operand of block J for a later
+    // block I is made by the wave that owns block J and handed over through LDS.
+    V ra[KS], rq[KS];             // row operands of the blocks below the diagonal
     // one copy per block index I (= the wave), so the tests of the later
     // blocks fold at compile time and the column operands of blocks that do
-    // not exist take no registers (181 instead of 247)
+    // not exist take no registers
     auto derive = [&](auto ic) {
         constexpr int I = decltype(ic)::value;
         E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
-        auto fac4 = [&](int row, int ks, int half) {
-            return *reinterpret_cast<const f4*>(s_fac + row * DK + 32 * ks + 16 * half + 4 * lg);
-        };
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             float qv[8], kh[8], kt[8], cl[3][8];
@@ -582,28 +630,33 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             for (int half = 0; half < 2; ++half) {
                 const f4 kw = R4::widen(kraw[ks][half]);
                 const f4 qw = R4::widen(qraw[ks][half]);
-                const f4 ref = fac4(I, ks, half);          // 2^ref_I
-                const f4 rref = fac4(4 + I, ks, half);     // 2^-ref_I
-                const f4 gam = fac4(11, ks, half);         // gamma = 2^end_3
-                f4 refl[3];                                // 2^ref of the later blocks
+                f4 Fb[4];
 #pragma unroll
-                for (int Il = 1; Il < 4; ++Il)
-                    if (Il > I) refl[Il - 1] = fac4(Il, ks, half);
+                for (int K = 0; K < 4; ++K)
+                    if (K != I) Fb[K] = *reinterpret_cast<const f4*>(s_F + K * DK + 32 * ks + 16 * half + 4 * lg);
+                f4 Eb = {1.f, 1.f, 1.f, 1.f}, Xb = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int K = 0; K < I; ++K) Eb = Eb * Fb[K];
+#pragma unroll
+                for (int K = I + 1; K < 4; ++K) Xb = Xb * Fb[K];
+                f4 mid[3];                         // F_{I+1} .. F_{Il-1} for the later blocks Il
+                mid[0] = f4{1.f, 1.f, 1.f, 1.f};
+                if (I + 2 < 4) mid[1] = Fb[I + 1 < 4 ? I + 1 : 0];
+                if (I + 3 < 4) mid[2] = mid[1] * Fb[I + 2 < 4 ? I + 2 : 0];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int e = 4 * half + i;
-                    const float G = b[ks][e], rG = __builtin_amdgcn_rcpf(G);
                     const float kv = valid ? kw[i] : 0.f, qx = valid ? qw[i] : 0.f;
-                    const float e1 = G * rref[i];                      // 2^(b - ref_I)
-                    ra[ks][e] = M::cvt(kv * e1);
-                    rq[ks][e] = M::cvt(qx * e1);
-                    Dc[ks][e] = M::cvt(kv * (rG * ref[i]));           // k 2^(ref_I - b)
+                    const float pfv = PF(ks, e), sfv = SF(ks, e);
+                    const float G = Eb[i] * pfv;
+                    ra[ks][e] = M::cvt(kv * pfv);
+                    rq[ks][e] = M::cvt(qx * pfv);
 #pragma unroll
                     for (int Il = 1; Il < 4; ++Il)
-                        if (Il > I) cl[Il - 1][e] = kv * (rG * refl[Il - 1][i]);
+                        if (Il > I) cl[Il - 1][e] = kv * (sfv * mid[Il - I - 1][i]);
                     kh[e] = kv * G;
                     qv[e] = qx * G;
-                    kt[e] = kv * (rG * gam[i]);                        // k gamma / Gamma
+                    kt[e] = kv * (sfv * Xb[i]);
                 }
             }
             M::store8(qh + frag_off(I * KS + ks, lane), qv);
@@ -635,7 +688,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     }
     __syncthreads();
 
-    // ---- (c) A (as A^T) and P (as P^T tiles) on the matrix cores ---------------
+    // ---- (c) A (as A^T) and P (as P^T tiles): blocks below the diagonal on
+    // the matrix cores, diagonal blocks from (a) --------------------------------
     {
         E* __restrict__ pout = reinterpret_cast<E*>(rec + R::P);
         f4 accP[4];
@@ -644,11 +698,16 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             accP[J] = f4{0.f, 0.f, 0.f, 0.f};
             if (J <= I) {
                 f4 accA = {0.f, 0.f, 0.f, 0.f};
+                if (J < I) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const V col = J == I ? Dc[ks] : M::load8(s_C + frag_off(pair_index(I, J) * KS + ks, lane));
-                    accA = M::mma(ra[ks], col, accA);
-                    accP[J] = M::mma(col, rq[ks], accP[J]);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const V col = M::load8(s_C + frag_off(pair_index(I, J) * KS + ks, lane));
+                        accA = M::mma(ra[ks], col, accA);
+                        accP[J] = M::mma(col, rq[ks], accP[J]);
+                    }
+                } else {
+                    accA = dA;
+                    accP[J] = dP;
                 }
                 // lane (lm, lg) holds A[16I + 4lg + i][16J + lm]; store A^T rows
                 const int s = 16 * J + lm;

@@ -90,28 +90,27 @@ __device__ __forceinline__ float* grec(const GParams& P, int h, int g, size_t of
 // gprep_kernel
 // ---------------------------------------------------------------------------
 template <int C> struct GPrepB {
-    static constexpr int NB = C / 16, NLT = NB * (NB + 1) / 2, NS = kThreads / kSL;
-    static constexpr int bytes = (3 * C * kLS + 2 * NLT * 256 + kWaves * 256 + 2 * C + NS * kSL + kSL) * 4;
+    static constexpr int NB = C / 16, NLT = NB * (NB + 1) / 2;
+    static constexpr int bytes = (3 * C * kLS + 2 * NLT * 256 + kWaves * 256 + 2 * C + NB * kSL) * 4;
 };
 
 template <int DK, int DV, int C, bool ABF16, int GATE>
 __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
     using R = GRec<DK, DV, C>;
     constexpr int NTH = kThreads, NW = kWaves, SL = kSL, LS = kLS;
-    constexpr int NB = GPrepB<C>::NB, NLT = GPrepB<C>::NLT, NS = GPrepB<C>::NS, SEG = C / NS;
-    constexpr int NTASK = 2 * NLT, TW = (NTASK + NW - 1) / NW;
+    constexpr int NB = GPrepB<C>::NB, NLT = GPrepB<C>::NLT;
+    constexpr int TW = (NLT + NW - 1) / NW;
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
-    float* sKh = lds;                    // K -> Gamma.K; pass 2: K -> beta.Gamma.K, V -> beta.V   [C][LS]
-    float* sKb = sKh + C * LS;           // gate -> log2 alpha -> K / Gamma; pass 2: b             [C][LS]
-    float* sQ = sKb + C * LS;            // Q -> Gamma.Q                                         [C][LS]
+    float* sK = lds;                     // K; pass 2: beta.Gamma.K, beta.V                      [C][LS]
+    float* sB = sK + C * LS;             // gate -> b inside each 16-token tile; pass 2: b      [C][LS]
+    float* sQ = sB + C * LS;             // Q                                                  [C][LS]
     float* sA = sQ + C * LS;             // A, packed lower tiles                                [NLT][256]
     float* sT = sA + NLT * 256;          // T, packed lower tiles                                [NLT][256]
     float* sX = sT + NLT * 256;          // T-solve scratch, one tile per wave                   [NW][256]
     float* sBeta = sX + NW * 256;        // [C]
     float* sGs = sBeta + C;              // scalar gate per row                                   [C]
-    float* sPart = sGs + C;              // scan segment sums                                     [NS][SL]
-    float* sGam = sPart + NS * SL;       // gamma of the current slice                            [SL]
+    float* sTot = sGs + C;               // log2 alpha summed over each 16-token tile           [NB][SL]
 
     const int H = P.H;
     const int h = blockIdx.x % H, g = blockIdx.x / H;
@@ -131,10 +130,15 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
     float* gKt = grec(P, h, g, R::KT);
     float* gGam = grec(P, h, g, R::GAM);
 
-    // ---- pass 1: per 32-channel slice, decay, Gamma-scaled operands, A and P tiles
-    f4 acc[TW];
+    // ---- pass 1: per 32-channel slice, decay, Gamma-scaled operands, A and P tiles.
+    // Every decay factor is 2^x with x <= 0, a sum of log2 alpha over the tokens
+    // it spans: cumulative sums restart at each 16-token tile, and products that
+    // cross tiles add the totals of the tiles in between, so nothing overflows
+    // and the sums stay short (chunk-wise normalisation, "Designing and
+    // Deploying Hybrid MLA and Linear Attention Architectures", section 3).
+    f4 accA[TW], accP[TW];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) acc[t] = zero4();
+    for (int t = 0; t < TW; ++t) accA[t] = accP[t] = zero4();
     for (int cs = 0; cs < DK; cs += SL) {
         {
             Tok<ABF16, DK, SL, NTH, C> tk, tq;
@@ -143,58 +147,135 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
             if constexpr (GATE != KDA_GATE_SCALAR) {
                 Tok<GBF16, DK, SL, NTH, C> tg;
                 tg.load(P.gate, row0, len, h, H, cs);
-                tg.put(sKb, LS);
+                tg.put(sB, LS);
             }
-            tk.put(sKh, LS);
+            tk.put(sK, LS);
             tq.put(sQ, LS);
         }
         __syncthreads();
-        {   // log2 alpha per element (padding rows: 0), segment sums
-            const int c = tid % SL, sg = tid / SL;
-            float part = 0.f;
-            for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-                float l2 = 0.f;
-                if (r < len) {
-                    if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
-                    else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sKb[r * LS + c]);
-                    else l2 = __builtin_amdgcn_logf(sKb[r * LS + c]);
+        {   // b = cumulative log2 alpha inside each tile (padding rows add 0).  A
+            // gate below 2^-150 counts as 2^-150: every fp32 factor that spans it
+            // is zero either way.
+            const int c = tid % SL, t = tid / SL;
+            if (t < NB) {
+                float b = 0.f;
+                for (int r = 16 * t; r < 16 * t + 16; ++r) {
+                    float l2 = 0.f;
+                    if (r < len) {
+                        if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
+                        else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sB[r * LS + c]);
+                        else l2 = __builtin_amdgcn_logf(sB[r * LS + c]);
+                        l2 = fmaxf(l2, -150.f);
+                    }
+                    b += l2;
+                    sB[r * LS + c] = b;
                 }
-                sKb[r * LS + c] = l2;
-                part += l2;
+                sTot[t * SL + c] = b;
             }
-            sPart[sg * SL + c] = part;
         }
         __syncthreads();
-        {   // b = cumsum(log2 alpha); Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q
-            const int c = tid % SL, sg = tid / SL;
-            float b = 0.f;
-            for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * SL + c];
-            for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-                b += sKb[r * LS + c];
-                const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-                const float kv = sKh[r * LS + c];
-                sKh[r * LS + c] = G * kv;
-                sKb[r * LS + c] = Gi * kv;
-                sQ[r * LS + c] *= G;
-                gB[r * DK + cs + c] = b;
-            }
-            if (sg == NS - 1) gGam[cs + c] = sGam[c] = __builtin_amdgcn_exp2f(b);
-        }
-        __syncthreads();
+        // record: b from the chunk start, Gamma.Q = 2^b Q, (gamma / Gamma).K and
+        // gamma; with pre / suf the totals of the tiles before / after the row's:
+        //   b = pre + b_t(r),  log2(gamma / Gamma_r) = T_t - b_t(r) + suf
         for (int idx = tid; idx < C * SL; idx += NTH) {
-            const int r = idx / SL, c = idx % SL;
-            gKt[r * DK + cs + c] = sGam[c] * sKb[r * LS + c];
-            gQh[r * DK + cs + c] = sQ[r * LS + c];
+            const int r = idx / SL, c = idx % SL, t = r / 16;
+            float pre = 0.f, suf = 0.f;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const float x = sTot[u * SL + c];
+                if (u < t) pre += x;
+                else if (u > t) suf += x;
+            }
+            const float bl = sB[r * LS + c];
+            const float b = pre + bl;
+            gB[r * DK + cs + c] = b;
+            gQh[r * DK + cs + c] = sQ[r * LS + c] * __builtin_amdgcn_exp2f(b);
+            gKt[r * DK + cs + c] = sK[r * LS + c] * __builtin_amdgcn_exp2f(sTot[t * SL + c] - bl + suf);
         }
-        // this slice's share of the A (Kh Kb^T) and P (Qh Kb^T) tiles
+        if (tid < SL) {
+            float tot = 0.f;
+#pragma unroll
+            for (int u = 0; u < NB; ++u) tot += sTot[u * SL + tid];
+            gGam[cs + tid] = __builtin_amdgcn_exp2f(tot);
+        }
+        // this slice's share of the tiles of A (K-hat K-bar^T) and P (Q-hat K-bar^T).
+        // Lane (i, j) takes channels 16 gg + 4 j + s2 of the slice.
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
             const int task = wave + NW * t;
-            if (task >= NTASK) continue;
+            if (task >= NLT) continue;
             int ti, tj;
-            lt_decode(task % NLT, ti, tj);
-            acc[t] = mm<SL, true, true>((task < NLT ? sKh : sQ) + ti * 16 * LS, LS, 1, sKb + tj * 16 * LS, 1, LS,
-                                        acc[t]);
+            lt_decode(task, ti, tj);
+            if (tj < ti) {
+                // 2^(b_r - b_s) = 2^(b_r - e) 2^(e - b_s), e = b at the end of tile tj:
+                // row factor b_t(r) + (totals of the tiles between), column factor
+                // T_tj - b_t(s)
+                const int r = 16 * ti + i, s = 16 * tj + i;
+#pragma unroll
+                for (int gg = 0; gg < SL / 16; ++gg) {
+                    const int c0 = 16 * gg + 4 * j;
+                    const f4 kr = *reinterpret_cast<const f4*>(sK + r * LS + c0);
+                    const f4 qr = *reinterpret_cast<const f4*>(sQ + r * LS + c0);
+                    const f4 ks = *reinterpret_cast<const f4*>(sK + s * LS + c0);
+                    const f4 br = *reinterpret_cast<const f4*>(sB + r * LS + c0);
+                    const f4 bs = *reinterpret_cast<const f4*>(sB + s * LS + c0);
+                    const f4 tt = *reinterpret_cast<const f4*>(sTot + tj * SL + c0);
+                    f4 mid = zero4();
+                    for (int u = tj + 1; u < ti; ++u) mid += *reinterpret_cast<const f4*>(sTot + u * SL + c0);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const float fr = __builtin_amdgcn_exp2f(br[s2] + mid[s2]);
+                        const float bk = ks[s2] * __builtin_amdgcn_exp2f(tt[s2] - bs[s2]);
+                        accA[t] = mfma4(kr[s2] * fr, bk, accA[t]);
+                        accP[t] = mfma4(qr[s2] * fr, bk, accP[t]);
+                    }
+                }
+            } else {
+                // Diagonal tile: a pair s < r is taken at the level p of the
+                // highest bit in which r and s differ (tile-local indices); the
+                // decay between them is pf_p(r) sf_p(s), the products from the
+                // start of r's aligned 2^p-token group to r and after s to the end
+                // of its group; level p scales each token by pf_p (bit p set) or
+                // sf_p (bit p clear) and keeps only its own pairs.  The diagonal
+                // of P takes no decay.
+                const int x = 16 * ti + i;
+                f4 la[4], lp[4], pd = zero4();
+#pragma unroll
+                for (int p = 0; p < 4; ++p) la[p] = lp[p] = zero4();
+#pragma unroll
+                for (int gg = 0; gg < SL / 16; ++gg) {
+                    const int c0 = 16 * gg + 4 * j;
+                    const f4 kx = *reinterpret_cast<const f4*>(sK + x * LS + c0);
+                    const f4 qx = *reinterpret_cast<const f4*>(sQ + x * LS + c0);
+                    const f4 bx = *reinterpret_cast<const f4*>(sB + x * LS + c0);
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) pd = mfma4(qx[s2], kx[s2], pd);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const bool up = (i >> p) & 1;
+                        const int ref = up ? (i & ~((1 << p) - 1)) - 1 : (i | ((1 << p) - 1));
+                        const f4 bref = *reinterpret_cast<const f4*>(sB + (16 * ti + ref) * LS + c0);
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) {
+                            const float f = __builtin_amdgcn_exp2f(up ? bx[s2] - bref[s2] : bref[s2] - bx[s2]);
+                            const float kc = kx[s2] * f, qc = qx[s2] * f;
+                            la[p] = mfma4(kc, kc, la[p]);
+                            lp[p] = mfma4(qc, kc, lp[p]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 4 * j + e;
+                    if (row == i) accP[t][e] += pd[e];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        if (((row ^ i) >> p) == 1 && ((row >> p) & 1)) {
+                            accA[t][e] += la[p][e];
+                            accP[t][e] += lp[p][e];
+                        }
+                }
+            }
         }
         __syncthreads();
     }
@@ -204,18 +285,18 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
 #pragma unroll
     for (int t = 0; t < TW; ++t) {
         const int task = wave + NW * t;
-        if (task >= NTASK) continue;
+        if (task >= NLT) continue;
         int ti, tj;
-        lt_decode(task % NLT, ti, tj);
-        f4 x = acc[t];
+        lt_decode(task, ti, tj);
+        f4 xa = accA[t], xp = accP[t];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int r = ti * 16 + 4 * j + e, s = tj * 16 + i;
-            if (task < NLT) x[e] = s < r ? sBeta[r] * x[e] : 0.f;
-            else x[e] = s <= r ? x[e] : 0.f;
+            xa[e] = s < r ? sBeta[r] * xa[e] : 0.f;
+            xp[e] = s <= r ? xp[e] : 0.f;
         }
-        if (task < NLT) store_tile(sA + lt(ti, tj) * 256, 16, x);
-        else store_tile(gP + ti * 16 * C + tj * 16, C, x);
+        store_tile(sA + lt(ti, tj) * 256, 16, xa);
+        store_tile(gP + ti * 16 * C + tj * 16, C, xp);
     }
     for (int idx = tid; idx < (NB * NB - NLT) * 256; idx += NTH) {     // P above the diagonal
         int u = idx >> 8;
@@ -275,25 +356,25 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
             Blk<C, SL, NTH> bb;
             tk.load(P.k, row0, len, h, H, c0);
             bb.load(gB + c0, DK);
-            tk.put(sKh, LS);
-            bb.put(sKb, LS);
+            tk.put(sK, LS);
+            bb.put(sB, LS);
         } else {
             Tok<ABF16, DV, SL, NTH, C> tv;
             tv.load(P.v, row0, len, h, H, c0);
-            tv.put(sKh, LS);
+            tv.put(sK, LS);
         }
         __syncthreads();
         for (int idx = tid; idx < C * SL; idx += NTH) {
             const int r = idx / SL, c = idx % SL;
-            const float sc = isw ? __builtin_amdgcn_exp2f(sKb[r * LS + c]) * sBeta[r] : sBeta[r];
-            sKh[r * LS + c] *= sc;
+            const float sc = isw ? __builtin_amdgcn_exp2f(sB[r * LS + c]) * sBeta[r] : sBeta[r];
+            sK[r * LS + c] *= sc;
         }
         __syncthreads();
         for (int t = wave; t < NB * (SL / 16); t += NW) {
             const int mb = t / (SL / 16), nb = t % (SL / 16);
             f4 x = zero4();
             for (int kb = 0; kb <= mb; ++kb)
-                x = mm<16, true, false>(sT + lt(mb, kb) * 256, 16, 1, sKh + kb * 16 * LS + nb * 16, LS, 1, x);
+                x = mm<16, true, false>(sT + lt(mb, kb) * 256, 16, 1, sK + kb * 16 * LS + nb * 16, LS, 1, x);
             if (isw) store_tile(gW + mb * 16 * DK + c0 + nb * 16, DK, x);
             else store_tile(gU + mb * 16 * DV + c0 + nb * 16, DV, x);
         }

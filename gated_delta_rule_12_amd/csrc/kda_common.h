@@ -46,6 +46,15 @@ __device__ __forceinline__ float log2_alpha_from_softplus_arg(float x) {
     return -(fmaxf(x, 0.f) * kLog2e + __builtin_amdgcn_logf(1.f + t));
 }
 
+// alpha = 1 / (1 + e^x) itself (the same gate, for the kernels that multiply
+// decay factors instead of adding logarithms); 0 and 1 at the extremes, never
+// above 1.
+__device__ __forceinline__ float alpha_from_softplus_arg(float x) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float t = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+    return (x > 0.f ? t : 1.f) * __builtin_amdgcn_rcpf(1.f + t);
+}
+
 // ---------------------------------------------------------------------------
 // Host-side launchers (defined next to their kernels).
 // ---------------------------------------------------------------------------

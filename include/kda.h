@@ -8,7 +8,7 @@
  *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
  *     o_t = S_t^T q_t
  *
- * with a per-key-channel forget gate alpha_t in (0,1]^{d_k} and a scalar
+ * with a per-key-channel forget gate alpha_t in [0,1]^{d_k} and a scalar
  * write strength beta_t.  (KDA update rule: "Hybrid Linear Attention
  * Architectures: Breaking Through the Long-Context Engineering Bottleneck in
  * LLMs", Core Module Design, Stage 3; "Linear Attention KDA Gating in a 3:1
@@ -31,12 +31,15 @@
  *    before anything is launched; the call then returns the status and has
  *    launched nothing.  A failed kernel launch returns KDA_ERROR_LAUNCH.
  *    Faults inside a kernel surface at the caller's next synchronisation.
- *  - Data VALUES are not validated.  Preconditions: alpha in (0, 1],
- *    beta in [0, 1]; for 16-bit activations every |v| and every state entry
- *    stays below 6.0e4 (half-precision range of the matrix-core operands);
- *    within any 8 consecutive tokens of a 64-token chunk the decay
- *    -sum(log alpha) of every channel stays below 10; cu_seqlens is
- *    non-decreasing with cu_seqlens[0] = 0 and cu_seqlens[N] = T.
+ *  - Data VALUES are not validated.  Preconditions: alpha in [0, 1] (any
+ *    value, exact 0 included: the forward and decode kernels form every
+ *    decay factor as a product of alpha over a run of tokens, never above 1,
+ *    so fast forgetting only underflows toward its exact limit), beta in
+ *    [0, 1]; for 16-bit activations every |v| and every state entry stays
+ *    below 6.0e4 (half-precision range of the matrix-core operands);
+ *    cu_seqlens is non-decreasing with cu_seqlens[0] = 0 and
+ *    cu_seqlens[N] = T.  kda_chunk_bwd has a narrower gate precondition,
+ *    stated at its declaration.
  *  - Supported: d_k in {64, 128}, d_v in {64, 128}; chunk_size 64 for
  *    every call, and also 32 or 128 for the chunkwise forward (a generic
  *    path with every product in fp32; the result is the same recurrence,
@@ -78,16 +81,17 @@ typedef enum {
 /*
  * Form of the forget gate passed to the *_gated entry points.
  *   KDA_GATE_ALPHA          alpha itself: fp32, one value per key channel
- *                           ([..., Dk]), in (0, 1].  The plain entry points
+ *                           ([..., Dk]), in [0, 1].  The plain entry points
  *                           take this form.
  *   KDA_GATE_SOFTPLUS_BF16  the gate's pre-activation x: bf16, one value per
  *                           key channel ([..., Dk]), with
  *                           log alpha = -softplus(x) = -log(1 + e^x), so
  *                           alpha = 1 / (1 + e^x) lies in (0, 1).  Half the
  *                           gate bytes of KDA_GATE_ALPHA; the kernels form
- *                           log alpha directly, exact near alpha -> 1.
+ *                           alpha (or log alpha) from x without rounding
+ *                           alpha to fp32 first.
  *   KDA_GATE_SCALAR         alpha fp32, ONE value per token and head
- *                           ([..., 1], i.e. the layout of beta), in (0, 1],
+ *                           ([..., 1], i.e. the layout of beta), in [0, 1],
  *                           applied to every key channel: the coarse scalar
  *                           gate of Gated DeltaNet ("Hybrid Linear Attention
  *                           Architectures...", Core Module Design, Stage 2).
@@ -133,7 +137,7 @@ KDA_API size_t kda_chunk_fwd_workspace_bytes(int B, int64_t T, int H, int Dk, in
  * Layout (contiguous):
  *   q, k       [B, T, H, Dk]   act_dtype
  *   v          [B, T, H, Dv]   act_dtype
- *   alpha      [B, T, H, Dk]   fp32, in (0, 1]
+ *   alpha      [B, T, H, Dk]   fp32, in [0, 1]
  *   beta       [B, T, H]       fp32, in [0, 1]
  *   o          [B, T, H, Dv]   out_dtype (written for every token)
  *   initial_state [N, H, Dk, Dv] fp32, or NULL for zeros
@@ -163,8 +167,8 @@ KDA_API kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
  * the place of `alpha` (layouts: [B, T, H, Dk] for KDA_GATE_ALPHA and
  * KDA_GATE_SOFTPLUS_BF16, [B, T, H] for KDA_GATE_SCALAR; alignment 16, 8
  * and 4 bytes).  Everything else is as for kda_chunk_fwd, which is this call
- * with KDA_GATE_ALPHA.  For KDA_GATE_SOFTPLUS_BF16 the decay precondition
- * reads: softplus(x) summed over any 8 consecutive tokens stays below 10.
+ * with KDA_GATE_ALPHA.  Any finite pre-activation x is allowed for
+ * KDA_GATE_SOFTPLUS_BF16.
  */
 KDA_API kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v,
                          const void *gate, kda_gate gate_kind, const float *beta,
@@ -202,7 +206,10 @@ KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, in
  *
  * Inputs, as for kda_chunk_fwd_gated (same layouts, alignment, sequences,
  * preconditions): q, k, v, gate (form gate_kind), beta, initial_state
- * (NULL = zeros), cu_seqlens / num_seqs.  Upstream gradients:
+ * (NULL = zeros), cu_seqlens / num_seqs.  Gate precondition of this call:
+ * alpha in (0, 1] with the decay of every channel over each 64-token chunk,
+ * -sum(log alpha), below 87 (the backward still forms Gamma and 1/Gamma of a
+ * chunk as single fp32 factors).  Upstream gradients:
  *   dout          [B, T, H, Dv]  act_dtype
  *   dfinal_state  [N, H, Dk, Dv] fp32, or NULL for zeros
  * Outputs (written for every token; none may overlap an input):

@@ -33,7 +33,7 @@ import torch
 import torch.nn.functional as F
 
 _TAGS = {"q": 1, "k": 2, "v": 3, "beta": 4, "alpha": 5, "s0": 6, "len": 7, "gx": 8, "ga": 9,
-         "do": 10, "dst": 11}
+         "do": 10, "dst": 11, "sg": 12}
 
 
 def _gen(seed: int, tag: str, device) -> torch.Generator:
@@ -117,6 +117,32 @@ def draw_gate(kind: str, lead: tuple, H: int, Dk: int, mu: float, seed: int, dev
         x = torch.randn(tuple(lead) + (H,), generator=_gen(seed, "ga", device), device=device) + mu
         return torch.exp(-F.softplus(x)).contiguous()
     raise ValueError(kind)
+
+
+def draw_strong_gate(kind: str, lead: tuple, H: int, Dk: int, mu: float, seed: int, device,
+                     tiny_frac: float = 0.25, tiny_lo: float = 1e-30, zero_frac: float = 0.02):
+    """A forget gate that reaches the fast-forgetting end of its range.
+
+    As ``draw_gate`` with mean pre-activation ``mu``, then a random
+    ``tiny_frac`` of the entries is replaced by alpha ~ log-uniform on
+    [tiny_lo, 1e-3] and a random ``zero_frac`` by alpha = 0 exactly ("alpha"
+    and "scalar" forms).  For "softplus" the replaced entries take the
+    pre-activation x ~ U[7, 100] (alpha = 1 / (1 + e^x) from 1e-3 down to
+    4e-44), and no entry is exactly 0.
+    """
+    g = draw_gate(kind, lead, H, Dk, mu, seed, device)
+    gen = _gen(seed, "sg", device)
+    u = torch.rand(g.shape, generator=gen, device=device)
+    w = torch.rand(g.shape, generator=gen, device=device)
+    tiny = u < tiny_frac
+    if kind == "softplus":
+        x = (7.0 + 93.0 * w).to(torch.bfloat16)
+        return torch.where(tiny, x, g).contiguous()
+    lo, hi = torch.log(torch.tensor(tiny_lo)), torch.log(torch.tensor(1e-3))
+    a = torch.exp(lo + (hi - lo) * w)
+    g = torch.where(tiny, a, g)
+    g = torch.where((u >= tiny_frac) & (u < tiny_frac + zero_frac), torch.zeros_like(g), g)
+    return g.contiguous()
 
 
 def draw_upstream(lead: tuple, N: int, H: int, Dk: int, Dv: int, dtype: str,
