@@ -391,6 +391,63 @@ def main():
             cfg["workload"] = wd.name
 
     out["config"] = cfg
+
+    # ---- parity and the CPU baseline: the fp64 oracle on the same inputs -------
+    # The oracle runs on a bounded sample (by default the whole forward
+    # workload: all heads, all tokens); its outputs check the timed forward
+    # and decode results before any variant overwrites them.
+    base = None
+    o_ref = s_ref = None
+    if not args.no_cpu_baseline and do_fwd:
+        import oracle
+        from tests.helpers import error_ratio
+        S = min(args.cpu_sample_tokens, wf.T)
+        sl = (slice(0, 1), slice(0, S))
+        f64 = lambda x: x[sl].to("cpu").to(torch.float64).numpy()
+        q, k, v, a, b = (f64(fi[key]) for key in ("q", "k", "v", "alpha", "beta"))
+        s0 = fi["initial_state"].cpu().double().numpy()
+        c0 = time.perf_counter()
+        o_ref, s_ref, used = oracle.kda_fwd(q, k, v, a, b, initial_state=s0, return_threads=True)
+        c1 = time.perf_counter()
+        del q, k, v, a, b
+        base = {"value": round(wf.H * S / (c1 - c0), 1), "unit": "token-heads/s", "cores": used,
+                "kind": "oracle",
+                "sample": f"first {S} of {wf.T} tokens, all {wf.H} heads of the forward workload "
+                          f"(fp64 token-by-token recurrence, {c1 - c0:.2f} s)",
+                "cpu": cpu_model()}
+        full = S == wf.T
+        out["parity"] = {
+            "o": round(error_ratio(o[sl], o_ref, "bf16", stored_bf16=True), 4),
+            "S_T": round(error_ratio(sT, s_ref, "bf16"), 4) if full else None,
+            "unit": "max error / allowed error (<= 1 passes)",
+            "tolerance": "max|err| <= 2e-2 x RMS(oracle) per tensor, plus half a bf16 ulp of each stored o",
+            "reference": f"fp64 oracle on {'every element' if full else f'the first {S} tokens'} "
+                         "of the timed forward's o and final state"}
+        if not full:
+            o_ref = s_ref = None        # the ablation below needs the whole reference
+        if do_dec:
+            s = W % wd.steps
+            dq, dk, dv, da, db = (di[key][s].cpu().double().numpy()
+                                  for key in ("q", "k", "v", "alpha", "beta"))
+            dst = di["state"].cpu().double().numpy()
+            c0 = time.perf_counter()
+            od_ref, st_ref, dused = oracle.kda_step(dq, dk, dv, da, db, dst, return_threads=True)
+            c1 = time.perf_counter()
+            base["decode"] = {"value": round(decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv)
+                                             / (c1 - c0) / 1e9, 3),
+                              "unit": "GB/s (fp32 byte ledger)", "cores": dused,
+                              "sample": f"one full decode step ({c1 - c0:.2f} s)"}
+            st_chk = di["state"].clone()
+            od_chk = kda.kda_recurrent_step(di["q"][s], di["k"][s], di["v"][s], di["alpha"][s],
+                                            di["beta"][s], st_chk, out_dtype=torch.bfloat16)
+            torch.cuda.synchronize()
+            out["decode"]["parity"] = {
+                "o": round(error_ratio(od_chk, od_ref, "bf16", stored_bf16=True), 4),
+                "state": round(error_ratio(st_chk, st_ref, "f32"), 4),
+                "unit": "max error / allowed error (<= 1 passes)",
+                "reference": "fp64 oracle step on all 8192 (sequence, head) pairs, from the workload's "
+                             "initial state; state tolerance: fp32 (1e-4 relative)"}
+            del dst, st_ref, st_chk
     if args.only is None and not args.no_variants:
         out["measured_peaks"] = measured_peaks(torch)
         # the other forget-gate forms on the same shapes (q, k, v, beta, states reused)
@@ -448,8 +505,15 @@ def main():
             byts = FWD_BYTES_PER_TOKEN_HEAD * units + 2 * wf.B * wf.H * wf.Dk * wf.Dv * 4
             ach = byts / (ms / 1e3) / 1e9
             tf = fwd_flops_per_token_head(C, wf.Dk, wf.Dv) * units / (ms / 1e3) / 1e12
+            par = None
+            if o_ref is not None:
+                fwd_c()
+                torch.cuda.synchronize()
+                par = {"o": round(error_ratio(o, o_ref, "bf16", stored_bf16=True), 4),
+                       "S_T": round(error_ratio(sT, s_ref, "bf16"), 4)}
             var[f"fwd_chunk{C}"] = {"value": round(units / (ms / 1e3), 1), "unit": "token-heads/s",
                                     "fwd_ms": round(ms, 4), "workspace_GiB": round(nbc / 2 ** 30, 2),
+                                    "parity": par,
                                     "roofline": {"bound": "hbm", "achieved": round(ach, 1),
                                                  "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                                  "frac": round(ach / HBM_PEAK_GBPS, 4),
@@ -460,6 +524,16 @@ def main():
             del wsc
         var["chunk_note"] = ("chunk sizes 32 and 128 take the generic path (every product on the fp32 "
                              "matrix cores, fp32 record); chunk 64 is the main line")
+        # accuracy - memory - time of the chunk-size ablation, one row per C
+        abl = {"64": {"fwd_ms": out["fwd_ms"], "workspace_GiB": round(ws_bytes / 2 ** 30, 2),
+                      "parity": ({"o": out["parity"]["o"], "S_T": out["parity"]["S_T"]}
+                                 if "parity" in out else None)}}
+        for C in (32, 128):
+            r = var[f"fwd_chunk{C}"]
+            abl[str(C)] = {"fwd_ms": r["fwd_ms"], "workspace_GiB": r["workspace_GiB"], "parity": r["parity"]}
+        var["chunk_ablation"] = {"rows": {c: abl[c] for c in ("32", "64", "128")},
+                                 "parity_unit": "max error / allowed error against the fp64 oracle "
+                                                "(bf16 o and fp32 final state of the forward workload)"}
         del o, sT, ws, fi
         torch.cuda.empty_cache()
         # the small dense workload (~0.1 GB, fits the 256 MB memory-side cache):
@@ -534,34 +608,9 @@ def main():
             out["decode"]["roofline"]["traffic"] = traffic["decode"]
             out["decode"]["roofline"]["traffic_unit"] = "bytes/launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)"
 
-    # ---- CPU baseline: the fp64 oracle on a bounded sample ---------------------
-    if not args.no_cpu_baseline and do_fwd:
+    # ---- CPU baseline (the oracle runs above, with the parity checks) ---------
+    if base is not None:
         import oracle
-        S = min(args.cpu_sample_tokens, wf.T)
-        sl = (slice(0, 1), slice(0, S))
-        f64 = lambda x: x[sl].to("cpu").to(torch.float64).numpy()
-        q, k, v, a, b = (f64(fi[key]) for key in ("q", "k", "v", "alpha", "beta"))
-        s0 = fi["initial_state"].cpu().double().numpy()
-        c0 = time.perf_counter()
-        _, _, used = oracle.kda_fwd(q, k, v, a, b, initial_state=s0, return_threads=True)
-        c1 = time.perf_counter()
-        base = {"value": round(wf.H * S / (c1 - c0), 1), "unit": "token-heads/s", "cores": used,
-                "kind": "oracle",
-                "sample": f"first {S} of {wf.T} tokens, all {wf.H} heads of the forward workload "
-                          f"(fp64 token-by-token recurrence, {c1 - c0:.2f} s)",
-                "cpu": cpu_model()}
-        if do_dec:
-            s = W % wd.steps
-            dq, dk, dv, da, db = (di[key][s].cpu().double().numpy()
-                                  for key in ("q", "k", "v", "alpha", "beta"))
-            dst = di["state"].cpu().double().numpy()
-            c0 = time.perf_counter()
-            _, _, dused = oracle.kda_step(dq, dk, dv, da, db, dst, return_threads=True)
-            c1 = time.perf_counter()
-            base["decode"] = {"value": round(decode_bytes_per_step(wd.B, wd.H, wd.Dk, wd.Dv)
-                                             / (c1 - c0) / 1e9, 3),
-                              "unit": "GB/s (fp32 byte ledger)", "cores": dused,
-                              "sample": f"one full decode step ({c1 - c0:.2f} s)"}
         if "variants" in out:
             Sb = min(4096, wf.T)
             slb = (slice(0, 1), slice(0, Sb))

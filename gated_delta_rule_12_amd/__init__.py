@@ -47,8 +47,8 @@ KDA_GATE_SCALAR = 2
 _GATES = {"alpha": KDA_GATE_ALPHA, "softplus": KDA_GATE_SOFTPLUS_BF16, "scalar": KDA_GATE_SCALAR}
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-            "kda_chunk_fwd_gated", "kda_chunk_bwd_workspace_bytes", "kda_chunk_bwd",
-            "kda_recurrent_step", "kda_recurrent_step_gated")
+            "kda_chunk_fwd_gated", "kda_chunk_bwd_workspace_bytes",
+            "kda_chunk_bwd", "kda_recurrent_step", "kda_recurrent_step_gated")
 
 _lib = None
 
@@ -114,12 +114,93 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr() or None
 
 
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _gate_spec(gate: str, lead: tuple, Dk: int):
+    """(dtype, shape) of the forget gate in the form ``gate``."""
+    if gate == "alpha":
+        return torch.float32, tuple(lead) + (Dk,)
+    if gate == "softplus":
+        return torch.bfloat16, tuple(lead) + (Dk,)
+    if gate == "scalar":
+        return torch.float32, tuple(lead)
+    raise ValueError(f"unknown gate form {gate!r}")
+
+
+def _check(dev, what: str, t: Optional[torch.Tensor], dtype, shape):
+    """``t`` (when given) is a GPU tensor on ``dev`` of this dtype and shape.
+    The kernels read raw memory, so a wrong device, dtype or shape must never
+    reach them."""
+    if t is None:
+        return
+    _need(isinstance(t, torch.Tensor), f"{what}: expected a tensor")
+    _need(t.is_cuda and t.device == dev, f"{what}: must be on {dev} (got {t.device})")
+    _need(t.dtype == dtype, f"{what}: dtype {t.dtype}, expected {dtype}")
+    _need(tuple(t.shape) == tuple(shape), f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_inputs(q, k, v, alpha, beta, gate, initial_state, cu_seqlens, N):
+    """Shapes, dtypes and devices shared by the forward and backward calls."""
+    _need(isinstance(q, torch.Tensor) and q.dim() == 4, "q: expected [B, T, H, Dk]")
+    _need(q.is_cuda, "q: must be a GPU tensor")
+    _need(q.dtype in (torch.float32, torch.bfloat16), f"q: unsupported dtype {q.dtype}")
+    dev = q.device
+    B, T, H, Dk = q.shape
+    _check(dev, "k", k, q.dtype, q.shape)
+    _need(isinstance(v, torch.Tensor) and v.dim() == 4, "v: expected [B, T, H, Dv]")
+    _check(dev, "v", v, q.dtype, (B, T, H, v.shape[-1]))
+    gdt, gshape = _gate_spec(gate, (B, T, H), Dk)
+    _check(dev, f"gate ({gate})", alpha, gdt, gshape)
+    _check(dev, "beta", beta, torch.float32, (B, T, H))
+    _check(dev, "initial_state", initial_state, torch.float32, (N, H, Dk, v.shape[-1]))
+    if cu_seqlens is not None:
+        _check(dev, "cu_seqlens", cu_seqlens, torch.int32, (N + 1,))
+        _need(B == 1, "cu_seqlens: packed sequences need B == 1")
+    return dev
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _scratch(nbytes: int, dev, stream) -> torch.Tensor:
+    """A workspace from torch's caching allocator.  When the call runs on a
+    stream other than the current one, the block is recorded on that stream
+    so that the allocator does not hand it out again while the call's
+    kernels may still use it."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if stream is not None:
+        s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=dev)
+        if s != torch.cuda.current_stream(dev):
+            ws.record_stream(s)
+    return ws
+
+
+def _fwd_outputs(q, k, v, alpha, beta, initial_state, final_state, cu_seqlens, o, out_dtype, gate):
+    """Check the forward's inputs and return (o, final_state or None, N),
+    allocating the outputs that were not given."""
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = _check_inputs(q, k, v, alpha, beta, gate, initial_state, cu_seqlens, N)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out_dtype is None:
+        out_dtype = q.dtype if o is None else o.dtype
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=dev)
+    _check(dev, "o", o, out_dtype, (B, T, H, Dv))
+    if final_state is True:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    _check(dev, "final_state", final_state, torch.float32, (N, H, Dk, Dv))
+    return o, final_state, N
 
 
 def kda_chunk_fwd_workspace_bytes(B: int, T: int, H: int, Dk: int, Dv: int, varlen: bool,
@@ -146,35 +227,32 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     [N,H,Dk,Dv] (may be ``initial_state`` itself, updated in place).
     Returns (o, final_state or None).
     """
+    o, final_state, N = _fwd_outputs(q, k, v, alpha, beta, initial_state, final_state,
+                                     cu_seqlens, o, out_dtype, gate)
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     act = _dt(q.dtype)
-    out_dtype = q.dtype if out_dtype is None else out_dtype
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
     dev = q.device
-    if o is None:
-        o = torch.empty((B, T, H, Dv), dtype=out_dtype, device=dev)
-    if final_state is True:
-        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
-    elif final_state is False:
-        final_state = None
+    sid = _stream(stream)
     need = kda_chunk_fwd_workspace_bytes(B, T, H, Dk, Dv, cu_seqlens is not None, N,
                                          chunk_size, act)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
+    elif workspace is not None:
+        _check(dev, "workspace", workspace, torch.uint8, (workspace.numel(),))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     g = _GATES[gate]
     if g == KDA_GATE_ALPHA:
         st = lib().kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                  _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
-                                 _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(out_dtype),
-                                 _ptr(workspace), ws_bytes, _stream(stream))
+                                 _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(o.dtype),
+                                 _ptr(workspace), ws_bytes, sid)
         where = "kda_chunk_fwd"
     else:
         st = lib().kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), g, _ptr(beta),
                                        _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
-                                       _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(out_dtype),
-                                       _ptr(workspace), ws_bytes, _stream(stream))
+                                       _ptr(o), B, T, H, Dk, Dv, chunk_size, act, _dt(o.dtype),
+                                       _ptr(workspace), ws_bytes, sid)
         where = "kda_chunk_fwd_gated"
     if st != KDA_SUCCESS:
         raise KDAError(st, where)
@@ -205,11 +283,13 @@ def kda_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
     or None when ``need_dinitial_state`` is False).  ``out`` may hold
     preallocated tensors under those names.
     """
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.numel() - 1
+    dev = _check_inputs(q, k, v, alpha, beta, gate, initial_state, cu_seqlens, N)
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
     act = _dt(q.dtype)
-    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
-    dev = q.device
+    _check(dev, "dout", dout, q.dtype, v.shape)
+    _check(dev, "dfinal_state", dfinal_state, torch.float32, (N, H, Dk, Dv))
     r = dict(out) if out else {}
     r.setdefault("dq", torch.empty_like(q))
     r.setdefault("dk", torch.empty_like(k))
@@ -220,9 +300,16 @@ def kda_chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
         r.setdefault("dinitial_state", torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev))
     else:
         r["dinitial_state"] = None
+    gdt, gshape = _gate_spec(gate, (B, T, H), Dk)
+    for key, dt, shp in (("dq", q.dtype, q.shape), ("dk", q.dtype, q.shape), ("dv", q.dtype, v.shape),
+                         ("dgate", torch.float32, gshape), ("dbeta", torch.float32, (B, T, H))):
+        _check(dev, key, r[key], dt, shp)
+    _check(dev, "dinitial_state", r["dinitial_state"], torch.float32, (N, H, Dk, Dv))
     need = kda_chunk_bwd_workspace_bytes(B, T, H, Dk, Dv, cu_seqlens is not None, N, chunk_size, act)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _scratch(need, dev, stream)
+    elif workspace is not None:
+        _check(dev, "workspace", workspace, torch.uint8, (workspace.numel(),))
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().kda_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _GATES[gate], _ptr(beta),
                              _ptr(initial_state), _ptr(cu_seqlens), N, _ptr(dout),
@@ -244,21 +331,33 @@ def kda_recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha:
     q, k [N,H,Dk]; v [N,H,Dv]; beta [N,H]; ``alpha`` in the form ``gate``
     (as for kda_chunk_fwd: [N,H,Dk], or [N,H] for "scalar").  Returns o [N,H,Dv].
     """
+    _need(isinstance(q, torch.Tensor) and q.dim() == 3 and q.is_cuda, "q: expected a GPU tensor [N, H, Dk]")
+    _need(q.dtype in (torch.float32, torch.bfloat16), f"q: unsupported dtype {q.dtype}")
+    dev = q.device
     N, H, Dk = q.shape
+    _need(isinstance(v, torch.Tensor) and v.dim() == 3, "v: expected [N, H, Dv]")
     Dv = v.shape[-1]
-    out_dtype = q.dtype if out_dtype is None else out_dtype
+    _check(dev, "k", k, q.dtype, q.shape)
+    _check(dev, "v", v, q.dtype, (N, H, Dv))
+    gdt, gshape = _gate_spec(gate, (N, H), Dk)
+    _check(dev, f"gate ({gate})", alpha, gdt, gshape)
+    _check(dev, "beta", beta, torch.float32, (N, H))
+    _check(dev, "state", state, torch.float32, (N, H, Dk, Dv))
+    if out_dtype is None:
+        out_dtype = q.dtype if o is None else o.dtype
     if o is None:
-        o = torch.empty((N, H, Dv), dtype=out_dtype, device=q.device)
+        o = torch.empty((N, H, Dv), dtype=out_dtype, device=dev)
+    _check(dev, "o", o, out_dtype, (N, H, Dv))
     g = _GATES[gate]
     if g == KDA_GATE_ALPHA:
         st = lib().kda_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                       _ptr(state), _ptr(o), N, H, Dk, Dv, _dt(q.dtype),
-                                      _dt(out_dtype), _stream(stream))
+                                      _dt(o.dtype), _stream(stream))
         where = "kda_recurrent_step"
     else:
         st = lib().kda_recurrent_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), g, _ptr(beta),
                                             _ptr(state), _ptr(o), N, H, Dk, Dv, _dt(q.dtype),
-                                            _dt(out_dtype), _stream(stream))
+                                            _dt(o.dtype), _stream(stream))
         where = "kda_recurrent_step_gated"
     if st != KDA_SUCCESS:
         raise KDAError(st, where)

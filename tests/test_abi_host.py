@@ -184,3 +184,18 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kda, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         kda.lib()
+
+
+def test_binding_rejects_bad_tensors_before_the_call():
+    """The Python binding refuses host tensors, wrong dtypes and wrong shapes
+    (the kernels read raw memory)."""
+    import torch
+    q = torch.zeros(1, 8, 2, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_chunk_fwd(q, q, q, q, torch.zeros(1, 8, 2))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_recurrent_step(q[0], q[0], q[0], q[0], torch.zeros(8, 2), torch.zeros(8, 2, 64, 64))
+    with pytest.raises(ValueError, match="unknown gate"):
+        kda._gate_spec("sigmoid", (1, 8, 2), 64)
+    assert kda._gate_spec("scalar", (1, 8, 2), 64) == (torch.float32, (1, 8, 2))
+    assert kda._gate_spec("softplus", (1, 8, 2), 64) == (torch.bfloat16, (1, 8, 2, 64))

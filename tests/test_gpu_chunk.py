@@ -143,47 +143,35 @@ def test_workload1_full(out):
     check_pair(o, sT, o_ref, s_ref, "bf16", out)
 
 
-def _sampled(inp, o, sT, pairs, seq_bounds):
-    """Compare o / S_T of the listed (sequence, head) pairs with the oracle run
-    on exactly those pairs' inputs."""
-    for n, h in pairs:
-        t0, t1 = seq_bounds(n)
-        b = 0 if inp["cu_seqlens"] is not None else n
-        sl = (slice(b, b + 1), slice(t0, t1), slice(h, h + 1))
-        s0 = inp["initial_state"]
-        o_ref, s_ref = oracle.kda_fwd(
-            to_np(inp["q"][sl]), to_np(inp["k"][sl]), to_np(inp["v"][sl]), to_np(inp["alpha"][sl]),
-            to_np(inp["beta"][sl]),
-            initial_state=None if s0 is None else to_np(s0[n:n + 1, h:h + 1]))
-        yield (n, h), o[sl], sT[n:n + 1, h:h + 1], o_ref, s_ref
-
-
 @pytest.mark.parametrize("out", ["bf16", "f32"])
-def test_workload2_full_sampled(out):
+def test_workload2_full(out):
     """B=1, H=32, T=65536, d=128, slow decay, random S0: the chunk-forward
-    benchmark launch.  Checked on 3 full heads (all 65536 tokens each)."""
+    benchmark launch, compared element by element on every head and token
+    and on the whole final state."""
     w = synth.WORKLOADS[2]
     print(f"[chunk {w.name} out={out}]", flush=True)
     inp = synth.workload_inputs(2, device=DEV)
     o, sT = gpu_fwd(inp, out)
-    for (n, h), og, sg, o_ref, s_ref in _sampled(inp, o, sT, [(0, 0), (0, 13), (0, 31)],
-                                                 lambda n: (0, w.T)):
-        print(f"  head {h}", flush=True)
-        check_pair(og, sg, o_ref, s_ref, "bf16", out)
+    o_ref, s_ref = oracle_fwd(inp)
+    check_pair(o, sT, o_ref, s_ref, "bf16", out)
 
 
-def test_workload4_varlen_full_sampled():
-    """64 packed sequences, lengths ~U[512, 32768], H=16, d=128, per-sequence S0;
-    checked on the longest, the shortest and two other sequences, 2 heads each."""
+def test_workload4_varlen_full():
+    """64 packed sequences, lengths ~U[512, 32768] (1.06M tokens), H=16, d=128,
+    per-sequence S0: every sequence, head and token compared with the oracle
+    (run sequence by sequence to bound host memory; the RMS of each bound is
+    taken over the whole output tensor)."""
     w = synth.WORKLOADS[4]
     print(f"[chunk {w.name}]", flush=True)
     inp = synth.workload_inputs(4, device=DEV)
-    cu = inp["cu_seqlens"].cpu().numpy()
-    lens = np.diff(cu)
-    pick = [int(np.argmax(lens)), int(np.argmin(lens)), 17, 40]
+    cu = inp["cu_seqlens"].cpu().numpy().astype(np.int64)
     o, sT = gpu_fwd(inp, "bf16")
-    pairs = [(n, h) for n in pick for h in (0, 11)]
-    for (n, h), og, sg, o_ref, s_ref in _sampled(inp, o, sT, pairs,
-                                                 lambda n: (int(cu[n]), int(cu[n + 1]))):
-        print(f"  seq {n} (len {lens[n]}) head {h}", flush=True)
-        check_pair(og, sg, o_ref, s_ref, "bf16", "bf16")
+    s0 = inp["initial_state"]
+    o_ref = np.empty(tuple(o.shape), dtype=np.float64)
+    s_ref = np.empty(tuple(sT.shape), dtype=np.float64)
+    for n in range(len(cu) - 1):
+        sl = (slice(0, 1), slice(int(cu[n]), int(cu[n + 1])))
+        o_ref[sl], s_ref[n:n + 1] = oracle.kda_fwd(
+            to_np(inp["q"][sl]), to_np(inp["k"][sl]), to_np(inp["v"][sl]), to_np(inp["alpha"][sl]),
+            to_np(inp["beta"][sl]), initial_state=to_np(s0[n:n + 1]))
+    check_pair(o, sT, o_ref, s_ref, "bf16", "bf16")

@@ -50,37 +50,21 @@ def test_decode_readback_overwrite():
     assert torch.allclose(o, inp["v"][0], atol=2e-5, rtol=0)
 
 
-def test_decode_full_workload_sampled():
+def test_decode_full_workload():
     """256 sequences x 32 heads, d=128, 100 in-place steps (the decode benchmark
-    launch); every step's output and the final state are checked on 48
-    sampled (sequence, head) pairs."""
+    launch): every step's whole output and the whole final state are compared
+    with the oracle run step by step on all 8192 (sequence, head) pairs."""
     w = synth.WORKLOADS[3]
     print(f"[decode full {w.name}]", flush=True)
     inp = synth.workload_inputs(3, device=DEV)
     state = inp["state"].clone()
-    g = np.random.default_rng(5)
-    ns = g.integers(0, w.B, size=48)
-    hs = g.integers(0, w.H, size=48)
-    nsel = torch.as_tensor(ns, device=DEV)
-    hsel = torch.as_tensor(hs, device=DEV)
-    outs = []
+    st = to_np(inp["state"])
+    worst = 0.0
     for s in range(w.steps):
         o = kda.kda_recurrent_step(inp["q"][s], inp["k"][s], inp["v"][s], inp["alpha"][s],
                                    inp["beta"][s], state, out_dtype=torch.bfloat16)
-        outs.append(o[nsel, hsel].float())
-    torch.cuda.synchronize()
-    got_o = torch.stack(outs).cpu()
-    got_s = state[nsel, hsel].cpu()
-
-    def pick(x):
-        return to_np(x[:, nsel, hsel])[:, :, None]          # [steps, P, 1, ...]
-
-    q, k, v, a, b = (pick(inp[key]) for key in ("q", "k", "v", "alpha", "beta"))
-    st = to_np(inp["state"][nsel, hsel])[:, None]
-    ref = []
-    for s in range(w.steps):
-        o_ref, st = oracle.kda_step(q[s], k[s], v[s], a[s], b[s], st)
-        ref.append(o_ref[:, 0])
-    ref = np.stack(ref)
-    check_close(got_o, ref, "bf16", stored_bf16=True, what="o (100 steps)")
-    check_close(got_s, st[:, 0], "f32", what="final state")
+        o_ref, st = oracle.kda_step(to_np(inp["q"][s]), to_np(inp["k"][s]), to_np(inp["v"][s]),
+                                    to_np(inp["alpha"][s]), to_np(inp["beta"][s]), st)
+        worst = max(worst, check_close(o, o_ref, "bf16", stored_bf16=True, what=f"o step {s}"))
+    r = check_close(state, st, "f32", what="final state (100 steps)")
+    print(f"  error/allowed: o {worst:.3f} (worst step)  state {r:.3f}", flush=True)
