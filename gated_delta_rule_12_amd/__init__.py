@@ -10,6 +10,7 @@ Functions carry the C names:
 
 * ``kda_chunk_fwd``                 chunkwise forward (prefill / training forward)
 * ``kda_chunk_fwd_gated``           the same with the gate in any ``kda_gate`` form
+* ``kda_chunk_fwd_static``          the same on the library's static workspace (no allocation)
 * ``kda_chunk_fwd_workspace_bytes`` workspace size of a chunkwise forward
 * ``kda_chunk_bwd``                 chunkwise backward (training): all input gradients
 * ``kda_chunk_bwd_workspace_bytes`` workspace size of a chunkwise backward
@@ -47,8 +48,11 @@ KDA_GATE_SCALAR = 2
 _GATES = {"alpha": KDA_GATE_ALPHA, "softplus": KDA_GATE_SOFTPLUS_BF16, "scalar": KDA_GATE_SCALAR}
 
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd",
-            "kda_chunk_fwd_gated", "kda_chunk_bwd_workspace_bytes",
+            "kda_chunk_fwd_gated", "kda_chunk_fwd_static", "kda_chunk_bwd_workspace_bytes",
             "kda_chunk_bwd", "kda_recurrent_step", "kda_recurrent_step_gated")
+
+# size of the static workspace of kda_chunk_fwd_static (KDA_STATIC_WORKSPACE_BYTES)
+KDA_STATIC_WORKSPACE_BYTES = 64 << 20
 
 _lib = None
 
@@ -78,6 +82,9 @@ def lib() -> ctypes.CDLL:
         L.kda_chunk_fwd_gated.restype = i32
         L.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
                                           i32, i64, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.kda_chunk_fwd_static.restype = i32
+        L.kda_chunk_fwd_static.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, i32, vp,
+                                           i32, i64, i32, i32, i32, i32, i32, i32, vp]
         L.kda_chunk_bwd_workspace_bytes.restype = sz
         L.kda_chunk_bwd_workspace_bytes.argtypes = [i32, i64, i32, i32, i32, i32, i32, i32, i32]
         L.kda_chunk_bwd.restype = i32
@@ -256,6 +263,30 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
         where = "kda_chunk_fwd_gated"
     if st != KDA_SUCCESS:
         raise KDAError(st, where)
+    return o, final_state
+
+
+def kda_chunk_fwd_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                         beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                         final_state=None, cu_seqlens: Optional[torch.Tensor] = None,
+                         o: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                         chunk_size: int = 64, stream=None,
+                         gate: str = "alpha") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``kda_chunk_fwd`` on the library's static workspace: the C call
+    allocates nothing (pass ``o`` and ``final_state`` to allocate nothing at
+    all).  Problems needing more than KDA_STATIC_WORKSPACE_BYTES of workspace
+    raise KDA_ERROR_WORKSPACE_TOO_SMALL.  Calls that may overlap on one GPU
+    share that workspace and must be ordered by the caller."""
+    o, final_state, N = _fwd_outputs(q, k, v, alpha, beta, initial_state, final_state,
+                                     cu_seqlens, o, out_dtype, gate)
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    st = lib().kda_chunk_fwd_static(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _GATES[gate], _ptr(beta),
+                                    _ptr(initial_state), _ptr(final_state), _ptr(cu_seqlens), N,
+                                    _ptr(o), B, T, H, Dk, Dv, chunk_size, _dt(q.dtype), _dt(o.dtype),
+                                    _stream(stream))
+    if st != KDA_SUCCESS:
+        raise KDAError(st, "kda_chunk_fwd_static")
     return o, final_state
 
 

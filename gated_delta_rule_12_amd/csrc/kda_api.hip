@@ -3,6 +3,8 @@
 // launches nothing.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kda_chunk.h"
 #include "kda_common.h"
 
@@ -36,6 +38,96 @@ bool valid_out(kda_dtype act, kda_dtype out) {
 }
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_SUCCESS : KDA_ERROR_LAUNCH; }
+
+// The workspace of kda_chunk_fwd_static: a file-scope device array, one copy
+// per GPU the library's code is loaded on, held until the process ends.  Its
+// name is only a host-side handle; the device address of each GPU's copy is
+// looked up once, with that GPU current, and kept here.
+static_assert(KDA_STATIC_WORKSPACE_BYTES % 256 == 0, "whole 256-byte lines");
+__device__ __align__(256) unsigned char scratch[KDA_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 128;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU that `stream` belongs to (the
+// current GPU for the null stream).
+kda_status static_workspace(hipStream_t stream, void** out) {
+    int dev = 0;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return KDA_ERROR_INVALID_VALUE;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return KDA_ERROR_LAUNCH;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return KDA_ERROR_NOT_SUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return KDA_ERROR_LAUNCH;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return KDA_ERROR_LAUNCH;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || p == nullptr) return KDA_ERROR_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_SUCCESS;
+}
+
+// Validation and dispatch of the chunkwise forward.  With `static_ws` the
+// workspace arguments are ignored and the library's static array is used.
+kda_status chunk_fwd(const void* q, const void* k, const void* v, const void* gate,
+                     kda_gate gate_kind, const float* beta, const float* initial_state,
+                     float* final_state, const int32_t* cu_seqlens, int num_seqs, void* o, int B,
+                     int64_t T, int H, int Dk, int Dv, int chunk_size, kda_dtype act_dtype,
+                     kda_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                     bool static_ws) {
+    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate_kind))
+        return KDA_ERROR_INVALID_VALUE;
+    if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
+    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
+    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 0)) return KDA_ERROR_INVALID_VALUE;
+    if (!supported_head(Dk) || !supported_head(Dv) || !supported_chunk(chunk_size))
+        return KDA_ERROR_NOT_SUPPORTED;
+
+    kda::ChunkPlan plan;
+    const kda_status ps = kda::make_chunk_plan(B, T, H, Dk, Dv, cu_seqlens != nullptr, num_seqs,
+                                               chunk_size, act_dtype == KDA_DTYPE_BF16, &plan);
+    if (ps != KDA_SUCCESS) return ps;
+
+    const bool has_tokens = (int64_t)B * T > 0;
+    if (has_tokens) {
+        if (!q || !k || !v || !gate || !beta || !o) return KDA_ERROR_INVALID_VALUE;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !gate_aligned(gate, gate_kind) ||
+            !aligned4(beta) || !aligned16(o))
+            return KDA_ERROR_INVALID_VALUE;
+    }
+    if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERROR_INVALID_VALUE;
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+        return KDA_ERROR_INVALID_VALUE;
+    if (static_ws) {
+        if (plan.workspace_bytes > KDA_STATIC_WORKSPACE_BYTES) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+        if (plan.N == 0) return KDA_SUCCESS;
+        const kda_status ws = static_workspace(static_cast<hipStream_t>(stream), &workspace);
+        if (ws != KDA_SUCCESS) return ws;
+    } else {
+        if (plan.N == 0) return KDA_SUCCESS;             // nothing to compute or write
+        if (plan.workspace_bytes > 0) {
+            if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+                return KDA_ERROR_INVALID_VALUE;
+            if (workspace_bytes < plan.workspace_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
+        }
+    }
+
+    kda::ChunkArgs a;
+    a.q = q; a.k = k; a.v = v; a.gate = gate; a.gate_kind = gate_kind; a.beta = beta;
+    a.initial_state = initial_state; a.final_state = final_state;
+    a.cu_seqlens = cu_seqlens; a.o = o; a.workspace = workspace;
+    a.act_bf16 = act_dtype == KDA_DTYPE_BF16;
+    a.out_bf16 = out_dtype == KDA_DTYPE_BF16;
+    return from_hip(kda::launch_chunk_fwd(plan, a, static_cast<hipStream_t>(stream)));
+}
 
 }  // namespace
 
@@ -79,43 +171,19 @@ kda_status kda_chunk_fwd_gated(const void* q, const void* k, const void* v, cons
                                void* o, int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
                                kda_dtype act_dtype, kda_dtype out_dtype, void* workspace,
                                size_t workspace_bytes, void* stream) {
-    if (!valid_dtype(act_dtype) || !valid_dtype(out_dtype) || !valid_gate(gate_kind))
-        return KDA_ERROR_INVALID_VALUE;
-    if (!valid_out(act_dtype, out_dtype)) return KDA_ERROR_NOT_SUPPORTED;
-    if (B < 0 || T < 0 || H <= 0 || Dk <= 0 || Dv <= 0) return KDA_ERROR_INVALID_VALUE;
-    if (cu_seqlens != nullptr && (B != 1 || num_seqs < 0)) return KDA_ERROR_INVALID_VALUE;
-    if (!supported_head(Dk) || !supported_head(Dv) || !supported_chunk(chunk_size))
-        return KDA_ERROR_NOT_SUPPORTED;
+    return chunk_fwd(q, k, v, gate, gate_kind, beta, initial_state, final_state, cu_seqlens,
+                     num_seqs, o, B, T, H, Dk, Dv, chunk_size, act_dtype, out_dtype, workspace,
+                     workspace_bytes, stream, false);
+}
 
-    kda::ChunkPlan plan;
-    const kda_status ps = kda::make_chunk_plan(B, T, H, Dk, Dv, cu_seqlens != nullptr, num_seqs,
-                                               chunk_size, act_dtype == KDA_DTYPE_BF16, &plan);
-    if (ps != KDA_SUCCESS) return ps;
-
-    const bool has_tokens = (int64_t)B * T > 0;
-    if (has_tokens) {
-        if (!q || !k || !v || !gate || !beta || !o) return KDA_ERROR_INVALID_VALUE;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !gate_aligned(gate, gate_kind) ||
-            !aligned4(beta) || !aligned16(o))
-            return KDA_ERROR_INVALID_VALUE;
-    }
-    if (cu_seqlens && !aligned16(cu_seqlens)) return KDA_ERROR_INVALID_VALUE;
-    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
-        return KDA_ERROR_INVALID_VALUE;
-    if (plan.N == 0) return KDA_SUCCESS;                 // nothing to compute or write
-    if (plan.workspace_bytes > 0) {
-        if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-            return KDA_ERROR_INVALID_VALUE;
-        if (workspace_bytes < plan.workspace_bytes) return KDA_ERROR_WORKSPACE_TOO_SMALL;
-    }
-
-    kda::ChunkArgs a;
-    a.q = q; a.k = k; a.v = v; a.gate = gate; a.gate_kind = gate_kind; a.beta = beta;
-    a.initial_state = initial_state; a.final_state = final_state;
-    a.cu_seqlens = cu_seqlens; a.o = o; a.workspace = workspace;
-    a.act_bf16 = act_dtype == KDA_DTYPE_BF16;
-    a.out_bf16 = out_dtype == KDA_DTYPE_BF16;
-    return from_hip(kda::launch_chunk_fwd(plan, a, static_cast<hipStream_t>(stream)));
+kda_status kda_chunk_fwd_static(const void* q, const void* k, const void* v, const void* gate,
+                                kda_gate gate_kind, const float* beta, const float* initial_state,
+                                float* final_state, const int32_t* cu_seqlens, int num_seqs,
+                                void* o, int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
+                                kda_dtype act_dtype, kda_dtype out_dtype, void* stream) {
+    return chunk_fwd(q, k, v, gate, gate_kind, beta, initial_state, final_state, cu_seqlens,
+                     num_seqs, o, B, T, H, Dk, Dv, chunk_size, act_dtype, out_dtype, nullptr, 0,
+                     stream, true);
 }
 
 size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv, int varlen,

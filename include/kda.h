@@ -181,6 +181,37 @@ KDA_API kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void 
                          void *stream);
 
 /*
+ * kda_chunk_fwd_gated for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): there is no workspace argument; the workspace is a static
+ * device array of KDA_STATIC_WORKSPACE_BYTES inside the library, one copy per
+ * GPU, reserved when the library's code is loaded on that GPU and held until
+ * the process ends.  The call allocates nothing.  Arguments, layouts,
+ * preconditions and results are those of kda_chunk_fwd_gated; `stream`
+ * selects the GPU (the current GPU for the null stream).
+ *   - A problem whose kda_chunk_fwd_workspace_bytes exceeds
+ *     KDA_STATIC_WORKSPACE_BYTES is rejected with
+ *     KDA_ERROR_WORKSPACE_TOO_SMALL before anything is launched (64 MiB:
+ *     e.g. 900 chunk-heads of 64 tokens at d = 128 with bf16 activations).
+ *   - Every call on one GPU uses that GPU's one array, whatever the stream:
+ *     calls that may overlap on one GPU (other streams, other host threads)
+ *     race and must be ordered by the caller.  The array needs no clearing:
+ *     every value a call uses from it, the same call has written first.
+ *   - The first call on a GPU looks up that GPU's copy of the array
+ *     (hipGetSymbolAddress); KDA_ERROR_LAUNCH if that lookup fails.
+ */
+#define KDA_STATIC_WORKSPACE_BYTES (64u << 20)
+
+KDA_API kda_status kda_chunk_fwd_static(const void *q, const void *k, const void *v,
+                         const void *gate, kda_gate gate_kind, const float *beta,
+                         const float *initial_state, float *final_state,
+                         const int32_t *cu_seqlens, int num_seqs,
+                         void *o,
+                         int B, int64_t T, int H, int Dk, int Dv, int chunk_size,
+                         kda_dtype act_dtype, kda_dtype out_dtype,
+                         void *stream);
+
+/*
  * Workspace size, in bytes, that kda_chunk_bwd needs for this problem (same
  * arguments as kda_chunk_fwd_workspace_bytes).  Returns 0 for argument
  * combinations kda_chunk_bwd would reject.  256-byte alignment; contents

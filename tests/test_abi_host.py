@@ -186,6 +186,35 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         kda.lib()
 
 
+def _chunk_static(**over):
+    L = kda.lib()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, gate=FAKE, g=kda.KDA_GATE_ALPHA, beta=FAKE, s0=None, sT=None,
+             cu=None, N=0, o=FAKE, B=1, T=128, H=2, Dk=64, Dv=64, C=64, act=kda.KDA_DTYPE_BF16,
+             out=kda.KDA_DTYPE_BF16, stream=None)
+    a.update(over)
+    return L.kda_chunk_fwd_static(a["q"], a["k"], a["v"], a["gate"], a["g"], a["beta"], a["s0"],
+                                  a["sT"], a["cu"], a["N"], a["o"], a["B"], a["T"], a["H"],
+                                  a["Dk"], a["Dv"], a["C"], a["act"], a["out"], a["stream"])
+
+
+def test_static_entry_point_limit_and_argument_errors():
+    """The static-workspace forward checks its arguments like the others and
+    rejects a problem whose workspace exceeds KDA_STATIC_WORKSPACE_BYTES before
+    touching any GPU (this host has none)."""
+    f = kda.kda_chunk_fwd_workspace_bytes
+    hdr = open(HDR).read()
+    assert re.search(r"#define KDA_STATIC_WORKSPACE_BYTES \(64u << 20\)", hdr)
+    assert kda.KDA_STATIC_WORKSPACE_BYTES == 64 << 20
+    # 32 heads x 64 chunks of bf16 records needs about 144 MiB: rejected
+    assert f(1, 4096, 32, 128, 128, False, 0, 64, kda.KDA_DTYPE_BF16) > kda.KDA_STATIC_WORKSPACE_BYTES
+    assert _chunk_static(T=4096, H=32, Dk=128, Dv=128) == kda.KDA_ERROR_WORKSPACE_TOO_SMALL
+    assert _chunk_static(q=None) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_static(k=FAKE + 8) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_static(C=96) == kda.KDA_ERROR_NOT_SUPPORTED
+    assert _chunk_static(g=9) == kda.KDA_ERROR_INVALID_VALUE
+    assert _chunk_static(B=0, q=None, k=None, v=None, gate=None, beta=None, o=None) == kda.KDA_SUCCESS
+
+
 def test_binding_rejects_bad_tensors_before_the_call():
     """The Python binding refuses host tensors, wrong dtypes and wrong shapes
     (the kernels read raw memory)."""
@@ -193,6 +222,8 @@ def test_binding_rejects_bad_tensors_before_the_call():
     q = torch.zeros(1, 8, 2, 64)
     with pytest.raises(ValueError, match="GPU"):
         kda.kda_chunk_fwd(q, q, q, q, torch.zeros(1, 8, 2))
+    with pytest.raises(ValueError, match="GPU"):
+        kda.kda_chunk_fwd_static(q, q, q, q, torch.zeros(1, 8, 2))
     with pytest.raises(ValueError, match="GPU"):
         kda.kda_recurrent_step(q[0], q[0], q[0], q[0], torch.zeros(8, 2), torch.zeros(8, 2, 64, 64))
     with pytest.raises(ValueError, match="unknown gate"):
