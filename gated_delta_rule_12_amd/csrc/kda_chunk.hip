@@ -908,34 +908,20 @@ struct StateStage {
 // the register budget of two waves per SIMD allows it (the fp32 d_k = 128
 // variant needs more than 256 registers per wave).
 template <int DK, bool F16> struct StateThreads { static constexpr int value = (F16 || DK == 64) ? 320 : 256; };
-#ifndef KDA_STATE_PREFETCH
-#define KDA_STATE_PREFETCH 2
-#endif
-constexpr int kStatePrefetch = KDA_STATE_PREFETCH;   // chunks ahead
-#ifndef KDA_PREFETCH_SHIFT
-#define KDA_PREFETCH_SHIFT 7
-#endif
-constexpr int kPrefetchShift = KDA_PREFETCH_SHIFT;   // log2 of the bytes per touched word
-
-#ifndef KDA_STATE_DEPTH
-#define KDA_STATE_DEPTH 2
-#endif
-template <bool F16> struct StateDepth { static constexpr int value = F16 ? KDA_STATE_DEPTH : 2; };
-
-// value-column tiles (16 columns each) per workgroup
-#ifndef KDA_STATE_TILES
-#define KDA_STATE_TILES 1
-#endif
+constexpr int kStatePrefetch = 2;       // chunks ahead that the prefetch wave touches
+constexpr int kPrefetchShift = 7;       // log2 of the bytes per touched word (one per 128-B line)
+constexpr int kStateDepth = 2;          // chunks of operands in the register ring
+constexpr int kStateTiles = 1;          // value-column tiles (16 columns each) per workgroup
 
 template <int DK, int DV, bool F16, bool OBF16>
 __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(const StateParams P) {
     using M = Mx<F16>;
     using E = typename M::E;
     using V = typename M::V;
-    constexpr int TW = KDA_STATE_TILES;
+    constexpr int TW = kStateTiles;
     using Stage = StateStage<DK, F16, TW>;
     using R = Rec<DK, DV, F16>;
-    constexpr int D = StateDepth<F16>::value;   // chunks in flight
+    constexpr int D = kStateDepth;          // chunks in flight
     constexpr int NTV = DV / (16 * TW);   // workgroups per (sequence, head)
     constexpr int RPW = DK / 4;           // state rows per wave
     constexpr int TPW = RPW / 16;         // 16-row tiles per wave
@@ -1241,7 +1227,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     sp.N = pl.N;
     sp.H = pl.H;
     const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
-    const int64_t blocks = (pairs + 7) / 8 * 8 * (DV / (16 * KDA_STATE_TILES));
+    const int64_t blocks = (pairs + 7) / 8 * 8 * (DV / (16 * kStateTiles));
     hipLaunchKernelGGL((state_kernel<DK, DV, F16, OBF16>), dim3(static_cast<unsigned>(blocks)),
                        dim3(StateThreads<DK, F16>::value), 0, stream, sp);
     return hipGetLastError();
