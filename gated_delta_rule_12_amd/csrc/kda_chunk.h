@@ -69,10 +69,12 @@ hipError_t launch_chunk_plan(const ChunkPlan& plan, const int32_t* cu_seqlens, v
                              hipStream_t stream);
 
 // Backward: the forward's chunk table followed by one record per
-// (head, chunk), at index h * gmax + g (layout in kda_chunk_bwd.hip).
+// (head, chunk), at index h * gmax + g (layout in kda_chunk_bwd.hip), then
+// the list of chunks that take the general form and a flag per chunk.
 struct ChunkBwdPlan {
     ChunkPlan fwd;                // sizes and chunk-table offsets (its records are unused)
     size_t off_rec = 0, rec_bytes = 0;
+    size_t off_slow = 0, off_flag = 0;
     size_t workspace_bytes = 0;
 };
 

@@ -116,6 +116,19 @@ template <> struct Mx<true> {
         for (int e = 0; e < 8; ++e) h[e] = static_cast<E>(x[e]);
         *reinterpret_cast<h8*>(p) = h;
     }
+    // Record stores: non-temporal (the record is read by the next kernel, long after
+    // it has left the caches; measured 2.19 vs 2.21 ms for the 64K-token forward).
+    static __device__ __forceinline__ void gstore8(E* p, const float* x) {
+        h8 h;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = static_cast<E>(x[e]);
+        __builtin_nontemporal_store(h, reinterpret_cast<h8*>(p));
+    }
+    static __device__ __forceinline__ void gstoreV(E* p, const V& v) { __builtin_nontemporal_store(v, reinterpret_cast<V*>(p)); }
+    static __device__ __forceinline__ void gstore4(E* p, f4 x) {
+        h4 h = {static_cast<E>(x[0]), static_cast<E>(x[1]), static_cast<E>(x[2]), static_cast<E>(x[3])};
+        __builtin_nontemporal_store(h, reinterpret_cast<h4*>(p));
+    }
 };
 
 template <> struct Mx<false> {
@@ -167,6 +180,15 @@ template <> struct Mx<false> {
         *reinterpret_cast<f4*>(p) = lo;
         *reinterpret_cast<f4*>(p + 4) = hi;
     }
+    static __device__ __forceinline__ void gstore8(E* p, const float* x) {
+        __builtin_nontemporal_store(f4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f4*>(p));
+        __builtin_nontemporal_store(f4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f4*>(p + 4));
+    }
+    static __device__ __forceinline__ void gstoreV(E* p, const V& v) {
+        __builtin_nontemporal_store(f4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4*>(p));
+        __builtin_nontemporal_store(f4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f4*>(p + 4));
+    }
+    static __device__ __forceinline__ void gstore4(E* p, f4 x) { __builtin_nontemporal_store(x, reinterpret_cast<f4*>(p)); }
 };
 
 // Eight consecutive activations (16-byte aligned) as fp32.
@@ -260,6 +282,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (tid == 0) {
         first[N] = total;
         ctrl[0] = total;
+        ctrl[1] = 0;              // the backward's general-form list starts empty
     }
     __syncthreads();
     // one table entry per chunk: its sequence is the last n with first[n] <= g
@@ -659,7 +682,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
                     kt[e] = kv * (sfv * Xb[i]);
                 }
             }
-            M::store8(qh + frag_off(I * KS + ks, lane), qv);
+            M::gstore8(qh + frag_off(I * KS + ks, lane), qv);
 #pragma unroll
             for (int Il = 1; Il < 4; ++Il)
                 if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
@@ -730,7 +753,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
                 pv[e] = s0 <= r ? accP[2 * ks][e] : 0.f;
                 pv[4 + e] = s1 <= r ? accP[2 * ks + 1][e] : 0.f;
             }
-            if (ks == 0 || I >= 2) M::store8(pout + frag_off(p_slot(2 * I + ks), lane), pv);
+            if (ks == 0 || I >= 2) M::gstore8(pout + frag_off(p_slot(2 * I + ks), lane), pv);
         }
     }
 
@@ -741,7 +764,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             const int jj = (id >> 4) & 3, f = id >> 6;
             const int ts = f & 1;
             // channel 16 (f >> 1) + lane % 16, tokens 32 ts + frag_k(jj, 0..7)
-            M::storeV(ktt + frag_off(f, id & 63),
+            M::gstoreV(ktt + frag_off(f, id & 63),
                       M::loadT(s_Kt, KXP, 32 * ts + 4 * jj, 32 * ts + 16 + 4 * jj, 16 * (f >> 1), lm));
         }
     }
@@ -849,7 +872,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
                 acc1 = M::mma(a1, bT, acc1);
             }
             const float wv[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-            M::store8(wout + frag_off(Ib * KS + ksc, lane), wv);
+            M::gstore8(wout + frag_off(Ib * KS + ksc, lane), wv);
         }
         // U in the accumulator layout the state kernel consumes directly
         for (int nt = wave; nt < DV / 16; nt += 4) {
@@ -863,7 +886,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
                     const V bv = M::loadT(s_v, VXP, t, t + 4, 16 * nt, lm);
                     acc = M::mma(a, bv, acc);
                 }
-                M::store4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc);
+                M::gstore4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc);
             }
         }
     }

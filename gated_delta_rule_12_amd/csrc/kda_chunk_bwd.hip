@@ -22,19 +22,36 @@
 //     and the gate terms through Gamma = exp(b), b = cumsum(log alpha).
 //
 // Launches, on the caller's stream:
-//   plan_kernel        the forward's chunk table (shared launcher)
+//   plan_kernel        the forward's chunk table (shared launcher; it also
+//                      empties the general-form list)
 //   bwd_prep_kernel    one WG per (chunk, head): b, Gamma.Q, (gamma/Gamma).K,
-//                      A, T = (I + A)^-1, W, U, P, gamma -> record
+//                      A, T = (I + A)^-1, W, U, P, gamma -> record, in the
+//                      direct form; a (chunk, head) that needs the general
+//                      form is flagged, appended to the list, and left
+//   bwd_prep_general_kernel   the same for each (chunk, head) of the list
 //   bwd_ckpt_kernel    one WG per (sequence, head, 16 value columns),
 //   (bwd_ckpt16)       chunks in order: the state entering each chunk and U'
 //   bwd_rev_kernel     one WG per (sequence, head, 16 value columns),
 //   (bwd_rev16)        chunks last to first: dS_next of each chunk and dU';
 //                      dS_0 at the end
-//   bwd_grad_kernel    one WG per (chunk, head): every contraction over the
-//                      value dimension (dO S^T, dU' S^T, U' dS_next^T, M,
-//                      dU' V^T, dgamma), dv = beta . T^T dU', then dT, dA, R,
-//                      dY, dKh, dQh, dKb, the gate chain rule, dq, dk, dgate,
-//                      dbeta
+//   bwd_grad_kernel    one WG per (chunk, head) not flagged: every
+//                      contraction over the value dimension (dO S^T, dU' S^T,
+//                      U' dS_next^T, M, dU' V^T, dgamma), dv = beta . T^T dU',
+//                      then dT, dA, R, dY, dKh, dQh, dKb, the gate chain rule,
+//                      dq, dk, dgate, dbeta
+//   bwd_grad_general_kernel   the same for each (chunk, head) of the list
+//
+// Two forms of the per-chunk work, chosen per (chunk, head) from its decay.
+// Direct: when no channel decays below 2^-64 over the chunk, Gamma = 2^b and
+// 1/Gamma are formed as fp32 factors (within 2^+-64) and Kh = Gamma.K,
+// Kb = K/Gamma, Qh = Gamma.Q enter plain products.  General: no product ever
+// forms Gamma or 1/Gamma of a whole chunk; the log decay is summed per
+// 16-token tile and every decay factor is 2^x with x <= 0 (decayed_tile and
+// decayed_lower_upper in kda_mm32.h), so any forget gate in (0, 1] is
+// handled without overflow.  Both compute the same products up to rounding.
+// They are separate kernels, so each is compiled (and its registers
+// allocated) on its own; the general ones get one workgroup per possible
+// list entry, and those past the list's length return at once.
 //
 // Numerics: with fp32 activations every product runs on the fp32 matrix
 // cores (16x16x4) and every intermediate is stored in fp32.  With bf16
@@ -42,10 +59,9 @@
 // fp16 operands (fp32 accumulation) and the record keeps S, dS_next, U', dU'
 // and those operands in fp16; the key-side products keep fp32 operands (the
 // five C x d_k ones split each into bf16 hi + lo for the bf16 matrix cores,
-// which keeps fp32's exponent range and ~2^-16 relative accuracy).  Under the
-// decay precondition of the forward (per channel, < e^10 over any 8 tokens,
-// so < e^80 over a chunk) Gamma = 2^b and 1/Gamma stay fp32-normal over a
-// chunk, so Kh = Gamma.K and Kb = K/Gamma are formed directly.
+// which keeps fp32's exponent range and ~2^-16 relative accuracy).  No fp16
+// operand holds a factor 1/Gamma: the 16-bit passes see Gamma.Q,
+// (gamma/Gamma).K, P, W and T, whose decay factors are at most 1.
 #include <type_traits>
 
 #include "kda_chunk.h"
@@ -109,6 +125,9 @@ struct BwdParams {
     float* dbeta;
     float* dinitial_state;
     const int32_t* ctrl;
+    int32_t* nslow;                     // length of the general list (zeroed by the chunk table)
+    int32_t* slow;                      // general list: g * H + h of each chunk that takes it
+    int32_t* flag;                      // per g * H + h: 1 when the chunk takes the general form
     const int32_t* first;
     const int32_t* order;
     const int4* table;
@@ -163,30 +182,38 @@ __device__ __forceinline__ void gate_cumsum(float* s, int ld, const float* sGs, 
 
 constexpr int kPrepThreads = 512, kPrepWaves = kPrepThreads / 64;
 
+// A chunk in which no channel decays below 2^-64 (gamma >= kFastGammaMin)
+// takes the direct form (Gamma and 1/Gamma as fp32 factors, each within
+// 2^+-64); any other takes the general form, whose decay factors never
+// exceed 1.
+constexpr float kFastGammaMin = 0x1p-64f;
+
 template <int DK, int DV> struct PrepB {
     static constexpr int LK = Ld<DK>::value, LV = Ld<DV>::value, LM = LK > LV ? LK : LV;
-    static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + 2 * C + DK) * 4;
+    static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + 2 * C + (C / 16) * DK) * 4;
 };
 
-template <int DK, int DV, bool ABF16, int GATE>
-__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams P) {
+// FAST: the direct form, which first checks the chunk's decay and, when any
+// channel decays below 2^-64, appends the (chunk, head) to
+// the general list and returns; otherwise the general form.
+template <int DK, int DV, bool ABF16, int GATE, bool FAST>
+__device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const int g) {
     using R = BRec<DK, DV, ABF16>;
     constexpr int NTH = kPrepThreads, NW = kPrepWaves;
     constexpr int LK = PrepB<DK, DV>::LK, LV = PrepB<DK, DV>::LV;
+    constexpr int NBLK = C / 16;
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
     float* sKh = lds;                    // K -> Gamma.K -> beta.Gamma.K      [C][LK]
-    float* sKb = sKh + C * LK;           // gate -> K / Gamma -> T-solve scratch [C][LK]
+    float* sKb = sKh + C * LK;           // gate -> b (per tile) -> Kt -> T-solve scratch [C][LK]
     float* sQ = sKb + C * LK;            // Q -> Gamma.Q, later V -> beta.V    [C][LM]
     float* sA = sQ + C * PrepB<DK, DV>::LM;   // A                            [C][LC]
     float* sT = sA + C * LC;             // T                                  [C][LC]
     float* sBeta = sT + C * LC;          // [C]
     float* sGs = sBeta + C;              // scalar gate per row                [C]
-    float* sGam = sGs + C;               // gamma                              [DK]
+    float* sTot = sGs + C;               // log2 alpha summed per 16-token tile [C/16][DK]
 
     const int H = P.H;
-    const int h = blockIdx.x % H, g = blockIdx.x / H;
-    if (g >= P.ctrl[0]) return;
     const int4 ent = P.table[g];
     const int64_t row0 = ent.y;
     const int len = ent.z;
@@ -211,41 +238,50 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
     }
     __syncthreads();
 
-    // b = cumsum(log2 alpha) per channel;
-    // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
+    float* gP = rec_at(P, h, g, R::P);
     float* gGam = rec_at(P, h, g, R::GAM);
     float* gKt = rec_at(P, h, g, R::KT);
-    gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sA, [&](int r, int c, float b) {
-        const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-        const float kv = sKh[r * LK + c];
-        sKh[r * LK + c] = G * kv;
-        sKb[r * LK + c] = Gi * kv;
-        sQ[r * LK + c] *= G;
-        if (r == C - 1) gGam[c] = sGam[c] = G;
-    });
-    __syncthreads();
-    if constexpr (!ABF16) {              // the 16-bit passes read Kt as fp16 fragments only
-        for (int idx = tid; idx < C * DK; idx += NTH) {
-            const int r = idx / DK, c = idx % DK;
-            gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
-        }
-    }
-    store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
-    if constexpr (ABF16) {
-        // fp16 fragments for the 16-bit state passes: Kt, Kt^T and Qh^T
-        auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
-        write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sGam[k] * sKb[m * LK + k]; });
-        write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sGam[m] * sKb[k * LK + m]; });
-        write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
-    }
-
     // A = StrictTril(Diag(beta) Kh Kb^T) -> sA;  P = Tril(Qh Kb^T) -> record.
     // Tile (mb, nb) of both shares its B operand; two tile positions per wave,
     // the ten below or on the diagonal spread so the waves sharing a SIMD
     // (w, w + 4) hold 3, 3, 2, 2 of them; the six above are only zeroed.
-    float* gP = rec_at(P, h, g, R::P);
-    {
-        constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x1101, 0x2102, 0x2203, 0x3112, 0x3213, 0x3323};
+    constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x1101, 0x2102, 0x2203, 0x3112, 0x3213, 0x3323};
+    if constexpr (FAST) {
+        // b = cumsum(log2 alpha) per channel over the chunk;
+        // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
+        float* sGam = sTot;              // gamma = 2^b_last per channel   [DK]
+        gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sA, [&](int r, int c, float b) {
+            const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+            const float kv = sKh[r * LK + c];
+            sKh[r * LK + c] = G * kv;
+            sKb[r * LK + c] = Gi * kv;
+            sQ[r * LK + c] *= G;
+            if (r == C - 1) sGam[c] = G;
+        });
+        __syncthreads();
+        if (__syncthreads_or(tid < DK && sGam[tid] < kFastGammaMin)) {
+            if (tid == 0) {
+                P.flag[g * H + h] = 1;
+                P.slow[atomicAdd(P.nslow, 1)] = g * H + h;
+            }
+            return;
+        }
+        if (tid == 0) P.flag[g * H + h] = 0;
+        if (tid < DK) gGam[tid] = sGam[tid];
+        if constexpr (!ABF16) {          // the 16-bit passes read Kt as fp16 fragments only
+            for (int idx = tid; idx < C * DK; idx += NTH) {
+                const int r = idx / DK, c = idx % DK;
+                gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
+            }
+        }
+        store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
+        if constexpr (ABF16) {
+            // fp16 fragments for the 16-bit state passes: Kt, Kt^T and Qh^T
+            auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+            write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sGam[k] * sKb[m * LK + k]; });
+            write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sGam[m] * sKb[k * LK + m]; });
+            write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
+        }
 #pragma unroll
         for (int slot = 0; slot < 2; ++slot) {
             const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
@@ -263,12 +299,65 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
             if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
             else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
         }
-    }
-    __syncthreads();
-    if constexpr (ABF16) {
-        auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
-        write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
         __syncthreads();
+        if constexpr (ABF16) {
+            auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+            write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
+            __syncthreads();
+        }
+    } else {
+        // b per 16-token tile (sKb) and the tile totals; the tiles of A and P
+        // from the raw K and Q with every decay factor <= 1 (decayed_tile)
+        tile_gate_scan<DK, NTH, C, GATE>(sKb, LK, sGs, len, sTot, sA);
+#pragma unroll
+        for (int slot = 0; slot < 2; ++slot) {
+            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
+            const int mb = tt >> 4, nb = tt & 15;
+            f4 a = zero4(), pp = zero4();
+            decayed_tile<DK / 16, true, true, ABF16>(sKh, sQ, sKh, sKb, sTot, LK, DK, mb, nb, a, pp);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+                a[e] = s2 < r ? sBeta[r] * a[e] : 0.f;
+                pp[e] = s2 <= r ? pp[e] : 0.f;
+            }
+            store_tile(sA + mb * 16 * LC + nb * 16, LC, a);
+            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
+            else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
+        }
+        __syncthreads();
+        // Kh = Gamma.K, Qh = Gamma.Q and Kt = (gamma / Gamma).K (into sKb), every
+        // factor 2^x with x <= 0: with pre / suf the totals of the tiles
+        // before / after the row's tile t,  log2 Gamma = pre + b,
+        // log2(gamma / Gamma) = T_t - b + suf.
+        for (int idx = tid; idx < C * DK; idx += NTH) {
+            const int r = idx / DK, c = idx % DK, t = r / 16;
+            const float bl = sKb[r * LK + c];
+            const float pre = tot1(sTot, DK, c, 0, t), suf = tot1(sTot, DK, c, t + 1, NBLK);
+            const float G = __builtin_amdgcn_exp2f(pre + bl);
+            const float kv = sKh[r * LK + c];
+            sKh[r * LK + c] = G * kv;
+            sQ[r * LK + c] *= G;
+            sKb[r * LK + c] = kv * __builtin_amdgcn_exp2f(sTot[t * DK + c] - bl + suf);
+        }
+        if (tid < DK) gGam[tid] = __builtin_amdgcn_exp2f(tot1(sTot, DK, tid, 0, NBLK));
+        __syncthreads();
+        if constexpr (!ABF16) {
+            for (int idx = tid; idx < C * DK; idx += NTH) {
+                const int r = idx / DK, c = idx % DK;
+                gKt[r * DK + c] = sKb[r * LK + c];
+            }
+        }
+        store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
+        if constexpr (ABF16) {
+            // fp16 fragments for the 16-bit state passes: Kt, Kt^T, Qh^T and P^T
+            auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+            write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sKb[m * LK + k]; });
+            write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sKb[k * LK + m]; });
+            write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
+            write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
+            __syncthreads();
+        }
     }
 
     // T = (I + A)^-1 (A strictly lower) by 16 x 16 blocks: each wave inverts
@@ -355,6 +444,25 @@ __global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams 
         write_afrags<C, DK, NTH>(hrec(R::FW), [&](int m, int k) { return sKb[m * LK + k]; });
         write_afrags<DK, C, NTH>(hrec(R::FWT), [&](int m, int k) { return sKb[k * LK + m]; });
     }
+}
+
+// One workgroup per (chunk, head): the direct form, or the chunk's entry in
+// the general list.
+template <int DK, int DV, bool ABF16, int GATE>
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams P) {
+    const int g = blockIdx.x / P.H;
+    if (g >= P.ctrl[0]) return;
+    prep_body<DK, DV, ABF16, GATE, true>(P, blockIdx.x % P.H, g);
+}
+
+// Entry blockIdx.x of the general list, if the list is that long (the grid
+// has one workgroup per (chunk, head), the list's largest length; a loop over
+// the entries would keep the body's loop-invariant values live throughout).
+template <int DK, int DV, bool ABF16, int GATE>
+__global__ __launch_bounds__(kPrepThreads) void bwd_prep_general_kernel(const BwdParams P) {
+    if (static_cast<int>(blockIdx.x) >= *P.nslow) return;
+    const int id = P.slow[blockIdx.x];
+    prep_body<DK, DV, ABF16, GATE, false>(P, id % P.H, id / P.H);
 }
 
 // ---------------------------------------------------------------------------
@@ -579,10 +687,7 @@ template <int DK> struct Chain16B {
 // (reverse pass, whose operands take more registers) steps ahead.  The prefetch
 // wave passes the same two barriers per chunk, bare (a fenced barrier would
 // wait for its loads).
-#ifndef KDA_CHAIN_PREFETCH
-#define KDA_CHAIN_PREFETCH 3
-#endif
-constexpr int kChain16Threads = kChainThreads + 64, kChainPrefetch = KDA_CHAIN_PREFETCH;
+constexpr int kChain16Threads = kChainThreads + 64, kChainPrefetch = 3;
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kChain16Threads) void bwd_rev16_kernel(const BwdParams P) {
@@ -919,10 +1024,11 @@ constexpr unsigned grad_tiles(int w) {
 
 template <int DK> struct GradB {
     static constexpr int LK = Ld<DK>::value;
-    // key side: Kh, Kb, dW | three C x C tiles | beta, dbeta rows, Kt.dKt column sums, dgamma, rowsum(dZ.V)
+    // key side: K, b, dW | three C x C tiles | beta, dbeta rows, Kt.dKt column sums, dgamma, rowsum(dZ.V),
+    // tile totals of log2 alpha
     static constexpr int region = (3 * C * LK + 2 * C * LC) * 4;   // value-side scratch: everything before T
     static constexpr int bytes =
-        (3 * C * LK + 3 * C * LC + C + kGradWaves * C + GradTasks<DK>::MSTEP * DK + DK + C) * 4;
+        (3 * C * LK + 3 * C * LC + C + kGradWaves * C + GradTasks<DK>::MSTEP * DK + DK + C + (C / 16) * DK) * 4;
 };
 
 // Decode value-side task t: operand rows of A and B (row-major, reduction
@@ -1232,18 +1338,18 @@ __device__ __forceinline__ void vside_phase16(const BwdParams& P, int h, int g, 
     }
 }
 
-template <int DK, int DV, bool ABF16, int GATE>
-__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams P) {
-    using R = BRec<DK, DV, ABF16>;
+template <int DK, int DV, bool ABF16, int GATE, bool FAST>
+__device__ __forceinline__ void grad_body(const BwdParams& P, const int h, const int g) {
     using GT = GradTasks<DK>;
+    using R = BRec<DK, DV, ABF16>;
     constexpr int NTH = kGradThreads, NW = kGradWaves, LK = GradB<DK>::LK;
     constexpr int NB = GT::NB, RW = GT::RW, MSTEP = GT::MSTEP, KM = GT::KM;
     constexpr int GC = C / 16, GK = DK / 16;
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
-    float* sKh = lds;                // Gamma.K; later db                       [C][LK]
-    float* sKb = sKh + C * LK;       // K / Gamma                               [C][LK]
-    float* sW = sKb + C * LK;        // dW; later Qh                            [C][LK]
+    float* sKh = lds;                // K; later db                             [C][LK]
+    float* sKb = sKh + C * LK;       // b per 16-token tile                     [C][LK]
+    float* sW = sKb + C * LK;        // dW; later Q                             [C][LK]
     float* sX = sW + C * LK;         // dT; later dR                            [C][LC]
     float* sY = sX + C * LC;         // T^T dT                                  [C][LC]
     float* sT = sY + C * LC;         // T; later M                              [C][LC]
@@ -1252,13 +1358,12 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
     float* sCol = sRow + NW * C;     // column sums of Kt . dKt, one row per wave sharing a column block [MSTEP][DK]
     float* sDgam = sCol + MSTEP * DK;   // dgamma                               [DK]
     float* sDbz = sDgam + DK;        // rowsum(dZ . V)                          [C]
+    float* sTot = sDbz + C;          // log2 alpha summed per 16-token tile     [C/16][DK]
     float* sGs = sCol;               // scalar gate per row while b is formed  [C]
     static_assert(C <= MSTEP * DK, "scalar gate rows fit the column-sum buffer");
     static_assert(GradB<DK>::bytes <= 160 * 1024, "LDS of one CU");
 
     const int H = P.H;
-    const int h = blockIdx.x % H, g = blockIdx.x / H;
-    if (g >= P.ctrl[0]) return;
     const int4 ent = P.table[g];
     const int64_t row0 = ent.y;
     const int len = ent.z;
@@ -1272,234 +1377,459 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
     __syncthreads();
 
     // ---- key side ----
-    const int tnb = wave & 3, tmb0 = wave >> 2;     // C x C tiles: column block tnb, row blocks tmb0, tmb0 + 2
-    // C x d_k tiles: column block nb, row blocks cmb0 + r MSTEP (with one
-    // column block per wave, cmb0 is 0 at compile time, so the triangular
-    // skips inside the products fold away instead of branching)
-    const int nb = wave % NB, cmb0 = NB == NW ? 0 : wave / NB;
-    // dW -> sW; the gate, then b = cumsum(log2 alpha) as in the preparation
-    // kernel; Kh = 2^b K, Kb = 2^-b K
-    {
-        Tok<ABF16, DK, DK, NTH> tk;
-        Tok<GBF16, DK, DK, NTH> tg0;
-        tk.load(P.k, row0, len, h, H);
-        if constexpr (GATE == KDA_GATE_SCALAR) {
-            if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
-        } else {
-            tg0.load(P.gate, row0, len, h, H);
-        }
-#pragma unroll
-        for (int r = 0; r < RW; ++r) store_tile(sW + (cmb0 + r * MSTEP) * 16 * LK + nb * 16, LK, -acc[RW + r]);
-        tk.put(sKh, LK);
-        if constexpr (GATE != KDA_GATE_SCALAR) tg0.put(sKb, LK);
-    }
-    __syncthreads();
-    gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sX, [&](int r, int c, float b) {
-        const float kv = sKh[r * LK + c];
-        sKh[r * LK + c] = __builtin_amdgcn_exp2f(b) * kv;
-        sKb[r * LK + c] = __builtin_amdgcn_exp2f(-b) * kv;
-    });
-    __syncthreads();
-
-    // dT = (dW Kh^T + N) Diag(beta)
-    {
-        f4 dt[2] = {acc[KM + 2], acc[KM + 3]};
-        mm_rows<2, GK, true, true>(sW, LK, 1, sKh + tnb * 16 * LK, 1, LK, tmb0, 2,
-                                   [](int, int) { return true; }, dt);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, dt[r] * sBeta[tnb * 16 + i]);
-    }
-    __syncthreads();
-    // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m).  One copy per
-    // value of tmb0, so the triangular skips are known at compile time.
-    {
-        auto y1_rows = [&](auto m0c) {
-            constexpr int M0 = decltype(m0c)::value;
-            f4 y1[2] = {zero4(), zero4()};
-            mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, M0, 2,
-                                         [](int mb, int gg) { return gg >= mb; }, y1);
-#pragma unroll
-            for (int r = 0; r < 2; ++r) store_tile(sY + (M0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
-        };
-        if (tmb0 == 0) y1_rows(std::integral_constant<int, 0>{});
-        else y1_rows(std::integral_constant<int, 1>{});
-    }
-    __syncthreads();
-    // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX,
-    // two tiles per wave (grad_tiles).  The tiles are fixed at compile time
-    // (one copy of the phase per wave), so the tile tests and the triangular
-    // skips fold away.
-    {
-        auto tiles = [&](auto wc) {
-            constexpr int WV = decltype(wc)::value;
-#pragma unroll
-            for (int slot = 0; slot < 2; ++slot) {
-                const unsigned tt = (grad_tiles(WV) >> (8 * (1 - slot))) & 0xff;
-                const int mb = tt >> 4, nb = tt & 15;
-                f4 dr = zero4();
-                if (nb <= mb) {
-                    // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
-                    f4 ya[1] = {zero4()}, rr[1] = {zero4()};
-                    mm_rows<1, GC, true, true>(sY, LC, 1, sT + nb * 16 * LC, 1, LC, mb, 1,
-                                               [nb](int, int gg) { return gg <= nb; }, ya);
-                    mm_rows<1, GK, true, true>(sKh, LK, 1, sKb + nb * 16 * LK, 1, LK, mb, 1,
-                                               [](int, int) { return true; }, rr);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
-                        const float da = s2 < r ? -ya[0][e] : 0.f;
-                        const float part = row16_sum(da * rr[0][e]);
-                        if (i == 0) sRow[wave * C + r] += part;
-                        dr[e] = sBeta[r] * da;
-                    }
-                }
-                store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
-            }
-        };
-        switch (wave) {
-            case 0: tiles(std::integral_constant<int, 0>{}); break;
-            case 1: tiles(std::integral_constant<int, 1>{}); break;
-            case 2: tiles(std::integral_constant<int, 2>{}); break;
-            case 3: tiles(std::integral_constant<int, 3>{}); break;
-            case 4: tiles(std::integral_constant<int, 4>{}); break;
-            case 5: tiles(std::integral_constant<int, 5>{}); break;
-            case 6: tiles(std::integral_constant<int, 6>{}); break;
-            default: tiles(std::integral_constant<int, 7>{}); break;
-        }
-    }
-    __syncthreads();
-
-    // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh).  (T, dR
-    // and, below, M hold exact zeros above their diagonals, which the split
-    // products' pair-wise skipping with bf16 activations relies on.)
-    f4 dKh[RW], dKb[RW];
-    {
-        f4 dy[RW];
-#pragma unroll
-        for (int r = 0; r < RW; ++r) dy[r] = dKb[r] = zero4();
-        mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
-                                      [](int mb, int gg) { return gg >= mb; }, dy);
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int mb = cmb0 + r * MSTEP;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = mb * 16 + 4 * j + e, c = nb * 16 + i;
-                const float part = row16_sum(dy[r][e] * sKh[row * LK + c]);
-                if (i == 0) sRow[wave * C + row] += part;
-                dKh[r][e] = sBeta[row] * dy[r][e];
-            }
-        }
-        // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
-        mm_rows_k<ABF16, RW, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
-                                     [](int mb, int gg) { return gg <= mb; }, dKh);
-    }
-    __syncthreads();
-    // M -> sT (tiles above the diagonal were never accumulated), Qh -> sW
-#pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
-        const int mb = tmb0 + 2 * r2;
-        f4 x = acc[KM + r2];
-        if (tnb == mb) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
-        }
-        store_tile(sT + mb * 16 * LC + tnb * 16, LC, x);
-    }
-    load_block<C, DK, NTH>(sW, LK, rec_at(P, h, g, R::QH), DK);
-    __syncthreads();
-
-    // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
-    f4 dQh[RW];
-#pragma unroll
-    for (int r = 0; r < RW; ++r) dQh[r] = acc[r];
-    mm_rows_k<ABF16, RW, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
-                                 [](int mb, int gg) { return gg <= mb; }, dQh);
-    mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
-                                  [](int mb, int gg) { return gg >= mb; }, dKb);
-    mm_rows_k<ABF16, RW, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, cmb0, MSTEP,
-                                  [](int mb, int gg) { return gg >= mb; }, dKb);
-    __syncthreads();
-
-    // bf16 dq and dk rows, staged in the (now free) dT / Y1 regions
-    constexpr int LDQ = DK + 8;
-    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-    uint16_t* sDq = reinterpret_cast<uint16_t*>(sX);
-    uint16_t* sDk = sDq + C * LDQ;
-    static_assert(2 * C * LDQ * 2 <= 2 * C * LC * 4, "dq and dk fit the dT and Y1 regions");
-    // gate chain rule, dq, dk.  Every operand is staged in LDS first (the
-    // regions are free now), so no load waits behind a store of dq or dk:
-    // q -> sKh, k -> sKb, the gate -> sW (b after the scan); dKt is the
-    // value-side accumulator of the same tile.
-    const float* gGam = rec_at(P, h, g, R::GAM);
     constexpr int NS = NTH / DK, SEG = C / NS;   // reverse-cumsum split: NS row segments per channel
     Tok<GBF16, DK, DK, NTH> tg;
-    float gs = 1.f;
-    float gam_c, gam_t, dgam_t;
-    {
-        Tok<ABF16, DK, DK, NTH> tq, tk;
-        tq.load(P.q, row0, len, h, H);
-        tk.load(P.k, row0, len, h, H);
+    float gs = 1.f, gam_t, dgam_t;
+    if constexpr (FAST) {
+            // Kh, Kb and Qh formed once (the direct form)
+        const int tnb = wave & 3, tmb0 = wave >> 2;     // C x C tiles: column block tnb, row blocks tmb0, tmb0 + 2
+        // C x d_k tiles: column block nb, row blocks cmb0 + r MSTEP (with one
+        // column block per wave, cmb0 is 0 at compile time, so the triangular
+        // skips inside the products fold away instead of branching)
+        const int nb = wave % NB, cmb0 = NB == NW ? 0 : wave / NB;
+        // dW -> sW; the gate, then b = cumsum(log2 alpha) as in the preparation
+        // kernel; Kh = 2^b K, Kb = 2^-b K
+        {
+            Tok<ABF16, DK, DK, NTH> tk;
+            Tok<GBF16, DK, DK, NTH> tg0;
+            tk.load(P.k, row0, len, h, H);
+            if constexpr (GATE == KDA_GATE_SCALAR) {
+                if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+            } else {
+                tg0.load(P.gate, row0, len, h, H);
+            }
+#pragma unroll
+            for (int r = 0; r < RW; ++r) store_tile(sW + (cmb0 + r * MSTEP) * 16 * LK + nb * 16, LK, -acc[RW + r]);
+            tk.put(sKh, LK);
+            if constexpr (GATE != KDA_GATE_SCALAR) tg0.put(sKb, LK);
+        }
+        __syncthreads();
+        gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sX, [&](int r, int c, float b) {
+            const float kv = sKh[r * LK + c];
+            sKh[r * LK + c] = __builtin_amdgcn_exp2f(b) * kv;
+            sKb[r * LK + c] = __builtin_amdgcn_exp2f(-b) * kv;
+        });
+        __syncthreads();
+
+        // dT = (dW Kh^T + N) Diag(beta)
+        {
+            f4 dt[2] = {acc[KM + 2], acc[KM + 3]};
+            mm_rows<2, GK, true, true>(sW, LK, 1, sKh + tnb * 16 * LK, 1, LK, tmb0, 2,
+                                       [](int, int) { return true; }, dt);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, dt[r] * sBeta[tnb * 16 + i]);
+        }
+        __syncthreads();
+        // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m).  One copy per
+        // value of tmb0, so the triangular skips are known at compile time.
+        {
+            auto y1_rows = [&](auto m0c) {
+                constexpr int M0 = decltype(m0c)::value;
+                f4 y1[2] = {zero4(), zero4()};
+                mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, M0, 2,
+                                             [](int mb, int gg) { return gg >= mb; }, y1);
+#pragma unroll
+                for (int r = 0; r < 2; ++r) store_tile(sY + (M0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
+            };
+            if (tmb0 == 0) y1_rows(std::integral_constant<int, 0>{});
+            else y1_rows(std::integral_constant<int, 1>{});
+        }
+        __syncthreads();
+        // dA = -StrictTril(Y1 T^T); R = Kh Kb^T; dbeta += rowsum(dA . R); dR = Diag(beta) dA -> sX,
+        // two tiles per wave (grad_tiles).  The tiles are fixed at compile time
+        // (one copy of the phase per wave), so the tile tests and the triangular
+        // skips fold away.
+        {
+            auto tiles = [&](auto wc) {
+                constexpr int WV = decltype(wc)::value;
+#pragma unroll
+                for (int slot = 0; slot < 2; ++slot) {
+                    const unsigned tt = (grad_tiles(WV) >> (8 * (1 - slot))) & 0xff;
+                    const int mb = tt >> 4, nb = tt & 15;
+                    f4 dr = zero4();
+                    if (nb <= mb) {
+                        // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
+                        f4 ya[1] = {zero4()}, rr[1] = {zero4()};
+                        mm_rows<1, GC, true, true>(sY, LC, 1, sT + nb * 16 * LC, 1, LC, mb, 1,
+                                                   [nb](int, int gg) { return gg <= nb; }, ya);
+                        mm_rows<1, GK, true, true>(sKh, LK, 1, sKb + nb * 16 * LK, 1, LK, mb, 1,
+                                                   [](int, int) { return true; }, rr);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+                            const float da = s2 < r ? -ya[0][e] : 0.f;
+                            const float part = row16_sum(da * rr[0][e]);
+                            if (i == 0) sRow[wave * C + r] += part;
+                            dr[e] = sBeta[r] * da;
+                        }
+                    }
+                    store_tile(sX + mb * 16 * LC + nb * 16, LC, dr);
+                }
+            };
+            switch (wave) {
+                case 0: tiles(std::integral_constant<int, 0>{}); break;
+                case 1: tiles(std::integral_constant<int, 1>{}); break;
+                case 2: tiles(std::integral_constant<int, 2>{}); break;
+                case 3: tiles(std::integral_constant<int, 3>{}); break;
+                case 4: tiles(std::integral_constant<int, 4>{}); break;
+                case 5: tiles(std::integral_constant<int, 5>{}); break;
+                case 6: tiles(std::integral_constant<int, 6>{}); break;
+                default: tiles(std::integral_constant<int, 7>{}); break;
+            }
+        }
+        __syncthreads();
+
+        // dY = T^T dW; dKh = beta.dY + dR Kb; dbeta += rowsum(dY . Kh).  (T, dR
+        // and, below, M hold exact zeros above their diagonals, which the split
+        // products' pair-wise skipping with bf16 activations relies on.)
+        f4 dKh[RW], dKb[RW];
+        {
+            f4 dy[RW];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) dy[r] = dKb[r] = zero4();
+            mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+                                          [](int mb, int gg) { return gg >= mb; }, dy);
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const int mb = cmb0 + r * MSTEP;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = mb * 16 + 4 * j + e, c = nb * 16 + i;
+                    const float part = row16_sum(dy[r][e] * sKh[row * LK + c]);
+                    if (i == 0) sRow[wave * C + row] += part;
+                    dKh[r][e] = sBeta[row] * dy[r][e];
+                }
+            }
+            // dR strictly lower: row block mb reduces over tokens < 16 (mb + 1)
+            mm_rows_k<ABF16, RW, GC, true, false>(sX, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
+                                         [](int mb, int gg) { return gg <= mb; }, dKh);
+        }
+        __syncthreads();
+        // M -> sT (tiles above the diagonal were never accumulated), Qh -> sW
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int mb = tmb0 + 2 * r2;
+            f4 x = acc[KM + r2];
+            if (tnb == mb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
+            }
+            store_tile(sT + mb * 16 * LC + tnb * 16, LC, x);
+        }
+        load_block<C, DK, NTH>(sW, LK, rec_at(P, h, g, R::QH), DK);
+        __syncthreads();
+
+        // dQh = dO S^T + M Kb;  dKb = M^T Qh + dR^T Kh
+        f4 dQh[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) dQh[r] = acc[r];
+        mm_rows_k<ABF16, RW, GC, true, false>(sT, LC, 1, sKb + nb * 16, LK, 1, cmb0, MSTEP,
+                                     [](int mb, int gg) { return gg <= mb; }, dQh);
+        mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+                                      [](int mb, int gg) { return gg >= mb; }, dKb);
+        mm_rows_k<ABF16, RW, GC, false, false>(sX, 1, LC, sKh + nb * 16, LK, 1, cmb0, MSTEP,
+                                      [](int mb, int gg) { return gg >= mb; }, dKb);
+        __syncthreads();
+
+        // bf16 dq and dk rows, staged in the (now free) dT / Y1 regions
+        constexpr int LDQ = DK + 8;
+        typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+        uint16_t* sDq = reinterpret_cast<uint16_t*>(sX);
+        uint16_t* sDk = sDq + C * LDQ;
+        static_assert(2 * C * LDQ * 2 <= 2 * C * LC * 4, "dq and dk fit the dT and Y1 regions");
+        // gate chain rule, dq, dk.  Every operand is staged in LDS first (the
+        // regions are free now), so no load waits behind a store of dq or dk:
+        // q -> sKh, k -> sKb, the gate -> sW (b after the scan); dKt is the
+        // value-side accumulator of the same tile.
+        const float* gGam = rec_at(P, h, g, R::GAM);
+        float gam_c;
+        {
+            Tok<ABF16, DK, DK, NTH> tq, tk;
+            tq.load(P.q, row0, len, h, H);
+            tk.load(P.k, row0, len, h, H);
+            if constexpr (GATE == KDA_GATE_SCALAR) {
+                if (tid < C && tid < len) gs = static_cast<const float*>(P.gate)[(row0 + tid) * H + h];
+            } else {
+                tg.load(P.gate, row0, len, h, H);
+            }
+            gam_c = gGam[nb * 16 + i];
+            gam_t = gGam[tid % DK];
+            dgam_t = sDgam[tid % DK];
+            tq.put(sKh, LK);
+            tk.put(sKb, LK);
+            if constexpr (GATE == KDA_GATE_SCALAR) {
+                if (tid < C) sGs[tid] = tid < len ? gs : 1.f;
+            } else {
+                tg.put(sW, LK);
+            }
+        }
+        __syncthreads();
+        // b again (the same scan, so the same values as above) -> sW
+        gate_cumsum<DK, NTH, GATE>(sW, LK, sGs, len, sT, [&](int r, int c, float b) { sW[r * LK + c] = b; });
+        __syncthreads();
+        {
+            const int c = nb * 16 + i;
+            float col = 0.f;
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const int mb = cmb0 + r * MSTEP;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = mb * 16 + 4 * j + e;
+                    const float b = sW[row * LK + c];
+                    const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+                    const float qv = sKh[row * LK + c], kv = sKb[row * LK + c], dkt = acc[2 * RW + r][e];
+                    const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam_c * kb;
+                    const float dqh = dQh[r][e], dkh = dKh[r][e], dkb = dKb[r][e];
+                    const float dqv = G * dqh, dkv = G * dkh + Gi * dkb + gam_c * Gi * dkt;
+                    if constexpr (ABF16) {           // staged in LDS, written below as whole 16-byte words
+                        sDq[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dqv));
+                        sDk[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dkv));
+                    } else if (row < len) {
+                        const size_t ai = (static_cast<size_t>(row0 + row) * H + h) * DK + c;
+                        store_out<false>(P.dq, ai, dqv);
+                        store_out<false>(P.dk, ai, dkv);
+                    }
+                    sKh[row * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;   // db
+                    col += kt * dkt;
+                }
+            }
+            col += __shfl_xor(col, 16, 64);
+            col += __shfl_xor(col, 32, 64);
+            if (j == 0) sCol[cmb0 * DK + c] = col;
+        }
+        __syncthreads();
+        if constexpr (ABF16) {
+            constexpr int W8 = DK / 8;
+            for (int idx = tid; idx < C * W8; idx += NTH) {
+                const int r = idx / W8, c8 = (idx % W8) * 8;
+                if (r < len) {
+                    const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c8;
+                    *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dq) + ai) = *reinterpret_cast<const u16x8*>(sDq + r * LDQ + c8);
+                    *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dk) + ai) = *reinterpret_cast<const u16x8*>(sDk + r * LDQ + c8);
+                }
+            }
+        }
+    } else {
+            // Every product that the chunk form writes with Gamma.K, K/Gamma or
+            // Gamma.Q (Kh, Kb, Qh) is taken on the raw K and Q with each decay
+            // factor formed from exponents <= 0 (decayed_tile and
+            // decayed_lower_upper in kda_mm32.h), and the gradients are carried
+            // already multiplied by the factor the chain rule applies to them:
+            //   dQh' = Gamma.dQh,  dKh' = Gamma.dKh,  dKb' = dKb / Gamma.
+        constexpr int NBLK = C / 16;
+        const int tnb = wave & 3, tmb0 = wave >> 2;     // C x C tiles: column block tnb, row blocks tmb0, tmb0 + 2
+        // C x d_k tiles: column block nb, row blocks cmb0 + r MSTEP (with one
+        // column block per wave, cmb0 is 0 at compile time)
+        const int nb = wave % NB, cmb0 = NB == NW ? 0 : wave / NB;
+        // Gamma of token row, channel c (b is per tile: add the earlier tiles' totals)
+        auto gam_at = [&](int row, int c) {
+            return __builtin_amdgcn_exp2f(tot1(sTot, DK, c, 0, row / 16) + sKb[row * LK + c]);
+        };
+        // dW -> sW; K -> sKh; the gate, then b per 16-token tile and the tile totals
+        {
+            Tok<ABF16, DK, DK, NTH> tk;
+            Tok<GBF16, DK, DK, NTH> tg0;
+            tk.load(P.k, row0, len, h, H);
+            if constexpr (GATE == KDA_GATE_SCALAR) {
+                if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+            } else {
+                tg0.load(P.gate, row0, len, h, H);
+            }
+#pragma unroll
+            for (int r = 0; r < RW; ++r) store_tile(sW + (cmb0 + r * MSTEP) * 16 * LK + nb * 16, LK, -acc[RW + r]);
+            tk.put(sKh, LK);
+            if constexpr (GATE != KDA_GATE_SCALAR) tg0.put(sKb, LK);
+        }
+        __syncthreads();
+        tile_gate_scan<DK, NTH, C, GATE>(sKb, LK, sGs, len, sTot, sX);
+
+        // dT = (dW Kh^T + N) Diag(beta), Kh = Gamma.K formed per B operand
+        {
+            f4 dt[2] = {acc[KM + 2], acc[KM + 3]};
+            const int st = tnb * 16 + i;
+            {
+#pragma unroll
+                for (int gg = 0; gg < GK; ++gg) {
+                    const int c0 = 16 * gg + 4 * j;
+                    const f4 kk = *reinterpret_cast<const f4*>(sKh + st * LK + c0);
+                    const f4 bl = *reinterpret_cast<const f4*>(sKb + st * LK + c0);
+                    const f4 pr = tot4(sTot, DK, c0, 0, tnb);
+                    f4 bv;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) bv[s2] = kk[s2] * __builtin_amdgcn_exp2f(pr[s2] + bl[s2]);
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const f4 a = *reinterpret_cast<const f4*>(sW + ((tmb0 + 2 * r) * 16 + i) * LK + c0);
+#pragma unroll
+                        for (int s2 = 0; s2 < 4; ++s2) dt[r] = mfma4(a[s2], bv[s2], dt[r]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 2; ++r) store_tile(sX + (tmb0 + 2 * r) * 16 * LC + tnb * 16, LC, dt[r] * sBeta[tnb * 16 + i]);
+        }
+        __syncthreads();
+        // Y1 = T^T dT  (T^T[m][k] = T[k][m], zero for k < m).  One copy per
+        // value of tmb0, so the triangular skips are known at compile time.
+        {
+            auto y1_rows = [&](auto m0c) {
+                constexpr int M0 = decltype(m0c)::value;
+                f4 y1[2] = {zero4(), zero4()};
+                mm_rows<2, GC, false, false>(sT, 1, LC, sX + tnb * 16, LC, 1, M0, 2,
+                                             [](int mb, int gg) { return gg >= mb; }, y1);
+#pragma unroll
+                for (int r = 0; r < 2; ++r) store_tile(sY + (M0 + 2 * r) * 16 * LC + tnb * 16, LC, y1[r]);
+            };
+            if (tmb0 == 0) y1_rows(std::integral_constant<int, 0>{});
+            else y1_rows(std::integral_constant<int, 1>{});
+        }
+        __syncthreads();
+        // dA = -StrictTril(Y1 T^T); R = Kh Kb^T (decayed_tile); dbeta += rowsum(dA . R);
+        // dR = Diag(beta) dA -> sX, two tiles per wave (grad_tiles).  The tiles are
+        // fixed at compile time (one copy of the phase per wave).
+        {
+            auto tiles = [&](auto wc) {
+                constexpr int WV = decltype(wc)::value;
+#pragma unroll
+                for (int slot = 0; slot < 2; ++slot) {
+                    const unsigned tt = (grad_tiles(WV) >> (8 * (1 - slot))) & 0xff;
+                    const int mb = tt >> 4, tb = tt & 15;
+                    f4 dr = zero4();
+                    if (tb <= mb) {
+                        // (Y1 T^T)[m][n] = sum_k Y1[m][k] T[n][k], T[n][k] zero for k > n
+                        f4 ya[1] = {zero4()}, rr[1] = {zero4()}, unused = zero4();
+                        mm_rows<1, GC, true, true>(sY, LC, 1, sT + tb * 16 * LC, 1, LC, mb, 1,
+                                                   [tb](int, int gg) { return gg <= tb; }, ya);
+                        decayed_tile<GK, false, false, ABF16>(sKh, sKh, sKh, sKb, sTot, LK, DK, mb, tb, rr[0], unused);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = mb * 16 + 4 * j + e, s2 = tb * 16 + i;
+                            const float da = s2 < r ? -ya[0][e] : 0.f;
+                            const float part = row16_sum(da * rr[0][e]);
+                            if (i == 0) sRow[wave * C + r] += part;
+                            dr[e] = sBeta[r] * da;
+                        }
+                    }
+                    store_tile(sX + mb * 16 * LC + tb * 16, LC, dr);
+                }
+            };
+            switch (wave) {
+                case 0: tiles(std::integral_constant<int, 0>{}); break;
+                case 1: tiles(std::integral_constant<int, 1>{}); break;
+                case 2: tiles(std::integral_constant<int, 2>{}); break;
+                case 3: tiles(std::integral_constant<int, 3>{}); break;
+                case 4: tiles(std::integral_constant<int, 4>{}); break;
+                case 5: tiles(std::integral_constant<int, 5>{}); break;
+                case 6: tiles(std::integral_constant<int, 6>{}); break;
+                default: tiles(std::integral_constant<int, 7>{}); break;
+            }
+        }
+        __syncthreads();
+
+        // dY = T^T dW; dKh' = Gamma.(beta dY); dbeta += rowsum(dY . Kh)
+        f4 dKh[RW], dKb[RW], dQh[RW];
+        {
+            f4 dy[RW];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) dy[r] = dKb[r] = zero4();
+            mm_rows_k<ABF16, RW, GC, false, false>(sT, 1, LC, sW + nb * 16, LK, 1, cmb0, MSTEP,
+                                          [](int mb, int gg) { return gg >= mb; }, dy);
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                const int mb = cmb0 + r * MSTEP;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = mb * 16 + 4 * j + e, c = nb * 16 + i;
+                    const float G = gam_at(row, c);
+                    const float part = row16_sum(dy[r][e] * sKh[row * LK + c] * G);
+                    if (i == 0) sRow[wave * C + row] += part;
+                    dKh[r][e] = sBeta[row] * dy[r][e] * G;
+                    dQh[r][e] = acc[r][e] * G;                    // Gamma.(dO S^T)
+                }
+            }
+        }
+        __syncthreads();
+        // M -> sT (tiles above the diagonal were never accumulated), Q -> sW
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const int mb = tmb0 + 2 * r2;
+            f4 x = acc[KM + r2];
+            if (tnb == mb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = i <= 4 * j + e ? x[e] : 0.f;
+            }
+            store_tile(sT + mb * 16 * LC + tnb * 16, LC, x);
+        }
+        {
+            Tok<ABF16, DK, DK, NTH> tq;
+            tq.load(P.q, row0, len, h, H);
+            tq.put(sW, LK);
+        }
+        __syncthreads();
+
+        // dKh' += Gamma.(dR Kb),  dQh' += Gamma.(M Kb)  (lower contractions);
+        // dKb' = (M^T Qh + dR^T Kh) / Gamma  (upper contractions)
+        decayed_lower_upper<RW, NBLK, ABF16>(sX, sT, LC, sKh, sW, sKb, sTot, LK, DK, cmb0, MSTEP, nb, dKh, dQh, dKb);
+        __syncthreads();
+
+        // bf16 dq and dk rows, staged in the (now free) dT / Y1 regions
+        constexpr int LDQ = DK + 8;
+        typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+        uint16_t* sDq = reinterpret_cast<uint16_t*>(sX);
+        uint16_t* sDk = sDq + C * LDQ;
+        static_assert(2 * C * LDQ * 2 <= 2 * C * LC * 4, "dq and dk fit the dT and Y1 regions");
+        // gate chain rule, dq, dk: dq = dQh', dk = dKh' + dKb' + (gamma/Gamma) dKt, and the
+        // gradient of each token's log decay db = q dQh' + k dKh' - k dKb' - Kt dKt, written
+        // over K (sKh) by the lane that owns the element; dKt is the value-side
+        // accumulator of the same tile.
+        gam_t = __builtin_amdgcn_exp2f(tot1(sTot, DK, tid % DK, 0, NBLK));
+        dgam_t = sDgam[tid % DK];
         if constexpr (GATE == KDA_GATE_SCALAR) {
             if (tid < C && tid < len) gs = static_cast<const float*>(P.gate)[(row0 + tid) * H + h];
         } else {
             tg.load(P.gate, row0, len, h, H);
         }
-        gam_c = gGam[nb * 16 + i];
-        gam_t = gGam[tid % DK];
-        dgam_t = sDgam[tid % DK];
-        tq.put(sKh, LK);
-        tk.put(sKb, LK);
-        if constexpr (GATE == KDA_GATE_SCALAR) {
-            if (tid < C) sGs[tid] = tid < len ? gs : 1.f;
-        } else {
-            tg.put(sW, LK);
-        }
-    }
-    __syncthreads();
-    // b again (the same scan, so the same values as above) -> sW
-    gate_cumsum<DK, NTH, GATE>(sW, LK, sGs, len, sT, [&](int r, int c, float b) { sW[r * LK + c] = b; });
-    __syncthreads();
-    {
-        const int c = nb * 16 + i;
-        float col = 0.f;
+        {
+            const int c = nb * 16 + i;
+            float col = 0.f;
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int mb = cmb0 + r * MSTEP;
+            for (int r = 0; r < RW; ++r) {
+                const int mb = cmb0 + r * MSTEP;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = mb * 16 + 4 * j + e;
-                const float b = sW[row * LK + c];
-                const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-                const float qv = sKh[row * LK + c], kv = sKb[row * LK + c], dkt = acc[2 * RW + r][e];
-                const float qh = G * qv, kh = G * kv, kb = Gi * kv, kt = gam_c * kb;
-                const float dqh = dQh[r][e], dkh = dKh[r][e], dkb = dKb[r][e];
-                const float dqv = G * dqh, dkv = G * dkh + Gi * dkb + gam_c * Gi * dkt;
-                if constexpr (ABF16) {           // staged in LDS, written below as whole 16-byte words
-                    sDq[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dqv));
-                    sDk[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dkv));
-                } else if (row < len) {
-                    const size_t ai = (static_cast<size_t>(row0 + row) * H + h) * DK + c;
-                    store_out<false>(P.dq, ai, dqv);
-                    store_out<false>(P.dk, ai, dkv);
+                for (int e = 0; e < 4; ++e) {
+                    const int row = mb * 16 + 4 * j + e, t = row / 16;
+                    const float bl = sKb[row * LK + c];
+                    const float ktf = __builtin_amdgcn_exp2f(sTot[t * DK + c] - bl + tot1(sTot, DK, c, t + 1, NBLK));
+                    const float qv = sW[row * LK + c], kv = sKh[row * LK + c], dkt = acc[2 * RW + r][e];
+                    const float dqv = dQh[r][e], dkv = dKh[r][e] + dKb[r][e] + ktf * dkt;
+                    if constexpr (ABF16) {           // staged in LDS, written below as whole 16-byte words
+                        sDq[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dqv));
+                        sDk[row * LDQ + c] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(dkv));
+                    } else if (row < len) {
+                        const size_t ai = (static_cast<size_t>(row0 + row) * H + h) * DK + c;
+                        store_out<false>(P.dq, ai, dqv);
+                        store_out<false>(P.dk, ai, dkv);
+                    }
+                    const float kt = kv * ktf;
+                    sKh[row * LK + c] = qv * dQh[r][e] + kv * dKh[r][e] - kv * dKb[r][e] - kt * dkt;   // db
+                    col += kt * dkt;
                 }
-                sKh[row * LK + c] = qh * dqh + kh * dkh - kb * dkb - kt * dkt;   // db
-                col += kt * dkt;
             }
+            col += __shfl_xor(col, 16, 64);
+            col += __shfl_xor(col, 32, 64);
+            if (j == 0) sCol[cmb0 * DK + c] = col;
         }
-        col += __shfl_xor(col, 16, 64);
-        col += __shfl_xor(col, 32, 64);
-        if (j == 0) sCol[cmb0 * DK + c] = col;
-    }
-    __syncthreads();
-    if constexpr (ABF16) {
-        constexpr int W8 = DK / 8;
-        for (int idx = tid; idx < C * W8; idx += NTH) {
-            const int r = idx / W8, c8 = (idx % W8) * 8;
-            if (r < len) {
-                const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c8;
-                *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dq) + ai) = *reinterpret_cast<const u16x8*>(sDq + r * LDQ + c8);
-                *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dk) + ai) = *reinterpret_cast<const u16x8*>(sDk + r * LDQ + c8);
+        __syncthreads();
+        if constexpr (ABF16) {
+            constexpr int W8 = DK / 8;
+            for (int idx = tid; idx < C * W8; idx += NTH) {
+                const int r = idx / W8, c8 = (idx % W8) * 8;
+                if (r < len) {
+                    const size_t ai = (static_cast<size_t>(row0 + r) * H + h) * DK + c8;
+                    *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dq) + ai) = *reinterpret_cast<const u16x8*>(sDq + r * LDQ + c8);
+                    *reinterpret_cast<u16x8*>(static_cast<uint16_t*>(P.dk) + ai) = *reinterpret_cast<const u16x8*>(sDk + r * LDQ + c8);
+                }
             }
         }
     }
@@ -1567,7 +1897,25 @@ __global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams 
     }
 }
 
+// One workgroup per (chunk, head) of the direct form (the preparation kernel
+// set its flag).
+template <int DK, int DV, bool ABF16, int GATE>
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_kernel(const BwdParams P) {
+    const int g = blockIdx.x / P.H;
+    if (g >= P.ctrl[0] || P.flag[blockIdx.x]) return;
+    grad_body<DK, DV, ABF16, GATE, true>(P, blockIdx.x % P.H, g);
+}
+
+// Entry blockIdx.x of the general list, as for the preparation kernel.
+template <int DK, int DV, bool ABF16, int GATE>
+__global__ __launch_bounds__(kGradThreads) void bwd_grad_general_kernel(const BwdParams P) {
+    if (static_cast<int>(blockIdx.x) >= *P.nslow) return;
+    const int id = P.slow[blockIdx.x];
+    grad_body<DK, DV, ABF16, GATE, false>(P, id % P.H, id / P.H);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 
 template <typename F>
 hipError_t set_lds(F* kfn, int bytes) {
@@ -1585,6 +1933,9 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
     p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dgate = a.dgate; p.dbeta = a.dbeta;
     p.dinitial_state = a.dinitial_state;
     p.ctrl = reinterpret_cast<const int32_t*>(ws + pl.off_ctrl);
+    p.nslow = reinterpret_cast<int32_t*>(ws + pl.off_ctrl) + 1;
+    p.slow = reinterpret_cast<int32_t*>(ws + bp.off_slow);
+    p.flag = reinterpret_cast<int32_t*>(ws + bp.off_flag);
     p.first = reinterpret_cast<const int32_t*>(ws + pl.off_first);
     p.order = reinterpret_cast<const int32_t*>(ws + pl.off_order);
     p.table = reinterpret_cast<const int4*>(ws + pl.off_table);
@@ -1597,6 +1948,9 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
     hipError_t e = launch_chunk_plan(pl, a.cu_seqlens, a.workspace, stream);
     if (e != hipSuccess) return e;
     const unsigned chunk_blocks = static_cast<unsigned>(pl.gmax * pl.H);
+    // the general-form kernels: one workgroup per list entry that may exist;
+    // those past the list's length return at once
+    const unsigned general_blocks = chunk_blocks;
     const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
     const unsigned chain_blocks = static_cast<unsigned>((pairs + 7) / 8 * 8 * (DV / 16));
     if (chunk_blocks > 0) {
@@ -1604,6 +1958,10 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         constexpr int l1 = PrepB<DK, DV>::bytes;
         if ((e = set_lds(k1, l1)) != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kPrepThreads), l1, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto k1g = bwd_prep_general_kernel<DK, DV, ABF16, GATE>;
+        if ((e = set_lds(k1g, l1)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1g, dim3(general_blocks), dim3(kPrepThreads), l1, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         auto k2 = ABF16 ? bwd_ckpt16_kernel<DK, DV> : bwd_ckpt_kernel<DK, DV>;
         constexpr int l2 = ABF16 ? Chain16B<DK>::bytes : CkptB<DK>::bytes;
@@ -1623,6 +1981,10 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
         constexpr int l4 = GradB<DK>::bytes;
         if ((e = set_lds(k4, l4)) != hipSuccess) return e;
         hipLaunchKernelGGL(k4, dim3(chunk_blocks), dim3(kGradThreads), l4, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto k4g = bwd_grad_general_kernel<DK, DV, ABF16, GATE>;
+        if ((e = set_lds(k4g, l4)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k4g, dim3(general_blocks), dim3(kGradThreads), l4, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1660,7 +2022,10 @@ kda_status make_chunk_bwd_plan(int B, int64_t T, int H, int Dk, int Dv, bool var
     const size_t end = act_bf16 ? rec_end(std::true_type{}) : rec_end(std::false_type{});
     bp.rec_bytes = align256(end);
     bp.off_rec = bp.fwd.off_rec;
-    bp.workspace_bytes = align256(bp.off_rec + static_cast<size_t>(bp.fwd.gmax) * H * bp.rec_bytes);
+    const size_t gh = static_cast<size_t>(bp.fwd.gmax) * H;
+    bp.off_slow = align256(bp.off_rec + gh * bp.rec_bytes);
+    bp.off_flag = align256(bp.off_slow + 4 * gh);
+    bp.workspace_bytes = align256(bp.off_flag + 4 * gh);
     *plan = bp;
     return KDA_SUCCESS;
 }

@@ -131,11 +131,9 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
     float* gGam = grec(P, h, g, R::GAM);
 
     // ---- pass 1: per 32-channel slice, decay, Gamma-scaled operands, A and P tiles.
-    // Every decay factor is 2^x with x <= 0, a sum of log2 alpha over the tokens
-    // it spans: cumulative sums restart at each 16-token tile, and products that
-    // cross tiles add the totals of the tiles in between, so nothing overflows
-    // and the sums stay short (chunk-wise normalisation, "Designing and
-    // Deploying Hybrid MLA and Linear Attention Architectures", section 3).
+    // Every decay factor is 2^x with x <= 0 (decayed_tile in kda_mm32.h):
+    // cumulative sums restart at each 16-token tile, and products that cross
+    // tiles add the totals of the tiles in between, so nothing overflows.
     f4 accA[TW], accP[TW];
 #pragma unroll
     for (int t = 0; t < TW; ++t) accA[t] = accP[t] = zero4();
@@ -198,84 +196,14 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
             for (int u = 0; u < NB; ++u) tot += sTot[u * SL + tid];
             gGam[cs + tid] = __builtin_amdgcn_exp2f(tot);
         }
-        // this slice's share of the tiles of A (K-hat K-bar^T) and P (Q-hat K-bar^T).
-        // Lane (i, j) takes channels 16 gg + 4 j + s2 of the slice.
+        // this slice's share of the tiles of A (K-hat K-bar^T) and P (Q-hat K-bar^T)
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
             const int task = wave + NW * t;
             if (task >= NLT) continue;
             int ti, tj;
             lt_decode(task, ti, tj);
-            if (tj < ti) {
-                // 2^(b_r - b_s) = 2^(b_r - e) 2^(e - b_s), e = b at the end of tile tj:
-                // row factor b_t(r) + (totals of the tiles between), column factor
-                // T_tj - b_t(s)
-                const int r = 16 * ti + i, s = 16 * tj + i;
-#pragma unroll
-                for (int gg = 0; gg < SL / 16; ++gg) {
-                    const int c0 = 16 * gg + 4 * j;
-                    const f4 kr = *reinterpret_cast<const f4*>(sK + r * LS + c0);
-                    const f4 qr = *reinterpret_cast<const f4*>(sQ + r * LS + c0);
-                    const f4 ks = *reinterpret_cast<const f4*>(sK + s * LS + c0);
-                    const f4 br = *reinterpret_cast<const f4*>(sB + r * LS + c0);
-                    const f4 bs = *reinterpret_cast<const f4*>(sB + s * LS + c0);
-                    const f4 tt = *reinterpret_cast<const f4*>(sTot + tj * SL + c0);
-                    f4 mid = zero4();
-                    for (int u = tj + 1; u < ti; ++u) mid += *reinterpret_cast<const f4*>(sTot + u * SL + c0);
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) {
-                        const float fr = __builtin_amdgcn_exp2f(br[s2] + mid[s2]);
-                        const float bk = ks[s2] * __builtin_amdgcn_exp2f(tt[s2] - bs[s2]);
-                        accA[t] = mfma4(kr[s2] * fr, bk, accA[t]);
-                        accP[t] = mfma4(qr[s2] * fr, bk, accP[t]);
-                    }
-                }
-            } else {
-                // Diagonal tile: a pair s < r is taken at the level p of the
-                // highest bit in which r and s differ (tile-local indices); the
-                // decay between them is pf_p(r) sf_p(s), the products from the
-                // start of r's aligned 2^p-token group to r and after s to the end
-                // of its group; level p scales each token by pf_p (bit p set) or
-                // sf_p (bit p clear) and keeps only its own pairs.  The diagonal
-                // of P takes no decay.
-                const int x = 16 * ti + i;
-                f4 la[4], lp[4], pd = zero4();
-#pragma unroll
-                for (int p = 0; p < 4; ++p) la[p] = lp[p] = zero4();
-#pragma unroll
-                for (int gg = 0; gg < SL / 16; ++gg) {
-                    const int c0 = 16 * gg + 4 * j;
-                    const f4 kx = *reinterpret_cast<const f4*>(sK + x * LS + c0);
-                    const f4 qx = *reinterpret_cast<const f4*>(sQ + x * LS + c0);
-                    const f4 bx = *reinterpret_cast<const f4*>(sB + x * LS + c0);
-#pragma unroll
-                    for (int s2 = 0; s2 < 4; ++s2) pd = mfma4(qx[s2], kx[s2], pd);
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const bool up = (i >> p) & 1;
-                        const int ref = up ? (i & ~((1 << p) - 1)) - 1 : (i | ((1 << p) - 1));
-                        const f4 bref = *reinterpret_cast<const f4*>(sB + (16 * ti + ref) * LS + c0);
-#pragma unroll
-                        for (int s2 = 0; s2 < 4; ++s2) {
-                            const float f = __builtin_amdgcn_exp2f(up ? bx[s2] - bref[s2] : bref[s2] - bx[s2]);
-                            const float kc = kx[s2] * f, qc = qx[s2] * f;
-                            la[p] = mfma4(kc, kc, la[p]);
-                            lp[p] = mfma4(qc, kc, lp[p]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int row = 4 * j + e;
-                    if (row == i) accP[t][e] += pd[e];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        if (((row ^ i) >> p) == 1 && ((row >> p) & 1)) {
-                            accA[t][e] += la[p][e];
-                            accP[t][e] += lp[p][e];
-                        }
-                }
-            }
+            decayed_tile<SL / 16, true, true>(sK, sQ, sK, sB, sTot, LS, SL, ti, tj, accA[t], accP[t]);
         }
         __syncthreads();
     }

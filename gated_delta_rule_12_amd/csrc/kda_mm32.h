@@ -433,5 +433,338 @@ __device__ __forceinline__ void mm_two(const float* pa0, const float* pa1, int a
         }
     }
 }
+
+// ---------------------------------------------------------------------------
+// Decay between tokens without overflow (chunk-wise normalisation, "Designing
+// and Deploying Hybrid MLA and Linear Attention Architectures", section 3).
+// The chunk's tokens fall in 16-token tiles; sB[r * ld + c] holds b, the
+// cumulative log2 alpha of channel c restarted at every tile (so b <= 0), and
+// sTot[t * ldt + c] the total of tile t.  The decay from token s to a later
+// token r, 2^(b_r - b_s) over the chunk, is only ever formed from exponents
+// <= 0, so no factor exceeds 1:
+//   * tiles I > J:  2^(b_r) * 2^(tot of the tiles between) * 2^(tot_J - b_s)
+//     (b is tile-local: the first factor runs from the start of tile I, the
+//     last from s to the end of tile J);
+//   * one tile: the pair (r, s) belongs to the level p of the highest bit in
+//     which the tile-local indices differ; both lie in one aligned group of
+//     2^(p+1) tokens, s in its lower and r in its upper half, and the decay
+//     is pf_p(r) sf_p(s), with pf_p(x) = 2^(b_x - b_lo) (lo: the token before
+//     x's aligned 2^p group) and sf_p(x) = 2^(b_hi - b_x) (hi: the last token
+//     of that group).  A level is one matrix product with both factors
+//     applied per token, of which only that level's pairs are kept.
+// ---------------------------------------------------------------------------
+
+// One 16-deep group of a 16x16 product, lane group j holding reduction
+// indices 4j..4j+3 of A and B (the layout of mfma4's four steps): on the fp32
+// matrix cores (four 16x16x4 steps), or with SPLIT on the bf16 ones with
+// every operand split into bf16 hi + lo (as mm_rows_x3: fp32's exponent
+// range, ~2^-16 relative; one 16x16x16 step per product).
+typedef short s4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split4_bf16(const f4& x, s4v& hi, s4v& lo) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const __bf16 h = static_cast<__bf16>(x[e]);
+        hi[e] = __builtin_bit_cast(short, h);
+        lo[e] = __builtin_bit_cast(short, static_cast<__bf16>(x[e] - static_cast<float>(h)));
+    }
+}
+template <bool SPLIT>
+__device__ __forceinline__ f4 mm16(f4 a, f4 b, f4 acc) {
+    if constexpr (SPLIT) {
+        s4v ah, al, bh, bl;
+        split4_bf16(a, ah, al);
+        split4_bf16(b, bh, bl);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(al, bh, acc, 0, 0, 0);
+        return acc;
+    } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = mfma4(a[s2], b[s2], acc);
+        return acc;
+    }
+}
+
+// tile-local index of the token whose b enters pf_p (x has bit p set) / sf_p
+__device__ __forceinline__ int lvl_lo(int x, int p) { return (x & ~((1 << p) - 1)) - 1; }
+__device__ __forceinline__ int lvl_hi(int x, int p) { return x | ((1 << p) - 1); }
+
+// pair (r, s) of one tile is taken at level p: p is the highest differing bit, r above s
+__device__ __forceinline__ bool lvl_pair(int r, int s, int p) { return ((r ^ s) >> p) == 1 && ((r >> p) & 1); }
+
+// sum of the tile totals of tiles lo .. hi-1 (4 channels from c)
+__device__ __forceinline__ f4 tot4(const float* sTot, int ldt, int c, int lo, int hi) {
+    f4 x = zero4();
+    for (int u = lo; u < hi; ++u) x += *reinterpret_cast<const f4*>(sTot + u * ldt + c);
+    return x;
+}
+__device__ __forceinline__ float tot1(const float* sTot, int ldt, int c, int lo, int hi) {
+    float x = 0.f;
+    for (int u = lo; u < hi; ++u) x += sTot[u * ldt + c];
+    return x;
+}
+
+// Tile-local cumulative log2 alpha of a chunk of ROWS tokens and DK channels.
+// On entry s[r * ld + c] holds the gate as given (the scalar gate: sGs[r]);
+// on exit s holds b (restarted every 16 rows; padding rows add 0) and
+// sTot[t * DK + c] the total of tile t.  A gate below 2^-150 counts as
+// 2^-150: every fp32 factor that spans it is zero either way.  NTH / DK row
+// segments per channel; sPart holds NTH floats of scratch.  Ends with a barrier.
+template <int DK, int NTH, int ROWS, int GATE>
+__device__ __forceinline__ void tile_gate_scan(float* s, int ld, const float* sGs, int len, float* sTot,
+                                               float* sPart) {
+    constexpr int NS = NTH / DK, SEG = ROWS / NS;
+    static_assert(NS * SEG == ROWS && SEG <= 16 && 16 % SEG == 0, "row segments tile the 16-token tiles");
+    const int c = threadIdx.x % DK, sg = threadIdx.x / DK, r0 = sg * SEG;
+    float x[SEG];
+#pragma unroll
+    for (int r = 0; r < SEG; ++r) {
+        const float g = GATE == KDA_GATE_SCALAR ? sGs[r0 + r] : s[(r0 + r) * ld + c];
+        float l2 = 0.f;
+        if (r0 + r < len) {
+            if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16) l2 = log2_alpha_from_softplus_arg(g);
+            else l2 = __builtin_amdgcn_logf(g);
+            l2 = fmaxf(l2, -150.f);
+        }
+        x[r] = (r ? x[r - 1] : 0.f) + l2;
+    }
+    sPart[sg * DK + c] = x[SEG - 1];
+    __syncthreads();
+    const int first = (r0 / 16) * (16 / SEG);        // first segment of this tile
+    float off = 0.f;
+    for (int s2 = first; s2 < sg; ++s2) off += sPart[s2 * DK + c];
+#pragma unroll
+    for (int r = 0; r < SEG; ++r) s[(r0 + r) * ld + c] = off + x[r];
+    if ((r0 + SEG) % 16 == 0) sTot[(r0 / 16) * DK + c] = off + x[SEG - 1];
+    __syncthreads();
+}
+
+// Tile (mb, nb) of the C x C products over G groups of 16 channels
+//   acc0 += (R0 . D) K^T,  acc1 += (R1 . D) K^T  (TWO),   D = decay from s to r,
+// with R0, R1, K raw token-major rows (stride ld, reduction along the row), b
+// in sB (same layout) and the tile totals in sTot (row stride ldt).  The
+// tile is lower-triangular: tiles above the diagonal are not computed.  On the
+// diagonal tile the strict lower part is formed; acc1 also gets its diagonal
+// (r = s, no decay) when DIAG1.  D-layout: lane (i, j) holds rows 4j + e,
+// column i of the tile.  SPLIT: the products on the bf16 matrix cores with
+// split operands (mm16).
+template <int G, bool TWO, bool DIAG1, bool SPLIT = false>
+__device__ __forceinline__ void decayed_tile(const float* R0, const float* R1, const float* K, const float* sB,
+                                             const float* sTot, int ld, int ldt, int mb, int nb, f4& acc0,
+                                             f4& acc1) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    if (nb < mb) {
+        const int r = 16 * mb + i, s = 16 * nb + i;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+            const int c0 = 16 * gg + 4 * j;
+            const f4 br = *reinterpret_cast<const f4*>(sB + r * ld + c0);
+            const f4 bs = *reinterpret_cast<const f4*>(sB + s * ld + c0);
+            const f4 tt = *reinterpret_cast<const f4*>(sTot + nb * ldt + c0);
+            const f4 mid = tot4(sTot, ldt, c0, nb + 1, mb);
+            const f4 r0v = *reinterpret_cast<const f4*>(R0 + r * ld + c0);
+            const f4 kv = *reinterpret_cast<const f4*>(K + s * ld + c0);
+            f4 r1v;
+            if constexpr (TWO) r1v = *reinterpret_cast<const f4*>(R1 + r * ld + c0);
+            f4 fr, bk;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                fr[s2] = __builtin_amdgcn_exp2f(br[s2] + mid[s2]);
+                bk[s2] = kv[s2] * __builtin_amdgcn_exp2f(tt[s2] - bs[s2]);
+            }
+            acc0 = mm16<SPLIT>(r0v * fr, bk, acc0);
+            if constexpr (TWO) acc1 = mm16<SPLIT>(r1v * fr, bk, acc1);
+        }
+    } else if (nb == mb) {
+        const int x = 16 * mb + i;
+        f4 la[4], lb[4], pd = zero4();
+#pragma unroll
+        for (int p = 0; p < 4; ++p) la[p] = lb[p] = zero4();
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+            const int c0 = 16 * gg + 4 * j;
+            const f4 kx = *reinterpret_cast<const f4*>(K + x * ld + c0);
+            const f4 bx = *reinterpret_cast<const f4*>(sB + x * ld + c0);
+            const f4 r0v = *reinterpret_cast<const f4*>(R0 + x * ld + c0);
+            f4 r1v;
+            if constexpr (TWO) r1v = *reinterpret_cast<const f4*>(R1 + x * ld + c0);
+            if constexpr (TWO && DIAG1) pd = mm16<SPLIT>(r1v, kx, pd);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const bool up = (i >> p) & 1;
+                const int ref = 16 * mb + (up ? lvl_lo(i, p) : lvl_hi(i, p));
+                const f4 bref = *reinterpret_cast<const f4*>(sB + ref * ld + c0);
+                f4 f;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) f[s2] = __builtin_amdgcn_exp2f(up ? bx[s2] - bref[s2] : bref[s2] - bx[s2]);
+                const f4 kc = kx * f;
+                la[p] = mm16<SPLIT>(r0v * f, kc, la[p]);
+                if constexpr (TWO) lb[p] = mm16<SPLIT>(r1v * f, kc, lb[p]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = 4 * j + e;
+            if (TWO && DIAG1 && row == i) acc1[e] += pd[e];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+                if (lvl_pair(row, i, p)) {
+                    acc0[e] += la[p][e];
+                    if constexpr (TWO) acc1[e] += lb[p][e];
+                }
+        }
+    }
+}
+
+// Decayed contractions over the tokens of a chunk (C x C by C x d_k) with b
+// in sB and the tile totals in sTot as above:
+//   lower:  Y[r, c] = sum_{s <= r} X[r, s] V[s, c] 2^(b_r - b_s)[c]
+//   upper:  Z[s, c] = sum_{r >= s} X[r, s] V[r, c] 2^(b_r - b_s)[c]
+// formed together, since they share every decay factor:
+//   y0 += lower(X0, K),  y1 += lower(X1, K),  z += upper(X1, Q) + upper(X0, K)
+// for the R row blocks mb0 + r * mstep and the 16 channels nb * 16 .. + 15
+// (column i of the D layout).  X0 is strictly lower-triangular, X1 includes
+// its diagonal (r = s, no decay); elements above the diagonal are never
+// read.  X is row-major (stride ldx), K, Q and sB token-major (stride ld),
+// sTot has row stride ldt.  Lane (i, j) holds the B operand rows 4j + s2 and
+// the output rows 4j + e of every block, so the factors of those tokens in
+// channel c serve both the operands and the outputs:
+//   pf(x) = 2^(b_x)          decay from the start of x's tile to x
+//   sf(x) = 2^(tot - b_x)    decay after x to the end of its tile
+// Blocks below the diagonal use Horner's rule over the tiles in between (one
+// multiply of the accumulator per block step, by the tile total 2^tot, a
+// factor of the channel only); diagonal blocks go level by level.
+template <int R, int NBLK, bool SPLIT = false>
+__device__ __forceinline__ void decayed_lower_upper(const float* X0, const float* X1, int ldx, const float* K,
+                                                    const float* Q, const float* sB, const float* sTot, int ld,
+                                                    int ldt, int mb0, int mstep, int nb, f4 (&y0)[R],
+                                                    f4 (&y1)[R], f4 (&z)[R]) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+    const int c = 16 * nb + i;
+    // the factors of this lane's four tokens of block t
+    auto pf4 = [&](int t) {
+        f4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_exp2f(sB[(16 * t + 4 * j + e) * ld + c]);
+        return x;
+    };
+    auto sf4 = [&](int t) {
+        const float tot = sTot[t * ldt + c];
+        f4 x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_exp2f(tot - sB[(16 * t + 4 * j + e) * ld + c]);
+        return x;
+    };
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+        const int I = mb0 + rr * mstep;
+        __builtin_amdgcn_sched_barrier(0);
+        // lower, blocks J < I: B = K[s] sf(s), Horner over J, rows times pf(r)
+        if (I > 0) {
+            f4 h0 = zero4(), h1 = zero4();
+            for (int J = 0; J < I; ++J) {
+                if (J > 0) {
+                    const float F = __builtin_amdgcn_exp2f(sTot[J * ldt + c]);
+                    h0 *= F;
+                    h1 *= F;
+                }
+                const f4 x0 = *reinterpret_cast<const f4*>(X0 + (16 * I + i) * ldx + 16 * J + 4 * j);
+                const f4 x1 = *reinterpret_cast<const f4*>(X1 + (16 * I + i) * ldx + 16 * J + 4 * j);
+                const f4 sfj = sf4(J);
+                f4 bk;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) bk[s2] = K[(16 * J + 4 * j + s2) * ld + c] * sfj[s2];
+                h0 = mm16<SPLIT>(x0, bk, h0);
+                h1 = mm16<SPLIT>(x1, bk, h1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const f4 pfi = pf4(I);
+            y0[rr] += h0 * pfi;
+            y1[rr] += h1 * pfi;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // upper, blocks I2 > I (the output block is I): B = V[r] pf(r), Horner
+        // over I2 from the last, rows times sf(s)
+        if (I < NBLK - 1) {
+            f4 h2 = zero4();
+            for (int I2 = NBLK - 1; I2 > I; --I2) {
+                if (I2 < NBLK - 1) h2 *= __builtin_amdgcn_exp2f(sTot[I2 * ldt + c]);
+                const f4 pfi2 = pf4(I2);
+                f4 a1, a0, bq, bk;
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) {
+                    const int rk = 16 * I2 + 4 * j + s2;
+                    a1[s2] = X1[rk * ldx + 16 * I + i];
+                    a0[s2] = X0[rk * ldx + 16 * I + i];
+                    bq[s2] = Q[rk * ld + c] * pfi2[s2];
+                    bk[s2] = K[rk * ld + c] * pfi2[s2];
+                }
+                h2 = mm16<SPLIT>(a1, bq, h2);
+                h2 = mm16<SPLIT>(a0, bk, h2);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            z[rr] += h2 * sf4(I);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // the diagonal block I, level by level
+        const f4 x0l = *reinterpret_cast<const f4*>(X0 + (16 * I + i) * ldx + 16 * I + 4 * j);
+        const f4 x1l = *reinterpret_cast<const f4*>(X1 + (16 * I + i) * ldx + 16 * I + 4 * j);
+        f4 x0u, x1u, kv, qv, bv;
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int rk = 16 * I + 4 * j + s2;
+            x0u[s2] = X0[rk * ldx + 16 * I + i];
+            x1u[s2] = X1[rk * ldx + 16 * I + i];
+            kv[s2] = K[rk * ld + c];
+            qv[s2] = Q[rk * ld + c];
+            bv[s2] = sB[rk * ld + c];
+        }
+        {   // the diagonal of X1 (r = s): lower X1[r][r] K[r], upper X1[s][s] Q[s]
+            f4 m1, m2;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const bool on = i == 4 * j + s2;
+                m1[s2] = on ? x1l[s2] : 0.f;
+                m2[s2] = on ? x1u[s2] : 0.f;
+            }
+            y1[rr] = mm16<SPLIT>(m1, kv, y1[rr]);
+            z[rr] = mm16<SPLIT>(m2, qv, z[rr]);
+        }
+        // (a loop at run time: unrolled, the four levels' operands crowd the registers)
+#pragma unroll 1
+        for (int p = 0; p < 4; ++p) {
+            // pf_p (bit p set) and sf_p of this lane's four tokens 4j + e
+            f4 pp, ss;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int xl = 4 * j + e;
+                const int lo = lvl_lo(xl, p) < 0 ? 0 : lvl_lo(xl, p);   // in range even if read speculatively
+                pp[e] = (xl >> p) & 1 ? __builtin_amdgcn_exp2f(bv[e] - sB[(16 * I + lo) * ld + c]) : 0.f;
+                ss[e] = __builtin_amdgcn_exp2f(sB[(16 * I + lvl_hi(xl, p)) * ld + c] - bv[e]);
+            }
+            f4 a0, a1, u1, u0;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int kl = 4 * j + s2;                      // reduction token (B row)
+                const bool lo = lvl_pair(i, kl, p);             // lower: r = i above s = kl
+                const bool up = lvl_pair(kl, i, p);             // upper: r = kl above s = i
+                a0[s2] = lo ? x0l[s2] : 0.f;
+                a1[s2] = lo ? x1l[s2] : 0.f;
+                u1[s2] = up ? x1u[s2] : 0.f;
+                u0[s2] = up ? x0u[s2] : 0.f;
+            }
+            const f4 bk = kv * ss;
+            f4 t0 = mm16<SPLIT>(a0, bk, zero4());
+            f4 t1 = mm16<SPLIT>(a1, bk, zero4());
+            f4 t2 = mm16<SPLIT>(u1, qv * pp, zero4());
+            t2 = mm16<SPLIT>(u0, kv * pp, t2);
+            y0[rr] += t0 * pp;
+            y1[rr] += t1 * pp;
+            z[rr] += t2 * ss;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
 }  // namespace mm32
 }  // namespace kda

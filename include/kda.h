@@ -218,7 +218,8 @@ KDA_API kda_status kda_chunk_fwd_static(const void *q, const void *k, const void
  * need not be initialised; not to be shared by calls that may overlap.
  * Per (chunk, head), with C = chunk_size: (3 C d_k + 3 C d_v + 2 d_k d_v +
  * 2 C^2 + d_k) * 4 bytes for fp32 activations, 14 C d_k + 8 C d_v +
- * 4 d_k d_v + 6 C^2 + 4 d_k bytes for bf16 (each rounded up to 256).
+ * 4 d_k d_v + 6 C^2 + 4 d_k bytes for bf16 (each rounded up to 256), plus
+ * 8 bytes (the list of chunks that take the general form, and a flag).
  */
 KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, int Dv,
                                      int varlen, int num_seqs, int chunk_size,
@@ -238,9 +239,14 @@ KDA_API size_t kda_chunk_bwd_workspace_bytes(int B, int64_t T, int H, int Dk, in
  * Inputs, as for kda_chunk_fwd_gated (same layouts, alignment, sequences,
  * preconditions): q, k, v, gate (form gate_kind), beta, initial_state
  * (NULL = zeros), cu_seqlens / num_seqs.  Gate precondition of this call:
- * alpha in (0, 1] with the decay of every channel over each 64-token chunk,
- * -sum(log alpha), below 87 (the backward still forms Gamma and 1/Gamma of a
- * chunk as single fp32 factors).  Upstream gradients:
+ * alpha in (0, 1], any decay strength.  A (chunk, head) in which every
+ * channel's decay over the chunk stays within 2^-64 runs in the direct
+ * form (Gamma and 1/Gamma of the chunk as fp32 factors); any other in the
+ * general form, whose decay factors never exceed 1.  The gate gradient is
+ * formed from dL/dlog(alpha): dL/dalpha = dL/dlog(alpha) / alpha, whose
+ * absolute error is that of dL/dlog(alpha) times 1/alpha, while the
+ * softplus form's dL/dx = -sigmoid(x) dL/dlog(alpha) keeps the accuracy of
+ * dL/dlog(alpha) at every alpha.  Upstream gradients:
  *   dout          [B, T, H, Dv]  act_dtype
  *   dfinal_state  [N, H, Dk, Dv] fp32, or NULL for zeros
  * Outputs (written for every token; none may overlap an input):
