@@ -160,11 +160,160 @@ def measured_bwd_traffic():
         for s in BWD_KERNEL_SOURCES:
             with open(os.path.join(ROOT, s), "rb") as f:
                 h.update(f.read())
-        if fields.get("sources_sha256") != h.hexdigest():
+        if fields.get("bwd_sources_sha256") != h.hexdigest():
             return None
         return int(float(fields["bwd_traffic_bytes"]))
     except (OSError, KeyError, ValueError):
         return None
+
+
+# ---------------------------------------------------------------------------
+# Summaries of rocprofv3 output (no GPU needed): the text files under
+# profiles/ are written by `python bench.py --summarize KIND ...` from the CSV
+# files of the rocprofv3 runs named in each summary's header.
+# ---------------------------------------------------------------------------
+LIB_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel", "decode_kernel",
+               "bwd_prep_kernel", "bwd_prep_general_kernel", "bwd_ckpt_kernel", "bwd_ckpt16_kernel",
+               "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel", "bwd_grad_general_kernel")
+FWD_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel")
+BWD_KERNELS = ("plan_kernel", "bwd_prep_kernel", "bwd_prep_general_kernel", "bwd_ckpt_kernel",
+               "bwd_ckpt16_kernel", "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel",
+               "bwd_grad_general_kernel")
+
+
+def _kernel_base(name):
+    """The kernel's identifier: 'void kda::(anonymous namespace)::prep_kernel<...>(...)' -> 'prep_kernel'."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("kda::(anonymous namespace)::", "").replace("kda::", "")
+    cut = len(n)
+    for ch in "<(":
+        k = n.find(ch)
+        if k >= 0:
+            cut = min(cut, k)
+    return n[:cut].split("::")[-1].strip()
+
+
+def _kernel_short(name):
+    """The identifier with its template arguments, without the parameter list."""
+    n = name[5:] if name.startswith("void ") else name
+    n = n.replace("kda::(anonymous namespace)::", "").replace("kda::", "")
+    depth = 0
+    for k, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return n[:k]
+    return n
+
+
+def sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for s in paths:
+        with open(os.path.join(ROOT, s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _csv_rows(pattern):
+    import csv
+    import glob
+    rows = []
+    for path in sorted(glob.glob(pattern, recursive=True)):
+        with open(path, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    if not rows:
+        raise SystemExit(f"bench.py --summarize: no rows in {pattern}")
+    return rows
+
+
+def _counter_means(pattern, counter):
+    """Mean counter value per dispatch, per library kernel (short name)."""
+    acc = {}
+    for r in _csv_rows(pattern):
+        if r["Counter_Name"] != counter or _kernel_base(r["Kernel_Name"]) not in LIB_KERNELS:
+            continue
+        v = acc.setdefault(_kernel_short(r["Kernel_Name"]), [])
+        v.append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def _copy_counter(pattern, counter):
+    """Mean counter value over the device-copy dispatches of --copy-calibration."""
+    vals = [float(r["Counter_Value"]) for r in _csv_rows(pattern)
+            if r["Counter_Name"] == counter and "copy" in r["Kernel_Name"]]
+    if not vals:
+        raise SystemExit(f"bench.py --summarize: no copy dispatch with {counter} in {pattern}")
+    return sum(vals) / len(vals)
+
+
+def summarize(kind, inputs, title, commands):
+    """Print a profiles/ summary.  kind:
+      trace    inputs = [kernel_stats.csv glob]
+      traffic  inputs = [FETCH_SIZE csv glob, WRITE_SIZE csv glob, copy FETCH_SIZE glob, copy WRITE_SIZE glob]
+      mfma     inputs = [MfmaUtil csv glob, MOPS csv glob]"""
+    print(f"# {title}")
+    for c in commands:
+        print(f"# {c}")
+    fwd_sha, bwd_sha = sources_sha256(KERNEL_SOURCES), sources_sha256(BWD_KERNEL_SOURCES)
+    if kind == "trace":
+        rows = [r for r in _csv_rows(inputs[0]) if _kernel_base(r["Name"]) in LIB_KERNELS]
+        print(f"# forward/decode sources sha256: {fwd_sha}")
+        print(f"# backward sources sha256: {bwd_sha}")
+        print("#")
+        print(f"# {'kernel':48s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+        sums, seen = {}, set()
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            base, avg = _kernel_base(r["Name"]), float(r["AverageNs"]) / 1e3
+            seen.add(base)
+            print(f"  {_kernel_short(r['Name']):48s} {int(r['Calls']):6d} {avg:10.2f} "
+                  f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}")
+            for grp, names in (("forward", FWD_KERNELS), ("backward", BWD_KERNELS), ("decode", ("decode_kernel",))):
+                if base in names:
+                    sums[grp] = sums.get(grp, 0.0) + avg
+        for grp, names in (("forward", FWD_KERNELS), ("backward", BWD_KERNELS), ("decode", ("decode_kernel",))):
+            if any(n in seen and n != "plan_kernel" for n in names):
+                print(f"# {grp} kernels, sum of averages: {sums[grp]:.2f} us")
+    elif kind == "traffic":
+        fetch, write = _counter_means(inputs[0], "FETCH_SIZE"), _counter_means(inputs[1], "WRITE_SIZE")
+        copy_bytes = 1 << 30
+        fs = copy_bytes / (_copy_counter(inputs[2], "FETCH_SIZE") * 1024)
+        ws = copy_bytes / (_copy_counter(inputs[3], "WRITE_SIZE") * 1024)
+        print(f"# copy calibration: 1 GiB read and 1 GiB written per dispatch -> "
+              f"FETCH_SIZE scale {fs:.6f}, WRITE_SIZE scale {ws:.6f}")
+        print(f"sources_sha256: {fwd_sha}")
+        print(f"bwd_sources_sha256: {bwd_sha}")
+        print(f"fetch_scale: {fs:.6f}")
+        print(f"write_scale: {ws:.6f}")
+        tot = {}
+        for k in sorted(set(fetch) | set(write)):
+            rb, wb = fetch.get(k, 0.0) * 1024 * fs, write.get(k, 0.0) * 1024 * ws
+            print(f"{k}: read_bytes {rb:.0f} write_bytes {wb:.0f} "
+                  f"(FETCH_SIZE {fetch.get(k, 0.0):.0f} KiB, WRITE_SIZE {write.get(k, 0.0):.0f} KiB)")
+            base = _kernel_base(k)
+            for grp, names in (("fwd", FWD_KERNELS), ("bwd", BWD_KERNELS), ("decode", ("decode_kernel",))):
+                if base in names:
+                    tot[grp] = tot.get(grp, 0.0) + rb + wb
+        kinds = {_kernel_base(k) for k in set(fetch) | set(write)}
+        for grp, names in (("fwd", FWD_KERNELS), ("bwd", BWD_KERNELS), ("decode", ("decode_kernel",))):
+            if any(n in kinds and n != "plan_kernel" for n in names):
+                print(f"{grp}_traffic_bytes: {tot[grp]:.0f}")
+    elif kind == "mfma":
+        util = _counter_means(inputs[0], "MfmaUtil")
+        mops = {c: _counter_means(inputs[1], c) for c in
+                ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")}
+        print("# MfmaUtil = 100 * sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMD_NUM) (rocprofv3's "
+              "derived metric); executed GFLOP = MOPS * 512 per dispatch")
+        print(f"# forward/decode sources sha256: {fwd_sha}")
+        print(f"# backward sources sha256: {bwd_sha}")
+        print(f"# {'kernel':48s} {'MfmaUtil %':>10s} {'f16 GFLOP':>10s} {'bf16 GFLOP':>10s} {'f32 GFLOP':>10s}")
+        for k in sorted(util):
+            g = [mops[c].get(k, 0.0) * 512 / 1e9 for c in mops]
+            print(f"  {k:48s} {util[k]:10.2f} {g[0]:10.1f} {g[1]:10.1f} {g[2]:10.1f}")
+    else:
+        raise SystemExit(f"bench.py --summarize: unknown kind {kind}")
 
 
 def cpu_model():
@@ -272,9 +421,17 @@ def main():
     ap.add_argument("--only", choices=["fwd", "decode", "bwd"], default=None)
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--summarize", choices=["trace", "traffic", "mfma"], default=None,
+                    help="print a profiles/ summary from rocprofv3 CSV files (globs given by --inputs)")
+    ap.add_argument("--inputs", nargs="*", default=[])
+    ap.add_argument("--title", default="")
+    ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the measured peaks and the other gate forms (profiler runs)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.inputs, args.title, args.command)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

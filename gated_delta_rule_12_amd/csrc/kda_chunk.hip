@@ -2,19 +2,22 @@
 //
 // The chunked algorithm of "Linear Attention KDA Gating in a 3:1 Hybrid
 // Architecture: Principles and Implementation Guide", section 3, carried out
-// in three launches on the caller's stream:
+// in four launches on the caller's stream:
 //
 //   plan_kernel   (integer)  chunk table: which sequence, first token row and
 //                 length every 64-token chunk has; sequence order by length.
 //   prep_kernel   (chunk-parallel, one workgroup per (chunk, head))
-//                 log-domain cumulative decay b = cumsum(log alpha) over the
-//                 chunk ("log-domain accumulation", "Designing and Deploying
-//                 Hybrid MLA and Linear Attention Architectures", section 3);
+//                 the in-chunk decay ("log-domain accumulation", "Designing
+//                 and Deploying Hybrid MLA and Linear Attention
+//                 Architectures", section 3);
 //                 A = strictly-lower(Diag(beta)(Gamma.K)(K/Gamma)^T) and
 //                 P = Tril((Gamma.Q)(K/Gamma)^T) on the matrix cores;
 //                 T = (I + A)^-1 by blocked forward substitution;
 //                 W = T Diag(beta)(Gamma.K), U = T Diag(beta) V on the matrix
-//                 cores; Gamma.Q, ((gamma/Gamma).K)^T and gamma.
+//                 cores; Gamma.Q, ((gamma/Gamma).K)^T and gamma -> record.
+//                 Direct form; a (chunk, head) outside its range is listed
+//                 for the next launch.
+//   prep_general_kernel  the same for each listed (chunk, head), general form.
 //   state_kernel  (sequential over the chunks of one sequence, one
 //                 workgroup per (sequence, head, 16 value columns))
 //                 U' = U - W S,  O = (Gamma.Q) S + P U',
@@ -30,11 +33,17 @@
 //
 // Numerics.  All accumulation is fp32.  With bf16 activations the matrix-core
 // operands are fp16 (11-bit significand, 8x finer than bf16); with fp32
-// activations every product runs on the fp32 matrix cores.  The decay factors
-// are never formed as e^{+b} alone: products e^{b_r - b_s} (s <= r) are split
-// as e^{b_r - ref} * e^{ref - b_s} around a reference token in the middle of
-// each 16-token block ("chunk-wise normalization", same section), so every
-// factor is bounded by the decay over at most 8 tokens.
+// activations every product runs on the fp32 matrix cores.  The decay between
+// two tokens, e^{b_r - b_s} (s <= r), takes one of two forms ("chunk-wise
+// normalization", same section):
+//   direct   split as e^{b_r - ref} * e^{ref - b_s} around a reference token
+//            in the middle of each 16-token block, so a factor spans at most
+//            8 tokens of decay; used when every channel decays by at most
+//            2^-64 over the chunk and, with fp16 operands, by at most 2^-14
+//            over each 16-token block, with |k|, |q| <= 2 (every fp16 operand
+//            then stays below 2^15);
+//   general  every factor a product of alpha over a run of tokens, never
+//            above 1, for any gate in [0, 1] (prep_general_kernel).
 #include <type_traits>
 
 #include "kda_chunk.h"
@@ -333,6 +342,8 @@ struct PrepParams {
     int H;
     int64_t T;     // tokens per sequence of a dense batch; 0 for varlen
     int cps;       // chunks per sequence of a dense batch
+    int32_t* nslow;   // length of the general-form list (zeroed by the chunk table)
+    int32_t* slow;    // general-form list: g * H + h of each (chunk, head) that takes it
 };
 
 template <int a, int b> struct CMax { static constexpr int value = a > b ? a : b; };
@@ -386,11 +397,37 @@ struct PrepLds {
     static constexpr int RD = CMax<C * ATP * 4, C * TPP * (int)sizeof(E)>::value;
     // small: beta [64]
     static constexpr int RS = C * 4;
-    // the block totals of the decay [4][DK] live in region d until A^T is
+    // the block totals of the decay [4][DK] (general form) or the totals and
+    // decay factors [4 + 16][DK] (direct form) live in region d until A^T is
     // written there
-    static_assert(RD >= 4 * DK * 4, "region d holds the block totals");
+    static_assert(RD >= 20 * DK * 4, "region d holds the direct form's decay tables");
     static constexpr int bytes = RA + RB + RC + RD + RS;
 };
+
+__device__ __forceinline__ int frag_k(int j, int e) { return e < 4 ? 4 * j + e : 12 + 4 * j + e; }
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Inclusive prefix sum over the 16 lanes of each DPP row (row_shr by 1, 2,
+// 4, 8; lanes shifted in from outside the row read 0).
+__device__ __forceinline__ float row_shr_f(float x, int n) {
+    const int xi = __builtin_bit_cast(int, x);
+    int y = 0;
+    switch (n) {
+        case 1: y = __builtin_amdgcn_update_dpp(0, xi, 0x111, 0xf, 0xf, false); break;
+        case 2: y = __builtin_amdgcn_update_dpp(0, xi, 0x112, 0xf, 0xf, false); break;
+        case 4: y = __builtin_amdgcn_update_dpp(0, xi, 0x114, 0xf, 0xf, false); break;
+        default: y = __builtin_amdgcn_update_dpp(0, xi, 0x118, 0xf, 0xf, false); break;
+    }
+    return __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float row_scan16(float x) {
+    x += row_shr_f(x, 1);
+    x += row_shr_f(x, 2);
+    x += row_shr_f(x, 4);
+    x += row_shr_f(x, 8);
+    return x;
+}
 
 // Lanes of one 16-lane row hold 16 consecutive tokens.  Returns x of lane
 // (lane ^ 2^p) | (2^p - 1): the last token of the other half of this token's
@@ -411,8 +448,8 @@ __device__ __forceinline__ float other_half_last(int p, float x, int lane) {
 // (I, J) with J < I -> index into the rescaling table
 __device__ __forceinline__ int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
 
-template <int DK, int DV, bool F16, int GATE>
-__global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
+template <int DK, int DV, bool F16, int GATE, bool FAST>
+__device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
     using L = PrepLds<DK, DV, F16>;
     using A = typename L::A;
     using M = Mx<F16>;
@@ -425,8 +462,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     constexpr int NV = C * VROW16 / 256;
 
     const int H = P.H;
-    const int g = blockIdx.x / H;
-    const int h = blockIdx.x - g * H;
+    const int g = blk / H;
+    const int h = blk - g * H;
     int t0, len;
     if (P.T > 0) {
         // dense batch: chunk g is chunk j of sequence n
@@ -502,202 +539,378 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
     const float bet_raw = P.beta[static_cast<size_t>(t0 + min(r, rl)) * H + h];
     const float bet = valid ? bet_raw : 0.f;
 
-    // ---- (a) decay inside each 16-token block, as products of alpha -------------
-    // No decay factor is ever formed above 1: every factor below is a product
-    // of alpha over a run of tokens, in [0, 1], so no gate in [0, 1] can
-    // overflow anything (strongly forgetting channels only underflow, towards
-    // the exact limit 0).  This is the chunk-wise normalisation that keeps chunk
-    // boundaries from overflowing ("Designing and Deploying Hybrid MLA and
-    // Linear Attention Architectures", section 3), taken down to single tokens.
-    // For this lane's token r and p = 0..4:
-    //   pf_p(r) = product of alpha over r's aligned group of 2^p tokens, up to r
-    //   sf_p(r) = product of alpha after r, to the end of that group.
-    // From groups of 2^p to 2^(p+1) tokens, a token in the upper half takes the
-    // lower half's total into pf, a token in the lower half the upper half's
-    // total into sf; that total is pf_p of the other half's last token.
-    constexpr bool SCAL = GATE == KDA_GATE_SCALAR;
-    float pf[KS][8], sf[KS][8];
-    auto PF = [&](int ks, int e) -> float& { return SCAL ? pf[0][0] : pf[ks][e]; };
-    auto SF = [&](int ks, int e) -> float& { return SCAL ? sf[0][0] : sf[ks][e]; };
-    if constexpr (SCAL) {
-        pf[0][0] = valid ? gscalar : 1.f;
-        sf[0][0] = 1.f;
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f4 av;
-                if constexpr (GATE == KDA_GATE_ALPHA) {
-                    av = graw[ks][half];
-                } else {
-                    const f4 xv = Raw4<true>::widen(graw[ks][half]);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) av[i] = alpha_from_softplus_arg(xv[i]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pf[ks][4 * half + i] = valid ? av[i] : 1.f;
-                    sf[ks][4 * half + i] = 1.f;
-                }
-            }
-    }
-    if (lg == 0) s_beta[r] = bet;
-
-    // Diagonal 16 x 16 blocks of A and P.  A pair of tokens s < r of this block
-    // is taken at the level p of the highest bit in which r and s differ: both
-    // lie in one aligned group of 2^(p+1) tokens, s in its lower half and r in
-    // its upper half, and the decay between them factors exactly as
-    //   prod_{t = s+1..r} alpha_t = pf_p(r) * sf_p(s),   both factors <= 1.
-    // Level p is one matrix-core product of k (and q) scaled by pf_p on tokens
-    // with bit p set and by sf_p on the others; only its own pairs are kept.
-    // Lane (lm, lg) gathers A[16I + 4lg + i][16I + lm] in dA and
-    // P[16I + lm][16I + 4lg + i] in dP (the layouts of the blocks below the
-    // diagonal in (c)).
-    f4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const bool up = (lm >> p) & 1;
-        f4 la = {0.f, 0.f, 0.f, 0.f}, lp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            V kc, qc;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f4 kw = R4::widen(kraw[ks][half]);
-                const f4 qw = R4::widen(qraw[ks][half]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * half + i;
-                    const float f = up ? PF(ks, e) : SF(ks, e);
-                    kc[e] = M::cvt((valid ? kw[i] : 0.f) * f);
-                    qc[e] = M::cvt((valid ? qw[i] : 0.f) * f);
-                }
-            }
-            la = M::mma(kc, kc, la);      // rows r (A operand), columns s (B operand)
-            lp = M::mma(kc, qc, lp);      // P^T: rows s, columns r
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ra_ = 4 * lg + i;
-            if (((ra_ ^ lm) >> p) == 1) {
-                if ((ra_ >> p) & 1) dA[i] = la[i];     // r = 4lg + i above s = lm
-                else dP[i] = lp[i];                    // r = lm above s = 4lg + i
-            }
-        }
-        // pf_p, sf_p -> pf_{p+1}, sf_{p+1}
-#pragma unroll
-        for (int ks = 0; ks < (SCAL ? 1 : KS); ++ks)
-#pragma unroll
-            for (int e = 0; e < (SCAL ? 1 : 8); ++e) {
-                const float o = other_half_last(p, pf[ks][e], lane);
-                if (up) pf[ks][e] *= o;
-                else sf[ks][e] *= o;
-            }
-    }
-    {   // the diagonal of P: q_r . k_r, no decay
-        f4 pd = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            V kc, qc;
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f4 kw = R4::widen(kraw[ks][half]);
-                const f4 qw = R4::widen(qraw[ks][half]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kc[4 * half + i] = M::cvt(valid ? kw[i] : 0.f);
-                    qc[4 * half + i] = M::cvt(valid ? qw[i] : 0.f);
-                }
-            }
-            pd = M::mma(kc, qc, pd);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * lg + i == lm) dP[i] = pd[i];
-    }
-    // block totals F_I (= pf_4 of the block's last token), [4][DK]
-    if (lm == 15) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int half = 0; half < 2; ++half)
-                *reinterpret_cast<f4*>(s_F + I * DK + 32 * ks + 16 * half + 4 * lg) =
-                    f4{PF(ks, 4 * half), PF(ks, 4 * half + 1), PF(ks, 4 * half + 2), PF(ks, 4 * half + 3)};
-    }
-    __syncthreads();
-    // gamma = F_0 F_1 F_2 F_3
-    if (tid < DK)
-        reinterpret_cast<float*>(rec + R::GAM)[tid] =
-            s_F[tid] * s_F[DK + tid] * s_F[2 * DK + tid] * s_F[3 * DK + tid];
-
-    // ---- (b) every decay-dependent quantity of this lane's elements -----------
-    // With E_I = F_0..F_{I-1} and X_I = F_{I+1}..F_3 (products, per channel):
-    //   Gamma_r = E_I pf_4(r),  gamma / Gamma_r = sf_4(r) X_I.
-    // Blocks below the diagonal (J < I) take 2^(b_r - b_s) as
-    //   [pf_4(r)] * [sf_4(s) F_{J+1} .. F_{I-1}]
-    // (split at the end of block I - 1): the row operands k pf_4, q pf_4 of
-    // block I serve every J < I, and the column operand of block J for a later
-    // block I is made by the wave that owns block J and handed over through LDS.
+    // Two forms of (a) - (c), chosen per (chunk, head) from its decay:
+    //   direct:  b = cumsum(log2 alpha) over the chunk; Gamma = 2^b and
+    //            1/Gamma as fp32 factors, each 16 x 16 block rebased at its
+    //            token 16I+7, so the 16-bit operands span at most 8 tokens of
+    //            decay (checked below against the operand range);
+    //   general: every decay factor a product of alpha over a run of tokens,
+    //            never above 1, for any gate in [0, 1].
+    // Both write the same record.
     V ra[KS], rq[KS];             // row operands of the blocks below the diagonal
-    // one copy per block index I (= the wave), so the tests of the later
-    // blocks fold at compile time and the column operands of blocks that do
-    // not exist take no registers
-    auto derive = [&](auto ic) {
-        constexpr int I = decltype(ic)::value;
-        E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
+    [[maybe_unused]] V Dc[KS];    // direct form: column operand of the diagonal block
+    [[maybe_unused]] f4 dA = {0.f, 0.f, 0.f, 0.f}, dP = {0.f, 0.f, 0.f, 0.f};   // general form: diagonal blocks
+    __shared__ int s_bad;         // direct form: some check failed (read at the end)
+    if constexpr (FAST) {
+        float* s_tot = s_AT;                                            // [4][DK], until (c)
+        float* s_fac = s_AT + 4 * DK;                                   // [16][DK], until (c)
+        auto chan = [&](int ks, int e) { return 32 * ks + frag_k(lg, e); };
+        float b[KS][8];
+        // ---- (a) b = inclusive cumsum of log2(alpha) over the chunk's tokens -----
+        // scan over the 16 tokens of this wave's block (lanes of one 16-lane row),
+        // then add the totals of the earlier blocks
+        // log2(alpha) of this lane's elements (0 past the chunk's end), scanned
+        if constexpr (GATE == KDA_GATE_SCALAR) {
+            const float x = row_scan16(valid ? flog2(gscalar) : 0.f);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            float qv[8], kh[8], kt[8], cl[3][8];
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const f4 kw = R4::widen(kraw[ks][half]);
-                const f4 qw = R4::widen(qraw[ks][half]);
-                f4 Fb[4];
+                for (int e = 0; e < 8; ++e) b[ks][e] = x;
+        } else {
 #pragma unroll
-                for (int K = 0; K < 4; ++K)
-                    if (K != I) Fb[K] = *reinterpret_cast<const f4*>(s_F + K * DK + 32 * ks + 16 * half + 4 * lg);
-                f4 Eb = {1.f, 1.f, 1.f, 1.f}, Xb = {1.f, 1.f, 1.f, 1.f};
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                for (int K = 0; K < I; ++K) Eb = Eb * Fb[K];
+                for (int half = 0; half < 2; ++half) {
+                    f4 lv;
+                    if constexpr (GATE == KDA_GATE_ALPHA) {
 #pragma unroll
-                for (int K = I + 1; K < 4; ++K) Xb = Xb * Fb[K];
-                f4 mid[3];                         // F_{I+1} .. F_{Il-1} for the later blocks Il
-                mid[0] = f4{1.f, 1.f, 1.f, 1.f};
-                if (I + 2 < 4) mid[1] = Fb[I + 1 < 4 ? I + 1 : 0];
-                if (I + 3 < 4) mid[2] = mid[1] * Fb[I + 2 < 4 ? I + 2 : 0];
+                        for (int i = 0; i < 4; ++i) lv[i] = flog2(graw[ks][half][i]);
+                    } else {
+                        const f4 xv = Raw4<true>::widen(graw[ks][half]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int e = 4 * half + i;
-                    const float kv = valid ? kw[i] : 0.f, qx = valid ? qw[i] : 0.f;
-                    const float pfv = PF(ks, e), sfv = SF(ks, e);
-                    const float G = Eb[i] * pfv;
-                    ra[ks][e] = M::cvt(kv * pfv);
-                    rq[ks][e] = M::cvt(qx * pfv);
+                        for (int i = 0; i < 4; ++i) lv[i] = log2_alpha_from_softplus_arg(xv[i]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) b[ks][4 * half + i] = row_scan16(valid ? lv[i] : 0.f);
+                }
+        }
+        if (lm == 15) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_tot[I * DK + chan(ks, e)] = b[ks][e];
+        }
+        if (lg == 0) s_beta[r] = bet;
+        __syncthreads();
+        for (int Ip = 0; Ip < I; ++Ip)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) b[ks][e] += s_tot[Ip * DK + chan(ks, e)];
+        // Gamma = 2^b and 1/Gamma for every element; every other decay factor is
+        // one of them times a per-channel constant taken at the block's reference
+        // token 16I+7 (lane 7 of the row) or its last token 16I+15 (lane 15):
+        //   s_fac rows 0..3 2^ref_I, 4..7 2^-ref_I, 8..11 2^end_I, 12..15 2^-end_I
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[ks][e] = fexp2(b[ks][e]);
+        if (lm == 7 || lm == 15) {
+            float* d0 = s_fac + ((lm == 7 ? 0 : 8) + I) * DK + 4 * lg;
+            float* d1 = d0 + 4 * DK;
+            auto rcp4 = [&](int ks, int o) {
+                return f4{__builtin_amdgcn_rcpf(b[ks][o]), __builtin_amdgcn_rcpf(b[ks][o + 1]),
+                          __builtin_amdgcn_rcpf(b[ks][o + 2]), __builtin_amdgcn_rcpf(b[ks][o + 3])};
+            };
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                *reinterpret_cast<f4*>(d0 + 32 * ks) = f4{b[ks][0], b[ks][1], b[ks][2], b[ks][3]};
+                *reinterpret_cast<f4*>(d0 + 32 * ks + 16) = f4{b[ks][4], b[ks][5], b[ks][6], b[ks][7]};
+                *reinterpret_cast<f4*>(d1 + 32 * ks) = rcp4(ks, 0);
+                *reinterpret_cast<f4*>(d1 + 32 * ks + 16) = rcp4(ks, 4);
+            }
+        }
+        // (cleared here, once the loads above have landed: a store at the
+        // kernel's start made the compiler wait for every load in flight)
+        if (tid == 0) s_bad = 0;
+        __syncthreads();
+        // The direct form holds when, for every channel, the decay over the chunk
+        // stays within 2^-64 (Gamma and 1/Gamma are fp32 factors) and, with
+        // 16-bit operands, the decay over each 16-token block within 2^-14 and
+        // |k|, |q| <= 2 (every operand below then stays within 2^15, inside fp16).
+        // Otherwise the (chunk, head) joins the general-form list at the end
+        // and the general kernel writes its whole record again (this
+        // workgroup still runs to the end: its addressing does not depend on
+        // the values, and an early exit here slowed every chunk down).
+        {
+            // branch-free (bitwise and / or); |k|, |q| are checked in derive
+            int bad = 0;
+            if (tid < DK) {
+                const float* e = s_fac + 8 * DK + tid;      // 2^end_I, I = 0..3
+                const float e0 = e[0], e1 = e[DK], e2 = e[2 * DK], e3 = e[3 * DK];
+                bool ok = e3 >= 0x1p-64f;
+                if constexpr (F16)
+                    ok = ok & (e0 >= 0x1p-14f) & (e1 >= 0x1p-14f * e0) & (e2 >= 0x1p-14f * e1) & (e3 >= 0x1p-14f * e2);
+                bad = !ok;
+            }
+            if (bad) atomicOr(&s_bad, 1);
+        }
+        float kqmax = 0.f;            // max |k|, |q| of this lane's elements (taken in derive)
+        // gamma
+        if (tid < DK) reinterpret_cast<float*>(rec + R::GAM)[tid] = s_fac[11 * DK + tid];
+
+        // ---- (b) every decay-dependent quantity of this lane's elements -----------
+        // A[r][s] and P[r][s] (s <= r) take 2^(b_r - b_s) = 2^(b_r - ref_I) 2^(ref_I - b_s)
+        // for r in block I: the row operands (k, q) 2^(b - ref_I) are shared by
+        // every column block; the column operand k_s 2^(ref_I - b_s) (<= 1 below
+        // the diagonal block) is made by the wave that owns token s, for every
+        // later block I, and handed over through LDS.
+        // one copy per block index I (= the wave), so the tests of the later
+        // blocks fold at compile time and the column operands of blocks that do
+        // not exist take no registers (181 instead of 247)
+        auto derive = [&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
+            auto fac4 = [&](int row, int ks, int half) {
+                return *reinterpret_cast<const f4*>(s_fac + row * DK + 32 * ks + 16 * half + 4 * lg);
+            };
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float qv[8], kh[8], kt[8], cl[3][8];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const f4 kw = R4::widen(kraw[ks][half]);
+                    const f4 qw = R4::widen(qraw[ks][half]);
+                    const f4 ref = fac4(I, ks, half);          // 2^ref_I
+                    const f4 rref = fac4(4 + I, ks, half);     // 2^-ref_I
+                    const f4 gam = fac4(11, ks, half);         // gamma = 2^end_3
+                    f4 refl[3];                                // 2^ref of the later blocks
 #pragma unroll
                     for (int Il = 1; Il < 4; ++Il)
-                        if (Il > I) cl[Il - 1][e] = kv * (sfv * mid[Il - I - 1][i]);
-                    kh[e] = kv * G;
-                    qv[e] = qx * G;
-                    kt[e] = kv * (sfv * Xb[i]);
+                        if (Il > I) refl[Il - 1] = fac4(Il, ks, half);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * half + i;
+                        const float G = b[ks][e], rG = __builtin_amdgcn_rcpf(G);
+                        const float kv = valid ? kw[i] : 0.f, qx = valid ? qw[i] : 0.f;
+                        if constexpr (F16) kqmax = fmaxf(kqmax, fmaxf(__builtin_fabsf(kv), __builtin_fabsf(qx)));
+                        const float e1 = G * rref[i];                      // 2^(b - ref_I)
+                        ra[ks][e] = M::cvt(kv * e1);
+                        rq[ks][e] = M::cvt(qx * e1);
+                        Dc[ks][e] = M::cvt(kv * (rG * ref[i]));           // k 2^(ref_I - b)
+#pragma unroll
+                        for (int Il = 1; Il < 4; ++Il)
+                            if (Il > I) cl[Il - 1][e] = kv * (rG * refl[Il - 1][i]);
+                        kh[e] = kv * G;
+                        qv[e] = qx * G;
+                        kt[e] = kv * (rG * gam[i]);                        // k gamma / Gamma
+                    }
+                }
+                M::gstore8(qh + frag_off(I * KS + ks, lane), qv);
+#pragma unroll
+                for (int Il = 1; Il < 4; ++Il)
+                    if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
+                const int c0 = 32 * ks + 4 * lg;
+                M::store4(s_khat + r * KXP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
+                M::store4(s_khat + r * KXP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
+                M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
+                M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
+            }
+            };
+        switch (I) {
+            case 0: derive(std::integral_constant<int, 0>{}); break;
+            case 1: derive(std::integral_constant<int, 1>{}); break;
+            case 2: derive(std::integral_constant<int, 2>{}); break;
+            default: derive(std::integral_constant<int, 3>{}); break;
+        }
+        if constexpr (F16)
+            if (!(kqmax <= 2.f)) atomicOr(&s_bad, 1);
+    } else {
+        // ---- (a) decay inside each 16-token block, as products of alpha -------------
+        // No decay factor is ever formed above 1: every factor below is a product
+        // of alpha over a run of tokens, in [0, 1], so no gate in [0, 1] can
+        // overflow anything (strongly forgetting channels only underflow, towards
+        // the exact limit 0).  This is the chunk-wise normalisation that keeps chunk
+        // boundaries from overflowing ("Designing and Deploying Hybrid MLA and
+        // Linear Attention Architectures", section 3), taken down to single tokens.
+        // For this lane's token r and p = 0..4:
+        //   pf_p(r) = product of alpha over r's aligned group of 2^p tokens, up to r
+        //   sf_p(r) = product of alpha after r, to the end of that group.
+        // From groups of 2^p to 2^(p+1) tokens, a token in the upper half takes the
+        // lower half's total into pf, a token in the lower half the upper half's
+        // total into sf; that total is pf_p of the other half's last token.
+        constexpr bool SCAL = GATE == KDA_GATE_SCALAR;
+        float pf[KS][8], sf[KS][8];
+        auto PF = [&](int ks, int e) -> float& { return SCAL ? pf[0][0] : pf[ks][e]; };
+        auto SF = [&](int ks, int e) -> float& { return SCAL ? sf[0][0] : sf[ks][e]; };
+        if constexpr (SCAL) {
+            pf[0][0] = valid ? gscalar : 1.f;
+            sf[0][0] = 1.f;
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    f4 av;
+                    if constexpr (GATE == KDA_GATE_ALPHA) {
+                        av = graw[ks][half];
+                    } else {
+                        const f4 xv = Raw4<true>::widen(graw[ks][half]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) av[i] = alpha_from_softplus_arg(xv[i]);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pf[ks][4 * half + i] = valid ? av[i] : 1.f;
+                        sf[ks][4 * half + i] = 1.f;
+                    }
+                }
+        }
+        if (lg == 0) s_beta[r] = bet;
+
+        // Diagonal 16 x 16 blocks of A and P.  A pair of tokens s < r of this block
+        // is taken at the level p of the highest bit in which r and s differ: both
+        // lie in one aligned group of 2^(p+1) tokens, s in its lower half and r in
+        // its upper half, and the decay between them factors exactly as
+        //   prod_{t = s+1..r} alpha_t = pf_p(r) * sf_p(s),   both factors <= 1.
+        // Level p is one matrix-core product of k (and q) scaled by pf_p on tokens
+        // with bit p set and by sf_p on the others; only its own pairs are kept.
+        // Lane (lm, lg) gathers A[16I + 4lg + i][16I + lm] in dA and
+        // P[16I + lm][16I + 4lg + i] in dP (the layouts of the blocks below the
+        // diagonal in (c)).
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const bool up = (lm >> p) & 1;
+            f4 la = {0.f, 0.f, 0.f, 0.f}, lp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                V kc, qc;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const f4 kw = R4::widen(kraw[ks][half]);
+                    const f4 qw = R4::widen(qraw[ks][half]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * half + i;
+                        const float f = up ? PF(ks, e) : SF(ks, e);
+                        kc[e] = M::cvt((valid ? kw[i] : 0.f) * f);
+                        qc[e] = M::cvt((valid ? qw[i] : 0.f) * f);
+                    }
+                }
+                la = M::mma(kc, kc, la);      // rows r (A operand), columns s (B operand)
+                lp = M::mma(kc, qc, lp);      // P^T: rows s, columns r
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ra_ = 4 * lg + i;
+                if (((ra_ ^ lm) >> p) == 1) {
+                    if ((ra_ >> p) & 1) dA[i] = la[i];     // r = 4lg + i above s = lm
+                    else dP[i] = lp[i];                    // r = lm above s = 4lg + i
                 }
             }
-            M::gstore8(qh + frag_off(I * KS + ks, lane), qv);
+            // pf_p, sf_p -> pf_{p+1}, sf_{p+1}
 #pragma unroll
-            for (int Il = 1; Il < 4; ++Il)
-                if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
-            const int c0 = 32 * ks + 4 * lg;
-            M::store4(s_khat + r * KXP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
-            M::store4(s_khat + r * KXP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
-            M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
-            M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
+            for (int ks = 0; ks < (SCAL ? 1 : KS); ++ks)
+#pragma unroll
+                for (int e = 0; e < (SCAL ? 1 : 8); ++e) {
+                    const float o = other_half_last(p, pf[ks][e], lane);
+                    if (up) pf[ks][e] *= o;
+                    else sf[ks][e] *= o;
+                }
         }
-        };
-    switch (I) {
-        case 0: derive(std::integral_constant<int, 0>{}); break;
-        case 1: derive(std::integral_constant<int, 1>{}); break;
-        case 2: derive(std::integral_constant<int, 2>{}); break;
-        default: derive(std::integral_constant<int, 3>{}); break;
+        {   // the diagonal of P: q_r . k_r, no decay
+            f4 pd = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                V kc, qc;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const f4 kw = R4::widen(kraw[ks][half]);
+                    const f4 qw = R4::widen(qraw[ks][half]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        kc[4 * half + i] = M::cvt(valid ? kw[i] : 0.f);
+                        qc[4 * half + i] = M::cvt(valid ? qw[i] : 0.f);
+                    }
+                }
+                pd = M::mma(kc, qc, pd);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * lg + i == lm) dP[i] = pd[i];
+        }
+        // block totals F_I (= pf_4 of the block's last token), [4][DK]
+        if (lm == 15) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+                    *reinterpret_cast<f4*>(s_F + I * DK + 32 * ks + 16 * half + 4 * lg) =
+                        f4{PF(ks, 4 * half), PF(ks, 4 * half + 1), PF(ks, 4 * half + 2), PF(ks, 4 * half + 3)};
+        }
+        __syncthreads();
+        // gamma = F_0 F_1 F_2 F_3
+        if (tid < DK)
+            reinterpret_cast<float*>(rec + R::GAM)[tid] =
+                s_F[tid] * s_F[DK + tid] * s_F[2 * DK + tid] * s_F[3 * DK + tid];
+
+        // ---- (b) every decay-dependent quantity of this lane's elements -----------
+        // With E_I = F_0..F_{I-1} and X_I = F_{I+1}..F_3 (products, per channel):
+        //   Gamma_r = E_I pf_4(r),  gamma / Gamma_r = sf_4(r) X_I.
+        // Blocks below the diagonal (J < I) take 2^(b_r - b_s) as
+        //   [pf_4(r)] * [sf_4(s) F_{J+1} .. F_{I-1}]
+        // (split at the end of block I - 1): the row operands k pf_4, q pf_4 of
+        // block I serve every J < I, and the column operand of block J for a later
+        // block I is made by the wave that owns block J and handed over through LDS.
+        // one copy per block index I (= the wave), so the tests of the later
+        // blocks fold at compile time and the column operands of blocks that do
+        // not exist take no registers
+        auto derive = [&](auto ic) {
+            constexpr int I = decltype(ic)::value;
+            E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                float qv[8], kh[8], kt[8], cl[3][8];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const f4 kw = R4::widen(kraw[ks][half]);
+                    const f4 qw = R4::widen(qraw[ks][half]);
+                    f4 Fb[4];
+#pragma unroll
+                    for (int K = 0; K < 4; ++K)
+                        if (K != I) Fb[K] = *reinterpret_cast<const f4*>(s_F + K * DK + 32 * ks + 16 * half + 4 * lg);
+                    f4 Eb = {1.f, 1.f, 1.f, 1.f}, Xb = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                    for (int K = 0; K < I; ++K) Eb = Eb * Fb[K];
+#pragma unroll
+                    for (int K = I + 1; K < 4; ++K) Xb = Xb * Fb[K];
+                    f4 mid[3];                         // F_{I+1} .. F_{Il-1} for the later blocks Il
+                    mid[0] = f4{1.f, 1.f, 1.f, 1.f};
+                    if (I + 2 < 4) mid[1] = Fb[I + 1 < 4 ? I + 1 : 0];
+                    if (I + 3 < 4) mid[2] = mid[1] * Fb[I + 2 < 4 ? I + 2 : 0];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * half + i;
+                        const float kv = valid ? kw[i] : 0.f, qx = valid ? qw[i] : 0.f;
+                        const float pfv = PF(ks, e), sfv = SF(ks, e);
+                        const float G = Eb[i] * pfv;
+                        ra[ks][e] = M::cvt(kv * pfv);
+                        rq[ks][e] = M::cvt(qx * pfv);
+#pragma unroll
+                        for (int Il = 1; Il < 4; ++Il)
+                            if (Il > I) cl[Il - 1][e] = kv * (sfv * mid[Il - I - 1][i]);
+                        kh[e] = kv * G;
+                        qv[e] = qx * G;
+                        kt[e] = kv * (sfv * Xb[i]);
+                    }
+                }
+                M::gstore8(qh + frag_off(I * KS + ks, lane), qv);
+#pragma unroll
+                for (int Il = 1; Il < 4; ++Il)
+                    if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
+                const int c0 = 32 * ks + 4 * lg;
+                M::store4(s_khat + r * KXP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
+                M::store4(s_khat + r * KXP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
+                M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
+                M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
+            }
+            };
+        switch (I) {
+            case 0: derive(std::integral_constant<int, 0>{}); break;
+            case 1: derive(std::integral_constant<int, 1>{}); break;
+            case 2: derive(std::integral_constant<int, 2>{}); break;
+            default: derive(std::integral_constant<int, 3>{}); break;
+        }
     }
     // v is first needed in (e); loading it here keeps it out of the
     // registers of the phases above
@@ -721,10 +934,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             accP[J] = f4{0.f, 0.f, 0.f, 0.f};
             if (J <= I) {
                 f4 accA = {0.f, 0.f, 0.f, 0.f};
-                if (J < I) {
+                if (FAST || J < I) {
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
-                        const V col = M::load8(s_C + frag_off(pair_index(I, J) * KS + ks, lane));
+                        V col;
+                        if constexpr (FAST) col = J == I ? Dc[ks] : M::load8(s_C + frag_off(pair_index(I, J) * KS + ks, lane));
+                        else col = M::load8(s_C + frag_off(pair_index(I, J) * KS + ks, lane));
                         accA = M::mma(ra[ks], col, accA);
                         accP[J] = M::mma(col, rq[ks], accP[J]);
                     }
@@ -890,6 +1105,26 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
             }
         }
     }
+    if constexpr (FAST) {
+        // s_bad was last written before the barrier that precedes (c)
+        if (tid == 0 && s_bad) P.slow[atomicAdd(P.nslow, 1)] = blk;
+    }
+}
+
+// One workgroup per (chunk, head): the direct form, or the (chunk, head)'s
+// entry in the general-form list.
+template <int DK, int DV, bool F16, int GATE>
+__global__ __launch_bounds__(256, 2) void prep_kernel(const PrepParams P) {
+    prep_body<DK, DV, F16, GATE, true>(P, blockIdx.x);
+}
+
+// Entry blockIdx.x of the general-form list, if the list is that long (one
+// workgroup per (chunk, head), the list's largest length; those past its end
+// return at once).
+template <int DK, int DV, bool F16, int GATE>
+__global__ __launch_bounds__(256, 2) void prep_general_kernel(const PrepParams P) {
+    if (static_cast<int>(blockIdx.x) >= *P.nslow) return;
+    prep_body<DK, DV, F16, GATE, false>(P, P.slow[blockIdx.x]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1229,16 +1464,24 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         pp.H = pl.H;
         pp.T = pl.varlen ? 0 : pl.T;
         pp.cps = static_cast<int>((pl.T + C - 1) / C);
+        pp.nslow = ctrl + 1;
+        pp.slow = reinterpret_cast<int32_t*>(ws + pl.off_slow);
         constexpr int lds = PrepLds<DK, DV, F16>::bytes;
         auto kfn = a.gate_kind == KDA_GATE_SOFTPLUS_BF16 ? prep_kernel<DK, DV, F16, KDA_GATE_SOFTPLUS_BF16>
                  : a.gate_kind == KDA_GATE_SCALAR        ? prep_kernel<DK, DV, F16, KDA_GATE_SCALAR>
                                                          : prep_kernel<DK, DV, F16, KDA_GATE_ALPHA>;
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(kfn),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kfn, dim3(static_cast<unsigned>(pl.gmax * pl.H)), dim3(256), lds, stream, pp);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        auto kgen = a.gate_kind == KDA_GATE_SOFTPLUS_BF16 ? prep_general_kernel<DK, DV, F16, KDA_GATE_SOFTPLUS_BF16>
+                  : a.gate_kind == KDA_GATE_SCALAR        ? prep_general_kernel<DK, DV, F16, KDA_GATE_SCALAR>
+                                                          : prep_general_kernel<DK, DV, F16, KDA_GATE_ALPHA>;
+        const dim3 grid(static_cast<unsigned>(pl.gmax * pl.H));
+        for (auto fn : {kfn, kgen}) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, pp);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
 
     StateParams sp;
@@ -1290,6 +1533,7 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.off_first = off; off = align256(off + 4 * (static_cast<size_t>(p.N) + 1));
     p.off_order = off; off = align256(off + 4 * static_cast<size_t>(p.N));
     p.off_table = off; off = align256(off + 16 * static_cast<size_t>(p.gmax));
+    p.off_slow = off;  off = align256(off + 4 * gh);    // general-form list of the C = 64 forward
     // per (head, chunk) record: qh, w, ktt, p (its six lower fragments), ut
     // (operand type), gam (fp32)
     if (chunk_size == C)
