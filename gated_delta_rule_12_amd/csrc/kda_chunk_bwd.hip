@@ -193,9 +193,9 @@ template <int DK, int DV> struct PrepB {
     static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + 2 * C + (C / 16) * DK) * 4;
 };
 
-// FAST: the direct form, which first checks the chunk's decay and, when any
-// channel decays below 2^-64, appends the (chunk, head) to
-// the general list and returns; otherwise the general form.
+// FAST: the direct form, which checks the chunk's decay and, when any channel
+// decays below 2^-64, flags the (chunk, head) and appends it to the general
+// list; otherwise the general form.
 template <int DK, int DV, bool ABF16, int GATE, bool FAST>
 __device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const int g) {
     using R = BRec<DK, DV, ABF16>;
@@ -246,10 +246,10 @@ __device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const
     // the ten below or on the diagonal spread so the waves sharing a SIMD
     // (w, w + 4) hold 3, 3, 2, 2 of them; the six above are only zeroed.
     constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x1101, 0x2102, 0x2203, 0x3112, 0x3213, 0x3323};
+    [[maybe_unused]] float* sGam = sTot; // direct form: gamma = 2^b_last per channel [DK], kept to the end
     if constexpr (FAST) {
         // b = cumsum(log2 alpha) per channel over the chunk;
         // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
-        float* sGam = sTot;              // gamma = 2^b_last per channel   [DK]
         gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sA, [&](int r, int c, float b) {
             const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
             const float kv = sKh[r * LK + c];
@@ -259,14 +259,10 @@ __device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const
             if (r == C - 1) sGam[c] = G;
         });
         __syncthreads();
-        if (__syncthreads_or(tid < DK && sGam[tid] < kFastGammaMin)) {
-            if (tid == 0) {
-                P.flag[g * H + h] = 1;
-                P.slow[atomicAdd(P.nslow, 1)] = g * H + h;
-            }
-            return;
-        }
-        if (tid == 0) P.flag[g * H + h] = 0;
+        // A (chunk, head) outside the direct form's range is flagged and
+        // listed at the end (gamma stays in sGam), and the general kernel
+        // writes its whole record again; this workgroup still runs to the end
+        // (its addressing does not depend on the values).
         if (tid < DK) gGam[tid] = sGam[tid];
         if constexpr (!ABF16) {          // the 16-bit passes read Kt as fp16 fragments only
             for (int idx = tid; idx < C * DK; idx += NTH) {
@@ -443,6 +439,18 @@ __device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const
         auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
         write_afrags<C, DK, NTH>(hrec(R::FW), [&](int m, int k) { return sKb[m * LK + k]; });
         write_afrags<DK, C, NTH>(hrec(R::FWT), [&](int m, int k) { return sKb[k * LK + m]; });
+    }
+    if constexpr (FAST) {
+        if (wave == 0) {                 // gamma (sGam) is left untouched since the scan
+            bool bad = false;
+#pragma unroll
+            for (int c = lane; c < DK; c += 64) bad |= sGam[c] < kFastGammaMin;
+            const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+            if (lane == 0) {
+                P.flag[g * H + h] = any;
+                if (any) P.slow[atomicAdd(P.nslow, 1)] = g * H + h;
+            }
+        }
     }
 }
 
