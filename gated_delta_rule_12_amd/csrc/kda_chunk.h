@@ -36,7 +36,7 @@ struct ChunkPlan {
     int64_t gmax = 0;             // chunk-table capacity
     size_t eb = 4;                // bytes per intermediate element
     size_t off_ctrl = 0, off_first = 0, off_order = 0, off_table = 0;
-    size_t off_slow = 0;          // (chunk, head) list of the C = 64 forward's general form
+    size_t off_slow = 0;          // (chunk, head) list of the preparation kernels' general form
     size_t off_rec = 0, rec_bytes = 0;
     size_t workspace_bytes = 0;
 };

@@ -1533,7 +1533,7 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
     p.off_first = off; off = align256(off + 4 * (static_cast<size_t>(p.N) + 1));
     p.off_order = off; off = align256(off + 4 * static_cast<size_t>(p.N));
     p.off_table = off; off = align256(off + 16 * static_cast<size_t>(p.gmax));
-    p.off_slow = off;  off = align256(off + 4 * gh);    // general-form list of the C = 64 forward
+    p.off_slow = off;  off = align256(off + 4 * gh);    // general-form list of the preparation kernels
     // per (head, chunk) record: qh, w, ktt, p (its six lower fragments), ut
     // (operand type), gam (fp32)
     if (chunk_size == C)

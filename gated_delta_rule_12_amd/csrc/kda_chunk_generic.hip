@@ -80,6 +80,8 @@ struct GParams {
     size_t rec_bytes;
     int64_t gmax;
     int N, H;
+    int32_t* nslow;   // length of the general-form list (zeroed by the chunk table)
+    int32_t* slow;    // general-form list: g * H + h of each (chunk, head) that takes it
 };
 
 __device__ __forceinline__ float* grec(const GParams& P, int h, int g, size_t off) {
@@ -90,16 +92,26 @@ __device__ __forceinline__ float* grec(const GParams& P, int h, int g, size_t of
 // gprep_kernel
 // ---------------------------------------------------------------------------
 template <int C> struct GPrepB {
-    static constexpr int NB = C / 16, NLT = NB * (NB + 1) / 2;
-    static constexpr int bytes = (3 * C * kLS + 2 * NLT * 256 + kWaves * 256 + 2 * C + NB * kSL) * 4;
+    static constexpr int NB = C / 16, NLT = NB * (NB + 1) / 2, NS = kThreads / kSL;
+    // the last region: the direct form's scan segment sums [NS][SL] and gamma
+    // of the slice [SL], or the general form's tile totals [NB][SL]
+    static constexpr int AUX = NS * kSL + kSL > NB * kSL ? NS * kSL + kSL : NB * kSL;
+    static constexpr int bytes = (3 * C * kLS + 2 * NLT * 256 + kWaves * 256 + 2 * C + AUX) * 4;
 };
 
-template <int DK, int DV, int C, bool ABF16, int GATE>
-__global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
+// FAST: the direct form (one cumulative log2 sum per channel over the chunk;
+// Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q in plain products), for every (chunk,
+// head); one in which some channel decays below 2^-64 over the chunk is
+// listed at the end for the general form (!FAST), whose decay factors are
+// all 2^x with x <= 0.  Both write the same record.
+template <int DK, int DV, int C, bool ABF16, int GATE, bool FAST>
+__device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
     using R = GRec<DK, DV, C>;
     constexpr int NTH = kThreads, NW = kWaves, SL = kSL, LS = kLS;
     constexpr int NB = GPrepB<C>::NB, NLT = GPrepB<C>::NLT;
-    constexpr int TW = (NLT + NW - 1) / NW;
+    constexpr int NS = GPrepB<C>::NS, SEG = C / NS;   // direct form: scan segments
+    constexpr int NTASK = 2 * NLT;        // direct form: A and P tiles as separate tasks
+    constexpr int TW = FAST ? (NTASK + NW - 1) / NW : (NLT + NW - 1) / NW;
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     extern __shared__ float lds[];
     float* sK = lds;                     // K; pass 2: beta.Gamma.K, beta.V                      [C][LS]
@@ -110,10 +122,12 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
     float* sX = sT + NLT * 256;          // T-solve scratch, one tile per wave                   [NW][256]
     float* sBeta = sX + NW * 256;        // [C]
     float* sGs = sBeta + C;              // scalar gate per row                                   [C]
-    float* sTot = sGs + C;               // log2 alpha summed over each 16-token tile           [NB][SL]
+    float* sTot = sGs + C;               // general: log2 alpha summed over each 16-token tile   [NB][SL]
+    [[maybe_unused]] float* sPart = sGs + C;          // direct: scan segment sums   [NS][SL]
+    [[maybe_unused]] float* sGam = sPart + NS * SL;   // direct: gamma of the slice  [SL]
 
     const int H = P.H;
-    const int h = blockIdx.x % H, g = blockIdx.x / H;
+    const int h = blk % H, g = blk / H;
     if (g >= P.ctrl[0]) return;
     const int4 ent = P.table[g];
     const int64_t row0 = ent.y;
@@ -130,101 +144,193 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
     float* gKt = grec(P, h, g, R::KT);
     float* gGam = grec(P, h, g, R::GAM);
 
-    // ---- pass 1: per 32-channel slice, decay, Gamma-scaled operands, A and P tiles.
-    // Every decay factor is 2^x with x <= 0 (decayed_tile in kda_mm32.h):
-    // cumulative sums restart at each 16-token tile, and products that cross
-    // tiles add the totals of the tiles in between, so nothing overflows.
-    f4 accA[TW], accP[TW];
+    float* gP = grec(P, h, g, R::P);
+    [[maybe_unused]] bool strong = false;   // direct form: some channel of this lane's decays below 2^-64
+    if constexpr (FAST) {
+        // ---- pass 1: per 32-channel slice, decay, Gamma-scaled operands, A and P tiles
+        f4 acc[TW];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) accA[t] = accP[t] = zero4();
-    for (int cs = 0; cs < DK; cs += SL) {
-        {
-            Tok<ABF16, DK, SL, NTH, C> tk, tq;
-            tk.load(P.k, row0, len, h, H, cs);
-            tq.load(P.q, row0, len, h, H, cs);
-            if constexpr (GATE != KDA_GATE_SCALAR) {
-                Tok<GBF16, DK, SL, NTH, C> tg;
-                tg.load(P.gate, row0, len, h, H, cs);
-                tg.put(sB, LS);
+        for (int t = 0; t < TW; ++t) acc[t] = zero4();
+        for (int cs = 0; cs < DK; cs += SL) {
+            {
+                Tok<ABF16, DK, SL, NTH, C> tk, tq;
+                tk.load(P.k, row0, len, h, H, cs);
+                tq.load(P.q, row0, len, h, H, cs);
+                if constexpr (GATE != KDA_GATE_SCALAR) {
+                    Tok<GBF16, DK, SL, NTH, C> tg;
+                    tg.load(P.gate, row0, len, h, H, cs);
+                    tg.put(sB, LS);
+                }
+                tk.put(sK, LS);
+                tq.put(sQ, LS);
             }
-            tk.put(sK, LS);
-            tq.put(sQ, LS);
-        }
-        __syncthreads();
-        {   // b = cumulative log2 alpha inside each tile (padding rows add 0).  A
-            // gate below 2^-150 counts as 2^-150: every fp32 factor that spans it
-            // is zero either way.
-            const int c = tid % SL, t = tid / SL;
-            if (t < NB) {
-                float b = 0.f;
-                for (int r = 16 * t; r < 16 * t + 16; ++r) {
+            __syncthreads();
+            {   // log2 alpha per element (padding rows: 0), segment sums
+                const int c = tid % SL, sg = tid / SL;
+                float part = 0.f;
+                for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
                     float l2 = 0.f;
                     if (r < len) {
                         if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
                         else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sB[r * LS + c]);
                         else l2 = __builtin_amdgcn_logf(sB[r * LS + c]);
-                        l2 = fmaxf(l2, -150.f);
                     }
-                    b += l2;
-                    sB[r * LS + c] = b;
+                    sB[r * LS + c] = l2;
+                    part += l2;
                 }
-                sTot[t * SL + c] = b;
+                sPart[sg * SL + c] = part;
             }
-        }
-        __syncthreads();
-        // record: b from the chunk start, Gamma.Q = 2^b Q, (gamma / Gamma).K and
-        // gamma; with pre / suf the totals of the tiles before / after the row's:
-        //   b = pre + b_t(r),  log2(gamma / Gamma_r) = T_t - b_t(r) + suf
-        for (int idx = tid; idx < C * SL; idx += NTH) {
-            const int r = idx / SL, c = idx % SL, t = r / 16;
-            float pre = 0.f, suf = 0.f;
-#pragma unroll
-            for (int u = 0; u < NB; ++u) {
-                const float x = sTot[u * SL + c];
-                if (u < t) pre += x;
-                else if (u > t) suf += x;
+            __syncthreads();
+            {   // b = cumsum(log2 alpha); Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q
+                const int c = tid % SL, sg = tid / SL;
+                float b = 0.f;
+                for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * SL + c];
+                for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
+                    b += sB[r * LS + c];
+                    const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+                    const float kv = sK[r * LS + c];
+                    sK[r * LS + c] = G * kv;
+                    sB[r * LS + c] = Gi * kv;
+                    sQ[r * LS + c] *= G;
+                    gB[r * DK + cs + c] = b;
+                }
+                if (sg == NS - 1) {
+                    gGam[cs + c] = sGam[c] = __builtin_amdgcn_exp2f(b);
+                    strong = strong || b < -64.f;     // (NaN stays here and propagates)
+                }
             }
-            const float bl = sB[r * LS + c];
-            const float b = pre + bl;
-            gB[r * DK + cs + c] = b;
-            gQh[r * DK + cs + c] = sQ[r * LS + c] * __builtin_amdgcn_exp2f(b);
-            gKt[r * DK + cs + c] = sK[r * LS + c] * __builtin_amdgcn_exp2f(sTot[t * SL + c] - bl + suf);
-        }
-        if (tid < SL) {
-            float tot = 0.f;
+            __syncthreads();
+            for (int idx = tid; idx < C * SL; idx += NTH) {
+                const int r = idx / SL, c = idx % SL;
+                gKt[r * DK + cs + c] = sGam[c] * sB[r * LS + c];
+                gQh[r * DK + cs + c] = sQ[r * LS + c];
+            }
+            // this slice's share of the A (Kh Kb^T) and P (Qh Kb^T) tiles
 #pragma unroll
-            for (int u = 0; u < NB; ++u) tot += sTot[u * SL + tid];
-            gGam[cs + tid] = __builtin_amdgcn_exp2f(tot);
+            for (int t = 0; t < TW; ++t) {
+                const int task = wave + NW * t;
+                if (task >= NTASK) continue;
+                int ti, tj;
+                lt_decode(task % NLT, ti, tj);
+                acc[t] = mm<SL, true, true>((task < NLT ? sK : sQ) + ti * 16 * LS, LS, 1, sB + tj * 16 * LS, 1, LS,
+                                            acc[t]);
+            }
+            __syncthreads();
         }
-        // this slice's share of the tiles of A (K-hat K-bar^T) and P (Q-hat K-bar^T)
+
+        // ---- A tiles (strictly lower, row-scaled by beta) to LDS; P tiles to the record
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            const int task = wave + NW * t;
+            if (task >= NTASK) continue;
+            int ti, tj;
+            lt_decode(task % NLT, ti, tj);
+            f4 x = acc[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = ti * 16 + 4 * j + e, s = tj * 16 + i;
+                if (task < NLT) x[e] = s < r ? sBeta[r] * x[e] : 0.f;
+                else x[e] = s <= r ? x[e] : 0.f;
+            }
+            if (task < NLT) store_tile(sA + lt(ti, tj) * 256, 16, x);
+            else store_tile(gP + ti * 16 * C + tj * 16, C, x);
+        }
+    } else {
+        // ---- pass 1: per 32-channel slice, decay, Gamma-scaled operands, A and P tiles.
+        // Every decay factor is 2^x with x <= 0 (decayed_tile in kda_mm32.h):
+        // cumulative sums restart at each 16-token tile, and products that cross
+        // tiles add the totals of the tiles in between, so nothing overflows.
+        f4 accA[TW], accP[TW];
+#pragma unroll
+        for (int t = 0; t < TW; ++t) accA[t] = accP[t] = zero4();
+        for (int cs = 0; cs < DK; cs += SL) {
+            {
+                Tok<ABF16, DK, SL, NTH, C> tk, tq;
+                tk.load(P.k, row0, len, h, H, cs);
+                tq.load(P.q, row0, len, h, H, cs);
+                if constexpr (GATE != KDA_GATE_SCALAR) {
+                    Tok<GBF16, DK, SL, NTH, C> tg;
+                    tg.load(P.gate, row0, len, h, H, cs);
+                    tg.put(sB, LS);
+                }
+                tk.put(sK, LS);
+                tq.put(sQ, LS);
+            }
+            __syncthreads();
+            {   // b = cumulative log2 alpha inside each tile (padding rows add 0).  A
+                // gate below 2^-150 counts as 2^-150: every fp32 factor that spans it
+                // is zero either way.
+                const int c = tid % SL, t = tid / SL;
+                if (t < NB) {
+                    float b = 0.f;
+                    for (int r = 16 * t; r < 16 * t + 16; ++r) {
+                        float l2 = 0.f;
+                        if (r < len) {
+                            if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
+                            else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sB[r * LS + c]);
+                            else l2 = __builtin_amdgcn_logf(sB[r * LS + c]);
+                            l2 = fmaxf(l2, -150.f);
+                        }
+                        b += l2;
+                        sB[r * LS + c] = b;
+                    }
+                    sTot[t * SL + c] = b;
+                }
+            }
+            __syncthreads();
+            // record: b from the chunk start, Gamma.Q = 2^b Q, (gamma / Gamma).K and
+            // gamma; with pre / suf the totals of the tiles before / after the row's:
+            //   b = pre + b_t(r),  log2(gamma / Gamma_r) = T_t - b_t(r) + suf
+            for (int idx = tid; idx < C * SL; idx += NTH) {
+                const int r = idx / SL, c = idx % SL, t = r / 16;
+                float pre = 0.f, suf = 0.f;
+#pragma unroll
+                for (int u = 0; u < NB; ++u) {
+                    const float x = sTot[u * SL + c];
+                    if (u < t) pre += x;
+                    else if (u > t) suf += x;
+                }
+                const float bl = sB[r * LS + c];
+                const float b = pre + bl;
+                gB[r * DK + cs + c] = b;
+                gQh[r * DK + cs + c] = sQ[r * LS + c] * __builtin_amdgcn_exp2f(b);
+                gKt[r * DK + cs + c] = sK[r * LS + c] * __builtin_amdgcn_exp2f(sTot[t * SL + c] - bl + suf);
+            }
+            if (tid < SL) {
+                float tot = 0.f;
+#pragma unroll
+                for (int u = 0; u < NB; ++u) tot += sTot[u * SL + tid];
+                gGam[cs + tid] = __builtin_amdgcn_exp2f(tot);
+            }
+            // this slice's share of the tiles of A (K-hat K-bar^T) and P (Q-hat K-bar^T)
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                const int task = wave + NW * t;
+                if (task >= NLT) continue;
+                int ti, tj;
+                lt_decode(task, ti, tj);
+                decayed_tile<SL / 16, true, true>(sK, sQ, sK, sB, sTot, LS, SL, ti, tj, accA[t], accP[t]);
+            }
+            __syncthreads();
+        }
+
+        // ---- A tiles (strictly lower, row-scaled by beta) to LDS; P tiles to the record
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
             const int task = wave + NW * t;
             if (task >= NLT) continue;
             int ti, tj;
             lt_decode(task, ti, tj);
-            decayed_tile<SL / 16, true, true>(sK, sQ, sK, sB, sTot, LS, SL, ti, tj, accA[t], accP[t]);
-        }
-        __syncthreads();
-    }
-
-    // ---- A tiles (strictly lower, row-scaled by beta) to LDS; P tiles to the record
-    float* gP = grec(P, h, g, R::P);
+            f4 xa = accA[t], xp = accP[t];
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-        const int task = wave + NW * t;
-        if (task >= NLT) continue;
-        int ti, tj;
-        lt_decode(task, ti, tj);
-        f4 xa = accA[t], xp = accP[t];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = ti * 16 + 4 * j + e, s = tj * 16 + i;
-            xa[e] = s < r ? sBeta[r] * xa[e] : 0.f;
-            xp[e] = s <= r ? xp[e] : 0.f;
+            for (int e = 0; e < 4; ++e) {
+                const int r = ti * 16 + 4 * j + e, s = tj * 16 + i;
+                xa[e] = s < r ? sBeta[r] * xa[e] : 0.f;
+                xp[e] = s <= r ? xp[e] : 0.f;
+            }
+            store_tile(sA + lt(ti, tj) * 256, 16, xa);
+            store_tile(gP + ti * 16 * C + tj * 16, C, xp);
         }
-        store_tile(sA + lt(ti, tj) * 256, 16, xa);
-        store_tile(gP + ti * 16 * C + tj * 16, C, xp);
     }
     for (int idx = tid; idx < (NB * NB - NLT) * 256; idx += NTH) {     // P above the diagonal
         int u = idx >> 8;
@@ -308,6 +414,28 @@ __global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
         }
         __syncthreads();
     }
+    if constexpr (FAST) {
+        // the lanes that checked (the last scan segment: wave NW - 1, lanes 32..63)
+        if (wave == NW - 1) {
+            const bool any = __builtin_amdgcn_ballot_w64(strong) != 0;
+            if (lane == 0 && any) P.slow[atomicAdd(P.nslow, 1)] = blk;
+        }
+    }
+}
+
+// One workgroup per (chunk, head): the direct form (listing the chunks that
+// need the general one).
+template <int DK, int DV, int C, bool ABF16, int GATE>
+__global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
+    gprep_body<DK, DV, C, ABF16, GATE, true>(P, blockIdx.x);
+}
+
+// Entry blockIdx.x of the general-form list, if the list is that long (one
+// workgroup per (chunk, head), the list's largest length).
+template <int DK, int DV, int C, bool ABF16, int GATE>
+__global__ __launch_bounds__(kThreads) void gprep_general_kernel(const GParams P) {
+    if (static_cast<int>(blockIdx.x) >= *P.nslow) return;
+    gprep_body<DK, DV, C, ABF16, GATE, false>(P, P.slow[blockIdx.x]);
 }
 
 // ---------------------------------------------------------------------------
@@ -499,6 +627,8 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     p.gmax = pl.gmax;
     p.N = pl.N;
     p.H = pl.H;
+    p.nslow = reinterpret_cast<int32_t*>(ws + pl.off_ctrl) + 1;
+    p.slow = reinterpret_cast<int32_t*>(ws + pl.off_slow);
 
     hipError_t e = launch_chunk_plan(pl, a.cu_seqlens, a.workspace, stream);
     if (e != hipSuccess) return e;
@@ -506,11 +636,12 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
     const unsigned chain_blocks = static_cast<unsigned>((pairs + 7) / 8 * 8 * (DV / 16));
     if (chunk_blocks > 0) {
-        auto k1 = gprep_kernel<DK, DV, C, ABF16, GATE>;
         constexpr int l1 = GPrepB<C>::bytes;
-        if ((e = set_lds(k1, l1)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kThreads), l1, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+        for (auto k1 : {gprep_kernel<DK, DV, C, ABF16, GATE>, gprep_general_kernel<DK, DV, C, ABF16, GATE>}) {
+            if ((e = set_lds(k1, l1)) != hipSuccess) return e;
+            hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kThreads), l1, stream, p);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     if (chain_blocks > 0) {
         auto k2 = gchain_kernel<DK, DV, C>;
