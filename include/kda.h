@@ -32,11 +32,14 @@
  *    launched nothing.  A failed kernel launch returns KDA_ERROR_LAUNCH.
  *    Faults inside a kernel surface at the caller's next synchronisation.
  *  - Data VALUES are not validated.  Preconditions: alpha in [0, 1] (any
- *    value, exact 0 included: the forward and decode kernels form every
- *    decay factor as a product of alpha over a run of tokens, never above 1,
- *    so fast forgetting only underflows toward its exact limit), beta in
- *    [0, 1]; for 16-bit activations every |v| and every state entry stays
- *    below 6.0e4 (half-precision range of the matrix-core operands);
+ *    value, exact 0 included: each (chunk, head) of the chunkwise forward
+ *    runs either a direct form whose rescaled operands are checked to stay
+ *    in range, or a general form in which every decay factor is a product of
+ *    alpha over a run of tokens, never above 1; decode uses products of
+ *    alpha only; so fast forgetting only underflows toward its exact limit),
+ *    beta in [0, 1]; for 16-bit activations every |q|, |k|, |v| and every
+ *    state entry stays below 6.0e4 (half-precision range of the matrix-core
+ *    operands);
  *    cu_seqlens is non-decreasing with cu_seqlens[0] = 0 and
  *    cu_seqlens[N] = T.  kda_chunk_bwd has a narrower gate precondition,
  *    stated at its declaration.
