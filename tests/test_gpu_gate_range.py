@@ -85,6 +85,55 @@ def test_chunk_fwd_alpha_half_everywhere(C, act):
     print(f"  error/allowed: o {r1:.3f}  S_T {r2:.3f}", flush=True)
 
 
+@pytest.mark.parametrize("C", [64, 32, 128])
+@pytest.mark.parametrize("gate", ["alpha", "softplus", "scalar"])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_chunk_fwd_mixed_forms(C, gate, act):
+    """Mild gates everywhere except every third (sequence, chunk, head), which
+    gets strong ones: the preparation kernels take the direct form for some
+    chunks and list the others for the general form within one call."""
+    print(f"[chunk mixed forms C={C} gate={gate} act={act}]", flush=True)
+    B, T, H, D = 2, 640, 3, 128
+    inp = synth.chunk_inputs(B, T, H, D, D, act, mu=-2.0, s0_std=0.05, seed=51, device=DEV)
+    mild = synth.draw_gate(gate, (B, T), H, D, -2.0, 51, DEV)
+    strong = synth.draw_strong_gate(gate, (B, T), H, D, 2.0, 52, DEV)
+    bb = torch.arange(B, device=DEV)[:, None, None]
+    cc = (torch.arange(T, device=DEV) // C)[None, :, None]
+    hh = torch.arange(H, device=DEV)[None, None, :]
+    sel = (bb + cc + hh) % 3 == 0
+    if gate != "scalar":
+        sel = sel[..., None]
+    g = torch.where(sel, strong, mild).contiguous()
+    o, sT = kda.kda_chunk_fwd(inp["q"], inp["k"], inp["v"], g, inp["beta"], initial_state=inp["initial_state"],
+                              final_state=True, out_dtype=torch.float32, gate=gate, chunk_size=C)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_fwd(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]),
+                                  oracle.alpha_from_gate(to_np(g), gate, D), to_np(inp["beta"]),
+                                  initial_state=to_np(inp["initial_state"]))
+    kind = "f32" if act == "f32" else "bf16"
+    r1 = check_close(o, o_ref, kind, what="o")
+    r2 = check_close(sT, s_ref, kind, what="final state")
+    print(f"  error/allowed: o {r1:.3f}  S_T {r2:.3f}", flush=True)
+
+
+def test_chunk_fwd_large_keys_take_the_general_form():
+    """bf16 keys and queries of norm 8 (entries above 2) with mild gates: the
+    C = 64 direct form's operand check sends every chunk to the general form,
+    whose factors never exceed 1; the result still matches the oracle."""
+    print("[chunk large keys]", flush=True)
+    inp = synth.chunk_inputs(2, 300, 2, 128, 128, "bf16", mu=-2.0, s0_std=0.05, seed=61, device=DEV)
+    k = (inp["k"].float() * 8).to(torch.bfloat16)
+    q = (inp["q"].float() * 8).to(torch.bfloat16)
+    o, sT = kda.kda_chunk_fwd(q, k, inp["v"], inp["alpha"], inp["beta"] / 64, initial_state=inp["initial_state"],
+                              final_state=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.kda_fwd(to_np(q), to_np(k), to_np(inp["v"]), to_np(inp["alpha"]), to_np(inp["beta"] / 64),
+                                  initial_state=to_np(inp["initial_state"]))
+    r1 = check_close(o, o_ref, "bf16", what="o")
+    r2 = check_close(sT, s_ref, "bf16", what="final state")
+    print(f"  error/allowed: o {r1:.3f}  S_T {r2:.3f}", flush=True)
+
+
 @pytest.mark.parametrize("gate", ["alpha", "softplus", "scalar"])
 @pytest.mark.parametrize("act,out", [("f32", "f32"), ("bf16", "bf16")])
 def test_decode_strong_decay(gate, act, out):
