@@ -125,16 +125,28 @@ template <> struct Mx<true> {
         for (int e = 0; e < 8; ++e) h[e] = static_cast<E>(x[e]);
         *reinterpret_cast<h8*>(p) = h;
     }
-    // Record stores: non-temporal (the record is read by the next kernel, long after
-    // it has left the caches; measured 2.19 vs 2.21 ms for the 64K-token forward).
-    static __device__ __forceinline__ void gstore8(E* p, const float* x) {
+    // Record stores, non-temporal when `nt` (records too large to stay in the
+    // caches until the next kernel reads them: 2.19 vs 2.21 ms on the 64K-token
+    // forward; records that fit are read back faster when stored normally).
+    static __device__ __forceinline__ void gstore8(E* p, const float* x, bool nt) {
+        if (!nt) {
+            store8(p, x);
+            return;
+        }
         h8 h;
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = static_cast<E>(x[e]);
         __builtin_nontemporal_store(h, reinterpret_cast<h8*>(p));
     }
-    static __device__ __forceinline__ void gstoreV(E* p, const V& v) { __builtin_nontemporal_store(v, reinterpret_cast<V*>(p)); }
-    static __device__ __forceinline__ void gstore4(E* p, f4 x) {
+    static __device__ __forceinline__ void gstoreV(E* p, const V& v, bool nt) {
+        if (nt) __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+        else storeV(p, v);
+    }
+    static __device__ __forceinline__ void gstore4(E* p, f4 x, bool nt) {
+        if (!nt) {
+            store4(p, x);
+            return;
+        }
         h4 h = {static_cast<E>(x[0]), static_cast<E>(x[1]), static_cast<E>(x[2]), static_cast<E>(x[3])};
         __builtin_nontemporal_store(h, reinterpret_cast<h4*>(p));
     }
@@ -189,15 +201,26 @@ template <> struct Mx<false> {
         *reinterpret_cast<f4*>(p) = lo;
         *reinterpret_cast<f4*>(p + 4) = hi;
     }
-    static __device__ __forceinline__ void gstore8(E* p, const float* x) {
+    static __device__ __forceinline__ void gstore8(E* p, const float* x, bool nt) {
+        if (!nt) {
+            store8(p, x);
+            return;
+        }
         __builtin_nontemporal_store(f4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f4*>(p));
         __builtin_nontemporal_store(f4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f4*>(p + 4));
     }
-    static __device__ __forceinline__ void gstoreV(E* p, const V& v) {
+    static __device__ __forceinline__ void gstoreV(E* p, const V& v, bool nt) {
+        if (!nt) {
+            storeV(p, v);
+            return;
+        }
         __builtin_nontemporal_store(f4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f4*>(p));
         __builtin_nontemporal_store(f4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f4*>(p + 4));
     }
-    static __device__ __forceinline__ void gstore4(E* p, f4 x) { __builtin_nontemporal_store(x, reinterpret_cast<f4*>(p)); }
+    static __device__ __forceinline__ void gstore4(E* p, f4 x, bool nt) {
+        if (nt) __builtin_nontemporal_store(x, reinterpret_cast<f4*>(p));
+        else store4(p, x);
+    }
 };
 
 // Eight consecutive activations (16-byte aligned) as fp32.
@@ -344,6 +367,7 @@ struct PrepParams {
     int cps;       // chunks per sequence of a dense batch
     int32_t* nslow;   // length of the general-form list (zeroed by the chunk table)
     int32_t* slow;    // general-form list: g * H + h of each (chunk, head) that takes it
+    bool nt;          // records stored non-temporally (too large to stay in the caches)
 };
 
 template <int a, int b> struct CMax { static constexpr int value = a > b ? a : b; };
@@ -696,7 +720,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
                         kt[e] = kv * (rG * gam[i]);                        // k gamma / Gamma
                     }
                 }
-                M::gstore8(qh + frag_off(I * KS + ks, lane), qv);
+                M::gstore8(qh + frag_off(I * KS + ks, lane), qv, P.nt);
 #pragma unroll
                 for (int Il = 1; Il < 4; ++Il)
                     if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
@@ -894,7 +918,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
                         kt[e] = kv * (sfv * Xb[i]);
                     }
                 }
-                M::gstore8(qh + frag_off(I * KS + ks, lane), qv);
+                M::gstore8(qh + frag_off(I * KS + ks, lane), qv, P.nt);
 #pragma unroll
                 for (int Il = 1; Il < 4; ++Il)
                     if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
@@ -968,7 +992,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
                 pv[e] = s0 <= r ? accP[2 * ks][e] : 0.f;
                 pv[4 + e] = s1 <= r ? accP[2 * ks + 1][e] : 0.f;
             }
-            if (ks == 0 || I >= 2) M::gstore8(pout + frag_off(p_slot(2 * I + ks), lane), pv);
+            if (ks == 0 || I >= 2) M::gstore8(pout + frag_off(p_slot(2 * I + ks), lane), pv, P.nt);
         }
     }
 
@@ -980,7 +1004,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
             const int ts = f & 1;
             // channel 16 (f >> 1) + lane % 16, tokens 32 ts + frag_k(jj, 0..7)
             M::gstoreV(ktt + frag_off(f, id & 63),
-                      M::loadT(s_Kt, KXP, 32 * ts + 4 * jj, 32 * ts + 16 + 4 * jj, 16 * (f >> 1), lm));
+                       M::loadT(s_Kt, KXP, 32 * ts + 4 * jj, 32 * ts + 16 + 4 * jj, 16 * (f >> 1), lm), P.nt);
         }
     }
     __syncthreads();
@@ -1087,7 +1111,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
                 acc1 = M::mma(a1, bT, acc1);
             }
             const float wv[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-            M::gstore8(wout + frag_off(Ib * KS + ksc, lane), wv);
+            M::gstore8(wout + frag_off(Ib * KS + ksc, lane), wv, P.nt);
         }
         // U in the accumulator layout the state kernel consumes directly
         for (int nt = wave; nt < DV / 16; nt += 4) {
@@ -1101,7 +1125,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
                     const V bv = M::loadT(s_v, VXP, t, t + 4, 16 * nt, lm);
                     acc = M::mma(a, bv, acc);
                 }
-                M::gstore4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc);
+                M::gstore4(uout + (static_cast<size_t>(nt * 4 + Ib) * 64 + lane) * 4, acc, P.nt);
             }
         }
     }
@@ -1466,6 +1490,9 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         pp.cps = static_cast<int>((pl.T + C - 1) / C);
         pp.nslow = ctrl + 1;
         pp.slow = reinterpret_cast<int32_t*>(ws + pl.off_slow);
+        // records beyond about half the 256 MB memory-side cache are gone from
+        // the caches before the state pass reads them
+        pp.nt = static_cast<size_t>(pl.gmax) * pl.H * pl.rec_bytes > (size_t(128) << 20);
         constexpr int lds = PrepLds<DK, DV, F16>::bytes;
         auto kfn = a.gate_kind == KDA_GATE_SOFTPLUS_BF16 ? prep_kernel<DK, DV, F16, KDA_GATE_SOFTPLUS_BF16>
                  : a.gate_kind == KDA_GATE_SCALAR        ? prep_kernel<DK, DV, F16, KDA_GATE_SCALAR>
