@@ -172,10 +172,10 @@ def measured_bwd_traffic():
 # profiles/ are written by `python bench.py --summarize KIND ...` from the CSV
 # files of the rocprofv3 runs named in each summary's header.
 # ---------------------------------------------------------------------------
-LIB_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel", "decode_kernel",
+LIB_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel", "state_split_kernel", "decode_kernel",
                "bwd_prep_kernel", "bwd_prep_general_kernel", "bwd_ckpt_kernel", "bwd_ckpt16_kernel",
                "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel", "bwd_grad_general_kernel")
-FWD_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel")
+FWD_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel", "state_split_kernel")
 BWD_KERNELS = ("plan_kernel", "bwd_prep_kernel", "bwd_prep_general_kernel", "bwd_ckpt_kernel",
                "bwd_ckpt16_kernel", "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel",
                "bwd_grad_general_kernel")

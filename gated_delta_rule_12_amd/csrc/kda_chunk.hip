@@ -18,12 +18,17 @@
 //                 Direct form; a (chunk, head) outside its range is listed
 //                 for the next launch.
 //   prep_general_kernel  the same for each listed (chunk, head), general form.
-//   state_kernel  (sequential over the chunks of one sequence, one
+//   state_split_kernel (fp16 records) / state_kernel (fp32 records)
+//                 (sequential over the chunks of one sequence, one
 //                 workgroup per (sequence, head, 16 value columns))
 //                 U' = U - W S,  O = (Gamma.Q) S + P U',
 //                 S <- Diag(gamma) S + ((gamma/Gamma).K)^T U'
 //                 (inter-chunk transition of section 3.1, masked intra-chunk
 //                 output of section 3.2), S kept in registers throughout.
+//
+// Records are stored chunk-major ([chunk][head]): the sequential pass walks
+// the chunks of all heads in step, and with head-major records the heads
+// that share an XCD would sit a multiple of 2 MiB apart, on the same L2 sets.
 //
 // Reading of the garbled passages: Gamma_r is the inclusive per-channel
 // product of alpha over the chunk's first r tokens; W and U are per-token
@@ -501,7 +506,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
         t0 = ent.y;
         len = ent.z;
     }
-    unsigned char* rec = P.rec + (static_cast<size_t>(h) * P.gmax + g) * P.rec_bytes;
+    unsigned char* rec = P.rec + (static_cast<size_t>(g) * P.H + h) * P.rec_bytes;
 
     extern __shared__ __align__(16) unsigned char lds[];
     E* s_C = reinterpret_cast<E*>(lds);                                 // column fragments
@@ -1152,7 +1157,8 @@ __global__ __launch_bounds__(256, 2) void prep_general_kernel(const PrepParams P
 }
 
 // ---------------------------------------------------------------------------
-// state_kernel: the sequential pass over the chunks of one sequence for one
+// state_kernel (fp32 records; fp16 records take state_split_kernel below):
+// the sequential pass over the chunks of one sequence for one
 // head and 16*TW value columns.  Wave w keeps state rows [w*DK/4, (w+1)*DK/4)
 // of those columns in fp32 registers; an operand-type copy of the state
 // slice lives in LDS for the next chunk's products.  Every operand fragment a
@@ -1263,8 +1269,8 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
         seq_t0 = e0.y;
         seq_end = e1.y + e1.z;
     }
-    const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.gmax * P.rec_bytes;
-    const size_t gstride = P.rec_bytes;
+    const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.rec_bytes;
+    const size_t gstride = static_cast<size_t>(H) * P.rec_bytes;
     // output rows of this lane: tokens 16w + 4lg + i of the chunk
     const size_t ostride = static_cast<size_t>(H) * DV;                 // elements per token row
     const size_t ocol = static_cast<size_t>(h) * DV + 16 * jt * TW + lm;
@@ -1466,6 +1472,281 @@ __global__ __launch_bounds__((StateThreads<DK, F16>::value)) void state_kernel(c
 }
 
 
+// ---------------------------------------------------------------------------
+// state_split_kernel (fp16 records): the same sequential pass with the chain
+// and the outputs on separate waves, two per SIMD.  Waves 0-3 carry the chain
+// of each chunk (X = W S, U' = U - X, S <- Diag(gamma) S + K~^T U'), waves 4-7
+// compute the outputs (O = (Gamma.Q) S + P U') beside them: their products
+// and stores fill the matrix cores and the memory path while the chain waits
+// on LDS and barriers.  Wave 8 touches the records two chunks ahead into L2.
+// Per chunk, two barriers: after U' is in LDS, and after the new state is.
+// ---------------------------------------------------------------------------
+constexpr int kSplitThreads = 576;
+
+template <int DK>
+struct ChainStage {
+    static constexpr int KS = DK / 32;
+    static constexpr int TPW = DK / 64;
+    h8 w[KS];        // rows 16c..16c+15 of W
+    h8 k[TPW][2];    // rows of ((gamma/Gamma).K)^T owned by this wave
+    h4 u;            // U: tokens 16c+4lg..+3 of this lane's column
+    float gm;        // gamma of owned state row (lane mod DK/4)
+};
+
+template <int DK>
+struct OutStage {
+    static constexpr int KS = DK / 32;
+    h8 q[KS];        // rows 16o..16o+15 of Gamma.Q
+    h8 p[2];         // row 16o+lm of P, tokens 0..63
+};
+
+template <int DK, int DV, bool OBF16>
+__global__ __launch_bounds__(kSplitThreads) void state_split_kernel(const StateParams P) {
+    using M = Mx<true>;
+    using E = _Float16;
+    using R = Rec<DK, DV, true>;
+    constexpr int D = kStateDepth;
+    constexpr int NTV = DV / 16;          // workgroups per (sequence, head)
+    constexpr int RPW = DK / 4;           // state rows per chain wave
+    constexpr int TPW = RPW / 16;
+    constexpr int KS = DK / 32;
+    constexpr int SP = DK + 8;            // LDS row stride of the state operand
+    constexpr int UP = C + 8;             // LDS row stride of U'
+    static_assert(NTV * 16 == DV, "value tiling");
+    static_assert((RPW & (RPW - 1)) == 0 && RPW <= 64, "a wave's gamma rows fit one word per lane");
+
+    // the NTV workgroups of one (sequence, head) on the same XCD
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7;
+    const int slot = bid >> 3;
+    const int pair = (slot / NTV) * 8 + xcd;
+    const int jt = slot - (slot / NTV) * NTV;
+    const int H = P.H;
+    if (pair >= P.N * H) return;
+    const int n = P.order[pair / H];
+    const int h = pair - (pair / H) * H;
+    const int g0 = P.first[n];
+    const int g1 = P.first[n + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // roles branch per wave
+    const int lm = lane & 15;
+    const int lg = lane >> 4;
+
+    __shared__ __align__(16) E s_S[16 * SP];   // [value column][key row]
+    __shared__ __align__(16) E s_U[16 * UP];   // [value column][token]
+    __shared__ __align__(16) int s_pf[64];      // sink of the prefetch loads
+
+    const size_t sbase = (static_cast<size_t>(n) * H + h) * (DK * DV);
+    const int col = 16 * jt + lm;
+    f4 S[TPW];
+    if (wave < 4) {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = RPW * wave + 16 * t + 4 * lg + i;
+                S[t][i] = P.initial_state ? P.initial_state[sbase + row * DV + col] : 0.f;
+            }
+            M::store4(s_S + lm * SP + RPW * wave + 16 * t + 4 * lg, S[t]);
+        }
+    }
+
+    int seq_t0 = 0, seq_end = 0;
+    if (g0 < g1) {
+        const int4 e0 = P.table[g0];
+        const int4 e1 = P.table[g1 - 1];
+        seq_t0 = e0.y;
+        seq_end = e1.y + e1.z;
+    }
+    const unsigned char* recs = P.rec + static_cast<size_t>(h) * P.rec_bytes;
+    const size_t gstride = static_cast<size_t>(H) * P.rec_bytes;
+    __syncthreads();
+
+    if (wave == 8) {
+        // one word of every 128-byte line, kStatePrefetch chunks ahead; this
+        // workgroup takes every NTV-th line.  Never waited on; the barriers
+        // carry no fence (a fence would wait for these loads to land).
+        const int nlines = static_cast<int>(P.rec_bytes >> kPrefetchShift);
+        auto prefetch = [&](int gp) {
+            const unsigned char* rec = recs + static_cast<size_t>(gp) * gstride;
+            for (int line = jt + NTV * lane; line < nlines; line += NTV * 64)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(rec + (static_cast<size_t>(line) << kPrefetchShift)),
+                    (__attribute__((address_space(3))) void*)s_pf, 4, 0, 0);
+        };
+        for (int gp = g0 + 1; gp < min(g0 + kStatePrefetch, g1); ++gp) prefetch(gp);
+        for (int g = g0; g < g1; ++g) {
+            if (g + kStatePrefetch < g1) prefetch(g + kStatePrefetch);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        return;
+    }
+
+    if (wave < 4) {
+        // ---- chain waves: c = wave owns tokens 16c..16c+15 of X and state rows RPW*c.. ----
+        const int c = wave;
+        using St = ChainStage<DK>;
+        // the chain goes first on a SIMD it shares with an output wave
+        __builtin_amdgcn_s_setprio(2);
+        auto load_a = [&](St& st, int g) {
+            const unsigned char* rec = recs + static_cast<size_t>(g) * gstride;
+            const E* wr = reinterpret_cast<const E*>(rec + R::W);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) st.w[ks] = M::load8(wr + frag_off(c * KS + ks, lane));
+            const E* ut = reinterpret_cast<const E*>(rec + R::UT);
+            st.u = M::load4(ut + (static_cast<size_t>(jt * 4 + c) * 64 + lane) * 4);
+            const float* gam = reinterpret_cast<const float*>(rec + R::GAM);
+            st.gm = gam[RPW * c + (lane & (RPW - 1))];
+        };
+        auto load_b = [&](St& st, int g) {
+            const unsigned char* rec = recs + static_cast<size_t>(g) * gstride;
+            const E* kt = reinterpret_cast<const E*>(rec + R::KTT);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                st.k[t][0] = M::load8(kt + frag_off((TPW * c + t) * 2, lane));
+                st.k[t][1] = M::load8(kt + frag_off((TPW * c + t) * 2 + 1, lane));
+            }
+        };
+        auto step = [&](const St& st, St& nx, int gn) {
+            h8 bS[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const E* sb = s_S + lm * SP + 32 * ks + 4 * lg;
+                bS[ks] = M::load4x2(sb, sb + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(nx, gn);
+            __builtin_amdgcn_sched_barrier(0);
+            f4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) X = M::mma(st.w[ks], bS[ks], X);
+            M::store4(s_U + lm * UP + 16 * c + 4 * lg, M::tof4(st.u) - X);
+            // gamma of state rows 16t + 4lg + i from the lanes that loaded them
+            f4 gmv[TPW];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    gmv[t][i] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * t + 4 * lg + i) << 2, __float_as_int(st.gm)));
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(nx, gn);
+            __builtin_amdgcn_sched_barrier(0);
+            const E* ub = s_U + lm * UP + 4 * lg;
+            const h8 bU0 = M::load4x2(ub, ub + 16);
+            const h8 bU1 = M::load4x2(ub + 32, ub + 48);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc = M::mma(st.k[t][0], bU0, acc);
+                acc = M::mma(st.k[t][1], bU1, acc);
+                S[t] = gmv[t] * S[t] + acc;
+                M::store4(s_S + lm * SP + RPW * c + 16 * t + 4 * lg, S[t]);
+            }
+            __syncthreads();
+        };
+        St st[D];
+        if (g0 < g1) {
+#pragma unroll
+            for (int j = 0; j < D - 1; ++j) {
+                load_a(st[j], min(g0 + j, g1 - 1));
+                load_b(st[j], min(g0 + j, g1 - 1));
+            }
+        }
+        for (int g = g0; g < g1; g += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                if (g + j < g1) step(st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1));
+        }
+        if (P.final_state) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = RPW * c + 16 * t + 4 * lg + i;
+                    P.final_state[sbase + row * DV + col] = S[t][i];
+                }
+        }
+        return;
+    }
+
+    // ---- output waves: o = wave - 4 owns tokens 16o..16o+15 ----
+    const int o = wave - 4;
+    using Os = OutStage<DK>;
+    const size_t ostride = static_cast<size_t>(H) * DV;
+    const size_t ocol = static_cast<size_t>(h) * DV + col;
+    // P2: rows of wave o reach tokens 32..63 of P (o >= 2)
+    auto run = [&](auto p2c) {
+        constexpr bool P2 = decltype(p2c)::value;
+        auto load_a = [&](Os& st, int g) {
+            const E* qr = reinterpret_cast<const E*>(recs + static_cast<size_t>(g) * gstride + R::QH);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) st.q[ks] = M::load8(qr + frag_off(o * KS + ks, lane));
+        };
+        auto load_b = [&](Os& st, int g) {
+            const E* pr = reinterpret_cast<const E*>(recs + static_cast<size_t>(g) * gstride + R::P);
+            st.p[0] = M::load8(pr + frag_off(p_slot(2 * o), lane));
+            if constexpr (P2) st.p[1] = M::load8(pr + frag_off(p_slot(2 * o + 1), lane));
+        };
+        auto step = [&](const Os& st, Os& nx, int gn, int gc) {
+            h8 bS[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const E* sb = s_S + lm * SP + 32 * ks + 4 * lg;
+                bS[ks] = M::load4x2(sb, sb + 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(nx, gn);
+            __builtin_amdgcn_sched_barrier(0);
+            f4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) O = M::mma(st.q[ks], bS[ks], O);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(nx, gn);
+            __builtin_amdgcn_sched_barrier(0);
+            const E* ub = s_U + lm * UP + 4 * lg;
+            const h8 bU0 = M::load4x2(ub, ub + 16);
+            O = M::mma(st.p[0], bU0, O);
+            if constexpr (P2) {
+                const h8 bU1 = M::load4x2(ub + 32, ub + 48);
+                O = M::mma(st.p[1], bU1, O);
+            }
+            const int t0 = seq_t0 + C * (gc - g0);
+            const int len = min(C, seq_end - t0);
+            const size_t obase = (static_cast<size_t>(t0) + 16 * o + 4 * lg) * ostride + ocol;
+            if (len == C) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) store_out<OBF16>(P.o, obase + i * ostride, O[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * o + 4 * lg + i < len) store_out<OBF16>(P.o, obase + i * ostride, O[i]);
+            }
+            __syncthreads();
+        };
+        Os st[D];
+        if (g0 < g1) {
+#pragma unroll
+            for (int j = 0; j < D - 1; ++j) {
+                load_a(st[j], min(g0 + j, g1 - 1));
+                load_b(st[j], min(g0 + j, g1 - 1));
+            }
+        }
+        for (int g = g0; g < g1; g += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j)
+                if (g + j < g1) step(st[j], st[(j + D - 1) % D], min(g + j + D - 1, g1 - 1), g + j);
+        }
+    };
+    if (o >= 2) run(std::true_type{});
+    else run(std::false_type{});
+}
+
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 template <int DK, int DV, bool F16, bool OBF16>
@@ -1521,8 +1802,12 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
     sp.H = pl.H;
     const int64_t pairs = static_cast<int64_t>(pl.N) * pl.H;
     const int64_t blocks = (pairs + 7) / 8 * 8 * (DV / (16 * kStateTiles));
-    hipLaunchKernelGGL((state_kernel<DK, DV, F16, OBF16>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(StateThreads<DK, F16>::value), 0, stream, sp);
+    if constexpr (F16)
+        hipLaunchKernelGGL((state_split_kernel<DK, DV, OBF16>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(kSplitThreads), 0, stream, sp);
+    else
+        hipLaunchKernelGGL((state_kernel<DK, DV, F16, OBF16>), dim3(static_cast<unsigned>(blocks)),
+                           dim3(StateThreads<DK, F16>::value), 0, stream, sp);
     return hipGetLastError();
 }
 
