@@ -253,7 +253,8 @@ def summarize(kind, inputs, title, commands):
     """Print a profiles/ summary.  kind:
       trace    inputs = [kernel_stats.csv glob]
       traffic  inputs = [FETCH_SIZE csv glob, WRITE_SIZE csv glob, copy FETCH_SIZE glob, copy WRITE_SIZE glob]
-      mfma     inputs = [MfmaUtil csv glob, MOPS csv glob]"""
+      mfma     inputs = [MfmaUtil csv glob, MOPS csv glob]
+      counters inputs = [counter csv glob, ...]: the mean per dispatch of every counter found"""
     print(f"# {title}")
     for c in commands:
         print(f"# {c}")
@@ -312,6 +313,23 @@ def summarize(kind, inputs, title, commands):
         for k in sorted(util):
             g = [mops[c].get(k, 0.0) * 512 / 1e9 for c in mops]
             print(f"  {k:48s} {util[k]:10.2f} {g[0]:10.1f} {g[1]:10.1f} {g[2]:10.1f}")
+    elif kind == "counters":
+        names = []
+        for pattern in inputs:
+            for r in _csv_rows(pattern):
+                if r["Counter_Name"] not in names:
+                    names.append(r["Counter_Name"])
+        means = {}
+        for c in names:
+            for pattern in inputs:
+                for k, v in _counter_means(pattern, c).items():
+                    means.setdefault(k, {})[c] = v
+        print(f"# forward/decode sources sha256: {fwd_sha}")
+        print(f"# backward sources sha256: {bwd_sha}")
+        print("# mean per dispatch, in millions")
+        print(f"# {'kernel':48s} " + " ".join(f"{c:>28s}" for c in names))
+        for k in sorted(means):
+            print(f"  {k:48s} " + " ".join(f"{means[k].get(c, 0.0) / 1e6:28.3f}" for c in names))
     else:
         raise SystemExit(f"bench.py --summarize: unknown kind {kind}")
 
@@ -421,7 +439,7 @@ def main():
     ap.add_argument("--only", choices=["fwd", "decode", "bwd"], default=None)
     ap.add_argument("--cpu-sample-tokens", type=int, default=65536)
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--summarize", choices=["trace", "traffic", "mfma"], default=None,
+    ap.add_argument("--summarize", choices=["trace", "traffic", "mfma", "counters"], default=None,
                     help="print a profiles/ summary from rocprofv3 CSV files (globs given by --inputs)")
     ap.add_argument("--inputs", nargs="*", default=[])
     ap.add_argument("--title", default="")

@@ -59,3 +59,63 @@ def test_more_than_one_gpu_exits_with_a_message(argv, env):
     assert r.returncode != 0
     assert "exactly one GPU" in r.stderr
     assert r.stdout == ""
+
+
+# ---------------------------------------------------------------------------
+# The profiles/ summaries: bench.py --summarize on small rocprofv3-shaped CSVs
+# ---------------------------------------------------------------------------
+PREP = "void kda::(anonymous namespace)::prep_kernel<128, 128, true, 0>(kda::(anonymous namespace)::PrepParams)"
+STATE = ("void kda::(anonymous namespace)::state_split_kernel<128, 128, true>"
+         "(kda::(anonymous namespace)::StateParams)")
+OTHER = "void at::native::elementwise_kernel<128, 4>(int)"
+COPY = "void bench_copy_kernel(float const*, float*)"
+
+
+def _write_csv(path, header, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+    return str(path)
+
+
+def test_trace_summary_keeps_library_kernels_and_sums_the_forward(tmp_path, capsys):
+    p = _write_csv(tmp_path / "run_kernel_stats.csv",
+                   ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+                   [[PREP, 4, 4_400_000, 1_100_000, 50, 1_000_000, 1_200_000, 0],
+                    [STATE, 4, 4_000_000, 1_000_000, 40, 990_000, 1_010_000, 0],
+                    [OTHER, 9, 900_000, 100_000, 10, 1, 2, 0]])
+    bench.summarize("trace", [p], "t", ["cmd"])
+    out = capsys.readouterr().out
+    assert "prep_kernel<128, 128, true, 0>" in out and "state_split_kernel<128, 128, true>" in out
+    assert "elementwise" not in out
+    assert "forward kernels, sum of averages: 2100.00 us" in out
+
+
+def test_traffic_summary_scales_by_the_copy(tmp_path, capsys):
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    f = _write_csv(tmp_path / "f.csv", hdr, [[PREP, "FETCH_SIZE", 1000], [PREP, "FETCH_SIZE", 3000]])
+    w = _write_csv(tmp_path / "w.csv", hdr, [[PREP, "WRITE_SIZE", 500]])
+    # the 1 GiB copy reads as 0.5 GiB of FETCH_SIZE and 1 GiB of WRITE_SIZE
+    cf = _write_csv(tmp_path / "cf.csv", hdr, [[COPY, "FETCH_SIZE", (1 << 30) / 2 / 1024]])
+    cw = _write_csv(tmp_path / "cw.csv", hdr, [[COPY, "WRITE_SIZE", (1 << 30) / 1024]])
+    bench.summarize("traffic", [f, w, cf, cw], "t", [])
+    out = capsys.readouterr().out
+    assert "fetch_scale: 2.000000" in out and "write_scale: 1.000000" in out
+    # mean FETCH_SIZE 2000 KiB x 2, WRITE_SIZE 500 KiB x 1
+    assert f"read_bytes {2000 * 1024 * 2} write_bytes {500 * 1024}" in out
+    assert f"fwd_traffic_bytes: {2000 * 1024 * 2 + 500 * 1024}" in out
+
+
+def test_counters_summary_lists_every_counter(tmp_path, capsys):
+    hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    a = _write_csv(tmp_path / "a.csv", hdr, [[STATE, "TCC_HIT_sum", 130e6], [STATE, "TCC_HIT_sum", 132e6],
+                                             [STATE, "TCC_MISS_sum", 22e6], [OTHER, "TCC_MISS_sum", 5e6]])
+    b = _write_csv(tmp_path / "b.csv", hdr, [[STATE, "TCP_TCC_READ_REQ_sum", 137e6]])
+    bench.summarize("counters", [a, b], "t", [])
+    out = capsys.readouterr().out
+    row = [l for l in out.splitlines() if l.strip().startswith("state_split_kernel")]
+    assert len(row) == 1
+    assert row[0].split()[-3:] == ["131.000", "22.000", "137.000"]
+    assert "elementwise" not in out
