@@ -256,6 +256,10 @@ template <> struct Load8<false> {
 // same product as long as both operands of an MFMA use it; this one lets a
 // 16x16 accumulator tile pair (rows 4j..4j+3 of each tile in lane (m, j))
 // be written as a fragment without moving data between lanes.
+// With 16-bit records, Gamma.Q is the exception: it is written from the
+// preparation pass's registers, whose lanes hold eight consecutive channels
+// (8j..8j+7, the matrix core's own order), so its reader takes the state
+// operand in that order.
 
 __device__ __forceinline__ size_t frag_off(int f, int lane) { return (static_cast<size_t>(f) * 64 + lane) * 8; }
 
@@ -533,8 +537,14 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
     const A* __restrict__ v = static_cast<const A*>(P.v);
     auto row_v = [&](int rr) { return (static_cast<size_t>(t0 + rr) * H + h) * DV; };
 
-    // Lane (lm, lg) owns token r and, in reduction step ks, the channels
-    // 32ks + frag_k(lg, e): two runs of four, at 32ks + 4lg and 32ks + 16 + 4lg.
+    // Lane (lm, lg) owns token r and, in reduction step ks, eight channels:
+    // with 16-bit activations the run 32ks + 8lg .. + 7, read as one 16-byte
+    // word per tensor (8-byte reads of two runs of four made each load touch
+    // 16 rows for 32 bytes each: 1.12 vs 1.00 ms on the 64K-token forward);
+    // with fp32 activations two runs of four, at 32ks + 4lg and 32ks + 16 + 4lg
+    // (frag_k).  Every operand built here uses the same channels, so the
+    // products agree; the Gamma.Q record carries this order to the state pass.
+    auto chan_h = [&](int ks, int half) { return F16 ? 32 * ks + 8 * lg + 4 * half : 32 * ks + frag_k(lg, 4 * half); };
 
     // ---- (0) global loads of alpha, k, q, beta (v follows in (b)) ---------------
     // Rows past the chunk's end re-read its last row (always in bounds) and
@@ -555,13 +565,24 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
-                const int c = 32 * ks + 16 * half + 4 * lg;
+                const int c = chan_h(ks, half);
                 if constexpr (GATE == KDA_GATE_ALPHA)
                     graw[ks][half] = *reinterpret_cast<const f4*>(static_cast<const float*>(P.gate) + rowk + c);
-                else if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16)
-                    graw[ks][half] = Raw4<true>::load(static_cast<const uint16_t*>(P.gate) + rowk + c);
-                kraw[ks][half] = R4::load(k + rowk + c);
-                qraw[ks][half] = R4::load(q + rowk + c);
+                if constexpr (F16) {
+                    // both runs of four in one 16-byte read
+                    if (half == 1) continue;
+                    auto split = [](uint4 w, uint2& lo, uint2& hi) { lo = uint2{w.x, w.y}; hi = uint2{w.z, w.w}; };
+                    if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16)
+                        split(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(P.gate) + rowk + c),
+                              graw[ks][0], graw[ks][1]);
+                    split(*reinterpret_cast<const uint4*>(k + rowk + c), kraw[ks][0], kraw[ks][1]);
+                    split(*reinterpret_cast<const uint4*>(q + rowk + c), qraw[ks][0], qraw[ks][1]);
+                } else {
+                    if constexpr (GATE == KDA_GATE_SOFTPLUS_BF16)
+                        graw[ks][half] = Raw4<true>::load(static_cast<const uint16_t*>(P.gate) + rowk + c);
+                    kraw[ks][half] = R4::load(k + rowk + c);
+                    qraw[ks][half] = R4::load(q + rowk + c);
+                }
             }
         if constexpr (GATE == KDA_GATE_SCALAR) gscalar = static_cast<const float*>(P.gate)[rowt];
     }
@@ -583,7 +604,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
     if constexpr (FAST) {
         float* s_tot = s_AT;                                            // [4][DK], until (c)
         float* s_fac = s_AT + 4 * DK;                                   // [16][DK], until (c)
-        auto chan = [&](int ks, int e) { return 32 * ks + frag_k(lg, e); };
+        auto chan = [&](int ks, int e) { return chan_h(ks, e >> 2) + (e & 3); };
         float b[KS][8];
         // ---- (a) b = inclusive cumsum of log2(alpha) over the chunk's tokens -----
         // scan over the 16 tokens of this wave's block (lanes of one 16-lane row),
@@ -635,7 +656,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) b[ks][e] = fexp2(b[ks][e]);
         if (lm == 7 || lm == 15) {
-            float* d0 = s_fac + ((lm == 7 ? 0 : 8) + I) * DK + 4 * lg;
+            float* d0 = s_fac + ((lm == 7 ? 0 : 8) + I) * DK;
             float* d1 = d0 + 4 * DK;
             auto rcp4 = [&](int ks, int o) {
                 return f4{__builtin_amdgcn_rcpf(b[ks][o]), __builtin_amdgcn_rcpf(b[ks][o + 1]),
@@ -643,10 +664,10 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
             };
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
-                *reinterpret_cast<f4*>(d0 + 32 * ks) = f4{b[ks][0], b[ks][1], b[ks][2], b[ks][3]};
-                *reinterpret_cast<f4*>(d0 + 32 * ks + 16) = f4{b[ks][4], b[ks][5], b[ks][6], b[ks][7]};
-                *reinterpret_cast<f4*>(d1 + 32 * ks) = rcp4(ks, 0);
-                *reinterpret_cast<f4*>(d1 + 32 * ks + 16) = rcp4(ks, 4);
+                *reinterpret_cast<f4*>(d0 + chan_h(ks, 0)) = f4{b[ks][0], b[ks][1], b[ks][2], b[ks][3]};
+                *reinterpret_cast<f4*>(d0 + chan_h(ks, 1)) = f4{b[ks][4], b[ks][5], b[ks][6], b[ks][7]};
+                *reinterpret_cast<f4*>(d1 + chan_h(ks, 0)) = rcp4(ks, 0);
+                *reinterpret_cast<f4*>(d1 + chan_h(ks, 1)) = rcp4(ks, 4);
             }
         }
         // (cleared here, once the loads above have landed: a store at the
@@ -691,7 +712,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
             constexpr int I = decltype(ic)::value;
             E* __restrict__ qh = reinterpret_cast<E*>(rec + R::QH);
             auto fac4 = [&](int row, int ks, int half) {
-                return *reinterpret_cast<const f4*>(s_fac + row * DK + 32 * ks + 16 * half + 4 * lg);
+                return *reinterpret_cast<const f4*>(s_fac + row * DK + chan_h(ks, half));
             };
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
@@ -729,11 +750,11 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
 #pragma unroll
                 for (int Il = 1; Il < 4; ++Il)
                     if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
-                const int c0 = 32 * ks + 4 * lg;
+                const int c0 = chan_h(ks, 0), c1 = chan_h(ks, 1);
                 M::store4(s_khat + r * KXP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
-                M::store4(s_khat + r * KXP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
+                M::store4(s_khat + r * KXP + c1, f4{kh[4], kh[5], kh[6], kh[7]});
                 M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
-                M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
+                M::store4(s_Kt + r * KXP + c1, f4{kt[4], kt[5], kt[6], kt[7]});
             }
             };
         switch (I) {
@@ -864,7 +885,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int half = 0; half < 2; ++half)
-                    *reinterpret_cast<f4*>(s_F + I * DK + 32 * ks + 16 * half + 4 * lg) =
+                    *reinterpret_cast<f4*>(s_F + I * DK + chan_h(ks, half)) =
                         f4{PF(ks, 4 * half), PF(ks, 4 * half + 1), PF(ks, 4 * half + 2), PF(ks, 4 * half + 3)};
         }
         __syncthreads();
@@ -897,7 +918,7 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
                     f4 Fb[4];
 #pragma unroll
                     for (int K = 0; K < 4; ++K)
-                        if (K != I) Fb[K] = *reinterpret_cast<const f4*>(s_F + K * DK + 32 * ks + 16 * half + 4 * lg);
+                        if (K != I) Fb[K] = *reinterpret_cast<const f4*>(s_F + K * DK + chan_h(ks, half));
                     f4 Eb = {1.f, 1.f, 1.f, 1.f}, Xb = {1.f, 1.f, 1.f, 1.f};
 #pragma unroll
                     for (int K = 0; K < I; ++K) Eb = Eb * Fb[K];
@@ -927,11 +948,11 @@ __device__ __forceinline__ void prep_body(const PrepParams& P, const int blk) {
 #pragma unroll
                 for (int Il = 1; Il < 4; ++Il)
                     if (Il > I) M::store8(s_C + frag_off(pair_index(Il, I) * KS + ks, lane), cl[Il - 1]);
-                const int c0 = 32 * ks + 4 * lg;
+                const int c0 = chan_h(ks, 0), c1 = chan_h(ks, 1);
                 M::store4(s_khat + r * KXP + c0, f4{kh[0], kh[1], kh[2], kh[3]});
-                M::store4(s_khat + r * KXP + c0 + 16, f4{kh[4], kh[5], kh[6], kh[7]});
+                M::store4(s_khat + r * KXP + c1, f4{kh[4], kh[5], kh[6], kh[7]});
                 M::store4(s_Kt + r * KXP + c0, f4{kt[0], kt[1], kt[2], kt[3]});
-                M::store4(s_Kt + r * KXP + c0 + 16, f4{kt[4], kt[5], kt[6], kt[7]});
+                M::store4(s_Kt + r * KXP + c1, f4{kt[4], kt[5], kt[6], kt[7]});
             }
             };
         switch (I) {
@@ -1697,12 +1718,11 @@ __global__ __launch_bounds__(PF ? kSplitThreads : kSplitThreads - 64, PF ? 1 : 2
             if constexpr (P2) st.p[1] = M::load8(pr + frag_off(p_slot(2 * o + 1), lane));
         };
         auto step = [&](const Os& st, Os& nx, int gn, int gc) {
+            // Gamma.Q comes in the preparation pass's channel order (eight
+            // consecutive channels per lane group), W in two runs of four
             h8 bS[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const E* sb = s_S + lm * SP + 32 * ks + 4 * lg;
-                bS[ks] = M::load4x2(sb, sb + 16);
-            }
+            for (int ks = 0; ks < KS; ++ks) bS[ks] = M::load8(s_S + lm * SP + 32 * ks + 8 * lg);
             __builtin_amdgcn_sched_barrier(0);
             load_a(nx, gn);
             __builtin_amdgcn_sched_barrier(0);
