@@ -193,11 +193,71 @@ template <int DK, int DV> struct PrepB {
     static constexpr int bytes = (2 * C * LK + C * LM + 2 * C * LC + 2 * C + (C / 16) * DK) * 4;
 };
 
-// FAST: the direct form, which checks the chunk's decay and, when any channel
-// decays below 2^-64, flags the (chunk, head) and appends it to the general
-// list; otherwise the general form.
-template <int DK, int DV, bool ABF16, int GATE, bool FAST>
-__device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const int g) {
+// T = (I + A)^-1 (A strictly lower, fp32 [C][LC] in sA) into sT by 16 x 16
+// blocks: each of waves 0..3 inverts one diagonal block by substitution (16
+// lanes, one column each), then T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj for
+// i - j = 1, 2, 3.  sX: one 16 x 16 fp32 tile of scratch per wave.  The
+// caller's writes before the call are ordered by its first barrier; it ends
+// with a barrier.
+__device__ __forceinline__ void solve_t(const float* sA, float* sT, float* sX) {
+    const int wave = wave_id(), lane = lane_id();
+    // Column-oriented: once t[s] is final, every later row takes its term at
+    // once (the same operations, in the same order per row, as row by row,
+    // but a chain of 16 steps instead of 120).  Column s of the block is read
+    // while column s - 1 is applied (not all 120 values first: that needs
+    // more registers than two workgroups per CU leave).
+    if (wave < 4 && lane < 16) {
+        const int col = lane, o = 16 * wave;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = r == col ? 1.f : 0.f;
+        float cur[16], nxt[16];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) cur[r] = sA[(o + r) * LC + o];
+#pragma unroll
+        for (int s2 = 0; s2 < 15; ++s2) {
+            if (s2 + 1 < 15) {
+#pragma unroll
+                for (int r = s2 + 2; r < 16; ++r) nxt[r] = sA[(o + r) * LC + o + s2 + 1];
+            }
+#pragma unroll
+            for (int r = s2 + 1; r < 16; ++r) t[r] -= cur[r] * t[s2];
+#pragma unroll
+            for (int r = s2 + 2; r < 16; ++r) cur[r] = nxt[r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(o + r) * LC + o + col] = t[r];
+    }
+    for (int idx = threadIdx.x; idx < 6 * 256; idx += kPrepThreads) {      // blocks above the diagonal
+        const int blk = idx >> 8, e = idx & 255;
+        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
+        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
+        sT[(mb * 16 + (e >> 4)) * LC + nb * 16 + (e & 15)] = 0.f;
+    }
+    __syncthreads();
+    for (int d = 1; d < 4; ++d) {
+        if (wave < 4 - d) {
+            const int bi = wave + d, bj = wave;
+            f4 x = zero4();
+            for (int bk = bj; bk < bi; ++bk)
+                x = mm<16, true, false>(sA + 16 * bi * LC + 16 * bk, LC, 1, sT + 16 * bk * LC + 16 * bj, LC, 1, x);
+            store_tile(sX + wave * 256, 16, x);
+        }
+        __syncthreads();
+        if (wave < 4 - d) {
+            const int bi = wave + d, bj = wave;
+            const f4 y = mm<16, true, false>(sT + 16 * bi * LC + 16 * bi, LC, 1, sX + wave * 256, 16, 1, zero4());
+            store_tile(sT + 16 * bi * LC + 16 * bj, LC, -y);
+        }
+        __syncthreads();
+    }
+}
+
+// The general form for one listed (chunk, head): every decay factor formed
+// from exponents <= 0, for any gate in [0, 1].  Channels are staged whole
+// (137 KB of LDS: one workgroup per CU); it only runs on the listed chunks.
+template <int DK, int DV, bool ABF16, int GATE>
+__device__ __forceinline__ void prep_general_body(const BwdParams& P, const int h, const int g) {
     using R = BRec<DK, DV, ABF16>;
     constexpr int NTH = kPrepThreads, NW = kPrepWaves;
     constexpr int LK = PrepB<DK, DV>::LK, LV = PrepB<DK, DV>::LV;
@@ -246,168 +306,65 @@ __device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const
     // the ten below or on the diagonal spread so the waves sharing a SIMD
     // (w, w + 4) hold 3, 3, 2, 2 of them; the six above are only zeroed.
     constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x1101, 0x2102, 0x2203, 0x3112, 0x3213, 0x3323};
-    [[maybe_unused]] float* sGam = sTot; // direct form: gamma = 2^b_last per channel [DK], kept to the end
-    if constexpr (FAST) {
-        // b = cumsum(log2 alpha) per channel over the chunk;
-        // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, Kt = 2^(b_last - b) K
-        gate_cumsum<DK, NTH, GATE>(sKb, LK, sGs, len, sA, [&](int r, int c, float b) {
-            const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
-            const float kv = sKh[r * LK + c];
-            sKh[r * LK + c] = G * kv;
-            sKb[r * LK + c] = Gi * kv;
-            sQ[r * LK + c] *= G;
-            if (r == C - 1) sGam[c] = G;
-        });
-        __syncthreads();
-        // A (chunk, head) outside the direct form's range is flagged and
-        // listed at the end (gamma stays in sGam), and the general kernel
-        // writes its whole record again; this workgroup still runs to the end
-        // (its addressing does not depend on the values).
-        if (tid < DK) gGam[tid] = sGam[tid];
-        if constexpr (!ABF16) {          // the 16-bit passes read Kt as fp16 fragments only
-            for (int idx = tid; idx < C * DK; idx += NTH) {
-                const int r = idx / DK, c = idx % DK;
-                gKt[r * DK + c] = sGam[c] * sKb[r * LK + c];
-            }
-        }
-        store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
-        if constexpr (ABF16) {
-            // fp16 fragments for the 16-bit state passes: Kt, Kt^T and Qh^T
-            auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
-            write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sGam[k] * sKb[m * LK + k]; });
-            write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sGam[m] * sKb[k * LK + m]; });
-            write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
-        }
+    // b per 16-token tile (sKb) and the tile totals; the tiles of A and P
+    // from the raw K and Q with every decay factor <= 1 (decayed_tile)
+    tile_gate_scan<DK, NTH, C, GATE>(sKb, LK, sGs, len, sTot, sA);
 #pragma unroll
-        for (int slot = 0; slot < 2; ++slot) {
-            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
-            const int mb = tt >> 4, nb = tt & 15;
-            f4 a = zero4(), pp = zero4();
-            if (nb <= mb)
-                mm_two<DK / 16, true, true>(sKh + mb * 16 * LK, sQ + mb * 16 * LK, LK, 1, sKb + nb * 16 * LK, 1, LK, a, pp);
+    for (int slot = 0; slot < 2; ++slot) {
+        const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
+        const int mb = tt >> 4, nb = tt & 15;
+        f4 a = zero4(), pp = zero4();
+        decayed_tile<DK / 16, true, true, ABF16>(sKh, sQ, sKh, sKb, sTot, LK, DK, mb, nb, a, pp);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
-                a[e] = s2 < r ? sBeta[r] * a[e] : 0.f;
-                pp[e] = s2 <= r ? pp[e] : 0.f;
-            }
-            store_tile(sA + mb * 16 * LC + nb * 16, LC, a);
-            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
-            else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
+        for (int e = 0; e < 4; ++e) {
+            const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+            a[e] = s2 < r ? sBeta[r] * a[e] : 0.f;
+            pp[e] = s2 <= r ? pp[e] : 0.f;
         }
-        __syncthreads();
-        if constexpr (ABF16) {
-            auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
-            write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
-            __syncthreads();
-        }
-    } else {
-        // b per 16-token tile (sKb) and the tile totals; the tiles of A and P
-        // from the raw K and Q with every decay factor <= 1 (decayed_tile)
-        tile_gate_scan<DK, NTH, C, GATE>(sKb, LK, sGs, len, sTot, sA);
-#pragma unroll
-        for (int slot = 0; slot < 2; ++slot) {
-            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
-            const int mb = tt >> 4, nb = tt & 15;
-            f4 a = zero4(), pp = zero4();
-            decayed_tile<DK / 16, true, true, ABF16>(sKh, sQ, sKh, sKb, sTot, LK, DK, mb, nb, a, pp);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
-                a[e] = s2 < r ? sBeta[r] * a[e] : 0.f;
-                pp[e] = s2 <= r ? pp[e] : 0.f;
-            }
-            store_tile(sA + mb * 16 * LC + nb * 16, LC, a);
-            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
-            else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
-        }
-        __syncthreads();
-        // Kh = Gamma.K, Qh = Gamma.Q and Kt = (gamma / Gamma).K (into sKb), every
-        // factor 2^x with x <= 0: with pre / suf the totals of the tiles
-        // before / after the row's tile t,  log2 Gamma = pre + b,
-        // log2(gamma / Gamma) = T_t - b + suf.
+        store_tile(sA + mb * 16 * LC + nb * 16, LC, a);
+        if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
+        else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
+    }
+    __syncthreads();
+    // Kh = Gamma.K, Qh = Gamma.Q and Kt = (gamma / Gamma).K (into sKb), every
+    // factor 2^x with x <= 0: with pre / suf the totals of the tiles
+    // before / after the row's tile t,  log2 Gamma = pre + b,
+    // log2(gamma / Gamma) = T_t - b + suf.
+    for (int idx = tid; idx < C * DK; idx += NTH) {
+        const int r = idx / DK, c = idx % DK, t = r / 16;
+        const float bl = sKb[r * LK + c];
+        const float pre = tot1(sTot, DK, c, 0, t), suf = tot1(sTot, DK, c, t + 1, NBLK);
+        const float G = __builtin_amdgcn_exp2f(pre + bl);
+        const float kv = sKh[r * LK + c];
+        sKh[r * LK + c] = G * kv;
+        sQ[r * LK + c] *= G;
+        sKb[r * LK + c] = kv * __builtin_amdgcn_exp2f(sTot[t * DK + c] - bl + suf);
+    }
+    if (tid < DK) gGam[tid] = __builtin_amdgcn_exp2f(tot1(sTot, DK, tid, 0, NBLK));
+    __syncthreads();
+    if constexpr (!ABF16) {
         for (int idx = tid; idx < C * DK; idx += NTH) {
-            const int r = idx / DK, c = idx % DK, t = r / 16;
-            const float bl = sKb[r * LK + c];
-            const float pre = tot1(sTot, DK, c, 0, t), suf = tot1(sTot, DK, c, t + 1, NBLK);
-            const float G = __builtin_amdgcn_exp2f(pre + bl);
-            const float kv = sKh[r * LK + c];
-            sKh[r * LK + c] = G * kv;
-            sQ[r * LK + c] *= G;
-            sKb[r * LK + c] = kv * __builtin_amdgcn_exp2f(sTot[t * DK + c] - bl + suf);
+            const int r = idx / DK, c = idx % DK;
+            gKt[r * DK + c] = sKb[r * LK + c];
         }
-        if (tid < DK) gGam[tid] = __builtin_amdgcn_exp2f(tot1(sTot, DK, tid, 0, NBLK));
+    }
+    store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
+    if constexpr (ABF16) {
+        // fp16 fragments for the 16-bit state passes: Kt, Kt^T, Qh^T and P^T
+        auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+        write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sKb[m * LK + k]; });
+        write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sKb[k * LK + m]; });
+        write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
+        write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
         __syncthreads();
-        if constexpr (!ABF16) {
-            for (int idx = tid; idx < C * DK; idx += NTH) {
-                const int r = idx / DK, c = idx % DK;
-                gKt[r * DK + c] = sKb[r * LK + c];
-            }
-        }
-        store_block<NTH>(rec_at(P, h, g, R::QH), DK, sQ, LK, C, DK);
-        if constexpr (ABF16) {
-            // fp16 fragments for the 16-bit state passes: Kt, Kt^T, Qh^T and P^T
-            auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
-            write_afrags<C, DK, NTH>(hrec(R::FKT), [&](int m, int k) { return sKb[m * LK + k]; });
-            write_afrags<DK, C, NTH>(hrec(R::FKTT), [&](int m, int k) { return sKb[k * LK + m]; });
-            write_afrags<DK, C, NTH>(hrec(R::FQHT), [&](int m, int k) { return sQ[k * LK + m]; });
-            write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
-            __syncthreads();
-        }
     }
 
-    // T = (I + A)^-1 (A strictly lower) by 16 x 16 blocks: each wave inverts
-    // one diagonal block by substitution (16 lanes, one column each), then
-    // T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj for i - j = 1, 2, 3.
-    float* sX = sKb;                     // scratch: one 16 x 16 tile per wave
-    // Column-oriented: once t[s] is final, every later row takes its term at
-    // once (the same operations, in the same order per row, as row by row,
-    // but a chain of 16 steps instead of 120).
-    if (wave < 4 && lane < 16) {
-        const int col = lane, o = 16 * wave;
-        float a[120];                    // the block's strict lower triangle, all reads issued first
-#pragma unroll
-        for (int r = 1, q = 0; r < 16; ++r)
-#pragma unroll
-            for (int s2 = 0; s2 < r; ++s2, ++q) a[q] = sA[(o + r) * LC + o + s2];
-        float t[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t[r] = r == col ? 1.f : 0.f;
-#pragma unroll
-        for (int s2 = 0; s2 < 15; ++s2)
-#pragma unroll
-            for (int r = s2 + 1; r < 16; ++r) t[r] -= a[r * (r - 1) / 2 + s2] * t[s2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(o + r) * LC + o + col] = t[r];
-    }
-    for (int idx = tid; idx < 6 * 256; idx += NTH) {      // blocks above the diagonal
-        const int blk = idx >> 8, e = idx & 255;
-        const int mb = blk < 3 ? 0 : blk < 5 ? 1 : 2;
-        const int nb = blk < 3 ? blk + 1 : blk < 5 ? blk - 1 : 3;
-        sT[(mb * 16 + (e >> 4)) * LC + nb * 16 + (e & 15)] = 0.f;
-    }
-    // Y = Diag(beta) Kh (in place)
+    // Y = Diag(beta) Kh (in place), then T = (I + A)^-1 with sKb as scratch
     for (int idx = tid; idx < C * DK; idx += NTH) {
         const int r = idx / DK, c = idx % DK;
         sKh[r * LK + c] *= sBeta[r];
     }
-    __syncthreads();
-    for (int d = 1; d < 4; ++d) {
-        if (wave < 4 - d) {
-            const int bi = wave + d, bj = wave;
-            f4 x = zero4();
-            for (int bk = bj; bk < bi; ++bk)
-                x = mm<16, true, false>(sA + 16 * bi * LC + 16 * bk, LC, 1, sT + 16 * bk * LC + 16 * bj, LC, 1, x);
-            store_tile(sX + wave * 256, 16, x);
-        }
-        __syncthreads();
-        if (wave < 4 - d) {
-            const int bi = wave + d, bj = wave;
-            const f4 y = mm<16, true, false>(sT + 16 * bi * LC + 16 * bi, LC, 1, sX + wave * 256, 16, 1, zero4());
-            store_tile(sT + 16 * bi * LC + 16 * bj, LC, -y);
-        }
-        __syncthreads();
-    }
+    solve_t(sA, sT, sKb);
     store_block<NTH>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
     tv.put_scaled(sQ, LV, sBeta);        // Z = Diag(beta) V
     __syncthreads();
@@ -440,27 +397,234 @@ __device__ __forceinline__ void prep_body(const BwdParams& P, const int h, const
         write_afrags<C, DK, NTH>(hrec(R::FW), [&](int m, int k) { return sKb[m * LK + k]; });
         write_afrags<DK, C, NTH>(hrec(R::FWT), [&](int m, int k) { return sKb[k * LK + m]; });
     }
-    if constexpr (FAST) {
-        if (wave == 0) {                 // gamma (sGam) is left untouched since the scan
-            bool bad = false;
+}
+
+// The direct form, channels 64 at a time.  Every channel's chunk decay is
+// assumed within 2^-64 (Gamma and 1/Gamma as fp32 factors); the chunk is
+// checked at the end and, when some channel decays further, flagged and
+// appended to the general list (its values here are then never used).  The
+// key channels are staged in slices of KSL, so the LDS holds four 64 x 68
+// fp32 tiles (73 KB: two workgroups per CU): A and P accumulate in the
+// waves' registers over the slices; after T, each slice's Diag(beta).Gamma.K
+// is formed again from k and the gate (the same scan, so the same values)
+// for W = T Diag(beta) Gamma.K, beside U = T Diag(beta) V for one value slice.
+constexpr int KSL = 64, LH = KSL + 4;
+static_assert(LH == LC, "the slice tiles and the C x C tiles share one row stride");
+
+template <int DK> struct PrepDirB {
+    static constexpr int bytes = (4 * C * LH + 2 * C + DK + kPrepThreads) * 4;
+};
+
+// write_afrags restricted to row blocks [mb0, mb0 + NMB) and reduction
+// blocks [kb0, kb0 + NKS) of an M x K matrix (same fragment layout)
+template <int M, int K, int NMB, int NKS, int NTH, typename F>
+__device__ __forceinline__ void write_afrags_part(_Float16* dst, int mb0, int kb0, F elem) {
+    constexpr int NKB = K / 32, N = NMB * NKS * 64;
+    static_assert(NMB <= M / 16 && NKS <= NKB, "a part of the matrix");
+    for (int idx = threadIdx.x; idx < N; idx += NTH) {
+        const int f = idx >> 6, ln = idx & 63, mb = mb0 + f / NKS, kb = kb0 + f % NKS;
+        const int m = 16 * mb + (ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
+        h8 v;
 #pragma unroll
-            for (int c = lane; c < DK; c += 64) bad |= sGam[c] < kFastGammaMin;
-            const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
-            if (lane == 0) {
-                P.flag[g * H + h] = any;
-                if (any) P.slow[atomicAdd(P.nslow, 1)] = g * H + h;
+        for (int e = 0; e < 8; ++e) v[e] = static_cast<_Float16>(elem(m, k0 + e));
+        *reinterpret_cast<h8*>(dst + afrag_off(mb, kb, NKB, ln)) = v;
+    }
+}
+
+template <int DK, int DV, bool ABF16, int GATE>
+__device__ __forceinline__ void prep_direct_body(const BwdParams& P, const int h, const int g) {
+    using R = BRec<DK, DV, ABF16>;
+    constexpr int NTH = kPrepThreads;
+    constexpr int NKS = DK / KSL, NVS = DV / KSL, NIT = NKS > NVS ? NKS : NVS;
+    constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
+    static_assert(DK % KSL == 0 && DV % KSL == 0, "whole slices");
+    extern __shared__ float lds[];
+    float* sX0 = lds;                    // K -> Gamma.K; T-solve scratch; Diag(beta).Gamma.K   [C][LH]
+    float* sX1 = sX0 + C * LH;           // gate -> K/Gamma; Diag(beta).V                        [C][LH]
+    float* sA = sX1 + C * LH;            // A; the gate (W pass); W, for its fragments           [C][LC]
+    float* sT = sA + C * LC;             // Q -> Gamma.Q; P; T                                    [C][LC]
+    float* sBeta = sT + C * LC;          // [C]
+    float* sGs = sBeta + C;              // scalar gate per row [C]
+    float* sGam = sGs + C;               // gamma = 2^b_last per channel [DK], kept to the end
+    float* sPart = sGam + DK;            // scan scratch [NTH]
+
+    const int H = P.H;
+    const int4 ent = P.table[g];
+    const int64_t row0 = ent.y;
+    const int len = ent.z;
+    const int tid = threadIdx.x, wave = wave_id(), lane = lane_id(), i = lane & 15, j = lane >> 4;
+    auto hrec = [&](size_t off) { return reinterpret_cast<_Float16*>(P.rec + (size_t(h) * P.gmax + g) * P.rec_bytes + off); };
+
+    Tok<ABF16, DK, KSL, NTH> tk, tq;     // the next key slice's k and q
+    Tok<GBF16, DK, KSL, NTH> tg;         // and its gate (per-channel forms)
+    auto load_slice = [&](int c0, bool withq) {
+        tk.load(P.k, row0, len, h, H, c0);
+        if (withq) tq.load(P.q, row0, len, h, H, c0);
+        if constexpr (GATE != KDA_GATE_SCALAR) tg.load(P.gate, row0, len, h, H, c0);
+    };
+    load_slice(0, true);
+    if constexpr (GATE == KDA_GATE_SCALAR) {
+        if (tid < C) sGs[tid] = tid < len ? static_cast<const float*>(P.gate)[(row0 + tid) * H + h] : 1.f;
+    }
+    if (tid < C) sBeta[tid] = tid < len ? P.beta[(row0 + tid) * H + h] : 0.f;
+
+    // A = StrictTril(Diag(beta) Kh Kb^T), P = Tril(Qh Kb^T), accumulated over
+    // the slices: tile (mb, nb) of both shares its B operand; two tile
+    // positions per wave, the ten below or on the diagonal spread so the
+    // waves sharing a SIMD (w, w + 4) hold 3, 3, 2, 2 of them; the six above
+    // are only zeroed.
+    constexpr unsigned kTiles[8] = {0x0010, 0x2030, 0x1101, 0x2102, 0x2203, 0x3112, 0x3213, 0x3323};
+    f4 accA[2] = {zero4(), zero4()}, accP[2] = {zero4(), zero4()};
+#pragma unroll 1
+    for (int ks = 0; ks < NKS; ++ks) {  // (kept rolled: unrolled, the slices' phases interleave and need ~200 registers)
+        const int c0 = ks * KSL;
+        tk.put(sX0, LH);
+        tq.put(sT, LH);
+        if constexpr (GATE != KDA_GATE_SCALAR) tg.put(sX1, LH);
+        __syncthreads();
+        // the next slice's loads fly during this slice's scan and products
+        if (ks + 1 < NKS) load_slice(c0 + KSL, true);
+        // b = cumsum(log2 alpha) per channel over the chunk;
+        // Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q, gamma = 2^b_last
+        gate_cumsum<KSL, NTH, GATE>(sX1, LH, sGs, len, sPart, [&](int r, int c, float b) {
+            const float G = __builtin_amdgcn_exp2f(b), Gi = __builtin_amdgcn_exp2f(-b);
+            const float kv = sX0[r * LH + c];
+            sX0[r * LH + c] = G * kv;
+            sX1[r * LH + c] = Gi * kv;
+            sT[r * LH + c] *= G;
+            if (r == C - 1) sGam[c0 + c] = G;
+        });
+        __syncthreads();
+        if (tid < KSL) rec_at(P, h, g, R::GAM)[c0 + tid] = sGam[c0 + tid];
+        if constexpr (!ABF16) {          // the 16-bit passes read Kt as fp16 fragments only
+            float* gKt = rec_at(P, h, g, R::KT);
+            for (int idx = tid; idx < C * KSL; idx += NTH) {
+                const int r = idx / KSL, c = idx % KSL;
+                gKt[r * DK + c0 + c] = sGam[c0 + c] * sX1[r * LH + c];
             }
+        }
+        store_block<NTH>(rec_at(P, h, g, R::QH) + c0, DK, sT, LH, C, KSL);
+        if constexpr (ABF16) {
+            // fp16 fragments of this slice for the 16-bit state passes: Kt
+            // (its reduction blocks), Kt^T and Qh^T (their row blocks)
+            write_afrags_part<C, DK, C / 16, KSL / 32, NTH>(hrec(R::FKT), 0, c0 / 32,
+                [&](int m, int k) { return sGam[k] * sX1[m * LH + k - c0]; });
+            write_afrags_part<DK, C, KSL / 16, C / 32, NTH>(hrec(R::FKTT), c0 / 16, 0,
+                [&](int m, int k) { return sGam[m] * sX1[k * LH + m - c0]; });
+            write_afrags_part<DK, C, KSL / 16, C / 32, NTH>(hrec(R::FQHT), c0 / 16, 0,
+                [&](int m, int k) { return sT[k * LH + m - c0]; });
+        }
+#pragma unroll
+        for (int slot = 0; slot < 2; ++slot) {
+            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
+            const int mb = tt >> 4, nb = tt & 15;
+            if (nb <= mb)
+                mm_two<KSL / 16, true, true>(sX0 + mb * 16 * LH, sT + mb * 16 * LH, LH, 1, sX1 + nb * 16 * LH, 1, LH,
+                                             accA[slot], accP[slot]);
+        }
+        __syncthreads();                 // the slice tiles are read; the next slice (or P) may overwrite them
+    }
+    {
+        float* gP = rec_at(P, h, g, R::P);
+#pragma unroll
+        for (int slot = 0; slot < 2; ++slot) {
+            const unsigned tt = (kTiles[wave] >> (8 * (1 - slot))) & 0xff;
+            const int mb = tt >> 4, nb = tt & 15;
+            f4 a = accA[slot], pp = accP[slot];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = mb * 16 + 4 * j + e, s2 = nb * 16 + i;
+                a[e] = s2 < r ? sBeta[r] * a[e] : 0.f;
+                pp[e] = s2 <= r ? pp[e] : 0.f;
+            }
+            store_tile(sA + mb * 16 * LC + nb * 16, LC, a);
+            if constexpr (ABF16) store_tile(sT + mb * 16 * LC + nb * 16, LC, pp);   // P, for P^T fragments
+            else store_tile(gP + mb * 16 * C + nb * 16, C, pp);
+        }
+    }
+    __syncthreads();
+    if constexpr (ABF16) {
+        write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
+        __syncthreads();
+    }
+    solve_t(sA, sT, sX0);
+    // the W pass's inputs (V is read only here; issued after the solve,
+    // whose 16 x 16 substitution needs the registers)
+    load_slice(0, false);
+    Tok<ABF16, DV, KSL, NTH> tv[NVS];
+#pragma unroll
+    for (int vs = 0; vs < NVS; ++vs) tv[vs].load(P.v, row0, len, h, H, vs * KSL);
+    store_block<NTH>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
+
+    // W = T Y, U = T Z (Y = Diag(beta) Gamma.K, Z = Diag(beta) V), one key
+    // slice and one value slice per pass: waves 0..3 the four 16-column
+    // blocks of W's slice, waves 4..7 those of U's, all four row blocks
+    // sharing each B read (T lower triangular: row block mb reduces over
+    // 16 (mb + 1) tokens).
+    float* gW = rec_at(P, h, g, R::W);
+    float* gU = rec_at(P, h, g, R::U);
+#pragma unroll 1
+    for (int it = 0; it < NIT; ++it) {
+        const int c0 = it * KSL;
+        if (it < NKS) {
+            tk.put(sX0, LH);
+            if constexpr (GATE != KDA_GATE_SCALAR) tg.put(sA, LH);
+        }
+#pragma unroll
+        for (int vs = 0; vs < NVS; ++vs)
+            if (vs == it) tv[vs].put_scaled(sX1, LH, sBeta);
+        __syncthreads();
+        if (it + 1 < NKS) load_slice(c0 + KSL, false);
+        if (it < NKS)
+            gate_cumsum<KSL, NTH, GATE>(sA, LH, sGs, len, sPart, [&](int r, int c, float b) {
+                sX0[r * LH + c] = (__builtin_amdgcn_exp2f(b) * sX0[r * LH + c]) * sBeta[r];
+            });
+        __syncthreads();
+        const bool isw = wave < 4;
+        const int nb = wave & 3;
+        if (isw ? it < NKS : it < NVS) {
+            f4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+            mm_rows<4, C / 16, true, false>(sT, LC, 1, (isw ? sX0 : sX1) + nb * 16, LH, 1, 0, 1,
+                                            [](int mb, int gg) { return gg <= mb; }, acc);
+#pragma unroll
+            for (int mb = 0; mb < 4; ++mb) {
+                if (isw) {
+                    if constexpr (ABF16) store_tile(sA + mb * 16 * LC + nb * 16, LC, acc[mb]);   // W, for its fragments
+                    else store_tile(gW + mb * 16 * DK + c0 + nb * 16, DK, acc[mb]);
+                } else {
+                    store_tile(gU + mb * 16 * DV + c0 + nb * 16, DV, acc[mb]);
+                }
+            }
+        }
+        if constexpr (ABF16) {
+            if (it < NKS) {
+                __syncthreads();
+                write_afrags_part<C, DK, C / 16, KSL / 32, NTH>(hrec(R::FW), 0, c0 / 32,
+                    [&](int m, int k) { return sA[m * LC + k - c0]; });
+                write_afrags_part<DK, C, KSL / 16, C / 32, NTH>(hrec(R::FWT), c0 / 16, 0,
+                    [&](int m, int k) { return sA[k * LC + m - c0]; });
+            }
+        }
+        __syncthreads();                 // before the next pass overwrites the slice tiles
+    }
+    if (wave == 0) {                     // gamma (sGam) is left untouched since the scans
+        bool bad = false;
+#pragma unroll
+        for (int c = lane; c < DK; c += 64) bad |= sGam[c] < kFastGammaMin;
+        const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+        if (lane == 0) {
+            P.flag[g * H + h] = any;
+            if (any) P.slow[atomicAdd(P.nslow, 1)] = g * H + h;
         }
     }
 }
 
-// One workgroup per (chunk, head): the direct form, or the chunk's entry in
-// the general list.
+// One workgroup per (chunk, head): the direct form (two per CU).
 template <int DK, int DV, bool ABF16, int GATE>
-__global__ __launch_bounds__(kPrepThreads) void bwd_prep_kernel(const BwdParams P) {
+__global__ __launch_bounds__(kPrepThreads, 4) void bwd_prep_kernel(const BwdParams P) {
     const int g = blockIdx.x / P.H;
     if (g >= P.ctrl[0]) return;
-    prep_body<DK, DV, ABF16, GATE, true>(P, blockIdx.x % P.H, g);
+    prep_direct_body<DK, DV, ABF16, GATE>(P, blockIdx.x % P.H, g);
 }
 
 // Entry blockIdx.x of the general list, if the list is that long (the grid
@@ -470,7 +634,7 @@ template <int DK, int DV, bool ABF16, int GATE>
 __global__ __launch_bounds__(kPrepThreads) void bwd_prep_general_kernel(const BwdParams P) {
     if (static_cast<int>(blockIdx.x) >= *P.nslow) return;
     const int id = P.slow[blockIdx.x];
-    prep_body<DK, DV, ABF16, GATE, false>(P, id % P.H, id / P.H);
+    prep_general_body<DK, DV, ABF16, GATE>(P, id % P.H, id / P.H);
 }
 
 // ---------------------------------------------------------------------------
@@ -1963,13 +2127,14 @@ hipError_t launch_bwd_typed(const ChunkBwdPlan& bp, const ChunkBwdArgs& a, hipSt
     const unsigned chain_blocks = static_cast<unsigned>((pairs + 7) / 8 * 8 * (DV / 16));
     if (chunk_blocks > 0) {
         auto k1 = bwd_prep_kernel<DK, DV, ABF16, GATE>;
-        constexpr int l1 = PrepB<DK, DV>::bytes;
+        constexpr int l1 = PrepDirB<DK>::bytes;
         if ((e = set_lds(k1, l1)) != hipSuccess) return e;
         hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kPrepThreads), l1, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         auto k1g = bwd_prep_general_kernel<DK, DV, ABF16, GATE>;
-        if ((e = set_lds(k1g, l1)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k1g, dim3(general_blocks), dim3(kPrepThreads), l1, stream, p);
+        constexpr int l1g = PrepB<DK, DV>::bytes;
+        if ((e = set_lds(k1g, l1g)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k1g, dim3(general_blocks), dim3(kPrepThreads), l1g, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         auto k2 = ABF16 ? bwd_ckpt16_kernel<DK, DV> : bwd_ckpt_kernel<DK, DV>;
         constexpr int l2 = ABF16 ? Chain16B<DK>::bytes : CkptB<DK>::bytes;
