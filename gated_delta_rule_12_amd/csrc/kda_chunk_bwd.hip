@@ -405,9 +405,10 @@ __device__ __forceinline__ void prep_general_body(const BwdParams& P, const int 
 // appended to the general list (its values here are then never used).  The
 // key channels are staged in slices of KSL, so the LDS holds four 64 x 68
 // fp32 tiles (73 KB: two workgroups per CU): A and P accumulate in the
-// waves' registers over the slices; after T, each slice's Diag(beta).Gamma.K
-// is formed again from k and the gate (the same scan, so the same values)
-// for W = T Diag(beta) Gamma.K, beside U = T Diag(beta) V for one value slice.
+// waves' registers over the slices; after T, W = T Diag(beta) Gamma.K takes
+// the last slice's Gamma.K still in LDS, and every other slice's formed again
+// from k and the gate (the same scan, so the same values), each pass beside
+// U = T Diag(beta) V for one value slice.
 constexpr int KSL = 64, LH = KSL + 4;
 static_assert(LH == LC, "the slice tiles and the C x C tiles share one row stride");
 
@@ -439,8 +440,8 @@ __device__ __forceinline__ void prep_direct_body(const BwdParams& P, const int h
     constexpr bool GBF16 = GATE == KDA_GATE_SOFTPLUS_BF16;
     static_assert(DK % KSL == 0 && DV % KSL == 0, "whole slices");
     extern __shared__ float lds[];
-    float* sX0 = lds;                    // K -> Gamma.K; T-solve scratch; Diag(beta).Gamma.K   [C][LH]
-    float* sX1 = sX0 + C * LH;           // gate -> K/Gamma; Diag(beta).V                        [C][LH]
+    float* sX0 = lds;                    // K -> Gamma.K (kept for W); Diag(beta).Gamma.K        [C][LH]
+    float* sX1 = sX0 + C * LH;           // gate -> K/Gamma; T-solve scratch; Diag(beta).V        [C][LH]
     float* sA = sX1 + C * LH;            // A; the gate (W pass); W, for its fragments           [C][LC]
     float* sT = sA + C * LC;             // Q -> Gamma.Q; P; T                                    [C][LC]
     float* sBeta = sT + C * LC;          // [C]
@@ -547,26 +548,28 @@ __device__ __forceinline__ void prep_direct_body(const BwdParams& P, const int h
         write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
         __syncthreads();
     }
-    solve_t(sA, sT, sX0);
+    solve_t(sA, sT, sX1);
     // the W pass's inputs (V is read only here; issued after the solve,
-    // whose 16 x 16 substitution needs the registers)
-    load_slice(0, false);
+    // whose 16 x 16 substitution needs the registers): the key slices other
+    // than the last, whose Gamma.K is still in sX0
+    if (NKS > 1) load_slice(0, false);
     Tok<ABF16, DV, KSL, NTH> tv[NVS];
 #pragma unroll
     for (int vs = 0; vs < NVS; ++vs) tv[vs].load(P.v, row0, len, h, H, vs * KSL);
     store_block<NTH>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
 
     // W = T Y, U = T Z (Y = Diag(beta) Gamma.K, Z = Diag(beta) V), one key
-    // slice and one value slice per pass: waves 0..3 the four 16-column
-    // blocks of W's slice, waves 4..7 those of U's, all four row blocks
-    // sharing each B read (T lower triangular: row block mb reduces over
-    // 16 (mb + 1) tokens).
+    // slice and one value slice per pass (key slices in the order NKS - 1,
+    // 0, 1, ...): waves 0..3 the four 16-column blocks of W's slice, waves
+    // 4..7 those of U's, all four row blocks sharing each B read (T lower
+    // triangular: row block mb reduces over 16 (mb + 1) tokens).
     float* gW = rec_at(P, h, g, R::W);
     float* gU = rec_at(P, h, g, R::U);
 #pragma unroll 1
     for (int it = 0; it < NIT; ++it) {
-        const int c0 = it * KSL;
-        if (it < NKS) {
+        const int c0 = (it == 0 ? NKS - 1 : it - 1) * KSL;   // this pass's key slice
+        const int v0 = it * KSL;                             // and value slice
+        if (it > 0 && it < NKS) {
             tk.put(sX0, LH);
             if constexpr (GATE != KDA_GATE_SCALAR) tg.put(sA, LH);
         }
@@ -574,11 +577,17 @@ __device__ __forceinline__ void prep_direct_body(const BwdParams& P, const int h
         for (int vs = 0; vs < NVS; ++vs)
             if (vs == it) tv[vs].put_scaled(sX1, LH, sBeta);
         __syncthreads();
-        if (it + 1 < NKS) load_slice(c0 + KSL, false);
-        if (it < NKS)
+        if (it > 0 && it + 1 < NKS) load_slice(it * KSL, false);
+        if (it == 0) {
+            for (int idx = tid; idx < C * KSL; idx += NTH) {
+                const int r = idx / KSL, c = idx % KSL;
+                sX0[r * LH + c] *= sBeta[r];
+            }
+        } else if (it < NKS) {
             gate_cumsum<KSL, NTH, GATE>(sA, LH, sGs, len, sPart, [&](int r, int c, float b) {
                 sX0[r * LH + c] = (__builtin_amdgcn_exp2f(b) * sX0[r * LH + c]) * sBeta[r];
             });
+        }
         __syncthreads();
         const bool isw = wave < 4;
         const int nb = wave & 3;
@@ -592,7 +601,7 @@ __device__ __forceinline__ void prep_direct_body(const BwdParams& P, const int h
                     if constexpr (ABF16) store_tile(sA + mb * 16 * LC + nb * 16, LC, acc[mb]);   // W, for its fragments
                     else store_tile(gW + mb * 16 * DK + c0 + nb * 16, DK, acc[mb]);
                 } else {
-                    store_tile(gU + mb * 16 * DV + c0 + nb * 16, DV, acc[mb]);
+                    store_tile(gU + mb * 16 * DV + v0 + nb * 16, DV, acc[mb]);
                 }
             }
         }
