@@ -442,14 +442,24 @@ __global__ __launch_bounds__(kThreads) void gprep_general_kernel(const GParams P
 // gchain_kernel: wave w holds state row block w (and w + 8); the C x 16
 // product U' = U - W S is split over the waves: row block w % (C/16), part
 // w / (C/16) of the d_k reduction, the parts handed to part 0 through LDS.
+// At C = 128 a ninth wave pulls the record lines the chain reads (Kt, W, U,
+// gamma) into L2 kGChainPrefetch chunks ahead, each of the d_v / 16 column
+// tiles of a (sequence, head) every (d_v / 16)-th line, on its own wait
+// counters (64K-token forward: 2.78 -> 2.38 ms; at C = 32, whose chunks'
+// operands are a quarter as large, it cost 3.75 -> 3.98 ms).
 // ---------------------------------------------------------------------------
+template <int C> struct GChainPF {
+    static constexpr bool on = C >= 128;
+    static constexpr int threads = on ? kThreads + 64 : kThreads;
+};
+constexpr int kGChainPrefetch = 2;
 template <int DK, int C> struct GChainB {
     static constexpr int LK = Ld<DK>::value, NSPLIT = kWaves / (C / 16);
     static constexpr int bytes = (2 * C * LK + DK * L16 + C * L16 + (NSPLIT - 1) * C * L16 + DK) * 4;
 };
 
 template <int DK, int DV, int C>
-__global__ __launch_bounds__(kThreads) void gchain_kernel(const GParams P) {
+__global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GParams P) {
     using R = GRec<DK, DV, C>;
     constexpr int NTH = kThreads, NW = kWaves, LK = GChainB<DK, C>::LK, NT = DV / 16;
     constexpr int NB = C / 16, NSPLIT = GChainB<DK, C>::NSPLIT, KP = DK / NSPLIT;
@@ -467,7 +477,26 @@ __global__ __launch_bounds__(kThreads) void gchain_kernel(const GParams P) {
     if (pair >= P.N * P.H) return;
     const int n = P.order[pair / P.H], h = pair % P.H;
     const int g0 = P.first[n], g1 = P.first[n + 1];
-    const int wave = wave_id(), j = lane_id() >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id()), j = lane_id() >> 4;
+    if (GChainPF<C>::on && wave == NW) {
+        // the prefetch wave: matches the four barriers per chunk of the
+        // others with bare ones (a fence would wait for these loads)
+        __shared__ int s_pf[64];
+        static_assert(R::W == R::KT + size_t(C) * DK * 4, "Kt and W are adjacent in the record");
+        auto touch = [&](int gp) {
+            l2_touch(grec(P, h, gp, R::KT), 2 * C * DK * 4, tile, NT, s_pf);
+            l2_touch(grec(P, h, gp, R::U), C * DV * 4, tile, NT, s_pf);
+            l2_touch(grec(P, h, gp, R::GAM), DK * 4, tile, NT, s_pf);
+        };
+        for (int gp = g0 + 1; gp < min(g0 + kGChainPrefetch, g1); ++gp) touch(gp);
+        for (int g = g0; g < g1; ++g) {
+            if (g + kGChainPrefetch < g1) touch(g + kGChainPrefetch);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);       // every load has landed before the wave ends
+        return;
+    }
     const int c0 = tile * 16;
     const int mb = wave % NB, part = wave / NB;
     const size_t sbase = (static_cast<size_t>(n) * P.H + h) * DK * DV;
@@ -647,7 +676,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         auto k2 = gchain_kernel<DK, DV, C>;
         constexpr int l2 = GChainB<DK, C>::bytes;
         if ((e = set_lds(k2, l2)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(kThreads), l2, stream, p);
+        hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(GChainPF<C>::threads), l2, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chunk_blocks > 0) {
