@@ -172,9 +172,10 @@ def measured_bwd_traffic():
 # profiles/ are written by `python bench.py --summarize KIND ...` from the CSV
 # files of the rocprofv3 runs named in each summary's header.
 # ---------------------------------------------------------------------------
+GEN_KERNELS = ("gprep_kernel", "gprep_general_kernel", "gchain_kernel", "gout_kernel")   # chunk sizes 32 / 128
 LIB_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel", "state_split_kernel", "decode_kernel",
                "bwd_prep_kernel", "bwd_prep_general_kernel", "bwd_ckpt_kernel", "bwd_ckpt16_kernel",
-               "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel", "bwd_grad_general_kernel")
+               "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel", "bwd_grad_general_kernel") + GEN_KERNELS
 FWD_KERNELS = ("plan_kernel", "prep_kernel", "prep_general_kernel", "state_kernel", "state_split_kernel")
 BWD_KERNELS = ("plan_kernel", "bwd_prep_kernel", "bwd_prep_general_kernel", "bwd_ckpt_kernel",
                "bwd_ckpt16_kernel", "bwd_rev_kernel", "bwd_rev16_kernel", "bwd_grad_kernel",
@@ -249,7 +250,14 @@ def _copy_counter(pattern, counter):
     return sum(vals) / len(vals)
 
 
-def summarize(kind, inputs, title, commands):
+def _chunk_arg(name):
+    """The chunk size of a generic-path kernel: its third template argument."""
+    short = _kernel_short(name)
+    args = short[short.find("<") + 1:short.rfind(">")].split(",")
+    return int(args[2]) if len(args) > 2 else 0
+
+
+def summarize(kind, inputs, title, commands, kernels=None):
     """Print a profiles/ summary.  kind:
       trace    inputs = [kernel_stats.csv glob]
       traffic  inputs = [FETCH_SIZE csv glob, WRITE_SIZE csv glob, copy FETCH_SIZE glob, copy WRITE_SIZE glob]
@@ -260,7 +268,9 @@ def summarize(kind, inputs, title, commands):
         print(f"# {c}")
     fwd_sha, bwd_sha = sources_sha256(KERNEL_SOURCES), sources_sha256(BWD_KERNEL_SOURCES)
     if kind == "trace":
-        rows = [r for r in _csv_rows(inputs[0]) if _kernel_base(r["Name"]) in LIB_KERNELS]
+        keep = kernels or LIB_KERNELS
+        rows = [r for r in _csv_rows(inputs[0]) if _kernel_base(r["Name"]) in LIB_KERNELS
+                and _kernel_base(r["Name"]) in keep]
         print(f"# forward/decode sources sha256: {fwd_sha}")
         print(f"# backward sources sha256: {bwd_sha}")
         print("#")
@@ -274,9 +284,14 @@ def summarize(kind, inputs, title, commands):
             for grp, names in (("forward", FWD_KERNELS), ("backward", BWD_KERNELS), ("decode", ("decode_kernel",))):
                 if base in names:
                     sums[grp] = sums.get(grp, 0.0) + avg
+            if base in GEN_KERNELS:
+                grp = f"chunk-{_chunk_arg(r['Name'])} forward (generic path)"
+                sums[grp] = sums.get(grp, 0.0) + avg
         for grp, names in (("forward", FWD_KERNELS), ("backward", BWD_KERNELS), ("decode", ("decode_kernel",))):
             if any(n in seen and n != "plan_kernel" for n in names):
                 print(f"# {grp} kernels, sum of averages: {sums[grp]:.2f} us")
+        for grp in sorted(k for k in sums if k.startswith("chunk-")):
+            print(f"# {grp} kernels (plan_kernel not included), sum of averages: {sums[grp]:.2f} us")
     elif kind == "traffic":
         fetch, write = _counter_means(inputs[0], "FETCH_SIZE"), _counter_means(inputs[1], "WRITE_SIZE")
         copy_bytes = 1 << 30
@@ -442,13 +457,15 @@ def main():
     ap.add_argument("--summarize", choices=["trace", "traffic", "mfma", "counters"], default=None,
                     help="print a profiles/ summary from rocprofv3 CSV files (globs given by --inputs)")
     ap.add_argument("--inputs", nargs="*", default=[])
+    ap.add_argument("--kernels", nargs="*", default=None,
+                    help="--summarize trace: keep only these kernels (names without template arguments)")
     ap.add_argument("--title", default="")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the measured peaks and the other gate forms (profiler runs)")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.inputs, args.title, args.command)
+        summarize(args.summarize, args.inputs, args.title, args.command, args.kernels)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
