@@ -564,21 +564,34 @@ __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GPar
 
 // ---------------------------------------------------------------------------
 // gout_kernel: O[:, 32 columns] = Qh S + P U' for one (chunk, head).
+// At C = 128 (QREG) output tile t is row block t % (C/16) and column block
+// t / (C/16), so each wave owns one row block: it reads its 16 rows of
+// Gamma.Q straight into registers at the start (the A operand of both its
+// tiles) and only S, P and U' are staged in LDS (74 KB: two workgroups per
+// CU; staging Gamma.Q too took 140 KB and 2.49 vs 1.89 ms).  At C = 32 the
+// four tiles' two row blocks would be read by two waves each, and Gamma.Q is
+// staged in LDS with the rest (1.57 vs 1.79 ms).
 // ---------------------------------------------------------------------------
 template <int DK, int C> struct GOutB {
+    static constexpr bool QREG = C >= 128;
     static constexpr int LK = Ld<DK>::value, NB = C / 16, NLT = NB * (NB + 1) / 2;
-    static constexpr int bytes = (C * LK + DK * kLS + NLT * 256 + C * kLS) * 4;
+    static constexpr int bytes = ((QREG ? 0 : C * LK) + DK * kLS + NLT * 256 + C * kLS) * 4;
 };
 
 template <int DK, int DV, int C, bool OBF16>
 __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
     using R = GRec<DK, DV, C>;
-    constexpr int NTH = kThreads, NW = kWaves, LK = GOutB<DK, C>::LK, SL = kSL, LS = kLS;
+    constexpr int NTH = kThreads, NW = kWaves, SL = kSL, LS = kLS;
     constexpr int NB = GOutB<DK, C>::NB, NLT = GOutB<DK, C>::NLT, NSV = DV / SL;
     constexpr int PIT = (NLT * 256 + NTH - 1) / NTH;
+    constexpr int NT = NB * (SL / 16);                 // output tiles
+    constexpr int KG = DK / 16;                        // 16-deep groups of Qh S
+    constexpr bool QREG = GOutB<DK, C>::QREG;
+    constexpr int LK = GOutB<DK, C>::LK;
+    static_assert(!QREG || NB == NW, "each wave's tiles share one row block");
     extern __shared__ float lds[];
-    float* sQh = lds;                // [C][LK]
-    float* sS = sQh + C * LK;        // S[:, slice]   [DK][LS]
+    float* sQh = lds;                // Gamma.Q [C][LK] (not QREG)
+    float* sS = lds + (QREG ? 0 : C * LK);   // S[:, slice]   [DK][LS]
     float* sP = sS + DK * LS;        // P, packed lower tiles [NLT][256]
     float* sU = sP + NLT * 256;      // U'[:, slice]  [C][LS]
 
@@ -591,13 +604,21 @@ __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
     const int len = ent.z;
     const int tid = threadIdx.x, wave = wave_id(), i = lane_id() & 15, j = lane_id() >> 4;
     const int s0 = sv * SL;
+    const int mb = wave % NB;        // QREG: this wave's row block
 
+    // QREG: this wave's rows of Gamma.Q in the A layout of the 16-deep groups
+    [[maybe_unused]] f4 aq[QREG ? KG : 1];
+    if constexpr (QREG) {
+        const float* gq = grec(P, h, g, R::QH) + static_cast<size_t>(mb * 16 + i) * DK + 4 * j;
+#pragma unroll
+        for (int gg = 0; gg < KG; ++gg) aq[gg] = *reinterpret_cast<const f4*>(gq + 16 * gg);
+    }
     {
-        Blk<C, DK, NTH> bq;
+        Blk<C, QREG ? 4 : DK, NTH> bq;      // (QREG: unused)
         Blk<DK, SL, NTH> bs;
         Blk<C, SL, NTH> bu;
         float pv[PIT];
-        bq.load(grec(P, h, g, R::QH), DK);
+        if constexpr (!QREG) bq.load(grec(P, h, g, R::QH), DK);
         bs.load(grec(P, h, g, R::SIN) + s0, DV);
         bu.load(grec(P, h, g, R::UC) + s0, DV);
         const float* gP = grec(P, h, g, R::P);
@@ -611,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
                 pv[it] = gP[(ti * 16 + (e >> 4)) * C + tj * 16 + (e & 15)];
             }
         }
-        bq.put(sQh, LK);
+        if constexpr (!QREG) bq.put(sQh, LK);
         bs.put(sS, LS);
         bu.put(sU, LS);
 #pragma unroll
@@ -621,14 +642,26 @@ __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
         }
     }
     __syncthreads();
-    for (int t = wave; t < NB * (SL / 16); t += NW) {
-        const int mb = t / (SL / 16), nb = t % (SL / 16);
-        f4 x = mm<DK, true, false>(sQh + mb * 16 * LK, LK, 1, sS + nb * 16, LS, 1, zero4());
-        for (int kb = 0; kb <= mb; ++kb)
-            x = mm<16, true, false>(sP + lt(mb, kb) * 256, 16, 1, sU + kb * 16 * LS + nb * 16, LS, 1, x);
+    for (int t = wave; t < NT; t += NW) {
+        const int tmb = QREG ? mb : t / (SL / 16);
+        const int nb = QREG ? t / NB : t % (SL / 16);
+        f4 x = zero4();
+        if constexpr (QREG) {
+            const float* pb = sS + 4 * j * LS + nb * 16 + i;
+#pragma unroll
+            for (int gg = 0; gg < KG; ++gg) {
+                const f4 b = f4{pb[16 * gg * LS], pb[(16 * gg + 1) * LS], pb[(16 * gg + 2) * LS], pb[(16 * gg + 3) * LS]};
+#pragma unroll
+                for (int s2 = 0; s2 < 4; ++s2) x = mfma4(aq[gg][s2], b[s2], x);
+            }
+        } else {
+            x = mm<DK, true, false>(sQh + tmb * 16 * LK, LK, 1, sS + nb * 16, LS, 1, x);
+        }
+        for (int kb = 0; kb <= tmb; ++kb)
+            x = mm<16, true, false>(sP + lt(tmb, kb) * 256, 16, 1, sU + kb * 16 * LS + nb * 16, LS, 1, x);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int r = mb * 16 + 4 * j + e;
+            const int r = tmb * 16 + 4 * j + e;
             if (r < len)
                 store_out<OBF16>(P.o, (static_cast<size_t>(row0 + r) * H + h) * DV + s0 + nb * 16 + i, x[e]);
         }
