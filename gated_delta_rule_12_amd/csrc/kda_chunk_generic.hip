@@ -54,7 +54,7 @@ template <int DK, int DV, int C> struct GRec {
     static constexpr size_t QH = 0;              // Gamma . Q                 [C][DK]
     static constexpr size_t KT = QH + CK;        // (gamma / Gamma) . K       [C][DK]
     static constexpr size_t W = KT + CK;         // T Diag(beta) (Gamma . K)  [C][DK]
-    static constexpr size_t B = W + CK;          // b = cumsum(log2 alpha)     [C][DK]
+    static constexpr size_t B = W + CK;          // b = cumsum(log2 alpha)     [C][DK]  (general form: its W pass reads it back)
     static constexpr size_t U = B + CK;          // T Diag(beta) V            [C][DV]
     static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]
     static constexpr size_t GAM = P + CC;        // gamma                     [DK]
@@ -144,6 +144,26 @@ __device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
     float* gKt = grec(P, h, g, R::KT);
     float* gGam = grec(P, h, g, R::GAM);
 
+    // direct form: log2 alpha of the gate slice staged in sB, per element
+    // (padding rows: 0), and the sums of each thread's segment of rows into
+    // sPart; b is then the running sum over the segments before and the rows
+    // of the thread's own (the same operations in both passes, so the same b)
+    [[maybe_unused]] auto log2_segments = [&]() {
+        const int c = tid % SL, sg = tid / SL;
+        float part = 0.f;
+        for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
+            float l2 = 0.f;
+            if (r < len) {
+                if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
+                else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sB[r * LS + c]);
+                else l2 = __builtin_amdgcn_logf(sB[r * LS + c]);
+            }
+            sB[r * LS + c] = l2;
+            part += l2;
+        }
+        sPart[sg * SL + c] = part;
+        __syncthreads();
+    };
     float* gP = grec(P, h, g, R::P);
     [[maybe_unused]] bool strong = false;   // direct form: some channel of this lane's decays below 2^-64
     if constexpr (FAST) {
@@ -165,22 +185,7 @@ __device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
                 tq.put(sQ, LS);
             }
             __syncthreads();
-            {   // log2 alpha per element (padding rows: 0), segment sums
-                const int c = tid % SL, sg = tid / SL;
-                float part = 0.f;
-                for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
-                    float l2 = 0.f;
-                    if (r < len) {
-                        if constexpr (GATE == KDA_GATE_SCALAR) l2 = __builtin_amdgcn_logf(sGs[r]);
-                        else if constexpr (GBF16) l2 = log2_alpha_from_softplus_arg(sB[r * LS + c]);
-                        else l2 = __builtin_amdgcn_logf(sB[r * LS + c]);
-                    }
-                    sB[r * LS + c] = l2;
-                    part += l2;
-                }
-                sPart[sg * SL + c] = part;
-            }
-            __syncthreads();
+            log2_segments();
             {   // b = cumsum(log2 alpha); Kh = 2^b K, Kb = 2^-b K, Qh = 2^b Q
                 const int c = tid % SL, sg = tid / SL;
                 float b = 0.f;
@@ -192,7 +197,6 @@ __device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
                     sK[r * LS + c] = G * kv;
                     sB[r * LS + c] = Gi * kv;
                     sQ[r * LS + c] *= G;
-                    gB[r * DK + cs + c] = b;
                 }
                 if (sg == NS - 1) {
                     gGam[cs + c] = sGam[c] = __builtin_amdgcn_exp2f(b);
@@ -387,21 +391,42 @@ __device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
         const int c0 = isw ? cs : cs - DK;
         if (isw) {
             Tok<ABF16, DK, SL, NTH, C> tk;
-            Blk<C, SL, NTH> bb;
             tk.load(P.k, row0, len, h, H, c0);
-            bb.load(gB + c0, DK);
+            if constexpr (FAST) {
+                // b again from the gate (not stored: 16 bytes per token and
+                // channel written and read back)
+                if constexpr (GATE != KDA_GATE_SCALAR) {
+                    Tok<GBF16, DK, SL, NTH, C> tg;
+                    tg.load(P.gate, row0, len, h, H, c0);
+                    tg.put(sB, LS);
+                }
+            } else {
+                Blk<C, SL, NTH> bb;
+                bb.load(gB + c0, DK);
+                bb.put(sB, LS);
+            }
             tk.put(sK, LS);
-            bb.put(sB, LS);
         } else {
             Tok<ABF16, DV, SL, NTH, C> tv;
             tv.load(P.v, row0, len, h, H, c0);
             tv.put(sK, LS);
         }
         __syncthreads();
-        for (int idx = tid; idx < C * SL; idx += NTH) {
-            const int r = idx / SL, c = idx % SL;
-            const float sc = isw ? __builtin_amdgcn_exp2f(sB[r * LS + c]) * sBeta[r] : sBeta[r];
-            sK[r * LS + c] *= sc;
+        if (FAST && isw) {
+            log2_segments();
+            const int c = tid % SL, sg = tid / SL;
+            float b = 0.f;
+            for (int s2 = 0; s2 < sg; ++s2) b += sPart[s2 * SL + c];
+            for (int r = sg * SEG; r < sg * SEG + SEG; ++r) {
+                b += sB[r * LS + c];
+                sK[r * LS + c] *= __builtin_amdgcn_exp2f(b) * sBeta[r];
+            }
+        } else {
+            for (int idx = tid; idx < C * SL; idx += NTH) {
+                const int r = idx / SL, c = idx % SL;
+                const float sc = isw ? __builtin_amdgcn_exp2f(sB[r * LS + c]) * sBeta[r] : sBeta[r];
+                sK[r * LS + c] *= sc;
+            }
         }
         __syncthreads();
         for (int t = wave; t < NB * (SL / 16); t += NW) {
