@@ -93,6 +93,21 @@ def test_trace_summary_keeps_library_kernels_and_sums_the_forward(tmp_path, caps
     assert "forward kernels, sum of averages: 2100.00 us" in out
 
 
+def test_trace_summary_sums_the_generic_path_per_chunk_size(tmp_path, capsys):
+    ns = "void kda::(anonymous namespace)::"
+    rows = [[ns + "gprep_kernel<128, 128, 32, true, 0>(kda::(anonymous namespace)::GParams)", 2, 4_000_000, 2_000_000, 0, 1, 2, 0],
+            [ns + "gchain_kernel<128, 128, 32>(kda::(anonymous namespace)::GParams)", 2, 6_000_000, 3_000_000, 0, 1, 2, 0],
+            [ns + "gout_kernel<128, 128, 128, true>(kda::(anonymous namespace)::GParams)", 2, 3_000_000, 1_500_000, 0, 1, 2, 0],
+            [PREP, 4, 4_400_000, 1_100_000, 50, 1_000_000, 1_200_000, 0]]
+    p = _write_csv(tmp_path / "run_kernel_stats.csv",
+                   ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"], rows)
+    bench.summarize("trace", [p], "t", [], kernels=["gprep_kernel", "gchain_kernel", "gout_kernel"])
+    out = capsys.readouterr().out
+    assert "prep_kernel<128, 128, true, 0>" not in out          # filtered out by --kernels
+    assert "chunk-32 forward (generic path) kernels (plan_kernel not included), sum of averages: 5000.00 us" in out
+    assert "chunk-128 forward (generic path) kernels (plan_kernel not included), sum of averages: 1500.00 us" in out
+
+
 def test_traffic_summary_scales_by_the_copy(tmp_path, capsys):
     hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
     f = _write_csv(tmp_path / "f.csv", hdr, [[PREP, "FETCH_SIZE", 1000], [PREP, "FETCH_SIZE", 3000]])
