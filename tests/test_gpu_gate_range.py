@@ -239,6 +239,24 @@ def test_chunk_bwd_mixed_forms(gate, act):
     _bwd_strong(gate, act, g, inp, 41)
 
 
+@pytest.mark.parametrize("Dk,Dv", [(128, 64), (64, 128)])
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_chunk_bwd_mixed_forms_unequal_heads(Dk, Dv, act):
+    """Both forms of the backward in one call where d_k != d_v: the direct
+    form's preparation stages the key channels and the value columns in
+    64-wide slices, so its W and U passes differ in number here."""
+    print(f"[bwd mixed forms Dk={Dk} Dv={Dv} act={act}]", flush=True)
+    B, T, H = 1, 384, 2
+    inp = synth.chunk_inputs(B, T, H, Dk, Dv, act, mu=-2.0, s0_std=0.05, seed=43, device=DEV)
+    mild = synth.draw_gate("alpha", (B, T), H, Dk, -2.0, 43, DEV)
+    strong = synth.draw_strong_gate("alpha", (B, T), H, Dk, 2.0, 44, DEV, zero_frac=0.0)
+    cc = (torch.arange(T, device=DEV) // 64)[None, :, None]
+    hh = torch.arange(H, device=DEV)[None, None, :]
+    sel = ((cc + hh) % 2 == 0)[..., None]
+    g = torch.where(sel, strong, mild).contiguous()
+    _bwd_strong("alpha", act, g, inp, 43)
+
+
 @pytest.mark.parametrize("gate", ["alpha", "softplus"])
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_chunk_bwd_strong_decay_varlen_small_heads(gate, act):
