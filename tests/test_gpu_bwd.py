@@ -116,10 +116,10 @@ def test_bwd_repeatable():
         assert torch.equal(r1[name], r2[name]), name
 
 
-def test_bwd_workload2_full_sampled():
+def test_bwd_workload2_full():
     """B=1, H=32, T=65536, d=128, slow decay, random S0: the backward the
-    benchmark times (same inputs, dO and dS_T ~ N(0, 1)).  All 32 heads run on
-    the GPU; 3 full heads (all 65536 tokens each) are recomputed by the oracle."""
+    benchmark times (same inputs, dO and dS_T ~ N(0, 1)), every element of
+    every gradient against the oracle's backward on all 32 heads."""
     w = synth.WORKLOADS[2]
     print(f"[bwd {w.name}]", flush=True)
     inp = synth.workload_inputs(2, device=DEV)
@@ -127,18 +127,13 @@ def test_bwd_workload2_full_sampled():
     r = kda.kda_chunk_bwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], up["dout"],
                           initial_state=inp["initial_state"], dfinal_state=up["dfinal_state"])
     torch.cuda.synchronize()
-    heads = [0, 13, 31]
-    sl = (slice(None), slice(None), heads)
-    ref = oracle.kda_bwd(to_np(inp["q"][sl]), to_np(inp["k"][sl]), to_np(inp["v"][sl]),
-                         to_np(inp["alpha"][sl]), to_np(inp["beta"][sl]), to_np(up["dout"][sl]),
-                         initial_state=to_np(inp["initial_state"][:, heads]),
-                         dfinal_state=to_np(up["dfinal_state"][:, heads]))
-    for hi, h in enumerate(heads):
-        ratios = []
-        for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
-            got = r["dgate" if name == "dalpha" else name][:, :, h]
-            ratios.append(check_close(got, ref[name][:, :, hi], "bf16",
-                                      stored_bf16=name in ("dq", "dk", "dv"), what=f"{name} head {h}"))
-        ratios.append(check_close(r["dinitial_state"][:, h], ref["dinitial_state"][:, hi], "bf16",
-                                  what=f"dS0 head {h}"))
-        print(f"  head {h}: error/allowed " + " ".join(f"{x:.3f}" for x in ratios), flush=True)
+    ref = oracle.kda_bwd(to_np(inp["q"]), to_np(inp["k"]), to_np(inp["v"]), to_np(inp["alpha"]),
+                         to_np(inp["beta"]), to_np(up["dout"]), initial_state=to_np(inp["initial_state"]),
+                         dfinal_state=to_np(up["dfinal_state"]))
+    ratios = {}
+    for name in ("dq", "dk", "dv", "dalpha", "dbeta"):
+        got = r["dgate" if name == "dalpha" else name]
+        ratios[name] = check_close(got, ref[name], "bf16", stored_bf16=name in ("dq", "dk", "dv"), what=name)
+        del got
+    ratios["dS0"] = check_close(r["dinitial_state"], ref["dinitial_state"], "bf16", what="dS0")
+    print("  error/allowed: " + "  ".join(f"{k} {v:.3f}" for k, v in ratios.items()), flush=True)
