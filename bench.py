@@ -818,6 +818,23 @@ def main():
                            "cores": rb["threads"], "kind": "oracle",
                            "sample": f"first {Sb} tokens, all {wf.H} heads, backward of the fp64 "
                                      f"recurrence ({c1 - c0:.2f} s)"}
+            # the GPU backward on the same sample, against that oracle result
+            from tests.helpers import error_ratio
+            gs = lambda x: x[slb].contiguous()
+            rg = kda.kda_chunk_bwd(gs(fi["q"]), gs(fi["k"]), gs(fi["v"]), gs(fi["alpha"]), gs(fi["beta"]),
+                                   up["dout"].to(dev), initial_state=fi["initial_state"],
+                                   dfinal_state=up["dfinal_state"].to(dev))
+            torch.cuda.synchronize()
+            par = {name: round(error_ratio(rg[name], rb[name], "bf16", stored_bf16=True), 4)
+                   for name in ("dq", "dk", "dv")}
+            par["dalpha"] = round(error_ratio(rg["dgate"], rb["dalpha"], "bf16"), 4)
+            par["dbeta"] = round(error_ratio(rg["dbeta"], rb["dbeta"], "bf16"), 4)
+            par["dS0"] = round(error_ratio(rg["dinitial_state"], rb["dinitial_state"], "bf16"), 4)
+            par["unit"] = "max error / allowed error (<= 1 passes)"
+            par["reference"] = (f"fp64 oracle backward on the first {Sb} tokens, all {wf.H} heads "
+                                "(the CPU-baseline sample), against kda_chunk_bwd on the same sample")
+            out["variants"]["bwd"]["parity"] = par
+            del rg
         if np.isfinite(base["value"]) and out.get("value"):
             base["gpu_over_cpu"] = round(out["value"] / base["value"], 1)
         out["cpu_baseline"] = base
