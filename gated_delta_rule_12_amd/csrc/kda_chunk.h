@@ -61,7 +61,7 @@ hipError_t launch_chunk_fwd(const ChunkPlan& plan, const ChunkArgs& args, hipStr
 
 // Chunk sizes other than 64 (kda_chunk_generic.hip): an fp32 path with its
 // own per-(head, chunk) record of generic_record_bytes bytes.
-size_t generic_record_bytes(int Dk, int Dv, int chunk_size);
+size_t generic_record_bytes(int Dk, int Dv, int chunk_size, bool act16);
 hipError_t launch_chunk_fwd_generic(const ChunkPlan& plan, const ChunkArgs& args, hipStream_t stream);
 
 // Enqueue the chunk-table kernel: fills ctrl, first, order and table of the

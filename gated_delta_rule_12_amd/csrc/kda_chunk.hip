@@ -1884,7 +1884,7 @@ kda_status make_chunk_plan(int B, int64_t T, int H, int Dk, int Dv, bool varlen,
         p.rec_bytes = align256(3 * static_cast<size_t>(C) * Dk * p.eb + static_cast<size_t>(kPFrags) * 512 * p.eb +
                                static_cast<size_t>(C) * Dv * p.eb + static_cast<size_t>(Dk) * 4);
     else
-        p.rec_bytes = align256(generic_record_bytes(Dk, Dv, chunk_size));
+        p.rec_bytes = align256(generic_record_bytes(Dk, Dv, chunk_size, p.eb == 2));
     p.off_rec = off;   off = align256(off + gh * p.rec_bytes);
     p.workspace_bytes = off;
     *plan = p;

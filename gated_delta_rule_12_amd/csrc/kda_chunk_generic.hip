@@ -24,6 +24,8 @@
 //                  state at the end.
 //   gout_kernel    one 512-thread WG per (chunk, head, 32 value columns):
 //                  O = Qh S + P U'.
+#include <type_traits>
+
 #include "kda_chunk.h"
 #include "kda_common.h"
 #include "kda_mm32.h"
@@ -48,8 +50,46 @@ __device__ __forceinline__ void lt_decode(int idx, int& i, int& j) {
     j = idx;
 }
 
+// Blk for an fp16 source (ROWS x NC, source row stride sld halves): four
+// halves per 8-byte load, widened to fp32 on the way into LDS.
+template <int ROWS, int NC, int NTH>
+struct BlkH {
+    static constexpr int V4 = NC / 4, N = ROWS * V4, IT = (N + NTH - 1) / NTH;
+    h4 t[IT];
+    __device__ __forceinline__ void load(const _Float16* src, int sld) {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N)
+                t[it] = *reinterpret_cast<const h4*>(src + static_cast<size_t>(idx / V4) * sld + (idx % V4) * 4);
+        }
+    }
+    __device__ __forceinline__ void put(float* dst, int ld) const {
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int idx = threadIdx.x + it * NTH;
+            if (N % NTH == 0 || idx < N)
+                *reinterpret_cast<f4*>(dst + (idx / V4) * ld + (idx % V4) * 4) =
+                    f4{static_cast<float>(t[it][0]), static_cast<float>(t[it][1]),
+                       static_cast<float>(t[it][2]), static_cast<float>(t[it][3])};
+        }
+    }
+};
+
+// store_tile into fp16 memory
+__device__ __forceinline__ void store_tile_h(_Float16* p, int ld, f4 v) {
+    const int i = lane_id() & 15, j = lane_id() >> 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[(4 * j + e) * ld + i] = static_cast<_Float16>(v[e]);
+}
+
 // Per-(head, chunk) fp32 record (byte offsets); rows are chunk-local tokens.
-template <int DK, int DV, int C> struct GRec {
+// With 16-bit activations (H16) the state entering the chunk and U' -- the
+// chain's outputs for the output pass -- are kept in fp16 (relative rounding
+// 2^-11, against the 2e-2 x RMS bar of those inputs; 64 KiB less per (chunk,
+// head) of state at d = 128).
+template <int DK, int DV, int C, bool H16 = false> struct GRec {
+    static constexpr size_t SE = H16 ? 2 : 4;    // bytes per element of SIN and UC
     static constexpr size_t CK = size_t(C) * DK * 4, CV = size_t(C) * DV * 4, CC = size_t(C) * C * 4;
     static constexpr size_t QH = 0;              // Gamma . Q                 [C][DK]
     static constexpr size_t KT = QH + CK;        // (gamma / Gamma) . K       [C][DK]
@@ -59,8 +99,8 @@ template <int DK, int DV, int C> struct GRec {
     static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]
     static constexpr size_t GAM = P + CC;        // gamma                     [DK]
     static constexpr size_t SIN = GAM + size_t(DK) * 4;   // state entering  [DK][DV]
-    static constexpr size_t UC = SIN + size_t(DK) * DV * 4;   // U - W S    [C][DV]
-    static constexpr size_t END = UC + CV;
+    static constexpr size_t UC = SIN + size_t(DK) * DV * SE;  // U - W S    [C][DV]
+    static constexpr size_t END = UC + size_t(C) * DV * SE;
 };
 
 struct GParams {
@@ -483,9 +523,9 @@ template <int DK, int C> struct GChainB {
     static constexpr int bytes = (2 * C * LK + DK * L16 + C * L16 + (NSPLIT - 1) * C * L16 + DK) * 4;
 };
 
-template <int DK, int DV, int C>
+template <int DK, int DV, int C, bool H16>
 __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GParams P) {
-    using R = GRec<DK, DV, C>;
+    using R = GRec<DK, DV, C, H16>;
     constexpr int NTH = kThreads, NW = kWaves, LK = GChainB<DK, C>::LK, NT = DV / 16;
     constexpr int NB = C / 16, NSPLIT = GChainB<DK, C>::NSPLIT, KP = DK / NSPLIT;
     constexpr int NRB = DK / 16, RBW = (NRB + NW - 1) / NW;
@@ -551,7 +591,8 @@ __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GPar
             const int rb = wave + NW * u;
             if (rb >= NRB) continue;
             store_tile(sS + rb * 16 * L16, L16, S[u]);
-            store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
+            if constexpr (H16) store_tile_h(reinterpret_cast<_Float16*>(gS) + rb * 16 * DV + c0, DV, S[u]);
+            else store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
         }
         __syncthreads();
         if (g + 1 < g1) fetch(g + 1);
@@ -564,7 +605,8 @@ __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GPar
 #pragma unroll
             for (int p2 = 1; p2 < NSPLIT; ++p2) uc -= load_tile(sPart + ((p2 - 1) * C + mb * 16) * L16, L16);
             store_tile(sU + mb * 16 * L16, L16, uc);
-            store_tile(grec(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
+            if constexpr (H16) store_tile_h(reinterpret_cast<_Float16*>(grec(P, h, g, R::UC)) + mb * 16 * DV + c0, DV, uc);
+            else store_tile(grec(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
         }
         __syncthreads();
         // S <- Diag(gamma) S + Kt^T U'
@@ -603,9 +645,9 @@ template <int DK, int C> struct GOutB {
     static constexpr int bytes = ((QREG ? 0 : C * LK) + DK * kLS + NLT * 256 + C * kLS) * 4;
 };
 
-template <int DK, int DV, int C, bool OBF16>
+template <int DK, int DV, int C, bool OBF16, bool H16>
 __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
-    using R = GRec<DK, DV, C>;
+    using R = GRec<DK, DV, C, H16>;
     constexpr int NTH = kThreads, NW = kWaves, SL = kSL, LS = kLS;
     constexpr int NB = GOutB<DK, C>::NB, NLT = GOutB<DK, C>::NLT, NSV = DV / SL;
     constexpr int PIT = (NLT * 256 + NTH - 1) / NTH;
@@ -640,12 +682,15 @@ __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
     }
     {
         Blk<C, QREG ? 4 : DK, NTH> bq;      // (QREG: unused)
-        Blk<DK, SL, NTH> bs;
-        Blk<C, SL, NTH> bu;
+        using BS = std::conditional_t<H16, BlkH<DK, SL, NTH>, Blk<DK, SL, NTH>>;
+        using BU = std::conditional_t<H16, BlkH<C, SL, NTH>, Blk<C, SL, NTH>>;
+        using SE = std::conditional_t<H16, _Float16, float>;
+        BS bs;
+        BU bu;
         float pv[PIT];
         if constexpr (!QREG) bq.load(grec(P, h, g, R::QH), DK);
-        bs.load(grec(P, h, g, R::SIN) + s0, DV);
-        bu.load(grec(P, h, g, R::UC) + s0, DV);
+        bs.load(reinterpret_cast<const SE*>(grec(P, h, g, R::SIN)) + s0, DV);
+        bu.load(reinterpret_cast<const SE*>(grec(P, h, g, R::UC)) + s0, DV);
         const float* gP = grec(P, h, g, R::P);
 #pragma unroll
         for (int it = 0; it < PIT; ++it) {
@@ -701,7 +746,7 @@ hipError_t set_lds(F* kfn, int bytes) {
 template <int DK, int DV, int C, bool ABF16, bool OBF16, int GATE>
 hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t stream) {
     unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-    if (GRec<DK, DV, C>::END > pl.rec_bytes) return hipErrorInvalidValue;
+    if (GRec<DK, DV, C, ABF16>::END > pl.rec_bytes) return hipErrorInvalidValue;
     GParams p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.gate = a.gate; p.beta = a.beta;
     p.initial_state = a.initial_state; p.final_state = a.final_state; p.o = a.o;
@@ -731,14 +776,14 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         }
     }
     if (chain_blocks > 0) {
-        auto k2 = gchain_kernel<DK, DV, C>;
+        auto k2 = gchain_kernel<DK, DV, C, ABF16>;
         constexpr int l2 = GChainB<DK, C>::bytes;
         if ((e = set_lds(k2, l2)) != hipSuccess) return e;
         hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(GChainPF<C>::threads), l2, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (chunk_blocks > 0) {
-        auto k3 = gout_kernel<DK, DV, C, OBF16>;
+        auto k3 = gout_kernel<DK, DV, C, OBF16, ABF16>;
         constexpr int l3 = GOutB<DK, C>::bytes;
         if ((e = set_lds(k3, l3)) != hipSuccess) return e;
         hipLaunchKernelGGL(k3, dim3(chunk_blocks * (DV / kSL)), dim3(kThreads), l3, stream, p);
@@ -770,17 +815,18 @@ hipError_t launch_c(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t stream)
 }
 
 template <int DK, int DV>
-size_t rec_end(int c) {
+size_t rec_end(int c, bool h16) {
+    if (h16) return c == 32 ? GRec<DK, DV, 32, true>::END : c == 128 ? GRec<DK, DV, 128, true>::END : GRec<DK, DV, 64, true>::END;
     return c == 32 ? GRec<DK, DV, 32>::END : c == 128 ? GRec<DK, DV, 128>::END : GRec<DK, DV, 64>::END;
 }
 
 }  // namespace
 
-size_t generic_record_bytes(int Dk, int Dv, int chunk_size) {
-    if (Dk == 128 && Dv == 128) return rec_end<128, 128>(chunk_size);
-    if (Dk == 64 && Dv == 64) return rec_end<64, 64>(chunk_size);
-    if (Dk == 128 && Dv == 64) return rec_end<128, 64>(chunk_size);
-    return rec_end<64, 128>(chunk_size);
+size_t generic_record_bytes(int Dk, int Dv, int chunk_size, bool act16) {
+    if (Dk == 128 && Dv == 128) return rec_end<128, 128>(chunk_size, act16);
+    if (Dk == 64 && Dv == 64) return rec_end<64, 64>(chunk_size, act16);
+    if (Dk == 128 && Dv == 64) return rec_end<128, 64>(chunk_size, act16);
+    return rec_end<64, 128>(chunk_size, act16);
 }
 
 hipError_t launch_chunk_fwd_generic(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t stream) {
