@@ -60,7 +60,7 @@ def test_workspace_size_plan():
     # unsupported combinations report 0
     assert f(1, 256, 1, 96, 64, False, 0, 64, kda.KDA_DTYPE_BF16) == 0
     assert f(1, 256, 1, 64, 64, False, 0, 96, kda.KDA_DTYPE_BF16) == 0
-    # chunk sizes 32 and 128 take the generic path, with its own (fp32) record
+    # chunk sizes 32 and 128 take the generic path, with its own record
     assert f(1, 256, 1, 64, 64, False, 0, 32, kda.KDA_DTYPE_BF16) > 0
     assert f(1, 256, 1, 64, 64, False, 0, 128, kda.KDA_DTYPE_BF16) > 0
     # the backward runs at C = 64 only
@@ -70,6 +70,23 @@ def test_workspace_size_plan():
     assert fb(1, 256, 1, 64, 64, False, 0, 128, kda.KDA_DTYPE_BF16) == 0
     assert f(2, 256, 1, 64, 64, True, 3, 64, kda.KDA_DTYPE_BF16) == 0
     assert f(1, 1 << 31, 1, 64, 64, False, 0, 64, kda.KDA_DTYPE_BF16) == 0
+
+
+@pytest.mark.parametrize("C", [32, 128])
+@pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
+def test_generic_record_size(C, Dk, Dv):
+    """One more chunk adds H generic records: Gamma.Q, Kt, W, b (C x d_k each),
+    U (C x d_v) and P (C x C) in fp32, gamma (d_k fp32), and the state
+    entering the chunk (d_k x d_v) and U' (C x d_v), which are fp16 with
+    16-bit activations and fp32 otherwise (up to the 256-byte alignment
+    steps of the regions that grow)."""
+    H = 3
+    f = kda.kda_chunk_fwd_workspace_bytes
+    for act, se in ((kda.KDA_DTYPE_F32, 4), (kda.KDA_DTYPE_BF16, 2)):
+        r = (4 * C * Dk + C * Dv + C * C + Dk) * 4 + (Dk * Dv + C * Dv) * se
+        r = (r + 255) // 256 * 256
+        diff = f(1, 10 * C, H, Dk, Dv, False, 0, C, act) - f(1, 9 * C, H, Dk, Dv, False, 0, C, act)
+        assert abs(diff - H * r) <= 4 * 256, (act, diff, H * r)
 
 
 def _chunk(**over):
