@@ -98,9 +98,12 @@ template <int DK, int DV, int C, bool H16 = false> struct GRec {
     static constexpr size_t U = B + CK;          // T Diag(beta) V            [C][DV]
     static constexpr size_t P = U + CV;          // Tril(Qh Kb^T)             [C][C]
     static constexpr size_t GAM = P + CC;        // gamma                     [DK]
+    // the chain's outputs for the output pass; at C = 32 the chain writes O
+    // itself (FUSED) and the record ends before them
+    static constexpr bool FUSED = C <= 32;
     static constexpr size_t SIN = GAM + size_t(DK) * 4;   // state entering  [DK][DV]
     static constexpr size_t UC = SIN + size_t(DK) * DV * SE;  // U - W S    [C][DV]
-    static constexpr size_t END = UC + size_t(C) * DV * SE;
+    static constexpr size_t END = FUSED ? SIN : UC + size_t(C) * DV * SE;
 };
 
 struct GParams {
@@ -518,17 +521,27 @@ template <int C> struct GChainPF {
     static constexpr int threads = on ? kThreads + 64 : kThreads;
 };
 constexpr int kGChainPrefetch = 2;
+// FUSED (C = 32): the chain also forms O = Gamma.Q S + P U' for its 16
+// columns, so neither the state entering each chunk nor U' goes through the
+// record and no output pass runs.  Gamma.Q S is split over the waves like
+// W S (row block w % (C/16), part w / (C/16) of d_k, partial sums through
+// LDS); the part-0 waves add them and P U' and store the rows.
 template <int DK, int C> struct GChainB {
-    static constexpr int LK = Ld<DK>::value, NSPLIT = kWaves / (C / 16);
-    static constexpr int bytes = (2 * C * LK + DK * L16 + C * L16 + (NSPLIT - 1) * C * L16 + DK) * 4;
+    static constexpr int LK = Ld<DK>::value, NSPLIT = kWaves / (C / 16), LP = C + 4;
+    static constexpr bool FUSED = C <= 32;
+    static constexpr int bytes = (2 * C * LK + DK * L16 + C * L16 + (NSPLIT - 1) * C * L16 + DK +
+                                  (FUSED ? C * LK + (NSPLIT - 1) * C * L16 + C * LP : 0)) * 4;
 };
 
-template <int DK, int DV, int C, bool H16>
+template <int DK, int DV, int C, bool H16, bool OBF16>
 __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GParams P) {
     using R = GRec<DK, DV, C, H16>;
     constexpr int NTH = kThreads, NW = kWaves, LK = GChainB<DK, C>::LK, NT = DV / 16;
     constexpr int NB = C / 16, NSPLIT = GChainB<DK, C>::NSPLIT, KP = DK / NSPLIT;
     constexpr int NRB = DK / 16, RBW = (NRB + NW - 1) / NW;
+    constexpr bool FUSED = GChainB<DK, C>::FUSED;
+    constexpr int LP = GChainB<DK, C>::LP;
+    static_assert(FUSED == R::FUSED, "the record and the chain agree on the fused output");
     extern __shared__ float lds[];
     float* sW = lds;                 // [C][LK]
     float* sKt = sW + C * LK;        // [C][LK]
@@ -536,6 +549,9 @@ __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GPar
     float* sU = sS + DK * L16;       // [C][16]
     float* sPart = sU + C * L16;     // [NSPLIT - 1][C][16]
     float* sGam = sPart + (NSPLIT - 1) * C * L16;   // [DK]
+    [[maybe_unused]] float* sQh = sGam + DK;                       // FUSED: Gamma.Q [C][LK]
+    [[maybe_unused]] float* sPartO = sQh + C * LK;                 // FUSED: [NSPLIT - 1][C][16]
+    [[maybe_unused]] float* sPm = sPartO + (NSPLIT - 1) * C * L16; // FUSED: P [C][LP]
 
     int tile, pair;
     chain_coords<NT>(tile, pair);
@@ -572,11 +588,17 @@ __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GPar
         S[u] = (P.initial_state && rb < NRB) ? load_tile(P.initial_state + sbase + rb * 16 * DV + c0, DV) : zero4();
     }
     Blk<C, DK, NTH> nW, nKt;
+    [[maybe_unused]] Blk<C, FUSED ? DK : 4, NTH> nQh;
+    [[maybe_unused]] Blk<C, FUSED ? C : 4, NTH> nP;
     f4 nU = zero4();
     float nGam = 0.f;
     auto fetch = [&](int g) {
         nW.load(grec(P, h, g, R::W), DK);
         nKt.load(grec(P, h, g, R::KT), DK);
+        if constexpr (FUSED) {
+            nQh.load(grec(P, h, g, R::QH), DK);
+            nP.load(grec(P, h, g, R::P), C);
+        }
         if (part == 0) nU = load_tile(grec(P, h, g, R::U) + mb * 16 * DV + c0, DV);
         if (threadIdx.x < DK) nGam = grec(P, h, g, R::GAM)[threadIdx.x];
     };
@@ -584,31 +606,63 @@ __global__ __launch_bounds__(GChainPF<C>::threads) void gchain_kernel(const GPar
     for (int g = g0; g < g1; ++g) {
         nW.put(sW, LK);
         nKt.put(sKt, LK);
+        if constexpr (FUSED) {
+            nQh.put(sQh, LK);
+            nP.put(sPm, LP);
+        }
         const f4 uu = nU;
         if (threadIdx.x < DK) sGam[threadIdx.x] = nGam;
-        float* gS = grec(P, h, g, R::SIN);
         for (int u = 0; u < RBW; ++u) {
             const int rb = wave + NW * u;
             if (rb >= NRB) continue;
             store_tile(sS + rb * 16 * L16, L16, S[u]);
-            if constexpr (H16) store_tile_h(reinterpret_cast<_Float16*>(gS) + rb * 16 * DV + c0, DV, S[u]);
-            else store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
+            if constexpr (!FUSED) {
+                float* gS = grec(P, h, g, R::SIN);
+                if constexpr (H16) store_tile_h(reinterpret_cast<_Float16*>(gS) + rb * 16 * DV + c0, DV, S[u]);
+                else store_tile(gS + rb * 16 * DV + c0, DV, S[u]);
+            }
         }
         __syncthreads();
         if (g + 1 < g1) fetch(g + 1);
-        // U' = U - W S
+        // U' = U - W S (and FUSED: Gamma.Q S), this wave's part of d_k
         const f4 x = mm<KP, true, false>(sW + mb * 16 * LK + part * KP, LK, 1, sS + part * KP * L16, L16, 1, zero4());
         if (part) store_tile(sPart + ((part - 1) * C + mb * 16) * L16, L16, x);
+        [[maybe_unused]] f4 y = zero4();
+        if constexpr (FUSED) {
+            y = mm<KP, true, false>(sQh + mb * 16 * LK + part * KP, LK, 1, sS + part * KP * L16, L16, 1, zero4());
+            if (part) store_tile(sPartO + ((part - 1) * C + mb * 16) * L16, L16, y);
+        }
         __syncthreads();
         if (part == 0) {
             f4 uc = uu - x;
 #pragma unroll
             for (int p2 = 1; p2 < NSPLIT; ++p2) uc -= load_tile(sPart + ((p2 - 1) * C + mb * 16) * L16, L16);
             store_tile(sU + mb * 16 * L16, L16, uc);
-            if constexpr (H16) store_tile_h(reinterpret_cast<_Float16*>(grec(P, h, g, R::UC)) + mb * 16 * DV + c0, DV, uc);
-            else store_tile(grec(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
+            if constexpr (FUSED) {
+#pragma unroll
+                for (int p2 = 1; p2 < NSPLIT; ++p2) y += load_tile(sPartO + ((p2 - 1) * C + mb * 16) * L16, L16);
+            } else if constexpr (H16) {
+                store_tile_h(reinterpret_cast<_Float16*>(grec(P, h, g, R::UC)) + mb * 16 * DV + c0, DV, uc);
+            } else {
+                store_tile(grec(P, h, g, R::UC) + mb * 16 * DV + c0, DV, uc);
+            }
         }
         __syncthreads();
+        if constexpr (FUSED) {
+            // O rows of row block mb: Gamma.Q S + P U' (P lower triangular)
+            if (part == 0) {
+                for (int kb = 0; kb <= mb; ++kb)
+                    y = mm<16, true, false>(sPm + mb * 16 * LP + kb * 16, LP, 1, sU + kb * 16 * L16, L16, 1, y);
+                const int4 ent = P.table[g];
+                const int i = lane_id() & 15;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = mb * 16 + 4 * j + e;
+                    if (r < ent.z)
+                        store_out<OBF16>(P.o, (static_cast<size_t>(ent.y + r) * P.H + h) * DV + c0 + i, y[e]);
+                }
+            }
+        }
         // S <- Diag(gamma) S + Kt^T U'
         for (int u = 0; u < RBW; ++u) {
             const int rb = wave + NW * u;
@@ -776,18 +830,20 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         }
     }
     if (chain_blocks > 0) {
-        auto k2 = gchain_kernel<DK, DV, C, ABF16>;
+        auto k2 = gchain_kernel<DK, DV, C, ABF16, GChainB<DK, C>::FUSED && OBF16>;
         constexpr int l2 = GChainB<DK, C>::bytes;
         if ((e = set_lds(k2, l2)) != hipSuccess) return e;
         hipLaunchKernelGGL(k2, dim3(chain_blocks), dim3(GChainPF<C>::threads), l2, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (chunk_blocks > 0) {
-        auto k3 = gout_kernel<DK, DV, C, OBF16, ABF16>;
-        constexpr int l3 = GOutB<DK, C>::bytes;
-        if ((e = set_lds(k3, l3)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k3, dim3(chunk_blocks * (DV / kSL)), dim3(kThreads), l3, stream, p);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
+    if constexpr (!GChainB<DK, C>::FUSED) {
+        if (chunk_blocks > 0) {
+            auto k3 = gout_kernel<DK, DV, C, OBF16, ABF16>;
+            constexpr int l3 = GOutB<DK, C>::bytes;
+            if ((e = set_lds(k3, l3)) != hipSuccess) return e;
+            hipLaunchKernelGGL(k3, dim3(chunk_blocks * (DV / kSL)), dim3(kThreads), l3, stream, p);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
     }
     return hipSuccess;
 }

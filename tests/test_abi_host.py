@@ -76,14 +76,15 @@ def test_workspace_size_plan():
 @pytest.mark.parametrize("Dk,Dv", [(128, 128), (64, 64), (128, 64), (64, 128)])
 def test_generic_record_size(C, Dk, Dv):
     """One more chunk adds H generic records: Gamma.Q, Kt, W, b (C x d_k each),
-    U (C x d_v) and P (C x C) in fp32, gamma (d_k fp32), and the state
-    entering the chunk (d_k x d_v) and U' (C x d_v), which are fp16 with
-    16-bit activations and fp32 otherwise (up to the 256-byte alignment
-    steps of the regions that grow)."""
+    U (C x d_v) and P (C x C) in fp32, gamma (d_k fp32), and at C = 128 the
+    state entering the chunk (d_k x d_v) and U' (C x d_v) for the output
+    pass, fp16 with 16-bit activations and fp32 otherwise (at C = 32 the
+    chain writes the output itself and the record ends at gamma); up to the
+    256-byte alignment steps of the regions that grow."""
     H = 3
     f = kda.kda_chunk_fwd_workspace_bytes
     for act, se in ((kda.KDA_DTYPE_F32, 4), (kda.KDA_DTYPE_BF16, 2)):
-        r = (4 * C * Dk + C * Dv + C * C + Dk) * 4 + (Dk * Dv + C * Dv) * se
+        r = (4 * C * Dk + C * Dv + C * C + Dk) * 4 + ((Dk * Dv + C * Dv) * se if C == 128 else 0)
         r = (r + 255) // 256 * 256
         diff = f(1, 10 * C, H, Dk, Dv, False, 0, C, act) - f(1, 9 * C, H, Dk, Dv, False, 0, C, act)
         assert abs(diff - H * r) <= 4 * 256, (act, diff, H * r)
