@@ -45,10 +45,10 @@
  *    stated at its declaration.
  *  - Supported: d_k in {64, 128}, d_v in {64, 128}; chunk_size 64 for
  *    every call, and also 32 or 128 for the chunkwise forward (a generic
- *    path with every product in fp32; with 16-bit activations it keeps the
- *    state entering each chunk and U' in fp16 in the workspace; the result
- *    is the same recurrence, the chunk size only changes how the work is
- *    cut).
+ *    path with every product in fp32; at chunk size 128 with 16-bit
+ *    activations it keeps the state entering each chunk and U' in fp16 in
+ *    the workspace; the result is the same recurrence, the chunk size only
+ *    changes how the work is cut).
  *    Activations (q, k, v) are either all fp32 or all bf16; alpha, beta and
  *    every state are fp32.  The output o is fp32, or bf16 when the
  *    activations are bf16 (rounded once, to nearest-even, from the fp32
