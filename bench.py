@@ -715,7 +715,9 @@ def main():
                                              "dtype": "f32"}}
             del wsc
         var["chunk_note"] = ("chunk sizes 32 and 128 take the generic path (every product on the fp32 "
-                             "matrix cores, fp32 record); chunk 64 is the main line")
+                             "matrix cores; at C = 32 the chain forms the output itself, at C = 128 an "
+                             "output pass reads the stored state and U', fp16 with bf16 activations); "
+                             "chunk 64 is the main line")
         # accuracy - memory - time of the chunk-size ablation, one row per C
         abl = {"64": {"fwd_ms": out["fwd_ms"], "workspace_GiB": round(ws_bytes / 2 ** 30, 2),
                       "parity": ({"o": out["parity"]["o"], "S_T": out["parity"]["S_T"]}
