@@ -6,9 +6,9 @@
 // The C = 64 kernels (kda_chunk.hip) are laid out for that one size; this
 // path computes the same chunked algorithm for C in {32, 128} with every
 // product on the fp32 matrix cores (the backward's building blocks), in
-// three launches after the shared chunk-table kernel:
+// three launches after the shared chunk-table kernel (two at C = 32):
 //
-//   gprep_kernel   one 512-thread WG per (chunk, head).  The key channels are
+//   gprep_kernel   one WG per (chunk, head), 512 threads (1024 at C = 128).  The key channels are
 //                  taken 32 at a time: b = cumsum(log2 alpha), Gamma.Q,
 //                  (gamma/Gamma).K and gamma go to the record, and the
 //                  16 x 16 tiles of A = StrictTril(Diag(beta) Kh Kb^T) and
@@ -19,11 +19,12 @@
 //                  LDS); W = T Diag(beta) Kh and U = T Diag(beta) V, again 32
 //                  columns at a time.
 //   gchain_kernel  one 512-thread WG per (sequence, head, 16 value columns),
-//                  chunks in order: writes the state entering each chunk and
-//                  U' = U - W S, then S <- Diag(gamma) S + Kt^T U'; the final
-//                  state at the end.
-//   gout_kernel    one 512-thread WG per (chunk, head, 32 value columns):
-//                  O = Qh S + P U'.
+//                  chunks in order: U' = U - W S, then S <- Diag(gamma) S +
+//                  Kt^T U'; the final state at the end.  At C = 128 the state
+//                  entering each chunk and U' go to the record for gout; at
+//                  C = 32 the chain forms O = Qh S + P U' itself.
+//   gout_kernel    (C = 128) one 512-thread WG per (chunk, head, 32 value
+//                  columns): O = Qh S + P U'.
 #include <type_traits>
 
 #include "kda_chunk.h"
@@ -134,12 +135,19 @@ __device__ __forceinline__ float* grec(const GParams& P, int h, int g, size_t of
 // ---------------------------------------------------------------------------
 // gprep_kernel
 // ---------------------------------------------------------------------------
+// Threads of a preparation workgroup: at C = 128 its 140 KB of LDS leave one
+// workgroup per CU, so it runs sixteen waves instead of eight.
+template <int C> struct GPrepT {
+    static constexpr int threads = C >= 128 ? 1024 : kThreads;
+};
+
 template <int C> struct GPrepB {
-    static constexpr int NB = C / 16, NLT = NB * (NB + 1) / 2, NS = kThreads / kSL;
+    static constexpr int NW = GPrepT<C>::threads / 64;
+    static constexpr int NB = C / 16, NLT = NB * (NB + 1) / 2, NS = GPrepT<C>::threads / kSL;
     // the last region: the direct form's scan segment sums [NS][SL] and gamma
     // of the slice [SL], or the general form's tile totals [NB][SL]
     static constexpr int AUX = NS * kSL + kSL > NB * kSL ? NS * kSL + kSL : NB * kSL;
-    static constexpr int bytes = (3 * C * kLS + 2 * NLT * 256 + kWaves * 256 + 2 * C + AUX) * 4;
+    static constexpr int bytes = (3 * C * kLS + 2 * NLT * 256 + NW * 256 + 2 * C + AUX) * 4;
 };
 
 // FAST: the direct form (one cumulative log2 sum per channel over the chunk;
@@ -150,7 +158,7 @@ template <int C> struct GPrepB {
 template <int DK, int DV, int C, bool ABF16, int GATE, bool FAST>
 __device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
     using R = GRec<DK, DV, C>;
-    constexpr int NTH = kThreads, NW = kWaves, SL = kSL, LS = kLS;
+    constexpr int NTH = GPrepT<C>::threads, NW = NTH / 64, SL = kSL, LS = kLS;
     constexpr int NB = GPrepB<C>::NB, NLT = GPrepB<C>::NLT;
     constexpr int NS = GPrepB<C>::NS, SEG = C / NS;   // direct form: scan segments
     constexpr int NTASK = 2 * NLT;        // direct form: A and P tiles as separate tasks
@@ -494,14 +502,14 @@ __device__ __forceinline__ void gprep_body(const GParams& P, const int blk) {
 // One workgroup per (chunk, head): the direct form (listing the chunks that
 // need the general one).
 template <int DK, int DV, int C, bool ABF16, int GATE>
-__global__ __launch_bounds__(kThreads) void gprep_kernel(const GParams P) {
+__global__ __launch_bounds__(GPrepT<C>::threads) void gprep_kernel(const GParams P) {
     gprep_body<DK, DV, C, ABF16, GATE, true>(P, blockIdx.x);
 }
 
 // Entry blockIdx.x of the general-form list, if the list is that long (one
 // workgroup per (chunk, head), the list's largest length).
 template <int DK, int DV, int C, bool ABF16, int GATE>
-__global__ __launch_bounds__(kThreads) void gprep_general_kernel(const GParams P) {
+__global__ __launch_bounds__(GPrepT<C>::threads) void gprep_general_kernel(const GParams P) {
     if (static_cast<int>(blockIdx.x) >= *P.nslow) return;
     gprep_body<DK, DV, C, ABF16, GATE, false>(P, P.slow[blockIdx.x]);
 }
@@ -825,7 +833,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
         constexpr int l1 = GPrepB<C>::bytes;
         for (auto k1 : {gprep_kernel<DK, DV, C, ABF16, GATE>, gprep_general_kernel<DK, DV, C, ABF16, GATE>}) {
             if ((e = set_lds(k1, l1)) != hipSuccess) return e;
-            hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(kThreads), l1, stream, p);
+            hipLaunchKernelGGL(k1, dim3(chunk_blocks), dim3(GPrepT<C>::threads), l1, stream, p);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
