@@ -548,14 +548,20 @@ __device__ __forceinline__ void prep_direct_body(const BwdParams& P, const int h
         write_afrags<C, C, NTH>(hrec(R::FPT), [&](int m, int k) { return sT[k * LC + m]; });
         __syncthreads();
     }
-    solve_t(sA, sT, sX1);
-    // the W pass's inputs (V is read only here; issued after the solve,
-    // whose 16 x 16 substitution needs the registers): the key slices other
-    // than the last, whose Gamma.K is still in sX0
-    if (NKS > 1) load_slice(0, false);
+    // the W pass's inputs: V (read only here) and the key slices other than
+    // the last, whose Gamma.K is still in sX0. bf16 tiles are issued before
+    // the solve, which then hides their latency; fp32 tiles hold twice the
+    // registers and would push the 16 x 16 substitution into scratch, so
+    // they follow it
     Tok<ABF16, DV, KSL, NTH> tv[NVS];
+    auto load_w_inputs = [&] {
+        if (NKS > 1) load_slice(0, false);
 #pragma unroll
-    for (int vs = 0; vs < NVS; ++vs) tv[vs].load(P.v, row0, len, h, H, vs * KSL);
+        for (int vs = 0; vs < NVS; ++vs) tv[vs].load(P.v, row0, len, h, H, vs * KSL);
+    };
+    if constexpr (ABF16) load_w_inputs();
+    solve_t(sA, sT, sX1);
+    if constexpr (!ABF16) load_w_inputs();
     store_block<NTH>(rec_at(P, h, g, R::TT), C, sT, LC, C, C);
 
     // W = T Y, U = T Z (Y = Diag(beta) Gamma.K, Z = Diag(beta) V), one key
