@@ -724,8 +724,14 @@ __global__ __launch_bounds__(kThreads) void gout_kernel(const GParams P) {
     float* sP = sS + DK * LS;        // P, packed lower tiles [NLT][256]
     float* sU = sP + NLT * 256;      // U'[:, slice]  [C][LS]
 
+    // Workgroups are dealt to the 8 XCDs round-robin: the NSV workgroups of
+    // one (chunk, head) get block indices NSV consecutive slots apart on one
+    // XCD, so its Gamma.Q and P are read into that XCD's L2 once. The grid is
+    // padded to a multiple of 8 (chunk, head) pairs.
     const int H = P.H;
-    const int sv = blockIdx.x % NSV, gh = blockIdx.x / NSV;
+    const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+    const int sv = slot % NSV, gh = (slot / NSV) * 8 + xcd;
+    if (gh >= P.gmax * H) return;
     const int h = gh % H, g = gh / H;
     if (g >= P.ctrl[0]) return;
     const int4 ent = P.table[g];
@@ -849,7 +855,7 @@ hipError_t launch_typed(const ChunkPlan& pl, const ChunkArgs& a, hipStream_t str
             auto k3 = gout_kernel<DK, DV, C, OBF16, ABF16>;
             constexpr int l3 = GOutB<DK, C>::bytes;
             if ((e = set_lds(k3, l3)) != hipSuccess) return e;
-            hipLaunchKernelGGL(k3, dim3(chunk_blocks * (DV / kSL)), dim3(kThreads), l3, stream, p);
+            hipLaunchKernelGGL(k3, dim3((chunk_blocks + 7) / 8 * 8 * (DV / kSL)), dim3(kThreads), l3, stream, p);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }
